@@ -1,0 +1,393 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Nothing here compares the oracle with itself in the same form: each test uses a
+closed form, an invariant, a library routine (torch SDPA in float64), a brute
+force over a tiny case, or a value printed on the pages (tests/golden/).
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from decoder_only_forward_amd import configs, synth
+from oracle import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# ---- the input generator -------------------------------------------------
+
+def test_splitmix64_published_sequence():
+    want = [int(r[0], 16) for r in _golden_rows("splitmix64_seed0.txt")]
+    assert [synth.splitmix64_int(0, i) for i in (1, 2, 3)] == want
+
+
+def test_generator_vector_path_matches_scalar_definition():
+    key = synth.tensor_key(0, 77)
+    r = synth._raw(key, 10, 5, "cpu")
+    want = [synth.splitmix64_int(key, 11 + j) for j in range(5)]
+    assert [int(x) & synth.MASK64 for x in r.tolist()] == want
+    z = synth.normal(0, 77, 3, 4)
+    for j in range(4):
+        e = 3 + j
+        u1 = ((synth.splitmix64_int(key, 2 * e + 1) >> 11) + 0.5) * 2.0 ** -53
+        u2 = ((synth.splitmix64_int(key, 2 * e + 2) >> 11) + 0.5) * 2.0 ** -53
+        assert z[j].item() == math.sqrt(-2 * math.log(u1)) * math.cos(2 * math.pi * u2)
+
+
+def test_generator_distribution_and_chunking():
+    z = synth.normal(0, 5, 0, 1 << 20)
+    assert abs(z.mean().item()) < 5e-3 and abs(z.std().item() - 1) < 5e-3
+    a = torch.empty(1000, dtype=torch.bfloat16)
+    b = torch.empty(1000, dtype=torch.bfloat16)
+    synth.fill_normal(a, 0, 9, 0.02, chunk=1 << 20)
+    synth.fill_normal(b, 0, 9, 0.02, chunk=37)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    t = synth.tokens(0, synth.PROMPT_STREAM, 4096, 151936)
+    assert t.min() >= 0 and t.max() < 151936
+
+
+# ---- RMSNorm (Pantheon, "RMSNorm") ----------------------------------------
+
+@pytest.mark.parametrize("kind", ["f32", "f64"])
+@pytest.mark.parametrize("c", [0.0, 1e-3, 0.5, 3.0, -7.0])
+def test_rmsnorm_constant_vector_closed_form(kind, c):
+    d, eps = 64, 1e-5
+    out = O.rmsnorm(np.full(d, c), np.ones(d), eps, kind)
+    want = c / math.sqrt(c * c + eps)
+    np.testing.assert_allclose(out, want, rtol=2e-6 if kind == "f32" else 1e-14, atol=1e-30)
+
+
+def test_rmsnorm_gain_is_elementwise_and_mean_not_sum():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(96)
+    for j in (0, 5, 95):
+        g = np.zeros(96)
+        g[j] = 2.0
+        out = O.rmsnorm(x, g, 1e-6, "f64")
+        assert np.count_nonzero(out) == 1 and out[j] != 0
+    out = O.rmsnorm(x, np.ones(96), 1e-12, "f64")
+    assert abs(np.mean(out ** 2) - 1.0) < 1e-9          # unit RMS => mean, not sum
+    np.testing.assert_allclose(O.rmsnorm(1000 * x, np.ones(96), 1e-12, "f64"), out, rtol=1e-9)
+
+
+# ---- RoPE (sipllm "RoPE is adjacent-pair"; rml "Rotary embeddings") -------
+
+def test_rope_position_zero_is_identity():
+    rng = np.random.default_rng(1)
+    h = rng.standard_normal(3 * 16)
+    np.testing.assert_array_equal(O.rope(h, 3, 16, 0, 1e4, "f64"), h)
+
+
+def test_rope_pair_angles_use_pair_index():
+    hd, theta = 16, 1e4
+    for pos in (1, 2, 7, 100):
+        for i in range(hd // 2):
+            h = np.zeros(hd)
+            h[2 * i] = 1.0                  # unit vector in pair i, adjacent elements
+            out = O.rope(h, 1, hd, pos, theta, "f64")
+            others = np.delete(out, [2 * i, 2 * i + 1])
+            assert np.all(others == 0)       # pairs are (2i, 2i+1), nothing else moves
+            ang = math.atan2(out[2 * i + 1], out[2 * i])
+            want = math.remainder(pos * theta ** (-2.0 * i / hd), 2 * math.pi)
+            assert abs(math.remainder(ang - want, 2 * math.pi)) < 1e-12
+    h = np.array([1.0, 0.0] + [0.0] * 14)
+    out = O.rope(h, 1, 16, 3, 1e4, "f64")    # pair 0 turns exactly pos radians
+    assert abs(out[0] - math.cos(3)) < 1e-15 and abs(out[1] - math.sin(3)) < 1e-15
+
+
+def test_rope_preserves_pair_norms_and_relative_position():
+    rng = np.random.default_rng(2)
+    hd = 64
+    q = rng.standard_normal(hd)
+    k = rng.standard_normal(hd)
+    qr = O.rope(q, 1, hd, 37, 1e6, "f64")
+    np.testing.assert_allclose(np.hypot(qr[0::2], qr[1::2]), np.hypot(q[0::2], q[1::2]), rtol=1e-13)
+    for (m, n, s) in ((5, 2, 11), (100, 99, 1000), (4096, 0, 3)):
+        a = O.rope(q, 1, hd, m, 1e4, "f64") @ O.rope(k, 1, hd, n, 1e4, "f64")
+        b = O.rope(q, 1, hd, m + s, 1e4, "f64") @ O.rope(k, 1, hd, n + s, 1e4, "f64")
+        assert abs(a - b) < 1e-9 * (1 + abs(a))
+
+
+# ---- attention (Pantheon "GQA"; rml "Attend"; zLLM section 2) -------------
+
+def _sdpa_ref(q, k, v, window):
+    """torch's scaled_dot_product_attention in float64 with a causal (and
+    optionally banded) boolean mask; GQA by the library's enable_gqa."""
+    n, nh, hd = q.shape
+    qt = torch.from_numpy(q).permute(1, 0, 2)[None]
+    kt = torch.from_numpy(k).permute(1, 0, 2)[None]
+    vt = torch.from_numpy(v).permute(1, 0, 2)[None]
+    i = torch.arange(n)[:, None]
+    j = torch.arange(n)[None, :]
+    mask = j <= i
+    if window:
+        mask &= j > i - window
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, enable_gqa=True)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+@pytest.mark.parametrize("nh,nkv,hd,window", [(4, 2, 16, 0), (14, 2, 64, 0), (9, 3, 64, 0),
+                                              (8, 8, 32, 0), (4, 1, 16, 5), (6, 2, 16, 3)])
+def test_attention_matches_library_sdpa(nh, nkv, hd, window):
+    rng = np.random.default_rng(nh * 100 + hd)
+    n = 23
+    q = rng.standard_normal((n, nh, hd))
+    k = rng.standard_normal((n, nkv, hd))
+    v = rng.standard_normal((n, nkv, hd))
+    got = O.attention_prefill(q, k, v, window, "f64")
+    np.testing.assert_allclose(got, _sdpa_ref(q, k, v, window), rtol=1e-11, atol=1e-12)
+    got32 = O.attention_prefill(q, k, v, window, "f32")
+    np.testing.assert_allclose(got32, got, rtol=1e-4, atol=1e-5)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((5, 2, 8))
+    k = np.repeat(rng.standard_normal((1, 1, 8)), 5, axis=0)   # all keys equal
+    v = rng.standard_normal((5, 1, 8))
+    o = O.attention_prefill(q, k, v, 0, "f64")
+    np.testing.assert_array_equal(o[0, 0], v[0, 0])           # one key -> exactly V
+    for t in range(5):                                          # equal keys -> mean of V
+        np.testing.assert_allclose(o[t, 1], v[:t + 1, 0].mean(axis=0), rtol=1e-13, atol=1e-14)
+
+
+def test_gqa_head_map_matches_golden_table():
+    rows = _golden_rows("gqa_ratios.txt")
+    for name, nq, nkv in rows:
+        cfg = configs.CONFIGS[name]
+        assert (cfg.n_heads, cfg.n_kv_heads) == (int(nq), int(nkv))
+        g = cfg.n_heads // cfg.n_kv_heads
+        for h in range(cfg.n_heads):
+            assert h * cfg.n_kv_heads // cfg.n_heads == h // g
+    # Qwen2.5: heads 0-6 read kv head 0, 7-13 read kv head 1
+    assert [h * 2 // 14 for h in range(14)] == [0] * 7 + [1] * 7
+    nkv, hd, kvsz = map(int, _golden_rows("kv_row_size.txt")[0])
+    for cfg in (configs.MISTRAL, configs.MIXTRAL):
+        assert (cfg.n_kv_heads, cfg.head_dim, cfg.kv_dim) == (nkv, hd, kvsz)
+
+
+# ---- MoE routing (Pantheon "Mixture of Experts"; rml "Mixture of experts") --
+
+def test_moe_route_brute_force_and_closed_form():
+    rng = np.random.default_rng(4)
+    for trial in range(50):
+        lg = rng.standard_normal(8) * 2
+        ids, w = O.moe_route(lg, 2, "f64")
+        best = max(itertools.combinations(range(8), 2), key=lambda p: (lg[p[0]] + lg[p[1]]))
+        assert set(ids.tolist()) == set(best)
+        assert lg[ids[0]] >= lg[ids[1]]                       # selection order: descending
+        e = np.exp(lg[ids] - lg[ids].max())
+        np.testing.assert_allclose(w, e / e.sum(), rtol=1e-13)  # softmax over the chosen
+        assert abs(w.sum() - 1) < 1e-15
+    ids, w = O.moe_route(lg, 1, "f64")
+    assert w[0] == 1.0 and ids[0] == int(np.argmax(lg))
+    ids, w = O.moe_route(lg, 8, "f64")                        # k = E: the full softmax
+    e = np.exp(lg - lg.max())
+    np.testing.assert_allclose(w, (e / e.sum())[ids], rtol=1e-13)
+    assert sorted(ids.tolist()) == list(range(8))
+
+
+def test_moe_route_ties_go_to_lower_id():
+    ids, w = O.moe_route(np.array([0.0, 1.0, 1.0, 1.0, -1, 0, 0, 1.0]), 2, "f32")
+    assert ids.tolist() == [1, 2] and w[0] == w[1] == np.float32(0.5)
+    ids, _ = O.moe_route(np.zeros(8), 3, "f64")
+    assert ids.tolist() == [0, 1, 2]
+
+
+# ---- whole-model invariants on tiny shapes --------------------------------
+
+def _model(cfg, kind="f32", n_slots=1, **kw):
+    w = synth.make_weights(cfg, seed=0)
+    return O.OracleModel(cfg, w, n_slots=n_slots, kind=kind, **kw), w
+
+
+TINY_SET = [configs.TINY, configs.TINY_MOE, configs.TINY_BIAS, configs.TINY_BF16]
+
+
+@pytest.mark.parametrize("cfg", TINY_SET + [configs.TINY_WINDOW], ids=lambda c: c.name)
+def test_prefill_equals_per_token_forward_bit_exact(cfg):
+    """sipllm "Single-pass prefill": same KV cache and logits as per-token calls."""
+    n = 16 if cfg.sliding_window else 8
+    toks = synth.tokens(0, synth.PROMPT_STREAM, n, cfg.vocab).tolist()
+    a, _ = _model(cfg)
+    b, _ = _model(cfg)
+    ra = a.prefill(toks, rows=list(range(n)), capture=True)
+    for t in range(n):
+        rb = b.decode([toks[t]], [t], capture=True)
+        np.testing.assert_array_equal(ra["logits"][t], rb["logits"][0])
+        np.testing.assert_array_equal(ra["hidden"][:, t], rb["hidden"][:, 0])
+        if cfg.n_experts:
+            np.testing.assert_array_equal(ra["ids"][:, t], rb["ids"][:, 0])
+    for l in range(cfg.n_layers):
+        lo = max(0, n - cfg.max_seq)
+        for p in range(lo, n):
+            for which in (0, 1):
+                np.testing.assert_array_equal(a.kv_row(l, 0, which, p), b.kv_row(l, 0, which, p))
+    assert a.length(0) == b.length(0) == n
+
+
+@pytest.mark.parametrize("cfg", TINY_SET, ids=lambda c: c.name)
+def test_batched_decode_equals_sequential(cfg):
+    """Pantheon "Batched Multi-Sequence Decode": bit-identical to B separate decodes."""
+    B, P = 3, 5
+    pr = synth.prompts(cfg, B, P + 2)
+    bat, _ = _model(cfg, n_slots=B)
+    for b in range(B):
+        bat.prefill(pr[b, :P].tolist(), slot=b)
+    r = bat.decode(pr[:, P].tolist(), [P] * B, capture=True)
+    r2 = bat.decode(pr[:, P + 1].tolist(), [P + 1] * B)
+    for b in range(B):
+        one, _ = _model(cfg)
+        one.prefill(pr[b, :P].tolist())
+        s = one.decode([pr[b, P].item()], [P], capture=True)
+        s2 = one.decode([pr[b, P + 1].item()], [P + 1])
+        np.testing.assert_array_equal(r["logits"][b], s["logits"][0])
+        np.testing.assert_array_equal(r["hidden"][:, b], s["hidden"][:, 0])
+        np.testing.assert_array_equal(r2["logits"][b], s2["logits"][0])
+
+
+def test_causal_mask_future_tokens_do_not_matter():
+    cfg = configs.TINY
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 12, cfg.vocab).tolist()
+    t = 6
+    alt = toks[:t + 1] + [(x + 17) % cfg.vocab for x in toks[t + 1:]]
+    a, _ = _model(cfg)
+    b, _ = _model(cfg)
+    ra = a.prefill(toks, rows=list(range(12)), capture=True)
+    rb = b.prefill(alt, rows=list(range(12)), capture=True)
+    np.testing.assert_array_equal(ra["logits"][:t + 1], rb["logits"][:t + 1])
+    np.testing.assert_array_equal(ra["hidden"][:, :t + 1], rb["hidden"][:, :t + 1])
+    assert not np.array_equal(ra["logits"][t + 1], rb["logits"][t + 1])
+    c, _ = _model(cfg)                              # a prefix prefill is row t of the full one
+    rc = c.prefill(toks[:t + 1])
+    np.testing.assert_array_equal(rc["logits"][0], ra["logits"][t])
+
+
+def test_ring_cache_equals_masked_linear_cache():
+    """Pantheon "Sliding Window": slot pos % W of a W-slot ring, against a linear
+    cache with the [pos-W+1, pos] mask of rml "Attend", W = 5 over 16 positions."""
+    cfg = configs.TINY_WINDOW
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 16, cfg.vocab).tolist()
+    w = synth.make_weights(cfg)
+    ring = O.OracleModel(cfg, w)
+    lin = O.OracleModel(cfg, w, window_by_mask=True, max_seq=16)
+    for t in range(16):
+        a = ring.decode([toks[t]], [t], capture=True)
+        b = lin.decode([toks[t]], [t], capture=True)
+        np.testing.assert_array_equal(a["logits"], b["logits"])
+        np.testing.assert_array_equal(a["hidden"], b["hidden"])
+    full = O.OracleModel(configs.TINY, synth.make_weights(configs.TINY))
+    f = full.prefill(toks, rows=list(range(16)))
+    r2 = O.OracleModel(cfg, w).prefill(toks, rows=list(range(16)))
+    np.testing.assert_array_equal(f["logits"][:5], r2["logits"][:5])   # window not yet binding
+    assert not np.array_equal(f["logits"][5:], r2["logits"][5:])
+
+
+def test_window_at_least_length_is_no_window():
+    cfg = configs.TINY
+    wcfg = cfg.replace(sliding_window=16, max_seq=16)
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 16, cfg.vocab).tolist()
+    w = synth.make_weights(cfg)
+    a = O.OracleModel(cfg, w).prefill(toks, rows=list(range(16)))
+    b = O.OracleModel(wcfg, w).prefill(toks, rows=list(range(16)))
+    np.testing.assert_array_equal(a["logits"], b["logits"])
+
+
+def test_gqa_equals_mha_with_repeated_kv_heads():
+    cfg = configs.TINY                       # 4 q heads over 2 kv heads
+    mha = cfg.replace(n_kv_heads=4)
+    w = synth.make_weights(cfg)
+    wm = {k: v for k, v in w.items() if k != "layers"}
+    wm["layers"] = []
+    hd = cfg.head_dim
+    for lw in w["layers"]:
+        m = dict(lw)
+        for role in ("wk", "wv"):
+            heads = [lw[role][(h * cfg.n_kv_heads // cfg.n_heads) * hd:
+                              (h * cfg.n_kv_heads // cfg.n_heads + 1) * hd] for h in range(4)]
+            m[role] = torch.cat(heads).contiguous()
+        wm["layers"].append(m)
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 9, cfg.vocab).tolist()
+    a = O.OracleModel(cfg, w).prefill(toks, rows=list(range(9)))
+    b = O.OracleModel(mha, wm).prefill(toks, rows=list(range(9)))
+    np.testing.assert_array_equal(a["logits"], b["logits"])
+
+
+def test_moe_with_identical_experts_is_the_dense_ffn():
+    cfg = configs.TINY_MOE
+    dense = configs.TINY
+    wd = synth.make_weights(dense)
+    wm = synth.make_weights(cfg)
+    for lm, ld in zip(wm["layers"], wd["layers"]):
+        for k in ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm"):
+            lm[k] = ld[k]
+        for k in ("w_gate", "w_up", "w_down"):
+            lm[k] = ld[k][None].repeat(cfg.n_experts, 1, 1).contiguous()
+    wm["embed"], wm["out_norm"], wm["lm_head"] = wd["embed"], wd["out_norm"], wd["lm_head"]
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 8, cfg.vocab).tolist()
+    a = O.OracleModel(cfg, wm, kind="f64").prefill(toks, rows=list(range(8)))
+    b = O.OracleModel(dense, wd, kind="f64").prefill(toks, rows=list(range(8)))
+    np.testing.assert_allclose(a["logits"], b["logits"], rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("cfg", TINY_SET + [configs.TINY_WINDOW], ids=lambda c: c.name)
+def test_float64_shadow_bounds_fp32_oracle(cfg):
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 8, cfg.vocab).tolist()
+    a, _ = _model(cfg, "f32")
+    b, _ = _model(cfg, "f64")
+    ra = a.prefill(toks, capture=True)
+    rb = b.prefill(toks, capture=True)
+    for _ in range(8):
+        nxt = a.argmax(ra["logits"][-1])
+        rel = np.linalg.norm(ra["logits"] - rb["logits"]) / np.linalg.norm(rb["logits"])
+        assert rel < 1e-5
+        p = a.length(0)
+        ra = a.decode([nxt], [p], capture=True)
+        rb = b.decode([nxt], [p], capture=True)
+    rel = np.linalg.norm(ra["hidden"] - rb["hidden"]) / np.linalg.norm(rb["hidden"])
+    assert rel < 1e-5
+
+
+@pytest.mark.slow
+def test_float64_shadow_smollm2_prefix():
+    cfg = configs.SMOLLM2
+    w = synth.make_weights(cfg)
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 16, cfg.vocab).tolist()
+    a = O.OracleModel(cfg, w, kind="f32").prefill(toks, capture=True)
+    b = O.OracleModel(cfg, w, kind="f64").prefill(toks, capture=True)
+    rel = np.linalg.norm(a["logits"] - b["logits"]) / np.linalg.norm(b["logits"])
+    assert rel < 1e-5
+    relh = np.linalg.norm(a["hidden"] - b["hidden"]) / np.linalg.norm(b["hidden"])
+    assert relh < 1e-5
+
+
+# ---- checks before any change (rml "One forward pass") --------------------
+
+def test_invalid_calls_change_nothing():
+    cfg = configs.TINY
+    m, _ = _model(cfg, n_slots=2)
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 4, cfg.vocab).tolist()
+    m.prefill(toks)
+    before = [m.kv_row(0, 0, 0, p).copy() for p in range(4)]
+    for bad in (lambda: m.prefill([cfg.vocab], start_pos=4),
+                lambda: m.prefill([1], start_pos=3),             # not the committed length
+                lambda: m.prefill([1] * 13, start_pos=4),        # 4 + 13 > max_seq 16
+                lambda: m.prefill([], start_pos=4),
+                lambda: m.decode([1, 2], [4, 1]),                # slot 1 is at 0
+                lambda: m.decode([-1], [4])):
+        with pytest.raises(O.OracleError):
+            bad()
+    assert m.length(0) == 4 and m.length(1) == 0
+    for p in range(4):
+        np.testing.assert_array_equal(m.kv_row(0, 0, 0, p), before[p])
+    m.reset(0)
+    assert m.length(0) == 0
