@@ -1,0 +1,207 @@
+"""Decode and prefill throughput of the decoder forward on one MI355X.
+
+Workload (default): the Mistral-7B shape (32 layers, d 4096, 32/8 heads of 128,
+ffn 14336, vocab 32000, 4096-slot ring KV cache), bf16 random-init weights from
+the seeded generator, drawn on the GPU.  Setup prefills a 4096-token random
+prompt into each of the 32 sequence slots (each call is one prefill sample);
+then decode runs at batch 32 at positions 4096.. (past the ring's first wrap).
+
+A step is one batched decode call over all layers (embedding to logits) plus
+the greedy choice of the B next tokens (the one device->host copy per step).
+`value` = B * K / (time of K steps).  Prefill tok/s = 4096 / (median prefill
+call).  The roofline objects use live HIP-event timings of each kernel class
+on the library's stream during the timed region.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mistral-7b]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "decode tok/s + prefill tok/s (Mistral-7B shape) and % of HBM / MFMA roofline"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(cfg, wd, steps=4):
+    """The oracle, untuned, on the host cores: greedy decode at B = 1 from an
+    empty cache (positions 0..steps-1) on the same model (weights copied to host)."""
+    import numpy as np
+    from oracle import oracle as O
+    O.build(force=False)
+    w = {k: (v.cpu() if v is not None else None) for k, v in wd.items() if k != "layers"}
+    w["layers"] = [{k: v.cpu() for k, v in lw.items()} for lw in wd["layers"]]
+    ora = O.OracleModel(cfg, w, n_slots=1, max_seq=cfg.max_seq)
+    tok = 1
+    t0 = time.perf_counter()
+    for p in range(steps):
+        r = ora.decode([tok], [p])
+        tok = int(np.argmax(r["logits"][0]))
+    dt = time.perf_counter() - t0
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": steps / dt, "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"{cfg.name} full depth, decode B=1 at positions 0..{steps - 1} "
+                      f"({dt:.1f} s; the context is short, attention is <1% of the per-token work)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=32)
+    ap.add_argument("--warmup", type=int, default=4)
+    ap.add_argument("--config", default="mistral-7b")
+    ap.add_argument("--batch", type=int, default=32)
+    ap.add_argument("--prompt", type=int, default=4096)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=4)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by sequence with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from decoder_only_forward_amd import configs, synth
+    from decoder_only_forward_amd import dec as D
+
+    cfg = configs.CONFIGS[args.config]
+    B, P = args.batch, args.prompt
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    wd = synth.make_weights(cfg, seed=0, device="cuda")
+    torch.cuda.synchronize()
+    log(f"weights {cfg.matrix_params() / 1e9:.2f} B params drawn in {time.perf_counter() - t0:.1f} s")
+    model = D.DecModel(cfg, wd, max_batch=B, max_prefill=P)
+    log(f"workspace {model.workspace.numel() / 2**30:.1f} GiB")
+    prompts = synth.prompts(cfg, B, P)
+
+    # setup: prefill every slot; each call is a prefill sample
+    logits1 = torch.empty(cfg.vocab, device="cuda")
+    model.timing_enable(D.DEC_K_GEMM)
+    model.timing_enable(D.DEC_K_ATTN_PREFILL)
+    pre_ms = []
+    for b in range(B):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        model.prefill(prompts[b].tolist(), seq=b, logits=logits1)
+        torch.cuda.synchronize()
+        pre_ms.append((time.perf_counter() - t) * 1e3)
+        if b == 0:
+            log(f"prefill slot 0: {pre_ms[0]:.1f} ms")
+    gemm_t = model.timing_read(D.DEC_K_GEMM)
+    apre_t = model.timing_read(D.DEC_K_ATTN_PREFILL)
+    model.timing_enable(D.DEC_K_GEMM, False)
+    model.timing_enable(D.DEC_K_ATTN_PREFILL, False)
+    pre_med = float(np.median(pre_ms))
+    log(f"prefill median {pre_med:.1f} ms over {B} calls")
+
+    logits = torch.empty((B, cfg.vocab), device="cuda")
+    nxt = model.greedy(logits1, 1)  # any valid tokens
+    toks = np.full(B, int(nxt[0]), dtype=np.int32)
+
+    def step():
+        pos = np.array([model.length(b) for b in range(B)], dtype=np.int32)
+        model.decode(toks, pos, logits=logits)
+        toks[:] = model.greedy(logits, B)
+
+    for _ in range(args.warmup):
+        step()
+    model.timing_enable(D.DEC_K_GEMV)
+    model.timing_enable(D.DEC_K_ATTN_DECODE)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t
+    gemv_t = model.timing_read(D.DEC_K_GEMV)
+    attn_t = model.timing_read(D.DEC_K_ATTN_DECODE)
+    model.timing_enable(D.DEC_K_GEMV, False)
+    model.timing_enable(D.DEC_K_ATTN_DECODE, False)
+    ms_step = dt * 1e3 / args.steps
+    value = B * args.steps / dt
+    log(f"decode B={B}: {ms_step:.2f} ms/step, {value:.1f} tok/s")
+
+    # smaller batches on the same cache (each row continues its own sequence)
+    extra = {}
+    for bb in (1, 8):
+        if bb >= B:
+            continue
+        lg = torch.empty((bb, cfg.vocab), device="cuda")
+        tk = toks[:bb].copy()
+        for _ in range(2):
+            pos = np.array([model.length(b) for b in range(bb)], dtype=np.int32)
+            model.decode(tk, pos, logits=lg)
+            tk[:] = model.greedy(lg, bb)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        n = max(8, args.steps // 2)
+        for _ in range(n):
+            pos = np.array([model.length(b) for b in range(bb)], dtype=np.int32)
+            model.decode(tk, pos, logits=lg)
+            tk[:] = model.greedy(lg, bb)
+        torch.cuda.synchronize()
+        e = time.perf_counter() - t
+        extra[f"b{bb}"] = {"tok_s": bb * n / e, "ms_per_step": e * 1e3 / n}
+        log(f"decode B={bb}: {e * 1e3 / n:.2f} ms/step")
+
+    def roof(t, bound):
+        if t["launches"] == 0 or t["ms"] <= 0:
+            return None
+        per = t["ms"] / t["launches"]
+        if bound == "hbm":
+            ach = t["bytes"] / t["launches"] / (per * 1e-3) / 1e9
+            return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "avg_launch_us": round(per * 1e3, 2), "launches": t["launches"]}
+        ach = t["flops"] / t["launches"] / (per * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "avg_launch_us": round(per * 1e3, 2), "launches": t["launches"]}
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 weights x fp32 (split-bf16 MFMA), fp32 KV",
+        "data": "synthetic (seeded random-init weights and prompts)",
+        "config": {"workload": f"{cfg.name} decode B={B} at positions {P}.. (ring KV {cfg.max_seq}), "
+                               f"prefill P={P}", "batch": B, "prompt": P, "layers": cfg.n_layers},
+        "prefill_tok_s": round(P / (pre_med * 1e-3), 1),
+        "prefill_ms": round(pre_med, 2),
+        "decode": extra,
+        "roofline": roof(attn_t, "hbm"),
+        "roofline_kernels": {"gemv_decode": roof(gemv_t, "hbm"), "gemm_prefill": roof(gemm_t, "mfma"),
+                             "attn_prefill_fp32": roof(apre_t, "mfma")},
+    }
+    if out["roofline"] is not None:
+        out["roofline"]["kernel"] = "attn_decode_kernel (split-KV GQA decode attention)"
+    if not args.no_cpu_baseline:
+        try:
+            out["cpu_baseline"] = cpu_baseline(cfg, wd, args.cpu_steps)
+        except Exception as e:  # the host may lack memory for the weights
+            out["cpu_baseline"] = {"value": None, "error": str(e)}
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

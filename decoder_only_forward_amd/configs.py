@@ -92,7 +92,7 @@ CONFIGS = {c.name: c for c in (TINY, SMOLLM2, QWEN25, MISTRAL, MIXTRAL)}
 TINY_WINDOW = TINY.replace(name="tiny-window", sliding_window=5, max_seq=5)
 TINY_MOE = TINY.replace(name="tiny-moe", n_experts=8, top_k=2)
 TINY_BIAS = TINY.replace(name="tiny-bias", qkv_bias=True, tied_embedding=True)
-TINY_BF16 = TINY.replace(name="tiny-bf16", weight_dtype=WEIGHT_BF16)
+TINY_BF16 = TINY.replace(name="tiny-bf16", weight_dtype=WEIGHT_BF16, ffn_dim=192)
 
 
 def one_layer(cfg: ModelConfig) -> ModelConfig:

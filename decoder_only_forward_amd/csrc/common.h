@@ -1,0 +1,69 @@
+// Device helpers shared by the gfx950 kernels of the decoder forward.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+#define WAVE 64
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round-to-nearest-even fp32 -> bf16 bits (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): the pair carries about
+// 16 significant bits, so a bf16 MFMA over (hi, lo) against exact bf16 weights
+// keeps the product close to fp32 accuracy.
+__device__ __forceinline__ void split_bf16(float x, uint32_t &hi, uint32_t &lo) {
+    hi = f32_to_bf16_bits(x);
+    lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, WAVE));
+    return v;
+}
+
+// Sum over a block of up to 1024 threads; `red` holds >= 16 floats of LDS.
+// Every thread gets the total.  The order is fixed (lane tree, then waves in
+// order), so the result is deterministic.
+__device__ __forceinline__ float block_sum(float v, float *red) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE, nw = (blockDim.x + WAVE - 1) / WAVE;
+    __syncthreads();
+    if (lane == 0) red[w] = v;
+    __syncthreads();
+    float t = 0.f;
+    for (int i = 0; i < nw; i++) t += red[i];
+    return t;
+}
+
+// Sum of S split partials of one element: p[s*stride + off], s ascending.
+__device__ __forceinline__ float sum_splits(const float *p, int S, size_t stride, size_t off) {
+    float v = p[off];
+    for (int s = 1; s < S; s++) v += p[s * stride + off];
+    return v;
+}
+
+__device__ __forceinline__ float4 sum_splits4(const float *p, int S, size_t stride, size_t off) {
+    float4 v = *reinterpret_cast<const float4 *>(p + off);
+    for (int s = 1; s < S; s++) {
+        float4 t = *reinterpret_cast<const float4 *>(p + s * stride + off);
+        v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
+    }
+    return v;
+}

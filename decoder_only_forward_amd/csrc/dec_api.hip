@@ -1,0 +1,591 @@
+// Host side of the C ABI: validation, the workspace plan, KV bookkeeping and
+// the per-layer launch sequence of prefill and batched decode.
+//
+// Step order of one layer (Pantheon "Llama Forward Pass", section "Forward Pass
+// Flow"; rml "The decoder", section "One forward pass"):
+//   norm -> q|k|v projection (+bias) -> RoPE + K/V store -> attention ->
+//   output projection + residual (+ FFN norm) -> gate|up -> silu*up -> down
+//   (or router -> top-k -> grouped experts) -> residual (+ next norm).
+// The residual add and the next RMSNorm share one kernel; split-K partials of
+// a projection are summed by the kernel that consumes them.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "dec.h"
+#include "kernels.h"
+
+namespace {
+
+struct Timing {
+    bool on = false;
+    std::vector<hipEvent_t> ev;  // pairs
+    size_t used = 0;
+    int64_t launches = 0;
+    double bytes = 0, flops = 0;
+};
+
+struct Plan {  // byte offsets into the workspace
+    size_t kv_layer;        // floats of one layer's K (or V) cache
+    size_t k, v, x, a_hi, a_lo, a_f32, part, q, attn, rope, tok, pos, slot, amax;
+    size_t moe_ids, moe_w, moe_cnt, moe_off, moe_pairs, g_hi, g_lo, g_f32, moe_y;
+    size_t part_floats, act_elems, total;
+    int rows;               // max rows of one pass (max(max_batch, max_prefill))
+};
+
+constexpr int MAX_ATTN_SPLITS = 64;
+
+}  // namespace
+
+struct dec_model {
+    dec_config c;
+    std::vector<dec_layer_weights> L;
+    const void *embed;
+    const float *out_norm;
+    const void *lm_head;
+    hipStream_t st;
+    char *ws;
+    Plan pl;
+    float *kc, *vc, *x, *a_f32, *part, *q, *attn, *moe_w, *g_f32, *moe_y;
+    u16 *a_hi, *a_lo, *g_hi, *g_lo;
+    float2 *rope;
+    int32_t *tok, *pos, *slot, *amax, *moe_ids, *moe_cnt, *moe_off, *moe_pairs;
+    std::vector<int> len;
+    float *cap_hidden = nullptr, *cap_router = nullptr;
+    int32_t *cap_ids = nullptr;
+    Timing tm[DEC_K_COUNT];
+    int wf32;
+    int ring;
+};
+
+namespace {
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int proj_splits(const dec_config &c, int N, int K, int B) {
+    if (c.weight_dtype == DEC_WEIGHT_F32 || B > 64) return 1;
+    return gemv_splits(N, K, B);
+}
+
+bool plan(const dec_config &c, Plan &p) {
+    const size_t d = c.hidden, hd = c.head_dim, qd = (size_t)c.n_heads * hd, kvd = (size_t)c.n_kv_heads * hd;
+    const size_t F = c.ffn_dim, E = c.n_experts, k = c.n_experts ? c.top_k : 0;
+    const int rows = std::max(c.max_batch, c.max_prefill);
+    const size_t prow = (size_t)rows * std::max<size_t>(k, 1);  // rows incl. MoE pairs
+    p.rows = rows;
+    p.kv_layer = (size_t)c.max_batch * c.n_kv_heads * c.max_seq * hd;
+    const size_t kmax = std::max(std::max(d, qd), F);
+    p.act_elems = prow * kmax;
+    // projection outputs: largest (splits x rows x N) over the projections
+    size_t pf = 0;
+    auto need = [&](int N, int K, int T) {
+        const int S = (T <= 64) ? proj_splits(c, N, K, T) : 1;
+        pf = std::max(pf, (size_t)S * T * N);
+    };
+    for (int T : {c.max_batch, std::min(c.max_prefill, 64), c.max_prefill}) {
+        if (T <= 0) continue;
+        need((int)(qd + 2 * kvd), (int)d, T);
+        need((int)d, (int)qd, T);
+        need(c.vocab, (int)d, std::min(T, c.max_batch));
+        if (E) {
+            const int TP = T * (int)k;
+            need((int)E, (int)d, T);
+            const int act = std::min<int>((int)E, TP);
+            // grouped projections: splits sized as for act experts' rows
+            const int Sgu = (T <= 64) ? proj_splits(c, (int)(2 * F) * act, (int)d, T) : 1;
+            const int Sd = (T <= 64) ? proj_splits(c, (int)d * act, (int)F, T) : 1;
+            pf = std::max(pf, (size_t)Sgu * TP * 2 * F);
+            pf = std::max(pf, (size_t)Sd * TP * d);
+        } else {
+            need((int)(2 * F), (int)d, T);
+            need((int)d, (int)F, T);
+        }
+    }
+    p.part_floats = pf;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
+    p.k = take(p.kv_layer * c.n_layers * 4);
+    p.v = take(p.kv_layer * c.n_layers * 4);
+    p.x = take((size_t)rows * d * 4);
+    const bool f32w = c.weight_dtype == DEC_WEIGHT_F32;
+    p.a_hi = take(f32w ? 0 : p.act_elems * 2);
+    p.a_lo = take(f32w ? 0 : p.act_elems * 2);
+    p.a_f32 = take(f32w ? p.act_elems * 4 : 0);
+    p.part = take(pf * 4);
+    p.q = take((size_t)rows * qd * 4);
+    p.attn = take((size_t)c.max_batch * c.n_heads * MAX_ATTN_SPLITS * (hd + 2) * 4);
+    p.rope = take((size_t)rows * (hd / 2) * 8);
+    p.tok = take((size_t)rows * 4);
+    p.pos = take((size_t)rows * 4);
+    p.slot = take((size_t)rows * 4);
+    p.amax = take((size_t)c.max_batch * 4);
+    p.moe_ids = take(prow * 4);
+    p.moe_w = take(prow * 4);
+    p.moe_cnt = take(64 * 4);
+    p.moe_off = take(65 * 4);
+    p.moe_pairs = take(prow * 4);
+    p.g_hi = take(E && !f32w ? prow * d * 2 : 0);
+    p.g_lo = take(E && !f32w ? prow * d * 2 : 0);
+    p.g_f32 = take(E && f32w ? prow * d * 4 : 0);
+    p.moe_y = take(E ? prow * d * 4 : 0);
+    p.total = off;
+    return true;
+}
+
+int validate_cfg(const dec_config *c) {
+    if (!c || c->struct_size != sizeof(dec_config)) return DEC_ERR_INVALID;
+    if (c->n_layers <= 0 || c->hidden <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+        c->ffn_dim <= 0 || c->vocab <= 0 || c->max_seq <= 0 || c->max_batch <= 0 || c->max_prefill <= 0)
+        return DEC_ERR_INVALID;
+    if (c->n_heads % c->n_kv_heads || c->head_dim % 2) return DEC_ERR_INVALID;
+    if (!(c->rms_eps > 0) || !(c->rope_theta > 0)) return DEC_ERR_INVALID;
+    if (c->n_experts < 0 || (c->n_experts > 0 && (c->top_k < 1 || c->top_k > c->n_experts))) return DEC_ERR_INVALID;
+    if (c->sliding_window < 0 || (c->sliding_window > 0 && c->max_seq > c->sliding_window)) return DEC_ERR_INVALID;
+    if (c->weight_dtype != DEC_WEIGHT_BF16 && c->weight_dtype != DEC_WEIGHT_F32) return DEC_ERR_INVALID;
+    if (c->qkv_bias != 0 && c->qkv_bias != 1) return DEC_ERR_INVALID;
+    // shapes the kernels are written for
+    if (c->max_batch > 64) return DEC_ERR_UNSUPPORTED;
+    if (c->head_dim != 16 && c->head_dim != 64 && c->head_dim != 128) return DEC_ERR_UNSUPPORTED;
+    if (c->n_heads / c->n_kv_heads > 8) return DEC_ERR_UNSUPPORTED;
+    if (c->n_experts > 32 || c->top_k > 8) return DEC_ERR_UNSUPPORTED;
+    if (c->hidden % 4 || c->ffn_dim % 4) return DEC_ERR_UNSUPPORTED;
+    if (c->weight_dtype == DEC_WEIGHT_BF16 &&
+        (c->hidden % 64 || (c->n_heads * c->head_dim) % 64 || c->ffn_dim % 64))
+        return DEC_ERR_UNSUPPORTED;
+    return DEC_OK;
+}
+
+// ---- timing --------------------------------------------------------------------
+struct Tick {
+    dec_model *m;
+    int cls;
+    hipEvent_t e1 = nullptr, e2 = nullptr;
+    Tick(dec_model *mm, int c) : m(mm), cls(c) {
+        Timing &t = m->tm[cls];
+        if (!t.on) return;
+        if (t.used + 2 > t.ev.size()) {
+            for (int i = 0; i < 256; i++) {
+                hipEvent_t e;
+                if (hipEventCreate(&e) != hipSuccess) return;
+                t.ev.push_back(e);
+            }
+        }
+        e1 = t.ev[t.used];
+        e2 = t.ev[t.used + 1];
+        t.used += 2;
+        hipEventRecord(e1, m->st);
+    }
+    void done(double bytes, double flops) {
+        if (!e1) return;
+        hipEventRecord(e2, m->st);
+        Timing &t = m->tm[cls];
+        t.launches++;
+        t.bytes += bytes;
+        t.flops += flops;
+    }
+};
+
+// ---- one pass over all layers for T rows ------------------------------------------
+struct Pass {
+    int T;
+    bool decode;        // true: rows are independent sequences (split-KV attention)
+    int start_pos;      // prefill: first position; slot = seq
+    int seq;
+    const int *hpos;    // host positions of the rows (for byte accounting)
+    float *logits;      // destination, or nullptr (no LM head)
+    int logit_row0;     // first row that gets logits
+    int logit_rows;
+    size_t cap_row;     // capture row offset and per-layer row count
+    size_t cap_rows;
+};
+
+Partials proj(dec_model *m, const WSeg *segs, int nseg, int K, int T, const u16 *hi, const u16 *lo,
+              const float *f32, int lda) {
+    int N = 0;
+    for (int i = 0; i < nseg; i++) N += segs[i].rows;
+    const bool gemv = T <= 64;
+    if (m->wf32) {
+        Tick tk(m, gemv ? DEC_K_GEMV : DEC_K_GEMM);
+        launch_gemm_f32(m->st, segs, nseg, K, f32, lda, T, m->part, N);
+        tk.done((double)N * K * 4 + (double)T * K * 4 + (double)T * N * 4, 2.0 * T * N * K);
+        return Partials{m->part, 1, 0, N};
+    }
+    if (gemv) {
+        const int S = gemv_splits(N, K, T);
+        Tick tk(m, DEC_K_GEMV);
+        launch_gemv(m->st, segs, nseg, K, hi, lo, lda, T, m->part, S, (size_t)T * N, N);
+        tk.done((double)N * K * 2 + (double)T * K * 4 + (double)T * N * 4, 2.0 * T * N * K);
+        return Partials{m->part, S, (size_t)T * N, N};
+    }
+    Tick tk(m, DEC_K_GEMM);
+    launch_gemm(m->st, segs, nseg, K, hi, lo, lda, T, m->part, N);
+    tk.done((double)N * K * 2 + (double)T * K * 4 + (double)T * N * 4, 2.0 * T * N * K);
+    return Partials{m->part, 1, 0, N};
+}
+
+// Grouped expert projection over TP = T*k pair rows in expert order.
+Partials proj_grouped(dec_model *m, const WSeg *segs, int nseg, int K, int T, const u16 *hi, const u16 *lo,
+                      const float *f32, int lda) {
+    const dec_config &c = m->c;
+    int N = 0;
+    for (int i = 0; i < nseg; i++) N += segs[i].rows;
+    const int TP = T * c.top_k, E = c.n_experts;
+    const size_t es = (size_t)segs[0].rows * K;
+    const int act = std::min(E, TP);
+    if (m->wf32) {
+        launch_gemm_f32_grouped(m->st, segs, nseg, K, f32, lda, T, E, m->moe_off, es, m->part, N);
+        return Partials{m->part, 1, 0, N};
+    }
+    if (T <= 64) {
+        const int S = gemv_splits(N * act, K, T);
+        Tick tk(m, DEC_K_GEMV);
+        launch_gemv_grouped(m->st, segs, nseg, K, hi, lo, lda, T, E, m->moe_off, es, m->part, S, (size_t)TP * N, N);
+        tk.done((double)N * K * 2 * act + (double)TP * K * 4 + (double)TP * N * 4, 2.0 * TP * N * K);
+        return Partials{m->part, S, (size_t)TP * N, N};
+    }
+    Tick tk(m, DEC_K_GEMM);
+    launch_gemm_grouped(m->st, segs, nseg, K, hi, lo, lda, T, E, m->moe_off, es, m->part, N);
+    tk.done((double)N * K * 2 * act + (double)TP * K * 4 + (double)TP * N * 4, 2.0 * TP * N * K);
+    return Partials{m->part, 1, 0, N};
+}
+
+void run_pass(dec_model *m, const Pass &ps) {
+    const dec_config &c = m->c;
+    const int T = ps.T, d = c.hidden, hd = c.head_dim, nh = c.n_heads, nkv = c.n_kv_heads;
+    const int qd = nh * hd, kvd = nkv * hd, F = c.ffn_dim;
+    const float eps = (float)c.rms_eps;
+    hipStream_t st = m->st;
+    const bool f32w = m->wf32;
+    u16 *ah = f32w ? nullptr : m->a_hi, *al = f32w ? nullptr : m->a_lo;
+    float *af = f32w ? m->a_f32 : nullptr;
+    auto caph = [&](int layer) -> float * {
+        return m->cap_hidden ? m->cap_hidden + ((size_t)layer * ps.cap_rows + ps.cap_row) * d : nullptr;
+    };
+
+    launch_residual_norm(st, RN_EMBED, T, d, m->x, m->tok, m->embed, f32w, Partials{nullptr, 0, 0, 0}, nullptr,
+                         nullptr, 0, m->L[0].attn_norm, eps, ah, al, af, caph(0));
+    launch_rope_table(st, m->pos, T, hd, c.rope_theta, m->rope);
+
+    for (int l = 0; l < c.n_layers; l++) {
+        const dec_layer_weights &w = m->L[l];
+        float *kc = m->kc + (size_t)l * m->pl.kv_layer;
+        float *vc = m->vc + (size_t)l * m->pl.kv_layer;
+        // q | k | v
+        WSeg qkv[3] = {{w.wq, qd}, {w.wk, kvd}, {w.wv, kvd}};
+        Partials pq = proj(m, qkv, 3, d, T, ah, al, af, d);
+        launch_rope_kv(st, T, pq, c.qkv_bias ? w.bq : nullptr, c.qkv_bias ? w.bk : nullptr,
+                       c.qkv_bias ? w.bv : nullptr, m->rope, m->pos, m->slot, nh, nkv, hd, m->q, kc, vc,
+                       c.max_seq, m->ring);
+        // attention -> a (row stride qd)
+        if (ps.decode) {
+            int maxread = 1;
+            double kvbytes = 0;
+            for (int b = 0; b < T; b++) {
+                const int r = std::min(ps.hpos[b] + 1, c.max_seq);
+                maxread = std::max(maxread, r);
+                kvbytes += 2.0 * r * kvd * 4;
+            }
+            const int S = std::min(attn_decode_splits(T, nkv, maxread), MAX_ATTN_SPLITS);
+            Tick tk(m, DEC_K_ATTN_DECODE);
+            launch_attn_decode(st, T, m->q, kc, vc, m->pos, m->slot, nh, nkv, hd, c.max_seq, c.sliding_window, S,
+                               m->attn, ah, al, af);
+            tk.done(kvbytes + 2.0 * T * qd * 4, 0);
+        } else {
+            double flops = 0;
+            for (int t = 0; t < T; t++) flops += 4.0 * hd * nh * (ps.start_pos + t + 1);
+            Tick tk(m, DEC_K_ATTN_PREFILL);
+            launch_attn_prefill(st, T, ps.start_pos, ps.seq, m->q, kc, vc, nh, nkv, hd, c.max_seq,
+                                c.sliding_window, ah, al, af);
+            tk.done((double)(ps.start_pos + T) * kvd * 8 + 2.0 * T * qd * 4, flops);
+        }
+        // output projection, residual, FFN norm
+        WSeg wo[1] = {{w.wo, d}};
+        Partials po = proj(m, wo, 1, qd, T, ah, al, af, qd);
+        launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, po, nullptr, nullptr, 0, w.ffn_norm,
+                             eps, ah, al, af, nullptr);
+        const float *next_gain = (l + 1 < c.n_layers) ? m->L[l + 1].attn_norm : m->out_norm;
+        if (c.n_experts == 0) {
+            WSeg gu[2] = {{w.w_gate, F}, {w.w_up, F}};
+            Partials pg = proj(m, gu, 2, d, T, ah, al, af, d);
+            launch_silu_mul(st, T, F, pg, ah, al, af);
+            WSeg wd[1] = {{w.w_down, d}};
+            Partials pd = proj(m, wd, 1, F, T, ah, al, af, F);
+            launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, pd, nullptr, nullptr, 0, next_gain,
+                                 eps, ah, al, af, caph(l + 1));
+        } else {
+            const int E = c.n_experts, k = c.top_k, TP = T * k;
+            WSeg wr[1] = {{w.router, E}};
+            Partials pr = proj(m, wr, 1, d, T, ah, al, af, d);
+            launch_moe_route(st, T, E, k, pr, m->moe_ids, m->moe_w,
+                             m->cap_router ? m->cap_router + ((size_t)l * ps.cap_rows + ps.cap_row) * E : nullptr,
+                             m->cap_ids ? m->cap_ids + ((size_t)l * ps.cap_rows + ps.cap_row) * k : nullptr,
+                             m->moe_cnt, m->moe_off, m->moe_pairs);
+            launch_moe_gather(st, T, k, d, m->moe_pairs, ah, al, af, f32w ? nullptr : m->g_hi,
+                              f32w ? nullptr : m->g_lo, f32w ? m->g_f32 : nullptr);
+            WSeg gu[2] = {{w.w_gate, F}, {w.w_up, F}};
+            Partials pg = proj_grouped(m, gu, 2, d, T, m->g_hi, m->g_lo, m->g_f32, d);
+            launch_silu_mul(st, TP, F, pg, ah, al, af);
+            WSeg wd[1] = {{w.w_down, d}};
+            Partials pd = proj_grouped(m, wd, 1, F, T, ah, al, af, F);
+            launch_moe_scatter(st, TP, d, m->moe_pairs, pd, m->moe_y);
+            launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, Partials{nullptr, 0, 0, 0}, m->moe_y,
+                                 m->moe_w, k, next_gain, eps, ah, al, af, caph(l + 1));
+        }
+    }
+    // LM head on the rows that need logits (a holds the final-norm rows)
+    if (ps.logits) {
+        const void *head = c.tied_embedding ? m->embed : m->lm_head;
+        WSeg hs[1] = {{head, c.vocab}};
+        const size_t ro = (size_t)ps.logit_row0 * d;
+        Partials pl = proj(m, hs, 1, d, ps.logit_rows, ah ? ah + ro : nullptr, al ? al + ro : nullptr,
+                           af ? af + ro : nullptr, d);
+        launch_reduce_splits(st, pl, ps.logit_rows, c.vocab, ps.logits, c.vocab);
+    }
+}
+
+int check_device(hipError_t e) { return e == hipSuccess ? DEC_OK : DEC_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+size_t dec_workspace_bytes(const dec_config *cfg) {
+    if (validate_cfg(cfg) != DEC_OK) return 0;
+    Plan p;
+    plan(*cfg, p);
+    return p.total;
+}
+
+int dec_create(const dec_config *cfg, const dec_weights *w, void *workspace, size_t ws_bytes, void *hip_stream,
+               dec_handle *out) {
+    if (!out) return DEC_ERR_INVALID;
+    *out = nullptr;
+    int rc = validate_cfg(cfg);
+    if (rc) return rc;
+    if (!w || w->struct_size != sizeof(dec_weights) || !w->embed || !w->out_norm || !w->layers)
+        return DEC_ERR_INVALID;
+    if (!cfg->tied_embedding && !w->lm_head) return DEC_ERR_INVALID;
+    for (int l = 0; l < cfg->n_layers; l++) {
+        const dec_layer_weights &L = w->layers[l];
+        if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.ffn_norm || !L.w_gate || !L.w_up || !L.w_down)
+            return DEC_ERR_INVALID;
+        if (cfg->qkv_bias && (!L.bq || !L.bk || !L.bv)) return DEC_ERR_INVALID;
+        if (cfg->n_experts && !L.router) return DEC_ERR_INVALID;
+    }
+    Plan p;
+    plan(*cfg, p);
+    if (!workspace || ((uintptr_t)workspace & 255)) return DEC_ERR_INVALID;
+    if (ws_bytes < p.total) return DEC_ERR_NOMEM;
+    dec_model *m = new (std::nothrow) dec_model();
+    if (!m) return DEC_ERR_NOMEM;
+    m->c = *cfg;
+    m->L.assign(w->layers, w->layers + cfg->n_layers);
+    m->embed = w->embed;
+    m->out_norm = w->out_norm;
+    m->lm_head = cfg->tied_embedding ? w->embed : w->lm_head;
+    m->st = (hipStream_t)hip_stream;
+    m->ws = (char *)workspace;
+    m->pl = p;
+    char *b = m->ws;
+    m->kc = (float *)(b + p.k);
+    m->vc = (float *)(b + p.v);
+    m->x = (float *)(b + p.x);
+    m->a_hi = (u16 *)(b + p.a_hi);
+    m->a_lo = (u16 *)(b + p.a_lo);
+    m->a_f32 = (float *)(b + p.a_f32);
+    m->part = (float *)(b + p.part);
+    m->q = (float *)(b + p.q);
+    m->attn = (float *)(b + p.attn);
+    m->rope = (float2 *)(b + p.rope);
+    m->tok = (int32_t *)(b + p.tok);
+    m->pos = (int32_t *)(b + p.pos);
+    m->slot = (int32_t *)(b + p.slot);
+    m->amax = (int32_t *)(b + p.amax);
+    m->moe_ids = (int32_t *)(b + p.moe_ids);
+    m->moe_w = (float *)(b + p.moe_w);
+    m->moe_cnt = (int32_t *)(b + p.moe_cnt);
+    m->moe_off = (int32_t *)(b + p.moe_off);
+    m->moe_pairs = (int32_t *)(b + p.moe_pairs);
+    m->g_hi = (u16 *)(b + p.g_hi);
+    m->g_lo = (u16 *)(b + p.g_lo);
+    m->g_f32 = (float *)(b + p.g_f32);
+    m->moe_y = (float *)(b + p.moe_y);
+    m->len.assign(cfg->max_batch, 0);
+    m->wf32 = cfg->weight_dtype == DEC_WEIGHT_F32;
+    m->ring = cfg->sliding_window > 0;
+    *out = m;
+    return DEC_OK;
+}
+
+void dec_destroy(dec_handle h) {
+    if (!h) return;
+    for (auto &t : h->tm)
+        for (hipEvent_t e : t.ev) hipEventDestroy(e);
+    delete h;
+}
+
+int dec_prefill(dec_handle h, int seq, const int32_t *tokens, int n, int start_pos, float *logits) {
+    if (!h || !tokens || !logits) return DEC_ERR_INVALID;
+    const dec_config &c = h->c;
+    if (seq < 0 || seq >= c.max_batch || n <= 0) return DEC_ERR_INVALID;
+    if (n > c.max_prefill) return DEC_ERR_RANGE;
+    for (int i = 0; i < n; i++)
+        if (tokens[i] < 0 || tokens[i] >= c.vocab) return DEC_ERR_INVALID;
+    if (start_pos != h->len[seq]) return DEC_ERR_INVALID;
+    if (!h->ring && (long)start_pos + n > (long)c.max_seq) return DEC_ERR_RANGE;
+    if ((long)start_pos + n > 0x7FFFFFFFL) return DEC_ERR_RANGE;
+
+    if (h->ring && (long)start_pos + n > (long)c.max_seq) {
+        // positions of this call would overwrite ring slots its own earlier
+        // positions still read: run them one at a time (same result as one
+        // pass, sipllm "Single-pass prefill").
+        for (int t = 0; t < n; t++) {
+            RowArgs ra;
+            ra.tok[0] = tokens[t];
+            ra.pos[0] = start_pos + t;
+            ra.slot[0] = seq;
+            launch_set_rows(h->st, ra, 1, h->tok, h->pos, h->slot);
+            Pass ps{};
+            ps.T = 1;
+            ps.decode = true;
+            ps.seq = seq;
+            const int hp = start_pos + t;
+            ps.hpos = &hp;
+            ps.logits = (t == n - 1) ? logits : nullptr;
+            ps.logit_row0 = 0;
+            ps.logit_rows = 1;
+            ps.cap_row = t;
+            ps.cap_rows = n;
+            run_pass(h, ps);
+        }
+    } else {
+        if (hipMemcpyAsync(h->tok, tokens, sizeof(int32_t) * n, hipMemcpyHostToDevice, h->st) != hipSuccess)
+            return DEC_ERR_DEVICE;
+        launch_set_seq_rows(h->st, n, start_pos, seq, h->pos, h->slot);
+        Pass ps{};
+        ps.T = n;
+        ps.decode = false;
+        ps.start_pos = start_pos;
+        ps.seq = seq;
+        ps.hpos = nullptr;
+        ps.logits = logits;
+        ps.logit_row0 = n - 1;
+        ps.logit_rows = 1;
+        ps.cap_row = 0;
+        ps.cap_rows = n;
+        run_pass(h, ps);
+    }
+    if (hipGetLastError() != hipSuccess) return DEC_ERR_DEVICE;
+    h->len[seq] = start_pos + n;
+    return DEC_OK;
+}
+
+int dec_decode(dec_handle h, int B, const int32_t *tokens, const int32_t *pos, float *logits) {
+    if (!h || !tokens || !pos || !logits) return DEC_ERR_INVALID;
+    const dec_config &c = h->c;
+    if (B <= 0 || B > c.max_batch) return DEC_ERR_INVALID;
+    for (int b = 0; b < B; b++) {
+        if (tokens[b] < 0 || tokens[b] >= c.vocab) return DEC_ERR_INVALID;
+        if (pos[b] != h->len[b]) return DEC_ERR_INVALID;
+        if (!h->ring && pos[b] + 1 > c.max_seq) return DEC_ERR_RANGE;
+        if (pos[b] == 0x7FFFFFFF) return DEC_ERR_RANGE;
+    }
+    RowArgs ra;
+    for (int b = 0; b < B; b++) {
+        ra.tok[b] = tokens[b];
+        ra.pos[b] = pos[b];
+        ra.slot[b] = b;
+    }
+    launch_set_rows(h->st, ra, B, h->tok, h->pos, h->slot);
+    Pass ps{};
+    ps.T = B;
+    ps.decode = true;
+    ps.hpos = pos;
+    ps.logits = logits;
+    ps.logit_row0 = 0;
+    ps.logit_rows = B;
+    ps.cap_row = 0;
+    ps.cap_rows = B;
+    run_pass(h, ps);
+    if (hipGetLastError() != hipSuccess) return DEC_ERR_DEVICE;
+    for (int b = 0; b < B; b++) h->len[b] = pos[b] + 1;
+    return DEC_OK;
+}
+
+int dec_kv_reset(dec_handle h, int seq) {
+    if (!h || seq < -1 || seq >= h->c.max_batch) return DEC_ERR_INVALID;
+    for (int s = 0; s < h->c.max_batch; s++)
+        if (seq == -1 || s == seq) h->len[s] = 0;
+    return DEC_OK;
+}
+
+int dec_kv_length(dec_handle h, int seq) {
+    if (!h || seq < 0 || seq >= h->c.max_batch) return DEC_ERR_INVALID;
+    return h->len[seq];
+}
+
+int dec_greedy(dec_handle h, const float *logits, int B, int32_t *tokens_out) {
+    if (!h || !logits || !tokens_out || B <= 0 || B > h->c.max_batch) return DEC_ERR_INVALID;
+    launch_argmax(h->st, logits, B, h->c.vocab, h->amax);
+    if (hipMemcpyAsync(tokens_out, h->amax, sizeof(int32_t) * B, hipMemcpyDeviceToHost, h->st) != hipSuccess)
+        return DEC_ERR_DEVICE;
+    return check_device(hipStreamSynchronize(h->st));
+}
+
+int dec_sync(dec_handle h) {
+    if (!h) return DEC_ERR_INVALID;
+    return check_device(hipStreamSynchronize(h->st));
+}
+
+int dec_set_capture(dec_handle h, float *hidden, int32_t *expert_ids, float *router) {
+    if (!h) return DEC_ERR_INVALID;
+    h->cap_hidden = hidden;
+    h->cap_ids = expert_ids;
+    h->cap_router = router;
+    return DEC_OK;
+}
+
+int dec_timing_enable(dec_handle h, int kernel_class, int on) {
+    if (!h || kernel_class < 0 || kernel_class >= DEC_K_COUNT) return DEC_ERR_INVALID;
+    Timing &t = h->tm[kernel_class];
+    if (hipStreamSynchronize(h->st) != hipSuccess) return DEC_ERR_DEVICE;
+    t.on = on != 0;
+    t.used = 0;
+    t.launches = 0;
+    t.bytes = t.flops = 0;
+    return DEC_OK;
+}
+
+int dec_timing_read(dec_handle h, int kernel_class, double *total_ms, int64_t *launches, double *bytes,
+                    double *flops) {
+    if (!h || kernel_class < 0 || kernel_class >= DEC_K_COUNT) return DEC_ERR_INVALID;
+    Timing &t = h->tm[kernel_class];
+    if (hipStreamSynchronize(h->st) != hipSuccess) return DEC_ERR_DEVICE;
+    double ms = 0;
+    for (size_t i = 0; i + 1 < t.used; i += 2) {
+        float e = 0;
+        if (hipEventElapsedTime(&e, t.ev[i], t.ev[i + 1]) != hipSuccess) return DEC_ERR_DEVICE;
+        ms += e;
+    }
+    if (total_ms) *total_ms = ms;
+    if (launches) *launches = t.launches;
+    if (bytes) *bytes = t.bytes;
+    if (flops) *flops = t.flops;
+    return DEC_OK;
+}
+
+const char *dec_status_str(int s) {
+    switch (s) {
+        case DEC_OK: return "ok";
+        case DEC_ERR_INVALID: return "invalid argument";
+        case DEC_ERR_RANGE: return "out of range";
+        case DEC_ERR_NOMEM: return "workspace too small";
+        case DEC_ERR_DEVICE: return "device error";
+        case DEC_ERR_UNSUPPORTED: return "unsupported shape";
+    }
+    return "unknown status";
+}
+
+}  // extern "C"

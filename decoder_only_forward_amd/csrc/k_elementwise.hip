@@ -1,0 +1,278 @@
+// Row-wise kernels of the forward: residual add + RMSNorm (with the embedding
+// gather as its first-layer form), the RoPE angle table, RoPE fused with the
+// K/V cache store, silu(gate)*up, and the greedy argmax.
+#include "common.h"
+#include "kernels.h"
+
+// ---- residual + RMSNorm ----------------------------------------------------
+// RMSNorm: a = x / sqrt(mean(x^2) + eps) * g  (Pantheon "Llama Forward Pass",
+// section "RMSNorm").  One block per row; each thread keeps its float4 chunks of
+// the row in registers between the sum of squares and the scaling.
+template <int VPT>
+__global__ void __launch_bounds__(256) residual_norm_kernel(
+    int mode, int d, float *__restrict__ x, const int32_t *__restrict__ tok,
+    const void *__restrict__ embed, int embed_f32, Partials add, const float *__restrict__ moe_y,
+    const float *__restrict__ moe_w, int k, const float *__restrict__ gain, float eps,
+    u16 *__restrict__ a_hi, u16 *__restrict__ a_lo, float *__restrict__ a_f32, float *__restrict__ cap) {
+    __shared__ float red[16];
+    const int t = blockIdx.x;
+    const int nv = d / 4;
+    float4 v[VPT];
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < VPT; u++) {
+        const int i4 = threadIdx.x + u * 256;
+        if (i4 >= nv) break;
+        const size_t off = (size_t)t * d + 4 * i4;
+        float4 r;
+        if (mode == RN_EMBED) {
+            const size_t e = (size_t)tok[t] * d + 4 * i4;
+            if (embed_f32) {
+                r = *reinterpret_cast<const float4 *>((const float *)embed + e);
+            } else {
+                const uint2 b = *reinterpret_cast<const uint2 *>((const u16 *)embed + e);
+                r.x = bf16_bits_to_f32(b.x & 0xFFFFu); r.y = bf16_bits_to_f32(b.x >> 16);
+                r.z = bf16_bits_to_f32(b.y & 0xFFFFu); r.w = bf16_bits_to_f32(b.y >> 16);
+            }
+        } else {
+            r = *reinterpret_cast<const float4 *>(x + off);
+            if (add.p) {
+                const float4 a = sum_splits4(add.p, add.S, add.stride, (size_t)t * add.ld + 4 * i4);
+                r.x += a.x; r.y += a.y; r.z += a.z; r.w += a.w;
+            }
+            if (moe_y) {
+                float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int j = 0; j < k; j++) {
+                    const float w = moe_w[t * k + j];
+                    const float4 e = *reinterpret_cast<const float4 *>(moe_y + ((size_t)t * k + j) * d + 4 * i4);
+                    y.x += w * e.x; y.y += w * e.y; y.z += w * e.z; y.w += w * e.w;
+                }
+                r.x += y.x; r.y += y.y; r.z += y.z; r.w += y.w;
+            }
+        }
+        *reinterpret_cast<float4 *>(x + off) = r;
+        if (cap) *reinterpret_cast<float4 *>(cap + off) = r;
+        ss += r.x * r.x + r.y * r.y + r.z * r.z + r.w * r.w;
+        v[u] = r;
+    }
+    const float tot = block_sum(ss, red);
+    if (!gain) return;
+    const float rs = 1.0f / sqrtf(tot / (float)d + eps);
+#pragma unroll
+    for (int u = 0; u < VPT; u++) {
+        const int i4 = threadIdx.x + u * 256;
+        if (i4 >= nv) break;
+        const size_t off = (size_t)t * d + 4 * i4;
+        const float4 g = *reinterpret_cast<const float4 *>(gain + 4 * i4);
+        float4 a;
+        a.x = v[u].x * rs * g.x; a.y = v[u].y * rs * g.y; a.z = v[u].z * rs * g.z; a.w = v[u].w * rs * g.w;
+        if (a_f32) *reinterpret_cast<float4 *>(a_f32 + off) = a;
+        if (a_hi) {
+            uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+            split_bf16(a.x, h0, l0); split_bf16(a.y, h1, l1);
+            split_bf16(a.z, h2, l2); split_bf16(a.w, h3, l3);
+            *reinterpret_cast<uint2 *>(a_hi + off) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+            *reinterpret_cast<uint2 *>(a_lo + off) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+        }
+    }
+}
+
+void launch_residual_norm(hipStream_t st, int mode, int T, int d, float *x, const int32_t *tok,
+                          const void *embed, int embed_f32, Partials add, const float *moe_y,
+                          const float *moe_w, int k, const float *gain, float eps, u16 *a_hi,
+                          u16 *a_lo, float *a_f32, float *cap) {
+    if (T <= 0) return;
+    const int nv = d / 4;
+    const int vpt = (nv + 255) / 256;
+#define RN(V) hipLaunchKernelGGL(residual_norm_kernel<V>, dim3(T), dim3(256), 0, st, mode, d, x, tok, \
+                                 embed, embed_f32, add, moe_y, moe_w, k, gain, eps, a_hi, a_lo, a_f32, cap)
+    if (vpt <= 1) RN(1);
+    else if (vpt <= 2) RN(2);
+    else if (vpt <= 4) RN(4);
+    else RN(8);
+#undef RN
+}
+
+// ---- RoPE ------------------------------------------------------------------
+// Pair i of a head turns theta^(-2i/hd) radians per position (rml "The
+// decoder", section "Rotary embeddings"); the angle and its cos/sin are formed
+// in double once per (position, pair) and shared by every head.
+__global__ void rope_table_kernel(const int32_t *__restrict__ pos, int T, int hd, double theta,
+                                  float2 *__restrict__ tab) {
+    const int half = hd / 2;
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= T * half) return;
+    const int t = idx / half, i = idx % half;
+    const double ang = (double)pos[t] * pow(theta, -2.0 * (double)i / (double)hd);
+    tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
+}
+
+void launch_rope_table(hipStream_t st, const int32_t *pos, int T, int hd, double theta, float2 *tab) {
+    const int n = T * (hd / 2);
+    if (n <= 0) return;
+    hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, pos, T, hd, theta, tab);
+}
+
+// Adjacent pairs (2i, 2i+1) rotate as (e0 c - e1 s, e0 s + e1 c) (sipllm
+// "Transformer forward pass", section "RoPE is adjacent-pair").  K and V go to
+// the cache slot of the position (Pantheon, "Sliding Window (Mistral)": write at
+// pos % max_seq when the cache is a ring).
+__global__ void __launch_bounds__(256) rope_kv_kernel(
+    Partials qkv, const float *__restrict__ bq, const float *__restrict__ bk, const float *__restrict__ bv,
+    const float2 *__restrict__ tab, const int32_t *__restrict__ pos, const int32_t *__restrict__ slot,
+    int nh, int nkv, int hd, float *__restrict__ q_out, float *__restrict__ kc, float *__restrict__ vc,
+    int max_seq, int ring) {
+    const int t = blockIdx.x;
+    const int qd = nh * hd, kvd = nkv * hd;
+    const int npairs = (qd + 2 * kvd) / 2;
+    const int p = pos[t];
+    const int s = ring ? p % max_seq : p;
+    const size_t slot_base = (size_t)slot[t] * nkv;
+    for (int pi = threadIdx.x; pi < npairs; pi += blockDim.x) {
+        const int col = 2 * pi;
+        const size_t off = (size_t)t * qkv.ld + col;
+        const float2 e = *reinterpret_cast<const float2 *>(qkv.p + off);
+        float e0 = e.x, e1 = e.y;
+        for (int sp = 1; sp < qkv.S; sp++) {
+            const float2 u = *reinterpret_cast<const float2 *>(qkv.p + sp * qkv.stride + off);
+            e0 += u.x; e1 += u.y;
+        }
+        if (col < qd) {
+            if (bq) { e0 += bq[col]; e1 += bq[col + 1]; }
+            const float2 cs = tab[(size_t)t * (hd / 2) + (col % hd) / 2];
+            *reinterpret_cast<float2 *>(q_out + (size_t)t * qd + col) =
+                make_float2(e0 * cs.x - e1 * cs.y, e0 * cs.y + e1 * cs.x);
+        } else if (col < qd + kvd) {
+            const int c = col - qd;
+            if (bk) { e0 += bk[c]; e1 += bk[c + 1]; }
+            const float2 cs = tab[(size_t)t * (hd / 2) + (c % hd) / 2];
+            const size_t dst = ((slot_base + c / hd) * max_seq + s) * hd + c % hd;
+            *reinterpret_cast<float2 *>(kc + dst) = make_float2(e0 * cs.x - e1 * cs.y, e0 * cs.y + e1 * cs.x);
+        } else {
+            const int c = col - qd - kvd;
+            if (bv) { e0 += bv[c]; e1 += bv[c + 1]; }
+            const size_t dst = ((slot_base + c / hd) * max_seq + s) * hd + c % hd;
+            *reinterpret_cast<float2 *>(vc + dst) = make_float2(e0, e1);
+        }
+    }
+}
+
+void launch_rope_kv(hipStream_t st, int T, Partials qkv, const float *bq, const float *bk,
+                    const float *bv, const float2 *tab, const int32_t *pos, const int32_t *slot,
+                    int nh, int nkv, int hd, float *q_out, float *kc, float *vc, int max_seq, int ring) {
+    if (T <= 0) return;
+    hipLaunchKernelGGL(rope_kv_kernel, dim3(T), dim3(256), 0, st, qkv, bq, bk, bv, tab, pos, slot, nh,
+                       nkv, hd, q_out, kc, vc, max_seq, ring);
+}
+
+// ---- SwiGLU activation -----------------------------------------------------
+// act = silu(gate) * up, silu(z) = z / (1 + e^-z)  (Pantheon, "SwiGLU FFN").
+__global__ void __launch_bounds__(256) silu_mul_kernel(int F, Partials gu, u16 *__restrict__ hi,
+                                                        u16 *__restrict__ lo, float *__restrict__ f32) {
+    const int t = blockIdx.y;
+    const int j4 = blockIdx.x * blockDim.x + threadIdx.x;
+    if (4 * j4 >= F) return;
+    const size_t off = (size_t)t * gu.ld + 4 * j4;
+    const float4 g = sum_splits4(gu.p, gu.S, gu.stride, off);
+    const float4 u = sum_splits4(gu.p, gu.S, gu.stride, off + F);
+    float4 a;
+    a.x = g.x / (1.0f + expf(-g.x)) * u.x;
+    a.y = g.y / (1.0f + expf(-g.y)) * u.y;
+    a.z = g.z / (1.0f + expf(-g.z)) * u.z;
+    a.w = g.w / (1.0f + expf(-g.w)) * u.w;
+    const size_t o = (size_t)t * F + 4 * j4;
+    if (f32) *reinterpret_cast<float4 *>(f32 + o) = a;
+    if (hi) {
+        uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+        split_bf16(a.x, h0, l0); split_bf16(a.y, h1, l1);
+        split_bf16(a.z, h2, l2); split_bf16(a.w, h3, l3);
+        *reinterpret_cast<uint2 *>(hi + o) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        *reinterpret_cast<uint2 *>(lo + o) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+    }
+}
+
+void launch_silu_mul(hipStream_t st, int T, int F, Partials gu, u16 *hi, u16 *lo, float *f32) {
+    if (T <= 0) return;
+    const int n4 = F / 4;
+    hipLaunchKernelGGL(silu_mul_kernel, dim3((n4 + 255) / 256, T), dim3(256), 0, st, F, gu, hi, lo, f32);
+}
+
+// ---- greedy ------------------------------------------------------------------
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+    return v > bv || (v == bv && i < bi);
+}
+
+__global__ void __launch_bounds__(1024) argmax_kernel(const float *__restrict__ logits, int V,
+                                                      int32_t *__restrict__ out) {
+    __shared__ float sv[16];
+    __shared__ int si[16];
+    const int b = blockIdx.x;
+    const float *row = logits + (size_t)b * V;
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int i = threadIdx.x; i < V; i += blockDim.x) {
+        const float v = row[i];
+        if (better(v, i, bv, bi)) { bv = v; bi = i; }
+    }
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, WAVE);
+        const int oi = __shfl_xor(bi, o, WAVE);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    const int lane = threadIdx.x % WAVE, w = threadIdx.x / WAVE;
+    if (lane == 0) { sv[w] = bv; si[w] = bi; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int i = 1; i < (int)(blockDim.x / WAVE); i++)
+            if (better(sv[i], si[i], bv, bi)) { bv = sv[i]; bi = si[i]; }
+        out[b] = bi == 0x7FFFFFFF ? 0 : bi;
+    }
+}
+
+void launch_argmax(hipStream_t st, const float *logits, int B, int V, int32_t *out) {
+    if (B <= 0) return;
+    hipLaunchKernelGGL(argmax_kernel, dim3(B), dim3(1024), 0, st, logits, V, out);
+}
+
+// ---- small helpers -------------------------------------------------------------
+// dst[t][n] = sum over splits of a GEMV output (used where no consumer kernel
+// folds the sum in, e.g. the LM head writing the caller's logits).
+__global__ void __launch_bounds__(256) reduce_splits_kernel(Partials src, int N, float *__restrict__ dst, int ldd) {
+    const int t = blockIdx.y;
+    const int n = blockIdx.x * blockDim.x + threadIdx.x;
+    if (n >= N) return;
+    dst[(size_t)t * ldd + n] = sum_splits(src.p, src.S, src.stride, (size_t)t * src.ld + n);
+}
+
+void launch_reduce_splits(hipStream_t st, Partials src, int T, int N, float *dst, int ldd) {
+    if (T <= 0) return;
+    hipLaunchKernelGGL(reduce_splits_kernel, dim3((N + 255) / 256, T), dim3(256), 0, st, src, N, dst, ldd);
+}
+
+// Decode rows travel as a kernel argument (no host buffer has to outlive the
+// call): tok/pos of row b, slot b.
+__global__ void set_rows_kernel(RowArgs a, int B, int32_t *__restrict__ tok, int32_t *__restrict__ pos,
+                                int32_t *__restrict__ slot) {
+    const int b = threadIdx.x;
+    if (b >= B) return;
+    tok[b] = a.tok[b];
+    pos[b] = a.pos[b];
+    slot[b] = a.slot[b];
+}
+
+void launch_set_rows(hipStream_t st, const RowArgs &a, int B, int32_t *tok, int32_t *pos, int32_t *slot) {
+    hipLaunchKernelGGL(set_rows_kernel, dim3(1), dim3(64), 0, st, a, B, tok, pos, slot);
+}
+
+// Prefill rows: positions start..start+T-1 of one slot.
+__global__ void set_seq_rows_kernel(int T, int start, int s, int32_t *__restrict__ pos, int32_t *__restrict__ slot) {
+    const int t = blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= T) return;
+    pos[t] = start + t;
+    slot[t] = s;
+}
+
+void launch_set_seq_rows(hipStream_t st, int T, int start, int s, int32_t *pos, int32_t *slot) {
+    if (T <= 0) return;
+    hipLaunchKernelGGL(set_seq_rows_kernel, dim3((T + 255) / 256), dim3(256), 0, st, T, start, s, pos, slot);
+}

@@ -1,0 +1,260 @@
+// Decode projections: out[b][n] = sum_k W[n][k] * a[b][k] for B <= 64 rows.
+//
+// The weight matrix is read exactly once per step, straight from HBM into
+// registers with 16-byte loads, and is the A operand of bf16 MFMAs
+// (16x16x32).  Activations are fp32 in the forward; they enter the MFMA as the
+// pair (hi, lo) of bf16 values whose sum carries ~16 bits, as two columns of the
+// B operand, so the product keeps near-fp32 accuracy while the weights stay
+// exact.  The reduction order over k is free, so each lane loads a contiguous
+// run of 8*J bf16 per row and the B operand follows the same permutation.
+//
+// Block = 4 waves, 128 weight rows (each wave 2 row tiles of 16); the B rows of
+// activations (hi and lo) for a chunk of k sit in LDS, shared by the 4 waves.
+// Grid = (row tiles, k splits[, experts]); split partials are summed by the
+// consumer kernel in a fixed order (no atomics).
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+struct GemvParams {
+    const u16 *w[MAX_SEGS];
+    int seg_end[MAX_SEGS];
+    int nseg;
+    int N, K;
+    const u16 *a_hi, *a_lo;
+    int lda, B;
+    float *out;
+    size_t split_stride;
+    int ldo;
+    int kps;   // k per split (multiple of 32*J)
+    int kc;    // k per LDS chunk (multiple of 32*J)
+    // Grouped experts: expert e = blockIdx.z owns activation rows
+    // [grp_off[e], grp_off[e+1]) and weight slice e (w + e*expert_stride).
+    const int32_t *grp_off;
+    size_t expert_stride;
+};
+
+constexpr int ROWS_PER_BLOCK = 128;
+
+template <int NT, int J>
+__global__ void __launch_bounds__(256) gemv_kernel(GemvParams p) {
+    extern __shared__ uint4 lds[];   // [kc/8][16*NT] chunks of 8 bf16
+    constexpr int NCOL = 16 * NT;
+    const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
+    const int r = lane & 15, c = lane >> 4;
+
+    int B = p.B, arow0 = 0, orow0 = 0;
+    size_t wofs = 0;
+    if (p.grp_off) {
+        const int e = blockIdx.z;
+        arow0 = p.grp_off[e];
+        B = p.grp_off[e + 1] - arow0;
+        if (B <= 0) return;
+        orow0 = arow0;
+        wofs = (size_t)e * p.expert_stride;
+    }
+
+    // weight rows of this lane (clamped; stores are masked)
+    const u16 *wrow[2];
+    int nrow[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; rt++) {
+        const int n = blockIdx.x * ROWS_PER_BLOCK + wv * 32 + rt * 16 + r;
+        const int nn = n < p.N ? n : p.N - 1;
+        int s = 0, start = 0;
+        while (s < p.nseg - 1 && nn >= p.seg_end[s]) { start = p.seg_end[s]; s++; }
+        wrow[rt] = p.w[s] + wofs + (size_t)(nn - start) * p.K;
+        nrow[rt] = n;
+    }
+
+    const int kbeg = blockIdx.y * p.kps;
+    const int kend = min(p.K, kbeg + p.kps);
+    floatx4 acc[2][NT];
+#pragma unroll
+    for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+        for (int t = 0; t < NT; t++) acc[rt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    if (kbeg < kend) {
+        const int nsteps = (kend - kbeg) / (32 * J);
+        uint4 a[2][J], an[2][J];
+#pragma unroll
+        for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+            for (int j = 0; j < J; j++)
+                a[rt][j] = *reinterpret_cast<const uint4 *>(wrow[rt] + kbeg + c * 8 * J + j * 8);
+
+        int chunk0 = kbeg;
+        for (int st = 0; st < nsteps; st++) {
+            const int k0 = kbeg + st * 32 * J;
+            if (((k0 - kbeg) % p.kc) == 0) {
+                chunk0 = k0;
+                const int kcl = min(p.kc, kend - k0);
+                const int c8 = kcl / 8;
+                __syncthreads();
+                for (int i = threadIdx.x; i < NCOL * c8; i += blockDim.x) {
+                    const int col = i / c8, ch = i % c8;
+                    const int t = col / 16, m = col % 16;
+                    const int b = t * 8 + (m & 7);
+                    uint4 v = make_uint4(0, 0, 0, 0);
+                    if (b < B) {
+                        const u16 *src = (m < 8 ? p.a_hi : p.a_lo) + (size_t)(arow0 + b) * p.lda + k0 + ch * 8;
+                        v = *reinterpret_cast<const uint4 *>(src);
+                    }
+                    lds[ch * NCOL + col] = v;
+                }
+                __syncthreads();
+            }
+            if (st + 1 < nsteps) {
+                const int kn = k0 + 32 * J;
+#pragma unroll
+                for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+                    for (int j = 0; j < J; j++)
+                        an[rt][j] = *reinterpret_cast<const uint4 *>(wrow[rt] + kn + c * 8 * J + j * 8);
+            }
+            const int ch0 = (k0 - chunk0) / 8 + c * J;
+#pragma unroll
+            for (int j = 0; j < J; j++) {
+#pragma unroll
+                for (int t = 0; t < NT; t++) {
+                    const uint4 bv = lds[(ch0 + j) * NCOL + t * 16 + r];
+                    const bf16x8 bop = __builtin_bit_cast(bf16x8, bv);
+#pragma unroll
+                    for (int rt = 0; rt < 2; rt++)
+                        acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, a[rt][j]), bop, acc[rt][t], 0, 0, 0);
+                }
+            }
+#pragma unroll
+            for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+                for (int j = 0; j < J; j++) a[rt][j] = an[rt][j];
+        }
+    }
+
+    // lane (r, c) holds rows 4c..4c+3 of each row tile for column r; column r
+    // (hi) and r+8 (lo) of the same batch row are summed.
+    float *out = p.out + (size_t)blockIdx.y * p.split_stride;
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+#pragma unroll
+        for (int rt = 0; rt < 2; rt++) {
+            floatx4 v = acc[rt][t];
+            floatx4 o;
+            o[0] = __shfl_xor(v[0], 8, WAVE);
+            o[1] = __shfl_xor(v[1], 8, WAVE);
+            o[2] = __shfl_xor(v[2], 8, WAVE);
+            o[3] = __shfl_xor(v[3], 8, WAVE);
+            const int b = t * 8 + (r & 7);
+            if (r < 8 && b < B) {
+                const int n0 = blockIdx.x * ROWS_PER_BLOCK + wv * 32 + rt * 16 + 4 * c;
+                float *dst = out + (size_t)(orow0 + b) * p.ldo + n0;
+                const float4 s = make_float4(v[0] + o[0], v[1] + o[1], v[2] + o[2], v[3] + o[3]);
+                if (n0 + 3 < p.N) {
+                    *reinterpret_cast<float4 *>(dst) = s;
+                } else {
+                    if (n0 < p.N) dst[0] = s.x;
+                    if (n0 + 1 < p.N) dst[1] = s.y;
+                    if (n0 + 2 < p.N) dst[2] = s.z;
+                }
+            }
+        }
+    }
+}
+
+template <int NT>
+void launch_nt(hipStream_t st, int J, const GemvParams &p, dim3 grid) {
+    const size_t lds = (size_t)(p.kc / 8) * 16 * NT * sizeof(uint4);
+    if (J == 4) hipLaunchKernelGGL((gemv_kernel<NT, 4>), grid, dim3(256), lds, st, p);
+    else if (J == 2) hipLaunchKernelGGL((gemv_kernel<NT, 2>), grid, dim3(256), lds, st, p);
+    else hipLaunchKernelGGL((gemv_kernel<NT, 1>), grid, dim3(256), lds, st, p);
+}
+
+int pick_j(int K) { return K % 128 == 0 ? 4 : (K % 64 == 0 ? 2 : 1); }
+
+void launch_common(hipStream_t st, GemvParams &p, int ksplit, int B_for_tiles, int E) {
+    const int J = pick_j(p.K);
+    const int g = 32 * J;
+    // exactly `ksplit` splits (the consumer sums that many); kps*ksplit >= K and
+    // a trailing split whose range is empty writes zeros.
+    int kps = (p.K + ksplit - 1) / ksplit;
+    kps = (kps + g - 1) / g * g;
+    const int NT = (B_for_tiles + 7) / 8;
+    int kc = 1024 / (NT <= 1 ? 1 : NT <= 2 ? 2 : NT <= 4 ? 4 : 8);
+    kc = kc / g * g;
+    if (kc < g) kc = g;
+    p.kps = kps;
+    p.kc = kc;
+    dim3 grid((p.N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK, ksplit, E);
+    if (NT <= 1) launch_nt<1>(st, J, p, grid);
+    else if (NT <= 2) launch_nt<2>(st, J, p, grid);
+    else if (NT <= 4) launch_nt<4>(st, J, p, grid);
+    else launch_nt<8>(st, J, p, grid);
+}
+
+}  // namespace
+
+int gemv_splits(int N, int K, int B) {
+    (void)B;
+    const int tiles = (N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
+    const int target = 1024;  // ~4 blocks per CU on 256 CUs
+    int s = (target + tiles - 1) / tiles;
+    const int maxs = K / 256 > 0 ? K / 256 : 1;
+    if (s > maxs) s = maxs;
+    if (s < 1) s = 1;
+    const int g = 32 * pick_j(K);
+    int kps = (K + s - 1) / s;
+    kps = (kps + g - 1) / g * g;
+    return (K + kps - 1) / kps;
+}
+
+void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi, const u16 *a_lo,
+                 int lda, int B, float *out, int ksplit, size_t split_stride, int ldo) {
+    GemvParams p{};
+    int end = 0;
+    for (int s = 0; s < nseg; s++) {
+        p.w[s] = (const u16 *)segs[s].w;
+        end += segs[s].rows;
+        p.seg_end[s] = end;
+    }
+    p.nseg = nseg;
+    p.N = end;
+    p.K = K;
+    p.a_hi = a_hi;
+    p.a_lo = a_lo;
+    p.lda = lda;
+    p.B = B;
+    p.out = out;
+    p.split_stride = split_stride;
+    p.ldo = ldo;
+    p.grp_off = nullptr;
+    launch_common(st, p, ksplit, B, 1);
+}
+
+// Grouped-expert form used by the MoE decode path (see k_moe.hip).
+void launch_gemv_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi,
+                         const u16 *a_lo, int lda, int max_rows, int E, const int32_t *offsets,
+                         size_t expert_stride, float *out, int ksplit, size_t split_stride, int ldo) {
+    GemvParams p{};
+    int end = 0;
+    for (int s = 0; s < nseg; s++) {
+        p.w[s] = (const u16 *)segs[s].w;
+        end += segs[s].rows;
+        p.seg_end[s] = end;
+    }
+    p.nseg = nseg;
+    p.N = end;
+    p.K = K;
+    p.a_hi = a_hi;
+    p.a_lo = a_lo;
+    p.lda = lda;
+    p.B = max_rows;
+    p.out = out;
+    p.split_stride = split_stride;
+    p.ldo = ldo;
+    p.grp_off = offsets;
+    p.expert_stride = expert_stride;
+    launch_common(st, p, ksplit, max_rows, E);
+}

@@ -1,0 +1,116 @@
+// Host-side launch interface of the gfx950 kernels (internal to libdec).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+typedef uint16_t u16;
+
+// A GEMM/GEMV output that may be split along K: the value of (row t, col) is
+// the sum over s ascending of p[s*stride + t*ld + col].
+struct Partials {
+    const float *p;
+    int S;
+    size_t stride;
+    int ld;
+};
+
+// One weight matrix [rows][K] of a column-concatenated projection (q|k|v, gate|up).
+struct WSeg {
+    const void *w;
+    int rows;
+};
+#define MAX_SEGS 3
+
+// Residual update + RMSNorm of one row per block:
+//   mode EMBED:  x = widen(E[tok[t]])
+//   otherwise:   x += sum of `add` splits (if any) + sum_j moe_w[t][j]*moe_y[t][j] (if any)
+// then a = x / sqrt(mean(x^2)+eps) * gain written as bf16 (hi, lo) and/or fp32.
+enum { RN_EMBED = 0, RN_ADD = 1 };
+void launch_residual_norm(hipStream_t st, int mode, int T, int d, float *x, const int32_t *tok,
+                          const void *embed, int embed_f32, Partials add, const float *moe_y,
+                          const float *moe_w, int k, const float *gain, float eps, u16 *a_hi,
+                          u16 *a_lo, float *a_f32, float *cap);
+
+// cos/sin of pos[t] * theta^(-2i/hd) for pair i, formed in double: tab[t][i].
+void launch_rope_table(hipStream_t st, const int32_t *pos, int T, int hd, double theta, float2 *tab);
+
+// q/k/v (+bias) -> RoPE on q and k -> q_out [T][q_dim]; k, v stored in the
+// layer's cache [slot][kvh][max_seq][hd] at position pos % max_seq (ring) or pos.
+void launch_rope_kv(hipStream_t st, int T, Partials qkv, const float *bq, const float *bk,
+                    const float *bv, const float2 *tab, const int32_t *pos, const int32_t *slot,
+                    int nh, int nkv, int hd, float *q_out, float *kc, float *vc, int max_seq, int ring);
+
+// act[t][j] = silu(g) * u with g = gu(t, j), u = gu(t, F + j); written as bf16
+// (hi, lo) and/or fp32 with row stride F.
+void launch_silu_mul(hipStream_t st, int T, int F, Partials gu, u16 *hi, u16 *lo, float *f32);
+
+// out[b] = argmax_v logits[b][v], lowest v on ties.
+void launch_argmax(hipStream_t st, const float *logits, int B, int V, int32_t *out);
+
+// Decode projection, bf16 weights: out[s][b][n] = sum over split s's K range of
+// W[n][k] * (a_hi[b][k] + a_lo[b][k]); 1 <= B <= 64.  Returns the split count used.
+int gemv_splits(int N, int K, int B);
+void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi, const u16 *a_lo,
+                 int lda, int B, float *out, int ksplit, size_t split_stride, int ldo);
+
+// Prefill projection, bf16 weights, MFMA: out[m][n] = sum_k (a_hi+a_lo)[m][k] W[n][k].
+void launch_gemm(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi, const u16 *a_lo,
+                 int lda, int M, float *out, int ldo);
+
+// fp32-weight projection (any M): out[m][n] = sum_k a[m][k] W[n][k].
+void launch_gemm_f32(hipStream_t st, const WSeg *segs, int nseg, int K, const float *a, int lda,
+                     int M, float *out, int ldo);
+
+// Split-KV decode attention.  Row b: query q[b][nh*hd], slot slot[b], position
+// pos[b]; keys/values of positions [lo, pos] in the layer cache.  Writes the
+// attention output as bf16 (hi, lo) and/or fp32 rows [B][nh*hd].
+int attn_decode_splits(int B, int nkv, int readable);
+void launch_attn_decode(hipStream_t st, int B, const float *q, const float *kc, const float *vc,
+                        const int32_t *pos, const int32_t *slot, int nh, int nkv, int hd,
+                        int max_seq, int window, int splits, float *part, u16 *o_hi, u16 *o_lo,
+                        float *o_f32);
+
+// Causal prefill attention for T rows of one sequence at positions
+// start_pos..start_pos+T-1, reading keys/values from the layer cache (the
+// chunk's own K/V already stored there).
+void launch_attn_prefill(hipStream_t st, int T, int start_pos, int slot, const float *q,
+                         const float *kc, const float *vc, int nh, int nkv, int hd, int max_seq,
+                         int window, u16 *o_hi, u16 *o_lo, float *o_f32);
+
+// MoE.  Router logits [T][E] (a GEMV/GEMM output) -> softmax, top-k by repeated
+// selection (ties to the lower id), renormalised weights; then the (token, slot)
+// pairs are grouped by expert (counting sort, stable in (token, slot) order).
+void launch_moe_route(hipStream_t st, int T, int E, int k, Partials logits, int32_t *ids,
+                      float *w, float *router_cap, int32_t *ids_cap, int32_t *counts,
+                      int32_t *offsets, int32_t *pairs);
+// Gather the normalised rows of the grouped pairs: dst[i] = src[pairs[i] / k].
+void launch_moe_gather(hipStream_t st, int T, int k, int d, const int32_t *pairs, const u16 *src_hi,
+                       const u16 *src_lo, const float *src_f32, u16 *dst_hi, u16 *dst_lo, float *dst_f32);
+// Grouped expert projections: expert e (grid z) multiplies rows
+// [offsets[e], offsets[e+1]) of `a` by its slice (segs[i].w + e*expert_stride)
+// of the stacked weights [E][rows][K]; out rows follow the grouped order.
+// max_rows bounds any expert's row count (a token picks an expert at most once).
+void launch_gemv_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi,
+                         const u16 *a_lo, int lda, int max_rows, int E, const int32_t *offsets,
+                         size_t expert_stride, float *out, int ksplit, size_t split_stride, int ldo);
+void launch_gemm_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi,
+                         const u16 *a_lo, int lda, int max_rows, int E, const int32_t *offsets,
+                         size_t expert_stride, float *out, int ldo);
+void launch_gemm_f32_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, const float *a, int lda,
+                             int max_rows, int E, const int32_t *offsets, size_t expert_stride, float *out,
+                             int ldo);
+// Scatter grouped expert outputs back to (token, slot) order: y[pairs[i]] = src[i].
+void launch_moe_scatter(hipStream_t st, int n_pairs, int d, const int32_t *pairs, Partials src, float *y);
+
+// Sum of GEMV split partials into a plain row-major destination.
+void launch_reduce_splits(hipStream_t st, Partials src, int T, int N, float *dst, int ldd);
+
+// Up to 64 decode rows passed by value to a setup kernel.
+struct RowArgs {
+    int32_t tok[64];
+    int32_t pos[64];
+    int32_t slot[64];
+};
+void launch_set_rows(hipStream_t st, const RowArgs &a, int B, int32_t *tok, int32_t *pos, int32_t *slot);
+void launch_set_seq_rows(hipStream_t st, int T, int start, int s, int32_t *pos, int32_t *slot);

@@ -1,0 +1,96 @@
+"""Helpers shared by the GPU parity tests: one seeded model on both sides, and
+the tolerance checks of the forward (rel L2 <= 1e-3 and max |diff| <= 2e-2 on
+logits; rel L2 <= 1e-3 per layer on hidden states; greedy tokens and expert
+ids exact wherever the oracle's margin exceeds 1e-3)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from decoder_only_forward_amd import synth
+from oracle import oracle as O
+
+LOGIT_REL_L2 = 1e-3
+LOGIT_MAX_ABS = 2e-2
+HIDDEN_REL_L2 = 1e-3
+MARGIN = 1e-3
+
+
+def to_device(w: dict) -> dict:
+    out = {k: (v.cuda() if isinstance(v, torch.Tensor) else None) for k, v in w.items() if k != "layers"}
+    out["layers"] = [{k: v.cuda() for k, v in lw.items()} for lw in w["layers"]]
+    return out
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
+
+
+def check_logits(gpu, ref, what=""):
+    g = np.asarray(gpu, dtype=np.float64)
+    r = np.asarray(ref, dtype=np.float64)
+    rl = rel_l2(g, r)
+    mx = float(np.max(np.abs(g - r)))
+    assert rl <= LOGIT_REL_L2 and mx <= LOGIT_MAX_ABS, f"{what}: logits rel L2 {rl:.3e}, max |diff| {mx:.3e}"
+    return rl, mx
+
+
+def check_argmax(gpu_row, ref_row, what=""):
+    r = np.asarray(ref_row, dtype=np.float64)
+    top = np.argsort(-r, kind="stable")[:2]
+    margin = r[top[0]] - r[top[1]]
+    g = int(np.argmax(np.asarray(gpu_row)))
+    if margin > MARGIN:
+        assert g == int(top[0]), f"{what}: argmax {g} != {int(top[0])} (margin {margin:.2e})"
+    else:  # a legitimate tie: the GPU token must be one of the near-best
+        assert r[top[0]] - r[g] <= MARGIN, f"{what}: argmax {g} not within margin"
+
+
+def check_hidden(gpu, ref, what=""):
+    for l in range(ref.shape[0]):
+        rl = rel_l2(gpu[l], ref[l])
+        assert rl <= HIDDEN_REL_L2, f"{what}: hidden after layer {l - 1} rel L2 {rl:.3e}"
+
+
+def check_experts(gpu_ids, ref_ids, ref_router, k, what=""):
+    """Expert ids must match exactly where the k-th / (k+1)-th router-logit
+    margin exceeds 1e-3; elsewhere the GPU's set must be a valid top-k."""
+    L, n, _ = ref_ids.shape
+    for l in range(L):
+        for t in range(n):
+            lg = np.asarray(ref_router[l, t], dtype=np.float64)
+            order = np.argsort(-lg, kind="stable")
+            if k < lg.size:
+                margin = lg[order[k - 1]] - lg[order[k]]
+            else:
+                margin = np.inf
+            if margin > MARGIN:
+                assert sorted(gpu_ids[l, t].tolist()) == sorted(ref_ids[l, t].tolist()), \
+                    f"{what}: layer {l} row {t} experts {gpu_ids[l, t]} != {ref_ids[l, t]}"
+            else:
+                kth = lg[order[k - 1]]
+                assert all(lg[e] >= kth - MARGIN for e in gpu_ids[l, t]), f"{what}: invalid near-tie choice"
+
+
+class Pair:
+    """A GPU DecModel and an oracle model over the same seeded weights."""
+
+    def __init__(self, cfg, n_slots=1, max_prefill=64, max_seq=None, seed=0, weights=None):
+        from decoder_only_forward_amd.dec import DecModel
+        self.cfg = cfg
+        self.w = weights if weights is not None else synth.make_weights(cfg, seed=seed)
+        self.wd = to_device(self.w)
+        self.gpu = DecModel(cfg, self.wd, max_batch=n_slots, max_prefill=max_prefill, max_seq=max_seq)
+        self.ora = O.OracleModel(cfg, self.w, n_slots=n_slots, max_seq=max_seq)
+
+    def capture_buffers(self, rows):
+        c = self.cfg
+        hid = torch.full(((c.n_layers + 1), rows, c.hidden), float("nan"), device="cuda")
+        ids = rl = None
+        if c.n_experts:
+            ids = torch.zeros((c.n_layers, rows, c.top_k), dtype=torch.int32, device="cuda")
+            rl = torch.zeros((c.n_layers, rows, c.n_experts), dtype=torch.float32, device="cuda")
+        self.gpu.set_capture(hid, ids, rl)
+        return hid, ids, rl

@@ -1,0 +1,108 @@
+"""The C ABI boundary on the host (no GPU): the library loads, exports every
+function include/dec.h declares, and rejects bad calls before touching the
+device, leaving every KV length unchanged (rml "The decoder", section "One
+forward pass", step 1)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from decoder_only_forward_amd import configs
+from decoder_only_forward_amd import dec as D
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    if not os.path.exists(D.LIB_PATH):
+        pytest.skip("libdec.so not built (run __graft_entry__.build())")
+    return D.load()
+
+
+def test_header_exports_are_all_present():
+    L = _lib()
+    with open(os.path.join(ROOT, "include", "dec.h")) as f:
+        names = re.findall(r"DEC_API\s+[\w\s\*]*?\b(dec_\w+)\s*\(", f.read())
+    assert len(names) >= 13 and set(D.EXPORTS) <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_workspace_bytes_is_host_only_and_validates():
+    _lib()
+    n = D.workspace_bytes(configs.MISTRAL, max_batch=32, max_prefill=4096)
+    kv = 2 * 32 * 32 * 8 * 4096 * 128 * 4          # fp32 K and V of 32 slots
+    assert n >= kv
+    assert D.workspace_bytes(configs.MISTRAL.replace(n_kv_heads=5), 1, 1) == 0     # heads do not split
+    assert D.workspace_bytes(configs.TINY.replace(head_dim=15), 1, 1) == 0         # odd head_dim
+    assert D.workspace_bytes(configs.TINY, 1, 0) == 0
+
+
+def _create(cfg, max_batch=2, max_prefill=8, ws=None, ws_bytes=None, **over):
+    L = _lib()
+    c = D.make_config(cfg, max_batch, max_prefill)
+    for k, v in over.items():
+        setattr(c, k, v)
+    need = L.dec_workspace_bytes(ctypes.byref(c))
+    fake = 0x7F0000000000          # never dereferenced: create only validates and records
+    layers = (D.DecLayerWeights * cfg.n_layers)()
+    for i in range(cfg.n_layers):
+        for f, _ in D.DecLayerWeights._fields_:
+            setattr(layers[i], f, fake)
+    w = D.DecWeights(ctypes.sizeof(D.DecWeights), fake, fake, fake, layers)
+    h = ctypes.c_void_p()
+    rc = L.dec_create(ctypes.byref(c), ctypes.byref(w), ws if ws is not None else fake,
+                      ws_bytes if ws_bytes is not None else need, None, ctypes.byref(h))
+    return rc, h, L
+
+
+def test_create_validation():
+    assert _create(configs.TINY, ws_bytes=16)[0] == D.DEC_ERR_NOMEM
+    assert _create(configs.TINY, ws=0x7F0000000001)[0] == D.DEC_ERR_INVALID      # misaligned
+    assert _create(configs.TINY, struct_size=8)[0] == D.DEC_ERR_INVALID
+    assert _create(configs.TINY, head_dim=32)[0] == D.DEC_ERR_UNSUPPORTED
+    assert _create(configs.TINY, max_batch=65)[0] == D.DEC_ERR_UNSUPPORTED
+    assert _create(configs.TINY, n_experts=2, top_k=3)[0] == D.DEC_ERR_INVALID   # top_k > n_experts
+    assert _create(configs.TINY_BF16, ffn_dim=100)[0] == D.DEC_ERR_UNSUPPORTED    # bf16 tiles need 64 | ffn
+    assert _create(configs.TINY_WINDOW, max_seq=6)[0] == D.DEC_ERR_INVALID       # ring longer than the window
+    rc, h, L = _create(configs.TINY)
+    assert rc == D.DEC_OK
+    L.dec_destroy(h)
+
+
+def test_bad_calls_change_nothing():
+    rc, h, L = _create(configs.TINY, max_batch=2, max_prefill=8)
+    assert rc == D.DEC_OK
+    fake_logits = ctypes.c_void_p(0x7F0000000000)
+    tok = np.array([1, 2, 3], dtype=np.int32)
+    bad = np.array([1, configs.TINY.vocab], dtype=np.int32)
+    pos = np.array([0, 0], dtype=np.int32)
+    cases = [
+        (L.dec_prefill, (h, 0, bad.ctypes.data, 2, 0, fake_logits), D.DEC_ERR_INVALID),   # id >= vocab
+        (L.dec_prefill, (h, 0, tok.ctypes.data, 0, 0, fake_logits), D.DEC_ERR_INVALID),   # empty
+        (L.dec_prefill, (h, 2, tok.ctypes.data, 3, 0, fake_logits), D.DEC_ERR_INVALID),   # no slot 2
+        (L.dec_prefill, (h, 0, tok.ctypes.data, 3, 1, fake_logits), D.DEC_ERR_INVALID),   # not the length
+        (L.dec_prefill, (h, 0, np.zeros(9, np.int32).ctypes.data, 9, 0, fake_logits), D.DEC_ERR_RANGE),
+        (L.dec_decode, (h, 3, tok.ctypes.data, np.zeros(3, np.int32).ctypes.data, fake_logits), D.DEC_ERR_INVALID),
+        (L.dec_decode, (h, 2, tok.ctypes.data, np.array([0, 5], np.int32).ctypes.data, fake_logits),
+         D.DEC_ERR_INVALID),
+        (L.dec_decode, (h, 2, bad.ctypes.data, pos.ctypes.data, fake_logits), D.DEC_ERR_INVALID),
+        (L.dec_kv_reset, (h, 5), D.DEC_ERR_INVALID),
+        (L.dec_greedy, (h, fake_logits, 3, tok.ctypes.data), D.DEC_ERR_INVALID),
+    ]
+    for fn, args, want in cases:
+        assert fn(*args) == want, (fn.__name__, args)
+        assert L.dec_kv_length(h, 0) == 0 and L.dec_kv_length(h, 1) == 0
+    assert L.dec_kv_length(h, 2) == D.DEC_ERR_INVALID
+    assert L.dec_status_str(D.DEC_ERR_RANGE) == b"out of range"
+    L.dec_destroy(h)
+
+
+def test_capacity_without_window_is_range_error():
+    rc, h, L = _create(configs.TINY, max_batch=1, max_prefill=64)     # max_seq 16
+    tok = np.zeros(17, dtype=np.int32)
+    assert L.dec_prefill(h, 0, tok.ctypes.data, 17, 0, ctypes.c_void_p(0x7F0000000000)) == D.DEC_ERR_RANGE
+    assert L.dec_kv_length(h, 0) == 0
+    L.dec_destroy(h)
