@@ -7,6 +7,9 @@ typedef uint16_t u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+// Native 16-byte vector (a plain ext_vector, unlike uint4, stays in registers
+// when held in arrays across loop iterations).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define WAVE 64
 

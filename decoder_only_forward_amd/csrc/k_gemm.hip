@@ -5,11 +5,8 @@
 // tile), the activation tile the B operand, fed twice (hi then lo) into the
 // same accumulator so the fp32 activations keep ~16 significant bits.
 //
-// Block tile 128 (features) x 128 (tokens) x 64 (k); 4 waves in 2x2, each wave
-// 64 x 64 = 4 x 4 MFMA tiles of 16x16x32.  Tiles are staged through LDS with
-// 16-byte global loads; the next k-tile is fetched into registers while the
-// current one is multiplied.  Rows are padded by 16 bytes so the MFMA operand
-// reads (16 rows x 16 bytes per lane group) fall in distinct banks.
+// Tiles are staged through LDS with 16-byte global loads; rows are padded by 16
+// bytes so the MFMA operand reads of one lane group fall in distinct banks.
 //
 // An optional expert grouping (MoE prefill) runs one grid slice per expert over
 // that expert's contiguous rows of `a` and its slice of the weights.
@@ -31,19 +28,23 @@ struct GemmParams {
     size_t expert_stride;
 };
 
-constexpr int BN = 128, BM = 128, BK = 64;
-constexpr int LDS_ROW = BK + 8;          // u16 per padded row (144 bytes)
-constexpr int TILE_U16 = 128 * LDS_ROW;  // one 128-row tile
+// Block tile: BN = 256 output features (weight rows) x BM = 128 tokens x BK = 64.
+// 8 waves as 4 (features) x 2 (tokens), each wave 64 x 64 = 2 x 2 MFMA tiles of
+// 32x32x16.  Two LDS stages and two register stages: the global loads of
+// k-tile k+2 are in flight while tile k is multiplied, so the HBM/L2 latency is
+// hidden behind two tiles of MFMA work.
+constexpr int BN = 256, BM = 128, BK = 64;
+constexpr int NTHR = 512;
+constexpr int LDR = BK + 8;                    // u16 per padded LDS row (144 bytes)
+constexpr int STAGE_U16 = (BN + 2 * BM) * LDR; // W, A_hi, A_lo of one k-tile
+constexpr int WLOADS = BN * BK / 8 / NTHR;     // 16-byte chunks per thread per tile (4)
+constexpr int ALOADS = BM * BK / 8 / NTHR;     // (2) for each of hi and lo
 
-__global__ void __launch_bounds__(256, 2) gemm_kernel(GemmParams p) {
-    __shared__ __attribute__((aligned(16))) u16 sw[TILE_U16];
-    __shared__ __attribute__((aligned(16))) u16 sh[TILE_U16];
-    __shared__ __attribute__((aligned(16))) u16 sl[TILE_U16];
-
+__global__ void __launch_bounds__(NTHR, 1) gemm_kernel(GemmParams p) {
+    extern __shared__ __attribute__((aligned(16))) u16 smem[];
     const int tid = threadIdx.x;
     const int lane = tid % WAVE, wv = tid / WAVE;
-    const int r = lane & 15, c = lane >> 4;
-    const int wn = wv & 1, wm = wv >> 1;  // wave's 64x64 sub-tile: features wn, tokens wm
+    const int wn = wv & 3, wm = wv >> 2;
 
     int M = p.M, mrow0 = 0;
     size_t wofs = 0;
@@ -53,100 +54,159 @@ __global__ void __launch_bounds__(256, 2) gemm_kernel(GemmParams p) {
         M = p.grp_off[e + 1] - mrow0;
         wofs = (size_t)e * p.expert_stride;
     }
-    const int m0 = blockIdx.y * BM;
+    // tile order: each XCD (blocks are dealt round-robin to 8 of them) walks a
+    // contiguous run of tiles, tokens fastest, so a weight tile stays in its L2.
+    const int ntn = (p.N + BN - 1) / BN, ntm = gridDim.y;
+    int bid = blockIdx.x + blockIdx.y * gridDim.x;
+    const int nblk = ntn * ntm;
+    if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+    const int tn = bid / ntm, tm = bid % ntm;
+    const int m0 = tm * BM;
     if (m0 >= M) return;
-    const int n0 = blockIdx.x * BN;
+    const int n0 = tn * BN;
 
-    // global -> LDS assignment: 4 passes of 256 threads over 128 rows x 8 chunks
-    const u16 *gw[4];
-    const u16 *gh[4];
-    const u16 *gl[4];
+    // per-thread global offsets (elements) of its 16-byte chunks
+    size_t ow[WLOADS], oa[ALOADS];
+    const u16 *wbase[WLOADS];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        const int idx = tid + i * 256;
+    for (int i = 0; i < WLOADS; i++) {
+        const int idx = tid + i * NTHR;
         const int row = idx >> 3, ch = idx & 7;
         int n = n0 + row;
         n = n < p.N ? n : p.N - 1;
-        int s = 0, start = 0;
-        while (s < p.nseg - 1 && n >= p.seg_end[s]) { start = p.seg_end[s]; s++; }
-        gw[i] = p.w[s] + wofs + (size_t)(n - start) * p.K + ch * 8;
+        const u16 *wp = p.w[0];
+        int start = 0;
+        if (p.nseg > 1 && n >= p.seg_end[0]) { wp = p.w[1]; start = p.seg_end[0]; }
+        if (p.nseg > 2 && n >= p.seg_end[1]) { wp = p.w[2]; start = p.seg_end[1]; }
+        wbase[i] = wp;
+        ow[i] = wofs + (size_t)(n - start) * p.K + ch * 8;
+    }
+#pragma unroll
+    for (int i = 0; i < ALOADS; i++) {
+        const int idx = tid + i * NTHR;
+        const int row = idx >> 3, ch = idx & 7;
         int m = m0 + row;
         m = m < M ? m : M - 1;
-        gh[i] = p.a_hi + (size_t)(mrow0 + m) * p.lda + ch * 8;
-        gl[i] = p.a_lo + (size_t)(mrow0 + m) * p.lda + ch * 8;
+        oa[i] = (size_t)(mrow0 + m) * p.lda + ch * 8;
     }
-    uint4 rw[4], rh[4], rl[4];
-    auto gload = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            rw[i] = *reinterpret_cast<const uint4 *>(gw[i] + k0);
-            rh[i] = *reinterpret_cast<const uint4 *>(gh[i] + k0);
-            rl[i] = *reinterpret_cast<const uint4 *>(gl[i] + k0);
-        }
-    };
-    auto lstore = [&]() {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int idx = tid + i * 256;
-            const int row = idx >> 3, ch = idx & 7;
-            *reinterpret_cast<uint4 *>(sw + row * LDS_ROW + ch * 8) = rw[i];
-            *reinterpret_cast<uint4 *>(sh + row * LDS_ROW + ch * 8) = rh[i];
-            *reinterpret_cast<uint4 *>(sl + row * LDS_ROW + ch * 8) = rl[i];
-        }
-    };
+    const u16 *__restrict__ ahi = p.a_hi;
+    const u16 *__restrict__ alo = p.a_lo;
 
-    floatx4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int j = 0; j < 4; j++) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+#define GEMM_GLOAD(W, H, L, kt)                                                                   \
+    do {                                                                                          \
+        const int k0_ = (kt) * BK;                                                                \
+        _Pragma("unroll") for (int i = 0; i < WLOADS; i++)                                        \
+            W[i] = *reinterpret_cast<const u32x4 *>(wbase[i] + ow[i] + k0_);                      \
+        _Pragma("unroll") for (int i = 0; i < ALOADS; i++) {                                      \
+            H[i] = *reinterpret_cast<const u32x4 *>(ahi + oa[i] + k0_);                           \
+            L[i] = *reinterpret_cast<const u32x4 *>(alo + oa[i] + k0_);                           \
+        }                                                                                         \
+    } while (0)
+#define GEMM_LSTORE(W, H, L, buf)                                                                 \
+    do {                                                                                          \
+        u16 *sw_ = smem + (buf) * STAGE_U16;                                                      \
+        u16 *sh_ = sw_ + BN * LDR;                                                                \
+        u16 *sl_ = sh_ + BM * LDR;                                                                \
+        _Pragma("unroll") for (int i = 0; i < WLOADS; i++) {                                      \
+            const int idx = tid + i * NTHR;                                                       \
+            *reinterpret_cast<u32x4 *>(sw_ + (idx >> 3) * LDR + (idx & 7) * 8) = W[i];            \
+        }                                                                                         \
+        _Pragma("unroll") for (int i = 0; i < ALOADS; i++) {                                      \
+            const int idx = tid + i * NTHR;                                                       \
+            *reinterpret_cast<u32x4 *>(sh_ + (idx >> 3) * LDR + (idx & 7) * 8) = H[i];            \
+            *reinterpret_cast<u32x4 *>(sl_ + (idx >> 3) * LDR + (idx & 7) * 8) = L[i];            \
+        }                                                                                         \
+    } while (0)
+
+    const floatx16 zero16 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    floatx16 acc00 = zero16, acc01 = zero16, acc10 = zero16, acc11 = zero16;
+
+    const int r32 = lane & 31, c2 = lane >> 5;
+    const int wrow0 = (wn * 64 + r32) * LDR + c2 * 8;
+    const int arow0 = (wm * 64 + r32) * LDR + c2 * 8;
+#define GEMM_COMPUTE(buf)                                                                         \
+    do {                                                                                          \
+        const u16 *sw_ = smem + (buf) * STAGE_U16;                                                \
+        const u16 *sh_ = sw_ + BN * LDR;                                                          \
+        const u16 *sl_ = sh_ + BM * LDR;                                                          \
+        _Pragma("unroll") for (int ks = 0; ks < BK / 16; ks++) {                                  \
+            const bf16x8 fw0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sw_ + wrow0 + ks * 16)); \
+            const bf16x8 fw1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sw_ + wrow0 + 32 * LDR + ks * 16)); \
+            const bf16x8 fh0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sh_ + arow0 + ks * 16)); \
+            const bf16x8 fh1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sh_ + arow0 + 32 * LDR + ks * 16)); \
+            const bf16x8 fl0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sl_ + arow0 + ks * 16)); \
+            const bf16x8 fl1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sl_ + arow0 + 32 * LDR + ks * 16)); \
+            acc00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw0, fh0, acc00, 0, 0, 0);           \
+            acc01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw0, fh1, acc01, 0, 0, 0);           \
+            acc10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw1, fh0, acc10, 0, 0, 0);           \
+            acc11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw1, fh1, acc11, 0, 0, 0);           \
+            acc00 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw0, fl0, acc00, 0, 0, 0);           \
+            acc01 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw0, fl1, acc01, 0, 0, 0);           \
+            acc10 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw1, fl0, acc10, 0, 0, 0);           \
+            acc11 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw1, fl1, acc11, 0, 0, 0);           \
+        }                                                                                         \
+    } while (0)
 
     const int nk = p.K / BK;
-    gload(0);
-    for (int kt = 0; kt < nk; kt++) {
-        __syncthreads();
-        lstore();
-        __syncthreads();
-        if (kt + 1 < nk) gload((kt + 1) * BK);
-#pragma unroll
-        for (int ks = 0; ks < BK / 32; ks++) {
-            bf16x8 fa[4], fh[4], fl[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int wr = wn * 64 + i * 16 + r;
-                fa[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(sw + wr * LDS_ROW + ks * 32 + c * 8));
-                const int ar = wm * 64 + i * 16 + r;
-                fh[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(sh + ar * LDS_ROW + ks * 32 + c * 8));
-                fl[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4 *>(sl + ar * LDS_ROW + ks * 32 + c * 8));
-            }
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fh[j], acc[i][j], 0, 0, 0);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[i], fl[j], acc[i][j], 0, 0, 0);
-                }
+    u32x4 raw[WLOADS], rah[ALOADS], ral[ALOADS];
+    u32x4 rbw[WLOADS], rbh[ALOADS], rbl[ALOADS];
+    GEMM_GLOAD(raw, rah, ral, 0);
+    if (nk > 1) GEMM_GLOAD(rbw, rbh, rbl, 1);
+    GEMM_LSTORE(raw, rah, ral, 0);
+    if (nk > 2) GEMM_GLOAD(raw, rah, ral, 2);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+        // buf 0 holds tile kt; rb* holds tile kt+1; ra* has tile kt+2 in flight
+        GEMM_COMPUTE(0);
+        if (kt + 1 < nk) {
+            GEMM_LSTORE(rbw, rbh, rbl, 1);
+            if (kt + 3 < nk) GEMM_GLOAD(rbw, rbh, rbl, kt + 3);
         }
+        __syncthreads();
+        if (kt + 1 >= nk) break;
+        // buf 1 holds tile kt+1; ra* holds tile kt+2; rb* has tile kt+3 in flight
+        GEMM_COMPUTE(1);
+        if (kt + 2 < nk) {
+            GEMM_LSTORE(raw, rah, ral, 0);
+            if (kt + 4 < nk) GEMM_GLOAD(raw, rah, ral, kt + 4);
+        }
+        __syncthreads();
     }
+#undef GEMM_GLOAD
+#undef GEMM_LSTORE
+#undef GEMM_COMPUTE
 
-    // acc[i][j]: features n0 + wn*64 + i*16 + 4c .. +3, token m0 + wm*64 + j*16 + r
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        const int m = m0 + wm * 64 + j * 16 + r;
-        if (m >= M) continue;
+    // acc<i><j>: features n0 + wn*64 + i*32 + (e/4)*8 + c2*4 + e%4, token m0 + wm*64 + j*32 + r32
+    auto store_tile = [&](const floatx16 v, int i, int j) {
+        const int m = m0 + wm * 64 + j * 32 + r32;
+        if (m >= M) return;
         float *dst = p.out + (size_t)(mrow0 + m) * p.ldo;
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int n = n0 + wn * 64 + i * 16 + 4 * c;
-            const floatx4 v = acc[i][j];
+        for (int g = 0; g < 4; g++) {
+            const int n = n0 + wn * 64 + i * 32 + g * 8 + c2 * 4;
             if (n + 3 < p.N) {
-                *reinterpret_cast<float4 *>(dst + n) = make_float4(v[0], v[1], v[2], v[3]);
+                *reinterpret_cast<float4 *>(dst + n) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
             } else {
-                if (n < p.N) dst[n] = v[0];
-                if (n + 1 < p.N) dst[n + 1] = v[1];
-                if (n + 2 < p.N) dst[n + 2] = v[2];
+                if (n < p.N) dst[n] = v[4 * g];
+                if (n + 1 < p.N) dst[n + 1] = v[4 * g + 1];
+                if (n + 2 < p.N) dst[n + 2] = v[4 * g + 2];
             }
         }
+    };
+    store_tile(acc00, 0, 0);
+    store_tile(acc01, 0, 1);
+    store_tile(acc10, 1, 0);
+    store_tile(acc11, 1, 1);
+}
+
+constexpr size_t GEMM_LDS = 2 * STAGE_U16 * sizeof(u16);
+
+// The two LDS stages exceed the default dynamic-LDS cap; raise it once.
+void gemm_lds_attr() {
+    static bool done = false;
+    if (!done) {
+        (void)hipFuncSetAttribute((const void *)gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)GEMM_LDS);
+        done = true;
     }
 }
 
@@ -177,7 +237,8 @@ void launch_gemm(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
     GemmParams p{};
     fill(p, segs, nseg, K, a_hi, a_lo, lda, M, out, ldo);
     dim3 grid((p.N + BN - 1) / BN, (M + BM - 1) / BM, 1);
-    hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, st, p);
+    gemm_lds_attr();
+    hipLaunchKernelGGL(gemm_kernel, grid, dim3(NTHR), GEMM_LDS, st, p);
 }
 
 void launch_gemm_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi,
@@ -189,7 +250,8 @@ void launch_gemm_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, cons
     p.grp_off = offsets;
     p.expert_stride = expert_stride;
     dim3 grid((p.N + BN - 1) / BN, (max_rows + BM - 1) / BM, E);
-    hipLaunchKernelGGL(gemm_kernel, grid, dim3(256), 0, st, p);
+    gemm_lds_attr();
+    hipLaunchKernelGGL(gemm_kernel, grid, dim3(NTHR), GEMM_LDS, st, p);
 }
 
 // ---- fp32 weights (the small fp32 model): one thread per output -----------

@@ -62,9 +62,11 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemvParams p) {
     for (int rt = 0; rt < 2; rt++) {
         const int n = blockIdx.x * ROWS_PER_BLOCK + wv * 32 + rt * 16 + r;
         const int nn = n < p.N ? n : p.N - 1;
-        int s = 0, start = 0;
-        while (s < p.nseg - 1 && nn >= p.seg_end[s]) { start = p.seg_end[s]; s++; }
-        wrow[rt] = p.w[s] + wofs + (size_t)(nn - start) * p.K;
+        const u16 *wp = p.w[0];
+        int start = 0;
+        if (p.nseg > 1 && nn >= p.seg_end[0]) { wp = p.w[1]; start = p.seg_end[0]; }
+        if (p.nseg > 2 && nn >= p.seg_end[1]) { wp = p.w[2]; start = p.seg_end[1]; }
+        wrow[rt] = wp + wofs + (size_t)(nn - start) * p.K;
         nrow[rt] = n;
     }
 
