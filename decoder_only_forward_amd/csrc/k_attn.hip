@@ -384,6 +384,225 @@ bool launch_prefill_hd(hipStream_t st, int G, dim3 grid, int T, int start_pos, i
 
 }  // namespace
 
+// ---- prefill on MFMA ---------------------------------------------------------------
+// Flash attention for head_dim 64/128.  A block holds 128 query vectors ((row,
+// head) pairs of one kv group) and streams the group's K/V in tiles of 64
+// positions through LDS, converted once to bf16 (hi, lo) pairs.  Per wave (32
+// query vectors):
+//   S^T = K Q^T   (32x32x16 MFMAs; lane q+32h owns 32 scores of query q, so
+//                  the row max / sum of the online softmax are in-lane plus one
+//                  shuffle)
+//   O^T += V^T P^T (P feeds the MFMA straight from the S^T accumulator; the key
+//                  order inside the contraction is relabelled to match, and V is
+//                  staged transposed so the relabelled reads are 8-byte runs)
+// Each product is hi*hi + hi*lo + lo*hi, which keeps the scores and outputs at
+// fp32 accuracy (the lo*lo term is below 2^-16 of the total).
+namespace {
+
+constexpr int NQV = 128, MKV = 64;
+
+__device__ __forceinline__ bf16x8 pack8(const uint32_t *h) {
+    u32x4 v;
+    v[0] = h[0] | (h[1] << 16); v[1] = h[2] | (h[3] << 16);
+    v[2] = h[4] | (h[5] << 16); v[3] = h[6] | (h[7] << 16);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int HD, int G>
+__global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
+    int T, int start_pos, int slot, const float *__restrict__ q, const float *__restrict__ kc,
+    const float *__restrict__ vc, int nh, int nkv, int max_seq, u16 *__restrict__ o_hi, u16 *__restrict__ o_lo,
+    float *__restrict__ o_f32) {
+    constexpr int ROWS = NQV / G;
+    constexpr int KLD = HD + 8;     // u16 per K row in LDS
+    constexpr int VLD = MKV + 4;    // u16 per transposed V row (136 bytes)
+    constexpr int KS = HD / 16;     // MFMA k-steps over head_dim
+    constexpr int DT = HD / 32;     // output dim tiles
+    __shared__ __attribute__((aligned(16))) u16 sKh[MKV * KLD];
+    __shared__ __attribute__((aligned(16))) u16 sKl[MKV * KLD];
+    __shared__ __attribute__((aligned(16))) u16 sVh[HD * VLD];
+    __shared__ __attribute__((aligned(16))) u16 sVl[HD * VLD];
+
+    const int kvh = blockIdx.y;
+    const int rb = gridDim.x - 1 - blockIdx.x;  // longest rows first
+    const int t0 = rb * ROWS;
+    const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
+    const int ql = lane & 31, hh = lane >> 5;
+    const int qv = wv * 32 + ql;
+    const int row = qv / G, g = qv % G;
+    const int t = t0 + row;
+    const bool live = row < ROWS && t < T;
+    const int qpos = live ? start_pos + t : -1;
+    const int h = kvh * G + g;
+
+    // Q^T operand (B of S^T): lane (q + 32hh), k-step s -> dims 16s + 8hh .. +8
+    bf16x8 qh[KS], qlo[KS];
+    {
+        const float *qp = q + (size_t)(live ? t : 0) * nh * HD + (size_t)h * HD + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < KS; s++) {
+            uint32_t hb[8], lb[8];
+            const float4 a = *reinterpret_cast<const float4 *>(qp + 16 * s);
+            const float4 b = *reinterpret_cast<const float4 *>(qp + 16 * s + 4);
+            const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int j = 0; j < 8; j++) split_bf16(live ? f[j] : 0.f, hb[j], lb[j]);
+            qh[s] = pack8(hb);
+            qlo[s] = pack8(lb);
+        }
+    }
+    const float zero16v = 0.f;
+    floatx16 o[DT];
+#pragma unroll
+    for (int d = 0; d < DT; d++)
+#pragma unroll
+        for (int e = 0; e < 16; e++) o[d][e] = zero16v;
+    float m = -INFINITY, l = 0.f;
+    const float scale = 1.0f / sqrtf((float)HD);
+
+    // largest query position of the wave and of the block
+    int wmax = qpos;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) wmax = max(wmax, __shfl_xor(wmax, off, WAVE));
+    const int last_pos = start_pos + min(T, t0 + ROWS) - 1;
+    const size_t head_base = ((size_t)slot * nkv + kvh) * max_seq;
+
+    for (int kb = 0; kb <= last_pos; kb += MKV) {
+        __syncthreads();
+        // K tile -> [key][dim] hi/lo; V tile -> transposed [dim][key] hi/lo
+        for (int i = tid; i < MKV * HD / 4; i += 256) {
+            const int key = i / (HD / 4), c4 = i % (HD / 4);
+            const int j = kb + key;
+            float4 kv = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (j <= last_pos) kv = *reinterpret_cast<const float4 *>(kc + (head_base + j) * HD + 4 * c4);
+            uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+            split_bf16(kv.x, h0, l0); split_bf16(kv.y, h1, l1); split_bf16(kv.z, h2, l2); split_bf16(kv.w, h3, l3);
+            *reinterpret_cast<uint2 *>(sKh + key * KLD + 4 * c4) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+            *reinterpret_cast<uint2 *>(sKl + key * KLD + 4 * c4) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+        }
+        for (int i = tid; i < (MKV / 2) * HD / 4; i += 256) {
+            const int kp = i / (HD / 4), c4 = i % (HD / 4);
+            const int j = kb + 2 * kp;
+            float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
+            if (j <= last_pos) v0 = *reinterpret_cast<const float4 *>(vc + (head_base + j) * HD + 4 * c4);
+            if (j + 1 <= last_pos) v1 = *reinterpret_cast<const float4 *>(vc + (head_base + j + 1) * HD + 4 * c4);
+            const float a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+            for (int e = 0; e < 4; e++) {
+                uint32_t ha, la, hb, lb;
+                split_bf16(a0[e], ha, la);
+                split_bf16(a1[e], hb, lb);
+                *reinterpret_cast<uint32_t *>(sVh + (4 * c4 + e) * VLD + 2 * kp) = ha | (hb << 16);
+                *reinterpret_cast<uint32_t *>(sVl + (4 * c4 + e) * VLD + 2 * kp) = la | (lb << 16);
+            }
+        }
+        __syncthreads();
+        if (kb > wmax) continue;  // every query of this wave is before the tile
+
+        // S^T for the 64 keys: two 32-key sub-tiles
+        floatx16 sc[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++) {
+#pragma unroll
+            for (int e = 0; e < 16; e++) sc[kt][e] = 0.f;
+#pragma unroll
+            for (int s2 = 0; s2 < KS; s2++) {
+                const int off = (kt * 32 + ql) * KLD + 16 * s2 + 8 * hh;
+                const bf16x8 kh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sKh + off));
+                const bf16x8 klo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sKl + off));
+                sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[s2], sc[kt], 0, 0, 0);
+                sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qlo[s2], sc[kt], 0, 0, 0);
+                sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo, qh[s2], sc[kt], 0, 0, 0);
+            }
+        }
+        // lane holds keys kb + kt*32 + (e/4)*8 + 4hh + e%4 of query qpos
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                const int key = kb + kt * 32 + (e / 4) * 8 + 4 * hh + (e % 4);
+                const float v = key <= qpos ? sc[kt][e] * scale : -INFINITY;
+                sc[kt][e] = v;
+                mx = fmaxf(mx, v);
+            }
+        mx = fmaxf(mx, __shfl_xor(mx, 32, WAVE));
+        const float mnew = fmaxf(m, mx);
+        const float corr = (mnew == -INFINITY) ? 1.f : expf(m - mnew);
+        float ps = 0.f;
+        uint32_t ph[2][16], plo[2][16];
+#pragma unroll
+        for (int kt = 0; kt < 2; kt++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) {
+                const float pe = (sc[kt][e] == -INFINITY) ? 0.f : expf(sc[kt][e] - mnew);
+                ps += pe;
+                split_bf16(pe, ph[kt][e], plo[kt][e]);
+            }
+        ps += __shfl_xor(ps, 32, WAVE);
+        l = l * corr + ps;
+        m = mnew;
+#pragma unroll
+        for (int d = 0; d < DT; d++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) o[d][e] *= corr;
+        // O^T += V^T P^T over 4 k-steps of 16 keys; step ks uses the lane's
+        // values e = (ks%2)*8 + j of sub-tile ks/2, i.e. keys 16ks + (j/4)*8 + 4hh + j%4
+#pragma unroll
+        for (int ks = 0; ks < 4; ks++) {
+            const bf16x8 bh = pack8(&ph[ks / 2][(ks % 2) * 8]);
+            const bf16x8 bl = pack8(&plo[ks / 2][(ks % 2) * 8]);
+#pragma unroll
+            for (int d = 0; d < DT; d++) {
+                const int vrow = (d * 32 + ql) * VLD + 16 * ks + 4 * hh;
+                const uint2 h0 = *reinterpret_cast<const uint2 *>(sVh + vrow);
+                const uint2 h1 = *reinterpret_cast<const uint2 *>(sVh + vrow + 8);
+                const uint2 l0 = *reinterpret_cast<const uint2 *>(sVl + vrow);
+                const uint2 l1 = *reinterpret_cast<const uint2 *>(sVl + vrow + 8);
+                const u32x4 vh4 = {h0.x, h0.y, h1.x, h1.y};
+                const u32x4 vl4 = {l0.x, l0.y, l1.x, l1.y};
+                const bf16x8 ah = __builtin_bit_cast(bf16x8, vh4);
+                const bf16x8 al = __builtin_bit_cast(bf16x8, vl4);
+                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, o[d], 0, 0, 0);
+                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, o[d], 0, 0, 0);
+                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, o[d], 0, 0, 0);
+            }
+        }
+    }
+    if (!live) return;
+    const float inv = 1.0f / l;
+    const size_t base = (size_t)t * nh * HD + (size_t)h * HD;
+#pragma unroll
+    for (int d = 0; d < DT; d++)
+#pragma unroll
+        for (int gq = 0; gq < 4; gq++) {
+            const int dim = d * 32 + gq * 8 + 4 * hh;
+#pragma unroll
+            for (int e = 0; e < 4; e++) store_out(o[d][4 * gq + e] * inv, base + dim + e, o_hi, o_lo, o_f32);
+        }
+}
+
+template <int HD>
+bool launch_prefill_mfma_hd(hipStream_t st, int G, int T, int start_pos, int slot, const float *q, const float *kc,
+                            const float *vc, int nh, int nkv, int max_seq, u16 *o_hi, u16 *o_lo, float *o_f32) {
+#define APM(GG) hipLaunchKernelGGL((attn_prefill_mfma_kernel<HD, GG>), dim3((T + NQV / GG - 1) / (NQV / GG), nkv), \
+                                   dim3(256), 0, st, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, o_hi, o_lo, o_f32)
+    switch (G) {
+        case 1: APM(1); return true;
+        case 2: APM(2); return true;
+        case 3: APM(3); return true;
+        case 4: APM(4); return true;
+        case 5: APM(5); return true;
+        case 6: APM(6); return true;
+        case 7: APM(7); return true;
+        case 8: APM(8); return true;
+    }
+#undef APM
+    return false;
+}
+
+}  // namespace
+
 void launch_attn_prefill(hipStream_t st, int T, int start_pos, int slot, const float *q, const float *kc,
                          const float *vc, int nh, int nkv, int hd, int max_seq, int window, u16 *o_hi,
                          u16 *o_lo, float *o_f32) {
@@ -391,7 +610,7 @@ void launch_attn_prefill(hipStream_t st, int T, int start_pos, int slot, const f
     if (T <= 0) return;
     const int G = nh / nkv;
     dim3 grid((T + BQ - 1) / BQ, nkv);
-    if (hd == 128) launch_prefill_hd<128, 2>(st, G, grid, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, o_hi, o_lo, o_f32);
-    else if (hd == 64) launch_prefill_hd<64, 1>(st, G, grid, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, o_hi, o_lo, o_f32);
+    if (hd == 128) launch_prefill_mfma_hd<128>(st, G, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, o_hi, o_lo, o_f32);
+    else if (hd == 64) launch_prefill_mfma_hd<64>(st, G, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, o_hi, o_lo, o_f32);
     else launch_prefill_hd<16, 1>(st, G, grid, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, o_hi, o_lo, o_f32);
 }
