@@ -19,17 +19,34 @@
 
 namespace {
 
+struct EvPair {
+    hipEvent_t e1, e2;
+};
+
 struct Timing {
     bool on = false;
-    std::vector<hipEvent_t> ev;  // pairs
-    size_t used = 0;
+    double ms = 0;
     int64_t launches = 0;
     double bytes = 0, flops = 0;
+    std::vector<EvPair> pending;  // recorded, not yet read
+};
+
+// One captured decode step: B rows, attention split count and logits buffer
+// fix the launch sequence; tokens/positions enter through the first node
+// (set_rows), whose arguments are replaced before each replay.  Per-kernel
+// timing and test captures run eagerly instead.
+struct GraphEntry {
+    int B = 0, S = 0;
+    float *logits = nullptr;
+    hipGraph_t graph = nullptr;
+    hipGraphExec_t exec = nullptr;
+    hipGraphNode_t root = nullptr;
+    hipKernelNodeParams kp{};
 };
 
 struct Plan {  // byte offsets into the workspace
     size_t kv_layer;        // floats of one layer's K (or V) cache
-    size_t k, v, x, a_hi, a_lo, a_f32, part, q, attn, rope, tok, pos, slot, amax;
+    size_t k, v, x, a_hi, a_lo, a_f32, part, q, attn, rope, tok, pos, slot, amax, ssq;
     size_t moe_ids, moe_w, moe_cnt, moe_off, moe_pairs, g_hi, g_lo, g_f32, moe_y;
     size_t part_floats, act_elems, total;
     int rows;               // max rows of one pass (max(max_batch, max_prefill))
@@ -48,7 +65,7 @@ struct dec_model {
     hipStream_t st;
     char *ws;
     Plan pl;
-    float *kc, *vc, *x, *a_f32, *part, *q, *attn, *moe_w, *g_f32, *moe_y;
+    float *kc, *vc, *x, *a_f32, *part, *q, *attn, *moe_w, *g_f32, *moe_y, *ssq;
     u16 *a_hi, *a_lo, *g_hi, *g_lo;
     float2 *rope;
     int32_t *tok, *pos, *slot, *amax, *moe_ids, *moe_cnt, *moe_off, *moe_pairs;
@@ -56,8 +73,14 @@ struct dec_model {
     float *cap_hidden = nullptr, *cap_router = nullptr;
     int32_t *cap_ids = nullptr;
     Timing tm[DEC_K_COUNT];
+    std::vector<hipEvent_t> pool;      // free events for eager timing
     int wf32;
     int ring;
+    // decode graphs: captured on `cs`, fenced to the caller's stream by events
+    hipStream_t cs = nullptr;
+    hipEvent_t fence_in = nullptr, fence_out = nullptr;
+    std::vector<GraphEntry> graphs;
+    std::vector<std::pair<std::vector<long long>, int>> seen;  // shapes met once (captured on the second)
 };
 
 namespace {
@@ -65,8 +88,9 @@ namespace {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int proj_splits(const dec_config &c, int N, int K, int B) {
+    (void)N;
     if (c.weight_dtype == DEC_WEIGHT_F32 || B > 64) return 1;
-    return gemv_splits(N, K, B);
+    return gemv_max_splits(K);
 }
 
 bool plan(const dec_config &c, Plan &p) {
@@ -121,6 +145,7 @@ bool plan(const dec_config &c, Plan &p) {
     p.pos = take((size_t)rows * 4);
     p.slot = take((size_t)rows * 4);
     p.amax = take((size_t)c.max_batch * 4);
+    p.ssq = take((size_t)rows * ((d + 1023) / 1024) * 4);
     p.moe_ids = take(prow * 4);
     p.moe_w = take(prow * 4);
     p.moe_cnt = take(64 * 4);
@@ -163,29 +188,58 @@ struct Tick {
     int cls;
     hipEvent_t e1 = nullptr, e2 = nullptr;
     Tick(dec_model *mm, int c) : m(mm), cls(c) {
-        Timing &t = m->tm[cls];
-        if (!t.on) return;
-        if (t.used + 2 > t.ev.size()) {
-            for (int i = 0; i < 256; i++) {
-                hipEvent_t e;
-                if (hipEventCreate(&e) != hipSuccess) return;
-                t.ev.push_back(e);
-            }
+        if (!m->tm[cls].on) return;
+        while (m->pool.size() < 2) {
+            hipEvent_t e;
+            if (hipEventCreate(&e) != hipSuccess) return;
+            m->pool.push_back(e);
         }
-        e1 = t.ev[t.used];
-        e2 = t.ev[t.used + 1];
-        t.used += 2;
+        e1 = m->pool.back(); m->pool.pop_back();
+        e2 = m->pool.back(); m->pool.pop_back();
         hipEventRecord(e1, m->st);
     }
     void done(double bytes, double flops) {
         if (!e1) return;
         hipEventRecord(e2, m->st);
         Timing &t = m->tm[cls];
+        t.pending.push_back(EvPair{e1, e2});
         t.launches++;
         t.bytes += bytes;
         t.flops += flops;
     }
 };
+
+// Read every recorded event pair into the running totals (waits for them).
+int harvest(dec_model *m) {
+    int rc = DEC_OK;
+    for (auto &t : m->tm) {
+        for (const EvPair &p : t.pending) {
+            float e = 0;
+            if (hipEventSynchronize(p.e2) != hipSuccess || hipEventElapsedTime(&e, p.e1, p.e2) != hipSuccess)
+                rc = DEC_ERR_DEVICE;
+            else
+                t.ms += e;
+            m->pool.push_back(p.e1);
+            m->pool.push_back(p.e2);
+        }
+        t.pending.clear();
+    }
+    return rc;
+}
+
+double kv_read_bytes(const dec_config &c, int T, const int *hpos) {
+    double b = 0;
+    for (int i = 0; i < T; i++) b += 2.0 * std::min(hpos[i] + 1, c.max_seq) * c.n_kv_heads * c.head_dim * 4;
+    return b;
+}
+
+int attn_splits_for(const dec_model *m, int T, const int *hpos) {
+    const dec_config &c = m->c;
+    int maxread = 1;
+    for (int b = 0; b < T; b++) maxread = std::max(maxread, std::min(hpos[b] + 1, c.max_seq));
+    return std::min(attn_decode_splits(T, c.n_kv_heads, maxread, c.head_dim, c.n_heads / c.n_kv_heads),
+                    MAX_ATTN_SPLITS);
+}
 
 // ---- one pass over all layers for T rows ------------------------------------------
 struct Pass {
@@ -265,7 +319,7 @@ void run_pass(dec_model *m, const Pass &ps) {
     };
 
     launch_residual_norm(st, RN_EMBED, T, d, m->x, m->tok, m->embed, f32w, Partials{nullptr, 0, 0, 0}, nullptr,
-                         nullptr, 0, m->L[0].attn_norm, eps, ah, al, af, caph(0));
+                         nullptr, 0, m->L[0].attn_norm, eps, ah, al, af, caph(0), m->ssq);
     launch_rope_table(st, m->pos, T, hd, c.rope_theta, m->rope);
 
     for (int l = 0; l < c.n_layers; l++) {
@@ -280,18 +334,11 @@ void run_pass(dec_model *m, const Pass &ps) {
                        c.max_seq, m->ring);
         // attention -> a (row stride qd)
         if (ps.decode) {
-            int maxread = 1;
-            double kvbytes = 0;
-            for (int b = 0; b < T; b++) {
-                const int r = std::min(ps.hpos[b] + 1, c.max_seq);
-                maxread = std::max(maxread, r);
-                kvbytes += 2.0 * r * kvd * 4;
-            }
-            const int S = std::min(attn_decode_splits(T, nkv, maxread), MAX_ATTN_SPLITS);
+            const int S = attn_splits_for(m, T, ps.hpos);
             Tick tk(m, DEC_K_ATTN_DECODE);
             launch_attn_decode(st, T, m->q, kc, vc, m->pos, m->slot, nh, nkv, hd, c.max_seq, c.sliding_window, S,
                                m->attn, ah, al, af);
-            tk.done(kvbytes + 2.0 * T * qd * 4, 0);
+            tk.done(kv_read_bytes(c, T, ps.hpos) + 2.0 * T * qd * 4, 0);
         } else {
             double flops = 0;
             for (int t = 0; t < T; t++) flops += 4.0 * hd * nh * (ps.start_pos + t + 1);
@@ -304,7 +351,7 @@ void run_pass(dec_model *m, const Pass &ps) {
         WSeg wo[1] = {{w.wo, d}};
         Partials po = proj(m, wo, 1, qd, T, ah, al, af, qd);
         launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, po, nullptr, nullptr, 0, w.ffn_norm,
-                             eps, ah, al, af, nullptr);
+                             eps, ah, al, af, nullptr, m->ssq);
         const float *next_gain = (l + 1 < c.n_layers) ? m->L[l + 1].attn_norm : m->out_norm;
         if (c.n_experts == 0) {
             WSeg gu[2] = {{w.w_gate, F}, {w.w_up, F}};
@@ -313,7 +360,7 @@ void run_pass(dec_model *m, const Pass &ps) {
             WSeg wd[1] = {{w.w_down, d}};
             Partials pd = proj(m, wd, 1, F, T, ah, al, af, F);
             launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, pd, nullptr, nullptr, 0, next_gain,
-                                 eps, ah, al, af, caph(l + 1));
+                                 eps, ah, al, af, caph(l + 1), m->ssq);
         } else {
             const int E = c.n_experts, k = c.top_k, TP = T * k;
             WSeg wr[1] = {{w.router, E}};
@@ -331,7 +378,7 @@ void run_pass(dec_model *m, const Pass &ps) {
             Partials pd = proj_grouped(m, wd, 1, F, T, ah, al, af, F);
             launch_moe_scatter(st, TP, d, m->moe_pairs, pd, m->moe_y);
             launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, Partials{nullptr, 0, 0, 0}, m->moe_y,
-                                 m->moe_w, k, next_gain, eps, ah, al, af, caph(l + 1));
+                                 m->moe_w, k, next_gain, eps, ah, al, af, caph(l + 1), m->ssq);
         }
     }
     // LM head on the rows that need logits (a holds the final-norm rows)
@@ -346,6 +393,91 @@ void run_pass(dec_model *m, const Pass &ps) {
 }
 
 int check_device(hipError_t e) { return e == hipSuccess ? DEC_OK : DEC_ERR_DEVICE; }
+
+}  // namespace
+
+namespace {
+
+// Lazily made: a non-blocking stream of default priority for decode graphs and
+// the two fence events that order it with the caller's stream.
+bool graph_stream(dec_model *m) {
+    if (m->cs) return true;
+    if (hipStreamCreateWithFlags(&m->cs, hipStreamNonBlocking) != hipSuccess) { m->cs = nullptr; return false; }
+    if (hipEventCreateWithFlags(&m->fence_in, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&m->fence_out, hipEventDisableTiming) != hipSuccess)
+        return false;
+    return true;
+}
+
+void destroy_graph(GraphEntry &g) {
+    if (g.exec) hipGraphExecDestroy(g.exec);
+    if (g.graph) hipGraphDestroy(g.graph);
+    g.exec = nullptr;
+    g.graph = nullptr;
+}
+
+unsigned timing_mask(const dec_model *m) {
+    unsigned k = 0;
+    for (int i = 0; i < DEC_K_COUNT; i++)
+        if (m->tm[i].on) k |= 1u << i;
+    return k;
+}
+
+int replay(dec_model *m, GraphEntry &g, const RowArgs &ra) {
+    int B = g.B;
+    int32_t *tok = m->tok, *ps = m->pos, *sl = m->slot;
+    void *args[] = {(void *)&ra, (void *)&B, (void *)&tok, (void *)&ps, (void *)&sl};
+    hipKernelNodeParams kp = g.kp;
+    kp.kernelParams = args;
+    kp.extra = nullptr;
+    if (hipGraphExecKernelNodeSetParams(g.exec, g.root, &kp) != hipSuccess) return DEC_ERR_DEVICE;
+    if (hipEventRecord(m->fence_in, m->st) != hipSuccess || hipStreamWaitEvent(m->cs, m->fence_in, 0) != hipSuccess ||
+        hipGraphLaunch(g.exec, m->cs) != hipSuccess || hipEventRecord(m->fence_out, m->cs) != hipSuccess ||
+        hipStreamWaitEvent(m->st, m->fence_out, 0) != hipSuccess)
+        return DEC_ERR_DEVICE;
+    return DEC_OK;
+}
+
+// Capture one decode step into a graph (returns null if capture is not possible).
+GraphEntry *capture(dec_model *m, const RowArgs &ra, int B, int S, const int *pos, float *logits) {
+    if (!graph_stream(m)) return nullptr;
+    GraphEntry g;
+    g.B = B;
+    g.S = S;
+    g.logits = logits;
+    hipStream_t user = m->st;
+    if (hipEventRecord(m->fence_in, user) != hipSuccess || hipStreamWaitEvent(m->cs, m->fence_in, 0) != hipSuccess)
+        return nullptr;
+    if (hipStreamBeginCapture(m->cs, hipStreamCaptureModeThreadLocal) != hipSuccess) return nullptr;
+    m->st = m->cs;
+    launch_set_rows(m->st, ra, B, m->tok, m->pos, m->slot);
+    Pass ps{};
+    ps.T = B;
+    ps.decode = true;
+    ps.hpos = pos;
+    ps.logits = logits;
+    ps.logit_row0 = 0;
+    ps.logit_rows = B;
+    ps.cap_row = 0;
+    ps.cap_rows = B;
+    run_pass(m, ps);
+    m->st = user;
+    hipGraph_t graph = nullptr;
+    const hipError_t ec = hipStreamEndCapture(m->cs, &graph);
+    (void)hipGetLastError();
+    if (ec != hipSuccess || !graph) { destroy_graph(g); return nullptr; }
+    g.graph = graph;
+    size_t n = 0;
+    if (hipGraphGetRootNodes(graph, nullptr, &n) != hipSuccess || n != 1) { destroy_graph(g); return nullptr; }
+    if (hipGraphGetRootNodes(graph, &g.root, &n) != hipSuccess ||
+        hipGraphKernelNodeGetParams(g.root, &g.kp) != hipSuccess ||
+        hipGraphInstantiate(&g.exec, graph, nullptr, nullptr, 0) != hipSuccess) {
+        destroy_graph(g);
+        return nullptr;
+    }
+    m->graphs.push_back(g);
+    return &m->graphs.back();
+}
 
 }  // namespace
 
@@ -403,6 +535,7 @@ int dec_create(const dec_config *cfg, const dec_weights *w, void *workspace, siz
     m->pos = (int32_t *)(b + p.pos);
     m->slot = (int32_t *)(b + p.slot);
     m->amax = (int32_t *)(b + p.amax);
+    m->ssq = (float *)(b + p.ssq);
     m->moe_ids = (int32_t *)(b + p.moe_ids);
     m->moe_w = (float *)(b + p.moe_w);
     m->moe_cnt = (int32_t *)(b + p.moe_cnt);
@@ -419,10 +552,18 @@ int dec_create(const dec_config *cfg, const dec_weights *w, void *workspace, siz
     return DEC_OK;
 }
 
+int dec_graph_count(dec_handle h) { return h ? (int)h->graphs.size() : DEC_ERR_INVALID; }
+
 void dec_destroy(dec_handle h) {
     if (!h) return;
-    for (auto &t : h->tm)
-        for (hipEvent_t e : t.ev) hipEventDestroy(e);
+    if (h->cs) hipStreamSynchronize(h->cs);
+    hipStreamSynchronize(h->st);
+    harvest(h);
+    for (auto &g : h->graphs) destroy_graph(g);
+    for (hipEvent_t e : h->pool) hipEventDestroy(e);
+    if (h->fence_in) hipEventDestroy(h->fence_in);
+    if (h->fence_out) hipEventDestroy(h->fence_out);
+    if (h->cs) hipStreamDestroy(h->cs);
     delete h;
 }
 
@@ -436,6 +577,7 @@ int dec_prefill(dec_handle h, int seq, const int32_t *tokens, int n, int start_p
     if (start_pos != h->len[seq]) return DEC_ERR_INVALID;
     if (!h->ring && (long)start_pos + n > (long)c.max_seq) return DEC_ERR_RANGE;
     if ((long)start_pos + n > 0x7FFFFFFFL) return DEC_ERR_RANGE;
+    if (timing_mask(h) && harvest(h) != DEC_OK) return DEC_ERR_DEVICE;
 
     if (h->ring && (long)start_pos + n > (long)c.max_seq) {
         // positions of this call would overwrite ring slots its own earlier
@@ -492,11 +634,36 @@ int dec_decode(dec_handle h, int B, const int32_t *tokens, const int32_t *pos, f
         if (!h->ring && pos[b] + 1 > c.max_seq) return DEC_ERR_RANGE;
         if (pos[b] == 0x7FFFFFFF) return DEC_ERR_RANGE;
     }
+    if (timing_mask(h) && harvest(h) != DEC_OK) return DEC_ERR_DEVICE;
     RowArgs ra;
     for (int b = 0; b < B; b++) {
         ra.tok[b] = tokens[b];
         ra.pos[b] = pos[b];
         ra.slot[b] = b;
+    }
+    if (!h->cap_hidden && !h->cap_ids && !h->cap_router && !timing_mask(h)) {
+        // replay (or capture, the second time this shape is seen) one graph per step
+        const int S = attn_splits_for(h, B, pos);
+        GraphEntry *g = nullptr;
+        for (auto &e : h->graphs)
+            if (e.B == B && e.S == S && e.logits == logits) g = &e;
+        if (!g) {
+            const std::vector<long long> key = {B, S, (long long)(uintptr_t)logits};
+            int *count = nullptr;
+            for (auto &kv : h->seen)
+                if (kv.first == key) count = &kv.second;
+            if (!count) {
+                h->seen.push_back({key, 1});
+            } else if (*count == 1) {
+                g = capture(h, ra, B, S, pos, logits);
+                *count = g ? 2 : 3;  // 3: capture failed, stay eager for this shape
+            }
+        }
+        if (g) {
+            if (replay(h, *g, ra) != DEC_OK) return DEC_ERR_DEVICE;
+            for (int b = 0; b < B; b++) h->len[b] = pos[b] + 1;
+            return DEC_OK;
+        }
     }
     launch_set_rows(h->st, ra, B, h->tok, h->pos, h->slot);
     Pass ps{};
@@ -549,10 +716,11 @@ int dec_set_capture(dec_handle h, float *hidden, int32_t *expert_ids, float *rou
 
 int dec_timing_enable(dec_handle h, int kernel_class, int on) {
     if (!h || kernel_class < 0 || kernel_class >= DEC_K_COUNT) return DEC_ERR_INVALID;
-    Timing &t = h->tm[kernel_class];
     if (hipStreamSynchronize(h->st) != hipSuccess) return DEC_ERR_DEVICE;
+    harvest(h);
+    Timing &t = h->tm[kernel_class];
     t.on = on != 0;
-    t.used = 0;
+    t.ms = 0;
     t.launches = 0;
     t.bytes = t.flops = 0;
     return DEC_OK;
@@ -561,15 +729,10 @@ int dec_timing_enable(dec_handle h, int kernel_class, int on) {
 int dec_timing_read(dec_handle h, int kernel_class, double *total_ms, int64_t *launches, double *bytes,
                     double *flops) {
     if (!h || kernel_class < 0 || kernel_class >= DEC_K_COUNT) return DEC_ERR_INVALID;
-    Timing &t = h->tm[kernel_class];
     if (hipStreamSynchronize(h->st) != hipSuccess) return DEC_ERR_DEVICE;
-    double ms = 0;
-    for (size_t i = 0; i + 1 < t.used; i += 2) {
-        float e = 0;
-        if (hipEventElapsedTime(&e, t.ev[i], t.ev[i + 1]) != hipSuccess) return DEC_ERR_DEVICE;
-        ms += e;
-    }
-    if (total_ms) *total_ms = ms;
+    if (harvest(h) != DEC_OK) return DEC_ERR_DEVICE;
+    const Timing &t = h->tm[kernel_class];
+    if (total_ms) *total_ms = t.ms;
     if (launches) *launches = t.launches;
     if (bytes) *bytes = t.bytes;
     if (flops) *flops = t.flops;

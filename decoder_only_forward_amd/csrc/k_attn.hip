@@ -22,6 +22,13 @@ namespace {
 
 constexpr int NB = 4;  // positions per lane group per iteration (loads in flight)
 
+// K/V rows are read once per decode step: non-temporal loads stream them past
+// the caches.
+__device__ __forceinline__ float4 ntload4(const float *p) {
+    const floatx4 v = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p));
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+
 __device__ __forceinline__ void store_out(float v, size_t off, u16 *o_hi, u16 *o_lo, float *o_f32) {
     if (o_f32) o_f32[off] = v;
     if (o_hi) {
@@ -86,16 +93,16 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(
             const int j = base + i * NG + gid;
             valid[i] = j < end;
             const int jj = valid[i] ? j : beg;
-            k0[i] = *reinterpret_cast<const float4 *>(K + (size_t)jj * HD + 4 * u);
-            k1[i] = *reinterpret_cast<const float4 *>(K + (size_t)jj * HD + 4 * LP + 4 * u);
+            k0[i] = ntload4(K + (size_t)jj * HD + 4 * u);
+            k1[i] = ntload4(K + (size_t)jj * HD + 4 * LP + 4 * u);
         }
         float4 v0[NB], v1[NB];
 #pragma unroll
         for (int i = 0; i < NB; i++) {
             const int j = base + i * NG + gid;
             const int jj = valid[i] ? j : beg;
-            v0[i] = *reinterpret_cast<const float4 *>(V + (size_t)jj * HD + 4 * u);
-            v1[i] = *reinterpret_cast<const float4 *>(V + (size_t)jj * HD + 4 * LP + 4 * u);
+            v0[i] = ntload4(V + (size_t)jj * HD + 4 * u);
+            v1[i] = ntload4(V + (size_t)jj * HD + 4 * LP + 4 * u);
         }
         float s[NB][G];
 #pragma unroll
@@ -231,10 +238,23 @@ bool launch_decode_hd(hipStream_t st, int G, dim3 grid, const float *q, const fl
 
 }  // namespace
 
-int attn_decode_splits(int B, int nkv, int readable) {
-    // enough blocks to cover the CUs about twice, at least ~256 positions each
-    int s = (512 + B * nkv - 1) / (B * nkv);
-    const int maxs = (readable + 255) / 256;
+int attn_decode_splits(int B, int nkv, int readable, int hd, int G) {
+    // fill the resident-block slots once (a second partial round would leave
+    // the memory system idle), with at least 128 positions per split
+    static int occ_cache[3] = {0, 0, 0};
+    const int which = hd == 128 ? 0 : hd == 64 ? 1 : 2;
+    if (!occ_cache[which]) {
+        int occ = 0;
+        const void *fn = hd == 128 ? (const void *)attn_decode_kernel<128, 4>
+                       : hd == 64  ? (const void *)attn_decode_kernel<64, 4>
+                                   : (const void *)attn_decode_kernel<16, 4>;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 256, 0) != hipSuccess || occ <= 0) occ = 2;
+        occ_cache[which] = occ;
+    }
+    (void)G;
+    const int slots = occ_cache[which] * num_cus();
+    int s = slots / (B * nkv);
+    const int maxs = (readable + 127) / 128;
     if (s > maxs) s = maxs;
     if (s > 64) s = 64;
     if (s < 1) s = 1;

@@ -77,11 +77,81 @@ __global__ void __launch_bounds__(256) residual_norm_kernel(
     }
 }
 
+// Few rows (decode): the residual update, which sums the split-K partials,
+// runs over a (row, 1024-column chunk) grid and leaves per-chunk sums of
+// squares; the norm kernel then scales each chunk.  Chunk sums are added in
+// chunk order, so the result does not depend on scheduling.
+constexpr int RN_CHUNK = 1024;
+
+__global__ void __launch_bounds__(256) residual_chunk_kernel(
+    int d, float *__restrict__ x, Partials add, const float *__restrict__ moe_y, const float *__restrict__ moe_w,
+    int k, float *__restrict__ cap, float *__restrict__ ssq) {
+    __shared__ float red[16];
+    const int t = blockIdx.x, ch = blockIdx.y;
+    const int i4 = (ch * RN_CHUNK) / 4 + threadIdx.x;
+    float ss = 0.f;
+    if (4 * i4 < min(d, (ch + 1) * RN_CHUNK)) {
+        const size_t off = (size_t)t * d + 4 * i4;
+        float4 r = *reinterpret_cast<const float4 *>(x + off);
+        if (add.p) {
+            const float4 a = sum_splits4(add.p, add.S, add.stride, (size_t)t * add.ld + 4 * i4);
+            r.x += a.x; r.y += a.y; r.z += a.z; r.w += a.w;
+        }
+        if (moe_y) {
+            float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+            for (int j = 0; j < k; j++) {
+                const float w = moe_w[t * k + j];
+                const float4 e = *reinterpret_cast<const float4 *>(moe_y + ((size_t)t * k + j) * d + 4 * i4);
+                y.x += w * e.x; y.y += w * e.y; y.z += w * e.z; y.w += w * e.w;
+            }
+            r.x += y.x; r.y += y.y; r.z += y.z; r.w += y.w;
+        }
+        *reinterpret_cast<float4 *>(x + off) = r;
+        if (cap) *reinterpret_cast<float4 *>(cap + off) = r;
+        ss = r.x * r.x + r.y * r.y + r.z * r.z + r.w * r.w;
+    }
+    const float tot = block_sum(ss, red);
+    if (threadIdx.x == 0) ssq[t * gridDim.y + ch] = tot;
+}
+
+__global__ void __launch_bounds__(256) norm_chunk_kernel(int d, const float *__restrict__ x, const float *__restrict__ ssq,
+                                                         int nch, const float *__restrict__ gain, float eps,
+                                                         u16 *__restrict__ a_hi, u16 *__restrict__ a_lo,
+                                                         float *__restrict__ a_f32) {
+    const int t = blockIdx.x, ch = blockIdx.y;
+    float tot = 0.f;
+    for (int c = 0; c < nch; c++) tot += ssq[t * nch + c];
+    const float rs = 1.0f / sqrtf(tot / (float)d + eps);
+    const int i4 = (ch * RN_CHUNK) / 4 + threadIdx.x;
+    if (4 * i4 >= min(d, (ch + 1) * RN_CHUNK)) return;
+    const size_t off = (size_t)t * d + 4 * i4;
+    const float4 v = *reinterpret_cast<const float4 *>(x + off);
+    const float4 g = *reinterpret_cast<const float4 *>(gain + 4 * i4);
+    float4 a;
+    a.x = v.x * rs * g.x; a.y = v.y * rs * g.y; a.z = v.z * rs * g.z; a.w = v.w * rs * g.w;
+    if (a_f32) *reinterpret_cast<float4 *>(a_f32 + off) = a;
+    if (a_hi) {
+        uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+        split_bf16(a.x, h0, l0); split_bf16(a.y, h1, l1);
+        split_bf16(a.z, h2, l2); split_bf16(a.w, h3, l3);
+        *reinterpret_cast<uint2 *>(a_hi + off) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        *reinterpret_cast<uint2 *>(a_lo + off) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+    }
+}
+
 void launch_residual_norm(hipStream_t st, int mode, int T, int d, float *x, const int32_t *tok,
                           const void *embed, int embed_f32, Partials add, const float *moe_y,
                           const float *moe_w, int k, const float *gain, float eps, u16 *a_hi,
-                          u16 *a_lo, float *a_f32, float *cap) {
+                          u16 *a_lo, float *a_f32, float *cap, float *ssq) {
     if (T <= 0) return;
+    if (mode == RN_ADD && T <= 64 && ssq) {
+        const int nch = (d + RN_CHUNK - 1) / RN_CHUNK;
+        hipLaunchKernelGGL(residual_chunk_kernel, dim3(T, nch), dim3(256), 0, st, d, x, add, moe_y, moe_w, k, cap, ssq);
+        if (gain)
+            hipLaunchKernelGGL(norm_chunk_kernel, dim3(T, nch), dim3(256), 0, st, d, x, ssq, nch, gain, eps, a_hi,
+                               a_lo, a_f32);
+        return;
+    }
     const int nv = d / 4;
     const int vpt = (nv + 255) / 256;
 #define RN(V) hipLaunchKernelGGL(residual_norm_kernel<V>, dim3(T), dim3(256), 0, st, mode, d, x, tok, \
@@ -124,11 +194,12 @@ __global__ void __launch_bounds__(256) rope_kv_kernel(
     int max_seq, int ring) {
     const int t = blockIdx.x;
     const int qd = nh * hd, kvd = nkv * hd;
-    const int npairs = (qd + 2 * kvd) / 2;
+    const int npairs = (qd + 2 * kvd) / 2;  // one pair per thread over a (row, chunk) grid
     const int p = pos[t];
     const int s = ring ? p % max_seq : p;
     const size_t slot_base = (size_t)slot[t] * nkv;
-    for (int pi = threadIdx.x; pi < npairs; pi += blockDim.x) {
+    const int pi = blockIdx.y * blockDim.x + threadIdx.x;
+    if (pi < npairs) {
         const int col = 2 * pi;
         const size_t off = (size_t)t * qkv.ld + col;
         const float2 e = *reinterpret_cast<const float2 *>(qkv.p + off);
@@ -161,8 +232,9 @@ void launch_rope_kv(hipStream_t st, int T, Partials qkv, const float *bq, const 
                     const float *bv, const float2 *tab, const int32_t *pos, const int32_t *slot,
                     int nh, int nkv, int hd, float *q_out, float *kc, float *vc, int max_seq, int ring) {
     if (T <= 0) return;
-    hipLaunchKernelGGL(rope_kv_kernel, dim3(T), dim3(256), 0, st, qkv, bq, bk, bv, tab, pos, slot, nh,
-                       nkv, hd, q_out, kc, vc, max_seq, ring);
+    const int npairs = (nh + 2 * nkv) * hd / 2;
+    hipLaunchKernelGGL(rope_kv_kernel, dim3(T, (npairs + 255) / 256), dim3(256), 0, st, qkv, bq, bk, bv, tab, pos,
+                       slot, nh, nkv, hd, q_out, kc, vc, max_seq, ring);
 }
 
 // ---- SwiGLU activation -----------------------------------------------------

@@ -37,6 +37,11 @@ struct GemvParams {
 
 constexpr int ROWS_PER_BLOCK = 128;
 
+// 16 bytes (8 bf16) of a weight row.  (Non-temporal loads were measured slower
+// here: a row's 128-byte line is read in 32-byte pieces by several
+// instructions, and without L2 allocation it is fetched more than once.)
+__device__ __forceinline__ u32x4 load_w16(const u16 *p) { return *reinterpret_cast<const u32x4 *>(p); }
+
 template <int NT, int J>
 __global__ void __launch_bounds__(256) gemv_kernel(GemvParams p) {
     extern __shared__ uint4 lds[];   // [kc/8][16*NT] chunks of 8 bf16
@@ -57,7 +62,6 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemvParams p) {
 
     // weight rows of this lane (clamped; stores are masked)
     const u16 *wrow[2];
-    int nrow[2];
 #pragma unroll
     for (int rt = 0; rt < 2; rt++) {
         const int n = blockIdx.x * ROWS_PER_BLOCK + wv * 32 + rt * 16 + r;
@@ -67,7 +71,6 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemvParams p) {
         if (p.nseg > 1 && nn >= p.seg_end[0]) { wp = p.w[1]; start = p.seg_end[0]; }
         if (p.nseg > 2 && nn >= p.seg_end[1]) { wp = p.w[2]; start = p.seg_end[1]; }
         wrow[rt] = wp + wofs + (size_t)(nn - start) * p.K;
-        nrow[rt] = n;
     }
 
     const int kbeg = blockIdx.y * p.kps;
@@ -80,12 +83,11 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemvParams p) {
 
     if (kbeg < kend) {
         const int nsteps = (kend - kbeg) / (32 * J);
-        uint4 a[2][J], an[2][J];
+        u32x4 a[2][J], an[2][J];
 #pragma unroll
         for (int rt = 0; rt < 2; rt++)
 #pragma unroll
-            for (int j = 0; j < J; j++)
-                a[rt][j] = *reinterpret_cast<const uint4 *>(wrow[rt] + kbeg + c * 8 * J + j * 8);
+            for (int j = 0; j < J; j++) a[rt][j] = load_w16(wrow[rt] + kbeg + c * 8 * J + j * 8);
 
         int chunk0 = kbeg;
         for (int st = 0; st < nsteps; st++) {
@@ -114,7 +116,7 @@ __global__ void __launch_bounds__(256) gemv_kernel(GemvParams p) {
                 for (int rt = 0; rt < 2; rt++)
 #pragma unroll
                     for (int j = 0; j < J; j++)
-                        an[rt][j] = *reinterpret_cast<const uint4 *>(wrow[rt] + kn + c * 8 * J + j * 8);
+                        an[rt][j] = load_w16(wrow[rt] + kn + c * 8 * J + j * 8);
             }
             const int ch0 = (k0 - chunk0) / 8 + c * J;
 #pragma unroll
@@ -198,12 +200,25 @@ void launch_common(hipStream_t st, GemvParams &p, int ksplit, int B_for_tiles, i
 
 }  // namespace
 
+int num_cus() {
+    static int n = 0;
+    if (!n) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+    }
+    return n;
+}
+
+int gemv_max_splits(int K) { return K / 256 > 0 ? K / 256 : 1; }
+
 int gemv_splits(int N, int K, int B) {
     (void)B;
     const int tiles = (N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
     const int target = 1024;  // ~4 blocks per CU on 256 CUs
     int s = (target + tiles - 1) / tiles;
-    const int maxs = K / 256 > 0 ? K / 256 : 1;
+    const int maxs = gemv_max_splits(K);
     if (s > maxs) s = maxs;
     if (s < 1) s = 1;
     const int g = 32 * pick_j(K);

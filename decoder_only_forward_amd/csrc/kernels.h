@@ -26,11 +26,13 @@ struct WSeg {
 //   mode EMBED:  x = widen(E[tok[t]])
 //   otherwise:   x += sum of `add` splits (if any) + sum_j moe_w[t][j]*moe_y[t][j] (if any)
 // then a = x / sqrt(mean(x^2)+eps) * gain written as bf16 (hi, lo) and/or fp32.
+// ssq: scratch of T*ceil(d/1024) floats, used to split the work over columns
+// when there are few rows (may be null: one block per row).
 enum { RN_EMBED = 0, RN_ADD = 1 };
 void launch_residual_norm(hipStream_t st, int mode, int T, int d, float *x, const int32_t *tok,
                           const void *embed, int embed_f32, Partials add, const float *moe_y,
                           const float *moe_w, int k, const float *gain, float eps, u16 *a_hi,
-                          u16 *a_lo, float *a_f32, float *cap);
+                          u16 *a_lo, float *a_f32, float *cap, float *ssq);
 
 // cos/sin of pos[t] * theta^(-2i/hd) for pair i, formed in double: tab[t][i].
 void launch_rope_table(hipStream_t st, const int32_t *pos, int T, int hd, double theta, float2 *tab);
@@ -51,6 +53,8 @@ void launch_argmax(hipStream_t st, const float *logits, int B, int V, int32_t *o
 // Decode projection, bf16 weights: out[s][b][n] = sum over split s's K range of
 // W[n][k] * (a_hi[b][k] + a_lo[b][k]); 1 <= B <= 64.  Returns the split count used.
 int gemv_splits(int N, int K, int B);
+int gemv_max_splits(int K);   // upper bound of gemv_splits (host-only, for the workspace plan)
+int num_cus();
 void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi, const u16 *a_lo,
                  int lda, int B, float *out, int ksplit, size_t split_stride, int ldo);
 
@@ -65,7 +69,7 @@ void launch_gemm_f32(hipStream_t st, const WSeg *segs, int nseg, int K, const fl
 // Split-KV decode attention.  Row b: query q[b][nh*hd], slot slot[b], position
 // pos[b]; keys/values of positions [lo, pos] in the layer cache.  Writes the
 // attention output as bf16 (hi, lo) and/or fp32 rows [B][nh*hd].
-int attn_decode_splits(int B, int nkv, int readable);
+int attn_decode_splits(int B, int nkv, int readable, int hd, int G);
 void launch_attn_decode(hipStream_t st, int B, const float *q, const float *kc, const float *vc,
                         const int32_t *pos, const int32_t *slot, int nh, int nkv, int hd,
                         int max_seq, int window, int splits, float *part, u16 *o_hi, u16 *o_lo,

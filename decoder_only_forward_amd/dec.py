@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(HERE, "libdec.so")
 DEC_OK, DEC_ERR_INVALID, DEC_ERR_RANGE, DEC_ERR_NOMEM, DEC_ERR_DEVICE, DEC_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 DEC_K_GEMV, DEC_K_ATTN_DECODE, DEC_K_GEMM, DEC_K_ATTN_PREFILL = 0, 1, 2, 3
 EXPORTS = ("dec_workspace_bytes", "dec_create", "dec_destroy", "dec_prefill", "dec_decode", "dec_kv_reset",
-           "dec_kv_length", "dec_greedy", "dec_sync", "dec_set_capture", "dec_timing_enable",
+           "dec_graph_count", "dec_kv_length", "dec_greedy", "dec_sync", "dec_set_capture", "dec_timing_enable",
            "dec_timing_read", "dec_status_str")
 
 
@@ -88,6 +88,8 @@ def load():
     L.dec_timing_read.restype = c_int
     L.dec_timing_read.argtypes = [vp, c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64),
                                   ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    L.dec_graph_count.restype = c_int
+    L.dec_graph_count.argtypes = [vp]
     L.dec_status_str.restype = ctypes.c_char_p
     L.dec_status_str.argtypes = [c_int]
     _lib = L
@@ -196,6 +198,9 @@ class DecModel:
         if r < 0:
             raise DecError(r, "dec_kv_length")
         return r
+
+    def graph_count(self) -> int:
+        return self.L.dec_graph_count(self.h)
 
     def sync(self):
         self._check(self.L.dec_sync(self.h), "dec_sync")

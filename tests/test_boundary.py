@@ -25,7 +25,7 @@ def test_header_exports_are_all_present():
     L = _lib()
     with open(os.path.join(ROOT, "include", "dec.h")) as f:
         names = re.findall(r"DEC_API\s+[\w\s\*]*?\b(dec_\w+)\s*\(", f.read())
-    assert len(names) >= 13 and set(D.EXPORTS) <= set(names)
+    assert len(names) >= 14 and set(D.EXPORTS) <= set(names)
     for n in names:
         assert hasattr(L, n), n
 

@@ -141,3 +141,35 @@ def test_smollm2_decode_b32():
             check_logits(g[b], r["logits"][b], f"row {b} step {s}")
             check_argmax(g[b], r["logits"][b], f"row {b} step {s}")
         nxt = [int(np.argmax(r["logits"][b])) for b in range(B)]
+
+
+def test_decode_graph_replay_is_bit_identical_to_eager():
+    """Decode steps replayed from a captured HIP graph give exactly the logits of
+    eager launches (the capture of test hidden states forces the eager path)."""
+    cfg = configs.SMOLLM2
+    B, P = 4, 6
+    w = synth.make_weights(cfg)
+    from parity_util import to_device
+    from decoder_only_forward_amd.dec import DecModel
+    wd = to_device(w)
+    pr = synth.prompts(cfg, B, P)
+    teach = synth.prompts(cfg, B, 5, stream=synth.TEACHER_STREAM)
+    outs = []
+    for eager in (True, False):
+        m = DecModel(cfg, wd, max_batch=B, max_prefill=P)
+        for b in range(B):
+            m.prefill(pr[b].tolist(), seq=b)
+        if eager:  # capture buffers hold B rows: set after the P-row prefills
+            hid = torch.empty((cfg.n_layers + 1, B, cfg.hidden), device="cuda")
+            m.set_capture(hid)
+        lg = torch.empty((B, cfg.vocab), device="cuda")
+        steps = []
+        for s in range(5):
+            m.decode(teach[:, s].tolist(), [P + s] * B, logits=lg)
+            steps.append(lg.cpu().numpy().copy())
+        outs.append(steps)
+        if not eager:
+            assert m.graph_count() >= 1
+        m.close()
+    for s in range(5):
+        assert np.array_equal(outs[0][s], outs[1][s]), f"step {s}"
