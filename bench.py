@@ -27,12 +27,38 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# HBM bytes per launch of the dominant decode kernel, from two rocprofv3 --pmc
+# passes (FETCH_SIZE, WRITE_SIZE) scaled by what the same counters read for a
+# 1 GiB device copy (x2.000 and x1.000): reported only while the kernel's
+# sources hash to the ones profiled, and only for the profiled workload.
+MEASURED_TRAFFIC = {
+    "attn_decode_kernel": {
+        "sources": {"decoder_only_forward_amd/csrc/k_attn_decode.hip":
+                    "3973c3fb7acf28bdc0469bb4333b49b2cce242d0c3073767b833c55d34787b4c",
+                    "decoder_only_forward_amd/csrc/common.h":
+                    "394ed98a1109455d98e2b24652372937a85b2028e1e5c3ff1d6749474c8ff8b6"},
+        "workload": ("mistral-7b", 32, 4096),
+        "bytes_per_launch": 1078641238,
+    },
+}
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode tok/s + prefill tok/s (Mistral-7B shape) and % of HBM / MFMA roofline"
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def measured_traffic(kernel, workload):
+    import hashlib
+    m = MEASURED_TRAFFIC.get(kernel)
+    if not m or m["workload"] != workload:
+        return None
+    for rel, sha in m["sources"].items():
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() != sha:
+                return None
+    return m["bytes_per_launch"]
 
 
 def cpu_baseline(cfg, wd, steps=4):
@@ -66,6 +92,8 @@ def main():
     ap.add_argument("--prompt", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=32)
+    ap.add_argument("--pmc-calibration", action="store_true",
+                    help="only run three 1 GiB device-to-device copies (PMC byte-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
@@ -76,6 +104,16 @@ def main():
     import torch
     from decoder_only_forward_amd import configs, synth
     from decoder_only_forward_amd import dec as D
+
+    if args.pmc_calibration:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)  # one kernel: 1 GiB read, 1 GiB written
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30, "launches": 3}))
+        return
 
     cfg = configs.CONFIGS[args.config]
     B, P = args.batch, args.prompt
@@ -207,6 +245,11 @@ def main():
     }
     if out["roofline"] is not None:
         out["roofline"]["kernel"] = "attn_decode_kernel (split-KV GQA decode attention)"
+        tr = measured_traffic("attn_decode_kernel", (cfg.name, B, P))
+        out["roofline"]["traffic"] = None if tr is None else round(tr / 1e9, 4)
+        out["roofline"]["traffic_unit"] = "GB per launch (rocprofv3 PMC)"
+        out["roofline"]["algorithmic_bytes_per_launch_gb"] = round(
+            attn_t["bytes"] / attn_t["launches"] / 1e9, 4)
     if not args.no_cpu_baseline:
         try:
             out["cpu_baseline"] = cpu_baseline(cfg, wd, args.cpu_steps)
