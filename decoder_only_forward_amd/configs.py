@@ -39,6 +39,17 @@ class ModelConfig:
     weight_dtype: int = WEIGHT_BF16
     rms_eps: float = 1e-5
     rope_theta: float = 10000.0
+    # RoPE variants (rml "The decoder", "Rotary embeddings"): pairing 0 rotates
+    # adjacent elements (2i, 2i+1), 1 rotates halves (i, i + hd/2); scaling 1 is
+    # llama3 frequency scaling with these parameters.
+    rope_pairing: int = 0
+    rope_scaling: int = 0
+    rope_factor: float = 8.0
+    rope_low_freq_factor: float = 1.0
+    rope_high_freq_factor: float = 4.0
+    rope_orig_ctx: int = 8192
+    # K/V cache element type: False = fp32, True = bf16 (rounded to nearest even).
+    kv_bf16: bool = False
 
     @property
     def q_dim(self) -> int:
@@ -93,6 +104,11 @@ TINY_WINDOW = TINY.replace(name="tiny-window", sliding_window=5, max_seq=5)
 TINY_MOE = TINY.replace(name="tiny-moe", n_experts=8, top_k=2)
 TINY_BIAS = TINY.replace(name="tiny-bias", qkv_bias=True, tied_embedding=True)
 TINY_BF16 = TINY.replace(name="tiny-bf16", weight_dtype=WEIGHT_BF16, ffn_dim=192)
+# llama3 scaling with a context short enough that all three frequency bands occur
+TINY_LLAMA3 = TINY.replace(name="tiny-llama3", rope_scaling=1, rope_factor=8.0, rope_low_freq_factor=1.0,
+                           rope_high_freq_factor=4.0, rope_orig_ctx=64)
+TINY_HALF = TINY.replace(name="tiny-half", rope_pairing=1)
+TINY_KVBF16 = TINY_BF16.replace(name="tiny-kvbf16", kv_bf16=True)
 
 
 def one_layer(cfg: ModelConfig) -> ModelConfig:

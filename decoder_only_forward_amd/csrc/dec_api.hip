@@ -170,6 +170,14 @@ int validate_cfg(const dec_config *c) {
     if (c->sliding_window < 0 || (c->sliding_window > 0 && c->max_seq > c->sliding_window)) return DEC_ERR_INVALID;
     if (c->weight_dtype != DEC_WEIGHT_BF16 && c->weight_dtype != DEC_WEIGHT_F32) return DEC_ERR_INVALID;
     if (c->qkv_bias != 0 && c->qkv_bias != 1) return DEC_ERR_INVALID;
+    if (c->rope_pairing != DEC_ROPE_ADJACENT && c->rope_pairing != DEC_ROPE_HALF) return DEC_ERR_INVALID;
+    if (c->rope_scaling != DEC_ROPE_PLAIN && c->rope_scaling != DEC_ROPE_LLAMA3) return DEC_ERR_INVALID;
+    if (c->rope_scaling == DEC_ROPE_LLAMA3 &&
+        (!(c->rope_factor > 0) || !(c->rope_low_freq_factor > 0) ||
+         !(c->rope_high_freq_factor > c->rope_low_freq_factor) || c->rope_orig_ctx <= 0))
+        return DEC_ERR_INVALID;
+    if (c->kv_dtype != DEC_KV_F32 && c->kv_dtype != DEC_KV_BF16) return DEC_ERR_INVALID;
+    if (c->kv_dtype == DEC_KV_BF16) return DEC_ERR_UNSUPPORTED;
     // shapes the kernels are written for
     if (c->max_batch > 64) return DEC_ERR_UNSUPPORTED;
     if (c->head_dim != 16 && c->head_dim != 64 && c->head_dim != 128) return DEC_ERR_UNSUPPORTED;
@@ -320,7 +328,8 @@ void run_pass(dec_model *m, const Pass &ps) {
 
     launch_residual_norm(st, RN_EMBED, T, d, m->x, m->tok, m->embed, f32w, Partials{nullptr, 0, 0, 0}, nullptr,
                          nullptr, 0, m->L[0].attn_norm, eps, ah, al, af, caph(0), m->ssq);
-    launch_rope_table(st, m->pos, T, hd, c.rope_theta, m->rope);
+    launch_rope_table(st, m->pos, T, hd, c.rope_theta, c.rope_scaling, c.rope_factor, c.rope_low_freq_factor,
+                      c.rope_high_freq_factor, c.rope_orig_ctx, m->rope);
 
     for (int l = 0; l < c.n_layers; l++) {
         const dec_layer_weights &w = m->L[l];
@@ -330,8 +339,8 @@ void run_pass(dec_model *m, const Pass &ps) {
         WSeg qkv[3] = {{w.wq, qd}, {w.wk, kvd}, {w.wv, kvd}};
         Partials pq = proj(m, qkv, 3, d, T, ah, al, af, d);
         launch_rope_kv(st, T, pq, c.qkv_bias ? w.bq : nullptr, c.qkv_bias ? w.bk : nullptr,
-                       c.qkv_bias ? w.bv : nullptr, m->rope, m->pos, m->slot, nh, nkv, hd, m->q, kc, vc,
-                       c.max_seq, m->ring);
+                       c.qkv_bias ? w.bv : nullptr, m->rope, m->pos, m->slot, nh, nkv, hd, c.rope_pairing, m->q, kc,
+                       vc, c.max_seq, m->ring);
         // attention -> a (row stride qd)
         if (ps.decode) {
             const int S = attn_splits_for(m, T, ps.hpos);

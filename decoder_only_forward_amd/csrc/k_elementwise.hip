@@ -164,77 +164,99 @@ void launch_residual_norm(hipStream_t st, int mode, int T, int d, float *x, cons
 }
 
 // ---- RoPE ------------------------------------------------------------------
-// Pair i of a head turns theta^(-2i/hd) radians per position (rml "The
-// decoder", section "Rotary embeddings"); the angle and its cos/sin are formed
-// in double once per (position, pair) and shared by every head.
-__global__ void rope_table_kernel(const int32_t *__restrict__ pos, int T, int hd, double theta,
-                                  float2 *__restrict__ tab) {
+// Pair i of a head turns f_i = theta^(-2i/hd) radians per position (rml "The
+// decoder", section "Rotary embeddings"); with llama3 scaling (same section and
+// its worked example) slow pairs are stretched: a wavelength 2*pi/f_i under
+// orig_ctx/high keeps f_i, over orig_ctx/low takes f_i/factor, and in between
+// s = (orig_ctx/wavelength - low)/(high - low) mixes (1 - s) f_i/factor + s f_i.
+// The angle and its cos/sin are formed in double once per (position, pair) and
+// shared by every head.
+__global__ void rope_table_kernel(const int32_t *__restrict__ pos, int T, int hd, double theta, int scaling,
+                                  double factor, double low, double high, int orig_ctx, float2 *__restrict__ tab) {
     const int half = hd / 2;
     const int idx = blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= T * half) return;
     const int t = idx / half, i = idx % half;
-    const double ang = (double)pos[t] * pow(theta, -2.0 * (double)i / (double)hd);
+    double f = pow(theta, -2.0 * (double)i / (double)hd);
+    if (scaling == 1) {
+        const double wl = 6.283185307179586476925 / f;
+        const double lo_wl = (double)orig_ctx / low, hi_wl = (double)orig_ctx / high;
+        if (wl > lo_wl) {
+            f = f / factor;
+        } else if (wl >= hi_wl) {
+            const double sm = ((double)orig_ctx / wl - low) / (high - low);
+            f = (1.0 - sm) * (f / factor) + sm * f;
+        }
+    }
+    const double ang = (double)pos[t] * f;
     tab[idx] = make_float2((float)cos(ang), (float)sin(ang));
 }
 
-void launch_rope_table(hipStream_t st, const int32_t *pos, int T, int hd, double theta, float2 *tab) {
+void launch_rope_table(hipStream_t st, const int32_t *pos, int T, int hd, double theta, int scaling,
+                       double factor, double low, double high, int orig_ctx, float2 *tab) {
     const int n = T * (hd / 2);
     if (n <= 0) return;
-    hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, pos, T, hd, theta, tab);
+    hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, st, pos, T, hd, theta, scaling,
+                       factor, low, high, orig_ctx, tab);
 }
 
-// Adjacent pairs (2i, 2i+1) rotate as (e0 c - e1 s, e0 s + e1 c) (sipllm
-// "Transformer forward pass", section "RoPE is adjacent-pair").  K and V go to
-// the cache slot of the position (Pantheon, "Sliding Window (Mistral)": write at
-// pos % max_seq when the cache is a ring).
+// Pairs rotate as (e0 c - e1 s, e0 s + e1 c): adjacent elements (2i, 2i+1)
+// (sipllm "Transformer forward pass", section "RoPE is adjacent-pair") or
+// halves (i, i + hd/2) (rml "Which dimensions pair").  K and V go to the cache
+// slot of the position (Pantheon, "Sliding Window (Mistral)": write at
+// pos % max_seq when the cache is a ring).  One thread per pair of a row.
 __global__ void __launch_bounds__(256) rope_kv_kernel(
     Partials qkv, const float *__restrict__ bq, const float *__restrict__ bk, const float *__restrict__ bv,
     const float2 *__restrict__ tab, const int32_t *__restrict__ pos, const int32_t *__restrict__ slot,
-    int nh, int nkv, int hd, float *__restrict__ q_out, float *__restrict__ kc, float *__restrict__ vc,
-    int max_seq, int ring) {
+    int nh, int nkv, int hd, int pairing, float *__restrict__ q_out, float *__restrict__ kc,
+    float *__restrict__ vc, int max_seq, int ring) {
     const int t = blockIdx.x;
-    const int qd = nh * hd, kvd = nkv * hd;
-    const int npairs = (qd + 2 * kvd) / 2;  // one pair per thread over a (row, chunk) grid
+    const int qd = nh * hd, kvd = nkv * hd, half = hd / 2;
+    const int npairs = (qd + 2 * kvd) / 2;
+    const int pi = blockIdx.y * blockDim.x + threadIdx.x;
+    if (pi >= npairs) return;
     const int p = pos[t];
     const int s = ring ? p % max_seq : p;
     const size_t slot_base = (size_t)slot[t] * nkv;
-    const int pi = blockIdx.y * blockDim.x + threadIdx.x;
-    if (pi < npairs) {
-        const int col = 2 * pi;
-        const size_t off = (size_t)t * qkv.ld + col;
-        const float2 e = *reinterpret_cast<const float2 *>(qkv.p + off);
-        float e0 = e.x, e1 = e.y;
-        for (int sp = 1; sp < qkv.S; sp++) {
-            const float2 u = *reinterpret_cast<const float2 *>(qkv.p + sp * qkv.stride + off);
-            e0 += u.x; e1 += u.y;
-        }
-        if (col < qd) {
-            if (bq) { e0 += bq[col]; e1 += bq[col + 1]; }
-            const float2 cs = tab[(size_t)t * (hd / 2) + (col % hd) / 2];
-            *reinterpret_cast<float2 *>(q_out + (size_t)t * qd + col) =
-                make_float2(e0 * cs.x - e1 * cs.y, e0 * cs.y + e1 * cs.x);
-        } else if (col < qd + kvd) {
-            const int c = col - qd;
-            if (bk) { e0 += bk[c]; e1 += bk[c + 1]; }
-            const float2 cs = tab[(size_t)t * (hd / 2) + (c % hd) / 2];
-            const size_t dst = ((slot_base + c / hd) * max_seq + s) * hd + c % hd;
-            *reinterpret_cast<float2 *>(kc + dst) = make_float2(e0 * cs.x - e1 * cs.y, e0 * cs.y + e1 * cs.x);
-        } else {
-            const int c = col - qd - kvd;
-            if (bv) { e0 += bv[c]; e1 += bv[c + 1]; }
-            const size_t dst = ((slot_base + c / hd) * max_seq + s) * hd + c % hd;
-            *reinterpret_cast<float2 *>(vc + dst) = make_float2(e0, e1);
-        }
+    // section, head and pair index within the head
+    int base, i;
+    if (pi < qd / 2) { base = 0; i = pi; }
+    else if (pi < (qd + kvd) / 2) { base = qd; i = pi - qd / 2; }
+    else { base = qd + kvd; i = pi - (qd + kvd) / 2; }
+    const int head = i / half, ip = i % half;
+    const bool rotate = base < qd + kvd;
+    const int e0c = head * hd + ((rotate && pairing) ? ip : 2 * ip);
+    const int e1c = head * hd + ((rotate && pairing) ? ip + half : 2 * ip + 1);
+    const size_t off = (size_t)t * qkv.ld + base;
+    float e0 = sum_splits(qkv.p, qkv.S, qkv.stride, off + e0c);
+    float e1 = sum_splits(qkv.p, qkv.S, qkv.stride, off + e1c);
+    const float *bias = base == 0 ? bq : (base == qd ? bk : bv);
+    if (bias) { e0 += bias[e0c]; e1 += bias[e1c]; }
+    if (rotate) {
+        const float2 cs = tab[(size_t)t * half + ip];
+        const float r0 = e0 * cs.x - e1 * cs.y, r1 = e0 * cs.y + e1 * cs.x;
+        e0 = r0;
+        e1 = r1;
+    }
+    if (base == 0) {
+        q_out[(size_t)t * qd + e0c] = e0;
+        q_out[(size_t)t * qd + e1c] = e1;
+    } else {
+        float *cache = base == qd ? kc : vc;
+        const size_t dst = ((slot_base + head) * max_seq + s) * hd;
+        cache[dst + e0c - head * hd] = e0;
+        cache[dst + e1c - head * hd] = e1;
     }
 }
 
 void launch_rope_kv(hipStream_t st, int T, Partials qkv, const float *bq, const float *bk,
                     const float *bv, const float2 *tab, const int32_t *pos, const int32_t *slot,
-                    int nh, int nkv, int hd, float *q_out, float *kc, float *vc, int max_seq, int ring) {
+                    int nh, int nkv, int hd, int pairing, float *q_out, float *kc, float *vc, int max_seq,
+                    int ring) {
     if (T <= 0) return;
     const int npairs = (nh + 2 * nkv) * hd / 2;
     hipLaunchKernelGGL(rope_kv_kernel, dim3(T, (npairs + 255) / 256), dim3(256), 0, st, qkv, bq, bk, bv, tab, pos,
-                       slot, nh, nkv, hd, q_out, kc, vc, max_seq, ring);
+                       slot, nh, nkv, hd, pairing, q_out, kc, vc, max_seq, ring);
 }
 
 // ---- SwiGLU activation -----------------------------------------------------

@@ -34,14 +34,18 @@ void launch_residual_norm(hipStream_t st, int mode, int T, int d, float *x, cons
                           const float *moe_w, int k, const float *gain, float eps, u16 *a_hi,
                           u16 *a_lo, float *a_f32, float *cap, float *ssq);
 
-// cos/sin of pos[t] * theta^(-2i/hd) for pair i, formed in double: tab[t][i].
-void launch_rope_table(hipStream_t st, const int32_t *pos, int T, int hd, double theta, float2 *tab);
+// cos/sin of pos[t] * f_i for pair i, f_i = theta^(-2i/hd) (llama3-scaled when
+// scaling == 1), formed in double: tab[t][i].
+void launch_rope_table(hipStream_t st, const int32_t *pos, int T, int hd, double theta, int scaling,
+                       double factor, double low, double high, int orig_ctx, float2 *tab);
 
 // q/k/v (+bias) -> RoPE on q and k -> q_out [T][q_dim]; k, v stored in the
 // layer's cache [slot][kvh][max_seq][hd] at position pos % max_seq (ring) or pos.
+// pairing 0 rotates elements (2i, 2i+1) of a head, 1 rotates (i, i + hd/2).
 void launch_rope_kv(hipStream_t st, int T, Partials qkv, const float *bq, const float *bk,
                     const float *bv, const float2 *tab, const int32_t *pos, const int32_t *slot,
-                    int nh, int nkv, int hd, float *q_out, float *kc, float *vc, int max_seq, int ring);
+                    int nh, int nkv, int hd, int pairing, float *q_out, float *kc, float *vc, int max_seq,
+                    int ring);
 
 // act[t][j] = silu(g) * u with g = gu(t, j), u = gu(t, F + j); written as bf16
 // (hi, lo) and/or fp32 with row stride F.

@@ -29,7 +29,9 @@ class DecConfig(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32)] + [(n, ctypes.c_int32) for n in (
         "n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab", "n_experts", "top_k",
         "qkv_bias", "tied_embedding", "sliding_window", "max_seq", "max_batch", "max_prefill",
-        "weight_dtype")] + [("rms_eps", ctypes.c_double), ("rope_theta", ctypes.c_double)]
+        "weight_dtype")] + [("rms_eps", ctypes.c_double), ("rope_theta", ctypes.c_double)] + [
+        (n, ctypes.c_int32) for n in ("rope_pairing", "rope_scaling", "rope_orig_ctx", "kv_dtype")] + [
+        (n, ctypes.c_double) for n in ("rope_factor", "rope_low_freq_factor", "rope_high_freq_factor")]
 
 
 class DecLayerWeights(ctypes.Structure):
@@ -101,7 +103,8 @@ def make_config(cfg: ModelConfig, max_batch: int, max_prefill: int, max_seq: Opt
                      cfg.head_dim, cfg.ffn_dim, cfg.vocab, cfg.n_experts, cfg.top_k, int(cfg.qkv_bias),
                      int(cfg.tied_embedding), cfg.sliding_window, cfg.max_seq if max_seq is None else max_seq,
                      max_batch, max_prefill, 1 if cfg.weight_dtype == WEIGHT_F32 else 0, cfg.rms_eps,
-                     cfg.rope_theta)
+                     cfg.rope_theta, cfg.rope_pairing, cfg.rope_scaling, cfg.rope_orig_ctx, int(cfg.kv_bf16),
+                     cfg.rope_factor, cfg.rope_low_freq_factor, cfg.rope_high_freq_factor)
 
 
 def workspace_bytes(cfg: ModelConfig, max_batch: int, max_prefill: int, max_seq: Optional[int] = None) -> int:

@@ -50,6 +50,9 @@ enum {
 };
 
 enum { DEC_WEIGHT_BF16 = 0, DEC_WEIGHT_F32 = 1 };
+enum { DEC_ROPE_ADJACENT = 0, DEC_ROPE_HALF = 1 };
+enum { DEC_ROPE_PLAIN = 0, DEC_ROPE_LLAMA3 = 1 };
+enum { DEC_KV_F32 = 0, DEC_KV_BF16 = 1 };
 
 /*
  * Model configuration: the base recipe plus switches (rml "The decoder",
@@ -84,6 +87,20 @@ typedef struct dec_config {
     int32_t weight_dtype;      /* DEC_WEIGHT_BF16 or DEC_WEIGHT_F32 */
     double rms_eps;
     double rope_theta;
+    /* RoPE variants (rml "The decoder", section "Rotary embeddings"):
+       rope_pairing DEC_ROPE_ADJACENT rotates elements (2i, 2i+1) of a head,
+       DEC_ROPE_HALF rotates (i, i + head_dim/2); rope_scaling DEC_ROPE_LLAMA3
+       applies llama3 frequency scaling: pairs whose wavelength 2*pi/f is under
+       orig_ctx/high_freq_factor keep f, those over orig_ctx/low_freq_factor use
+       f/factor, and between them s = (orig_ctx/wavelength - low)/(high - low)
+       gives (1 - s) f/factor + s f. */
+    int32_t rope_pairing;
+    int32_t rope_scaling;
+    int32_t rope_orig_ctx;
+    int32_t kv_dtype;          /* DEC_KV_F32 or DEC_KV_BF16 (K/V rounded to nearest even when stored) */
+    double rope_factor;
+    double rope_low_freq_factor;
+    double rope_high_freq_factor;
 } dec_config;
 
 /*

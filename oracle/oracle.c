@@ -17,7 +17,10 @@
  *   - RMSNorm: Pantheon, section "RMSNorm";
  *   - RoPE on adjacent pairs (2i, 2i+1), pair i turning theta^(-2i/head_dim)
  *     rad per position: sipllm, "RoPE is adjacent-pair"; rml "The decoder",
- *     "Rotary embeddings";
+ *     "Rotary embeddings"; the halves pairing (i, i + hd/2) and llama3
+ *     frequency scaling as described there ("Which dimensions pair", worked
+ *     example of the scaling);
+ *   - optional bf16 K/V cache (rml, "Attend": the cache stores its dtype);
  *   - GQA head map h -> h*n_kv/n_head: Pantheon, "Grouped Query Attention";
  *   - attention as materialised scores, softmax, weighted sum (rml's AttendRef,
  *     "Attend"); window start max(0, pos-W+1): rml, "Attend";
@@ -65,6 +68,13 @@ typedef struct {
        using a ring; a second code path that exists only to pin the ring. */
     int32_t window_by_mask;
     double rms_eps, rope_theta;
+    /* RoPE variants: pairing 0 = adjacent (2i, 2i+1), 1 = halves (i, i + hd/2);
+       scaling 0 = none, 1 = llama3 frequency scaling with factor, low/high
+       frequency factors and original context. */
+    int32_t rope_pairing, rope_scaling, rope_orig_ctx;
+    /* 1: K and V are rounded to bf16 (nearest even) when stored in the cache. */
+    int32_t kv_bf16;
+    double rope_factor, rope_low_freq_factor, rope_high_freq_factor;
 } ocfg;
 
 typedef struct {
@@ -117,20 +127,53 @@ EXPORT void SYM(rmsnorm)(const real *x, const float *g, int d, double eps, real 
     for (int i = 0; i < d; i++) out[i] = x[i] * r * (real)g[i];
 }
 
-/* Rotate adjacent pairs of each of n_heads heads of h[n_heads*hd] in place.
-   Angle of pair i at `pos` = pos * theta^(-2i/hd), formed in double. */
-EXPORT void SYM(rope)(real *h, int n_heads, int hd, int pos, double theta) {
+/* llama3 frequency scaling of one pair's frequency (rml "The decoder",
+   "Rotary embeddings" and its worked example): with wavelength 2*pi/f, pairs
+   under orig_ctx/high keep f, pairs over orig_ctx/low turn `factor` times
+   slower, and in between smooth = (orig_ctx/wavelength - low) / (high - low)
+   blends (1 - smooth) * f/factor + smooth * f. */
+EXPORT double SYM(llama3_inv_freq)(double f, double factor, double low, double high, int orig_ctx) {
+    const double pi = 3.14159265358979323846;
+    double wavelen = 2.0 * pi / f;
+    if (wavelen < (double)orig_ctx / high) return f;
+    if (wavelen > (double)orig_ctx / low) return f / factor;
+    double smooth = ((double)orig_ctx / wavelen - low) / (high - low);
+    return (1.0 - smooth) * (f / factor) + smooth * f;
+}
+
+/* Rotate the pairs of each of n_heads heads of h[n_heads*hd] in place.  Pair i
+   turns pos * theta^(-2i/hd) radians (optionally llama3-scaled), angle formed in
+   double; pairing 0 rotates (2i, 2i+1), pairing 1 rotates (i, i + hd/2). */
+EXPORT void SYM(rope_ex)(real *h, int n_heads, int hd, int pos, double theta, int pairing, int scaling,
+                         double factor, double low, double high, int orig_ctx) {
     for (int i = 0; i < hd / 2; i++) {
         double inv_freq = pow(theta, -2.0 * (double)i / (double)hd);
+        if (scaling == 1) inv_freq = SYM(llama3_inv_freq)(inv_freq, factor, low, high, orig_ctx);
         double ang = (double)pos * inv_freq;
         real c = (real)cos(ang), s = (real)sin(ang);
+        int a = pairing ? i : 2 * i, b = pairing ? i + hd / 2 : 2 * i + 1;
         for (int hh = 0; hh < n_heads; hh++) {
-            real *p = h + (size_t)hh * hd + 2 * i;
-            real e0 = p[0], e1 = p[1];
-            p[0] = e0 * c - e1 * s;
-            p[1] = e0 * s + e1 * c;
+            real *p = h + (size_t)hh * hd;
+            real e0 = p[a], e1 = p[b];
+            p[a] = e0 * c - e1 * s;
+            p[b] = e0 * s + e1 * c;
         }
     }
+}
+
+/* Plain RoPE: adjacent pairs, no scaling. */
+EXPORT void SYM(rope)(real *h, int n_heads, int hd, int pos, double theta) {
+    SYM(rope_ex)(h, n_heads, hd, pos, theta, 0, 0, 1.0, 1.0, 1.0, 1);
+}
+
+/* Nearest-even bf16 of a value (through fp32), kept in the oracle's type. */
+static real bf16_round(real v) {
+    float f = (float)v;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    u = (u + 0x7FFFu + ((u >> 16) & 1u)) & 0xFFFF0000u;
+    memcpy(&f, &u, sizeof f);
+    return (real)f;
 }
 
 static inline real silu(real z) { return z / ((real)1 + R_EXP(-z)); }
@@ -212,6 +255,10 @@ static int cfg_valid(const ocfg *c) {
     if (c->n_heads % c->n_kv_heads) return 0;
     if (c->head_dim % 2) return 0;
     if (!(c->rms_eps > 0) || !(c->rope_theta > 0)) return 0;
+    if (c->rope_pairing < 0 || c->rope_pairing > 1 || c->rope_scaling < 0 || c->rope_scaling > 1) return 0;
+    if (c->rope_scaling == 1 && (!(c->rope_factor > 0) || !(c->rope_low_freq_factor > 0) ||
+                                 !(c->rope_high_freq_factor > c->rope_low_freq_factor) || c->rope_orig_ctx <= 0))
+        return 0;
     if (c->n_experts < 0 || c->n_experts > 256) return 0;
     if (c->n_experts > 0 && (c->top_k < 1 || c->top_k > c->n_experts)) return 0;
     if (c->sliding_window < 0) return 0;
@@ -310,8 +357,14 @@ static void block_kv(omodel *m, int l, int slot, int pos, const real *x, scratch
         for (int i = 0; i < kvd; i++) s->k[i] += (real)L->bk[i];
         for (int i = 0; i < kvd; i++) s->v[i] += (real)L->bv[i];
     }
-    SYM(rope)(s->q, c->n_heads, hd, pos, c->rope_theta);
-    SYM(rope)(s->k, c->n_kv_heads, hd, pos, c->rope_theta);
+    SYM(rope_ex)(s->q, c->n_heads, hd, pos, c->rope_theta, c->rope_pairing, c->rope_scaling, c->rope_factor,
+                 c->rope_low_freq_factor, c->rope_high_freq_factor, c->rope_orig_ctx);
+    SYM(rope_ex)(s->k, c->n_kv_heads, hd, pos, c->rope_theta, c->rope_pairing, c->rope_scaling, c->rope_factor,
+                 c->rope_low_freq_factor, c->rope_high_freq_factor, c->rope_orig_ctx);
+    if (c->kv_bf16) {
+        for (int i = 0; i < kvd; i++) s->k[i] = bf16_round(s->k[i]);
+        for (int i = 0; i < kvd; i++) s->v[i] = bf16_round(s->v[i]);
+    }
     int ring = c->sliding_window > 0 && !c->window_by_mask;
     int sl = ring ? pos % c->max_seq : pos;
     size_t off = (((size_t)l * c->n_slots + slot) * c->max_seq + sl) * (size_t)kvd;

@@ -38,7 +38,9 @@ class OCfg(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab",
         "n_experts", "top_k", "qkv_bias", "sliding_window", "max_seq", "n_slots", "weight_f32",
-        "window_by_mask")] + [("rms_eps", ctypes.c_double), ("rope_theta", ctypes.c_double)]
+        "window_by_mask")] + [("rms_eps", ctypes.c_double), ("rope_theta", ctypes.c_double)] + [
+        (n, ctypes.c_int32) for n in ("rope_pairing", "rope_scaling", "rope_orig_ctx", "kv_bf16")] + [
+        (n, ctypes.c_double) for n in ("rope_factor", "rope_low_freq_factor", "rope_high_freq_factor")]
 
 
 class OLayer(ctypes.Structure):
@@ -60,7 +62,8 @@ def lib(kind: str = "f32"):
                           ("prefill", ctypes.c_int), ("decode", ctypes.c_int),
                           ("length", ctypes.c_int), ("argmax", ctypes.c_int),
                           ("rmsnorm", None), ("rope", None), ("moe_route", None),
-                          ("attention_prefill", None), ("kv_row", None)):
+                          ("attention_prefill", None), ("kv_row", None), ("rope_ex", None),
+                          ("llama3_inv_freq", ctypes.c_double)):
             f = getattr(L, pre + name)
             f.restype = res
             setattr(L, name, f)
@@ -82,6 +85,11 @@ def lib(kind: str = "f32"):
                                 ctypes.c_void_p]
         L.attention_prefill.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int] * 5 + [ctypes.c_void_p]
         L.kv_row.argtypes = [ctypes.c_void_p] + [ctypes.c_int] * 4 + [ctypes.c_void_p]
+        L.rope_ex.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                              ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                              ctypes.c_int]
+        L.llama3_inv_freq.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                      ctypes.c_int]
         _loaded[kind] = L
     return _loaded[kind]
 
@@ -116,6 +124,18 @@ def rope(h, n_heads, hd, pos, theta, kind="f32"):
     h = np.array(h, dtype=dt, order="C", copy=True)
     lib(kind).rope(_ptr(h), n_heads, hd, pos, theta)
     return h
+
+
+def rope_ex(h, n_heads, hd, pos, theta, pairing=0, scaling=0, factor=8.0, low=1.0, high=4.0, orig_ctx=8192,
+            kind="f32"):
+    dt = np_dtype(kind)
+    h = np.array(h, dtype=dt, order="C", copy=True)
+    lib(kind).rope_ex(_ptr(h), n_heads, hd, pos, theta, pairing, scaling, factor, low, high, orig_ctx)
+    return h
+
+
+def llama3_inv_freq(f, factor, low, high, orig_ctx, kind="f64"):
+    return lib(kind).llama3_inv_freq(f, factor, low, high, orig_ctx)
 
 
 def moe_route(logits, k, kind="f32"):
@@ -160,7 +180,9 @@ class OracleModel:
         self.ocfg = OCfg(cfg.n_layers, cfg.hidden, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim,
                          cfg.ffn_dim, cfg.vocab, cfg.n_experts, cfg.top_k, int(cfg.qkv_bias),
                          cfg.sliding_window, ms, n_slots, int(cfg.weight_dtype == 1),
-                         int(window_by_mask), cfg.rms_eps, cfg.rope_theta)
+                         int(window_by_mask), cfg.rms_eps, cfg.rope_theta, cfg.rope_pairing, cfg.rope_scaling,
+                         cfg.rope_orig_ctx, int(cfg.kv_bf16), cfg.rope_factor, cfg.rope_low_freq_factor,
+                         cfg.rope_high_freq_factor)
         self.n_slots = n_slots
         arr = (OLayer * cfg.n_layers)()
         for i, lw in enumerate(weights["layers"]):

@@ -113,3 +113,11 @@ def test_mixtral_one_layer_prefill_512_and_decode_b16():
     cfg = configs.one_layer(configs.MIXTRAL)
     _run(cfg, P=512, B=16, steps=3, sample_rows=[0, 5, 255, 511],
          decode_rows=[0, 15], sample_steps={0, 2})
+
+
+def test_mistral_one_layer_llama3_scaling_and_half_pairing():
+    """RoPE variants at head_dim 128: llama3 frequency scaling (factor 8,
+    low/high 1/4, original context 8192) with rotate-half pairing."""
+    cfg = configs.one_layer(configs.MISTRAL).replace(name="mistral-1l-llama3-half", rope_pairing=1,
+                                                      rope_scaling=1, rope_orig_ctx=8192, rope_factor=8.0)
+    _run(cfg, P=1024, B=2, steps=3, sample_rows=[0, 511, 1023], decode_rows=[1], sample_steps={0, 2})

@@ -46,7 +46,10 @@ def _run_stream(pair, prompt, steps, what, slot=0):
 
 
 TINY_SET = [configs.TINY, configs.TINY_MOE, configs.TINY_BIAS, configs.TINY_BF16,
-            configs.TINY_BF16.replace(name="tiny-bf16-moe", n_experts=8, top_k=2)]
+            configs.TINY_BF16.replace(name="tiny-bf16-moe", n_experts=8, top_k=2),
+            configs.TINY_LLAMA3, configs.TINY_HALF,
+            configs.TINY_BF16.replace(name="tiny-bf16-llama3-half", rope_pairing=1, rope_scaling=1,
+                                      rope_orig_ctx=64)]
 
 
 @pytest.mark.parametrize("cfg", TINY_SET, ids=lambda c: c.name)

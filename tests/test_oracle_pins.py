@@ -391,3 +391,99 @@ def test_invalid_calls_change_nothing():
         np.testing.assert_array_equal(m.kv_row(0, 0, 0, p), before[p])
     m.reset(0)
     assert m.length(0) == 0
+
+
+# ---- RoPE variants (rml "The decoder", "Rotary embeddings") ----------------
+
+def test_llama3_scaling_matches_worked_example():
+    rows = _golden_rows("llama3_rope_example.txt")
+    factor, low, high, orig = float(rows[0][0]), float(rows[0][1]), float(rows[0][2]), int(rows[0][3])
+    for wl, ratio in rows[1:]:
+        f = 2 * math.pi / float(wl)
+        got = O.llama3_inv_freq(f, factor, low, high, orig)
+        assert abs(got / f - float(ratio)) < 1e-12, (wl, got / f)
+    # the blend of the example, written out: (1 - 1/3) * f/8 + 1/3 * f
+    f = 2 * math.pi / 4096
+    assert abs(O.llama3_inv_freq(f, 8, 1, 4, 8192) - ((2 / 3) * f / 8 + f / 3)) < 1e-15
+
+
+def test_llama3_scaling_with_factor_one_is_plain_rope():
+    rng = np.random.default_rng(5)
+    h = rng.standard_normal(2 * 64)
+    for pos in (0, 7, 5000):
+        a = O.rope_ex(h, 2, 64, pos, 5e5, scaling=1, factor=1.0, low=1.0, high=4.0, orig_ctx=8192, kind="f64")
+        b = O.rope_ex(h, 2, 64, pos, 5e5, kind="f64")
+        np.testing.assert_allclose(a, b, rtol=1e-12, atol=1e-12)  # the band blend rounds
+
+
+def test_half_pairing_is_adjacent_pairing_of_permuted_dims():
+    """rotate-half pairs (i, i + hd/2); permuting dims so those pairs become
+    adjacent turns it into the adjacent rotation (the GGUF row permutation the
+    sipllm and rml pages describe)."""
+    rng = np.random.default_rng(6)
+    hd, nh = 16, 3
+    perm = np.empty(hd, dtype=int)            # adjacent slot 2i <- dim i, 2i+1 <- dim i + hd/2
+    perm[0::2] = np.arange(hd // 2)
+    perm[1::2] = np.arange(hd // 2) + hd // 2
+    h = rng.standard_normal((nh, hd))
+    for kind in ("f32", "f64"):
+        for pos in (0, 1, 9, 777):
+            half = O.rope_ex(h.reshape(-1), nh, hd, pos, 1e4, pairing=1, kind=kind).reshape(nh, hd)
+            adj = O.rope_ex(h[:, perm].reshape(-1), nh, hd, pos, 1e4, pairing=0, kind=kind).reshape(nh, hd)
+            back = np.empty_like(adj)
+            back[:, perm] = adj
+            np.testing.assert_array_equal(half, back)
+
+
+def test_half_pairing_model_equals_adjacent_model_with_permuted_rows():
+    cfg = configs.TINY_HALF
+    adj = configs.TINY
+    w = synth.make_weights(cfg)
+    hd = cfg.head_dim
+    perm = np.empty(hd, dtype=int)
+    perm[0::2] = np.arange(hd // 2)
+    perm[1::2] = np.arange(hd // 2) + hd // 2
+    wa = {k: v for k, v in w.items() if k != "layers"}
+    wa["layers"] = []
+    for lw in w["layers"]:
+        m = dict(lw)
+        for role, nh in (("wq", cfg.n_heads), ("wk", cfg.n_kv_heads)):
+            rows = np.concatenate([hh * hd + perm for hh in range(nh)])
+            m[role] = lw[role][torch.from_numpy(rows)].contiguous()
+        wa["layers"].append(m)
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 10, cfg.vocab).tolist()
+    a = O.OracleModel(cfg, w, kind="f64").prefill(toks, rows=list(range(10)))
+    b = O.OracleModel(adj, wa, kind="f64").prefill(toks, rows=list(range(10)))
+    np.testing.assert_allclose(a["logits"], b["logits"], rtol=1e-12, atol=1e-13)
+
+
+def test_llama3_model_differs_only_through_the_slow_pairs():
+    """With orig_ctx 64 the tiny model has pairs in all three bands; the
+    scaled model must differ from the plain one, and agree at position 0."""
+    cfg = configs.TINY_LLAMA3
+    w = synth.make_weights(cfg)
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 6, cfg.vocab).tolist()
+    a = O.OracleModel(cfg, w).prefill(toks, rows=list(range(6)))
+    b = O.OracleModel(configs.TINY, w).prefill(toks, rows=list(range(6)))
+    np.testing.assert_array_equal(a["logits"][0], b["logits"][0])
+    assert not np.array_equal(a["logits"][1:], b["logits"][1:])
+
+
+# ---- bf16 K/V cache -------------------------------------------------------------
+
+def test_bf16_kv_rows_are_nearest_even_bf16_of_fp32_rows():
+    cfg = configs.TINY_KVBF16
+    w = synth.make_weights(cfg)
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 5, cfg.vocab).tolist()
+    a = O.OracleModel(cfg, w)
+    b = O.OracleModel(cfg.replace(kv_bf16=False), w)
+    a.prefill(toks)
+    b.prefill(toks)
+    for p in range(5):
+        for which in (0, 1):
+            want = torch.from_numpy(b.kv_row(0, 0, which, p)).to(torch.bfloat16).to(torch.float32).numpy()
+            np.testing.assert_array_equal(a.kv_row(0, 0, which, p), want)
+    ra = a.decode([3], [5])["logits"]
+    rb = b.decode([3], [5])["logits"]
+    rel = np.linalg.norm(ra - rb) / np.linalg.norm(rb)
+    assert 0 < rel < 2e-2
