@@ -31,16 +31,7 @@ HBM_PEAK_GBS = 8000.0
 # passes (FETCH_SIZE, WRITE_SIZE) scaled by what the same counters read for a
 # 1 GiB device copy (x2.000 and x1.000): reported only while the kernel's
 # sources hash to the ones profiled, and only for the profiled workload.
-MEASURED_TRAFFIC = {
-    "attn_decode_kernel": {
-        "sources": {"decoder_only_forward_amd/csrc/k_attn_decode.hip":
-                    "3973c3fb7acf28bdc0469bb4333b49b2cce242d0c3073767b833c55d34787b4c",
-                    "decoder_only_forward_amd/csrc/common.h":
-                    "394ed98a1109455d98e2b24652372937a85b2028e1e5c3ff1d6749474c8ff8b6"},
-        "workload": ("mistral-7b", 32, 4096),
-        "bytes_per_launch": 1078641238,
-    },
-}
+MEASURED_TRAFFIC = {}
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode tok/s + prefill tok/s (Mistral-7B shape) and % of HBM / MFMA roofline"
 
@@ -50,6 +41,7 @@ def log(*a):
 
 
 def measured_traffic(kernel, workload):
+    """kernel: (name, cache type); workload: (config name, batch, prompt)."""
     import hashlib
     m = MEASURED_TRAFFIC.get(kernel)
     if not m or m["workload"] != workload:
@@ -82,6 +74,104 @@ def cpu_baseline(cfg, wd, steps=4):
                       f"({dt:.1f} s; the context is short, attention is <1% of the per-token work)"}
 
 
+def run_workload(cfg, wd, B, P, steps, warmup, small_batches=()):
+    """Prefill P tokens into each of B slots, then time batched greedy decode."""
+    import numpy as np
+    import torch
+    from decoder_only_forward_amd import synth
+    from decoder_only_forward_amd import dec as D
+
+    model = D.DecModel(cfg, wd, max_batch=B, max_prefill=P)
+    kvname = "bf16" if cfg.kv_bf16 else "fp32"
+    log(f"[{kvname} KV] workspace {model.workspace.numel() / 2**30:.1f} GiB")
+    prompts = synth.prompts(cfg, B, P)
+
+    # setup: prefill every slot; each call is a prefill sample
+    logits1 = torch.empty(cfg.vocab, device="cuda")
+    model.timing_enable(D.DEC_K_GEMM)
+    model.timing_enable(D.DEC_K_ATTN_PREFILL)
+    pre_ms = []
+    for b in range(B):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        model.prefill(prompts[b].tolist(), seq=b, logits=logits1)
+        torch.cuda.synchronize()
+        pre_ms.append((time.perf_counter() - t) * 1e3)
+        if b == 0:
+            log(f"[{kvname} KV] prefill slot 0: {pre_ms[0]:.1f} ms")
+    gemm_t = model.timing_read(D.DEC_K_GEMM)
+    apre_t = model.timing_read(D.DEC_K_ATTN_PREFILL)
+    model.timing_enable(D.DEC_K_GEMM, False)
+    model.timing_enable(D.DEC_K_ATTN_PREFILL, False)
+    pre_med = float(np.median(pre_ms))
+    log(f"[{kvname} KV] prefill median {pre_med:.1f} ms over {B} calls")
+
+    logits = torch.empty((B, cfg.vocab), device="cuda")
+    nxt = model.greedy(logits1, 1)  # any valid tokens
+    toks = np.full(B, int(nxt[0]), dtype=np.int32)
+
+    def step():
+        pos = np.array([model.length(b) for b in range(B)], dtype=np.int32)
+        model.decode(toks, pos, logits=logits)
+        toks[:] = model.greedy(logits, B)
+
+    for _ in range(warmup):
+        step()
+    # timed region 1: throughput (decode steps replay a captured HIP graph)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t
+    ms_step = dt * 1e3 / steps
+    value = B * steps / dt
+    log(f"[{kvname} KV] decode B={B}: {ms_step:.2f} ms/step, {value:.1f} tok/s ({model.graph_count()} graphs)")
+    # timed region 2: the same steps with every GEMV and attention launch
+    # bracketed by HIP events on the library's stream (eager launches)
+    model.timing_enable(D.DEC_K_GEMV)
+    model.timing_enable(D.DEC_K_ATTN_DECODE)
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    dt_timed = time.perf_counter() - t
+    gemv_t = model.timing_read(D.DEC_K_GEMV)
+    attn_t = model.timing_read(D.DEC_K_ATTN_DECODE)
+    model.timing_enable(D.DEC_K_GEMV, False)
+    model.timing_enable(D.DEC_K_ATTN_DECODE, False)
+    log(f"[{kvname} KV] decode B={B} with kernel events (eager): {dt_timed * 1e3 / steps:.2f} ms/step")
+
+    # smaller batches on the same cache (each row continues its own sequence)
+    extra = {}
+    for bb in small_batches:
+        if bb >= B:
+            continue
+        lg = torch.empty((bb, cfg.vocab), device="cuda")
+        tk = toks[:bb].copy()
+        for _ in range(2):
+            pos = np.array([model.length(b) for b in range(bb)], dtype=np.int32)
+            model.decode(tk, pos, logits=lg)
+            tk[:] = model.greedy(lg, bb)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        n = max(8, steps // 2)
+        for _ in range(n):
+            pos = np.array([model.length(b) for b in range(bb)], dtype=np.int32)
+            model.decode(tk, pos, logits=lg)
+            tk[:] = model.greedy(lg, bb)
+        torch.cuda.synchronize()
+        e = time.perf_counter() - t
+        extra[f"b{bb}"] = {"tok_s": round(bb * n / e, 2), "ms_per_step": round(e * 1e3 / n, 3)}
+        log(f"[{kvname} KV] decode B={bb}: {e * 1e3 / n:.2f} ms/step")
+    model.close()
+    del model
+    torch.cuda.empty_cache()
+    return {"value": value, "ms_step": ms_step, "pre_med": pre_med, "gemm": gemm_t, "apre": apre_t,
+            "gemv": gemv_t, "attn": attn_t, "extra": extra, "dt_timed": dt_timed}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -92,6 +182,8 @@ def main():
     ap.add_argument("--prompt", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=32)
+    ap.add_argument("--kv", choices=("both", "fp32"), default="both",
+                    help="both: the fp32-cache run gives `value`, a bf16-cache run is reported beside it")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="only run three 1 GiB device-to-device copies (PMC byte-counter calibration)")
     args = ap.parse_args()
@@ -122,89 +214,14 @@ def main():
     wd = synth.make_weights(cfg, seed=0, device="cuda")
     torch.cuda.synchronize()
     log(f"weights {cfg.matrix_params() / 1e9:.2f} B params drawn in {time.perf_counter() - t0:.1f} s")
-    model = D.DecModel(cfg, wd, max_batch=B, max_prefill=P)
-    log(f"workspace {model.workspace.numel() / 2**30:.1f} GiB")
-    prompts = synth.prompts(cfg, B, P)
 
-    # setup: prefill every slot; each call is a prefill sample
-    logits1 = torch.empty(cfg.vocab, device="cuda")
-    model.timing_enable(D.DEC_K_GEMM)
-    model.timing_enable(D.DEC_K_ATTN_PREFILL)
-    pre_ms = []
-    for b in range(B):
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        model.prefill(prompts[b].tolist(), seq=b, logits=logits1)
-        torch.cuda.synchronize()
-        pre_ms.append((time.perf_counter() - t) * 1e3)
-        if b == 0:
-            log(f"prefill slot 0: {pre_ms[0]:.1f} ms")
-    gemm_t = model.timing_read(D.DEC_K_GEMM)
-    apre_t = model.timing_read(D.DEC_K_ATTN_PREFILL)
-    model.timing_enable(D.DEC_K_GEMM, False)
-    model.timing_enable(D.DEC_K_ATTN_PREFILL, False)
-    pre_med = float(np.median(pre_ms))
-    log(f"prefill median {pre_med:.1f} ms over {B} calls")
-
-    logits = torch.empty((B, cfg.vocab), device="cuda")
-    nxt = model.greedy(logits1, 1)  # any valid tokens
-    toks = np.full(B, int(nxt[0]), dtype=np.int32)
-
-    def step():
-        pos = np.array([model.length(b) for b in range(B)], dtype=np.int32)
-        model.decode(toks, pos, logits=logits)
-        toks[:] = model.greedy(logits, B)
-
-    for _ in range(args.warmup):
-        step()
-    # timed region 1: throughput (decode steps replay a captured HIP graph)
-    torch.cuda.synchronize()
-    t = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    dt = time.perf_counter() - t
-    ms_step = dt * 1e3 / args.steps
-    value = B * args.steps / dt
-    log(f"decode B={B}: {ms_step:.2f} ms/step, {value:.1f} tok/s ({model.graph_count()} graphs)")
-    # timed region 2: the same steps with every GEMV and attention launch
-    # bracketed by HIP events on the library's stream (eager launches)
-    model.timing_enable(D.DEC_K_GEMV)
-    model.timing_enable(D.DEC_K_ATTN_DECODE)
-    torch.cuda.synchronize()
-    t = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    dt_timed = time.perf_counter() - t
-    gemv_t = model.timing_read(D.DEC_K_GEMV)
-    attn_t = model.timing_read(D.DEC_K_ATTN_DECODE)
-    model.timing_enable(D.DEC_K_GEMV, False)
-    model.timing_enable(D.DEC_K_ATTN_DECODE, False)
-    log(f"decode B={B} with kernel events (eager): {dt_timed * 1e3 / args.steps:.2f} ms/step")
-
-    # smaller batches on the same cache (each row continues its own sequence)
-    extra = {}
-    for bb in (1, 8):
-        if bb >= B:
-            continue
-        lg = torch.empty((bb, cfg.vocab), device="cuda")
-        tk = toks[:bb].copy()
-        for _ in range(2):
-            pos = np.array([model.length(b) for b in range(bb)], dtype=np.int32)
-            model.decode(tk, pos, logits=lg)
-            tk[:] = model.greedy(lg, bb)
-        torch.cuda.synchronize()
-        t = time.perf_counter()
-        n = max(8, args.steps // 2)
-        for _ in range(n):
-            pos = np.array([model.length(b) for b in range(bb)], dtype=np.int32)
-            model.decode(tk, pos, logits=lg)
-            tk[:] = model.greedy(lg, bb)
-        torch.cuda.synchronize()
-        e = time.perf_counter() - t
-        extra[f"b{bb}"] = {"tok_s": bb * n / e, "ms_per_step": e * 1e3 / n}
-        log(f"decode B={bb}: {e * 1e3 / n:.2f} ms/step")
+    main_run = run_workload(cfg, wd, B, P, args.steps, args.warmup, small_batches=(1, 8))
+    bf16_run = None
+    if args.kv == "both":
+        bf16_run = run_workload(cfg.replace(kv_bf16=True), wd, B, P, args.steps, args.warmup, small_batches=(1, 8))
+    value, ms_step, pre_med = main_run["value"], main_run["ms_step"], main_run["pre_med"]
+    gemm_t, apre_t, gemv_t, attn_t = main_run["gemm"], main_run["apre"], main_run["gemv"], main_run["attn"]
+    extra, dt_timed = main_run["extra"], main_run["dt_timed"]
 
     def roof(t, bound):
         if t["launches"] == 0 or t["ms"] <= 0:
@@ -239,17 +256,34 @@ def main():
         "prefill_ms": round(pre_med, 2),
         "decode": extra,
         "ms_per_step_with_kernel_events": round(dt_timed * 1e3 / args.steps, 3),
-        "roofline": roof(attn_t, "hbm"),
         "roofline_kernels": {"gemv_decode": roof(gemv_t, "hbm"), "gemm_prefill": roof(gemm_t, "mfma"),
-                             "attn_prefill_fp32": roof(apre_t, "mfma")},
+                             "attn_prefill": roof(apre_t, "mfma")},
     }
-    if out["roofline"] is not None:
-        out["roofline"]["kernel"] = "attn_decode_kernel (split-KV GQA decode attention)"
-        tr = measured_traffic("attn_decode_kernel", (cfg.name, B, P))
-        out["roofline"]["traffic"] = None if tr is None else round(tr / 1e9, 4)
-        out["roofline"]["traffic_unit"] = "GB per launch (rocprofv3 PMC)"
-        out["roofline"]["algorithmic_bytes_per_launch_gb"] = round(
-            attn_t["bytes"] / attn_t["launches"] / 1e9, 4)
+
+    def attn_roof(t, kv):
+        r = roof(t, "hbm")
+        if r is not None:
+            r["kernel"] = f"attn_decode_kernel (split-KV GQA decode attention, {kv} KV)"
+            tr = measured_traffic(("attn_decode_kernel", kv), (cfg.name, B, P))
+            r["traffic"] = None if tr is None else round(tr / 1e9, 4)
+            r["traffic_unit"] = "GB per launch (rocprofv3 PMC)"
+            r["algorithmic_bytes_per_launch_gb"] = round(t["bytes"] / t["launches"] / 1e9, 4)
+        return r
+
+    out["roofline"] = attn_roof(attn_t, "fp32")
+    if bf16_run is not None:
+        out["kv_bf16"] = {
+            "note": "same workload with the K/V cache stored as nearest-even bf16 (arithmetic fp32)",
+            "decode_tok_s": round(bf16_run["value"], 2),
+            "ms_per_step": round(bf16_run["ms_step"], 3),
+            "prefill_tok_s": round(P / (bf16_run["pre_med"] * 1e-3), 1),
+            "prefill_ms": round(bf16_run["pre_med"], 2),
+            "decode": bf16_run["extra"],
+            "ms_per_step_with_kernel_events": round(bf16_run["dt_timed"] * 1e3 / args.steps, 3),
+            "roofline": attn_roof(bf16_run["attn"], "bf16"),
+            "roofline_kernels": {"gemv_decode": roof(bf16_run["gemv"], "hbm"),
+                                 "attn_prefill": roof(bf16_run["apre"], "mfma")},
+        }
     if not args.no_cpu_baseline:
         try:
             out["cpu_baseline"] = cpu_baseline(cfg, wd, args.cpu_steps)

@@ -45,7 +45,7 @@ struct GraphEntry {
 };
 
 struct Plan {  // byte offsets into the workspace
-    size_t kv_layer;        // floats of one layer's K (or V) cache
+    size_t kv_layer;        // elements of one layer's K (or V) cache
     size_t k, v, x, a_hi, a_lo, a_f32, part, q, attn, rope, tok, pos, slot, amax, ssq;
     size_t moe_ids, moe_w, moe_cnt, moe_off, moe_pairs, g_hi, g_lo, g_f32, moe_y;
     size_t part_floats, act_elems, total;
@@ -65,7 +65,9 @@ struct dec_model {
     hipStream_t st;
     char *ws;
     Plan pl;
-    float *kc, *vc, *x, *a_f32, *part, *q, *attn, *moe_w, *g_f32, *moe_y, *ssq;
+    char *kc, *vc;          // caches, kv_es bytes per element
+    int kv_es;
+    float *x, *a_f32, *part, *q, *attn, *moe_w, *g_f32, *moe_y, *ssq;
     u16 *a_hi, *a_lo, *g_hi, *g_lo;
     float2 *rope;
     int32_t *tok, *pos, *slot, *amax, *moe_ids, *moe_cnt, *moe_off, *moe_pairs;
@@ -130,8 +132,9 @@ bool plan(const dec_config &c, Plan &p) {
     p.part_floats = pf;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-    p.k = take(p.kv_layer * c.n_layers * 4);
-    p.v = take(p.kv_layer * c.n_layers * 4);
+    const size_t es = c.kv_dtype == DEC_KV_BF16 ? 2 : 4;
+    p.k = take(p.kv_layer * c.n_layers * es);
+    p.v = take(p.kv_layer * c.n_layers * es);
     p.x = take((size_t)rows * d * 4);
     const bool f32w = c.weight_dtype == DEC_WEIGHT_F32;
     p.a_hi = take(f32w ? 0 : p.act_elems * 2);
@@ -177,7 +180,6 @@ int validate_cfg(const dec_config *c) {
          !(c->rope_high_freq_factor > c->rope_low_freq_factor) || c->rope_orig_ctx <= 0))
         return DEC_ERR_INVALID;
     if (c->kv_dtype != DEC_KV_F32 && c->kv_dtype != DEC_KV_BF16) return DEC_ERR_INVALID;
-    if (c->kv_dtype == DEC_KV_BF16) return DEC_ERR_UNSUPPORTED;
     // shapes the kernels are written for
     if (c->max_batch > 64) return DEC_ERR_UNSUPPORTED;
     if (c->head_dim != 16 && c->head_dim != 64 && c->head_dim != 128) return DEC_ERR_UNSUPPORTED;
@@ -237,7 +239,8 @@ int harvest(dec_model *m) {
 
 double kv_read_bytes(const dec_config &c, int T, const int *hpos) {
     double b = 0;
-    for (int i = 0; i < T; i++) b += 2.0 * std::min(hpos[i] + 1, c.max_seq) * c.n_kv_heads * c.head_dim * 4;
+    const int es = c.kv_dtype == DEC_KV_BF16 ? 2 : 4;
+    for (int i = 0; i < T; i++) b += 2.0 * std::min(hpos[i] + 1, c.max_seq) * c.n_kv_heads * c.head_dim * es;
     return b;
 }
 
@@ -245,7 +248,8 @@ int attn_splits_for(const dec_model *m, int T, const int *hpos) {
     const dec_config &c = m->c;
     int maxread = 1;
     for (int b = 0; b < T; b++) maxread = std::max(maxread, std::min(hpos[b] + 1, c.max_seq));
-    return std::min(attn_decode_splits(T, c.n_kv_heads, maxread, c.head_dim, c.n_heads / c.n_kv_heads),
+    return std::min(attn_decode_splits(T, c.n_kv_heads, maxread, c.head_dim, c.n_heads / c.n_kv_heads,
+                                       c.kv_dtype == DEC_KV_BF16),
                     MAX_ATTN_SPLITS);
 }
 
@@ -333,28 +337,29 @@ void run_pass(dec_model *m, const Pass &ps) {
 
     for (int l = 0; l < c.n_layers; l++) {
         const dec_layer_weights &w = m->L[l];
-        float *kc = m->kc + (size_t)l * m->pl.kv_layer;
-        float *vc = m->vc + (size_t)l * m->pl.kv_layer;
+        char *kc = m->kc + (size_t)l * m->pl.kv_layer * m->kv_es;
+        char *vc = m->vc + (size_t)l * m->pl.kv_layer * m->kv_es;
+        const int kvb = m->kv_es == 2;
         // q | k | v
         WSeg qkv[3] = {{w.wq, qd}, {w.wk, kvd}, {w.wv, kvd}};
         Partials pq = proj(m, qkv, 3, d, T, ah, al, af, d);
         launch_rope_kv(st, T, pq, c.qkv_bias ? w.bq : nullptr, c.qkv_bias ? w.bk : nullptr,
                        c.qkv_bias ? w.bv : nullptr, m->rope, m->pos, m->slot, nh, nkv, hd, c.rope_pairing, m->q, kc,
-                       vc, c.max_seq, m->ring);
+                       vc, c.max_seq, m->ring, kvb);
         // attention -> a (row stride qd)
         if (ps.decode) {
             const int S = attn_splits_for(m, T, ps.hpos);
             Tick tk(m, DEC_K_ATTN_DECODE);
-            launch_attn_decode(st, T, m->q, kc, vc, m->pos, m->slot, nh, nkv, hd, c.max_seq, c.sliding_window, S,
+            launch_attn_decode(st, T, m->q, kc, vc, kvb, m->pos, m->slot, nh, nkv, hd, c.max_seq, c.sliding_window, S,
                                m->attn, ah, al, af);
             tk.done(kv_read_bytes(c, T, ps.hpos) + 2.0 * T * qd * 4, 0);
         } else {
             double flops = 0;
             for (int t = 0; t < T; t++) flops += 4.0 * hd * nh * (ps.start_pos + t + 1);
             Tick tk(m, DEC_K_ATTN_PREFILL);
-            launch_attn_prefill(st, T, ps.start_pos, ps.seq, m->q, kc, vc, nh, nkv, hd, c.max_seq,
+            launch_attn_prefill(st, T, ps.start_pos, ps.seq, m->q, kc, vc, kvb, nh, nkv, hd, c.max_seq,
                                 c.sliding_window, ah, al, af);
-            tk.done((double)(ps.start_pos + T) * kvd * 8 + 2.0 * T * qd * 4, flops);
+            tk.done((double)(ps.start_pos + T) * kvd * 2 * m->kv_es + 2.0 * T * qd * 4, flops);
         }
         // output projection, residual, FFN norm
         WSeg wo[1] = {{w.wo, d}};
@@ -530,8 +535,9 @@ int dec_create(const dec_config *cfg, const dec_weights *w, void *workspace, siz
     m->ws = (char *)workspace;
     m->pl = p;
     char *b = m->ws;
-    m->kc = (float *)(b + p.k);
-    m->vc = (float *)(b + p.v);
+    m->kc = b + p.k;
+    m->vc = b + p.v;
+    m->kv_es = cfg->kv_dtype == DEC_KV_BF16 ? 2 : 4;
     m->x = (float *)(b + p.x);
     m->a_hi = (u16 *)(b + p.a_hi);
     m->a_lo = (u16 *)(b + p.a_lo);

@@ -7,10 +7,18 @@
 //
 // Split-KV: grid (splits, kv heads, rows).  A block streams one kv head's K/V
 // rows of one split once from HBM and applies them to all G query heads of the
-// group.  LP lanes share one position (each lane 8 dims, two float4 loads per
-// row); every lane group keeps its own softmax state over the positions it
-// visits, and the groups are merged at the end (in-wave by shuffles, across
-// waves through LDS), then across splits by a merge kernel.
+// group.  LP = HD/DPL lanes share one position, each lane holding DPL of its
+// dims (DPL = 16 for groups of up to 4 heads, else 8, which bounds the q and
+// accumulator registers); a lane reads its dims as 16-byte words interleaved
+// with the other lanes of the group, so each load instruction covers a
+// contiguous 16*LP-byte run of the row.  Work that every lane of a group
+// repeats (score reduction, softmax update) is paid once per LP lanes, so the
+// wider lanes halve it per position.  Scores are reduced within a row of 16
+// lanes by DPP moves.  The online softmax runs in base 2: q is pre-scaled by
+// log2(e)/sqrt(hd), so each weight is one exp2 of a difference.  Each lane
+// group keeps its own running state over the positions it visits; the groups
+// are merged at the end (in-wave by shuffles, across waves through LDS), then
+// across splits by a merge kernel.
 //
 // Ring cache: softmax does not depend on key order, and keys are stored already
 // rotated, so the readable slots [0, min(pos+1, max_seq)) are read as one
@@ -20,14 +28,64 @@
 
 namespace {
 
-constexpr int NB = 4;  // positions per lane group per iteration (loads in flight)
+constexpr float LOG2E = 1.4426950408889634f;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // K/V rows are read once per decode step: non-temporal loads stream them past
 // the caches.
-__device__ __forceinline__ float4 ntload4(const float *p) {
-    const floatx4 v = __builtin_nontemporal_load(reinterpret_cast<const floatx4 *>(p));
-    return make_float4(v[0], v[1], v[2], v[3]);
+__device__ __forceinline__ u32x4 ntload16(const void *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
 }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// v + (v of the lane given by a DPP pattern within its row of 16 lanes)
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int o = __builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false);
+    return v + __int_as_float(o);
+}
+
+// Sum over each aligned group of LP lanes (LP <= 16); every lane gets its
+// group's sum.  quad_perm [1,0,3,2] and [2,3,0,1] pair lanes at distance 1 and
+// 2; row_half_mirror then pairs the two quads of 8 lanes, row_mirror the two
+// halves of 16.
+template <int LP>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (LP >= 2) v = dpp_add<0xB1>(v);
+    if constexpr (LP >= 4) v = dpp_add<0x4E>(v);
+    if constexpr (LP >= 8) v = dpp_add<0x141>(v);
+    if constexpr (LP >= 16) v = dpp_add<0x140>(v);
+    return v;
+}
+
+// Per-lane view of a cache row: NV 16-byte words of EPW elements each.  Word w
+// of lane u sits at element (w*LP + u)*EPW of the row.
+template <int HD, int DPL, bool KB>
+struct Row {
+    static constexpr int ES = KB ? 2 : 4;       // bytes per element
+    static constexpr int EPW = 16 / ES;         // elements per 16-byte word
+    static constexpr int NV = DPL / EPW;        // words per lane per row
+    static constexpr int LP = HD / DPL;
+    static __device__ __forceinline__ int dim(int u, int e) { return ((e / EPW) * LP + u) * EPW + e % EPW; }
+    static __device__ __forceinline__ void load(const char *row, int u, u32x4 (&r)[NV]) {
+#pragma unroll
+        for (int w = 0; w < NV; w++) r[w] = ntload16(row + (size_t)((w * LP + u) * EPW) * ES);
+    }
+    static __device__ __forceinline__ void unpack(const u32x4 (&r)[NV], float (&f)[DPL]) {
+#pragma unroll
+        for (int w = 0; w < NV; w++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                if constexpr (KB) {
+                    f[w * 8 + 2 * j] = __uint_as_float(r[w][j] << 16);
+                    f[w * 8 + 2 * j + 1] = __uint_as_float(r[w][j] & 0xFFFF0000u);
+                } else {
+                    f[w * 4 + j] = __uint_as_float(r[w][j]);
+                }
+            }
+    }
+};
 
 __device__ __forceinline__ void store_out(float v, size_t off, u16 *o_hi, u16 *o_lo, float *o_f32) {
     if (o_f32) o_f32[off] = v;
@@ -39,15 +97,24 @@ __device__ __forceinline__ void store_out(float v, size_t off, u16 *o_hi, u16 *o
     }
 }
 
-template <int HD, int G>
-__global__ void __launch_bounds__(256) attn_decode_kernel(
-    const float *__restrict__ q, const float *__restrict__ kc, const float *__restrict__ vc,
+template <int G>
+constexpr int dims_per_lane() { return G <= 4 ? 16 : 8; }
+
+template <int HD, int G, bool KB>
+__global__ void __launch_bounds__(256, 2) attn_decode_kernel(
+    const float *__restrict__ q, const void *__restrict__ kc, const void *__restrict__ vc,
     const int32_t *__restrict__ pos, const int32_t *__restrict__ slot, int nh, int nkv, int max_seq,
     int splits, float *__restrict__ part, u16 *__restrict__ o_hi, u16 *__restrict__ o_lo,
     float *__restrict__ o_f32) {
-    constexpr int LP = HD / 8;             // lanes per position
-    constexpr int PPW = WAVE / LP;         // positions per wave
-    constexpr int NG = 4 * PPW;            // lane groups per block
+    constexpr int DPL = dims_per_lane<G>() < HD ? dims_per_lane<G>() : HD;
+    using R = Row<HD, DPL, KB>;
+    constexpr int LP = R::LP;                 // lanes per position
+    constexpr int PPW = WAVE / LP;            // positions per wave
+    constexpr int NG = 4 * PPW;               // lane groups per block
+    constexpr int NV = R::NV;
+    // positions per lane group per iteration: 8 (fp32) or 4 (bf16) words of K
+    // and of V in flight per lane
+    constexpr int NB = (KB ? 4 : 8) / NV;
     __shared__ float sm[4][G], sl[4][G];
     __shared__ float sacc[4][G][HD];
 
@@ -63,83 +130,121 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(
     const int end = min(nread, beg + chunk);
 
     const size_t head_base = ((size_t)slot[b] * nkv + kvh) * max_seq;
-    const float *K = kc + head_base * HD;
-    const float *V = vc + head_base * HD;
-    const float scale = 1.0f / sqrtf((float)HD);
+    const char *K = static_cast<const char *>(kc) + head_base * HD * R::ES;
+    const char *V = static_cast<const char *>(vc) + head_base * HD * R::ES;
+    const float qscale = LOG2E / sqrtf((float)HD);
 
-    float qr[G][8];
+    // fp32 cache: q in fp32.  bf16 cache: q as (hi, lo) bf16 pairs matching
+    // the packing of the key words, for v_dot2 against the stored keys.
+    constexpr int QN = KB ? DPL / 2 : DPL;
+    float qr[G][KB ? 1 : DPL];
+    uint32_t qph[G][KB ? QN : 1], qpl[G][KB ? QN : 1];
 #pragma unroll
     for (int g = 0; g < G; g++) {
-        const float *qh = q + (size_t)b * nh * HD + (size_t)(kvh * G + g) * HD;
-        const float4 a = *reinterpret_cast<const float4 *>(qh + 4 * u);
-        const float4 c = *reinterpret_cast<const float4 *>(qh + 4 * LP + 4 * u);
-        qr[g][0] = a.x; qr[g][1] = a.y; qr[g][2] = a.z; qr[g][3] = a.w;
-        qr[g][4] = c.x; qr[g][5] = c.y; qr[g][6] = c.z; qr[g][7] = c.w;
+        const float *qg = q + (size_t)b * nh * HD + (size_t)(kvh * G + g) * HD;
+        if constexpr (KB) {
+#pragma unroll
+            for (int j = 0; j < QN; j++) {
+                uint32_t h0, l0, h1, l1;
+                split_bf16(qg[R::dim(u, 2 * j)] * qscale, h0, l0);
+                split_bf16(qg[R::dim(u, 2 * j + 1)] * qscale, h1, l1);
+                qph[g][j] = h0 | (h1 << 16);
+                qpl[g][j] = l0 | (l1 << 16);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < DPL; e++) qr[g][e] = qg[R::dim(u, e)] * qscale;
+        }
     }
-    float m[G], l[G], acc[G][8];
+    float m[G], l[G], acc[G][DPL];
 #pragma unroll
     for (int g = 0; g < G; g++) {
         m[g] = -INFINITY;
         l[g] = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; i++) acc[g][i] = 0.f;
+        for (int i = 0; i < DPL; i++) acc[g][i] = 0.f;
     }
 
     for (int base = beg; base < end; base += NG * NB) {
-        float4 k0[NB], k1[NB];
+        u32x4 kr[NB][NV], vr[NB][NV];
         bool valid[NB];
 #pragma unroll
         for (int i = 0; i < NB; i++) {
             const int j = base + i * NG + gid;
             valid[i] = j < end;
             const int jj = valid[i] ? j : beg;
-            k0[i] = ntload4(K + (size_t)jj * HD + 4 * u);
-            k1[i] = ntload4(K + (size_t)jj * HD + 4 * LP + 4 * u);
+            R::load(K + (size_t)jj * HD * R::ES, u, kr[i]);
         }
-        float4 v0[NB], v1[NB];
 #pragma unroll
         for (int i = 0; i < NB; i++) {
             const int j = base + i * NG + gid;
             const int jj = valid[i] ? j : beg;
-            v0[i] = ntload4(V + (size_t)jj * HD + 4 * u);
-            v1[i] = ntload4(V + (size_t)jj * HD + 4 * LP + 4 * u);
+            R::load(V + (size_t)jj * HD * R::ES, u, vr[i]);
         }
         float s[NB][G];
 #pragma unroll
-        for (int i = 0; i < NB; i++)
+        for (int i = 0; i < NB; i++) {
+            if constexpr (KB) {
 #pragma unroll
-            for (int g = 0; g < G; g++) {
-                float d = qr[g][0] * k0[i].x + qr[g][1] * k0[i].y + qr[g][2] * k0[i].z + qr[g][3] * k0[i].w +
-                          qr[g][4] * k1[i].x + qr[g][5] * k1[i].y + qr[g][6] * k1[i].z + qr[g][7] * k1[i].w;
+                for (int g = 0; g < G; g++) {
+                    float d = 0.f;
 #pragma unroll
-                for (int o = LP / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, WAVE);
-                s[i][g] = valid[i] ? d * scale : -INFINITY;
+                    for (int w = 0; w < NV; w++)
+#pragma unroll
+                        for (int j = 0; j < 4; j++) {
+                            // copy the element out first: a bit cast of a vector
+                            // element reads the vector's first element
+                            const uint32_t kw = kr[i][w][j];
+                            const bf16x2 kk = __builtin_bit_cast(bf16x2, kw);
+                            d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qph[g][w * 4 + j]), kk,
+                                                                d, false);
+                            d = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, qpl[g][w * 4 + j]), kk,
+                                                                d, false);
+                        }
+                    d = group_sum<LP>(d);
+                    s[i][g] = valid[i] ? d : -INFINITY;
+                }
+            } else {
+                float kf[DPL];
+                R::unpack(kr[i], kf);
+#pragma unroll
+                for (int g = 0; g < G; g++) {
+                    float d = 0.f;
+#pragma unroll
+                    for (int e = 0; e < DPL; e++) d += qr[g][e] * kf[e];
+                    d = group_sum<LP>(d);
+                    s[i][g] = valid[i] ? d : -INFINITY;
+                }
             }
+        }
+        // online softmax update per head: s becomes the weights of this batch
 #pragma unroll
         for (int g = 0; g < G; g++) {
             float mx = m[g];
 #pragma unroll
             for (int i = 0; i < NB; i++) mx = fmaxf(mx, s[i][g]);
-            if (mx == -INFINITY) continue;
-            const float corr = expf(m[g] - mx);
+            const bool none = mx == -INFINITY;  // no readable position yet
+            const float corr = none ? 1.f : fast_exp2(m[g] - mx);
             m[g] = mx;
-            float pe[NB];
             float ps = 0.f;
 #pragma unroll
             for (int i = 0; i < NB; i++) {
-                pe[i] = expf(s[i][g] - mx);
-                ps += pe[i];
+                s[i][g] = none ? 0.f : fast_exp2(s[i][g] - mx);
+                ps += s[i][g];
             }
             l[g] = l[g] * corr + ps;
 #pragma unroll
-            for (int e = 0; e < 8; e++) acc[g][e] *= corr;
+            for (int e = 0; e < DPL; e++) acc[g][e] *= corr;
+        }
+        // weighted V rows, one row live at a time
 #pragma unroll
-            for (int i = 0; i < NB; i++) {
-                acc[g][0] += pe[i] * v0[i].x; acc[g][1] += pe[i] * v0[i].y;
-                acc[g][2] += pe[i] * v0[i].z; acc[g][3] += pe[i] * v0[i].w;
-                acc[g][4] += pe[i] * v1[i].x; acc[g][5] += pe[i] * v1[i].y;
-                acc[g][6] += pe[i] * v1[i].z; acc[g][7] += pe[i] * v1[i].w;
-            }
+        for (int i = 0; i < NB; i++) {
+            float vf[DPL];
+            R::unpack(vr[i], vf);
+#pragma unroll
+            for (int g = 0; g < G; g++)
+#pragma unroll
+                for (int e = 0; e < DPL; e++) acc[g][e] += s[i][g] * vf[e];
         }
     }
 
@@ -151,11 +256,11 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(
             const float mo = __shfl_xor(m[g], o, WAVE);
             const float lo = __shfl_xor(l[g], o, WAVE);
             const float mx = fmaxf(m[g], mo);
-            const float a = mx == -INFINITY ? 0.f : expf(m[g] - mx);
-            const float bb = mx == -INFINITY ? 0.f : expf(mo - mx);
+            const float a = mx == -INFINITY ? 0.f : fast_exp2(m[g] - mx);
+            const float bb = mx == -INFINITY ? 0.f : fast_exp2(mo - mx);
             l[g] = l[g] * a + lo * bb;
 #pragma unroll
-            for (int e = 0; e < 8; e++) {
+            for (int e = 0; e < DPL; e++) {
                 const float ao = __shfl_xor(acc[g][e], o, WAVE);
                 acc[g][e] = acc[g][e] * a + ao * bb;
             }
@@ -167,10 +272,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(
         for (int g = 0; g < G; g++) {
             if (u == 0) { sm[wv][g] = m[g]; sl[wv][g] = l[g]; }
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                sacc[wv][g][4 * u + e] = acc[g][e];
-                sacc[wv][g][4 * LP + 4 * u + e] = acc[g][4 + e];
-            }
+            for (int e = 0; e < DPL; e++) sacc[wv][g][R::dim(u, e)] = acc[g][e];
         }
     }
     __syncthreads();
@@ -183,7 +285,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(
         float L = 0.f, A = 0.f;
 #pragma unroll
         for (int w = 0; w < 4; w++) {
-            const float f = mx == -INFINITY ? 0.f : expf(sm[w][g] - mx);
+            const float f = mx == -INFINITY ? 0.f : fast_exp2(sm[w][g] - mx);
             L += sl[w][g] * f;
             A += sacc[w][g][i] * f;
         }
@@ -191,6 +293,7 @@ __global__ void __launch_bounds__(256) attn_decode_kernel(
         if (splits == 1) {
             store_out(A / L, (size_t)b * nh * HD + (size_t)h * HD + i, o_hi, o_lo, o_f32);
         } else {
+            // partial: unnormalised output, base-2 running maximum, normaliser
             float *dst = part + (((size_t)b * nh + h) * splits + split) * (HD + 2);
             dst[i] = A;
             if (i == 0) { dst[HD] = mx; dst[HD + 1] = L; }
@@ -208,7 +311,7 @@ __global__ void attn_merge_kernel(int nh, int hd, int splits, const float *__res
         float L = 0.f, A = 0.f;
         for (int s = 0; s < splits; s++) {
             const float ms = src[s * (hd + 2) + hd];
-            const float f = ms == -INFINITY ? 0.f : expf(ms - mx);
+            const float f = ms == -INFINITY ? 0.f : fast_exp2(ms - mx);
             L += src[s * (hd + 2) + hd + 1] * f;
             A += src[s * (hd + 2) + i] * f;
         }
@@ -216,12 +319,12 @@ __global__ void attn_merge_kernel(int nh, int hd, int splits, const float *__res
     }
 }
 
-template <int HD>
-bool launch_decode_hd(hipStream_t st, int G, dim3 grid, const float *q, const float *kc, const float *vc,
+template <int HD, bool KB>
+bool launch_decode_hd(hipStream_t st, int G, dim3 grid, const float *q, const void *kc, const void *vc,
                       const int32_t *pos, const int32_t *slot, int nh, int nkv, int max_seq, int splits,
                       float *part, u16 *o_hi, u16 *o_lo, float *o_f32) {
-#define AD(GG) hipLaunchKernelGGL((attn_decode_kernel<HD, GG>), grid, dim3(256), 0, st, q, kc, vc, pos, slot, \
-                                  nh, nkv, max_seq, splits, part, o_hi, o_lo, o_f32)
+#define AD(GG) hipLaunchKernelGGL((attn_decode_kernel<HD, GG, KB>), grid, dim3(256), 0, st, q, kc, vc, pos, \
+                                  slot, nh, nkv, max_seq, splits, part, o_hi, o_lo, o_f32)
     switch (G) {
         case 1: AD(1); return true;
         case 2: AD(2); return true;
@@ -236,23 +339,29 @@ bool launch_decode_hd(hipStream_t st, int G, dim3 grid, const float *q, const fl
     return false;
 }
 
+template <bool KB>
+const void *decode_probe_fn(int hd) {
+    return hd == 128 ? (const void *)attn_decode_kernel<128, 4, KB>
+         : hd == 64  ? (const void *)attn_decode_kernel<64, 4, KB>
+                     : (const void *)attn_decode_kernel<16, 4, KB>;
+}
+
 }  // namespace
 
-int attn_decode_splits(int B, int nkv, int readable, int hd, int G) {
+int attn_decode_splits(int B, int nkv, int readable, int hd, int G, int kv_bf16) {
     // fill the resident-block slots once (a second partial round would leave
     // the memory system idle), with at least 128 positions per split
-    static int occ_cache[3] = {0, 0, 0};
+    static int occ_cache[2][3] = {{0, 0, 0}, {0, 0, 0}};
     const int which = hd == 128 ? 0 : hd == 64 ? 1 : 2;
-    if (!occ_cache[which]) {
+    int &occ_c = occ_cache[kv_bf16 ? 1 : 0][which];
+    if (!occ_c) {
         int occ = 0;
-        const void *fn = hd == 128 ? (const void *)attn_decode_kernel<128, 4>
-                       : hd == 64  ? (const void *)attn_decode_kernel<64, 4>
-                                   : (const void *)attn_decode_kernel<16, 4>;
+        const void *fn = kv_bf16 ? decode_probe_fn<true>(hd) : decode_probe_fn<false>(hd);
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 256, 0) != hipSuccess || occ <= 0) occ = 2;
-        occ_cache[which] = occ;
+        occ_c = occ;
     }
     (void)G;
-    const int slots = occ_cache[which] * num_cus();
+    const int slots = occ_c * num_cus();
     int s = slots / (B * nkv);
     const int maxs = (readable + 127) / 128;
     if (s > maxs) s = maxs;
@@ -261,18 +370,26 @@ int attn_decode_splits(int B, int nkv, int readable, int hd, int G) {
     return s;
 }
 
-void launch_attn_decode(hipStream_t st, int B, const float *q, const float *kc, const float *vc,
+void launch_attn_decode(hipStream_t st, int B, const float *q, const void *kc, const void *vc, int kv_bf16,
                         const int32_t *pos, const int32_t *slot, int nh, int nkv, int hd, int max_seq,
                         int window, int splits, float *part, u16 *o_hi, u16 *o_lo, float *o_f32) {
     (void)window;
     if (B <= 0) return;
     const int G = nh / nkv;
     dim3 grid(splits, nkv, B);
-    if (hd == 128) launch_decode_hd<128>(st, G, grid, q, kc, vc, pos, slot, nh, nkv, max_seq, splits, part, o_hi, o_lo, o_f32);
-    else if (hd == 64) launch_decode_hd<64>(st, G, grid, q, kc, vc, pos, slot, nh, nkv, max_seq, splits, part, o_hi, o_lo, o_f32);
-    else launch_decode_hd<16>(st, G, grid, q, kc, vc, pos, slot, nh, nkv, max_seq, splits, part, o_hi, o_lo, o_f32);
+#define LD(HD, KB) launch_decode_hd<HD, KB>(st, G, grid, q, kc, vc, pos, slot, nh, nkv, max_seq, splits, part, \
+                                            o_hi, o_lo, o_f32)
+    if (kv_bf16) {
+        if (hd == 128) LD(128, true);
+        else if (hd == 64) LD(64, true);
+        else LD(16, true);
+    } else {
+        if (hd == 128) LD(128, false);
+        else if (hd == 64) LD(64, false);
+        else LD(16, false);
+    }
+#undef LD
     if (splits > 1)
         hipLaunchKernelGGL(attn_merge_kernel, dim3(nh, B), dim3(hd < 64 ? 64 : hd), 0, st, nh, hd, splits, part,
                            o_hi, o_lo, o_f32);
 }
-

@@ -18,6 +18,18 @@ __device__ __forceinline__ void store_out(float v, size_t off, u16 *o_hi, u16 *o
     }
 }
 
+// Four cached elements starting at element e of a K/V cache (fp32, or bf16 bits).
+template <bool KB>
+__device__ __forceinline__ float4 load_kv4(const void *cache, size_t e) {
+    if constexpr (KB) {
+        const uint2 r = *reinterpret_cast<const uint2 *>(static_cast<const u16 *>(cache) + e);
+        return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u),
+                           __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xFFFF0000u));
+    } else {
+        return *reinterpret_cast<const float4 *>(static_cast<const float *>(cache) + e);
+    }
+}
+
 }  // namespace
 
 // ---- prefill ------------------------------------------------------------------
@@ -30,10 +42,10 @@ namespace {
 
 constexpr int BQ = 32, BKV = 32, SB = 8;
 
-template <int HD, int G, int SPLIT>
+template <int HD, int G, int SPLIT, bool KB>
 __global__ void __launch_bounds__(BQ * G * SPLIT) attn_prefill_kernel(
-    int T, int start_pos, int slot, const float *__restrict__ q, const float *__restrict__ kc,
-    const float *__restrict__ vc, int nh, int nkv, int max_seq, u16 *__restrict__ o_hi, u16 *__restrict__ o_lo,
+    int T, int start_pos, int slot, const float *__restrict__ q, const void *__restrict__ kc,
+    const void *__restrict__ vc, int nh, int nkv, int max_seq, u16 *__restrict__ o_hi, u16 *__restrict__ o_lo,
     float *__restrict__ o_f32) {
     constexpr int D = HD / SPLIT;
     constexpr int NT = BQ * G * SPLIT;
@@ -71,8 +83,8 @@ __global__ void __launch_bounds__(BQ * G * SPLIT) attn_prefill_kernel(
             const int j = kb + row;
             float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
             if (j <= last_pos) {
-                kv = *reinterpret_cast<const float4 *>(kc + (head_base + j) * HD + 4 * c4);
-                vv = *reinterpret_cast<const float4 *>(vc + (head_base + j) * HD + 4 * c4);
+                kv = load_kv4<KB>(kc, (head_base + j) * HD + 4 * c4);
+                vv = load_kv4<KB>(vc, (head_base + j) * HD + 4 * c4);
             }
             *reinterpret_cast<float4 *>(&sk[row][4 * c4]) = kv;
             *reinterpret_cast<float4 *>(&sv[row][4 * c4]) = vv;
@@ -126,11 +138,11 @@ __global__ void __launch_bounds__(BQ * G * SPLIT) attn_prefill_kernel(
     for (int i = 0; i < D; i++) store_out(acc[i] * inv, off + i, o_hi, o_lo, o_f32);
 }
 
-template <int HD, int SPLIT>
+template <int HD, int SPLIT, bool KB>
 bool launch_prefill_hd(hipStream_t st, int G, dim3 grid, int T, int start_pos, int slot, const float *q,
-                       const float *kc, const float *vc, int nh, int nkv, int max_seq, u16 *o_hi, u16 *o_lo,
+                       const void *kc, const void *vc, int nh, int nkv, int max_seq, u16 *o_hi, u16 *o_lo,
                        float *o_f32) {
-#define AP(GG) hipLaunchKernelGGL((attn_prefill_kernel<HD, GG, SPLIT>), grid, dim3(BQ * GG * SPLIT), 0, st, T, \
+#define AP(GG) hipLaunchKernelGGL((attn_prefill_kernel<HD, GG, SPLIT, KB>), grid, dim3(BQ * GG * SPLIT), 0, st, T, \
                                   start_pos, slot, q, kc, vc, nh, nkv, max_seq, o_hi, o_lo, o_f32)
     switch (G) {
         case 1: AP(1); return true;
@@ -160,7 +172,9 @@ bool launch_prefill_hd(hipStream_t st, int G, dim3 grid, int T, int start_pos, i
 //                  order inside the contraction is relabelled to match, and V is
 //                  staged transposed so the relabelled reads are 8-byte runs)
 // Each product is hi*hi + hi*lo + lo*hi, which keeps the scores and outputs at
-// fp32 accuracy (the lo*lo term is below 2^-16 of the total).
+// fp32 accuracy (the lo*lo term is below 2^-16 of the total).  A bf16 cache
+// holds K and V exactly in bf16, so their lo parts vanish: the tiles are staged
+// as stored and each product is hi*hi + hi*lo (Q and P still split).
 namespace {
 
 constexpr int NQV = 128, MKV = 64;
@@ -172,10 +186,10 @@ __device__ __forceinline__ bf16x8 pack8(const uint32_t *h) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int HD, int G>
+template <int HD, int G, bool KB>
 __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
-    int T, int start_pos, int slot, const float *__restrict__ q, const float *__restrict__ kc,
-    const float *__restrict__ vc, int nh, int nkv, int max_seq, u16 *__restrict__ o_hi, u16 *__restrict__ o_lo,
+    int T, int start_pos, int slot, const float *__restrict__ q, const void *__restrict__ kc,
+    const void *__restrict__ vc, int nh, int nkv, int max_seq, u16 *__restrict__ o_hi, u16 *__restrict__ o_lo,
     float *__restrict__ o_f32) {
     constexpr int ROWS = NQV / G;
     constexpr int KLD = HD + 8;     // u16 per K row in LDS
@@ -183,9 +197,9 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
     constexpr int KS = HD / 16;     // MFMA k-steps over head_dim
     constexpr int DT = HD / 32;     // output dim tiles
     __shared__ __attribute__((aligned(16))) u16 sKh[MKV * KLD];
-    __shared__ __attribute__((aligned(16))) u16 sKl[MKV * KLD];
+    __shared__ __attribute__((aligned(16))) u16 sKl[KB ? 8 : MKV * KLD];
     __shared__ __attribute__((aligned(16))) u16 sVh[HD * VLD];
-    __shared__ __attribute__((aligned(16))) u16 sVl[HD * VLD];
+    __shared__ __attribute__((aligned(16))) u16 sVl[KB ? 8 : HD * VLD];
 
     const int kvh = blockIdx.y;
     const int rb = gridDim.x - 1 - blockIdx.x;  // longest rows first
@@ -234,30 +248,57 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
     for (int kb = 0; kb <= last_pos; kb += MKV) {
         __syncthreads();
         // K tile -> [key][dim] hi/lo; V tile -> transposed [dim][key] hi/lo
-        for (int i = tid; i < MKV * HD / 4; i += 256) {
-            const int key = i / (HD / 4), c4 = i % (HD / 4);
-            const int j = kb + key;
-            float4 kv = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (j <= last_pos) kv = *reinterpret_cast<const float4 *>(kc + (head_base + j) * HD + 4 * c4);
-            uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-            split_bf16(kv.x, h0, l0); split_bf16(kv.y, h1, l1); split_bf16(kv.z, h2, l2); split_bf16(kv.w, h3, l3);
-            *reinterpret_cast<uint2 *>(sKh + key * KLD + 4 * c4) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-            *reinterpret_cast<uint2 *>(sKl + key * KLD + 4 * c4) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
-        }
-        for (int i = tid; i < (MKV / 2) * HD / 4; i += 256) {
-            const int kp = i / (HD / 4), c4 = i % (HD / 4);
-            const int j = kb + 2 * kp;
-            float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
-            if (j <= last_pos) v0 = *reinterpret_cast<const float4 *>(vc + (head_base + j) * HD + 4 * c4);
-            if (j + 1 <= last_pos) v1 = *reinterpret_cast<const float4 *>(vc + (head_base + j + 1) * HD + 4 * c4);
-            const float a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
+        if constexpr (KB) {
+            const u16 *k16 = static_cast<const u16 *>(kc), *v16 = static_cast<const u16 *>(vc);
+            for (int i = tid; i < MKV * HD / 8; i += 256) {
+                const int key = i / (HD / 8), c8 = i % (HD / 8);
+                const int j = kb + key;
+                u32x4 kv = {0u, 0u, 0u, 0u};
+                if (j <= last_pos) kv = *reinterpret_cast<const u32x4 *>(k16 + (head_base + j) * HD + 8 * c8);
+                *reinterpret_cast<u32x4 *>(sKh + key * KLD + 8 * c8) = kv;
+            }
+            for (int i = tid; i < (MKV / 2) * HD / 8; i += 256) {
+                const int kp = i / (HD / 8), c8 = i % (HD / 8);
+                const int j = kb + 2 * kp;
+                u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = v0;
+                if (j <= last_pos) v0 = *reinterpret_cast<const u32x4 *>(v16 + (head_base + j) * HD + 8 * c8);
+                if (j + 1 <= last_pos) v1 = *reinterpret_cast<const u32x4 *>(v16 + (head_base + j + 1) * HD + 8 * c8);
 #pragma unroll
-            for (int e = 0; e < 4; e++) {
-                uint32_t ha, la, hb, lb;
-                split_bf16(a0[e], ha, la);
-                split_bf16(a1[e], hb, lb);
-                *reinterpret_cast<uint32_t *>(sVh + (4 * c4 + e) * VLD + 2 * kp) = ha | (hb << 16);
-                *reinterpret_cast<uint32_t *>(sVl + (4 * c4 + e) * VLD + 2 * kp) = la | (lb << 16);
+                for (int e = 0; e < 4; e++) {
+                    // dims 8c8+2e (low halves) and 8c8+2e+1 (high halves)
+                    *reinterpret_cast<uint32_t *>(sVh + (8 * c8 + 2 * e) * VLD + 2 * kp) =
+                        (v0[e] & 0xFFFFu) | (v1[e] << 16);
+                    *reinterpret_cast<uint32_t *>(sVh + (8 * c8 + 2 * e + 1) * VLD + 2 * kp) =
+                        (v0[e] >> 16) | (v1[e] & 0xFFFF0000u);
+                }
+            }
+        } else {
+            const float *k32 = static_cast<const float *>(kc), *v32 = static_cast<const float *>(vc);
+            for (int i = tid; i < MKV * HD / 4; i += 256) {
+                const int key = i / (HD / 4), c4 = i % (HD / 4);
+                const int j = kb + key;
+                float4 kv = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (j <= last_pos) kv = *reinterpret_cast<const float4 *>(k32 + (head_base + j) * HD + 4 * c4);
+                uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+                split_bf16(kv.x, h0, l0); split_bf16(kv.y, h1, l1); split_bf16(kv.z, h2, l2); split_bf16(kv.w, h3, l3);
+                *reinterpret_cast<uint2 *>(sKh + key * KLD + 4 * c4) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                *reinterpret_cast<uint2 *>(sKl + key * KLD + 4 * c4) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+            }
+            for (int i = tid; i < (MKV / 2) * HD / 4; i += 256) {
+                const int kp = i / (HD / 4), c4 = i % (HD / 4);
+                const int j = kb + 2 * kp;
+                float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
+                if (j <= last_pos) v0 = *reinterpret_cast<const float4 *>(v32 + (head_base + j) * HD + 4 * c4);
+                if (j + 1 <= last_pos) v1 = *reinterpret_cast<const float4 *>(v32 + (head_base + j + 1) * HD + 4 * c4);
+                const float a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    uint32_t ha, la, hb, lb;
+                    split_bf16(a0[e], ha, la);
+                    split_bf16(a1[e], hb, lb);
+                    *reinterpret_cast<uint32_t *>(sVh + (4 * c4 + e) * VLD + 2 * kp) = ha | (hb << 16);
+                    *reinterpret_cast<uint32_t *>(sVl + (4 * c4 + e) * VLD + 2 * kp) = la | (lb << 16);
+                }
             }
         }
         __syncthreads();
@@ -273,10 +314,12 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
             for (int s2 = 0; s2 < KS; s2++) {
                 const int off = (kt * 32 + ql) * KLD + 16 * s2 + 8 * hh;
                 const bf16x8 kh = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sKh + off));
-                const bf16x8 klo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sKl + off));
                 sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qh[s2], sc[kt], 0, 0, 0);
                 sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kh, qlo[s2], sc[kt], 0, 0, 0);
-                sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo, qh[s2], sc[kt], 0, 0, 0);
+                if constexpr (!KB) {
+                    const bf16x8 klo = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sKl + off));
+                    sc[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo, qh[s2], sc[kt], 0, 0, 0);
+                }
             }
         }
         // lane holds keys kb + kt*32 + (e/4)*8 + 4hh + e%4 of query qpos
@@ -321,15 +364,17 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
                 const int vrow = (d * 32 + ql) * VLD + 16 * ks + 4 * hh;
                 const uint2 h0 = *reinterpret_cast<const uint2 *>(sVh + vrow);
                 const uint2 h1 = *reinterpret_cast<const uint2 *>(sVh + vrow + 8);
-                const uint2 l0 = *reinterpret_cast<const uint2 *>(sVl + vrow);
-                const uint2 l1 = *reinterpret_cast<const uint2 *>(sVl + vrow + 8);
                 const u32x4 vh4 = {h0.x, h0.y, h1.x, h1.y};
-                const u32x4 vl4 = {l0.x, l0.y, l1.x, l1.y};
                 const bf16x8 ah = __builtin_bit_cast(bf16x8, vh4);
-                const bf16x8 al = __builtin_bit_cast(bf16x8, vl4);
                 o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, o[d], 0, 0, 0);
                 o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, o[d], 0, 0, 0);
-                o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, o[d], 0, 0, 0);
+                if constexpr (!KB) {
+                    const uint2 l0 = *reinterpret_cast<const uint2 *>(sVl + vrow);
+                    const uint2 l1 = *reinterpret_cast<const uint2 *>(sVl + vrow + 8);
+                    const u32x4 vl4 = {l0.x, l0.y, l1.x, l1.y};
+                    const bf16x8 al = __builtin_bit_cast(bf16x8, vl4);
+                    o[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, o[d], 0, 0, 0);
+                }
             }
         }
     }
@@ -346,10 +391,10 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
         }
 }
 
-template <int HD>
-bool launch_prefill_mfma_hd(hipStream_t st, int G, int T, int start_pos, int slot, const float *q, const float *kc,
-                            const float *vc, int nh, int nkv, int max_seq, u16 *o_hi, u16 *o_lo, float *o_f32) {
-#define APM(GG) hipLaunchKernelGGL((attn_prefill_mfma_kernel<HD, GG>), dim3((T + NQV / GG - 1) / (NQV / GG), nkv), \
+template <int HD, bool KB>
+bool launch_prefill_mfma_hd(hipStream_t st, int G, int T, int start_pos, int slot, const float *q, const void *kc,
+                            const void *vc, int nh, int nkv, int max_seq, u16 *o_hi, u16 *o_lo, float *o_f32) {
+#define APM(GG) hipLaunchKernelGGL((attn_prefill_mfma_kernel<HD, GG, KB>), dim3((T + NQV / GG - 1) / (NQV / GG), nkv), \
                                    dim3(256), 0, st, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, o_hi, o_lo, o_f32)
     switch (G) {
         case 1: APM(1); return true;
@@ -367,14 +412,26 @@ bool launch_prefill_mfma_hd(hipStream_t st, int G, int T, int start_pos, int slo
 
 }  // namespace
 
-void launch_attn_prefill(hipStream_t st, int T, int start_pos, int slot, const float *q, const float *kc,
-                         const float *vc, int nh, int nkv, int hd, int max_seq, int window, u16 *o_hi,
+void launch_attn_prefill(hipStream_t st, int T, int start_pos, int slot, const float *q, const void *kc,
+                         const void *vc, int kv_bf16, int nh, int nkv, int hd, int max_seq, int window, u16 *o_hi,
                          u16 *o_lo, float *o_f32) {
     (void)window;
     if (T <= 0) return;
     const int G = nh / nkv;
     dim3 grid((T + BQ - 1) / BQ, nkv);
-    if (hd == 128) launch_prefill_mfma_hd<128>(st, G, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, o_hi, o_lo, o_f32);
-    else if (hd == 64) launch_prefill_mfma_hd<64>(st, G, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, o_hi, o_lo, o_f32);
-    else launch_prefill_hd<16, 1>(st, G, grid, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, o_hi, o_lo, o_f32);
+#define LM(HD, KB) launch_prefill_mfma_hd<HD, KB>(st, G, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, o_hi, \
+                                                  o_lo, o_f32)
+#define LF(HD, KB) launch_prefill_hd<HD, 1, KB>(st, G, grid, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, \
+                                                o_hi, o_lo, o_f32)
+    if (kv_bf16) {
+        if (hd == 128) LM(128, true);
+        else if (hd == 64) LM(64, true);
+        else LF(16, true);
+    } else {
+        if (hd == 128) LM(128, false);
+        else if (hd == 64) LM(64, false);
+        else LF(16, false);
+    }
+#undef LM
+#undef LF
 }

@@ -208,8 +208,8 @@ void launch_rope_table(hipStream_t st, const int32_t *pos, int T, int hd, double
 __global__ void __launch_bounds__(256) rope_kv_kernel(
     Partials qkv, const float *__restrict__ bq, const float *__restrict__ bk, const float *__restrict__ bv,
     const float2 *__restrict__ tab, const int32_t *__restrict__ pos, const int32_t *__restrict__ slot,
-    int nh, int nkv, int hd, int pairing, float *__restrict__ q_out, float *__restrict__ kc,
-    float *__restrict__ vc, int max_seq, int ring) {
+    int nh, int nkv, int hd, int pairing, float *__restrict__ q_out, void *__restrict__ kc,
+    void *__restrict__ vc, int max_seq, int ring, int kv_bf16) {
     const int t = blockIdx.x;
     const int qd = nh * hd, kvd = nkv * hd, half = hd / 2;
     const int npairs = (qd + 2 * kvd) / 2;
@@ -242,21 +242,28 @@ __global__ void __launch_bounds__(256) rope_kv_kernel(
         q_out[(size_t)t * qd + e0c] = e0;
         q_out[(size_t)t * qd + e1c] = e1;
     } else {
-        float *cache = base == qd ? kc : vc;
+        void *cache = base == qd ? kc : vc;
         const size_t dst = ((slot_base + head) * max_seq + s) * hd;
-        cache[dst + e0c - head * hd] = e0;
-        cache[dst + e1c - head * hd] = e1;
+        if (kv_bf16) {
+            u16 *c16 = static_cast<u16 *>(cache);
+            c16[dst + e0c - head * hd] = (u16)f32_to_bf16_bits(e0);
+            c16[dst + e1c - head * hd] = (u16)f32_to_bf16_bits(e1);
+        } else {
+            float *c32 = static_cast<float *>(cache);
+            c32[dst + e0c - head * hd] = e0;
+            c32[dst + e1c - head * hd] = e1;
+        }
     }
 }
 
 void launch_rope_kv(hipStream_t st, int T, Partials qkv, const float *bq, const float *bk,
                     const float *bv, const float2 *tab, const int32_t *pos, const int32_t *slot,
-                    int nh, int nkv, int hd, int pairing, float *q_out, float *kc, float *vc, int max_seq,
-                    int ring) {
+                    int nh, int nkv, int hd, int pairing, float *q_out, void *kc, void *vc, int max_seq,
+                    int ring, int kv_bf16) {
     if (T <= 0) return;
     const int npairs = (nh + 2 * nkv) * hd / 2;
     hipLaunchKernelGGL(rope_kv_kernel, dim3(T, (npairs + 255) / 256), dim3(256), 0, st, qkv, bq, bk, bv, tab, pos,
-                       slot, nh, nkv, hd, pairing, q_out, kc, vc, max_seq, ring);
+                       slot, nh, nkv, hd, pairing, q_out, kc, vc, max_seq, ring, kv_bf16);
 }
 
 // ---- SwiGLU activation -----------------------------------------------------

@@ -40,12 +40,13 @@ void launch_rope_table(hipStream_t st, const int32_t *pos, int T, int hd, double
                        double factor, double low, double high, int orig_ctx, float2 *tab);
 
 // q/k/v (+bias) -> RoPE on q and k -> q_out [T][q_dim]; k, v stored in the
-// layer's cache [slot][kvh][max_seq][hd] at position pos % max_seq (ring) or pos.
+// layer's cache [slot][kvh][max_seq][hd] at position pos % max_seq (ring) or pos,
+// as fp32, or as nearest-even bf16 when kv_bf16 is set.
 // pairing 0 rotates elements (2i, 2i+1) of a head, 1 rotates (i, i + hd/2).
 void launch_rope_kv(hipStream_t st, int T, Partials qkv, const float *bq, const float *bk,
                     const float *bv, const float2 *tab, const int32_t *pos, const int32_t *slot,
-                    int nh, int nkv, int hd, int pairing, float *q_out, float *kc, float *vc, int max_seq,
-                    int ring);
+                    int nh, int nkv, int hd, int pairing, float *q_out, void *kc, void *vc, int max_seq,
+                    int ring, int kv_bf16);
 
 // act[t][j] = silu(g) * u with g = gu(t, j), u = gu(t, F + j); written as bf16
 // (hi, lo) and/or fp32 with row stride F.
@@ -71,11 +72,12 @@ void launch_gemm_f32(hipStream_t st, const WSeg *segs, int nseg, int K, const fl
                      int M, float *out, int ldo);
 
 // Split-KV decode attention.  Row b: query q[b][nh*hd], slot slot[b], position
-// pos[b]; keys/values of positions [lo, pos] in the layer cache.  Writes the
+// pos[b]; keys/values of positions [lo, pos] in the layer cache (fp32, or bf16
+// when kv_bf16 is set).  Writes the
 // attention output as bf16 (hi, lo) and/or fp32 rows [B][nh*hd].
-int attn_decode_splits(int B, int nkv, int readable, int hd, int G);
-void launch_attn_decode(hipStream_t st, int B, const float *q, const float *kc, const float *vc,
-                        const int32_t *pos, const int32_t *slot, int nh, int nkv, int hd,
+int attn_decode_splits(int B, int nkv, int readable, int hd, int G, int kv_bf16);
+void launch_attn_decode(hipStream_t st, int B, const float *q, const void *kc, const void *vc,
+                        int kv_bf16, const int32_t *pos, const int32_t *slot, int nh, int nkv, int hd,
                         int max_seq, int window, int splits, float *part, u16 *o_hi, u16 *o_lo,
                         float *o_f32);
 
@@ -83,7 +85,7 @@ void launch_attn_decode(hipStream_t st, int B, const float *q, const float *kc, 
 // start_pos..start_pos+T-1, reading keys/values from the layer cache (the
 // chunk's own K/V already stored there).
 void launch_attn_prefill(hipStream_t st, int T, int start_pos, int slot, const float *q,
-                         const float *kc, const float *vc, int nh, int nkv, int hd, int max_seq,
+                         const void *kc, const void *vc, int kv_bf16, int nh, int nkv, int hd, int max_seq,
                          int window, u16 *o_hi, u16 *o_lo, float *o_f32);
 
 // MoE.  Router logits [T][E] (a GEMV/GEMM output) -> softmax, top-k by repeated

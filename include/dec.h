@@ -97,7 +97,14 @@ typedef struct dec_config {
     int32_t rope_pairing;
     int32_t rope_scaling;
     int32_t rope_orig_ctx;
-    int32_t kv_dtype;          /* DEC_KV_F32 or DEC_KV_BF16 (K/V rounded to nearest even when stored) */
+    /* Element type of the K/V cache (rml "The decoder", section "Attend": the
+       cache has a choice of element type and attention widens each row to fp32
+       as it reads it).  DEC_KV_F32: fp32.  DEC_KV_BF16: each rotated key and
+       each value element is rounded to the nearest-even bf16 when stored,
+       halving the cache's bytes and its bytes read per decode step; every
+       later read (decode and prefill) sees the rounded value.  Arithmetic
+       stays fp32. */
+    int32_t kv_dtype;
     double rope_factor;
     double rope_low_freq_factor;
     double rope_high_freq_factor;

@@ -1,7 +1,19 @@
 """Helpers shared by the GPU parity tests: one seeded model on both sides, and
 the tolerance checks of the forward (rel L2 <= 1e-3 and max |diff| <= 2e-2 on
 logits; rel L2 <= 1e-3 per layer on hidden states; greedy tokens and expert
-ids exact wherever the oracle's margin exceeds 1e-3)."""
+ids exact wherever the oracle's margin exceeds 1e-3).
+
+A bf16 K/V cache has its own bound, set by its rounding and how that rounding
+propagates (zLLM "The Algorithm Layer", section 6: tolerances follow the
+dtype and the error propagation, and rest on evidence for bf16 outputs).
+Every stored element is rounded to bf16 from an fp32 value that carries its
+implementation's own summation-order error, so two correct implementations
+round some elements to neighbouring bf16 values, and those one-ulp
+differences feed every later layer.  The reference is then the oracle's fp64
+instantiation (exact arithmetic, the same rounding at the same point) and the
+bound is 4u = 2^-7 on logits and hidden states, u = 2^-9 being bf16's unit
+roundoff; the CPU tests pin the oracle's own fp32-vs-fp64 spread under the
+same bound.  Greedy tokens must match where the margin exceeds 1e-2."""
 from __future__ import annotations
 
 import numpy as np
@@ -14,6 +26,20 @@ LOGIT_REL_L2 = 1e-3
 LOGIT_MAX_ABS = 2e-2
 HIDDEN_REL_L2 = 1e-3
 MARGIN = 1e-3
+KV_BF16_REL_L2 = 2.0 ** -7
+KV_BF16_MARGIN = 1e-2
+
+
+def tol(cfg) -> dict:
+    """Tolerances for a config: the fp32-cache defaults, or the bf16-cache bound."""
+    if getattr(cfg, "kv_bf16", False):
+        return {"rel": KV_BF16_REL_L2, "margin": KV_BF16_MARGIN}
+    return {"rel": LOGIT_REL_L2, "margin": MARGIN}
+
+
+def oracle_kind(cfg) -> str:
+    """The oracle instantiation a config's GPU results are compared with."""
+    return "f64" if getattr(cfg, "kv_bf16", False) else "f32"
 
 
 def to_device(w: dict) -> dict:
@@ -28,30 +54,30 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-30))
 
 
-def check_logits(gpu, ref, what=""):
+def check_logits(gpu, ref, what="", rel=LOGIT_REL_L2, margin=None):
     g = np.asarray(gpu, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
     rl = rel_l2(g, r)
     mx = float(np.max(np.abs(g - r)))
-    assert rl <= LOGIT_REL_L2 and mx <= LOGIT_MAX_ABS, f"{what}: logits rel L2 {rl:.3e}, max |diff| {mx:.3e}"
+    assert rl <= rel and mx <= LOGIT_MAX_ABS, f"{what}: logits rel L2 {rl:.3e}, max |diff| {mx:.3e}"
     return rl, mx
 
 
-def check_argmax(gpu_row, ref_row, what=""):
+def check_argmax(gpu_row, ref_row, what="", rel=None, margin=MARGIN):
     r = np.asarray(ref_row, dtype=np.float64)
     top = np.argsort(-r, kind="stable")[:2]
-    margin = r[top[0]] - r[top[1]]
+    gap = r[top[0]] - r[top[1]]
     g = int(np.argmax(np.asarray(gpu_row)))
-    if margin > MARGIN:
-        assert g == int(top[0]), f"{what}: argmax {g} != {int(top[0])} (margin {margin:.2e})"
+    if gap > margin:
+        assert g == int(top[0]), f"{what}: argmax {g} != {int(top[0])} (margin {gap:.2e})"
     else:  # a legitimate tie: the GPU token must be one of the near-best
-        assert r[top[0]] - r[g] <= MARGIN, f"{what}: argmax {g} not within margin"
+        assert r[top[0]] - r[g] <= margin, f"{what}: argmax {g} not within margin"
 
 
-def check_hidden(gpu, ref, what=""):
+def check_hidden(gpu, ref, what="", rel=HIDDEN_REL_L2, margin=None):
     for l in range(ref.shape[0]):
         rl = rel_l2(gpu[l], ref[l])
-        assert rl <= HIDDEN_REL_L2, f"{what}: hidden after layer {l - 1} rel L2 {rl:.3e}"
+        assert rl <= rel, f"{what}: hidden after layer {l - 1} rel L2 {rl:.3e}"
 
 
 def check_experts(gpu_ids, ref_ids, ref_router, k, what=""):
@@ -83,7 +109,8 @@ class Pair:
         self.w = weights if weights is not None else synth.make_weights(cfg, seed=seed)
         self.wd = to_device(self.w)
         self.gpu = DecModel(cfg, self.wd, max_batch=n_slots, max_prefill=max_prefill, max_seq=max_seq)
-        self.ora = O.OracleModel(cfg, self.w, n_slots=n_slots, max_seq=max_seq)
+        self.ora = O.OracleModel(cfg, self.w, n_slots=n_slots, max_seq=max_seq, kind=oracle_kind(cfg))
+        self.tol = tol(cfg)
 
     def capture_buffers(self, rows):
         c = self.cfg

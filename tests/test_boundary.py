@@ -40,6 +40,13 @@ def test_workspace_bytes_is_host_only_and_validates():
     assert D.workspace_bytes(configs.TINY, 1, 0) == 0
 
 
+def test_bf16_cache_halves_the_kv_bytes():
+    _lib()
+    f32 = D.workspace_bytes(configs.MISTRAL, max_batch=32, max_prefill=4096)
+    b16 = D.workspace_bytes(configs.MISTRAL.replace(kv_bf16=True), max_batch=32, max_prefill=4096)
+    assert f32 - b16 == 2 * 32 * 32 * 8 * 4096 * 128 * 2   # K and V, 2 bytes saved per element
+
+
 def _create(cfg, max_batch=2, max_prefill=8, ws=None, ws_bytes=None, **over):
     L = _lib()
     c = D.make_config(cfg, max_batch, max_prefill)
@@ -67,6 +74,10 @@ def test_create_validation():
     assert _create(configs.TINY, n_experts=2, top_k=3)[0] == D.DEC_ERR_INVALID   # top_k > n_experts
     assert _create(configs.TINY_BF16, ffn_dim=100)[0] == D.DEC_ERR_UNSUPPORTED    # bf16 tiles need 64 | ffn
     assert _create(configs.TINY_WINDOW, max_seq=6)[0] == D.DEC_ERR_INVALID       # ring longer than the window
+    assert _create(configs.TINY, kv_dtype=2)[0] == D.DEC_ERR_INVALID              # no such cache type
+    rc, h, L = _create(configs.TINY_KVBF16)
+    assert rc == D.DEC_OK
+    L.dec_destroy(h)
     rc, h, L = _create(configs.TINY)
     assert rc == D.DEC_OK
     L.dec_destroy(h)

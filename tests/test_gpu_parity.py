@@ -24,9 +24,9 @@ def _run_stream(pair, prompt, steps, what, slot=0):
     g = pair.gpu.prefill(prompt)
     r = pair.ora.prefill(prompt, capture=True)
     torch.cuda.synchronize()
-    check_logits(g.cpu().numpy(), r["logits"][0], f"{what} prefill")
-    check_argmax(g.cpu().numpy(), r["logits"][0], f"{what} prefill")
-    check_hidden(hid.cpu().numpy(), r["hidden"], f"{what} prefill")
+    check_logits(g.cpu().numpy(), r["logits"][0], f"{what} prefill", **pair.tol)
+    check_argmax(g.cpu().numpy(), r["logits"][0], f"{what} prefill", **pair.tol)
+    check_hidden(hid.cpu().numpy(), r["hidden"], f"{what} prefill", **pair.tol)
     if c.n_experts:
         check_experts(ids.cpu().numpy(), r["ids"], r["router"], c.top_k, f"{what} prefill")
     nxt = int(np.argmax(r["logits"][0]))
@@ -36,9 +36,9 @@ def _run_stream(pair, prompt, steps, what, slot=0):
         g = pair.gpu.decode([nxt], [p])
         r = pair.ora.decode([nxt], [p], capture=True)
         torch.cuda.synchronize()
-        check_logits(g.cpu().numpy()[0], r["logits"][0], f"{what} step {s}")
-        check_argmax(g.cpu().numpy()[0], r["logits"][0], f"{what} step {s}")
-        check_hidden(hid.cpu().numpy(), r["hidden"], f"{what} step {s}")
+        check_logits(g.cpu().numpy()[0], r["logits"][0], f"{what} step {s}", **pair.tol)
+        check_argmax(g.cpu().numpy()[0], r["logits"][0], f"{what} step {s}", **pair.tol)
+        check_hidden(hid.cpu().numpy(), r["hidden"], f"{what} step {s}", **pair.tol)
         if c.n_experts:
             check_experts(ids.cpu().numpy(), r["ids"], r["router"], c.top_k, f"{what} step {s}")
         nxt = int(np.argmax(r["logits"][0]))

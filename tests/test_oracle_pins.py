@@ -487,3 +487,27 @@ def test_bf16_kv_rows_are_nearest_even_bf16_of_fp32_rows():
     rb = b.decode([3], [5])["logits"]
     rel = np.linalg.norm(ra - rb) / np.linalg.norm(rb)
     assert 0 < rel < 2e-2
+
+
+def test_bf16_cache_spread_between_oracle_precisions_is_within_its_bound():
+    """Evidence for the bf16-cache tolerance (4u = 2^-7, u the bf16 unit
+    roundoff): the oracle's fp32 and fp64 instantiations, each rounding K/V to
+    bf16 at store, differ by far more than with an fp32 cache (a rounding
+    decision flips on fp32 noise and the one-ulp change feeds later layers) yet
+    stay within the bound at 30 layers."""
+    B, P = 8, 4
+    spread = {}
+    for kvb in (False, True):
+        cfg = configs.SMOLLM2.replace(kv_bf16=kvb)
+        w = synth.make_weights(cfg)
+        pr = synth.prompts(cfg, B, P)
+        out = {}
+        for kind in ("f32", "f64"):
+            m = O.OracleModel(cfg, w, n_slots=B, kind=kind)
+            for b in range(B):
+                m.prefill(pr[b].tolist(), slot=b)
+            out[kind] = m.decode([1 + b for b in range(B)], [P] * B)["logits"].astype(np.float64)
+        spread[kvb] = max(np.linalg.norm(out["f32"][b] - out["f64"][b]) / np.linalg.norm(out["f64"][b])
+                          for b in range(B))
+    assert spread[False] < 1e-5
+    assert 20 * spread[False] < spread[True] <= 2.0 ** -7
