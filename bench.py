@@ -31,7 +31,16 @@ HBM_PEAK_GBS = 8000.0
 # passes (FETCH_SIZE, WRITE_SIZE) scaled by what the same counters read for a
 # 1 GiB device copy (x2.000 and x1.000): reported only while the kernel's
 # sources hash to the ones profiled, and only for the profiled workload.
-MEASURED_TRAFFIC = {}
+_ATTN_SOURCES = {"decoder_only_forward_amd/csrc/k_attn_decode.hip":
+                 "1084c52bf6de3c084abce53d1b288424c98f0d0cf2b8dbe1236f077a5378e7b6",
+                 "decoder_only_forward_amd/csrc/common.h":
+                 "394ed98a1109455d98e2b24652372937a85b2028e1e5c3ff1d6749474c8ff8b6"}
+MEASURED_TRAFFIC = {
+    ("attn_decode_kernel", "fp32"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
+                                     "bytes_per_launch": 1076060816},
+    ("attn_decode_kernel", "bf16"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
+                                     "bytes_per_launch": 539231560},
+}
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode tok/s + prefill tok/s (Mistral-7B shape) and % of HBM / MFMA roofline"
 
