@@ -136,6 +136,18 @@ def run_workload(cfg, wd, B, P, steps, warmup, small_batches=()):
     ms_step = dt * 1e3 / steps
     value = B * steps / dt
     log(f"[{kvname} KV] decode B={B}: {ms_step:.2f} ms/step, {value:.1f} tok/s ({model.graph_count()} graphs)")
+    # timed region 1b: the same steps as one device-resident greedy loop (the
+    # choices feed the next step on the GPU; one graph replay per step)
+    loop_logits = torch.empty((B, cfg.vocab), device="cuda")
+    loop_out = torch.empty((steps, B), dtype=torch.int32, device="cuda")
+    model.decode_greedy(toks, min(2, steps), logits=loop_logits, out=loop_out[:min(2, steps)])  # capture
+    torch.cuda.synchronize()
+    t = time.perf_counter()
+    model.decode_greedy(toks, steps, logits=loop_logits, out=loop_out)
+    torch.cuda.synchronize()
+    dt_loop = time.perf_counter() - t
+    toks[:] = loop_out[-1].cpu().numpy()
+    log(f"[{kvname} KV] decode B={B} device loop: {dt_loop * 1e3 / steps:.2f} ms/step, {B * steps / dt_loop:.1f} tok/s")
     # timed region 2: the same steps with every GEMV and attention launch
     # bracketed by HIP events on the library's stream (eager launches)
     model.timing_enable(D.DEC_K_GEMV)
@@ -178,7 +190,8 @@ def run_workload(cfg, wd, B, P, steps, warmup, small_batches=()):
     del model
     torch.cuda.empty_cache()
     return {"value": value, "ms_step": ms_step, "pre_med": pre_med, "gemm": gemm_t, "apre": apre_t,
-            "gemv": gemv_t, "attn": attn_t, "extra": extra, "dt_timed": dt_timed}
+            "gemv": gemv_t, "attn": attn_t, "extra": extra, "dt_timed": dt_timed,
+            "loop": {"tok_s": round(B * steps / dt_loop, 2), "ms_per_step": round(dt_loop * 1e3 / steps, 3)}}
 
 
 def main():
@@ -264,6 +277,7 @@ def main():
         "prefill_tok_s": round(P / (pre_med * 1e-3), 1),
         "prefill_ms": round(pre_med, 2),
         "decode": extra,
+        "decode_device_loop": main_run["loop"],
         "ms_per_step_with_kernel_events": round(dt_timed * 1e3 / args.steps, 3),
         "roofline_kernels": {"gemv_decode": roof(gemv_t, "hbm"), "gemm_prefill": roof(gemm_t, "mfma"),
                              "attn_prefill": roof(apre_t, "mfma")},
@@ -288,6 +302,7 @@ def main():
             "prefill_tok_s": round(P / (bf16_run["pre_med"] * 1e-3), 1),
             "prefill_ms": round(bf16_run["pre_med"], 2),
             "decode": bf16_run["extra"],
+            "decode_device_loop": bf16_run["loop"],
             "ms_per_step_with_kernel_events": round(bf16_run["dt_timed"] * 1e3 / args.steps, 3),
             "roofline": attn_roof(bf16_run["attn"], "bf16"),
             "roofline_kernels": {"gemv_decode": roof(bf16_run["gemv"], "hbm"),

@@ -37,6 +37,7 @@ struct Timing {
 // timing and test captures run eagerly instead.
 struct GraphEntry {
     int B = 0, S = 0;
+    bool greedy = false;    // ends with the greedy choice into amax (device loop)
     float *logits = nullptr;
     hipGraph_t graph = nullptr;
     hipGraphExec_t exec = nullptr;
@@ -114,7 +115,7 @@ bool plan(const dec_config &c, Plan &p) {
         if (T <= 0) continue;
         need((int)(qd + 2 * kvd), (int)d, T);
         need((int)d, (int)qd, T);
-        need(c.vocab, (int)d, std::min(T, c.max_batch));
+        need(c.vocab, (int)d, std::min(T, 64));  // LM head: decode rows or <= 64 all-logits rows
         if (E) {
             const int TP = T * (int)k;
             need((int)E, (int)d, T);
@@ -267,16 +268,19 @@ struct Pass {
     size_t cap_rows;
 };
 
+// Projection of T rows.  The result is a set of split partials in `part`; a
+// single-split result (GEMM, fp32 weights) goes to `out` instead when given.
 Partials proj(dec_model *m, const WSeg *segs, int nseg, int K, int T, const u16 *hi, const u16 *lo,
-              const float *f32, int lda) {
+              const float *f32, int lda, float *out = nullptr) {
     int N = 0;
     for (int i = 0; i < nseg; i++) N += segs[i].rows;
     const bool gemv = T <= 64;
+    float *dst = out ? out : m->part;
     if (m->wf32) {
         Tick tk(m, gemv ? DEC_K_GEMV : DEC_K_GEMM);
-        launch_gemm_f32(m->st, segs, nseg, K, f32, lda, T, m->part, N);
+        launch_gemm_f32(m->st, segs, nseg, K, f32, lda, T, dst, N);
         tk.done((double)N * K * 4 + (double)T * K * 4 + (double)T * N * 4, 2.0 * T * N * K);
-        return Partials{m->part, 1, 0, N};
+        return Partials{dst, 1, 0, N};
     }
     if (gemv) {
         const int S = gemv_splits(N, K, T);
@@ -286,9 +290,9 @@ Partials proj(dec_model *m, const WSeg *segs, int nseg, int K, int T, const u16 
         return Partials{m->part, S, (size_t)T * N, N};
     }
     Tick tk(m, DEC_K_GEMM);
-    launch_gemm(m->st, segs, nseg, K, hi, lo, lda, T, m->part, N);
+    launch_gemm(m->st, segs, nseg, K, hi, lo, lda, T, dst, N);
     tk.done((double)N * K * 2 + (double)T * K * 4 + (double)T * N * 4, 2.0 * T * N * K);
-    return Partials{m->part, 1, 0, N};
+    return Partials{dst, 1, 0, N};
 }
 
 // Grouped expert projection over TP = T*k pair rows in expert order.
@@ -401,8 +405,8 @@ void run_pass(dec_model *m, const Pass &ps) {
         WSeg hs[1] = {{head, c.vocab}};
         const size_t ro = (size_t)ps.logit_row0 * d;
         Partials pl = proj(m, hs, 1, d, ps.logit_rows, ah ? ah + ro : nullptr, al ? al + ro : nullptr,
-                           af ? af + ro : nullptr, d);
-        launch_reduce_splits(st, pl, ps.logit_rows, c.vocab, ps.logits, c.vocab);
+                           af ? af + ro : nullptr, d, ps.logits);
+        if (pl.p != ps.logits) launch_reduce_splits(st, pl, ps.logit_rows, c.vocab, ps.logits, c.vocab);
     }
 }
 
@@ -437,10 +441,12 @@ unsigned timing_mask(const dec_model *m) {
     return k;
 }
 
-int replay(dec_model *m, GraphEntry &g, const RowArgs &ra) {
+// Launch a captured step; its first node (the row setup) takes this step's rows,
+// token source and history row.
+int replay(dec_model *m, GraphEntry &g, const RowArgs &ra, const int32_t *src, int32_t *hist) {
     int B = g.B;
     int32_t *tok = m->tok, *ps = m->pos, *sl = m->slot;
-    void *args[] = {(void *)&ra, (void *)&B, (void *)&tok, (void *)&ps, (void *)&sl};
+    void *args[] = {(void *)&ra, (void *)&B, (void *)&src, (void *)&hist, (void *)&tok, (void *)&ps, (void *)&sl};
     hipKernelNodeParams kp = g.kp;
     kp.kernelParams = args;
     kp.extra = nullptr;
@@ -453,18 +459,20 @@ int replay(dec_model *m, GraphEntry &g, const RowArgs &ra) {
 }
 
 // Capture one decode step into a graph (returns null if capture is not possible).
-GraphEntry *capture(dec_model *m, const RowArgs &ra, int B, int S, const int *pos, float *logits) {
+// A greedy step ends with the argmax of its logits into amax.
+GraphEntry *capture(dec_model *m, const RowArgs &ra, int B, int S, const int *pos, float *logits, bool greedy) {
     if (!graph_stream(m)) return nullptr;
     GraphEntry g;
     g.B = B;
     g.S = S;
+    g.greedy = greedy;
     g.logits = logits;
     hipStream_t user = m->st;
     if (hipEventRecord(m->fence_in, user) != hipSuccess || hipStreamWaitEvent(m->cs, m->fence_in, 0) != hipSuccess)
         return nullptr;
     if (hipStreamBeginCapture(m->cs, hipStreamCaptureModeThreadLocal) != hipSuccess) return nullptr;
     m->st = m->cs;
-    launch_set_rows(m->st, ra, B, m->tok, m->pos, m->slot);
+    launch_set_rows(m->st, ra, B, nullptr, nullptr, m->tok, m->pos, m->slot);
     Pass ps{};
     ps.T = B;
     ps.decode = true;
@@ -475,6 +483,7 @@ GraphEntry *capture(dec_model *m, const RowArgs &ra, int B, int S, const int *po
     ps.cap_row = 0;
     ps.cap_rows = B;
     run_pass(m, ps);
+    if (greedy) launch_argmax(m->st, logits, B, m->c.vocab, m->amax);
     m->st = user;
     hipGraph_t graph = nullptr;
     const hipError_t ec = hipStreamEndCapture(m->cs, &graph);
@@ -583,7 +592,12 @@ void dec_destroy(dec_handle h) {
 }
 
 int dec_prefill(dec_handle h, int seq, const int32_t *tokens, int n, int start_pos, float *logits) {
-    if (!h || !tokens || !logits) return DEC_ERR_INVALID;
+    return dec_prefill_ex(h, seq, tokens, n, start_pos, logits, 0);
+}
+
+int dec_prefill_ex(dec_handle h, int seq, const int32_t *tokens, int n, int start_pos, float *logits,
+                   int all_logits) {
+    if (!h || !tokens || !logits || (all_logits != 0 && all_logits != 1)) return DEC_ERR_INVALID;
     const dec_config &c = h->c;
     if (seq < 0 || seq >= c.max_batch || n <= 0) return DEC_ERR_INVALID;
     if (n > c.max_prefill) return DEC_ERR_RANGE;
@@ -603,14 +617,14 @@ int dec_prefill(dec_handle h, int seq, const int32_t *tokens, int n, int start_p
             ra.tok[0] = tokens[t];
             ra.pos[0] = start_pos + t;
             ra.slot[0] = seq;
-            launch_set_rows(h->st, ra, 1, h->tok, h->pos, h->slot);
+            launch_set_rows(h->st, ra, 1, nullptr, nullptr, h->tok, h->pos, h->slot);
             Pass ps{};
             ps.T = 1;
             ps.decode = true;
             ps.seq = seq;
             const int hp = start_pos + t;
             ps.hpos = &hp;
-            ps.logits = (t == n - 1) ? logits : nullptr;
+            ps.logits = all_logits ? logits + (size_t)t * c.vocab : (t == n - 1) ? logits : nullptr;
             ps.logit_row0 = 0;
             ps.logit_rows = 1;
             ps.cap_row = t;
@@ -628,8 +642,8 @@ int dec_prefill(dec_handle h, int seq, const int32_t *tokens, int n, int start_p
         ps.seq = seq;
         ps.hpos = nullptr;
         ps.logits = logits;
-        ps.logit_row0 = n - 1;
-        ps.logit_rows = 1;
+        ps.logit_row0 = all_logits ? 0 : n - 1;
+        ps.logit_rows = all_logits ? n : 1;
         ps.cap_row = 0;
         ps.cap_rows = n;
         run_pass(h, ps);
@@ -661,7 +675,7 @@ int dec_decode(dec_handle h, int B, const int32_t *tokens, const int32_t *pos, f
         const int S = attn_splits_for(h, B, pos);
         GraphEntry *g = nullptr;
         for (auto &e : h->graphs)
-            if (e.B == B && e.S == S && e.logits == logits) g = &e;
+            if (e.B == B && e.S == S && e.logits == logits && !e.greedy) g = &e;
         if (!g) {
             const std::vector<long long> key = {B, S, (long long)(uintptr_t)logits};
             int *count = nullptr;
@@ -670,17 +684,17 @@ int dec_decode(dec_handle h, int B, const int32_t *tokens, const int32_t *pos, f
             if (!count) {
                 h->seen.push_back({key, 1});
             } else if (*count == 1) {
-                g = capture(h, ra, B, S, pos, logits);
+                g = capture(h, ra, B, S, pos, logits, false);
                 *count = g ? 2 : 3;  // 3: capture failed, stay eager for this shape
             }
         }
         if (g) {
-            if (replay(h, *g, ra) != DEC_OK) return DEC_ERR_DEVICE;
+            if (replay(h, *g, ra, nullptr, nullptr) != DEC_OK) return DEC_ERR_DEVICE;
             for (int b = 0; b < B; b++) h->len[b] = pos[b] + 1;
             return DEC_OK;
         }
     }
-    launch_set_rows(h->st, ra, B, h->tok, h->pos, h->slot);
+    launch_set_rows(h->st, ra, B, nullptr, nullptr, h->tok, h->pos, h->slot);
     Pass ps{};
     ps.T = B;
     ps.decode = true;
@@ -693,6 +707,58 @@ int dec_decode(dec_handle h, int B, const int32_t *tokens, const int32_t *pos, f
     run_pass(h, ps);
     if (hipGetLastError() != hipSuccess) return DEC_ERR_DEVICE;
     for (int b = 0; b < B; b++) h->len[b] = pos[b] + 1;
+    return DEC_OK;
+}
+
+int dec_decode_greedy(dec_handle h, int B, const int32_t *tokens, int steps, int32_t *tokens_out, float *logits) {
+    if (!h || !tokens || !tokens_out || !logits) return DEC_ERR_INVALID;
+    const dec_config &c = h->c;
+    if (B <= 0 || B > c.max_batch || steps <= 0) return DEC_ERR_INVALID;
+    for (int b = 0; b < B; b++) {
+        if (tokens[b] < 0 || tokens[b] >= c.vocab) return DEC_ERR_INVALID;
+        if (!h->ring && (long)h->len[b] + steps > (long)c.max_seq) return DEC_ERR_RANGE;
+        if ((long)h->len[b] + steps > 0x7FFFFFFFL) return DEC_ERR_RANGE;
+    }
+    if (timing_mask(h) && harvest(h) != DEC_OK) return DEC_ERR_DEVICE;
+    const bool graphs = !h->cap_hidden && !h->cap_ids && !h->cap_router && !timing_mask(h);
+    int hpos[64];
+    for (int s = 0; s < steps; s++) {
+        RowArgs ra;
+        for (int b = 0; b < B; b++) {
+            ra.tok[b] = tokens[b];  // read by the first step only
+            ra.pos[b] = hpos[b] = h->len[b] + s;
+            ra.slot[b] = b;
+        }
+        // step s > 0 embeds the previous step's choice and appends it to the output
+        const int32_t *src = s ? h->amax : nullptr;
+        int32_t *hist = s ? tokens_out + (size_t)(s - 1) * B : nullptr;
+        GraphEntry *g = nullptr;
+        if (graphs) {
+            const int S = attn_splits_for(h, B, hpos);
+            for (auto &e : h->graphs)
+                if (e.B == B && e.S == S && e.logits == logits && e.greedy) g = &e;
+            if (!g && steps - s >= 2) g = capture(h, ra, B, S, hpos, logits, true);
+        }
+        if (g) {
+            if (replay(h, *g, ra, src, hist) != DEC_OK) return DEC_ERR_DEVICE;
+            continue;
+        }
+        launch_set_rows(h->st, ra, B, src, hist, h->tok, h->pos, h->slot);
+        Pass ps{};
+        ps.T = B;
+        ps.decode = true;
+        ps.hpos = hpos;
+        ps.logits = logits;
+        ps.logit_row0 = 0;
+        ps.logit_rows = B;
+        ps.cap_row = 0;
+        ps.cap_rows = B;
+        run_pass(h, ps);
+        launch_argmax(h->st, logits, B, c.vocab, h->amax);
+    }
+    launch_copy_ids(h->st, h->amax, B, tokens_out + (size_t)(steps - 1) * B);
+    if (hipGetLastError() != hipSuccess) return DEC_ERR_DEVICE;
+    for (int b = 0; b < B; b++) h->len[b] += steps;
     return DEC_OK;
 }
 

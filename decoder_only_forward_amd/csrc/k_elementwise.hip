@@ -352,17 +352,33 @@ void launch_reduce_splits(hipStream_t st, Partials src, int T, int N, float *dst
 
 // Decode rows travel as a kernel argument (no host buffer has to outlive the
 // call): tok/pos of row b, slot b.
-__global__ void set_rows_kernel(RowArgs a, int B, int32_t *__restrict__ tok, int32_t *__restrict__ pos,
-                                int32_t *__restrict__ slot) {
+// Decode rows: token, position and slot of each row.  The tokens come from the
+// arguments, or, when src is given, from device memory (the previous step's
+// greedy choice), which is then also appended to hist when that is given.
+__global__ void set_rows_kernel(RowArgs a, int B, const int32_t *__restrict__ src, int32_t *__restrict__ hist,
+                                int32_t *__restrict__ tok, int32_t *__restrict__ pos, int32_t *__restrict__ slot) {
     const int b = threadIdx.x;
     if (b >= B) return;
-    tok[b] = a.tok[b];
+    const int32_t t = src ? src[b] : a.tok[b];
+    if (hist) hist[b] = t;
+    tok[b] = t;
     pos[b] = a.pos[b];
     slot[b] = a.slot[b];
 }
 
-void launch_set_rows(hipStream_t st, const RowArgs &a, int B, int32_t *tok, int32_t *pos, int32_t *slot) {
-    hipLaunchKernelGGL(set_rows_kernel, dim3(1), dim3(64), 0, st, a, B, tok, pos, slot);
+void launch_set_rows(hipStream_t st, const RowArgs &a, int B, const int32_t *src, int32_t *hist, int32_t *tok,
+                     int32_t *pos, int32_t *slot) {
+    hipLaunchKernelGGL(set_rows_kernel, dim3(1), dim3(64), 0, st, a, B, src, hist, tok, pos, slot);
+}
+
+// dst[i] = src[i], i < n (n <= 64): the last greedy choice of a device loop.
+__global__ void copy_ids_kernel(const int32_t *__restrict__ src, int n, int32_t *__restrict__ dst) {
+    const int i = threadIdx.x;
+    if (i < n) dst[i] = src[i];
+}
+
+void launch_copy_ids(hipStream_t st, const int32_t *src, int n, int32_t *dst) {
+    hipLaunchKernelGGL(copy_ids_kernel, dim3(1), dim3(64), 0, st, src, n, dst);
 }
 
 // Prefill rows: positions start..start+T-1 of one slot.

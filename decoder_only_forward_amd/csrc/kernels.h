@@ -122,5 +122,9 @@ struct RowArgs {
     int32_t pos[64];
     int32_t slot[64];
 };
-void launch_set_rows(hipStream_t st, const RowArgs &a, int B, int32_t *tok, int32_t *pos, int32_t *slot);
+// Decode rows (B <= 64): tokens from a.tok, or from device src when given (also
+// appended to hist when given); positions and slots from a.
+void launch_set_rows(hipStream_t st, const RowArgs &a, int B, const int32_t *src, int32_t *hist, int32_t *tok,
+                     int32_t *pos, int32_t *slot);
+void launch_copy_ids(hipStream_t st, const int32_t *src, int n, int32_t *dst);
 void launch_set_seq_rows(hipStream_t st, int T, int start, int s, int32_t *pos, int32_t *slot);

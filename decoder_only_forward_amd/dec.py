@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(HERE, "libdec.so")
 
 DEC_OK, DEC_ERR_INVALID, DEC_ERR_RANGE, DEC_ERR_NOMEM, DEC_ERR_DEVICE, DEC_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 DEC_K_GEMV, DEC_K_ATTN_DECODE, DEC_K_GEMM, DEC_K_ATTN_PREFILL = 0, 1, 2, 3
-EXPORTS = ("dec_workspace_bytes", "dec_create", "dec_destroy", "dec_prefill", "dec_decode", "dec_kv_reset",
+EXPORTS = ("dec_workspace_bytes", "dec_create", "dec_destroy", "dec_prefill", "dec_prefill_ex", "dec_decode",
+           "dec_decode_greedy", "dec_kv_reset",
            "dec_graph_count", "dec_kv_length", "dec_greedy", "dec_sync", "dec_set_capture", "dec_timing_enable",
            "dec_timing_read", "dec_status_str")
 
@@ -73,8 +74,12 @@ def load():
     L.dec_destroy.argtypes = [vp]
     L.dec_prefill.restype = c_int
     L.dec_prefill.argtypes = [vp, c_int, vp, c_int, c_int, vp]
+    L.dec_prefill_ex.restype = c_int
+    L.dec_prefill_ex.argtypes = [vp, c_int, vp, c_int, c_int, vp, c_int]
     L.dec_decode.restype = c_int
     L.dec_decode.argtypes = [vp, c_int, vp, vp, vp]
+    L.dec_decode_greedy.restype = c_int
+    L.dec_decode_greedy.argtypes = [vp, c_int, vp, c_int, vp, vp]
     L.dec_kv_reset.restype = c_int
     L.dec_kv_reset.argtypes = [vp, c_int]
     L.dec_kv_length.restype = c_int
@@ -171,12 +176,17 @@ class DecModel:
             raise DecError(rc, what)
 
     def prefill(self, tokens: Sequence[int], seq: int = 0, start_pos: int = 0,
-                logits: Optional[torch.Tensor] = None) -> torch.Tensor:
+                logits: Optional[torch.Tensor] = None, all_logits: bool = False) -> torch.Tensor:
+        """Logits of the last position [vocab], or of every position [n, vocab]."""
         tok = _i32(tokens)
         if logits is None:
-            logits = torch.empty(self.cfg.vocab, dtype=torch.float32, device="cuda")
-        self._check(self.L.dec_prefill(self.h, seq, tok.ctypes.data, tok.size, start_pos, _dptr(logits)),
-                    "dec_prefill")
+            shape = (tok.size, self.cfg.vocab) if all_logits else (self.cfg.vocab,)
+            logits = torch.empty(shape, dtype=torch.float32, device="cuda")
+        if all_logits:
+            rc = self.L.dec_prefill_ex(self.h, seq, tok.ctypes.data, tok.size, start_pos, _dptr(logits), 1)
+        else:
+            rc = self.L.dec_prefill(self.h, seq, tok.ctypes.data, tok.size, start_pos, _dptr(logits))
+        self._check(rc, "dec_prefill")
         return logits
 
     def decode(self, tokens: Sequence[int], pos: Sequence[int],
@@ -187,6 +197,19 @@ class DecModel:
         self._check(self.L.dec_decode(self.h, tok.size, tok.ctypes.data, ps.ctypes.data, _dptr(logits)),
                     "dec_decode")
         return logits
+
+    def decode_greedy(self, tokens: Sequence[int], steps: int, logits: Optional[torch.Tensor] = None,
+                      out: Optional[torch.Tensor] = None):
+        """`steps` greedy steps on the device from tokens[b] at each row's length.
+        Returns (choices [steps, B] int32 on the device, logits [B, vocab])."""
+        tok = _i32(tokens)
+        if logits is None:
+            logits = torch.empty((tok.size, self.cfg.vocab), dtype=torch.float32, device="cuda")
+        if out is None:
+            out = torch.empty((steps, tok.size), dtype=torch.int32, device="cuda")
+        self._check(self.L.dec_decode_greedy(self.h, tok.size, tok.ctypes.data, steps, _dptr(out), _dptr(logits)),
+                    "dec_decode_greedy")
+        return out, logits
 
     def greedy(self, logits: torch.Tensor, B: int) -> np.ndarray:
         out = np.empty(B, dtype=np.int32)

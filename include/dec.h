@@ -172,6 +172,17 @@ DEC_API void dec_destroy(dec_handle h);
 DEC_API int dec_prefill(dec_handle h, int seq, const int32_t *tokens, int n, int start_pos, float *logits);
 
 /*
+ * dec_prefill with a choice of which rows get logits (rml "The decoder",
+ * section "One forward pass", step 7: only the rows that need logits get the
+ * final norm and the output product, the last row or, with all_logits, every
+ * row).  all_logits = 0: as dec_prefill.  all_logits = 1: logits is device
+ * float[n][vocab], row t the logits after position start_pos + t.  Any other
+ * value is DEC_ERR_INVALID.  Errors and state changes as dec_prefill.
+ */
+DEC_API int dec_prefill_ex(dec_handle h, int seq, const int32_t *tokens, int n, int start_pos, float *logits,
+                           int all_logits);
+
+/*
  * One decode step of B independent sequences (Pantheon, section "Batched
  * Multi-Sequence Decode"): row b uses slot b, reads token tokens[b] at
  * position pos[b] == slot b's committed length, and writes logits row b.
@@ -180,6 +191,26 @@ DEC_API int dec_prefill(dec_handle h, int seq, const int32_t *tokens, int n, int
  * On success each slot b < B has length pos[b] + 1.
  */
 DEC_API int dec_decode(dec_handle h, int B, const int32_t *tokens, const int32_t *pos, float *logits);
+
+/*
+ * `steps` greedy decode steps of B sequences with the tokens kept on the GPU
+ * (Pantheon, section "Optional GPU Paths": a GPU-resident decode runs the whole
+ * layer chain on the device with one synchronisation per step; here there is
+ * none inside the loop).  Step 0 reads tokens[b] (host int32[B]) for row b at
+ * position slot b's committed length; every later step reads the greedy
+ * choice of the step before it (largest logit, lowest id on ties, as
+ * dec_greedy), chosen on the device.  Each step is one captured graph replay.
+ *   tokens_out: device int32[steps][B]: row s holds the choices made from
+ *               step s's logits (the input of step s + 1).
+ *   logits:     device float[B][vocab], scratch for every step; it holds the
+ *               last step's logits when the call's work completes.
+ * Capacity is checked for all steps before anything is enqueued (a full
+ * cache is DEC_ERR_RANGE, bad ids or sizes DEC_ERR_INVALID; nothing changes).
+ * On success each slot b < B has length += steps.  Asynchronous on the
+ * handle's stream.
+ */
+DEC_API int dec_decode_greedy(dec_handle h, int B, const int32_t *tokens, int steps, int32_t *tokens_out,
+                              float *logits);
 
 /* Set slot `seq`'s committed length to 0 (seq = -1: every slot).  No memory is
    cleared: only min(pos+1, max_seq) positions are ever read. */

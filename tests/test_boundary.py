@@ -102,6 +102,13 @@ def test_bad_calls_change_nothing():
         (L.dec_decode, (h, 2, bad.ctypes.data, pos.ctypes.data, fake_logits), D.DEC_ERR_INVALID),
         (L.dec_kv_reset, (h, 5), D.DEC_ERR_INVALID),
         (L.dec_greedy, (h, fake_logits, 3, tok.ctypes.data), D.DEC_ERR_INVALID),
+        (L.dec_prefill_ex, (h, 0, tok.ctypes.data, 3, 0, fake_logits, 2), D.DEC_ERR_INVALID),   # all_logits 0/1
+        (L.dec_prefill_ex, (h, 0, bad.ctypes.data, 2, 0, fake_logits, 1), D.DEC_ERR_INVALID),
+        (L.dec_decode_greedy, (h, 2, tok.ctypes.data, 0, fake_logits, fake_logits), D.DEC_ERR_INVALID),  # 0 steps
+        (L.dec_decode_greedy, (h, 3, tok.ctypes.data, 2, fake_logits, fake_logits), D.DEC_ERR_INVALID),  # B > slots
+        (L.dec_decode_greedy, (h, 2, bad.ctypes.data, 2, fake_logits, fake_logits), D.DEC_ERR_INVALID),
+        (L.dec_decode_greedy, (h, 2, tok.ctypes.data, 17, fake_logits, fake_logits), D.DEC_ERR_RANGE),  # > max_seq
+        (L.dec_decode_greedy, (h, 2, tok.ctypes.data, 2, None, fake_logits), D.DEC_ERR_INVALID),
     ]
     for fn, args, want in cases:
         assert fn(*args) == want, (fn.__name__, args)
