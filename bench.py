@@ -186,12 +186,29 @@ def run_workload(cfg, wd, B, P, steps, warmup, small_batches=()):
         e = time.perf_counter() - t
         extra[f"b{bb}"] = {"tok_s": round(bb * n / e, 2), "ms_per_step": round(e * 1e3 / n, 3)}
         log(f"[{kvname} KV] decode B={bb}: {e * 1e3 / n:.2f} ms/step")
+    # AppendPrefill past the ring's size in one pass (deferred commit): 512
+    # tokens appended to slot 0, whose ring is already full
+    append = None
+    if cfg.sliding_window and cfg.max_seq == cfg.sliding_window:
+        n_app = min(512, P)
+        app = synth.prompts(cfg, 1, 3 * n_app, stream=synth.TEACHER_STREAM)[0].tolist()
+        ms = []
+        for i in range(3):
+            torch.cuda.synchronize()
+            t = time.perf_counter()
+            model.prefill(app[i * n_app:(i + 1) * n_app], seq=0, start_pos=model.length(0), logits=logits1)
+            torch.cuda.synchronize()
+            ms.append((time.perf_counter() - t) * 1e3)
+        med = float(np.median(ms))
+        append = {"tokens": n_app, "ms": round(med, 2), "tok_s": round(n_app / (med * 1e-3), 1)}
+        log(f"[{kvname} KV] append {n_app} tokens past the ring: {med:.1f} ms")
     model.close()
     del model
     torch.cuda.empty_cache()
     return {"value": value, "ms_step": ms_step, "pre_med": pre_med, "gemm": gemm_t, "apre": apre_t,
             "gemv": gemv_t, "attn": attn_t, "extra": extra, "dt_timed": dt_timed,
-            "loop": {"tok_s": round(B * steps / dt_loop, 2), "ms_per_step": round(dt_loop * 1e3 / steps, 3)}}
+            "loop": {"tok_s": round(B * steps / dt_loop, 2), "ms_per_step": round(dt_loop * 1e3 / steps, 3)},
+            "append": append}
 
 
 def main():
@@ -278,6 +295,7 @@ def main():
         "prefill_ms": round(pre_med, 2),
         "decode": extra,
         "decode_device_loop": main_run["loop"],
+        "append_prefill_past_ring": main_run["append"],
         "ms_per_step_with_kernel_events": round(dt_timed * 1e3 / args.steps, 3),
         "roofline_kernels": {"gemv_decode": roof(gemv_t, "hbm"), "gemm_prefill": roof(gemm_t, "mfma"),
                              "attn_prefill": roof(apre_t, "mfma")},
@@ -303,6 +321,7 @@ def main():
             "prefill_ms": round(bf16_run["pre_med"], 2),
             "decode": bf16_run["extra"],
             "decode_device_loop": bf16_run["loop"],
+            "append_prefill_past_ring": bf16_run["append"],
             "ms_per_step_with_kernel_events": round(bf16_run["dt_timed"] * 1e3 / args.steps, 3),
             "roofline": attn_roof(bf16_run["attn"], "bf16"),
             "roofline_kernels": {"gemv_decode": roof(bf16_run["gemv"], "hbm"),

@@ -47,7 +47,7 @@ struct GraphEntry {
 
 struct Plan {  // byte offsets into the workspace
     size_t kv_layer;        // elements of one layer's K (or V) cache
-    size_t k, v, x, a_hi, a_lo, a_f32, part, q, attn, rope, tok, pos, slot, amax, ssq;
+    size_t k, v, ck, cv, x, a_hi, a_lo, a_f32, part, q, attn, rope, tok, pos, slot, amax, ssq;
     size_t moe_ids, moe_w, moe_cnt, moe_off, moe_pairs, g_hi, g_lo, g_f32, moe_y;
     size_t part_floats, act_elems, total;
     int rows;               // max rows of one pass (max(max_batch, max_prefill))
@@ -67,6 +67,7 @@ struct dec_model {
     char *ws;
     Plan pl;
     char *kc, *vc;          // caches, kv_es bytes per element
+    char *ck, *cv;          // chunk K/V of a deferred-commit prefill (ring only)
     int kv_es;
     float *x, *a_f32, *part, *q, *attn, *moe_w, *g_f32, *moe_y, *ssq;
     u16 *a_hi, *a_lo, *g_hi, *g_lo;
@@ -136,6 +137,11 @@ bool plan(const dec_config &c, Plan &p) {
     const size_t es = c.kv_dtype == DEC_KV_BF16 ? 2 : 4;
     p.k = take(p.kv_layer * c.n_layers * es);
     p.v = take(p.kv_layer * c.n_layers * es);
+    // one layer's K/V of a prefill chunk held back from a ring cache until the
+    // chunk's attention is done (deferred commit)
+    const bool ring = c.sliding_window > 0 && c.max_seq == c.sliding_window;
+    p.ck = take(ring ? (size_t)c.max_prefill * kvd * es : 0);
+    p.cv = take(ring ? (size_t)c.max_prefill * kvd * es : 0);
     p.x = take((size_t)rows * d * 4);
     const bool f32w = c.weight_dtype == DEC_WEIGHT_F32;
     p.a_hi = take(f32w ? 0 : p.act_elems * 2);
@@ -260,6 +266,7 @@ struct Pass {
     bool decode;        // true: rows are independent sequences (split-KV attention)
     int start_pos;      // prefill: first position; slot = seq
     int seq;
+    bool deferred;      // prefill into a ring past its size: K/V held back until attention is done
     const int *hpos;    // host positions of the rows (for byte accounting)
     float *logits;      // destination, or nullptr (no LM head)
     int logit_row0;     // first row that gets logits
@@ -347,9 +354,11 @@ void run_pass(dec_model *m, const Pass &ps) {
         // q | k | v
         WSeg qkv[3] = {{w.wq, qd}, {w.wk, kvd}, {w.wv, kvd}};
         Partials pq = proj(m, qkv, 3, d, T, ah, al, af, d);
+        // K/V into the layer cache, or held in the chunk buffers (deferred commit)
         launch_rope_kv(st, T, pq, c.qkv_bias ? w.bq : nullptr, c.qkv_bias ? w.bk : nullptr,
-                       c.qkv_bias ? w.bv : nullptr, m->rope, m->pos, m->slot, nh, nkv, hd, c.rope_pairing, m->q, kc,
-                       vc, c.max_seq, m->ring, kvb);
+                       c.qkv_bias ? w.bv : nullptr, m->rope, m->pos, m->slot, nh, nkv, hd, c.rope_pairing, m->q,
+                       ps.deferred ? (void *)m->ck : (void *)kc, ps.deferred ? (void *)m->cv : (void *)vc,
+                       c.max_seq, m->ring, kvb, ps.deferred);
         // attention -> a (row stride qd)
         if (ps.decode) {
             const int S = attn_splits_for(m, T, ps.hpos);
@@ -358,12 +367,23 @@ void run_pass(dec_model *m, const Pass &ps) {
                                m->attn, ah, al, af);
             tk.done(kv_read_bytes(c, T, ps.hpos) + 2.0 * T * qd * 4, 0);
         } else {
-            double flops = 0;
-            for (int t = 0; t < T; t++) flops += 4.0 * hd * nh * (ps.start_pos + t + 1);
+            // keys per query: positions [p - window + 1, p] (window 0: [0, p])
+            const int W = c.sliding_window;
+            double flops = 0, keys = 0;
+            for (int t = 0; t < T; t++) {
+                const double p = ps.start_pos + t;
+                flops += 4.0 * hd * nh * (W ? std::min<double>(p + 1, W) : p + 1);
+            }
+            keys = W ? std::min<double>(ps.start_pos + T, (double)W + T) : ps.start_pos + T;
             Tick tk(m, DEC_K_ATTN_PREFILL);
-            launch_attn_prefill(st, T, ps.start_pos, ps.seq, m->q, kc, vc, kvb, nh, nkv, hd, c.max_seq,
-                                c.sliding_window, ah, al, af);
-            tk.done((double)(ps.start_pos + T) * kvd * 2 * m->kv_es + 2.0 * T * qd * 4, flops);
+            // history is read through ring slots only when the call reaches past
+            // max_seq (the deferred case); below that, slot == position
+            launch_attn_prefill(st, T, ps.start_pos, ps.seq, m->q, kc, vc, kvb, nh, nkv, hd, c.max_seq, W,
+                                ps.deferred, ps.deferred ? m->ck : nullptr, ps.deferred ? m->cv : nullptr, ah, al,
+                                af);
+            tk.done(keys * kvd * 2 * m->kv_es + 2.0 * T * qd * 4, flops);
+            if (ps.deferred)
+                launch_commit_chunk(st, m->ck, m->cv, T, ps.start_pos, ps.seq, nkv, hd, m->kv_es, c.max_seq, kc, vc);
         }
         // output projection, residual, FFN norm
         WSeg wo[1] = {{w.wo, d}};
@@ -546,6 +566,8 @@ int dec_create(const dec_config *cfg, const dec_weights *w, void *workspace, siz
     char *b = m->ws;
     m->kc = b + p.k;
     m->vc = b + p.v;
+    m->ck = b + p.ck;
+    m->cv = b + p.cv;
     m->kv_es = cfg->kv_dtype == DEC_KV_BF16 ? 2 : 4;
     m->x = (float *)(b + p.x);
     m->a_hi = (u16 *)(b + p.a_hi);
@@ -571,7 +593,9 @@ int dec_create(const dec_config *cfg, const dec_weights *w, void *workspace, siz
     m->moe_y = (float *)(b + p.moe_y);
     m->len.assign(cfg->max_batch, 0);
     m->wf32 = cfg->weight_dtype == DEC_WEIGHT_F32;
-    m->ring = cfg->sliding_window > 0;
+    // a ring of max_seq == window slots; a window longer than max_seq never
+    // wraps (positions are capped at max_seq like a full-causal cache)
+    m->ring = cfg->sliding_window > 0 && cfg->max_seq == cfg->sliding_window;
     *out = m;
     return DEC_OK;
 }
@@ -608,46 +632,26 @@ int dec_prefill_ex(dec_handle h, int seq, const int32_t *tokens, int n, int star
     if ((long)start_pos + n > 0x7FFFFFFFL) return DEC_ERR_RANGE;
     if (timing_mask(h) && harvest(h) != DEC_OK) return DEC_ERR_DEVICE;
 
-    if (h->ring && (long)start_pos + n > (long)c.max_seq) {
-        // positions of this call would overwrite ring slots its own earlier
-        // positions still read: run them one at a time (same result as one
-        // pass, sipllm "Single-pass prefill").
-        for (int t = 0; t < n; t++) {
-            RowArgs ra;
-            ra.tok[0] = tokens[t];
-            ra.pos[0] = start_pos + t;
-            ra.slot[0] = seq;
-            launch_set_rows(h->st, ra, 1, nullptr, nullptr, h->tok, h->pos, h->slot);
-            Pass ps{};
-            ps.T = 1;
-            ps.decode = true;
-            ps.seq = seq;
-            const int hp = start_pos + t;
-            ps.hpos = &hp;
-            ps.logits = all_logits ? logits + (size_t)t * c.vocab : (t == n - 1) ? logits : nullptr;
-            ps.logit_row0 = 0;
-            ps.logit_rows = 1;
-            ps.cap_row = t;
-            ps.cap_rows = n;
-            run_pass(h, ps);
-        }
-    } else {
-        if (hipMemcpyAsync(h->tok, tokens, sizeof(int32_t) * n, hipMemcpyHostToDevice, h->st) != hipSuccess)
-            return DEC_ERR_DEVICE;
-        launch_set_seq_rows(h->st, n, start_pos, seq, h->pos, h->slot);
-        Pass ps{};
-        ps.T = n;
-        ps.decode = false;
-        ps.start_pos = start_pos;
-        ps.seq = seq;
-        ps.hpos = nullptr;
-        ps.logits = logits;
-        ps.logit_row0 = all_logits ? 0 : n - 1;
-        ps.logit_rows = all_logits ? n : 1;
-        ps.cap_row = 0;
-        ps.cap_rows = n;
-        run_pass(h, ps);
-    }
+    if (hipMemcpyAsync(h->tok, tokens, sizeof(int32_t) * n, hipMemcpyHostToDevice, h->st) != hipSuccess)
+        return DEC_ERR_DEVICE;
+    launch_set_seq_rows(h->st, n, start_pos, seq, h->pos, h->slot);
+    Pass ps{};
+    ps.T = n;
+    ps.decode = false;
+    ps.start_pos = start_pos;
+    ps.seq = seq;
+    // positions past the ring's size would overwrite slots the chunk's own
+    // earlier queries still read: hold the chunk's K/V back until its
+    // attention is done, then commit (zLLM "The Algorithm Layer", section 5:
+    // AppendPrefill appends a span after existing history)
+    ps.deferred = h->ring && (long)start_pos + n > (long)c.max_seq;
+    ps.hpos = nullptr;
+    ps.logits = logits;
+    ps.logit_row0 = all_logits ? 0 : n - 1;
+    ps.logit_rows = all_logits ? n : 1;
+    ps.cap_row = 0;
+    ps.cap_rows = n;
+    run_pass(h, ps);
     if (hipGetLastError() != hipSuccess) return DEC_ERR_DEVICE;
     h->len[seq] = start_pos + n;
     return DEC_OK;

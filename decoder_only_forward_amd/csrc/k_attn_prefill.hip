@@ -18,15 +18,30 @@ __device__ __forceinline__ void store_out(float v, size_t off, u16 *o_hi, u16 *o
     }
 }
 
-// Four cached elements starting at element e of a K/V cache (fp32, or bf16 bits).
+// Byte address of the K (or V) row of position j for kv head kvh: row t of the
+// chunk buffer [T][nkv][HD] for chunk positions when a chunk buffer is given,
+// else the layer cache row at slot j % ring_mod (ring) or j.
+// GEN = false: every position is in the cache at slot == position.
+template <int HD, bool KB, bool GEN>
+__device__ __forceinline__ const char *kv_row(const void *cache, const void *chunk, size_t head_base, int j,
+                                              int start_pos, int ring_mod, int nkv, int kvh) {
+    constexpr int ES = KB ? 2 : 4;
+    if constexpr (!GEN) return static_cast<const char *>(cache) + (head_base + j) * HD * ES;
+    if (j >= start_pos)
+        return static_cast<const char *>(chunk) + ((size_t)(j - start_pos) * nkv + kvh) * HD * ES;
+    const int s = ring_mod ? j % ring_mod : j;
+    return static_cast<const char *>(cache) + (head_base + s) * HD * ES;
+}
+
+// Four elements of a K/V row (fp32, or bf16 bits), from element e.
 template <bool KB>
-__device__ __forceinline__ float4 load_kv4(const void *cache, size_t e) {
+__device__ __forceinline__ float4 row4(const char *row, int e) {
     if constexpr (KB) {
-        const uint2 r = *reinterpret_cast<const uint2 *>(static_cast<const u16 *>(cache) + e);
+        const uint2 r = *reinterpret_cast<const uint2 *>(row + (size_t)e * 2);
         return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u),
                            __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xFFFF0000u));
     } else {
-        return *reinterpret_cast<const float4 *>(static_cast<const float *>(cache) + e);
+        return *reinterpret_cast<const float4 *>(row + (size_t)e * 4);
     }
 }
 
@@ -42,10 +57,11 @@ namespace {
 
 constexpr int BQ = 32, BKV = 32, SB = 8;
 
-template <int HD, int G, int SPLIT, bool KB>
+template <int HD, int G, int SPLIT, bool KB, bool GEN>
 __global__ void __launch_bounds__(BQ * G * SPLIT) attn_prefill_kernel(
     int T, int start_pos, int slot, const float *__restrict__ q, const void *__restrict__ kc,
-    const void *__restrict__ vc, int nh, int nkv, int max_seq, u16 *__restrict__ o_hi, u16 *__restrict__ o_lo,
+    const void *__restrict__ vc, int nh, int nkv, int max_seq, int window, int ring_mod,
+    const void *__restrict__ ck, const void *__restrict__ cv, u16 *__restrict__ o_hi, u16 *__restrict__ o_lo,
     float *__restrict__ o_f32) {
     constexpr int D = HD / SPLIT;
     constexpr int NT = BQ * G * SPLIT;
@@ -76,15 +92,18 @@ __global__ void __launch_bounds__(BQ * G * SPLIT) attn_prefill_kernel(
 
     const size_t head_base = ((size_t)slot * nkv + kvh) * max_seq;
     const int last_pos = start_pos + min(T, t0 + BQ) - 1;  // largest query position of the block
-    for (int kb = 0; kb <= last_pos; kb += BKV) {
+    // GEN: positions may lie before the window (ring past its size)
+    const int first_key = GEN && window ? max(0, start_pos + t0 - window + 1) : 0;
+    const int lo_q = GEN && window ? qpos - window + 1 : 0;  // this query's oldest key
+    for (int kb = first_key; kb <= last_pos; kb += BKV) {
         __syncthreads();
         for (int i = tid; i < BKV * HD / 4; i += NT) {
             const int row = i / (HD / 4), c4 = i % (HD / 4);
             const int j = kb + row;
             float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
             if (j <= last_pos) {
-                kv = load_kv4<KB>(kc, (head_base + j) * HD + 4 * c4);
-                vv = load_kv4<KB>(vc, (head_base + j) * HD + 4 * c4);
+                kv = row4<KB>(kv_row<HD, KB, GEN>(kc, ck, head_base, j, start_pos, ring_mod, nkv, kvh), 4 * c4);
+                vv = row4<KB>(kv_row<HD, KB, GEN>(vc, cv, head_base, j, start_pos, ring_mod, nkv, kvh), 4 * c4);
             }
             *reinterpret_cast<float4 *>(&sk[row][4 * c4]) = kv;
             *reinterpret_cast<float4 *>(&sv[row][4 * c4]) = vv;
@@ -104,11 +123,12 @@ __global__ void __launch_bounds__(BQ * G * SPLIT) attn_prefill_kernel(
                 }
 #pragma unroll
                 for (int o = SPLIT / 2; o > 0; o >>= 1) d += __shfl_xor(d, o, WAVE);
-                s[jj] = (j0 + jj < nkeys) ? d * scale : -INFINITY;
+                s[jj] = (j0 + jj < nkeys && (!GEN || kb + j0 + jj >= lo_q)) ? d * scale : -INFINITY;
             }
             float mx = m;
 #pragma unroll
             for (int jj = 0; jj < SB; jj++) mx = fmaxf(mx, s[jj]);
+            if (mx == -INFINITY) continue;  // every key of the group is outside the window
             const float corr = expf(m - mx);
             m = mx;
             float pe[SB], ps = 0.f;
@@ -138,12 +158,13 @@ __global__ void __launch_bounds__(BQ * G * SPLIT) attn_prefill_kernel(
     for (int i = 0; i < D; i++) store_out(acc[i] * inv, off + i, o_hi, o_lo, o_f32);
 }
 
-template <int HD, int SPLIT, bool KB>
+template <int HD, int SPLIT, bool KB, bool GEN>
 bool launch_prefill_hd(hipStream_t st, int G, dim3 grid, int T, int start_pos, int slot, const float *q,
-                       const void *kc, const void *vc, int nh, int nkv, int max_seq, u16 *o_hi, u16 *o_lo,
-                       float *o_f32) {
-#define AP(GG) hipLaunchKernelGGL((attn_prefill_kernel<HD, GG, SPLIT, KB>), grid, dim3(BQ * GG * SPLIT), 0, st, T, \
-                                  start_pos, slot, q, kc, vc, nh, nkv, max_seq, o_hi, o_lo, o_f32)
+                       const void *kc, const void *vc, int nh, int nkv, int max_seq, int window, int ring_mod,
+                       const void *ck, const void *cv, u16 *o_hi, u16 *o_lo, float *o_f32) {
+#define AP(GG) hipLaunchKernelGGL((attn_prefill_kernel<HD, GG, SPLIT, KB, GEN>), grid, dim3(BQ * GG * SPLIT), 0, st, T, \
+                                  start_pos, slot, q, kc, vc, nh, nkv, max_seq, window, ring_mod, ck, cv, o_hi, \
+                                  o_lo, o_f32)
     switch (G) {
         case 1: AP(1); return true;
         case 2: AP(2); return true;
@@ -186,10 +207,11 @@ __device__ __forceinline__ bf16x8 pack8(const uint32_t *h) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int HD, int G, bool KB>
+template <int HD, int G, bool KB, bool GEN>
 __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
     int T, int start_pos, int slot, const float *__restrict__ q, const void *__restrict__ kc,
-    const void *__restrict__ vc, int nh, int nkv, int max_seq, u16 *__restrict__ o_hi, u16 *__restrict__ o_lo,
+    const void *__restrict__ vc, int nh, int nkv, int max_seq, int window, int ring_mod,
+    const void *__restrict__ ck, const void *__restrict__ cv, u16 *__restrict__ o_hi, u16 *__restrict__ o_lo,
     float *__restrict__ o_f32) {
     constexpr int ROWS = NQV / G;
     constexpr int KLD = HD + 8;     // u16 per K row in LDS
@@ -243,26 +265,30 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) wmax = max(wmax, __shfl_xor(wmax, off, WAVE));
     const int last_pos = start_pos + min(T, t0 + ROWS) - 1;
+    // GEN: positions may lie before the window (ring past its size)
+    const int first_key = GEN && window ? max(0, start_pos + t0 - window + 1) : 0;
+    const int lo_q = GEN && window ? qpos - window + 1 : 0;  // this lane's query's oldest key
     const size_t head_base = ((size_t)slot * nkv + kvh) * max_seq;
 
-    for (int kb = 0; kb <= last_pos; kb += MKV) {
+    for (int kb = first_key; kb <= last_pos; kb += MKV) {
         __syncthreads();
         // K tile -> [key][dim] hi/lo; V tile -> transposed [dim][key] hi/lo
+        auto krow = [&](int j) { return kv_row<HD, KB, GEN>(kc, ck, head_base, j, start_pos, ring_mod, nkv, kvh); };
+        auto vrow = [&](int j) { return kv_row<HD, KB, GEN>(vc, cv, head_base, j, start_pos, ring_mod, nkv, kvh); };
         if constexpr (KB) {
-            const u16 *k16 = static_cast<const u16 *>(kc), *v16 = static_cast<const u16 *>(vc);
             for (int i = tid; i < MKV * HD / 8; i += 256) {
                 const int key = i / (HD / 8), c8 = i % (HD / 8);
                 const int j = kb + key;
                 u32x4 kv = {0u, 0u, 0u, 0u};
-                if (j <= last_pos) kv = *reinterpret_cast<const u32x4 *>(k16 + (head_base + j) * HD + 8 * c8);
+                if (j <= last_pos) kv = *reinterpret_cast<const u32x4 *>(krow(j) + 16 * c8);
                 *reinterpret_cast<u32x4 *>(sKh + key * KLD + 8 * c8) = kv;
             }
             for (int i = tid; i < (MKV / 2) * HD / 8; i += 256) {
                 const int kp = i / (HD / 8), c8 = i % (HD / 8);
                 const int j = kb + 2 * kp;
                 u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = v0;
-                if (j <= last_pos) v0 = *reinterpret_cast<const u32x4 *>(v16 + (head_base + j) * HD + 8 * c8);
-                if (j + 1 <= last_pos) v1 = *reinterpret_cast<const u32x4 *>(v16 + (head_base + j + 1) * HD + 8 * c8);
+                if (j <= last_pos) v0 = *reinterpret_cast<const u32x4 *>(vrow(j) + 16 * c8);
+                if (j + 1 <= last_pos) v1 = *reinterpret_cast<const u32x4 *>(vrow(j + 1) + 16 * c8);
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
                     // dims 8c8+2e (low halves) and 8c8+2e+1 (high halves)
@@ -273,12 +299,11 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
                 }
             }
         } else {
-            const float *k32 = static_cast<const float *>(kc), *v32 = static_cast<const float *>(vc);
             for (int i = tid; i < MKV * HD / 4; i += 256) {
                 const int key = i / (HD / 4), c4 = i % (HD / 4);
                 const int j = kb + key;
                 float4 kv = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (j <= last_pos) kv = *reinterpret_cast<const float4 *>(k32 + (head_base + j) * HD + 4 * c4);
+                if (j <= last_pos) kv = *reinterpret_cast<const float4 *>(krow(j) + 16 * c4);
                 uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
                 split_bf16(kv.x, h0, l0); split_bf16(kv.y, h1, l1); split_bf16(kv.z, h2, l2); split_bf16(kv.w, h3, l3);
                 *reinterpret_cast<uint2 *>(sKh + key * KLD + 4 * c4) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
@@ -288,8 +313,8 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
                 const int kp = i / (HD / 4), c4 = i % (HD / 4);
                 const int j = kb + 2 * kp;
                 float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
-                if (j <= last_pos) v0 = *reinterpret_cast<const float4 *>(v32 + (head_base + j) * HD + 4 * c4);
-                if (j + 1 <= last_pos) v1 = *reinterpret_cast<const float4 *>(v32 + (head_base + j + 1) * HD + 4 * c4);
+                if (j <= last_pos) v0 = *reinterpret_cast<const float4 *>(vrow(j) + 16 * c4);
+                if (j + 1 <= last_pos) v1 = *reinterpret_cast<const float4 *>(vrow(j + 1) + 16 * c4);
                 const float a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
@@ -329,7 +354,7 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
 #pragma unroll
             for (int e = 0; e < 16; e++) {
                 const int key = kb + kt * 32 + (e / 4) * 8 + 4 * hh + (e % 4);
-                const float v = key <= qpos ? sc[kt][e] * scale : -INFINITY;
+                const float v = (key <= qpos && (!GEN || key >= lo_q)) ? sc[kt][e] * scale : -INFINITY;
                 sc[kt][e] = v;
                 mx = fmaxf(mx, v);
             }
@@ -391,11 +416,13 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
         }
 }
 
-template <int HD, bool KB>
+template <int HD, bool KB, bool GEN>
 bool launch_prefill_mfma_hd(hipStream_t st, int G, int T, int start_pos, int slot, const float *q, const void *kc,
-                            const void *vc, int nh, int nkv, int max_seq, u16 *o_hi, u16 *o_lo, float *o_f32) {
-#define APM(GG) hipLaunchKernelGGL((attn_prefill_mfma_kernel<HD, GG, KB>), dim3((T + NQV / GG - 1) / (NQV / GG), nkv), \
-                                   dim3(256), 0, st, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, o_hi, o_lo, o_f32)
+                            const void *vc, int nh, int nkv, int max_seq, int window, int ring_mod, const void *ck,
+                            const void *cv, u16 *o_hi, u16 *o_lo, float *o_f32) {
+#define APM(GG) hipLaunchKernelGGL((attn_prefill_mfma_kernel<HD, GG, KB, GEN>), dim3((T + NQV / GG - 1) / (NQV / GG), nkv), \
+                                   dim3(256), 0, st, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, window, \
+                                   ring_mod, ck, cv, o_hi, o_lo, o_f32)
     switch (G) {
         case 1: APM(1); return true;
         case 2: APM(2); return true;
@@ -413,25 +440,34 @@ bool launch_prefill_mfma_hd(hipStream_t st, int G, int T, int start_pos, int slo
 }  // namespace
 
 void launch_attn_prefill(hipStream_t st, int T, int start_pos, int slot, const float *q, const void *kc,
-                         const void *vc, int kv_bf16, int nh, int nkv, int hd, int max_seq, int window, u16 *o_hi,
-                         u16 *o_lo, float *o_f32) {
-    (void)window;
+                         const void *vc, int kv_bf16, int nh, int nkv, int hd, int max_seq, int window, int ring,
+                         const void *ck, const void *cv, u16 *o_hi, u16 *o_lo, float *o_f32) {
     if (T <= 0) return;
     const int G = nh / nkv;
+    const int ring_mod = ring ? max_seq : 0;
     dim3 grid((T + BQ - 1) / BQ, nkv);
-#define LM(HD, KB) launch_prefill_mfma_hd<HD, KB>(st, G, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, o_hi, \
-                                                  o_lo, o_f32)
-#define LF(HD, KB) launch_prefill_hd<HD, 1, KB>(st, G, grid, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, \
-                                                o_hi, o_lo, o_f32)
-    if (kv_bf16) {
-        if (hd == 128) LM(128, true);
-        else if (hd == 64) LM(64, true);
-        else LF(16, true);
-    } else {
-        if (hd == 128) LM(128, false);
-        else if (hd == 64) LM(64, false);
-        else LF(16, false);
+    // the general form (ring slots, chunk buffers, window bound) only for a
+    // chunk held back from the cache; otherwise slot == position
+#define LM(HD, KB, GEN) launch_prefill_mfma_hd<HD, KB, GEN>(st, G, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, \
+                                                            window, ring_mod, ck, cv, o_hi, o_lo, o_f32)
+#define LF(HD, KB, GEN) launch_prefill_hd<HD, 1, KB, GEN>(st, G, grid, T, start_pos, slot, q, kc, vc, nh, nkv, \
+                                                          max_seq, window, ring_mod, ck, cv, o_hi, o_lo, o_f32)
+#define PICK(GEN)                                   \
+    if (kv_bf16) {                                  \
+        if (hd == 128) LM(128, true, GEN);          \
+        else if (hd == 64) LM(64, true, GEN);       \
+        else LF(16, true, GEN);                     \
+    } else {                                        \
+        if (hd == 128) LM(128, false, GEN);         \
+        else if (hd == 64) LM(64, false, GEN);      \
+        else LF(16, false, GEN);                    \
     }
+    if (ck) {
+        PICK(true)
+    } else {
+        PICK(false)
+    }
+#undef PICK
 #undef LM
 #undef LF
 }

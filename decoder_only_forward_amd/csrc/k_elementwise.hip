@@ -209,7 +209,7 @@ __global__ void __launch_bounds__(256) rope_kv_kernel(
     Partials qkv, const float *__restrict__ bq, const float *__restrict__ bk, const float *__restrict__ bv,
     const float2 *__restrict__ tab, const int32_t *__restrict__ pos, const int32_t *__restrict__ slot,
     int nh, int nkv, int hd, int pairing, float *__restrict__ q_out, void *__restrict__ kc,
-    void *__restrict__ vc, int max_seq, int ring, int kv_bf16) {
+    void *__restrict__ vc, int max_seq, int ring, int kv_bf16, int chunk) {
     const int t = blockIdx.x;
     const int qd = nh * hd, kvd = nkv * hd, half = hd / 2;
     const int npairs = (qd + 2 * kvd) / 2;
@@ -243,7 +243,8 @@ __global__ void __launch_bounds__(256) rope_kv_kernel(
         q_out[(size_t)t * qd + e1c] = e1;
     } else {
         void *cache = base == qd ? kc : vc;
-        const size_t dst = ((slot_base + head) * max_seq + s) * hd;
+        // the layer cache at the position's slot, or row t of a chunk buffer [T][nkv][hd]
+        const size_t dst = chunk ? ((size_t)t * nkv + head) * hd : ((slot_base + head) * max_seq + s) * hd;
         if (kv_bf16) {
             u16 *c16 = static_cast<u16 *>(cache);
             c16[dst + e0c - head * hd] = (u16)f32_to_bf16_bits(e0);
@@ -259,11 +260,37 @@ __global__ void __launch_bounds__(256) rope_kv_kernel(
 void launch_rope_kv(hipStream_t st, int T, Partials qkv, const float *bq, const float *bk,
                     const float *bv, const float2 *tab, const int32_t *pos, const int32_t *slot,
                     int nh, int nkv, int hd, int pairing, float *q_out, void *kc, void *vc, int max_seq,
-                    int ring, int kv_bf16) {
+                    int ring, int kv_bf16, int chunk) {
     if (T <= 0) return;
     const int npairs = (nh + 2 * nkv) * hd / 2;
     hipLaunchKernelGGL(rope_kv_kernel, dim3(T, (npairs + 255) / 256), dim3(256), 0, st, qkv, bq, bk, bv, tab, pos,
-                       slot, nh, nkv, hd, pairing, q_out, kc, vc, max_seq, ring, kv_bf16);
+                       slot, nh, nkv, hd, pairing, q_out, kc, vc, max_seq, ring, kv_bf16, chunk);
+}
+
+// Commit a chunk's K/V rows [T][nkv][hd] to the ring slots of positions
+// start..start+T-1 of sequence slot `s`.  Only the last min(T, max_seq) rows
+// are written: an earlier row's slot is taken again by a later one.
+__global__ void commit_chunk_kernel(const uint32_t *__restrict__ ck, const uint32_t *__restrict__ cv, int T,
+                                    int first, int start, int s, int nkv, int words, int max_seq,
+                                    uint32_t *__restrict__ kc, uint32_t *__restrict__ vc) {
+    const int t = first + blockIdx.x, h = blockIdx.y;
+    if (t >= T) return;
+    const size_t src = ((size_t)t * nkv + h) * words;
+    const size_t dst = (((size_t)s * nkv + h) * max_seq + (start + t) % max_seq) * words;
+    for (int i = threadIdx.x; i < words; i += blockDim.x) {
+        kc[dst + i] = ck[src + i];
+        vc[dst + i] = cv[src + i];
+    }
+}
+
+void launch_commit_chunk(hipStream_t st, const void *ck, const void *cv, int T, int start, int s, int nkv, int hd,
+                         int es, int max_seq, void *kc, void *vc) {
+    const int first = T > max_seq ? T - max_seq : 0;
+    const int words = hd * es / 4;
+    if (T - first <= 0) return;
+    hipLaunchKernelGGL(commit_chunk_kernel, dim3(T - first, nkv), dim3(64), 0, st,
+                       static_cast<const uint32_t *>(ck), static_cast<const uint32_t *>(cv), T, first, start, s, nkv,
+                       words, max_seq, static_cast<uint32_t *>(kc), static_cast<uint32_t *>(vc));
 }
 
 // ---- SwiGLU activation -----------------------------------------------------

@@ -41,12 +41,17 @@ void launch_rope_table(hipStream_t st, const int32_t *pos, int T, int hd, double
 
 // q/k/v (+bias) -> RoPE on q and k -> q_out [T][q_dim]; k, v stored in the
 // layer's cache [slot][kvh][max_seq][hd] at position pos % max_seq (ring) or pos,
-// as fp32, or as nearest-even bf16 when kv_bf16 is set.
+// or, when chunk is set, in rows [T][nkv][hd] of the buffers kc, vc; as fp32,
+// or as nearest-even bf16 when kv_bf16 is set.
 // pairing 0 rotates elements (2i, 2i+1) of a head, 1 rotates (i, i + hd/2).
 void launch_rope_kv(hipStream_t st, int T, Partials qkv, const float *bq, const float *bk,
                     const float *bv, const float2 *tab, const int32_t *pos, const int32_t *slot,
                     int nh, int nkv, int hd, int pairing, float *q_out, void *kc, void *vc, int max_seq,
-                    int ring, int kv_bf16);
+                    int ring, int kv_bf16, int chunk);
+// Store a chunk's rows [T][nkv][hd] (es bytes per element) at the ring slots of
+// positions start.. of sequence slot s: the last min(T, max_seq) rows.
+void launch_commit_chunk(hipStream_t st, const void *ck, const void *cv, int T, int start, int s, int nkv, int hd,
+                         int es, int max_seq, void *kc, void *vc);
 
 // act[t][j] = silu(g) * u with g = gu(t, j), u = gu(t, F + j); written as bf16
 // (hi, lo) and/or fp32 with row stride F.
@@ -82,11 +87,15 @@ void launch_attn_decode(hipStream_t st, int B, const float *q, const void *kc, c
                         float *o_f32);
 
 // Causal prefill attention for T rows of one sequence at positions
-// start_pos..start_pos+T-1, reading keys/values from the layer cache (the
-// chunk's own K/V already stored there).
+// start_pos..start_pos+T-1.  Query p attends to positions [p - window + 1, p]
+// (window 0: [0, p]).  Keys/values of positions before start_pos come from the
+// layer cache (slot pos % max_seq when ring is set, else pos); the chunk's own
+// come from the cache as well (ck == nullptr: already stored there) or from the
+// chunk buffers ck, cv [T][nkv][hd] (deferred commit).
 void launch_attn_prefill(hipStream_t st, int T, int start_pos, int slot, const float *q,
                          const void *kc, const void *vc, int kv_bf16, int nh, int nkv, int hd, int max_seq,
-                         int window, u16 *o_hi, u16 *o_lo, float *o_f32);
+                         int window, int ring, const void *ck, const void *cv, u16 *o_hi, u16 *o_lo,
+                         float *o_f32);
 
 // MoE.  Router logits [T][E] (a GEMV/GEMM output) -> softmax, top-k by repeated
 // selection (ties to the lower id), renormalised weights; then the (token, slot)

@@ -44,7 +44,9 @@ def test_bf16_cache_halves_the_kv_bytes():
     _lib()
     f32 = D.workspace_bytes(configs.MISTRAL, max_batch=32, max_prefill=4096)
     b16 = D.workspace_bytes(configs.MISTRAL.replace(kv_bf16=True), max_batch=32, max_prefill=4096)
-    assert f32 - b16 == 2 * 32 * 32 * 8 * 4096 * 128 * 2   # K and V, 2 bytes saved per element
+    kv = 2 * 32 * 32 * 8 * 4096 * 128 * 2        # K and V of 32 slots, 2 bytes saved per element
+    chunk = 2 * 4096 * 8 * 128 * 2                # the ring's deferred-commit chunk K/V (max_prefill rows)
+    assert f32 - b16 == kv + chunk
 
 
 def _create(cfg, max_batch=2, max_prefill=8, ws=None, ws_bytes=None, **over):
