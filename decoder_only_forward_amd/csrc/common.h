@@ -56,17 +56,53 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
 }
 
 // Sum of S split partials of one element: p[s*stride + off], s ascending.
+// The loads of a batch are issued together (the partials come from L2 or HBM,
+// and one dependent load per split would serialise S memory latencies); the
+// additions keep the order s = 0, 1, ..., S-1, so the result is the same.
 __device__ __forceinline__ float sum_splits(const float *p, int S, size_t stride, size_t off) {
     float v = p[off];
-    for (int s = 1; s < S; s++) v += p[s * stride + off];
+    int s = 1;
+    for (; s + 8 <= S; s += 8) {
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) t[i] = p[(s + i) * stride + off];
+#pragma unroll
+        for (int i = 0; i < 8; i++) v += t[i];
+    }
+    if (s + 4 <= S) {
+        float t[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) t[i] = p[(s + i) * stride + off];
+#pragma unroll
+        for (int i = 0; i < 4; i++) v += t[i];
+        s += 4;
+    }
+    for (; s < S; s++) v += p[s * stride + off];
     return v;
+}
+
+__device__ __forceinline__ void add4(float4 &v, const float4 t) {
+    v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
 }
 
 __device__ __forceinline__ float4 sum_splits4(const float *p, int S, size_t stride, size_t off) {
     float4 v = *reinterpret_cast<const float4 *>(p + off);
-    for (int s = 1; s < S; s++) {
-        float4 t = *reinterpret_cast<const float4 *>(p + s * stride + off);
-        v.x += t.x; v.y += t.y; v.z += t.z; v.w += t.w;
+    int s = 1;
+    for (; s + 8 <= S; s += 8) {
+        float4 t[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) t[i] = *reinterpret_cast<const float4 *>(p + (s + i) * stride + off);
+#pragma unroll
+        for (int i = 0; i < 8; i++) add4(v, t[i]);
     }
+    if (s + 4 <= S) {
+        float4 t[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) t[i] = *reinterpret_cast<const float4 *>(p + (s + i) * stride + off);
+#pragma unroll
+        for (int i = 0; i < 4; i++) add4(v, t[i]);
+        s += 4;
+    }
+    for (; s < S; s++) add4(v, *reinterpret_cast<const float4 *>(p + s * stride + off));
     return v;
 }

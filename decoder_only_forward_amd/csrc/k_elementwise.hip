@@ -6,10 +6,11 @@
 
 // ---- residual + RMSNorm ----------------------------------------------------
 // RMSNorm: a = x / sqrt(mean(x^2) + eps) * g  (Pantheon "Llama Forward Pass",
-// section "RMSNorm").  One block per row; each thread keeps its float4 chunks of
-// the row in registers between the sum of squares and the scaling.
-template <int VPT>
-__global__ void __launch_bounds__(256) residual_norm_kernel(
+// section "RMSNorm").  One block of NTH threads per row; each thread keeps its
+// float4 chunks of the row in registers between the sum of squares and the
+// scaling.
+template <int VPT, int NTH>
+__global__ void __launch_bounds__(NTH) residual_norm_kernel(
     int mode, int d, float *__restrict__ x, const int32_t *__restrict__ tok,
     const void *__restrict__ embed, int embed_f32, Partials add, const float *__restrict__ moe_y,
     const float *__restrict__ moe_w, int k, const float *__restrict__ gain, float eps,
@@ -21,7 +22,7 @@ __global__ void __launch_bounds__(256) residual_norm_kernel(
     float ss = 0.f;
 #pragma unroll
     for (int u = 0; u < VPT; u++) {
-        const int i4 = threadIdx.x + u * 256;
+        const int i4 = threadIdx.x + u * NTH;
         if (i4 >= nv) break;
         const size_t off = (size_t)t * d + 4 * i4;
         float4 r;
@@ -60,7 +61,7 @@ __global__ void __launch_bounds__(256) residual_norm_kernel(
     const float rs = 1.0f / sqrtf(tot / (float)d + eps);
 #pragma unroll
     for (int u = 0; u < VPT; u++) {
-        const int i4 = threadIdx.x + u * 256;
+        const int i4 = threadIdx.x + u * NTH;
         if (i4 >= nv) break;
         const size_t off = (size_t)t * d + 4 * i4;
         const float4 g = *reinterpret_cast<const float4 *>(gain + 4 * i4);
@@ -77,10 +78,11 @@ __global__ void __launch_bounds__(256) residual_norm_kernel(
     }
 }
 
-// Few rows (decode): the residual update, which sums the split-K partials,
-// runs over a (row, 1024-column chunk) grid and leaves per-chunk sums of
-// squares; the norm kernel then scales each chunk.  Chunk sums are added in
-// chunk order, so the result does not depend on scheduling.
+// Few rows (decode) of a row wider than one block covers: the residual update,
+// which sums the split-K partials, runs over a (row, 1024-column chunk) grid
+// and leaves per-chunk sums of squares; the norm kernel then scales each chunk.
+// Chunk sums are added in chunk order, so the result does not depend on
+// scheduling.
 constexpr int RN_CHUNK = 1024;
 
 __global__ void __launch_bounds__(256) residual_chunk_kernel(
@@ -144,6 +146,16 @@ void launch_residual_norm(hipStream_t st, int mode, int T, int d, float *x, cons
                           const float *moe_w, int k, const float *gain, float eps, u16 *a_hi,
                           u16 *a_lo, float *a_f32, float *cap, float *ssq) {
     if (T <= 0) return;
+    const int nv = d / 4;
+    if (T <= 64 && nv <= 1024) {
+        // few rows: one 1024-thread block per row, one float4 per thread
+#define RN1(NT) hipLaunchKernelGGL((residual_norm_kernel<1, NT>), dim3(T), dim3(NT), 0, st, mode, d, x, tok, embed, \
+                                   embed_f32, add, moe_y, moe_w, k, gain, eps, a_hi, a_lo, a_f32, cap)
+        if (nv <= 256) RN1(256);
+        else RN1(1024);
+#undef RN1
+        return;
+    }
     if (mode == RN_ADD && T <= 64 && ssq) {
         const int nch = (d + RN_CHUNK - 1) / RN_CHUNK;
         hipLaunchKernelGGL(residual_chunk_kernel, dim3(T, nch), dim3(256), 0, st, d, x, add, moe_y, moe_w, k, cap, ssq);
@@ -152,9 +164,8 @@ void launch_residual_norm(hipStream_t st, int mode, int T, int d, float *x, cons
                                a_lo, a_f32);
         return;
     }
-    const int nv = d / 4;
     const int vpt = (nv + 255) / 256;
-#define RN(V) hipLaunchKernelGGL(residual_norm_kernel<V>, dim3(T), dim3(256), 0, st, mode, d, x, tok, \
+#define RN(V) hipLaunchKernelGGL((residual_norm_kernel<V, 256>), dim3(T), dim3(256), 0, st, mode, d, x, tok, \
                                  embed, embed_f32, add, moe_y, moe_w, k, gain, eps, a_hi, a_lo, a_f32, cap)
     if (vpt <= 1) RN(1);
     else if (vpt <= 2) RN(2);
