@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(HERE, "libdec.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["k_elementwise.hip", "k_gemv.hip", "k_gemm.hip", "k_attn_decode.hip", "k_attn_prefill.hip", "k_moe.hip", "dec_api.hip"]
+SOURCES = ["k_elementwise.hip", "k_gemv.hip", "k_gemm.hip", "k_attn_decode.hip", "k_attn_prefill.hip", "k_attn_prefill_tiles.hip", "k_moe.hip", "dec_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden",

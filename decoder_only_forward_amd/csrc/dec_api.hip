@@ -47,7 +47,7 @@ struct GraphEntry {
 
 struct Plan {  // byte offsets into the workspace
     size_t kv_layer;        // elements of one layer's K (or V) cache
-    size_t k, v, ck, cv, x, a_hi, a_lo, a_f32, part, q, attn, rope, tok, pos, slot, amax, ssq;
+    size_t k, v, ck, cv, kvimg, x, a_hi, a_lo, a_f32, part, q, attn, rope, tok, pos, slot, amax, ssq;
     size_t moe_ids, moe_w, moe_cnt, moe_off, moe_pairs, g_hi, g_lo, g_f32, moe_y;
     size_t part_floats, act_elems, total;
     int rows;               // max rows of one pass (max(max_batch, max_prefill))
@@ -68,6 +68,7 @@ struct dec_model {
     Plan pl;
     char *kc, *vc;          // caches, kv_es bytes per element
     char *ck, *cv;          // chunk K/V of a deferred-commit prefill (ring only)
+    void *kvimg;            // prefill attention's K/V tile images (null: not used)
     int kv_es;
     float *x, *a_f32, *part, *q, *attn, *moe_w, *g_f32, *moe_y, *ssq;
     u16 *a_hi, *a_lo, *g_hi, *g_lo;
@@ -142,6 +143,9 @@ bool plan(const dec_config &c, Plan &p) {
     const bool ring = c.sliding_window > 0 && c.max_seq == c.sliding_window;
     p.ck = take(ring ? (size_t)c.max_prefill * kvd * es : 0);
     p.cv = take(ring ? (size_t)c.max_prefill * kvd * es : 0);
+    // prefill attention's K/V tile images (positions [0, max_seq) of one sequence)
+    p.kvimg = take(c.weight_dtype == DEC_WEIGHT_F32 ? 0
+                   : attn_tiles_bytes(c.max_seq, c.n_kv_heads, c.head_dim, c.kv_dtype == DEC_KV_BF16));
     p.x = take((size_t)rows * d * 4);
     const bool f32w = c.weight_dtype == DEC_WEIGHT_F32;
     p.a_hi = take(f32w ? 0 : p.act_elems * 2);
@@ -378,9 +382,12 @@ void run_pass(dec_model *m, const Pass &ps) {
             Tick tk(m, DEC_K_ATTN_PREFILL);
             // history is read through ring slots only when the call reaches past
             // max_seq (the deferred case); below that, slot == position
-            launch_attn_prefill(st, T, ps.start_pos, ps.seq, m->q, kc, vc, kvb, nh, nkv, hd, c.max_seq, W,
-                                ps.deferred, ps.deferred ? m->ck : nullptr, ps.deferred ? m->cv : nullptr, ah, al,
-                                af);
+            if (ps.deferred || !m->kvimg ||
+                !launch_attn_prefill_tiles(st, T, ps.start_pos, ps.seq, m->q, kc, vc, kvb, nh, nkv, hd, c.max_seq,
+                                           m->kvimg, ah, al, af))
+                launch_attn_prefill(st, T, ps.start_pos, ps.seq, m->q, kc, vc, kvb, nh, nkv, hd, c.max_seq, W,
+                                    ps.deferred, ps.deferred ? m->ck : nullptr, ps.deferred ? m->cv : nullptr, ah,
+                                    al, af);
             tk.done(keys * kvd * 2 * m->kv_es + 2.0 * T * qd * 4, flops);
             if (ps.deferred)
                 launch_commit_chunk(st, m->ck, m->cv, T, ps.start_pos, ps.seq, nkv, hd, m->kv_es, c.max_seq, kc, vc);
@@ -568,6 +575,7 @@ int dec_create(const dec_config *cfg, const dec_weights *w, void *workspace, siz
     m->vc = b + p.v;
     m->ck = b + p.ck;
     m->cv = b + p.cv;
+    m->kvimg = p.kvimg < p.x ? (void *)(b + p.kvimg) : nullptr;
     m->kv_es = cfg->kv_dtype == DEC_KV_BF16 ? 2 : 4;
     m->x = (float *)(b + p.x);
     m->a_hi = (u16 *)(b + p.a_hi);

@@ -97,6 +97,16 @@ void launch_attn_prefill(hipStream_t st, int T, int start_pos, int slot, const f
                          int window, int ring, const void *ck, const void *cv, u16 *o_hi, u16 *o_lo,
                          float *o_f32);
 
+// The same attention over pre-split K/V tiles (head_dim 64 or 128, every key
+// position at its own slot: start_pos + T <= max_seq).  Each call first writes
+// the tiles of positions [0, start_pos + T) of sequence `slot` into `img`
+// (attn_tiles_bytes(max_seq, nkv, hd, kv_bf16) bytes), then runs the MFMA
+// kernel.  Returns false for an unsupported head_dim (nothing launched).
+size_t attn_tiles_bytes(int max_pos, int nkv, int hd, int kv_bf16);
+bool launch_attn_prefill_tiles(hipStream_t st, int T, int start_pos, int slot, const float *q, const void *kc,
+                               const void *vc, int kv_bf16, int nh, int nkv, int hd, int max_seq, void *img,
+                               u16 *o_hi, u16 *o_lo, float *o_f32);
+
 // MoE.  Router logits [T][E] (a GEMV/GEMM output) -> softmax, top-k by repeated
 // selection (ties to the lower id), renormalised weights; then the (token, slot)
 // pairs are grouped by expert (counting sort, stable in (token, slot) order).

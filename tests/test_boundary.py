@@ -46,7 +46,10 @@ def test_bf16_cache_halves_the_kv_bytes():
     b16 = D.workspace_bytes(configs.MISTRAL.replace(kv_bf16=True), max_batch=32, max_prefill=4096)
     kv = 2 * 32 * 32 * 8 * 4096 * 128 * 2        # K and V of 32 slots, 2 bytes saved per element
     chunk = 2 * 4096 * 8 * 128 * 2                # the ring's deferred-commit chunk K/V (max_prefill rows)
-    assert f32 - b16 == kv + chunk
+    # prefill attention's K/V tile images (64 tiles x 8 heads): bf16 (hi, lo) pairs of K and V^T
+    # (72 KiB per tile, padded rows) against the bf16 cache's exact halves (40 KiB per tile)
+    img = 64 * 8 * (73728 - 40960)
+    assert f32 - b16 == kv + chunk + img
 
 
 def _create(cfg, max_batch=2, max_prefill=8, ws=None, ws_bytes=None, **over):
