@@ -231,11 +231,198 @@ void fill(GemmParams &p, const WSeg *segs, int nseg, int K, const u16 *a_hi, con
 
 }  // namespace
 
+// ---- large grids: 256 x 256 tiles fed by direct-to-LDS loads ----------------
+// Block tile 256 features x 256 tokens x 32 k; 8 waves as 2 (features) x 4
+// (tokens), each 128 x 64 = 4 x 2 MFMA tiles of 32x32x16, so a weight fragment
+// read from LDS serves both the hi and the lo pass of two token tiles.  Tiles
+// go from global memory straight into a 3-stage LDS ring (global_load_lds, no
+// register staging): the loads of k-tile t+2 are in flight while tile t is
+// multiplied.  Rows of a stage are 64 bytes with their four 16-byte chunks
+// XOR-swizzled by row, so the 16 rows an MFMA operand read touches per lane
+// group fall in distinct banks.  The tile order gives each XCD a contiguous
+// range of feature tiles, walked four token tiles at a time, so the blocks an
+// XCD runs together share few weight and activation panels in its L2.
+namespace {
+
+constexpr int DBN = 256, DBM = 256, DBK = 32;
+constexpr int DNTHR = 512;
+constexpr int DARR = 256 * DBK;              // u16 per operand array of a stage (16 KB)
+constexpr int DSTAGE = 3 * DARR;             // W, A_hi, A_lo
+constexpr int DNSTAGE = 3;
+constexpr int DGROUP = 4;                    // token tiles an XCD walks together
+constexpr size_t DMA_LDS = DNSTAGE * DSTAGE * sizeof(u16);
+#define LDS_AS __attribute__((address_space(3)))
+
+// 16-byte chunk c (of 4) of row r is stored at chunk c ^ ((r >> 2) & 3) of the row
+__device__ __forceinline__ int dswz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+
+__global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p) {
+    extern __shared__ __attribute__((aligned(16))) u16 smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid % WAVE, wv = tid / WAVE;
+    const int wn = wv & 1, wm = wv >> 1;
+    const int M = p.M;
+
+    const int ntn = (p.N + DBN - 1) / DBN, ntm = gridDim.y;
+    const int bid = blockIdx.x + blockIdx.y * gridDim.x;
+    int tn, tm;
+    if ((ntn & 7) == 0) {
+        // blocks are dealt round-robin to 8 XCDs: XCD x owns feature tiles
+        // [x*ntn/8, (x+1)*ntn/8) and walks them DGROUP token tiles at a time
+        const int x = bid & 7, lt = bid >> 3, nx = ntn >> 3;
+        const int G = DGROUP < ntm ? DGROUP : ntm;
+        const int tg = lt / (G * nx), rem = lt - tg * G * nx;
+        const int gsz = min(G, ntm - tg * G);
+        tn = x * nx + rem / gsz;
+        tm = tg * G + rem % gsz;
+    } else {
+        int b = bid;
+        const int nblk = ntn * ntm;
+        if ((nblk & 7) == 0) b = (b & 7) * (nblk >> 3) + (b >> 3);
+        tn = b / ntm;
+        tm = b % ntm;
+    }
+    const int m0 = tm * DBM;
+    if (m0 >= M) return;
+    const int n0 = tn * DBN;
+
+    // load instruction i (0, 1) of an operand array: wave wv fills the 1 KB slot
+    // i*8 + wv, lane L the 16-byte chunk slot*64 + L, i.e. row r = chunk / 4 and
+    // the logical chunk the swizzle stores there
+    const u16 *src[6];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int P = (i * 8 + wv) * 64 + lane;
+        const int r = P >> 2, c = (P & 3) ^ ((r >> 2) & 3);
+        int n = n0 + r;
+        n = n < p.N ? n : p.N - 1;
+        const u16 *wp = p.w[0];
+        int start = 0;
+        if (p.nseg > 1 && n >= p.seg_end[0]) { wp = p.w[1]; start = p.seg_end[0]; }
+        if (p.nseg > 2 && n >= p.seg_end[1]) { wp = p.w[2]; start = p.seg_end[1]; }
+        src[i] = wp + (size_t)(n - start) * p.K + c * 8;
+        int m = m0 + r;
+        m = m < M ? m : M - 1;
+        src[2 + i] = p.a_hi + (size_t)m * p.lda + c * 8;
+        src[4 + i] = p.a_lo + (size_t)m * p.lda + c * 8;
+    }
+    const int nk = p.K / DBK;
+    // every iteration issues its loads (the last tile again past the end), so
+    // the count of outstanding loads is the same everywhere
+    auto load_tile = [&](int kt, int stage) {
+        const int k0 = (kt < nk ? kt : nk - 1) * DBK;
+#pragma unroll
+        for (int a = 0; a < 3; a++)
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                LDS_AS u16 *dst = (LDS_AS u16 *)smem + stage * DSTAGE + a * DARR + (i * 8 + wv) * 512;
+                __builtin_amdgcn_global_load_lds((const void *)(src[a * 2 + i] + k0), (LDS_AS void *)dst, 16, 0, 0);
+            }
+    };
+
+    floatx16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
+
+    const int r32 = lane & 31, c2 = lane >> 5;
+    auto compute = [&](int stage) {
+        const u16 *sw = smem + stage * DSTAGE;
+        const u16 *sh = sw + DARR;
+        const u16 *sl = sh + DARR;
+#pragma unroll
+        for (int ks = 0; ks < DBK / 16; ks++) {
+            bf16x8 fw[4], fh[2], fl[2];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                fw[i] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
+                                                       sw + 8 * dswz(wn * 128 + i * 32 + r32, 2 * ks + c2)));
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const int off = 8 * dswz(wm * 64 + j * 32 + r32, 2 * ks + c2);
+                fh[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sh + off));
+                fl[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sl + off));
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++) {
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fh[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fl[j], acc[i][j], 0, 0, 0);
+                }
+        }
+    };
+
+    // Barrier between k-tiles: wait until only the newest tile's 6 loads may be
+    // outstanding and every LDS read is done, then s_barrier.  (__syncthreads
+    // would also wait for the newest tile: its fence covers the LDS writes of
+    // every outstanding load.)  s_waitcnt fields: vmcnt 6, expcnt 7, lgkmcnt 0.
+    constexpr int WAIT_VM6_LGKM0 = 6 | (7 << 4) | (0 << 8);
+    load_tile(0, 0);
+    load_tile(1, 1);
+    __builtin_amdgcn_s_waitcnt(WAIT_VM6_LGKM0);
+    __builtin_amdgcn_s_barrier();
+    for (int kt = 0; kt < nk; kt++) {
+        // stage (kt+2)%3 held tile kt-1, which every wave finished reading before
+        // the previous barrier; tile kt+1 is complete after this iteration's wait
+        load_tile(kt + 2, (kt + 2) % DNSTAGE);
+        compute(kt % DNSTAGE);
+        __builtin_amdgcn_s_waitcnt(WAIT_VM6_LGKM0);
+        __builtin_amdgcn_s_barrier();
+    }
+    // the loads issued past the last tile land in stages nobody reads again;
+    // they must finish before the block's LDS is released
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+
+    // acc[i][j]: features n0 + wn*128 + i*32 + (e/4)*8 + c2*4 + e%4, token m0 + wm*64 + j*32 + r32
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int m = m0 + wm * 64 + j * 32 + r32;
+            if (m >= M) continue;
+            float *dst = p.out + (size_t)m * p.ldo;
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int n = n0 + wn * 128 + i * 32 + g * 8 + c2 * 4;
+                const floatx16 &v = acc[i][j];
+                if (n + 3 < p.N) {
+                    *reinterpret_cast<float4 *>(dst + n) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+                } else {
+                    if (n < p.N) dst[n] = v[4 * g];
+                    if (n + 1 < p.N) dst[n + 1] = v[4 * g + 1];
+                    if (n + 2 < p.N) dst[n + 2] = v[4 * g + 2];
+                }
+            }
+        }
+}
+
+bool dma_lds_attr() {
+    static int ok = -1;
+    if (ok < 0)
+        ok = hipFuncSetAttribute((const void *)gemm_dma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)DMA_LDS) == hipSuccess;
+    return ok == 1;
+}
+
+}  // namespace
+
 void launch_gemm(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi, const u16 *a_lo,
                  int lda, int M, float *out, int ldo) {
     if (M <= 0) return;
     GemmParams p{};
     fill(p, segs, nseg, K, a_hi, a_lo, lda, M, out, ldo);
+    // grids of at least one 256 x 256 tile per CU take the direct-to-LDS kernel;
+    // smaller ones keep more, smaller blocks
+    const long big = (long)((p.N + DBN - 1) / DBN) * ((M + DBM - 1) / DBM);
+    if (K % DBK == 0 && big >= num_cus() && dma_lds_attr()) {
+        hipLaunchKernelGGL(gemm_dma_kernel, dim3((p.N + DBN - 1) / DBN, (M + DBM - 1) / DBM, 1), dim3(DNTHR), DMA_LDS,
+                           st, p);
+        return;
+    }
     dim3 grid((p.N + BN - 1) / BN, (M + BM - 1) / BM, 1);
     gemm_lds_attr();
     hipLaunchKernelGGL(gemm_kernel, grid, dim3(NTHR), GEMM_LDS, st, p);
