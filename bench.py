@@ -34,12 +34,12 @@ HBM_PEAK_GBS = 8000.0
 _ATTN_SOURCES = {"decoder_only_forward_amd/csrc/k_attn_decode.hip":
                  "1084c52bf6de3c084abce53d1b288424c98f0d0cf2b8dbe1236f077a5378e7b6",
                  "decoder_only_forward_amd/csrc/common.h":
-                 "394ed98a1109455d98e2b24652372937a85b2028e1e5c3ff1d6749474c8ff8b6"}
+                 "4c1abc6ecd4c94ab3996e24a5cb4f31b82f3cc871264bbeaa118f84a57e98843"}
 MEASURED_TRAFFIC = {
     ("attn_decode_kernel", "fp32"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 1076060816},
+                                     "bytes_per_launch": 1076092044},
     ("attn_decode_kernel", "bf16"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 539231560},
+                                     "bytes_per_launch": 539260935},
 }
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode tok/s + prefill tok/s (Mistral-7B shape) and % of HBM / MFMA roofline"
