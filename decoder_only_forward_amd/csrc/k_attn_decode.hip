@@ -301,20 +301,45 @@ __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
     }
 }
 
-__global__ void attn_merge_kernel(int nh, int hd, int splits, const float *__restrict__ part,
-                                  u16 *__restrict__ o_hi, u16 *__restrict__ o_lo, float *__restrict__ o_f32) {
-    const int h = blockIdx.x, b = blockIdx.y;
-    const float *src = part + ((size_t)b * nh + h) * splits * (hd + 2);
-    float mx = -INFINITY;
-    for (int s = 0; s < splits; s++) mx = fmaxf(mx, src[s * (hd + 2) + hd]);
-    for (int i = threadIdx.x; i < hd; i += blockDim.x) {
-        float L = 0.f, A = 0.f;
-        for (int s = 0; s < splits; s++) {
-            const float ms = src[s * (hd + 2) + hd];
-            const float f = ms == -INFINITY ? 0.f : fast_exp2(ms - mx);
-            L += src[s * (hd + 2) + hd + 1] * f;
-            A += src[s * (hd + 2) + i] * f;
+// Merge of the splits of one (row, head): weights f_s = 2^(m_s - max m) are
+// formed once per split into LDS; every output dim then sums its splits in
+// ascending order (the loads of a batch issued together), and so does the
+// normaliser.  At most 64 splits (the launcher's bound).
+__global__ void __launch_bounds__(128) attn_merge_kernel(int nh, int hd, int splits, const float *__restrict__ part,
+                                                         u16 *__restrict__ o_hi, u16 *__restrict__ o_lo,
+                                                         float *__restrict__ o_f32) {
+    __shared__ float fs[64], ls[64];
+    __shared__ float sL;
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int ld = hd + 2;
+    const float *src = part + ((size_t)b * nh + h) * splits * ld;
+    if (tid < WAVE) {
+        const float ms = tid < splits ? src[tid * ld + hd] : -INFINITY;
+        const float mx = wave_max(ms);
+        if (tid < splits) {
+            fs[tid] = ms == -INFINITY ? 0.f : fast_exp2(ms - mx);
+            ls[tid] = src[tid * ld + hd + 1];
         }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float L = 0.f;
+        for (int s = 0; s < splits; s++) L += ls[s] * fs[s];
+        sL = L;
+    }
+    __syncthreads();
+    const float L = sL;
+    for (int i = tid; i < hd; i += blockDim.x) {
+        float A = 0.f;
+        int s = 0;
+        for (; s + 8 <= splits; s += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++) v[u] = src[(s + u) * ld + i];
+#pragma unroll
+            for (int u = 0; u < 8; u++) A += v[u] * fs[s + u];
+        }
+        for (; s < splits; s++) A += src[s * ld + i] * fs[s];
         store_out(A / L, (size_t)b * nh * hd + (size_t)h * hd + i, o_hi, o_lo, o_f32);
     }
 }
