@@ -223,8 +223,12 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
     __shared__ __attribute__((aligned(16))) u16 sVh[HD * VLD];
     __shared__ __attribute__((aligned(16))) u16 sVl[KB ? 8 : HD * VLD];
 
-    const int kvh = blockIdx.y;
-    const int rb = gridDim.x - 1 - blockIdx.x;  // longest rows first
+    // blocks are dispatched in linear order (x fastest): walk the row blocks
+    // from the longest (last rows) down, all kv heads of one row block together,
+    // so the longest blocks start first on every CU
+    const int lin = blockIdx.x + blockIdx.y * gridDim.x;
+    const int kvh = lin % gridDim.y;
+    const int rb = gridDim.x - 1 - lin / gridDim.y;
     const int t0 = rb * ROWS;
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
     const int ql = lane & 31, hh = lane >> 5;

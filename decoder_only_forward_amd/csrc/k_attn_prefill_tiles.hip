@@ -147,8 +147,12 @@ __global__ void __launch_bounds__(NTHR, 1) attn_tiles_kernel(int T, int start_po
     constexpr int DT = HD / 32;     // output dim tiles
     constexpr int IMGU16 = I::BYTES / 2;
 
-    const int kvh = blockIdx.y;
-    const int rb = gridDim.x - 1 - blockIdx.x;  // longest rows first
+    // blocks are dispatched in linear order (x fastest): walk the row blocks
+    // from the longest (last rows) down, all kv heads of one row block together,
+    // so the longest blocks start first on every CU
+    const int lin = blockIdx.x + blockIdx.y * gridDim.x;
+    const int kvh = lin % gridDim.y;
+    const int rb = gridDim.x - 1 - lin / gridDim.y;
     const int t0 = rb * ROWS;
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
     const int ql = lane & 31, hh = lane >> 5;
