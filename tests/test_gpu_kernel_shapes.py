@@ -1,0 +1,64 @@
+"""Parity at shapes chosen to reach the edges of the prefill kernels.
+
+* The 256 x 256-tile GEMM (taken when a projection has at least one tile per
+  CU) with a feature count that is not a multiple of 256 and a token count that
+  is not a multiple of 256: the clamped loads and masked stores of both tails.
+* The tile-image prefill attention with ragged chunk lengths and start_pos > 0
+  (AppendPrefill reading the cached history through the per-layer tile pass),
+  with an fp32 and with a bf16 K/V cache, at head_dim 64 and 128.
+
+Each case compares every prefill row's hidden state after the layer and the
+last row's logits with the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+from decoder_only_forward_amd import configs, synth
+from parity_util import Pair, check_argmax, check_logits, rel_l2, tol, HIDDEN_REL_L2
+
+pytestmark = pytest.mark.gpu
+
+
+def _chunks(pair, toks, sizes, what):
+    c = pair.cfg
+    tl = pair.tol
+    hid_tol = HIDDEN_REL_L2 if not c.kv_bf16 else tl["rel"]
+    start = 0
+    for n in sizes:
+        part = toks[start:start + n]
+        hid, _, _ = pair.capture_buffers(n)
+        g = pair.gpu.prefill(part, start_pos=start).cpu().numpy()
+        r = pair.ora.prefill(part, start_pos=start, capture=True)
+        torch.cuda.synchronize()
+        h = hid.cpu().numpy()
+        for t in range(n):
+            rl = rel_l2(h[1, t], r["hidden"][1, t])
+            assert rl <= hid_tol, f"{what} chunk at {start}: row {t} hidden rel L2 {rl:.3e}"
+        check_logits(g, r["logits"][0], f"{what} chunk at {start}", **tl)
+        check_argmax(g, r["logits"][0], f"{what} chunk at {start}", **tl)
+        start += n
+
+
+ODD = configs.ModelConfig("odd-1l", n_layers=1, hidden=512, n_heads=4, n_kv_heads=2, head_dim=128,
+                          ffn_dim=14400, vocab=1000, max_seq=1024, rms_eps=1e-5, rope_theta=1e4)
+
+
+def test_gemm_feature_and_token_tails_on_the_large_tile_kernel():
+    """gate|up has 28800 features (112.5 tiles of 256) and the prompt 700 tokens
+    (2.7 tiles): 339 tiles, so the 256x256 kernel runs with both tails."""
+    pair = Pair(ODD, max_prefill=700)
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 700, ODD.vocab).tolist()
+    _chunks(pair, toks, [700], "odd shape")
+
+
+@pytest.mark.parametrize("kv_bf16", [False, True], ids=["fp32-cache", "bf16-cache"])
+@pytest.mark.parametrize("base", [configs.SMOLLM2, configs.MISTRAL], ids=["hd64-g3", "hd128-g4"])
+def test_tile_attention_appends_ragged_chunks(base, kv_bf16):
+    """Chunks of 100, 93 and 57 tokens (starts 0, 100, 193): every chunk after
+    the first reads history written by earlier calls through the tile pass."""
+    cfg = configs.one_layer(base).replace(name=base.name + "-1l-append", kv_bf16=kv_bf16,
+                                          sliding_window=0, max_seq=256)
+    pair = Pair(cfg, max_prefill=100)
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 250, cfg.vocab).tolist()
+    _chunks(pair, toks, [100, 93, 57], cfg.name)
