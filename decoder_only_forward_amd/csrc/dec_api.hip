@@ -47,7 +47,7 @@ struct GraphEntry {
 
 struct Plan {  // byte offsets into the workspace
     size_t kv_layer;        // elements of one layer's K (or V) cache
-    size_t k, v, ck, cv, kvimg, x, a_hi, a_lo, a_f32, part, q, attn, rope, tok, pos, slot, amax, ssq;
+    size_t k, v, ck, cv, kvimg, s_hi, s_lo, x, a_hi, a_lo, a_f32, part, q, attn, rope, tok, pos, slot, amax, ssq;
     size_t moe_ids, moe_w, moe_cnt, moe_off, moe_pairs, g_hi, g_lo, g_f32, moe_y;
     size_t part_floats, act_elems, total;
     int rows;               // max rows of one pass (max(max_batch, max_prefill))
@@ -69,6 +69,7 @@ struct dec_model {
     char *kc, *vc;          // caches, kv_es bytes per element
     char *ck, *cv;          // chunk K/V of a deferred-commit prefill (ring only)
     void *kvimg;            // prefill attention's K/V tile images (null: not used)
+    u16 *s_hi, *s_lo;       // fused SwiGLU output of a prefill (null: not used)
     int kv_es;
     float *x, *a_f32, *part, *q, *attn, *moe_w, *g_f32, *moe_y, *ssq;
     u16 *a_hi, *a_lo, *g_hi, *g_lo;
@@ -143,6 +144,10 @@ bool plan(const dec_config &c, Plan &p) {
     const bool ring = c.sliding_window > 0 && c.max_seq == c.sliding_window;
     p.ck = take(ring ? (size_t)c.max_prefill * kvd * es : 0);
     p.cv = take(ring ? (size_t)c.max_prefill * kvd * es : 0);
+    // silu(gate) * up of a prefill's dense FFN, written by the fused gate|up GEMM
+    const bool fuse_silu = !E && c.weight_dtype != DEC_WEIGHT_F32 && c.max_prefill > 64;
+    p.s_hi = take(fuse_silu ? (size_t)c.max_prefill * F * 2 : 0);
+    p.s_lo = take(fuse_silu ? (size_t)c.max_prefill * F * 2 : 0);
     // prefill attention's K/V tile images (positions [0, max_seq) of one sequence)
     p.kvimg = take(c.weight_dtype == DEC_WEIGHT_F32 ? 0
                    : attn_tiles_bytes(c.max_seq, c.n_kv_heads, c.head_dim, c.kv_dtype == DEC_KV_BF16));
@@ -227,6 +232,12 @@ struct Tick {
         t.launches++;
         t.bytes += bytes;
         t.flops += flops;
+    }
+    void cancel() {  // nothing was launched: give the events back
+        if (!e1) return;
+        m->pool.push_back(e1);
+        m->pool.push_back(e2);
+        e1 = e2 = nullptr;
     }
 };
 
@@ -400,10 +411,20 @@ void run_pass(dec_model *m, const Pass &ps) {
         const float *next_gain = (l + 1 < c.n_layers) ? m->L[l + 1].attn_norm : m->out_norm;
         if (c.n_experts == 0) {
             WSeg gu[2] = {{w.w_gate, F}, {w.w_up, F}};
-            Partials pg = proj(m, gu, 2, d, T, ah, al, af, d);
-            launch_silu_mul(st, T, F, pg, ah, al, af);
+            // a large prefill takes the gate|up GEMM with silu(gate) * up in its epilogue
+            bool fused = false;
+            if (!f32w && T > 64 && m->s_hi) {
+                Tick tk(m, DEC_K_GEMM);
+                fused = launch_gemm_silu(st, w.w_gate, w.w_up, F, d, ah, al, d, T, m->s_hi, m->s_lo, F);
+                if (fused) tk.done(2.0 * F * d * 2 + (double)T * d * 4 + (double)T * F * 4, 2.0 * T * 2 * F * d);
+                else tk.cancel();
+            }
+            if (!fused) {
+                Partials pg = proj(m, gu, 2, d, T, ah, al, af, d);
+                launch_silu_mul(st, T, F, pg, ah, al, af);
+            }
             WSeg wd[1] = {{w.w_down, d}};
-            Partials pd = proj(m, wd, 1, F, T, ah, al, af, F);
+            Partials pd = proj(m, wd, 1, F, T, fused ? m->s_hi : ah, fused ? m->s_lo : al, af, F);
             launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, pd, nullptr, nullptr, 0, next_gain,
                                  eps, ah, al, af, caph(l + 1), m->ssq);
         } else {
@@ -576,6 +597,8 @@ int dec_create(const dec_config *cfg, const dec_weights *w, void *workspace, siz
     m->ck = b + p.ck;
     m->cv = b + p.cv;
     m->kvimg = p.kvimg < p.x ? (void *)(b + p.kvimg) : nullptr;
+    m->s_hi = p.s_hi < p.s_lo ? (u16 *)(b + p.s_hi) : nullptr;
+    m->s_lo = m->s_hi ? (u16 *)(b + p.s_lo) : nullptr;
     m->kv_es = cfg->kv_dtype == DEC_KV_BF16 ? 2 : 4;
     m->x = (float *)(b + p.x);
     m->a_hi = (u16 *)(b + p.a_hi);

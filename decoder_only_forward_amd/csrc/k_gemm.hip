@@ -256,14 +256,22 @@ constexpr size_t DMA_LDS = DNSTAGE * DSTAGE * sizeof(u16);
 // 16-byte chunk c (of 4) of row r is stored at chunk c ^ ((r >> 2) & 3) of the row
 __device__ __forceinline__ int dswz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 
-__global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p) {
+// SILU: the SwiGLU form.  p.w[0] is the gate and p.w[1] the up matrix, each
+// p.N rows; a block tile covers 128 gate features and the same 128 up
+// features (wave wn: 64 of each, its MFMA row tiles 0, 1 gate and 2, 3 up), so
+// each lane holds gate and up of the same (feature, token) and the epilogue
+// writes silu(gate) * up as bf16 (hi, lo) pairs, row stride p.ldo.
+template <bool SILU>
+__global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *__restrict__ s_hi,
+                                                            u16 *__restrict__ s_lo) {
     extern __shared__ __attribute__((aligned(16))) u16 smem[];
     const int tid = threadIdx.x;
     const int lane = tid % WAVE, wv = tid / WAVE;
     const int wn = wv & 1, wm = wv >> 1;
     const int M = p.M;
 
-    const int ntn = (p.N + DBN - 1) / DBN, ntm = gridDim.y;
+    constexpr int FPT = SILU ? DBN / 2 : DBN;    // output features per block tile
+    const int ntn = (p.N + FPT - 1) / FPT, ntm = gridDim.y;
     const int bid = blockIdx.x + blockIdx.y * gridDim.x;
     int tn, tm;
     if ((ntn & 7) == 0) {
@@ -284,7 +292,7 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p) {
     }
     const int m0 = tm * DBM;
     if (m0 >= M) return;
-    const int n0 = tn * DBN;
+    const int n0 = tn * FPT;
 
     // load instruction i (0, 1) of an operand array: wave wv fills the 1 KB slot
     // i*8 + wv, lane L the 16-byte chunk slot*64 + L, i.e. row r = chunk / 4 and
@@ -294,13 +302,21 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p) {
     for (int i = 0; i < 2; i++) {
         const int P = (i * 8 + wv) * 64 + lane;
         const int r = P >> 2, c = (P & 3) ^ ((r >> 2) & 3);
-        int n = n0 + r;
-        n = n < p.N ? n : p.N - 1;
-        const u16 *wp = p.w[0];
-        int start = 0;
-        if (p.nseg > 1 && n >= p.seg_end[0]) { wp = p.w[1]; start = p.seg_end[0]; }
-        if (p.nseg > 2 && n >= p.seg_end[1]) { wp = p.w[2]; start = p.seg_end[1]; }
-        src[i] = wp + (size_t)(n - start) * p.K + c * 8;
+        if constexpr (SILU) {
+            // LDS row r: wave r / 128, MFMA row tile (r % 128) / 32 (0, 1 gate; 2, 3 up)
+            const int t = (r & 127) >> 5;
+            int f = n0 + (r >> 7) * 64 + (t & 1) * 32 + (r & 31);
+            f = f < p.N ? f : p.N - 1;
+            src[i] = (t < 2 ? p.w[0] : p.w[1]) + (size_t)f * p.K + c * 8;
+        } else {
+            int n = n0 + r;
+            n = n < p.N ? n : p.N - 1;
+            const u16 *wp = p.w[0];
+            int start = 0;
+            if (p.nseg > 1 && n >= p.seg_end[0]) { wp = p.w[1]; start = p.seg_end[0]; }
+            if (p.nseg > 2 && n >= p.seg_end[1]) { wp = p.w[2]; start = p.seg_end[1]; }
+            src[i] = wp + (size_t)(n - start) * p.K + c * 8;
+        }
         int m = m0 + r;
         m = m < M ? m : M - 1;
         src[2 + i] = p.a_hi + (size_t)m * p.lda + c * 8;
@@ -377,6 +393,40 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p) {
     // they must finish before the block's LDS is released
     __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
 
+    if constexpr (SILU) {
+        // acc[i][j] (gate, i = 0, 1) and acc[i+2][j] (up): feature
+        // n0 + wn*64 + i*32 + (e/4)*8 + c2*4 + e%4, token m0 + wm*64 + j*32 + r32
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const int m = m0 + wm * 64 + j * 32 + r32;
+                if (m >= M) continue;
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    const int f = n0 + wn * 64 + i * 32 + g * 8 + c2 * 4;
+                    uint32_t hb[4], lb[4];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const float gt = acc[i][j][4 * g + e], up = acc[i + 2][j][4 * g + e];
+                        split_bf16(gt / (1.0f + expf(-gt)) * up, hb[e], lb[e]);
+                    }
+                    const size_t off = (size_t)m * p.ldo + f;
+                    if (f + 3 < p.N) {
+                        *reinterpret_cast<uint2 *>(s_hi + off) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+                        *reinterpret_cast<uint2 *>(s_lo + off) = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            if (f + e < p.N) {
+                                s_hi[off + e] = (u16)hb[e];
+                                s_lo[off + e] = (u16)lb[e];
+                            }
+                    }
+                }
+            }
+        return;
+    }
     // acc[i][j]: features n0 + wn*128 + i*32 + (e/4)*8 + c2*4 + e%4, token m0 + wm*64 + j*32 + r32
 #pragma unroll
     for (int i = 0; i < 4; i++)
@@ -403,7 +453,9 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p) {
 bool dma_lds_attr() {
     static int ok = -1;
     if (ok < 0)
-        ok = hipFuncSetAttribute((const void *)gemm_dma_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+        ok = hipFuncSetAttribute((const void *)gemm_dma_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)DMA_LDS) == hipSuccess &&
+             hipFuncSetAttribute((const void *)gemm_dma_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                  (int)DMA_LDS) == hipSuccess;
     return ok == 1;
 }
@@ -419,13 +471,27 @@ void launch_gemm(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
     // smaller ones keep more, smaller blocks
     const long big = (long)((p.N + DBN - 1) / DBN) * ((M + DBM - 1) / DBM);
     if (K % DBK == 0 && big >= num_cus() && dma_lds_attr()) {
-        hipLaunchKernelGGL(gemm_dma_kernel, dim3((p.N + DBN - 1) / DBN, (M + DBM - 1) / DBM, 1), dim3(DNTHR), DMA_LDS,
-                           st, p);
+        hipLaunchKernelGGL(gemm_dma_kernel<false>, dim3((p.N + DBN - 1) / DBN, (M + DBM - 1) / DBM, 1), dim3(DNTHR),
+                           DMA_LDS, st, p, nullptr, nullptr);
         return;
     }
     dim3 grid((p.N + BN - 1) / BN, (M + BM - 1) / BM, 1);
     gemm_lds_attr();
     hipLaunchKernelGGL(gemm_kernel, grid, dim3(NTHR), GEMM_LDS, st, p);
+}
+
+bool launch_gemm_silu(hipStream_t st, const void *w_gate, const void *w_up, int F, int K, const u16 *a_hi,
+                      const u16 *a_lo, int lda, int M, u16 *s_hi, u16 *s_lo, int ldo) {
+    if (M <= 0) return true;
+    const long tiles = (long)((F + DBN / 2 - 1) / (DBN / 2)) * ((M + DBM - 1) / DBM);
+    if (K % DBK != 0 || tiles < num_cus() || !dma_lds_attr()) return false;
+    GemmParams p{};
+    WSeg segs[2] = {{w_gate, F}, {w_up, F}};
+    fill(p, segs, 2, K, a_hi, a_lo, lda, M, nullptr, ldo);
+    p.N = F;
+    hipLaunchKernelGGL(gemm_dma_kernel<true>, dim3((F + DBN / 2 - 1) / (DBN / 2), (M + DBM - 1) / DBM, 1), dim3(DNTHR),
+                       DMA_LDS, st, p, s_hi, s_lo);
+    return true;
 }
 
 void launch_gemm_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi,

@@ -72,6 +72,13 @@ void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
 void launch_gemm(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi, const u16 *a_lo,
                  int lda, int M, float *out, int ldo);
 
+// The gate|up projection of a SwiGLU FFN with silu(gate) * up fused into the
+// epilogue, written as bf16 (hi, lo) pairs [M][ldo] (F features).  Taken only
+// when the grid has at least one 256 x 256 tile per CU; returns false (nothing
+// launched) otherwise.  s_hi/s_lo must not alias a_hi/a_lo.
+bool launch_gemm_silu(hipStream_t st, const void *w_gate, const void *w_up, int F, int K, const u16 *a_hi,
+                      const u16 *a_lo, int lda, int M, u16 *s_hi, u16 *s_lo, int ldo);
+
 // fp32-weight projection (any M): out[m][n] = sum_k a[m][k] W[n][k].
 void launch_gemm_f32(hipStream_t st, const WSeg *segs, int nseg, int K, const float *a, int lda,
                      int M, float *out, int ldo);
