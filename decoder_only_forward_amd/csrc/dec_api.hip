@@ -331,7 +331,7 @@ Partials proj_grouped(dec_model *m, const WSeg *segs, int nseg, int K, int T, co
         return Partials{m->part, 1, 0, N};
     }
     if (T <= 64) {
-        const int S = gemv_splits(N * act, K, T);
+        const int S = gemv_grouped_splits(N * act, K, T);
         Tick tk(m, DEC_K_GEMV);
         launch_gemv_grouped(m->st, segs, nseg, K, hi, lo, lda, T, E, m->moe_off, es, m->part, S, (size_t)TP * N, N);
         tk.done((double)N * K * 2 * act + (double)TP * K * 4 + (double)TP * N * 4, 2.0 * TP * N * K);

@@ -12,6 +12,13 @@
 // activations (hi and lo) for a chunk of k sit in LDS, shared by the 4 waves.
 // Grid = (row tiles, k splits[, experts]); split partials are summed by the
 // consumer kernel in a fixed order (no atomics).
+//
+// When K is a multiple of 128 the dense projections take gemv_dma_kernel
+// instead: each 128-k stage of the block's weight rows and of the activation
+// columns goes from global memory straight into a ring of LDS stages
+// (global_load_lds, no register staging), so the weight stream keeps several
+// stages in flight while earlier ones are multiplied, and one block per CU
+// with splits = CUs / row tiles covers the matrix in a single round.
 #include "common.h"
 #include "kernels.h"
 
@@ -200,6 +207,167 @@ void launch_common(hipStream_t st, GemvParams &p, int ksplit, int B_for_tiles, i
 
 }  // namespace
 
+namespace {
+
+constexpr int DKS = 128;           // k per stage
+constexpr int DROWS = 128;         // weight rows per block
+#define LDS_AS __attribute__((address_space(3)))
+
+template <int NT>
+constexpr int dma_stages() { return NT <= 1 ? 4 : NT <= 4 ? 3 : 2; }
+template <int NT>
+constexpr size_t dma_lds() { return (size_t)dma_stages<NT>() * (DROWS * DKS + 16 * NT * DKS) * 2; }
+
+// Stage layout: the weight tile [128 rows][128 k] then the activation tile
+// [16*NT columns][128 k] (column t*16 + m: hi of batch row t*8 + m for m < 8,
+// lo of batch row t*8 + m - 8 above), bf16; each 256-byte row holds 16 chunks
+// of 16 bytes, chunk c of row r stored at c ^ (r & 15), so the 16 rows an
+// operand read touches per lane group fall in distinct banks.
+template <int NT>
+__global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
+    extern __shared__ __attribute__((aligned(16))) u16 smem[];
+    constexpr int NSTAGE = dma_stages<NT>();
+    constexpr int WST = DROWS * DKS;           // u16 of the weight tile
+    constexpr int STG = WST + 16 * NT * DKS;   // u16 per stage
+    constexpr int NLD = 8 + NT;                // 16-byte loads per thread per stage
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int r = lane & 15, c = lane >> 4;
+    const int B = p.B;
+    const int n0 = blockIdx.x * DROWS;
+    const int kbeg = blockIdx.y * p.kps;
+    const int kend = min(p.K, kbeg + p.kps);
+    const int nst = kbeg < kend ? (kend - kbeg) / DKS : 0;
+
+    // load i of this thread fills stage chunk P = (i*4 + wv)*64 + lane (lane
+    // L of a wave writes 16 bytes at the wave's base + 16 L): the weight tile
+    // for i < 8, the activation tile after; row P / 16, logical chunk
+    // (P % 16) ^ (row & 15)
+    const u16 *src[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; i++) {
+        const int P = (i * 4 + wv) * 64 + lane;
+        if (i < 8) {
+            const int row = P >> 4, lc = (P & 15) ^ (row & 15);
+            int n = n0 + row;
+            n = n < p.N ? n : p.N - 1;
+            const u16 *wp = p.w[0];
+            int start = 0;
+            if (p.nseg > 1 && n >= p.seg_end[0]) { wp = p.w[1]; start = p.seg_end[0]; }
+            if (p.nseg > 2 && n >= p.seg_end[1]) { wp = p.w[2]; start = p.seg_end[1]; }
+            src[i] = wp + (size_t)(n - start) * p.K + kbeg + lc * 8;
+        } else {
+            const int Q = P - 8 * 256;
+            const int col = Q >> 4, lc = (Q & 15) ^ (col & 15);
+            const int t = col >> 4, m = col & 15;
+            int b = t * 8 + (m & 7);
+            b = b < B ? b : B - 1;   // columns past B read a valid row; their outputs are not stored
+            src[i] = (m < 8 ? p.a_hi : p.a_lo) + (size_t)b * p.lda + kbeg + lc * 8;
+        }
+    }
+    // every iteration issues its loads (the last stage again past the end), so
+    // the count of outstanding loads is the same everywhere
+    auto load_stage = [&](int g, int stage) {
+        const int k0 = (g < nst ? g : nst - 1) * DKS;
+#pragma unroll
+        for (int i = 0; i < NLD; i++) {
+            LDS_AS u16 *dst = (LDS_AS u16 *)smem + stage * STG + (i * 4 + wv) * 512;
+            __builtin_amdgcn_global_load_lds((const void *)(src[i] + k0), (LDS_AS void *)dst, 16, 0, 0);
+        }
+    };
+
+    floatx4 acc[2][NT];
+#pragma unroll
+    for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+        for (int t = 0; t < NT; t++) acc[rt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    if (nst > 0) {
+        // between stages: wait until the loads of the newest NSTAGE-2 stages at
+        // most are outstanding and every LDS read is done, then a plain barrier
+        // (__syncthreads would also wait for the newest stages).  s_waitcnt
+        // fields: vmcnt (bits 3:0 and 15:14), expcnt 7, lgkmcnt 0.
+        constexpr int WAITN = NLD * (NSTAGE - 2);
+        constexpr int WAIT = (WAITN & 15) | (7 << 4) | (0 << 8) | ((WAITN >> 4) << 14);
+#pragma unroll
+        for (int g = 0; g < NSTAGE - 1; g++) load_stage(g, g);
+        __builtin_amdgcn_s_waitcnt(WAIT);
+        __builtin_amdgcn_s_barrier();
+        for (int g = 0; g < nst; g++) {
+            // stage (g-1) % NSTAGE, which this load refills, was finished by every
+            // wave before the previous barrier
+            load_stage(g + NSTAGE - 1, (g + NSTAGE - 1) % NSTAGE);
+            const u16 *sw = smem + (g % NSTAGE) * STG;
+            const u16 *sa = sw + WST;
+#pragma unroll
+            for (int s = 0; s < DKS / 32; s++) {
+                const int lc = s * 4 + c;
+                bf16x8 wf[2];
+#pragma unroll
+                for (int rt = 0; rt < 2; rt++) {
+                    const int row = wv * 32 + rt * 16 + r;
+                    wf[rt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sw + row * DKS + 8 * (lc ^ (row & 15))));
+                }
+#pragma unroll
+                for (int t = 0; t < NT; t++) {
+                    const int col = t * 16 + r;
+                    const bf16x8 bf = __builtin_bit_cast(
+                        bf16x8, *reinterpret_cast<const u32x4 *>(sa + col * DKS + 8 * (lc ^ (col & 15))));
+#pragma unroll
+                    for (int rt = 0; rt < 2; rt++)
+                        acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[rt], bf, acc[rt][t], 0, 0, 0);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(WAIT);
+            __builtin_amdgcn_s_barrier();
+        }
+        // the loads issued past the last stage must land before the block's LDS
+        // is released
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    }
+
+    // lane (r, c) holds rows 4c..4c+3 of each row tile for column r; column r
+    // (hi) and r+8 (lo) of the same batch row are summed.
+    float *out = p.out + (size_t)blockIdx.y * p.split_stride;
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+#pragma unroll
+        for (int rt = 0; rt < 2; rt++) {
+            floatx4 v = acc[rt][t];
+            floatx4 o;
+            o[0] = __shfl_xor(v[0], 8, WAVE);
+            o[1] = __shfl_xor(v[1], 8, WAVE);
+            o[2] = __shfl_xor(v[2], 8, WAVE);
+            o[3] = __shfl_xor(v[3], 8, WAVE);
+            const int b = t * 8 + (r & 7);
+            if (r < 8 && b < B) {
+                const int nn = n0 + wv * 32 + rt * 16 + 4 * c;
+                float *dst = out + (size_t)b * p.ldo + nn;
+                const float4 sv = make_float4(v[0] + o[0], v[1] + o[1], v[2] + o[2], v[3] + o[3]);
+                if (nn + 3 < p.N) {
+                    *reinterpret_cast<float4 *>(dst) = sv;
+                } else {
+                    if (nn < p.N) dst[0] = sv.x;
+                    if (nn + 1 < p.N) dst[1] = sv.y;
+                    if (nn + 2 < p.N) dst[2] = sv.z;
+                }
+            }
+        }
+    }
+}
+
+template <int NT>
+bool launch_dma_nt(hipStream_t st, const GemvParams &p, dim3 grid) {
+    static int ok = -1;
+    if (ok < 0)
+        ok = hipFuncSetAttribute((const void *)gemv_dma_kernel<NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)dma_lds<NT>()) == hipSuccess;
+    if (ok != 1) return false;
+    hipLaunchKernelGGL((gemv_dma_kernel<NT>), grid, dim3(256), dma_lds<NT>(), st, p);
+    return true;
+}
+
+}  // namespace
+
 int num_cus() {
     static int n = 0;
     if (!n) {
@@ -211,19 +379,37 @@ int num_cus() {
     return n;
 }
 
-int gemv_max_splits(int K) { return K / 256 > 0 ? K / 256 : 1; }
+int gemv_max_splits(int K) {
+    if (K % 128 == 0) return K / 128 > 0 ? K / 128 : 1;
+    return K / 256 > 0 ? K / 256 : 1;
+}
 
-int gemv_splits(int N, int K, int B) {
+// The split rule of the register-staged kernel (MoE grouped projections, and K
+// not a multiple of 128): about 1024 blocks of 4 waves, splits of 256+ k.
+int gemv_grouped_splits(int N, int K, int B) {
     (void)B;
     const int tiles = (N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
     const int target = 1024;  // ~4 blocks per CU on 256 CUs
     int s = (target + tiles - 1) / tiles;
-    const int maxs = gemv_max_splits(K);
+    const int maxs = K / 256 > 0 ? K / 256 : 1;
     if (s > maxs) s = maxs;
     if (s < 1) s = 1;
     const int g = 32 * pick_j(K);
     int kps = (K + s - 1) / s;
     kps = (kps + g - 1) / g * g;
+    return (K + kps - 1) / kps;
+}
+
+int gemv_splits(int N, int K, int B) {
+    if (K % DKS != 0) return gemv_grouped_splits(N, K, B);
+    // one block per CU, a single round: splits = CUs / row tiles
+    const int tiles = (N + DROWS - 1) / DROWS;
+    int s = num_cus() / tiles;
+    const int maxs = K / DKS;
+    if (s > maxs) s = maxs;
+    if (s < 1) s = 1;
+    int kps = (K + s - 1) / s;
+    kps = (kps + DKS - 1) / DKS * DKS;
     return (K + kps - 1) / kps;
 }
 
@@ -247,6 +433,19 @@ void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
     p.split_stride = split_stride;
     p.ldo = ldo;
     p.grp_off = nullptr;
+    if (B <= 0) return;
+    if (K % DKS == 0) {
+        int kps = (K + ksplit - 1) / ksplit;
+        kps = (kps + DKS - 1) / DKS * DKS;
+        p.kps = kps;
+        const dim3 grid((p.N + DROWS - 1) / DROWS, ksplit, 1);
+        const int NT = (B + 7) / 8;
+        const bool done = NT <= 1 ? launch_dma_nt<1>(st, p, grid)
+                          : NT <= 2 ? launch_dma_nt<2>(st, p, grid)
+                          : NT <= 4 ? launch_dma_nt<4>(st, p, grid)
+                                    : launch_dma_nt<8>(st, p, grid);
+        if (done) return;
+    }
     launch_common(st, p, ksplit, B, 1);
 }
 
