@@ -27,19 +27,30 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-# HBM bytes per launch of the dominant decode kernel, from two rocprofv3 --pmc
-# passes (FETCH_SIZE, WRITE_SIZE) scaled by what the same counters read for a
-# 1 GiB device copy (x2.000 and x1.000): reported only while the kernel's
-# sources hash to the ones profiled, and only for the profiled workload.
-_ATTN_SOURCES = {"decoder_only_forward_amd/csrc/k_attn_decode.hip":
-                 "1084c52bf6de3c084abce53d1b288424c98f0d0cf2b8dbe1236f077a5378e7b6",
-                 "decoder_only_forward_amd/csrc/common.h":
-                 "4c1abc6ecd4c94ab3996e24a5cb4f31b82f3cc871264bbeaa118f84a57e98843"}
+# HBM bytes per launch of the measured kernels, from two rocprofv3 --pmc passes
+# (FETCH_SIZE, WRITE_SIZE) scaled by what the same counters read for a 1 GiB
+# device copy (x2.000 and x1.000): reported only while the kernel's sources hash
+# to the ones profiled, and only for the profiled workload.  GEMV and GEMM
+# figures are the mean over the launches of one step's mix of projections.
+_COMMON = {"decoder_only_forward_amd/csrc/common.h":
+           "4c1abc6ecd4c94ab3996e24a5cb4f31b82f3cc871264bbeaa118f84a57e98843"}
+_ATTN_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_decode.hip":
+                                 "260c81848d3ab8f870ab8f2345932ae86d051d16c909d38970cfd18605cb752e"})
+_GEMV_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemv.hip":
+                                 "d29a93bb8b472cfcd3ebfedd21c7e24006c422acc9b49340e77beb3e291ff0dc"})
+_GEMM_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemm.hip":
+                                 "bad153d55eb07af7b12ec5c221f25e2fe649cdb1f0dc78776ee10d178ba04e34"})
 MEASURED_TRAFFIC = {
     ("attn_decode_kernel", "fp32"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 1076092044},
+                                     "bytes_per_launch": 1076058487},
     ("attn_decode_kernel", "bf16"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 539260935},
+                                     "bytes_per_launch": 539258404},
+    ("gemv_decode", "fp32"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
+                              "bytes_per_launch": 121232331},
+    ("gemv_decode", "bf16"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
+                              "bytes_per_launch": 121232331},
+    ("gemm_prefill", "fp32"): {"sources": _GEMM_SOURCES, "workload": ("mistral-7b", 32, 4096),
+                               "bytes_per_launch": 1661499703},
 }
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode tok/s + prefill tok/s (Mistral-7B shape) and % of HBM / MFMA roofline"
@@ -262,18 +273,20 @@ def main():
     gemm_t, apre_t, gemv_t, attn_t = main_run["gemm"], main_run["apre"], main_run["gemv"], main_run["attn"]
     extra, dt_timed = main_run["extra"], main_run["dt_timed"]
 
-    def roof(t, bound):
+    def roof(t, bound, traffic_key=None):
         if t["launches"] == 0 or t["ms"] <= 0:
             return None
+        tr = measured_traffic(traffic_key, (cfg.name, B, P)) if traffic_key else None
+        tr = None if tr is None else round(tr / 1e9, 4)
         per = t["ms"] / t["launches"]
         if bound == "hbm":
             ach = t["bytes"] / t["launches"] / (per * 1e-3) / 1e9
             return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": tr, "traffic_unit": "GB per launch (rocprofv3 PMC)",
                     "avg_launch_us": round(per * 1e3, 2), "launches": t["launches"]}
         ach = t["flops"] / t["launches"] / (per * 1e-3) / 1e12
         return {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                "frac": round(ach / BF16_PEAK_TFLOPS, 4), "traffic": tr, "traffic_unit": "GB per launch (rocprofv3 PMC)",
                 "avg_launch_us": round(per * 1e3, 2), "launches": t["launches"]}
 
     out = {
@@ -297,17 +310,15 @@ def main():
         "decode_device_loop": main_run["loop"],
         "append_prefill_past_ring": main_run["append"],
         "ms_per_step_with_kernel_events": round(dt_timed * 1e3 / args.steps, 3),
-        "roofline_kernels": {"gemv_decode": roof(gemv_t, "hbm"), "gemm_prefill": roof(gemm_t, "mfma"),
+        "roofline_kernels": {"gemv_decode": roof(gemv_t, "hbm", ("gemv_decode", "fp32")),
+                             "gemm_prefill": roof(gemm_t, "mfma", ("gemm_prefill", "fp32")),
                              "attn_prefill": roof(apre_t, "mfma")},
     }
 
     def attn_roof(t, kv):
-        r = roof(t, "hbm")
+        r = roof(t, "hbm", ("attn_decode_kernel", kv))
         if r is not None:
             r["kernel"] = f"attn_decode_kernel (split-KV GQA decode attention, {kv} KV)"
-            tr = measured_traffic(("attn_decode_kernel", kv), (cfg.name, B, P))
-            r["traffic"] = None if tr is None else round(tr / 1e9, 4)
-            r["traffic_unit"] = "GB per launch (rocprofv3 PMC)"
             r["algorithmic_bytes_per_launch_gb"] = round(t["bytes"] / t["launches"] / 1e9, 4)
         return r
 
@@ -324,7 +335,7 @@ def main():
             "append_prefill_past_ring": bf16_run["append"],
             "ms_per_step_with_kernel_events": round(bf16_run["dt_timed"] * 1e3 / args.steps, 3),
             "roofline": attn_roof(bf16_run["attn"], "bf16"),
-            "roofline_kernels": {"gemv_decode": roof(bf16_run["gemv"], "hbm"),
+            "roofline_kernels": {"gemv_decode": roof(bf16_run["gemv"], "hbm", ("gemv_decode", "bf16")),
                                  "attn_prefill": roof(bf16_run["apre"], "mfma")},
         }
     if not args.no_cpu_baseline:
