@@ -93,10 +93,9 @@ namespace {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-int proj_splits(const dec_config &c, int N, int K, int B) {
-    (void)N;
+int proj_splits(const dec_config &c, int N, int K, int B, bool grouped = false) {
     if (c.weight_dtype == DEC_WEIGHT_F32 || B > 64) return 1;
-    return gemv_max_splits(K);
+    return grouped ? gemv_grouped_max_splits(K) : gemv_max_splits(N, K);
 }
 
 bool plan(const dec_config &c, Plan &p) {
@@ -124,8 +123,8 @@ bool plan(const dec_config &c, Plan &p) {
             need((int)E, (int)d, T);
             const int act = std::min<int>((int)E, TP);
             // grouped projections: splits sized as for act experts' rows
-            const int Sgu = (T <= 64) ? proj_splits(c, (int)(2 * F) * act, (int)d, T) : 1;
-            const int Sd = (T <= 64) ? proj_splits(c, (int)d * act, (int)F, T) : 1;
+            const int Sgu = (T <= 64) ? proj_splits(c, (int)(2 * F) * act, (int)d, T, true) : 1;
+            const int Sd = (T <= 64) ? proj_splits(c, (int)d * act, (int)F, T, true) : 1;
             pf = std::max(pf, (size_t)Sgu * TP * 2 * F);
             pf = std::max(pf, (size_t)Sd * TP * d);
         } else {

@@ -40,6 +40,7 @@ struct GemvParams {
     // [grp_off[e], grp_off[e+1]) and weight slice e (w + e*expert_stride).
     const int32_t *grp_off;
     size_t expert_stride;
+    int rot;   // LDS-ring kernel: start each block's k walk at stage blockIdx.x % stages
 };
 
 constexpr int ROWS_PER_BLOCK = 128;
@@ -209,27 +210,29 @@ void launch_common(hipStream_t st, GemvParams &p, int ksplit, int B_for_tiles, i
 
 namespace {
 
-constexpr int DKS = 128;           // k per stage
+constexpr int DKS = 64;            // k per stage
+constexpr int DCH = DKS / 8;       // 16-byte chunks per stage row
 constexpr int DROWS = 128;         // weight rows per block
+constexpr int DNSTAGE = 3;         // LDS ring depth
 #define LDS_AS __attribute__((address_space(3)))
 
 template <int NT>
-constexpr int dma_stages() { return NT <= 1 ? 4 : NT <= 4 ? 3 : 2; }
-template <int NT>
-constexpr size_t dma_lds() { return (size_t)dma_stages<NT>() * (DROWS * DKS + 16 * NT * DKS) * 2; }
+constexpr size_t dma_lds() { return (size_t)DNSTAGE * (DROWS * DKS + 16 * NT * DKS) * 2; }
 
-// Stage layout: the weight tile [128 rows][128 k] then the activation tile
-// [16*NT columns][128 k] (column t*16 + m: hi of batch row t*8 + m for m < 8,
-// lo of batch row t*8 + m - 8 above), bf16; each 256-byte row holds 16 chunks
-// of 16 bytes, chunk c of row r stored at c ^ (r & 15), so the 16 rows an
-// operand read touches per lane group fall in distinct banks.
+// Stage layout: the weight tile [128 rows][64 k] then the activation tile
+// [16*NT columns][64 k] (column t*16 + m: hi of batch row t*8 + m for m < 8,
+// lo of batch row t*8 + m - 8 above), bf16; each 128-byte row holds 8 chunks
+// of 16 bytes, chunk c of row r stored at c ^ (r & 7), so each group of 8 rows
+// an operand read touches covers all banks.
 template <int NT>
 __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
+    static_assert(NT >= 2, "the activation tile needs one load per wave");
     extern __shared__ __attribute__((aligned(16))) u16 smem[];
-    constexpr int NSTAGE = dma_stages<NT>();
+    constexpr int NSTAGE = DNSTAGE;
     constexpr int WST = DROWS * DKS;           // u16 of the weight tile
     constexpr int STG = WST + 16 * NT * DKS;   // u16 per stage
-    constexpr int NLD = 8 + NT;                // 16-byte loads per thread per stage
+    constexpr int NW = DROWS * DCH / 256;      // weight loads per thread per stage (4)
+    constexpr int NLD = NW + NT / 2;           // 16-byte loads per thread per stage
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int r = lane & 15, c = lane >> 4;
     const int B = p.B;
@@ -237,17 +240,21 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
     const int kbeg = blockIdx.y * p.kps;
     const int kend = min(p.K, kbeg + p.kps);
     const int nst = kbeg < kend ? (kend - kbeg) / DKS : 0;
+    // Rows whose pitch is a multiple of 8 KB, read at one column offset by
+    // every block at once, concentrate on few memory channels; a per-block
+    // start stage spreads the column offsets in flight.
+    const int rot = p.rot && nst > 0 ? (int)(blockIdx.x % nst) : 0;
 
     // load i of this thread fills stage chunk P = (i*4 + wv)*64 + lane (lane
     // L of a wave writes 16 bytes at the wave's base + 16 L): the weight tile
-    // for i < 8, the activation tile after; row P / 16, logical chunk
-    // (P % 16) ^ (row & 15)
+    // for i < NW, the activation tile after; row P / 8, logical chunk
+    // (P % 8) ^ (row & 7)
     const u16 *src[NLD];
 #pragma unroll
     for (int i = 0; i < NLD; i++) {
         const int P = (i * 4 + wv) * 64 + lane;
-        if (i < 8) {
-            const int row = P >> 4, lc = (P & 15) ^ (row & 15);
+        if (i < NW) {
+            const int row = P / DCH, lc = (P % DCH) ^ (row & (DCH - 1));
             int n = n0 + row;
             n = n < p.N ? n : p.N - 1;
             const u16 *wp = p.w[0];
@@ -256,8 +263,8 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
             if (p.nseg > 2 && n >= p.seg_end[1]) { wp = p.w[2]; start = p.seg_end[1]; }
             src[i] = wp + (size_t)(n - start) * p.K + kbeg + lc * 8;
         } else {
-            const int Q = P - 8 * 256;
-            const int col = Q >> 4, lc = (Q & 15) ^ (col & 15);
+            const int Q = P - NW * 256;
+            const int col = Q / DCH, lc = (Q % DCH) ^ (col & (DCH - 1));
             const int t = col >> 4, m = col & 15;
             int b = t * 8 + (m & 7);
             b = b < B ? b : B - 1;   // columns past B read a valid row; their outputs are not stored
@@ -267,7 +274,9 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
     // every iteration issues its loads (the last stage again past the end), so
     // the count of outstanding loads is the same everywhere
     auto load_stage = [&](int g, int stage) {
-        const int k0 = (g < nst ? g : nst - 1) * DKS;
+        int gg = (g < nst ? g : nst - 1) + rot;
+        gg = gg >= nst ? gg - nst : gg;
+        const int k0 = gg * DKS;
 #pragma unroll
         for (int i = 0; i < NLD; i++) {
             LDS_AS u16 *dst = (LDS_AS u16 *)smem + stage * STG + (i * 4 + wv) * 512;
@@ -287,6 +296,7 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
         // (__syncthreads would also wait for the newest stages).  s_waitcnt
         // fields: vmcnt (bits 3:0 and 15:14), expcnt 7, lgkmcnt 0.
         constexpr int WAITN = NLD * (NSTAGE - 2);
+        static_assert(WAITN < 64, "vmcnt field");
         constexpr int WAIT = (WAITN & 15) | (7 << 4) | (0 << 8) | ((WAITN >> 4) << 14);
 #pragma unroll
         for (int g = 0; g < NSTAGE - 1; g++) load_stage(g, g);
@@ -305,13 +315,13 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
 #pragma unroll
                 for (int rt = 0; rt < 2; rt++) {
                     const int row = wv * 32 + rt * 16 + r;
-                    wf[rt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sw + row * DKS + 8 * (lc ^ (row & 15))));
+                    wf[rt] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sw + row * DKS + 8 * (lc ^ (row & (DCH - 1)))));
                 }
 #pragma unroll
                 for (int t = 0; t < NT; t++) {
                     const int col = t * 16 + r;
                     const bf16x8 bf = __builtin_bit_cast(
-                        bf16x8, *reinterpret_cast<const u32x4 *>(sa + col * DKS + 8 * (lc ^ (col & 15))));
+                        bf16x8, *reinterpret_cast<const u32x4 *>(sa + col * DKS + 8 * (lc ^ (col & (DCH - 1)))));
 #pragma unroll
                     for (int rt = 0; rt < 2; rt++)
                         acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[rt], bf, acc[rt][t], 0, 0, 0);
@@ -379,19 +389,25 @@ int num_cus() {
     return n;
 }
 
-int gemv_max_splits(int K) {
-    if (K % 128 == 0) return K / 128 > 0 ? K / 128 : 1;
-    return K / 256 > 0 ? K / 256 : 1;
+int gemv_max_splits(int N, int K) {
+    if (K % DKS != 0) return gemv_grouped_max_splits(K);
+    // one block per CU on up to 256 CUs
+    const int tiles = (N + DROWS - 1) / DROWS;
+    int s = 256 / tiles;
+    if (s > K / DKS) s = K / DKS;
+    return s < 1 ? 1 : s;
 }
 
+int gemv_grouped_max_splits(int K) { return K / 256 > 0 ? K / 256 : 1; }
+
 // The split rule of the register-staged kernel (MoE grouped projections, and K
-// not a multiple of 128): about 1024 blocks of 4 waves, splits of 256+ k.
+// not a multiple of 64): about 1024 blocks of 4 waves, splits of 256+ k.
 int gemv_grouped_splits(int N, int K, int B) {
     (void)B;
     const int tiles = (N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
     const int target = 1024;  // ~4 blocks per CU on 256 CUs
     int s = (target + tiles - 1) / tiles;
-    const int maxs = K / 256 > 0 ? K / 256 : 1;
+    const int maxs = gemv_grouped_max_splits(K);
     if (s > maxs) s = maxs;
     if (s < 1) s = 1;
     const int g = 32 * pick_j(K);
@@ -405,7 +421,7 @@ int gemv_splits(int N, int K, int B) {
     // one block per CU, a single round: splits = CUs / row tiles
     const int tiles = (N + DROWS - 1) / DROWS;
     int s = num_cus() / tiles;
-    const int maxs = K / DKS;
+    const int maxs = gemv_max_splits(N, K);
     if (s > maxs) s = maxs;
     if (s < 1) s = 1;
     int kps = (K + s - 1) / s;
@@ -438,10 +454,11 @@ void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
         int kps = (K + ksplit - 1) / ksplit;
         kps = (kps + DKS - 1) / DKS * DKS;
         p.kps = kps;
+        // a row pitch that is a multiple of 8 KB with few split offsets: rotate
+        p.rot = (K % 4096 == 0 && ksplit < 8) ? 1 : 0;
         const dim3 grid((p.N + DROWS - 1) / DROWS, ksplit, 1);
-        const int NT = (B + 7) / 8;
-        const bool done = NT <= 1 ? launch_dma_nt<1>(st, p, grid)
-                          : NT <= 2 ? launch_dma_nt<2>(st, p, grid)
+        const int NT = (B + 7) / 8;   // B <= 16 shares the two-tile kernel
+        const bool done = NT <= 2 ? launch_dma_nt<2>(st, p, grid)
                           : NT <= 4 ? launch_dma_nt<4>(st, p, grid)
                                     : launch_dma_nt<8>(st, p, grid);
         if (done) return;

@@ -64,7 +64,9 @@ void launch_argmax(hipStream_t st, const float *logits, int B, int V, int32_t *o
 // W[n][k] * (a_hi[b][k] + a_lo[b][k]); 1 <= B <= 64.  Returns the split count used.
 int gemv_splits(int N, int K, int B);
 int gemv_grouped_splits(int N, int K, int B);   // the split count for launch_gemv_grouped
-int gemv_max_splits(int K);   // upper bound of both (host-only, for the workspace plan)
+// upper bounds of gemv_splits and gemv_grouped_splits (host-only, for the workspace plan)
+int gemv_max_splits(int N, int K);
+int gemv_grouped_max_splits(int K);
 int num_cus();
 void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi, const u16 *a_lo,
                  int lda, int B, float *out, int ksplit, size_t split_stride, int ldo);
