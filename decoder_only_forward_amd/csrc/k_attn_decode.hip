@@ -374,8 +374,10 @@ const void *decode_probe_fn(int hd) {
 }  // namespace
 
 int attn_decode_splits(int B, int nkv, int readable, int hd, int G, int kv_bf16) {
-    // fill the resident-block slots once (a second partial round would leave
-    // the memory system idle), with at least 128 positions per split
+    // One round of blocks.  An fp32 cache is streamed at the memory's rate by
+    // one block per CU, and each extra split costs the merge pass; with a bf16
+    // cache the lanes' arithmetic is the limit, so every resident-block slot is
+    // filled.  At least 128 positions per split.
     static int occ_cache[2][3] = {{0, 0, 0}, {0, 0, 0}};
     const int which = hd == 128 ? 0 : hd == 64 ? 1 : 2;
     int &occ_c = occ_cache[kv_bf16 ? 1 : 0][which];
@@ -386,9 +388,9 @@ int attn_decode_splits(int B, int nkv, int readable, int hd, int G, int kv_bf16)
         occ_c = occ;
     }
     (void)G;
-    const int slots = occ_c * num_cus();
+    const int slots = (kv_bf16 ? occ_c : 1) * num_cus();
     int s = slots / (B * nkv);
-    const int maxs = (readable + 127) / 128;
+    const int maxs = readable / 128;
     if (s > maxs) s = maxs;
     if (s > 64) s = 64;
     if (s < 1) s = 1;
