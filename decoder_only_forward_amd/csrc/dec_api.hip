@@ -143,10 +143,12 @@ bool plan(const dec_config &c, Plan &p) {
     const bool ring = c.sliding_window > 0 && c.max_seq == c.sliding_window;
     p.ck = take(ring ? (size_t)c.max_prefill * kvd * es : 0);
     p.cv = take(ring ? (size_t)c.max_prefill * kvd * es : 0);
-    // silu(gate) * up of a prefill's dense FFN, written by the fused gate|up GEMM
-    const bool fuse_silu = !E && c.weight_dtype != DEC_WEIGHT_F32 && c.max_prefill > 64;
-    p.s_hi = take(fuse_silu ? (size_t)c.max_prefill * F * 2 : 0);
-    p.s_lo = take(fuse_silu ? (size_t)c.max_prefill * F * 2 : 0);
+    // silu(gate) * up of the dense FFN, written by the fused gate|up GEMM
+    // (prefill rows) or GEMV (up to 64 rows)
+    const bool fuse_silu = !E && c.weight_dtype != DEC_WEIGHT_F32;
+    const size_t s_rows = fuse_silu ? std::max<size_t>(c.max_prefill, std::min(rows, 64)) : 0;
+    p.s_hi = take(s_rows * F * 2);
+    p.s_lo = take(s_rows * F * 2);
     // prefill attention's K/V tile images (positions [0, max_seq) of one sequence)
     p.kvimg = take(c.weight_dtype == DEC_WEIGHT_F32 ? 0
                    : attn_tiles_bytes(c.max_seq, c.n_kv_heads, c.head_dim, c.kv_dtype == DEC_KV_BF16));
@@ -415,6 +417,12 @@ void run_pass(dec_model *m, const Pass &ps) {
             if (!f32w && T > 64 && m->s_hi) {
                 Tick tk(m, DEC_K_GEMM);
                 fused = launch_gemm_silu(st, w.w_gate, w.w_up, F, d, ah, al, d, T, m->s_hi, m->s_lo, F);
+                if (fused) tk.done(2.0 * F * d * 2 + (double)T * d * 4 + (double)T * F * 4, 2.0 * T * 2 * F * d);
+                else tk.cancel();
+            } else if (!f32w && T <= 64 && m->s_hi && gemv_splits(2 * F, d, T) == 1) {
+                // the unfused projection would take one k split too: fuse the activation
+                Tick tk(m, DEC_K_GEMV);
+                fused = launch_gemv_silu(st, w.w_gate, w.w_up, F, d, ah, al, d, T, m->s_hi, m->s_lo, F);
                 if (fused) tk.done(2.0 * F * d * 2 + (double)T * d * 4 + (double)T * F * 4, 2.0 * T * 2 * F * d);
                 else tk.cancel();
             }

@@ -41,6 +41,9 @@ struct GemvParams {
     const int32_t *grp_off;
     size_t expert_stride;
     int rot;   // LDS-ring kernel: start each block's k walk at stage blockIdx.x % stages
+    // LDS-ring kernel with silu(gate) * up in its epilogue: w[0] gate, w[1] up,
+    // N features; the product goes to (s_hi, s_lo) [B][ldo] as bf16 pairs
+    u16 *s_hi, *s_lo;
 };
 
 constexpr int ROWS_PER_BLOCK = 128;
@@ -224,7 +227,12 @@ constexpr size_t dma_lds() { return (size_t)DNSTAGE * (DROWS * DKS + 16 * NT * D
 // lo of batch row t*8 + m - 8 above), bf16; each 128-byte row holds 8 chunks
 // of 16 bytes, chunk c of row r stored at c ^ (r & 7), so each group of 8 rows
 // an operand read touches covers all banks.
-template <int NT>
+//
+// SILU: the block's 128 rows are 64 features of the gate matrix and the same 64
+// of the up matrix, interleaved by 16 so that each wave's two row tiles hold
+// gate and up of the same 16 features; the epilogue writes silu(gate) * up
+// (single k split only).
+template <int NT, bool SILU>
 __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
     static_assert(NT >= 2, "the activation tile needs one load per wave");
     extern __shared__ __attribute__((aligned(16))) u16 smem[];
@@ -236,7 +244,7 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int r = lane & 15, c = lane >> 4;
     const int B = p.B;
-    const int n0 = blockIdx.x * DROWS;
+    const int n0 = blockIdx.x * (SILU ? DROWS / 2 : DROWS);
     const int kbeg = blockIdx.y * p.kps;
     const int kend = min(p.K, kbeg + p.kps);
     const int nst = kbeg < kend ? (kend - kbeg) / DKS : 0;
@@ -255,13 +263,19 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
         const int P = (i * 4 + wv) * 64 + lane;
         if (i < NW) {
             const int row = P / DCH, lc = (P % DCH) ^ (row & (DCH - 1));
-            int n = n0 + row;
-            n = n < p.N ? n : p.N - 1;
-            const u16 *wp = p.w[0];
-            int start = 0;
-            if (p.nseg > 1 && n >= p.seg_end[0]) { wp = p.w[1]; start = p.seg_end[0]; }
-            if (p.nseg > 2 && n >= p.seg_end[1]) { wp = p.w[2]; start = p.seg_end[1]; }
-            src[i] = wp + (size_t)(n - start) * p.K + kbeg + lc * 8;
+            if constexpr (SILU) {
+                int f = n0 + (row >> 5) * 16 + (row & 15);
+                f = f < p.N ? f : p.N - 1;
+                src[i] = (((row >> 4) & 1) ? p.w[1] : p.w[0]) + (size_t)f * p.K + kbeg + lc * 8;
+            } else {
+                int n = n0 + row;
+                n = n < p.N ? n : p.N - 1;
+                const u16 *wp = p.w[0];
+                int start = 0;
+                if (p.nseg > 1 && n >= p.seg_end[0]) { wp = p.w[1]; start = p.seg_end[0]; }
+                if (p.nseg > 2 && n >= p.seg_end[1]) { wp = p.w[2]; start = p.seg_end[1]; }
+                src[i] = wp + (size_t)(n - start) * p.K + kbeg + lc * 8;
+            }
         } else {
             const int Q = P - NW * 256;
             const int col = Q / DCH, lc = (Q % DCH) ^ (col & (DCH - 1));
@@ -337,42 +351,64 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
 
     // lane (r, c) holds rows 4c..4c+3 of each row tile for column r; column r
     // (hi) and r+8 (lo) of the same batch row are summed.
-    float *out = p.out + (size_t)blockIdx.y * p.split_stride;
+    floatx4 sum[2][NT];
 #pragma unroll
-    for (int t = 0; t < NT; t++) {
+    for (int t = 0; t < NT; t++)
 #pragma unroll
-        for (int rt = 0; rt < 2; rt++) {
-            floatx4 v = acc[rt][t];
-            floatx4 o;
-            o[0] = __shfl_xor(v[0], 8, WAVE);
-            o[1] = __shfl_xor(v[1], 8, WAVE);
-            o[2] = __shfl_xor(v[2], 8, WAVE);
-            o[3] = __shfl_xor(v[3], 8, WAVE);
+        for (int rt = 0; rt < 2; rt++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) sum[rt][t][j] = acc[rt][t][j] + __shfl_xor(acc[rt][t][j], 8, WAVE);
+    if constexpr (SILU) {
+        // silu(z) = z / (1 + e^-z), as the separate activation kernel forms it
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
             const int b = t * 8 + (r & 7);
-            if (r < 8 && b < B) {
-                const int nn = n0 + wv * 32 + rt * 16 + 4 * c;
-                float *dst = out + (size_t)b * p.ldo + nn;
-                const float4 sv = make_float4(v[0] + o[0], v[1] + o[1], v[2] + o[2], v[3] + o[3]);
-                if (nn + 3 < p.N) {
-                    *reinterpret_cast<float4 *>(dst) = sv;
-                } else {
-                    if (nn < p.N) dst[0] = sv.x;
-                    if (nn + 1 < p.N) dst[1] = sv.y;
-                    if (nn + 2 < p.N) dst[2] = sv.z;
+            const int f = n0 + wv * 16 + 4 * c;
+            if (r < 8 && b < B && f + 3 < p.N) {
+                uint32_t h[4], l[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const float g = sum[0][t][j], u = sum[1][t][j];
+                    split_bf16(g / (1.0f + expf(-g)) * u, h[j], l[j]);
+                }
+                const size_t o = (size_t)b * p.ldo + f;
+                *reinterpret_cast<uint2 *>(p.s_hi + o) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                *reinterpret_cast<uint2 *>(p.s_lo + o) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+            }
+        }
+    } else {
+        float *out = p.out + (size_t)blockIdx.y * p.split_stride;
+#pragma unroll
+        for (int t = 0; t < NT; t++) {
+#pragma unroll
+            for (int rt = 0; rt < 2; rt++) {
+                const floatx4 v = sum[rt][t];
+                const int b = t * 8 + (r & 7);
+                if (r < 8 && b < B) {
+                    const int nn = n0 + wv * 32 + rt * 16 + 4 * c;
+                    float *dst = out + (size_t)b * p.ldo + nn;
+                    const float4 sv = make_float4(v[0], v[1], v[2], v[3]);
+                    if (nn + 3 < p.N) {
+                        *reinterpret_cast<float4 *>(dst) = sv;
+                    } else {
+                        if (nn < p.N) dst[0] = sv.x;
+                        if (nn + 1 < p.N) dst[1] = sv.y;
+                        if (nn + 2 < p.N) dst[2] = sv.z;
+                    }
                 }
             }
         }
     }
 }
 
-template <int NT>
+template <int NT, bool SILU>
 bool launch_dma_nt(hipStream_t st, const GemvParams &p, dim3 grid) {
     static int ok = -1;
     if (ok < 0)
-        ok = hipFuncSetAttribute((const void *)gemv_dma_kernel<NT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        ok = hipFuncSetAttribute((const void *)gemv_dma_kernel<NT, SILU>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                  (int)dma_lds<NT>()) == hipSuccess;
     if (ok != 1) return false;
-    hipLaunchKernelGGL((gemv_dma_kernel<NT>), grid, dim3(256), dma_lds<NT>(), st, p);
+    hipLaunchKernelGGL((gemv_dma_kernel<NT, SILU>), grid, dim3(256), dma_lds<NT>(), st, p);
     return true;
 }
 
@@ -458,12 +494,37 @@ void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
         p.rot = (K % 4096 == 0 && ksplit < 8) ? 1 : 0;
         const dim3 grid((p.N + DROWS - 1) / DROWS, ksplit, 1);
         const int NT = (B + 7) / 8;   // B <= 16 shares the two-tile kernel
-        const bool done = NT <= 2 ? launch_dma_nt<2>(st, p, grid)
-                          : NT <= 4 ? launch_dma_nt<4>(st, p, grid)
-                                    : launch_dma_nt<8>(st, p, grid);
+        const bool done = NT <= 2 ? launch_dma_nt<2, false>(st, p, grid)
+                          : NT <= 4 ? launch_dma_nt<4, false>(st, p, grid)
+                                    : launch_dma_nt<8, false>(st, p, grid);
         if (done) return;
     }
     launch_common(st, p, ksplit, B, 1);
+}
+
+bool launch_gemv_silu(hipStream_t st, const void *w_gate, const void *w_up, int F, int K, const u16 *a_hi,
+                      const u16 *a_lo, int lda, int B, u16 *s_hi, u16 *s_lo, int ldo) {
+    if (B <= 0 || B > 64 || K % DKS != 0 || F % (DROWS / 2) != 0) return false;
+    GemvParams p{};
+    p.w[0] = (const u16 *)w_gate;
+    p.w[1] = (const u16 *)w_up;
+    p.nseg = 2;
+    p.N = F;
+    p.K = K;
+    p.a_hi = a_hi;
+    p.a_lo = a_lo;
+    p.lda = lda;
+    p.B = B;
+    p.ldo = ldo;
+    p.kps = K;
+    p.rot = K % 4096 == 0 ? 1 : 0;
+    p.s_hi = s_hi;
+    p.s_lo = s_lo;
+    const dim3 grid(F / (DROWS / 2), 1, 1);
+    const int NT = (B + 7) / 8;
+    return NT <= 2 ? launch_dma_nt<2, true>(st, p, grid)
+         : NT <= 4 ? launch_dma_nt<4, true>(st, p, grid)
+                   : launch_dma_nt<8, true>(st, p, grid);
 }
 
 // Grouped-expert form used by the MoE decode path (see k_moe.hip).

@@ -62,3 +62,37 @@ def test_tile_attention_appends_ragged_chunks(base, kv_bf16):
     pair = Pair(cfg, max_prefill=100)
     toks = synth.tokens(0, synth.PROMPT_STREAM, 250, cfg.vocab).tolist()
     _chunks(pair, toks, [100, 93, 57], cfg.name)
+
+
+def test_fused_swiglu_decode_projection_at_prefill_and_decode_rows():
+    """gate|up of 2 x 14400 features is 225 row tiles, so the decode projection
+    takes one k split and writes silu(gate) * up from its epilogue: a 40-token
+    prefill (40 rows, the 8-tile kernel) into each of 3 slots, then 2 decode
+    steps at B = 3 (the 2-tile kernel with spare columns), every row's hidden
+    state after the layer and the logits against the oracle."""
+    B, P = 3, 40
+    pair = Pair(ODD, n_slots=B, max_prefill=P)
+    c, tl = ODD, pair.tol
+    prompts = synth.prompts(c, B, P)
+    for b in range(B):
+        hid, _, _ = pair.capture_buffers(P)
+        g = pair.gpu.prefill(prompts[b].tolist(), seq=b).cpu().numpy()
+        r = pair.ora.prefill(prompts[b].tolist(), slot=b, capture=True)
+        torch.cuda.synchronize()
+        h = hid.cpu().numpy()
+        for t in range(P):
+            rl = rel_l2(h[1, t], r["hidden"][1, t])
+            assert rl <= HIDDEN_REL_L2, f"prefill slot {b}: row {t} hidden rel L2 {rl:.3e}"
+        check_logits(g, r["logits"][0], f"prefill slot {b}", **tl)
+    teach = synth.prompts(c, B, 2, stream=synth.TEACHER_STREAM)
+    for s in range(2):
+        hid, _, _ = pair.capture_buffers(B)
+        lg = pair.gpu.decode(teach[:, s].tolist(), [P + s] * B).cpu().numpy()
+        r = pair.ora.decode(teach[:, s].tolist(), [P + s] * B, capture=True)
+        torch.cuda.synchronize()
+        h = hid.cpu().numpy()
+        for b in range(B):
+            rl = rel_l2(h[1, b], r["hidden"][1, b])
+            assert rl <= HIDDEN_REL_L2, f"decode step {s} row {b}: hidden rel L2 {rl:.3e}"
+            check_logits(lg[b], r["logits"][b], f"decode step {s} row {b}", **tl)
+            check_argmax(lg[b], r["logits"][b], f"decode step {s} row {b}", **tl)
