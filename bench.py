@@ -35,22 +35,22 @@ HBM_PEAK_GBS = 8000.0
 _COMMON = {"decoder_only_forward_amd/csrc/common.h":
            "4c1abc6ecd4c94ab3996e24a5cb4f31b82f3cc871264bbeaa118f84a57e98843"}
 _ATTN_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_decode.hip":
-                                 "260c81848d3ab8f870ab8f2345932ae86d051d16c909d38970cfd18605cb752e"})
+                                 "c2f5c9d72da35645a599ebcb8442ac997bcd6b0e8a23d7d744ac74e8f8e304f8"})
 _GEMV_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemv.hip":
-                                 "d29a93bb8b472cfcd3ebfedd21c7e24006c422acc9b49340e77beb3e291ff0dc"})
+                                 "ca9db334d689a3f9e6e4f9feeee324a2e27cda46915fd554ac490e770628809b"})
 _GEMM_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemm.hip":
                                  "bad153d55eb07af7b12ec5c221f25e2fe649cdb1f0dc78776ee10d178ba04e34"})
 MEASURED_TRAFFIC = {
     ("attn_decode_kernel", "fp32"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 1076058487},
+                                     "bytes_per_launch": 1074938114},
     ("attn_decode_kernel", "bf16"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 539258404},
+                                     "bytes_per_launch": 539258490},
     ("gemv_decode", "fp32"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                              "bytes_per_launch": 121232331},
+                              "bytes_per_launch": 121573472},
     ("gemv_decode", "bf16"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                              "bytes_per_launch": 121232331},
+                              "bytes_per_launch": 121573472},
     ("gemm_prefill", "fp32"): {"sources": _GEMM_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                               "bytes_per_launch": 1661499703},
+                               "bytes_per_launch": 1658793148},
 }
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode tok/s + prefill tok/s (Mistral-7B shape) and % of HBM / MFMA roofline"
