@@ -427,10 +427,13 @@ int num_cus() {
 
 int gemv_max_splits(int N, int K) {
     if (K % DKS != 0) return gemv_grouped_max_splits(K);
-    // one block per CU on up to 256 CUs
+    // one block per CU on up to 256 CUs; a matrix of a few rows (the MoE
+    // router) gains little from more blocks while its consumer sums S
+    // partials per output, so at most 2N splits
     const int tiles = (N + DROWS - 1) / DROWS;
     int s = 256 / tiles;
     if (s > K / DKS) s = K / DKS;
+    if (s > 2 * N) s = 2 * N;
     return s < 1 ? 1 : s;
 }
 

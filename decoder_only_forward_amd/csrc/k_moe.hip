@@ -23,16 +23,26 @@ __global__ void __launch_bounds__(NT) moe_route_kernel(int T, int E, int k, Part
     __shared__ int cnt[NT][MAXE];
     __shared__ int off[MAXE + 1];
     const int tid = threadIdx.x;
-    // 1. per token: softmax, top-k, renormalise
-    for (int t = tid; t < T; t += NT) {
-        float p[MAXE];
-        float mx = -INFINITY;
-        for (int e = 0; e < E; e++) {
-            const float v = sum_splits(lg.p, lg.S, lg.stride, (size_t)t * lg.ld + e);
-            p[e] = v;
-            if (rcap) rcap[(size_t)t * E + e] = v;
-            mx = fmaxf(mx, v);
+    // 1. per token: EP (E rounded up to a power of two) lanes per token, lane e
+    //    < E sums expert e's split partials, then the token's first lane forms
+    //    the softmax, the top-k and the renormalised weights
+    const int lane = tid % WAVE, wv = tid / WAVE;
+    int EP = 1;
+    while (EP < E) EP <<= 1;
+    const int tpw = WAVE / EP;   // tokens per wave per pass
+    for (int base = wv * tpw; base < T; base += (NT / WAVE) * tpw) {
+        const int t = base + lane / EP, e0 = lane % EP;
+        float v = -INFINITY;
+        if (t < T && e0 < E) {
+            v = sum_splits(lg.p, lg.S, lg.stride, (size_t)t * lg.ld + e0);
+            if (rcap) rcap[(size_t)t * E + e0] = v;
         }
+        float p[MAXE];
+#pragma unroll
+        for (int e = 0; e < MAXE; e++) p[e] = __shfl(v, (lane & ~(EP - 1)) + (e & (EP - 1)), WAVE);
+        if (e0 != 0 || t >= T) continue;
+        float mx = -INFINITY;
+        for (int e = 0; e < E; e++) mx = fmaxf(mx, p[e]);
         float z = 0.f;
         for (int e = 0; e < E; e++) { p[e] = expf(p[e] - mx); z += p[e]; }
         for (int e = 0; e < E; e++) p[e] = p[e] / z;
@@ -54,16 +64,19 @@ __global__ void __launch_bounds__(NT) moe_route_kernel(int T, int E, int k, Part
         }
     }
     __syncthreads();
-    // 2. stable counting sort of pair index t*k+j by expert
+    // 2. stable counting sort of pair index t*k+j by expert: thread i < nthr
+    //    counts a contiguous run of pairs, the per-expert scan walks the runs
+    //    in order (only as many runs as there are pairs, for short decode rows)
     const int n = T * k;
-    const int per = (n + NT - 1) / NT;
+    const int nthr = n < NT ? n : NT;
+    const int per = (n + nthr - 1) / nthr;
     const int lo = tid * per, hi = min(n, lo + per);
     for (int e = 0; e < E; e++) cnt[tid][e] = 0;
     for (int i = lo; i < hi; i++) cnt[tid][ids[i]]++;
     __syncthreads();
     if (tid < E) {
         int run = 0;
-        for (int i = 0; i < NT; i++) {
+        for (int i = 0; i < nthr; i++) {
             const int c = cnt[i][tid];
             cnt[i][tid] = run;
             run += c;
