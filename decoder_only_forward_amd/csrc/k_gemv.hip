@@ -243,7 +243,17 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
     constexpr int NLD = NW + NT / 2;           // 16-byte loads per thread per stage
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int r = lane & 15, c = lane >> 4;
-    const int B = p.B;
+    int B = p.B, arow0 = 0;
+    size_t wofs = 0;
+    if (!SILU && p.grp_off) {
+        // grouped experts: expert e = blockIdx.z owns activation (and output)
+        // rows [grp_off[e], grp_off[e+1]) and weight slice e
+        const int e = blockIdx.z;
+        arow0 = p.grp_off[e];
+        B = p.grp_off[e + 1] - arow0;
+        if (B <= 0) return;
+        wofs = (size_t)e * p.expert_stride;
+    }
     const int n0 = blockIdx.x * (SILU ? DROWS / 2 : DROWS);
     const int kbeg = blockIdx.y * p.kps;
     const int kend = min(p.K, kbeg + p.kps);
@@ -274,7 +284,7 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
                 int start = 0;
                 if (p.nseg > 1 && n >= p.seg_end[0]) { wp = p.w[1]; start = p.seg_end[0]; }
                 if (p.nseg > 2 && n >= p.seg_end[1]) { wp = p.w[2]; start = p.seg_end[1]; }
-                src[i] = wp + (size_t)(n - start) * p.K + kbeg + lc * 8;
+                src[i] = wp + wofs + (size_t)(n - start) * p.K + kbeg + lc * 8;
             }
         } else {
             const int Q = P - NW * 256;
@@ -282,7 +292,7 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
             const int t = col >> 4, m = col & 15;
             int b = t * 8 + (m & 7);
             b = b < B ? b : B - 1;   // columns past B read a valid row; their outputs are not stored
-            src[i] = (m < 8 ? p.a_hi : p.a_lo) + (size_t)b * p.lda + kbeg + lc * 8;
+            src[i] = (m < 8 ? p.a_hi : p.a_lo) + (size_t)(arow0 + b) * p.lda + kbeg + lc * 8;
         }
     }
     // every iteration issues its loads (the last stage again past the end), so
@@ -386,7 +396,7 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
                 const int b = t * 8 + (r & 7);
                 if (r < 8 && b < B) {
                     const int nn = n0 + wv * 32 + rt * 16 + 4 * c;
-                    float *dst = out + (size_t)b * p.ldo + nn;
+                    float *dst = out + (size_t)(arow0 + b) * p.ldo + nn;
                     const float4 sv = make_float4(v[0], v[1], v[2], v[3]);
                     if (nn + 3 < p.N) {
                         *reinterpret_cast<float4 *>(dst) = sv;
@@ -553,5 +563,18 @@ void launch_gemv_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, cons
     p.ldo = ldo;
     p.grp_off = offsets;
     p.expert_stride = expert_stride;
+    if (max_rows <= 0) return;
+    if (K % DKS == 0) {
+        int kps = (K + ksplit - 1) / ksplit;
+        kps = (kps + DKS - 1) / DKS * DKS;
+        p.kps = kps;
+        p.rot = (K % 4096 == 0 && ksplit < 8) ? 1 : 0;
+        const dim3 grid((p.N + DROWS - 1) / DROWS, ksplit, E);
+        const int NT = (max_rows + 7) / 8;
+        const bool done = NT <= 2 ? launch_dma_nt<2, false>(st, p, grid)
+                          : NT <= 4 ? launch_dma_nt<4, false>(st, p, grid)
+                                    : launch_dma_nt<8, false>(st, p, grid);
+        if (done) return;
+    }
     launch_common(st, p, ksplit, max_rows, E);
 }
