@@ -1,24 +1,20 @@
 // Decode projections: out[b][n] = sum_k W[n][k] * a[b][k] for B <= 64 rows.
 //
-// The weight matrix is read exactly once per step, straight from HBM into
-// registers with 16-byte loads, and is the A operand of bf16 MFMAs
-// (16x16x32).  Activations are fp32 in the forward; they enter the MFMA as the
-// pair (hi, lo) of bf16 values whose sum carries ~16 bits, as two columns of the
-// B operand, so the product keeps near-fp32 accuracy while the weights stay
-// exact.  The reduction order over k is free, so each lane loads a contiguous
-// run of 8*J bf16 per row and the B operand follows the same permutation.
+// The weight matrix is read exactly once per step from HBM and is the A operand
+// of bf16 MFMAs (16x16x32).  Activations are fp32 in the forward; they enter
+// the MFMA as the pair (hi, lo) of bf16 values whose sum carries ~16 bits, as
+// two columns of the B operand, so the product keeps near-fp32 accuracy while
+// the weights stay exact.
 //
-// Block = 4 waves, 128 weight rows (each wave 2 row tiles of 16); the B rows of
-// activations (hi and lo) for a chunk of k sit in LDS, shared by the 4 waves.
-// Grid = (row tiles, k splits[, experts]); split partials are summed by the
-// consumer kernel in a fixed order (no atomics).
-//
-// When K is a multiple of 128 the dense projections take gemv_dma_kernel
-// instead: each 128-k stage of the block's weight rows and of the activation
-// columns goes from global memory straight into a ring of LDS stages
-// (global_load_lds, no register staging), so the weight stream keeps several
-// stages in flight while earlier ones are multiplied, and one block per CU
-// with splits = CUs / row tiles covers the matrix in a single round.
+// Block = 4 waves, 128 weight rows (each wave 2 row tiles of 16).  Each 64-k
+// stage of the block's weight rows and of the activation columns goes from
+// global memory straight into a ring of LDS stages (global_load_lds, no
+// register staging), so the weight stream keeps stages in flight while earlier
+// ones are multiplied.  Grid = (row tiles, k splits[, experts]) with one block
+// per CU and splits = CUs / row tiles, so the matrix is covered in one round;
+// split partials are summed by the consumer kernel in a fixed order (no
+// atomics).  K must be a multiple of 64 (dec_create admits bf16 weights only
+// for such shapes).
 #include "common.h"
 #include "kernels.h"
 
@@ -34,184 +30,16 @@ struct GemvParams {
     float *out;
     size_t split_stride;
     int ldo;
-    int kps;   // k per split (multiple of 32*J)
-    int kc;    // k per LDS chunk (multiple of 32*J)
+    int kps;   // k per split (multiple of 64)
     // Grouped experts: expert e = blockIdx.z owns activation rows
     // [grp_off[e], grp_off[e+1]) and weight slice e (w + e*expert_stride).
     const int32_t *grp_off;
     size_t expert_stride;
-    int rot;   // LDS-ring kernel: start each block's k walk at stage blockIdx.x % stages
-    // LDS-ring kernel with silu(gate) * up in its epilogue: w[0] gate, w[1] up,
-    // N features; the product goes to (s_hi, s_lo) [B][ldo] as bf16 pairs
+    int rot;   // start each block's k walk at stage blockIdx.x % stages
+    // silu(gate) * up in the epilogue: w[0] gate, w[1] up, N features; the
+    // product goes to (s_hi, s_lo) [B][ldo] as bf16 pairs
     u16 *s_hi, *s_lo;
 };
-
-constexpr int ROWS_PER_BLOCK = 128;
-
-// 16 bytes (8 bf16) of a weight row.  (Non-temporal loads were measured slower
-// here: a row's 128-byte line is read in 32-byte pieces by several
-// instructions, and without L2 allocation it is fetched more than once.)
-__device__ __forceinline__ u32x4 load_w16(const u16 *p) { return *reinterpret_cast<const u32x4 *>(p); }
-
-template <int NT, int J>
-__global__ void __launch_bounds__(256) gemv_kernel(GemvParams p) {
-    extern __shared__ uint4 lds[];   // [kc/8][16*NT] chunks of 8 bf16
-    constexpr int NCOL = 16 * NT;
-    const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
-    const int r = lane & 15, c = lane >> 4;
-
-    int B = p.B, arow0 = 0, orow0 = 0;
-    size_t wofs = 0;
-    if (p.grp_off) {
-        const int e = blockIdx.z;
-        arow0 = p.grp_off[e];
-        B = p.grp_off[e + 1] - arow0;
-        if (B <= 0) return;
-        orow0 = arow0;
-        wofs = (size_t)e * p.expert_stride;
-    }
-
-    // weight rows of this lane (clamped; stores are masked)
-    const u16 *wrow[2];
-#pragma unroll
-    for (int rt = 0; rt < 2; rt++) {
-        const int n = blockIdx.x * ROWS_PER_BLOCK + wv * 32 + rt * 16 + r;
-        const int nn = n < p.N ? n : p.N - 1;
-        const u16 *wp = p.w[0];
-        int start = 0;
-        if (p.nseg > 1 && nn >= p.seg_end[0]) { wp = p.w[1]; start = p.seg_end[0]; }
-        if (p.nseg > 2 && nn >= p.seg_end[1]) { wp = p.w[2]; start = p.seg_end[1]; }
-        wrow[rt] = wp + wofs + (size_t)(nn - start) * p.K;
-    }
-
-    const int kbeg = blockIdx.y * p.kps;
-    const int kend = min(p.K, kbeg + p.kps);
-    floatx4 acc[2][NT];
-#pragma unroll
-    for (int rt = 0; rt < 2; rt++)
-#pragma unroll
-        for (int t = 0; t < NT; t++) acc[rt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-    if (kbeg < kend) {
-        const int nsteps = (kend - kbeg) / (32 * J);
-        u32x4 a[2][J], an[2][J];
-#pragma unroll
-        for (int rt = 0; rt < 2; rt++)
-#pragma unroll
-            for (int j = 0; j < J; j++) a[rt][j] = load_w16(wrow[rt] + kbeg + c * 8 * J + j * 8);
-
-        int chunk0 = kbeg;
-        for (int st = 0; st < nsteps; st++) {
-            const int k0 = kbeg + st * 32 * J;
-            if (((k0 - kbeg) % p.kc) == 0) {
-                chunk0 = k0;
-                const int kcl = min(p.kc, kend - k0);
-                const int c8 = kcl / 8;
-                __syncthreads();
-                for (int i = threadIdx.x; i < NCOL * c8; i += blockDim.x) {
-                    const int col = i / c8, ch = i % c8;
-                    const int t = col / 16, m = col % 16;
-                    const int b = t * 8 + (m & 7);
-                    uint4 v = make_uint4(0, 0, 0, 0);
-                    if (b < B) {
-                        const u16 *src = (m < 8 ? p.a_hi : p.a_lo) + (size_t)(arow0 + b) * p.lda + k0 + ch * 8;
-                        v = *reinterpret_cast<const uint4 *>(src);
-                    }
-                    lds[ch * NCOL + col] = v;
-                }
-                __syncthreads();
-            }
-            if (st + 1 < nsteps) {
-                const int kn = k0 + 32 * J;
-#pragma unroll
-                for (int rt = 0; rt < 2; rt++)
-#pragma unroll
-                    for (int j = 0; j < J; j++)
-                        an[rt][j] = load_w16(wrow[rt] + kn + c * 8 * J + j * 8);
-            }
-            const int ch0 = (k0 - chunk0) / 8 + c * J;
-#pragma unroll
-            for (int j = 0; j < J; j++) {
-#pragma unroll
-                for (int t = 0; t < NT; t++) {
-                    const uint4 bv = lds[(ch0 + j) * NCOL + t * 16 + r];
-                    const bf16x8 bop = __builtin_bit_cast(bf16x8, bv);
-#pragma unroll
-                    for (int rt = 0; rt < 2; rt++)
-                        acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, a[rt][j]), bop, acc[rt][t], 0, 0, 0);
-                }
-            }
-#pragma unroll
-            for (int rt = 0; rt < 2; rt++)
-#pragma unroll
-                for (int j = 0; j < J; j++) a[rt][j] = an[rt][j];
-        }
-    }
-
-    // lane (r, c) holds rows 4c..4c+3 of each row tile for column r; column r
-    // (hi) and r+8 (lo) of the same batch row are summed.
-    float *out = p.out + (size_t)blockIdx.y * p.split_stride;
-#pragma unroll
-    for (int t = 0; t < NT; t++) {
-#pragma unroll
-        for (int rt = 0; rt < 2; rt++) {
-            floatx4 v = acc[rt][t];
-            floatx4 o;
-            o[0] = __shfl_xor(v[0], 8, WAVE);
-            o[1] = __shfl_xor(v[1], 8, WAVE);
-            o[2] = __shfl_xor(v[2], 8, WAVE);
-            o[3] = __shfl_xor(v[3], 8, WAVE);
-            const int b = t * 8 + (r & 7);
-            if (r < 8 && b < B) {
-                const int n0 = blockIdx.x * ROWS_PER_BLOCK + wv * 32 + rt * 16 + 4 * c;
-                float *dst = out + (size_t)(orow0 + b) * p.ldo + n0;
-                const float4 s = make_float4(v[0] + o[0], v[1] + o[1], v[2] + o[2], v[3] + o[3]);
-                if (n0 + 3 < p.N) {
-                    *reinterpret_cast<float4 *>(dst) = s;
-                } else {
-                    if (n0 < p.N) dst[0] = s.x;
-                    if (n0 + 1 < p.N) dst[1] = s.y;
-                    if (n0 + 2 < p.N) dst[2] = s.z;
-                }
-            }
-        }
-    }
-}
-
-template <int NT>
-void launch_nt(hipStream_t st, int J, const GemvParams &p, dim3 grid) {
-    const size_t lds = (size_t)(p.kc / 8) * 16 * NT * sizeof(uint4);
-    if (J == 4) hipLaunchKernelGGL((gemv_kernel<NT, 4>), grid, dim3(256), lds, st, p);
-    else if (J == 2) hipLaunchKernelGGL((gemv_kernel<NT, 2>), grid, dim3(256), lds, st, p);
-    else hipLaunchKernelGGL((gemv_kernel<NT, 1>), grid, dim3(256), lds, st, p);
-}
-
-int pick_j(int K) { return K % 128 == 0 ? 4 : (K % 64 == 0 ? 2 : 1); }
-
-void launch_common(hipStream_t st, GemvParams &p, int ksplit, int B_for_tiles, int E) {
-    const int J = pick_j(p.K);
-    const int g = 32 * J;
-    // exactly `ksplit` splits (the consumer sums that many); kps*ksplit >= K and
-    // a trailing split whose range is empty writes zeros.
-    int kps = (p.K + ksplit - 1) / ksplit;
-    kps = (kps + g - 1) / g * g;
-    const int NT = (B_for_tiles + 7) / 8;
-    int kc = 1024 / (NT <= 1 ? 1 : NT <= 2 ? 2 : NT <= 4 ? 4 : 8);
-    kc = kc / g * g;
-    if (kc < g) kc = g;
-    p.kps = kps;
-    p.kc = kc;
-    dim3 grid((p.N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK, ksplit, E);
-    if (NT <= 1) launch_nt<1>(st, J, p, grid);
-    else if (NT <= 2) launch_nt<2>(st, J, p, grid);
-    else if (NT <= 4) launch_nt<4>(st, J, p, grid);
-    else launch_nt<8>(st, J, p, grid);
-}
-
-}  // namespace
-
-namespace {
 
 constexpr int DKS = 64;            // k per stage
 constexpr int DCH = DKS / 8;       // 16-byte chunks per stage row
@@ -412,14 +240,23 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
 }
 
 template <int NT, bool SILU>
-bool launch_dma_nt(hipStream_t st, const GemvParams &p, dim3 grid) {
-    static int ok = -1;
-    if (ok < 0)
-        ok = hipFuncSetAttribute((const void *)gemv_dma_kernel<NT, SILU>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)dma_lds<NT>()) == hipSuccess;
-    if (ok != 1) return false;
+void launch_dma_nt(hipStream_t st, const GemvParams &p, dim3 grid) {
+    // rings above 64 KB need the attribute; a failure shows as a launch error
+    static bool attr = false;
+    if (!attr) {
+        (void)hipFuncSetAttribute((const void *)gemv_dma_kernel<NT, SILU>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)dma_lds<NT>());
+        attr = true;
+    }
     hipLaunchKernelGGL((gemv_dma_kernel<NT, SILU>), grid, dim3(256), dma_lds<NT>(), st, p);
-    return true;
+}
+
+template <bool SILU>
+void launch_dma(hipStream_t st, const GemvParams &p, dim3 grid, int rows) {
+    const int NT = (rows + 7) / 8;   // up to 16 rows share the two-tile kernel
+    if (NT <= 2) launch_dma_nt<2, SILU>(st, p, grid);
+    else if (NT <= 4) launch_dma_nt<4, SILU>(st, p, grid);
+    else launch_dma_nt<8, SILU>(st, p, grid);
 }
 
 }  // namespace
@@ -436,7 +273,6 @@ int num_cus() {
 }
 
 int gemv_max_splits(int N, int K) {
-    if (K % DKS != 0) return gemv_grouped_max_splits(K);
     // one block per CU on up to 256 CUs; a matrix of a few rows (the MoE
     // router) gains little from more blocks while its consumer sums S
     // partials per output, so at most 2N splits
@@ -449,24 +285,24 @@ int gemv_max_splits(int N, int K) {
 
 int gemv_grouped_max_splits(int K) { return K / 256 > 0 ? K / 256 : 1; }
 
-// The split rule of the register-staged kernel (MoE grouped projections, and K
-// not a multiple of 64): about 1024 blocks of 4 waves, splits of 256+ k.
+// MoE grouped projections: which experts have rows is known only on the
+// device, so the grid covers all of them; about 1024 blocks over the row
+// tiles of the experts that can be active, splits of 256+ k.
 int gemv_grouped_splits(int N, int K, int B) {
     (void)B;
-    const int tiles = (N + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK;
-    const int target = 1024;  // ~4 blocks per CU on 256 CUs
+    const int tiles = (N + DROWS - 1) / DROWS;
+    const int target = 1024;
     int s = (target + tiles - 1) / tiles;
     const int maxs = gemv_grouped_max_splits(K);
     if (s > maxs) s = maxs;
     if (s < 1) s = 1;
-    const int g = 32 * pick_j(K);
     int kps = (K + s - 1) / s;
-    kps = (kps + g - 1) / g * g;
+    kps = (kps + DKS - 1) / DKS * DKS;
     return (K + kps - 1) / kps;
 }
 
 int gemv_splits(int N, int K, int B) {
-    if (K % DKS != 0) return gemv_grouped_splits(N, K, B);
+    (void)B;
     // one block per CU, a single round: splits = CUs / row tiles
     const int tiles = (N + DROWS - 1) / DROWS;
     int s = num_cus() / tiles;
@@ -499,20 +335,14 @@ void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
     p.ldo = ldo;
     p.grp_off = nullptr;
     if (B <= 0) return;
-    if (K % DKS == 0) {
-        int kps = (K + ksplit - 1) / ksplit;
-        kps = (kps + DKS - 1) / DKS * DKS;
-        p.kps = kps;
-        // a row pitch that is a multiple of 8 KB with few split offsets: rotate
-        p.rot = (K % 4096 == 0 && ksplit < 8) ? 1 : 0;
-        const dim3 grid((p.N + DROWS - 1) / DROWS, ksplit, 1);
-        const int NT = (B + 7) / 8;   // B <= 16 shares the two-tile kernel
-        const bool done = NT <= 2 ? launch_dma_nt<2, false>(st, p, grid)
-                          : NT <= 4 ? launch_dma_nt<4, false>(st, p, grid)
-                                    : launch_dma_nt<8, false>(st, p, grid);
-        if (done) return;
-    }
-    launch_common(st, p, ksplit, B, 1);
+    // exactly `ksplit` splits (the consumer sums that many); a trailing split
+    // whose range is empty writes zeros
+    int kps = (K + ksplit - 1) / ksplit;
+    kps = (kps + DKS - 1) / DKS * DKS;
+    p.kps = kps;
+    // a row pitch that is a multiple of 8 KB with few split offsets: rotate
+    p.rot = (K % 4096 == 0 && ksplit < 8) ? 1 : 0;
+    launch_dma<false>(st, p, dim3((p.N + DROWS - 1) / DROWS, ksplit, 1), B);
 }
 
 bool launch_gemv_silu(hipStream_t st, const void *w_gate, const void *w_up, int F, int K, const u16 *a_hi,
@@ -533,11 +363,8 @@ bool launch_gemv_silu(hipStream_t st, const void *w_gate, const void *w_up, int 
     p.rot = K % 4096 == 0 ? 1 : 0;
     p.s_hi = s_hi;
     p.s_lo = s_lo;
-    const dim3 grid(F / (DROWS / 2), 1, 1);
-    const int NT = (B + 7) / 8;
-    return NT <= 2 ? launch_dma_nt<2, true>(st, p, grid)
-         : NT <= 4 ? launch_dma_nt<4, true>(st, p, grid)
-                   : launch_dma_nt<8, true>(st, p, grid);
+    launch_dma<true>(st, p, dim3(F / (DROWS / 2), 1, 1), B);
+    return true;
 }
 
 // Grouped-expert form used by the MoE decode path (see k_moe.hip).
@@ -564,17 +391,9 @@ void launch_gemv_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, cons
     p.grp_off = offsets;
     p.expert_stride = expert_stride;
     if (max_rows <= 0) return;
-    if (K % DKS == 0) {
-        int kps = (K + ksplit - 1) / ksplit;
-        kps = (kps + DKS - 1) / DKS * DKS;
-        p.kps = kps;
-        p.rot = (K % 4096 == 0 && ksplit < 8) ? 1 : 0;
-        const dim3 grid((p.N + DROWS - 1) / DROWS, ksplit, E);
-        const int NT = (max_rows + 7) / 8;
-        const bool done = NT <= 2 ? launch_dma_nt<2, false>(st, p, grid)
-                          : NT <= 4 ? launch_dma_nt<4, false>(st, p, grid)
-                                    : launch_dma_nt<8, false>(st, p, grid);
-        if (done) return;
-    }
-    launch_common(st, p, ksplit, max_rows, E);
+    int kps = (K + ksplit - 1) / ksplit;
+    kps = (kps + DKS - 1) / DKS * DKS;
+    p.kps = kps;
+    p.rot = (K % 4096 == 0 && ksplit < 8) ? 1 : 0;
+    launch_dma<false>(st, p, dim3((p.N + DROWS - 1) / DROWS, ksplit, E), max_rows);
 }

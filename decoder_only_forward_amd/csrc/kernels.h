@@ -61,7 +61,8 @@ void launch_silu_mul(hipStream_t st, int T, int F, Partials gu, u16 *hi, u16 *lo
 void launch_argmax(hipStream_t st, const float *logits, int B, int V, int32_t *out);
 
 // Decode projection, bf16 weights: out[s][b][n] = sum over split s's K range of
-// W[n][k] * (a_hi[b][k] + a_lo[b][k]); 1 <= B <= 64.  Returns the split count used.
+// W[n][k] * (a_hi[b][k] + a_lo[b][k]); 1 <= B <= 64, K a multiple of 64.
+// gemv_splits gives the split count to launch with.
 int gemv_splits(int N, int K, int B);
 int gemv_grouped_splits(int N, int K, int B);   // the split count for launch_gemv_grouped
 // upper bounds of gemv_splits and gemv_grouped_splits (host-only, for the workspace plan)
