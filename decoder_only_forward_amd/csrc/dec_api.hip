@@ -110,7 +110,10 @@ bool plan(const dec_config &c, Plan &p) {
     // projection outputs: largest (splits x rows x N) over the projections
     size_t pf = 0;
     auto need = [&](int N, int K, int T) {
-        const int S = (T <= 64) ? proj_splits(c, N, K, T) : 1;
+        // GEMM rows: room for the k split a 256-CU device takes (a device with
+        // another count falls back to one split where the room is short)
+        const int S = (T <= 64) ? proj_splits(c, N, K, T)
+                                : (c.weight_dtype == DEC_WEIGHT_F32 ? 1 : gemm_splits_for(N, K, T, 256));
         pf = std::max(pf, (size_t)S * T * N);
     };
     for (int T : {c.max_batch, std::min(c.max_prefill, 64), c.max_prefill}) {
@@ -312,10 +315,13 @@ Partials proj(dec_model *m, const WSeg *segs, int nseg, int K, int T, const u16 
         tk.done((double)N * K * 2 + (double)T * K * 4 + (double)T * N * 4, 2.0 * T * N * K);
         return Partials{m->part, S, (size_t)T * N, N};
     }
+    // into the partial buffer, a grid with a half-empty last round is split over k
+    const size_t tn = (size_t)T * N;
+    const int S = (!out && 2 * tn <= m->pl.part_floats) ? gemm_splits(N, K, T) : 1;
     Tick tk(m, DEC_K_GEMM);
-    launch_gemm(m->st, segs, nseg, K, hi, lo, lda, T, dst, N);
+    launch_gemm(m->st, segs, nseg, K, hi, lo, lda, T, dst, N, S, tn);
     tk.done((double)N * K * 2 + (double)T * K * 4 + (double)T * N * 4, 2.0 * T * N * K);
-    return Partials{dst, 1, 0, N};
+    return Partials{dst, S, S > 1 ? tn : 0, N};
 }
 
 // Grouped expert projection over TP = T*k pair rows in expert order.

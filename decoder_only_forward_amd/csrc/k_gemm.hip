@@ -26,6 +26,10 @@ struct GemmParams {
     int ldo;
     const int32_t *grp_off;
     size_t expert_stride;
+    // direct-to-LDS kernel, split over k: block z covers k in
+    // [z*kchunk, (z+1)*kchunk) and writes out + z*split_stride
+    int kchunk;
+    size_t split_stride;
 };
 
 // Block tile: BN = 256 output features (weight rows) x BM = 128 tokens x BK = 64.
@@ -227,6 +231,8 @@ void fill(GemmParams &p, const WSeg *segs, int nseg, int K, const u16 *a_hi, con
     p.lda = lda;
     p.out = out;
     p.ldo = ldo;
+    p.kchunk = K;
+    p.split_stride = 0;
 }
 
 }  // namespace
@@ -293,6 +299,7 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
     const int m0 = tm * DBM;
     if (m0 >= M) return;
     const int n0 = tn * FPT;
+    const int kz0 = blockIdx.z * p.kchunk;   // 0 for SILU (one split)
 
     // load instruction i (0, 1) of an operand array: wave wv fills the 1 KB slot
     // i*8 + wv, lane L the 16-byte chunk slot*64 + L, i.e. row r = chunk / 4 and
@@ -307,7 +314,7 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
             const int t = (r & 127) >> 5;
             int f = n0 + (r >> 7) * 64 + (t & 1) * 32 + (r & 31);
             f = f < p.N ? f : p.N - 1;
-            src[i] = (t < 2 ? p.w[0] : p.w[1]) + (size_t)f * p.K + c * 8;
+            src[i] = (t < 2 ? p.w[0] : p.w[1]) + (size_t)f * p.K + kz0 + c * 8;
         } else {
             int n = n0 + r;
             n = n < p.N ? n : p.N - 1;
@@ -315,14 +322,14 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
             int start = 0;
             if (p.nseg > 1 && n >= p.seg_end[0]) { wp = p.w[1]; start = p.seg_end[0]; }
             if (p.nseg > 2 && n >= p.seg_end[1]) { wp = p.w[2]; start = p.seg_end[1]; }
-            src[i] = wp + (size_t)(n - start) * p.K + c * 8;
+            src[i] = wp + (size_t)(n - start) * p.K + kz0 + c * 8;
         }
         int m = m0 + r;
         m = m < M ? m : M - 1;
-        src[2 + i] = p.a_hi + (size_t)m * p.lda + c * 8;
-        src[4 + i] = p.a_lo + (size_t)m * p.lda + c * 8;
+        src[2 + i] = p.a_hi + (size_t)m * p.lda + kz0 + c * 8;
+        src[4 + i] = p.a_lo + (size_t)m * p.lda + kz0 + c * 8;
     }
-    const int nk = p.K / DBK;
+    const int nk = min(p.kchunk, p.K - kz0) / DBK;
     // every iteration issues its loads (the last tile again past the end), so
     // the count of outstanding loads is the same everywhere
     auto load_tile = [&](int kt, int stage) {
@@ -434,7 +441,7 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
         for (int j = 0; j < 2; j++) {
             const int m = m0 + wm * 64 + j * 32 + r32;
             if (m >= M) continue;
-            float *dst = p.out + (size_t)m * p.ldo;
+            float *dst = p.out + blockIdx.z * p.split_stride + (size_t)m * p.ldo;
 #pragma unroll
             for (int g = 0; g < 4; g++) {
                 const int n = n0 + wn * 128 + i * 32 + g * 8 + c2 * 4;
@@ -462,8 +469,20 @@ bool dma_lds_attr() {
 
 }  // namespace
 
+int gemm_splits_for(int N, int K, int M, int cus) {
+    // grids of at least one 256 x 256 tile per CU take the direct-to-LDS
+    // kernel; one whose last round is at most half full (1.5 rounds of q+k+v
+    // at 4096 tokens) is split in two over k, which evens the rounds
+    const long nb = (long)((N + DBN - 1) / DBN) * ((M + DBM - 1) / DBM);
+    if (K % (2 * DBK) != 0 || nb < cus) return 1;
+    const long r1 = (nb + cus - 1) / cus, r2 = (2 * nb + cus - 1) / cus;
+    return r2 < 2 * r1 ? 2 : 1;
+}
+
+int gemm_splits(int N, int K, int M) { return gemm_splits_for(N, K, M, num_cus()); }
+
 void launch_gemm(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi, const u16 *a_lo,
-                 int lda, int M, float *out, int ldo) {
+                 int lda, int M, float *out, int ldo, int ksplit, size_t split_stride) {
     if (M <= 0) return;
     GemmParams p{};
     fill(p, segs, nseg, K, a_hi, a_lo, lda, M, out, ldo);
@@ -471,10 +490,17 @@ void launch_gemm(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
     // smaller ones keep more, smaller blocks
     const long big = (long)((p.N + DBN - 1) / DBN) * ((M + DBM - 1) / DBM);
     if (K % DBK == 0 && big >= num_cus() && dma_lds_attr()) {
-        hipLaunchKernelGGL(gemm_dma_kernel<false>, dim3((p.N + DBN - 1) / DBN, (M + DBM - 1) / DBM, 1), dim3(DNTHR),
-                           DMA_LDS, st, p, nullptr, nullptr);
+        if (ksplit == 2 && K % (2 * DBK) == 0) {
+            p.kchunk = K / 2;
+            p.split_stride = split_stride;
+        } else {
+            ksplit = 1;
+        }
+        hipLaunchKernelGGL(gemm_dma_kernel<false>, dim3((p.N + DBN - 1) / DBN, (M + DBM - 1) / DBM, ksplit),
+                           dim3(DNTHR), DMA_LDS, st, p, nullptr, nullptr);
         return;
     }
+    // (one split: the caller asked for two only where gemm_splits gave two)
     dim3 grid((p.N + BN - 1) / BN, (M + BM - 1) / BM, 1);
     gemm_lds_attr();
     hipLaunchKernelGGL(gemm_kernel, grid, dim3(NTHR), GEMM_LDS, st, p);
