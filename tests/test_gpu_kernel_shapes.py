@@ -96,3 +96,17 @@ def test_fused_swiglu_decode_projection_at_prefill_and_decode_rows():
             assert rl <= HIDDEN_REL_L2, f"decode step {s} row {b}: hidden rel L2 {rl:.3e}"
             check_logits(lg[b], r["logits"][b], f"decode step {s} row {b}", **tl)
             check_argmax(lg[b], r["logits"][b], f"decode step {s} row {b}", **tl)
+
+
+WIDE_Q = configs.ModelConfig("wide-q-1l", n_layers=1, hidden=512, n_heads=32, n_kv_heads=8, head_dim=128,
+                             ffn_dim=1024, vocab=1000, max_seq=4096, rms_eps=1e-5, rope_theta=1e4)
+
+
+def test_gemm_two_way_k_split_with_a_token_tail():
+    """q|k|v of 6144 features over 2800 tokens is 24 x 11 = 264 tiles of 256 x 256:
+    a second round of 8 tiles, so the projection is split in two over k (528
+    blocks) and the RoPE/KV pass sums the two partials; the last token tile
+    holds 240 rows."""
+    pair = Pair(WIDE_Q, max_prefill=2800, max_seq=4096)
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 2800, WIDE_Q.vocab).tolist()
+    _chunks(pair, toks, [2800], "two-way k split")
