@@ -29,6 +29,17 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t &hi, uint32_t &lo) 
     lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
 }
 
+// The same split for two values at once, packed as the MFMA operands take
+// them (a in the low half, b in the high half): v_cvt_pk_bf16_f32 rounds to
+// nearest even, so the bits equal those of split_bf16.
+typedef __bf16 bf16x2_cvt __attribute__((ext_vector_type(2)));
+typedef float f32x2_cvt __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split2_bf16(float a, float b, uint32_t &hi, uint32_t &lo) {
+    hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_cvt){a, b}, bf16x2_cvt));
+    const float ah = __uint_as_float(hi << 16), bh = __uint_as_float(hi & 0xFFFF0000u);
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_cvt){a - ah, b - bh}, bf16x2_cvt));
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);

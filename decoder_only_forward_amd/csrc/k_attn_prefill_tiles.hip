@@ -262,14 +262,16 @@ __global__ void __launch_bounds__(NTHR, 1) attn_tiles_kernel(int T, int start_po
             const float mref = mnew == -INFINITY ? 0.f : mnew;
             const float corr = __builtin_amdgcn_exp2f(m - mref);
             float ps = 0.f;
-            uint32_t ph[2][16], plo[2][16];
+            uint32_t ph[2][8], plo[2][8];   // (hi, lo) bf16 pairs of weights e, e+1
 #pragma unroll
             for (int kt = 0; kt < 2; kt++)
 #pragma unroll
-                for (int e = 0; e < 16; e++) {
-                    const float pe = __builtin_amdgcn_exp2f(sc[kt][e] - mref);
-                    ps += pe;
-                    split_bf16(pe, ph[kt][e], plo[kt][e]);
+                for (int e = 0; e < 16; e += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(sc[kt][e] - mref);
+                    const float p1 = __builtin_amdgcn_exp2f(sc[kt][e + 1] - mref);
+                    ps += p0;
+                    ps += p1;
+                    split2_bf16(p0, p1, ph[kt][e / 2], plo[kt][e / 2]);
                 }
             ps += __shfl_xor(ps, 32, WAVE);
             l = l * corr + ps;
@@ -284,8 +286,9 @@ __global__ void __launch_bounds__(NTHR, 1) attn_tiles_kernel(int T, int start_po
             // values e = (ks%2)*8 + j of sub-tile ks/2, i.e. keys 16ks + (j/4)*8 + 4hh + j%4
 #pragma unroll
             for (int ks = 0; ks < 4; ks++) {
-                const bf16x8 bh = pack8(&ph[ks / 2][(ks % 2) * 8]);
-                const bf16x8 bl = pack8(&plo[ks / 2][(ks % 2) * 8]);
+                const uint32_t *hp = &ph[ks / 2][(ks % 2) * 4], *lp = &plo[ks / 2][(ks % 2) * 4];
+                const bf16x8 bh = __builtin_bit_cast(bf16x8, u32x4{hp[0], hp[1], hp[2], hp[3]});
+                const bf16x8 bl = __builtin_bit_cast(bf16x8, u32x4{lp[0], lp[1], lp[2], lp[3]});
 #pragma unroll
                 for (int d = 0; d < DT; d++) {
                     const int vrow = (d * 32 + ql) * I::VLD + 16 * ks + 4 * hh;
