@@ -15,9 +15,9 @@
 //     K/V element instead of once per (element, query block).
 //  2. attn_tiles_kernel: a block of 8 waves holds 256 query vectors ((row, head)
 //     pairs of one kv group) and walks the key tiles up to its last query.  The
-//     next tile's image is loaded into registers while the current one is
-//     multiplied, then stored into the other half of a double-buffered LDS
-//     area: one barrier per tile.  Per wave (32 query vectors):
+//     next tile's image goes from global memory straight into the other half of
+//     a double-buffered LDS area (direct-to-LDS loads) while the current one is
+//     multiplied: one barrier per tile.  Per wave (32 query vectors):
 //       S^T = K Q^T    (32x32x16 MFMAs; lane q+32h owns 32 scores of query q)
 //       O^T += V^T P^T (P straight from the S^T accumulator, keys relabelled
 //                       to match the accumulator layout, V^T rows read as
@@ -198,29 +198,25 @@ __global__ void __launch_bounds__(NTHR, 1) attn_tiles_kernel(int T, int start_po
     const int ntiles = last_pos / TK + 1;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(img + (size_t)kvh * ntiles_all * IMGU16);
 
-    // the next tile's image travels through registers in two halves (the
-    // first half is stored once the scores are formed, the second is loaded
-    // then), which bounds the registers held across the MFMA work
-    constexpr int C1 = (I::CHUNKS + 1) / 2;
-    u32x4 pre[C1];
-    auto fetch = [&](int j, int c0, int c1) {
+    // the next tile's image goes from global memory straight into the other
+    // LDS buffer (global_load_lds: lane L of a wave writes 16 bytes at the
+    // wave's base + 16 L, so chunk tid + c*NTHR lands at that chunk of the
+    // buffer); it is issued at the top of an iteration and waited for at the
+    // barrier that ends it
+    auto dma = [&](int j, int buf) {
 #pragma unroll
-        for (int c = c0; c < c1; c++) pre[c - c0] = src[(size_t)j * (IMGU16 / 8) + tid + c * NTHR];
+        for (int c = 0; c < I::CHUNKS; c++) {
+            __attribute__((address_space(3))) u16 *dst =
+                (__attribute__((address_space(3))) u16 *)lds + buf * IMGU16 + (size_t)(c * NTHR + wv * WAVE) * 8;
+            __builtin_amdgcn_global_load_lds((const void *)(src + (size_t)j * (IMGU16 / 8) + tid + c * NTHR),
+                                             (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+        }
     };
-    auto stash = [&](int buf, int c0, int c1) {
-        u32x4 *dst = reinterpret_cast<u32x4 *>(lds + buf * IMGU16);
-#pragma unroll
-        for (int c = c0; c < c1; c++) dst[tid + c * NTHR] = pre[c - c0];
-    };
-    fetch(0, 0, C1);
-    stash(0, 0, C1);
-    fetch(0, C1, I::CHUNKS);
-    stash(0, C1, I::CHUNKS);
+    dma(0, 0);
     __syncthreads();
 
     for (int j = 0; j < ntiles; j++) {
-        const int jn = j + 1 < ntiles ? j + 1 : j;
-        fetch(jn, 0, C1);
+        if (j + 1 < ntiles) dma(j + 1, (j + 1) & 1);
         const int kb = j * TK;
         if (kb <= wmax) {
             const u16 *sb = lds + (j & 1) * IMGU16;
@@ -280,8 +276,6 @@ __global__ void __launch_bounds__(NTHR, 1) attn_tiles_kernel(int T, int start_po
             for (int d = 0; d < DT; d++)
 #pragma unroll
                 for (int e = 0; e < 16; e++) o[d][e] *= corr;
-            if (j + 1 < ntiles) stash((j + 1) & 1, 0, C1);
-            fetch(jn, C1, I::CHUNKS);
             // O^T += V^T P^T over 4 k-steps of 16 keys; step ks uses the lane's
             // values e = (ks%2)*8 + j of sub-tile ks/2, i.e. keys 16ks + (j/4)*8 + 4hh + j%4
 #pragma unroll
@@ -305,13 +299,10 @@ __global__ void __launch_bounds__(NTHR, 1) attn_tiles_kernel(int T, int start_po
                     }
                 }
             }
-        } else {
-            if (j + 1 < ntiles) stash((j + 1) & 1, 0, C1);
-            fetch(jn, C1, I::CHUNKS);
         }
-        // the other buffer held tile j-1, which every wave finished before the
-        // previous barrier
-        if (j + 1 < ntiles) stash((j + 1) & 1, C1, I::CHUNKS);
+        // the other buffer, refilled above, held tile j-1, which every wave
+        // finished before the previous barrier; __syncthreads also waits for
+        // the direct-to-LDS loads
         __syncthreads();
     }
     if (!live) return;
