@@ -33,24 +33,24 @@ HBM_PEAK_GBS = 8000.0
 # to the ones profiled, and only for the profiled workload.  GEMV and GEMM
 # figures are the mean over the launches of one step's mix of projections.
 _COMMON = {"decoder_only_forward_amd/csrc/common.h":
-           "4c1abc6ecd4c94ab3996e24a5cb4f31b82f3cc871264bbeaa118f84a57e98843"}
+           "34608c55f95e88c4c9dc0713feb1c89be769be0a7ff3031fa8e6327276c4082b"}
 _ATTN_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_decode.hip":
                                  "c2f5c9d72da35645a599ebcb8442ac997bcd6b0e8a23d7d744ac74e8f8e304f8"})
 _GEMV_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemv.hip":
-                                 "ca9db334d689a3f9e6e4f9feeee324a2e27cda46915fd554ac490e770628809b"})
+                                 "42717548295ea5b1f828e3448fa2a67abc59e13a469e355d94e596bba6844e8e"})
 _GEMM_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemm.hip":
-                                 "bad153d55eb07af7b12ec5c221f25e2fe649cdb1f0dc78776ee10d178ba04e34"})
+                                 "2b5a11a5b66d407bcf10b64d4014b202650f0e067b23c57659c2175110e22eee"})
 MEASURED_TRAFFIC = {
     ("attn_decode_kernel", "fp32"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 1074938114},
+                                     "bytes_per_launch": 1074935628},
     ("attn_decode_kernel", "bf16"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 539258490},
+                                     "bytes_per_launch": 539257292},
     ("gemv_decode", "fp32"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                              "bytes_per_launch": 121573472},
+                              "bytes_per_launch": 121476548},
     ("gemv_decode", "bf16"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                              "bytes_per_launch": 121573472},
+                              "bytes_per_launch": 121476548},
     ("gemm_prefill", "fp32"): {"sources": _GEMM_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                               "bytes_per_launch": 1658793148},
+                               "bytes_per_launch": 1703703371},
 }
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode tok/s + prefill tok/s (Mistral-7B shape) and % of HBM / MFMA roofline"
