@@ -57,12 +57,16 @@ constexpr size_t dma_lds() { return (size_t)DNSTAGE * (DROWS * DKS + 16 * NT * D
 // of 16 bytes, chunk c of row r stored at c ^ (r & 7), so each group of 8 rows
 // an operand read touches covers all banks.
 //
-// SILU: the block's 128 rows are 64 features of the gate matrix and the same 64
-// of the up matrix, interleaved by 16 so that each wave's two row tiles hold
-// gate and up of the same 16 features; the epilogue writes silu(gate) * up
-// (single k split only).
-template <int NT, bool SILU>
+// FORM: DENSE, one matrix (up to three row segments); GROUPED, grid z is the
+// expert (MoE); SILU_FUSED, the block's 128 rows are 64 features of the gate
+// matrix and the same 64 of the up matrix, interleaved by 16 so that each
+// wave's two row tiles hold gate and up of the same 16 features, and the
+// epilogue writes silu(gate) * up (single k split only).
+enum { DENSE = 0, SILU_FUSED = 1, GROUPED = 2 };
+
+template <int NT, int FORM>
 __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
+    constexpr bool SILU = FORM == SILU_FUSED;
     static_assert(NT >= 2, "the activation tile needs one load per wave");
     extern __shared__ __attribute__((aligned(16))) u16 smem[];
     constexpr int NSTAGE = DNSTAGE;
@@ -74,7 +78,7 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
     const int r = lane & 15, c = lane >> 4;
     int B = p.B, arow0 = 0;
     size_t wofs = 0;
-    if (!SILU && p.grp_off) {
+    if constexpr (FORM == GROUPED) {
         // grouped experts: expert e = blockIdx.z owns activation (and output)
         // rows [grp_off[e], grp_off[e+1]) and weight slice e
         const int e = blockIdx.z;
@@ -248,24 +252,24 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
     }
 }
 
-template <int NT, bool SILU>
+template <int NT, int FORM>
 void launch_dma_nt(hipStream_t st, const GemvParams &p, dim3 grid) {
     // rings above 64 KB need the attribute; a failure shows as a launch error
     static bool attr = false;
     if (!attr) {
-        (void)hipFuncSetAttribute((const void *)gemv_dma_kernel<NT, SILU>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        (void)hipFuncSetAttribute((const void *)gemv_dma_kernel<NT, FORM>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                   (int)dma_lds<NT>());
         attr = true;
     }
-    hipLaunchKernelGGL((gemv_dma_kernel<NT, SILU>), grid, dim3(256), dma_lds<NT>(), st, p);
+    hipLaunchKernelGGL((gemv_dma_kernel<NT, FORM>), grid, dim3(256), dma_lds<NT>(), st, p);
 }
 
-template <bool SILU>
+template <int FORM>
 void launch_dma(hipStream_t st, const GemvParams &p, dim3 grid, int rows) {
     const int NT = (rows + 7) / 8;   // up to 16 rows share the two-tile kernel
-    if (NT <= 2) launch_dma_nt<2, SILU>(st, p, grid);
-    else if (NT <= 4) launch_dma_nt<4, SILU>(st, p, grid);
-    else launch_dma_nt<8, SILU>(st, p, grid);
+    if (NT <= 2) launch_dma_nt<2, FORM>(st, p, grid);
+    else if (NT <= 4) launch_dma_nt<4, FORM>(st, p, grid);
+    else launch_dma_nt<8, FORM>(st, p, grid);
 }
 
 }  // namespace
@@ -351,7 +355,7 @@ void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
     p.kps = kps;
     // a row pitch that is a multiple of 8 KB with few split offsets: rotate
     p.rot = (K % 4096 == 0 && ksplit < 8) ? 1 : 0;
-    launch_dma<false>(st, p, dim3((p.N + DROWS - 1) / DROWS, ksplit, 1), B);
+    launch_dma<DENSE>(st, p, dim3((p.N + DROWS - 1) / DROWS, ksplit, 1), B);
 }
 
 bool launch_gemv_silu(hipStream_t st, const void *w_gate, const void *w_up, int F, int K, const u16 *a_hi,
@@ -372,7 +376,7 @@ bool launch_gemv_silu(hipStream_t st, const void *w_gate, const void *w_up, int 
     p.rot = K % 4096 == 0 ? 1 : 0;
     p.s_hi = s_hi;
     p.s_lo = s_lo;
-    launch_dma<true>(st, p, dim3(F / (DROWS / 2), 1, 1), B);
+    launch_dma<SILU_FUSED>(st, p, dim3(F / (DROWS / 2), 1, 1), B);
     return true;
 }
 
@@ -404,5 +408,5 @@ void launch_gemv_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, cons
     kps = (kps + DKS - 1) / DKS * DKS;
     p.kps = kps;
     p.rot = (K % 4096 == 0 && ksplit < 8) ? 1 : 0;
-    launch_dma<false>(st, p, dim3((p.N + DROWS - 1) / DROWS, ksplit, E), max_rows);
+    launch_dma<GROUPED>(st, p, dim3((p.N + DROWS - 1) / DROWS, ksplit, E), max_rows);
 }
