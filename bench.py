@@ -37,20 +37,20 @@ _COMMON = {"decoder_only_forward_amd/csrc/common.h":
 _ATTN_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_decode.hip":
                                  "c2f5c9d72da35645a599ebcb8442ac997bcd6b0e8a23d7d744ac74e8f8e304f8"})
 _GEMV_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemv.hip":
-                                 "42717548295ea5b1f828e3448fa2a67abc59e13a469e355d94e596bba6844e8e"})
+                                 "5fe17c415267820e0c5c5c87e16293bd009e032ca630472f127e01eb345a4cae"})
 _GEMM_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemm.hip":
                                  "2b5a11a5b66d407bcf10b64d4014b202650f0e067b23c57659c2175110e22eee"})
 MEASURED_TRAFFIC = {
     ("attn_decode_kernel", "fp32"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 1074935628},
+                                     "bytes_per_launch": 1074937829},
     ("attn_decode_kernel", "bf16"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 539257292},
+                                     "bytes_per_launch": 539258340},
     ("gemv_decode", "fp32"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                              "bytes_per_launch": 121476548},
+                              "bytes_per_launch": 121772189},
     ("gemv_decode", "bf16"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                              "bytes_per_launch": 121476548},
+                              "bytes_per_launch": 121772189},
     ("gemm_prefill", "fp32"): {"sources": _GEMM_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                               "bytes_per_launch": 1703703371},
+                               "bytes_per_launch": 1697973483},
 }
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode tok/s + prefill tok/s (Mistral-7B shape) and % of HBM / MFMA roofline"
