@@ -85,14 +85,14 @@ void launch_gemm(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
 // epilogue, written as bf16 (hi, lo) pairs [M][ldo] (F features).  Taken only
 // when the grid has at least one 256 x 256 tile per CU; returns false (nothing
 // launched) otherwise.  s_hi/s_lo must not alias a_hi/a_lo.
+bool launch_gemm_silu(hipStream_t st, const void *w_gate, const void *w_up, int F, int K, const u16 *a_hi,
+                      const u16 *a_lo, int lda, int M, u16 *s_hi, u16 *s_lo, int ldo);
 // Decode form of the fused SwiGLU: gate and up of F features (bf16 [F, K]
 // each) against B <= 64 activation rows, one k split, silu(gate) * up written
 // as bf16 (hi, lo) pairs to s_hi/s_lo [B][ldo].  Returns false (nothing
 // launched) for shapes it does not take: K or F not a multiple of 64.
 bool launch_gemv_silu(hipStream_t st, const void *w_gate, const void *w_up, int F, int K, const u16 *a_hi,
                       const u16 *a_lo, int lda, int B, u16 *s_hi, u16 *s_lo, int ldo);
-bool launch_gemm_silu(hipStream_t st, const void *w_gate, const void *w_up, int F, int K, const u16 *a_hi,
-                      const u16 *a_lo, int lda, int M, u16 *s_hi, u16 *s_lo, int ldo);
 
 // fp32-weight projection (any M): out[m][n] = sum_k a[m][k] W[n][k].
 void launch_gemm_f32(hipStream_t st, const WSeg *segs, int nseg, int K, const float *a, int lda,
