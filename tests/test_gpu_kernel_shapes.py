@@ -15,7 +15,7 @@ import pytest
 import torch
 
 from decoder_only_forward_amd import configs, synth
-from parity_util import Pair, check_argmax, check_logits, rel_l2, tol, HIDDEN_REL_L2
+from parity_util import Pair, check_argmax, check_experts, check_hidden, check_logits, rel_l2, tol, HIDDEN_REL_L2
 
 pytestmark = pytest.mark.gpu
 
@@ -110,3 +110,47 @@ def test_gemm_two_way_k_split_with_a_token_tail():
     pair = Pair(WIDE_Q, max_prefill=2800, max_seq=4096)
     toks = synth.tokens(0, synth.PROMPT_STREAM, 2800, WIDE_Q.vocab).tolist()
     _chunks(pair, toks, [2800], "two-way k split")
+
+
+def test_grouped_expert_projections_at_every_row_tile_count():
+    """bf16 experts through the grouped LDS-ring GEMV with 1, 3 and 8 column
+    tiles of 8 rows: a 40-token prefill (each expert takes up to 40 rows), then
+    decode steps at B = 64 (the maximum), 24 and 5; experts, every row's hidden
+    state after each layer and the logits against the oracle."""
+    cfg = configs.TINY_BF16.replace(name="tiny-bf16-moe-64", n_experts=8, top_k=2, max_seq=64)
+    B, P = 64, 40
+    pair = Pair(cfg, n_slots=B, max_prefill=P, max_seq=64)
+    tl = pair.tol
+    hid, ids, rl = pair.capture_buffers(P)
+    first = synth.prompts(cfg, 1, P)[0].tolist()
+    g = pair.gpu.prefill(first, seq=0).cpu().numpy()
+    r = pair.ora.prefill(first, slot=0, capture=True)
+    torch.cuda.synchronize()
+    check_logits(g, r["logits"][0], "prefill 40", **tl)
+    check_experts(ids.cpu().numpy(), r["ids"], r["router"], cfg.top_k, "prefill 40")
+    h = hid.cpu().numpy()
+    for l in range(cfg.n_layers + 1):
+        for t in range(P):
+            rl2 = rel_l2(h[l, t], r["hidden"][l, t])
+            assert rl2 <= HIDDEN_REL_L2, f"prefill 40: layer {l - 1} row {t} hidden rel L2 {rl2:.3e}"
+    pair.gpu.set_capture(None, None, None)
+    short = synth.prompts(cfg, B, 3)
+    for b in range(1, B):
+        pair.gpu.prefill(short[b].tolist(), seq=b)
+        pair.ora.prefill(short[b].tolist(), slot=b)
+    lens = [P] + [3] * (B - 1)
+    teach = synth.prompts(cfg, B, 3, stream=synth.TEACHER_STREAM)
+    for s, rows in enumerate((64, 24, 5)):
+        hid, ids, rl = pair.capture_buffers(rows)
+        toks = teach[:rows, s].tolist()
+        pos = lens[:rows]
+        lg = pair.gpu.decode(toks, pos).cpu().numpy()
+        r = pair.ora.decode(toks, pos, capture=True)
+        torch.cuda.synchronize()
+        what = f"decode B={rows}"
+        check_experts(ids.cpu().numpy(), r["ids"], r["router"], cfg.top_k, what)
+        check_hidden(hid.cpu().numpy(), r["hidden"], what)
+        for b in range(rows):
+            check_logits(lg[b], r["logits"][b], f"{what} row {b}", **tl)
+        for b in range(rows):
+            lens[b] += 1
