@@ -202,53 +202,56 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
 
     // lane (r, c) holds rows 4c..4c+3 of each row tile for column r; column r
     // (hi) and r+8 (lo) of the same batch row are summed.
-    floatx4 sum[2][NT];
-#pragma unroll
-    for (int t = 0; t < NT; t++)
-#pragma unroll
-        for (int rt = 0; rt < 2; rt++)
-#pragma unroll
-            for (int j = 0; j < 4; j++) sum[rt][t][j] = acc[rt][t][j] + __shfl_xor(acc[rt][t][j], 8, WAVE);
     if constexpr (SILU) {
         // silu(z) = z / (1 + e^-z), as the separate activation kernel forms it
 #pragma unroll
         for (int t = 0; t < NT; t++) {
+            floatx4 g = acc[0][t], u = acc[1][t];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                g[j] += __shfl_xor(g[j], 8, WAVE);
+                u[j] += __shfl_xor(u[j], 8, WAVE);
+            }
             const int b = t * 8 + (r & 7);
             const int f = n0 + wv * 16 + 4 * c;
             if (r < 8 && b < B && f + 3 < p.N) {
                 uint32_t h[4], l[4];
 #pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const float g = sum[0][t][j], u = sum[1][t][j];
-                    split_bf16(g / (1.0f + expf(-g)) * u, h[j], l[j]);
-                }
+                for (int j = 0; j < 4; j++) split_bf16(g[j] / (1.0f + expf(-g[j])) * u[j], h[j], l[j]);
                 const size_t o = (size_t)b * p.ldo + f;
                 *reinterpret_cast<uint2 *>(p.s_hi + o) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
                 *reinterpret_cast<uint2 *>(p.s_lo + o) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
             }
         }
     } else {
+        // each tile's hi and lo columns are summed just before its store; a
+        // block wholly inside the N rows stores without per-row checks
         float *out = p.out + (size_t)blockIdx.y * p.split_stride;
+        auto store = [&](bool tail) {
 #pragma unroll
-        for (int t = 0; t < NT; t++) {
+            for (int t = 0; t < NT; t++) {
 #pragma unroll
-            for (int rt = 0; rt < 2; rt++) {
-                const floatx4 v = sum[rt][t];
-                const int b = t * 8 + (r & 7);
-                if (r < 8 && b < B) {
-                    const int nn = n0 + wv * 32 + rt * 16 + 4 * c;
-                    float *dst = out + (size_t)(arow0 + b) * p.ldo + nn;
-                    const float4 sv = make_float4(v[0], v[1], v[2], v[3]);
-                    if (nn + 3 < p.N) {
-                        *reinterpret_cast<float4 *>(dst) = sv;
-                    } else {
-                        if (nn < p.N) dst[0] = sv.x;
-                        if (nn + 1 < p.N) dst[1] = sv.y;
-                        if (nn + 2 < p.N) dst[2] = sv.z;
+                for (int rt = 0; rt < 2; rt++) {
+                    floatx4 v = acc[rt][t];
+#pragma unroll
+                    for (int j = 0; j < 4; j++) v[j] += __shfl_xor(v[j], 8, WAVE);
+                    const int b = t * 8 + (r & 7);
+                    if (r < 8 && b < B) {
+                        const int nn = n0 + wv * 32 + rt * 16 + 4 * c;
+                        float *dst = out + (size_t)(arow0 + b) * p.ldo + nn;
+                        if (!tail || nn + 3 < p.N) {
+                            *reinterpret_cast<float4 *>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+                        } else {
+                            if (nn < p.N) dst[0] = v[0];
+                            if (nn + 1 < p.N) dst[1] = v[1];
+                            if (nn + 2 < p.N) dst[2] = v[2];
+                        }
                     }
                 }
             }
-        }
+        };
+        if (n0 + DROWS <= p.N) store(false);
+        else store(true);
     }
 }
 
