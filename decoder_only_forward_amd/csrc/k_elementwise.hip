@@ -56,6 +56,16 @@ __global__ void __launch_bounds__(NTH) residual_norm_kernel(
         ss += r.x * r.x + r.y * r.y + r.z * r.z + r.w * r.w;
         v[u] = r;
     }
+    // the gain is loaded while the block reduces: its latency overlaps the barriers
+    float4 g[VPT];
+    if (gain) {
+#pragma unroll
+        for (int u = 0; u < VPT; u++) {
+            const int i4 = threadIdx.x + u * NTH;
+            if (i4 >= nv) break;
+            g[u] = *reinterpret_cast<const float4 *>(gain + 4 * i4);
+        }
+    }
     const float tot = block_sum(ss, red);
     if (!gain) return;
     const float rs = 1.0f / sqrtf(tot / (float)d + eps);
@@ -64,16 +74,16 @@ __global__ void __launch_bounds__(NTH) residual_norm_kernel(
         const int i4 = threadIdx.x + u * NTH;
         if (i4 >= nv) break;
         const size_t off = (size_t)t * d + 4 * i4;
-        const float4 g = *reinterpret_cast<const float4 *>(gain + 4 * i4);
         float4 a;
-        a.x = v[u].x * rs * g.x; a.y = v[u].y * rs * g.y; a.z = v[u].z * rs * g.z; a.w = v[u].w * rs * g.w;
+        a.x = v[u].x * rs * g[u].x; a.y = v[u].y * rs * g[u].y;
+        a.z = v[u].z * rs * g[u].z; a.w = v[u].w * rs * g[u].w;
         if (a_f32) *reinterpret_cast<float4 *>(a_f32 + off) = a;
         if (a_hi) {
-            uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
-            split_bf16(a.x, h0, l0); split_bf16(a.y, h1, l1);
-            split_bf16(a.z, h2, l2); split_bf16(a.w, h3, l3);
-            *reinterpret_cast<uint2 *>(a_hi + off) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-            *reinterpret_cast<uint2 *>(a_lo + off) = make_uint2(l0 | (l1 << 16), l2 | (l3 << 16));
+            uint2 h, l;
+            split2_bf16(a.x, a.y, h.x, l.x);
+            split2_bf16(a.z, a.w, h.y, l.y);
+            *reinterpret_cast<uint2 *>(a_hi + off) = h;
+            *reinterpret_cast<uint2 *>(a_lo + off) = l;
         }
     }
 }
