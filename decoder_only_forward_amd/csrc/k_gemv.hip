@@ -15,6 +15,8 @@
 // split partials are summed by the consumer kernel in a fixed order (no
 // atomics).  K must be a multiple of 64 (dec_create admits bf16 weights only
 // for such shapes).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -37,8 +39,10 @@ struct GemvParams {
     size_t expert_stride;
     int rot;   // start each block's k walk at stage blockIdx.x % stages
     // silu(gate) * up in the epilogue: w[0] gate, w[1] up, N features; the
-    // product goes to (s_hi, s_lo) [B][ldo] as bf16 pairs
+    // product goes to (s_hi, s_lo) [B][ldo] as bf16 pairs; rt row tiles of 16
+    // per block (8 features each)
     u16 *s_hi, *s_lo;
+    int rt;
 };
 
 constexpr int DKS = 64;            // k per stage
@@ -58,11 +62,18 @@ constexpr size_t dma_lds() { return (size_t)DNSTAGE * (DROWS * DKS + 16 * NT * D
 // an operand read touches covers all banks.
 //
 // FORM: DENSE, one matrix (up to three row segments); GROUPED, grid z is the
-// expert (MoE); SILU_FUSED, the block's 128 rows are 64 features of the gate
-// matrix and the same 64 of the up matrix, interleaved by 16 so that each
-// wave's two row tiles hold gate and up of the same 16 features, and the
-// epilogue writes silu(gate) * up (single k split only).
+// expert (MoE); SILU_FUSED, row tile t of the block (t < rt <= 8) holds 8
+// features of the gate matrix in rows 0-7 and the same 8 of the up matrix in
+// rows 8-15, and the epilogue writes silu(gate) * up (single k split only).
+// With 8 features per tile the grid can be sized to the CU count (Mistral's
+// 14336 features: 7 tiles in each of 256 blocks).
 enum { DENSE = 0, SILU_FUSED = 1, GROUPED = 2 };
+
+// s_waitcnt immediate that lets n loads per stage of the newest DNSTAGE-2
+// stages stay outstanding: vmcnt (bits 3:0 and 15:14), expcnt 7, lgkmcnt 0
+constexpr int ring_wait(int n) {
+    return ((n * (DNSTAGE - 2)) & 15) | (7 << 4) | (0 << 8) | (((n * (DNSTAGE - 2)) >> 4) << 14);
+}
 
 template <int NT, int FORM>
 __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
@@ -74,7 +85,8 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
     constexpr int STG = WST + 16 * NT * DKS;   // u16 per stage
     constexpr int NW = DROWS * DCH / 256;      // weight loads per thread per stage (4)
     constexpr int NLD = NW + NT / 2;           // 16-byte loads per thread per stage
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    // the wave index as a scalar: tests on it branch per wave, not per lane
+    const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, c = lane >> 4;
     int B = p.B, arow0 = 0;
     size_t wofs = 0;
@@ -87,7 +99,8 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
         if (B <= 0) return;
         wofs = (size_t)e * p.expert_stride;
     }
-    const int n0 = blockIdx.x * (SILU ? DROWS / 2 : DROWS);
+    const int RT = SILU ? p.rt : DROWS / 16;   // row tiles of 16 in use
+    const int n0 = blockIdx.x * (SILU ? 8 * RT : DROWS);
     const int kbeg = blockIdx.y * p.kps;
     const int kend = min(p.K, kbeg + p.kps);
     const int nst = kbeg < kend ? (kend - kbeg) / DKS : 0;
@@ -107,9 +120,9 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
         if (i < NW) {
             const int row = P / DCH, lc = (P % DCH) ^ (row & (DCH - 1));
             if constexpr (SILU) {
-                int f = n0 + (row >> 5) * 16 + (row & 15);
+                int f = n0 + (row >> 4) * 8 + (row & 7);
                 f = f < p.N ? f : p.N - 1;
-                src[i] = (((row >> 4) & 1) ? p.w[1] : p.w[0]) + (size_t)f * p.K + kbeg + lc * 8;
+                src[i] = (((row >> 3) & 1) ? p.w[1] : p.w[0]) + (size_t)f * p.K + kbeg + lc * 8;
             } else {
                 int n = n0 + row;
                 n = n < p.N ? n : p.N - 1;
@@ -128,9 +141,13 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
             src[i] = (m < 8 ? p.a_hi : p.a_lo) + (size_t)(arow0 + b) * p.lda + kbeg + lc * 8;
         }
     }
-    // every iteration issues its loads (the last stage again past the end), so
-    // the count of outstanding loads is the same everywhere
-    auto load_stage = [&](int g, int stage) {
+    // Every iteration issues its loads (the last stage again past the end), so
+    // the count of outstanding loads is the same everywhere.  A wave issues the
+    // first NWL of its weight loads: all NW, or in the SILU form those of rows
+    // in the rt tiles (load i of wave wv fills rows 8*(i*4 + wv)..); the loop
+    // is instantiated per count, so its vmcnt waits stay immediates.
+    auto load_stage = [&](int g, int stage, auto nwl_c) {
+        constexpr int NWL = decltype(nwl_c)::value;
         int gg = (g < nst ? g : nst - 1) + rot;
         gg = gg >= nst ? gg - nst : gg;
         const int k0 = gg * DKS;
@@ -138,7 +155,7 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
         // against 6.3 TB/s without the hint); the activation columns, which
         // every block of a split reads, keep the default policy
 #pragma unroll
-        for (int i = 0; i < NW; i++) {
+        for (int i = 0; i < NWL; i++) {
             LDS_AS u16 *dst = (LDS_AS u16 *)smem + stage * STG + (i * 4 + wv) * 512;
             __builtin_amdgcn_global_load_lds((const void *)(src[i] + k0), (LDS_AS void *)dst, 16, 0, CPOL_NT);
         }
@@ -155,22 +172,23 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
 #pragma unroll
         for (int t = 0; t < NT; t++) acc[rt][t] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    if (nst > 0) {
+    // The tiles of a SILU block past rt are multiplied like the others (on
+    // stale LDS) but never stored.
+    auto ring_loop = [&](auto nwl_c) {
+        constexpr int NWL = decltype(nwl_c)::value;
         // between stages: wait until the loads of the newest NSTAGE-2 stages at
         // most are outstanding and every LDS read is done, then a plain barrier
-        // (__syncthreads would also wait for the newest stages).  s_waitcnt
-        // fields: vmcnt (bits 3:0 and 15:14), expcnt 7, lgkmcnt 0.
-        constexpr int WAITN = NLD * (NSTAGE - 2);
-        static_assert(WAITN < 64, "vmcnt field");
-        constexpr int WAIT = (WAITN & 15) | (7 << 4) | (0 << 8) | ((WAITN >> 4) << 14);
+        // (__syncthreads would also wait for the newest stages)
+        static_assert((NWL + NT / 2) * (NSTAGE - 2) < 64, "vmcnt field");
+        constexpr int WAIT = ring_wait(NWL + NT / 2);
 #pragma unroll
-        for (int g = 0; g < NSTAGE - 1; g++) load_stage(g, g);
+        for (int g = 0; g < NSTAGE - 1; g++) load_stage(g, g, nwl_c);
         __builtin_amdgcn_s_waitcnt(WAIT);
         __builtin_amdgcn_s_barrier();
         for (int g = 0; g < nst; g++) {
             // stage (g-1) % NSTAGE, which this load refills, was finished by every
             // wave before the previous barrier
-            load_stage(g + NSTAGE - 1, (g + NSTAGE - 1) % NSTAGE);
+            load_stage(g + NSTAGE - 1, (g + NSTAGE - 1) % NSTAGE, nwl_c);
             const u16 *sw = smem + (g % NSTAGE) * STG;
             const u16 *sa = sw + WST;
 #pragma unroll
@@ -198,29 +216,53 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
         // the loads issued past the last stage must land before the block's LDS
         // is released
         __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    };
+    if (nst > 0) {
+        if constexpr (!SILU) {
+            ring_loop(std::integral_constant<int, NW>{});
+        } else {
+            static_assert(NW == 4, "one instance per weight-load count");
+            int nwl = 0;   // wave-uniform
+#pragma unroll
+            for (int i = 0; i < NW; i++) nwl += i * 4 + wv < 2 * RT;
+            switch (nwl) {
+                case 4: ring_loop(std::integral_constant<int, 4>{}); break;
+                case 3: ring_loop(std::integral_constant<int, 3>{}); break;
+                case 2: ring_loop(std::integral_constant<int, 2>{}); break;
+                case 1: ring_loop(std::integral_constant<int, 1>{}); break;
+                default: ring_loop(std::integral_constant<int, 0>{}); break;
+            }
+        }
     }
 
     // lane (r, c) holds rows 4c..4c+3 of each row tile for column r; column r
     // (hi) and r+8 (lo) of the same batch row are summed.
     if constexpr (SILU) {
-        // silu(z) = z / (1 + e^-z), as the separate activation kernel forms it
+        // gate rows 4c.. of a tile sit in lanes c = 0, 1 and the up rows of the
+        // same features in lanes c + 2 (32 lanes on); silu(z) = z / (1 + e^-z),
+        // as the separate activation kernel forms it
 #pragma unroll
-        for (int t = 0; t < NT; t++) {
-            floatx4 g = acc[0][t], u = acc[1][t];
+        for (int rt = 0; rt < 2; rt++) {
+            const int tile = 2 * wv + rt;
+            if (tile >= RT) continue;   // wave-uniform
 #pragma unroll
-            for (int j = 0; j < 4; j++) {
-                g[j] += __shfl_xor(g[j], 8, WAVE);
-                u[j] += __shfl_xor(u[j], 8, WAVE);
-            }
-            const int b = t * 8 + (r & 7);
-            const int f = n0 + wv * 16 + 4 * c;
-            if (r < 8 && b < B && f + 3 < p.N) {
-                uint32_t h[4], l[4];
+            for (int t = 0; t < NT; t++) {
+                floatx4 g = acc[rt][t], u;
 #pragma unroll
-                for (int j = 0; j < 4; j++) split_bf16(g[j] / (1.0f + expf(-g[j])) * u[j], h[j], l[j]);
-                const size_t o = (size_t)b * p.ldo + f;
-                *reinterpret_cast<uint2 *>(p.s_hi + o) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-                *reinterpret_cast<uint2 *>(p.s_lo + o) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+                for (int j = 0; j < 4; j++) {
+                    g[j] += __shfl_xor(g[j], 8, WAVE);
+                    u[j] = __shfl_xor(g[j], 32, WAVE);
+                }
+                const int b = t * 8 + (r & 7);
+                const int f = n0 + 8 * tile + 4 * c;
+                if (c < 2 && r < 8 && b < B && f + 3 < p.N) {
+                    uint32_t h[4], l[4];
+#pragma unroll
+                    for (int j = 0; j < 4; j++) split_bf16(g[j] / (1.0f + expf(-g[j])) * u[j], h[j], l[j]);
+                    const size_t o = (size_t)b * p.ldo + f;
+                    *reinterpret_cast<uint2 *>(p.s_hi + o) = make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                    *reinterpret_cast<uint2 *>(p.s_lo + o) = make_uint2(l[0] | (l[1] << 16), l[2] | (l[3] << 16));
+                }
             }
         }
     } else {
@@ -363,7 +405,15 @@ void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
 
 bool launch_gemv_silu(hipStream_t st, const void *w_gate, const void *w_up, int F, int K, const u16 *a_hi,
                       const u16 *a_lo, int lda, int B, u16 *s_hi, u16 *s_lo, int ldo) {
-    if (B <= 0 || B > 64 || K % DKS != 0 || F % (DROWS / 2) != 0) return false;
+    if (B <= 0 || B > 64 || K % DKS != 0 || F % 8 != 0) return false;
+    // Up to 32 rows the 8-feature tiles are spread over the CUs (rt tiles per
+    // block, one block per CU).  With more rows each block's activation tile
+    // outweighs its weight rows, and fewer, full blocks (8 tiles) measured
+    // faster (Qwen2.5-0.5B at B = 64: 20 us against 22).
+    const int units = F / 8, cus = num_cus();
+    int rt = B > 32 ? DROWS / 16 : (units + cus - 1) / cus;
+    rt = rt < 1 ? 1 : (rt > DROWS / 16 ? DROWS / 16 : rt);
+    const int blocks = (units + rt - 1) / rt;
     GemvParams p{};
     p.w[0] = (const u16 *)w_gate;
     p.w[1] = (const u16 *)w_up;
@@ -379,7 +429,8 @@ bool launch_gemv_silu(hipStream_t st, const void *w_gate, const void *w_up, int 
     p.rot = K % 4096 == 0 ? 1 : 0;
     p.s_hi = s_hi;
     p.s_lo = s_lo;
-    launch_dma<SILU_FUSED>(st, p, dim3(F / (DROWS / 2), 1, 1), B);
+    p.rt = rt;
+    launch_dma<SILU_FUSED>(st, p, dim3(blocks, 1, 1), B);
     return true;
 }
 

@@ -90,7 +90,8 @@ bool launch_gemm_silu(hipStream_t st, const void *w_gate, const void *w_up, int 
 // Decode form of the fused SwiGLU: gate and up of F features (bf16 [F, K]
 // each) against B <= 64 activation rows, one k split, silu(gate) * up written
 // as bf16 (hi, lo) pairs to s_hi/s_lo [B][ldo].  Returns false (nothing
-// launched) for shapes it does not take: K or F not a multiple of 64.
+// launched) for shapes it does not take: K not a multiple of 64 or F not a
+// multiple of 8.
 bool launch_gemv_silu(hipStream_t st, const void *w_gate, const void *w_up, int F, int K, const u16 *a_hi,
                       const u16 *a_lo, int lda, int B, u16 *s_hi, u16 *s_lo, int ldo);
 
