@@ -586,12 +586,19 @@ int dec_create(const dec_config *cfg, const dec_weights *w, void *workspace, siz
     if (!w || w->struct_size != sizeof(dec_weights) || !w->embed || !w->out_norm || !w->layers)
         return DEC_ERR_INVALID;
     if (!cfg->tied_embedding && !w->lm_head) return DEC_ERR_INVALID;
+    // every weight is read in 16-byte words
+    auto misaligned = [](const void *q) { return q && ((uintptr_t)q & 15); };
+    if (misaligned(w->embed) || misaligned(w->out_norm) || misaligned(w->lm_head)) return DEC_ERR_INVALID;
     for (int l = 0; l < cfg->n_layers; l++) {
         const dec_layer_weights &L = w->layers[l];
         if (!L.attn_norm || !L.wq || !L.wk || !L.wv || !L.wo || !L.ffn_norm || !L.w_gate || !L.w_up || !L.w_down)
             return DEC_ERR_INVALID;
         if (cfg->qkv_bias && (!L.bq || !L.bk || !L.bv)) return DEC_ERR_INVALID;
         if (cfg->n_experts && !L.router) return DEC_ERR_INVALID;
+        for (const void *q : {(const void *)L.attn_norm, L.wq, L.wk, L.wv, (const void *)L.bq, (const void *)L.bk,
+                              (const void *)L.bv, L.wo, (const void *)L.ffn_norm, L.w_gate, L.w_up, L.w_down,
+                              L.router})
+            if (misaligned(q)) return DEC_ERR_INVALID;
     }
     Plan p;
     plan(*cfg, p);

@@ -225,7 +225,20 @@ void launch_rope_table(hipStream_t st, const int32_t *pos, int T, int hd, double
 // (sipllm "Transformer forward pass", section "RoPE is adjacent-pair") or
 // halves (i, i + hd/2) (rml "Which dimensions pair").  K and V go to the cache
 // slot of the position (Pantheon, "Sliding Window (Mistral)": write at
-// pos % max_seq when the cache is a ring).  One thread per pair of a row.
+// pos % max_seq when the cache is a ring).  One thread per 4 consecutive pairs
+// of a head (hd is 16, 64 or 128), moved as float4 words: elements
+// [i, i+4) and [i+hd/2, i+hd/2+4) for halves, [2i, 2i+8) for adjacent pairs
+// (and for v, which is not rotated).
+__device__ __forceinline__ void store4(void *cache, size_t at, int kv_bf16, float4 v) {
+    if (kv_bf16) {
+        *reinterpret_cast<uint2 *>(static_cast<u16 *>(cache) + at) =
+            make_uint2(f32_to_bf16_bits(v.x) | (f32_to_bf16_bits(v.y) << 16),
+                       f32_to_bf16_bits(v.z) | (f32_to_bf16_bits(v.w) << 16));
+    } else {
+        *reinterpret_cast<float4 *>(static_cast<float *>(cache) + at) = v;
+    }
+}
+
 __global__ void __launch_bounds__(256) rope_kv_kernel(
     Partials qkv, const float *__restrict__ bq, const float *__restrict__ bk, const float *__restrict__ bv,
     const float2 *__restrict__ tab, const int32_t *__restrict__ pos, const int32_t *__restrict__ slot,
@@ -234,47 +247,66 @@ __global__ void __launch_bounds__(256) rope_kv_kernel(
     const int t = blockIdx.x;
     const int qd = nh * hd, kvd = nkv * hd, half = hd / 2;
     const int npairs = (qd + 2 * kvd) / 2;
-    const int pi = blockIdx.y * blockDim.x + threadIdx.x;
+    const int pi = 4 * (blockIdx.y * blockDim.x + threadIdx.x);   // first of this thread's 4 pairs
     if (pi >= npairs) return;
-    const int p = pos[t];
-    const int s = ring ? p % max_seq : p;
-    const size_t slot_base = (size_t)slot[t] * nkv;
-    // section, head and pair index within the head
+    // section, head and pair index within the head (all 4 pairs share them)
     int base, i;
     if (pi < qd / 2) { base = 0; i = pi; }
     else if (pi < (qd + kvd) / 2) { base = qd; i = pi - qd / 2; }
     else { base = qd + kvd; i = pi - (qd + kvd) / 2; }
     const int head = i / half, ip = i % half;
     const bool rotate = base < qd + kvd;
-    const int e0c = head * hd + ((rotate && pairing) ? ip : 2 * ip);
-    const int e1c = head * hd + ((rotate && pairing) ? ip + half : 2 * ip + 1);
+    const bool halves = rotate && pairing;
+    // element offsets within the section of the two float4 words
+    const int w0 = head * hd + (halves ? ip : 2 * ip);
+    const int w1 = halves ? w0 + half : w0 + 4;
     const size_t off = (size_t)t * qkv.ld + base;
-    float e0 = sum_splits(qkv.p, qkv.S, qkv.stride, off + e0c);
-    float e1 = sum_splits(qkv.p, qkv.S, qkv.stride, off + e1c);
+    float4 a = sum_splits4(qkv.p, qkv.S, qkv.stride, off + w0);
+    float4 c = sum_splits4(qkv.p, qkv.S, qkv.stride, off + w1);
     const float *bias = base == 0 ? bq : (base == qd ? bk : bv);
-    if (bias) { e0 += bias[e0c]; e1 += bias[e1c]; }
+    if (bias) {
+        add4(a, *reinterpret_cast<const float4 *>(bias + w0));
+        add4(c, *reinterpret_cast<const float4 *>(bias + w1));
+    }
     if (rotate) {
-        const float2 cs = tab[(size_t)t * half + ip];
-        const float r0 = e0 * cs.x - e1 * cs.y, r1 = e0 * cs.y + e1 * cs.x;
-        e0 = r0;
-        e1 = r1;
+        // pair j: (e0, e1) = (a[j], c[j]) for halves, else elements 2j, 2j+1 of a|c
+        float e0[4], e1[4];
+        if (halves) {
+            e0[0] = a.x; e0[1] = a.y; e0[2] = a.z; e0[3] = a.w;
+            e1[0] = c.x; e1[1] = c.y; e1[2] = c.z; e1[3] = c.w;
+        } else {
+            e0[0] = a.x; e1[0] = a.y; e0[1] = a.z; e1[1] = a.w;
+            e0[2] = c.x; e1[2] = c.y; e0[3] = c.z; e1[3] = c.w;
+        }
+        const float4 cs01 = *reinterpret_cast<const float4 *>(tab + (size_t)t * half + ip);
+        const float4 cs23 = *reinterpret_cast<const float4 *>(tab + (size_t)t * half + ip + 2);
+        const float cw[4] = {cs01.x, cs01.z, cs23.x, cs23.z}, sw[4] = {cs01.y, cs01.w, cs23.y, cs23.w};
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const float r0 = e0[j] * cw[j] - e1[j] * sw[j], r1 = e0[j] * sw[j] + e1[j] * cw[j];
+            e0[j] = r0;
+            e1[j] = r1;
+        }
+        if (halves) {
+            a = make_float4(e0[0], e0[1], e0[2], e0[3]);
+            c = make_float4(e1[0], e1[1], e1[2], e1[3]);
+        } else {
+            a = make_float4(e0[0], e1[0], e0[1], e1[1]);
+            c = make_float4(e0[2], e1[2], e0[3], e1[3]);
+        }
     }
     if (base == 0) {
-        q_out[(size_t)t * qd + e0c] = e0;
-        q_out[(size_t)t * qd + e1c] = e1;
+        *reinterpret_cast<float4 *>(q_out + (size_t)t * qd + w0) = a;
+        *reinterpret_cast<float4 *>(q_out + (size_t)t * qd + w1) = c;
     } else {
+        const int p = pos[t];
+        const int s = ring ? p % max_seq : p;
         void *cache = base == qd ? kc : vc;
         // the layer cache at the position's slot, or row t of a chunk buffer [T][nkv][hd]
-        const size_t dst = chunk ? ((size_t)t * nkv + head) * hd : ((slot_base + head) * max_seq + s) * hd;
-        if (kv_bf16) {
-            u16 *c16 = static_cast<u16 *>(cache);
-            c16[dst + e0c - head * hd] = (u16)f32_to_bf16_bits(e0);
-            c16[dst + e1c - head * hd] = (u16)f32_to_bf16_bits(e1);
-        } else {
-            float *c32 = static_cast<float *>(cache);
-            c32[dst + e0c - head * hd] = e0;
-            c32[dst + e1c - head * hd] = e1;
-        }
+        const size_t dst = chunk ? ((size_t)t * nkv + head) * hd
+                                 : (((size_t)slot[t] * nkv + head) * max_seq + s) * hd;
+        store4(cache, dst + w0 - head * hd, kv_bf16, a);
+        store4(cache, dst + w1 - head * hd, kv_bf16, c);
     }
 }
 
@@ -283,8 +315,8 @@ void launch_rope_kv(hipStream_t st, int T, Partials qkv, const float *bq, const 
                     int nh, int nkv, int hd, int pairing, float *q_out, void *kc, void *vc, int max_seq,
                     int ring, int kv_bf16, int chunk) {
     if (T <= 0) return;
-    const int npairs = (nh + 2 * nkv) * hd / 2;
-    hipLaunchKernelGGL(rope_kv_kernel, dim3(T, (npairs + 255) / 256), dim3(256), 0, st, qkv, bq, bk, bv, tab, pos,
+    const int nquads = (nh + 2 * nkv) * hd / 8;
+    hipLaunchKernelGGL(rope_kv_kernel, dim3(T, (nquads + 255) / 256), dim3(256), 0, st, qkv, bq, bk, bv, tab, pos,
                        slot, nh, nkv, hd, pairing, q_out, kc, vc, max_seq, ring, kv_bf16, chunk);
 }
 
@@ -359,9 +391,20 @@ __global__ void __launch_bounds__(1024) argmax_kernel(const float *__restrict__ 
     const float *row = logits + (size_t)b * V;
     float bv = -INFINITY;
     int bi = 0x7FFFFFFF;
-    for (int i = threadIdx.x; i < V; i += blockDim.x) {
-        const float v = row[i];
-        if (better(v, i, bv, bi)) { bv = v; bi = i; }
+    // eight loads per thread in flight, then compared in index order
+    constexpr int U = 8;
+    for (int i0 = threadIdx.x; i0 < V; i0 += blockDim.x * U) {
+        float v[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int i = i0 + u * blockDim.x;
+            v[u] = i < V ? row[i] : -INFINITY;
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int i = i0 + u * blockDim.x;
+            if (i < V && better(v[u], i, bv, bi)) { bv = v[u]; bi = i; }
+        }
     }
     for (int o = 32; o > 0; o >>= 1) {
         const float ov = __shfl_xor(bv, o, WAVE);

@@ -111,9 +111,10 @@ typedef struct dec_config {
 } dec_config;
 
 /*
- * Weights of one layer: device pointers, row-major [out][in].  Matrices are
- * bf16 (or fp32 when weight_dtype == DEC_WEIGHT_F32); norm gains and biases
- * are always fp32.  Dense:  w_gate, w_up [ffn][d], w_down [d][ffn].
+ * Weights of one layer: device pointers, row-major [out][in], each 16-byte
+ * aligned (the kernels read them in 16-byte words; dec_create returns
+ * DEC_ERR_INVALID otherwise).  Matrices are bf16 (or fp32 when weight_dtype ==
+ * DEC_WEIGHT_F32); norm gains and biases are always fp32.  Dense:  w_gate, w_up [ffn][d], w_down [d][ffn].
  * MoE: router [E][d]; w_gate, w_up [E][ffn][d]; w_down [E][d][ffn], expert e
  * being the e-th slice (Pantheon, section "Mixture of Experts (Mixtral)",
  * merged expert tensors).  bq/bk/bv only with qkv_bias; router only with MoE.

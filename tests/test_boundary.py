@@ -52,7 +52,7 @@ def test_bf16_cache_halves_the_kv_bytes():
     assert f32 - b16 == kv + chunk + img
 
 
-def _create(cfg, max_batch=2, max_prefill=8, ws=None, ws_bytes=None, **over):
+def _create(cfg, max_batch=2, max_prefill=8, ws=None, ws_bytes=None, layer_field=None, **over):
     L = _lib()
     c = D.make_config(cfg, max_batch, max_prefill)
     for k, v in over.items():
@@ -63,6 +63,8 @@ def _create(cfg, max_batch=2, max_prefill=8, ws=None, ws_bytes=None, **over):
     for i in range(cfg.n_layers):
         for f, _ in D.DecLayerWeights._fields_:
             setattr(layers[i], f, fake)
+    if layer_field is not None:    # (field, address) set in the last layer
+        setattr(layers[cfg.n_layers - 1], *layer_field)
     w = D.DecWeights(ctypes.sizeof(D.DecWeights), fake, fake, fake, layers)
     h = ctypes.c_void_p()
     rc = L.dec_create(ctypes.byref(c), ctypes.byref(w), ws if ws is not None else fake,
@@ -73,6 +75,12 @@ def _create(cfg, max_batch=2, max_prefill=8, ws=None, ws_bytes=None, **over):
 def test_create_validation():
     assert _create(configs.TINY, ws_bytes=16)[0] == D.DEC_ERR_NOMEM
     assert _create(configs.TINY, ws=0x7F0000000001)[0] == D.DEC_ERR_INVALID      # misaligned
+    # weights are read in 16-byte words: a pointer off that grid is refused
+    assert _create(configs.TINY, layer_field=("wq", 0x7F0000000008))[0] == D.DEC_ERR_INVALID
+    assert _create(configs.QWEN25, layer_field=("bk", 0x7F0000000004))[0] == D.DEC_ERR_INVALID
+    rc, h, L = _create(configs.TINY, layer_field=("w_down", 0x7F0000000010))
+    assert rc == D.DEC_OK
+    L.dec_destroy(h)
     assert _create(configs.TINY, struct_size=8)[0] == D.DEC_ERR_INVALID
     assert _create(configs.TINY, head_dim=32)[0] == D.DEC_ERR_UNSUPPORTED
     assert _create(configs.TINY, max_batch=65)[0] == D.DEC_ERR_UNSUPPORTED
