@@ -376,19 +376,22 @@ void run_pass(dec_model *m, const Pass &ps) {
         // q | k | v
         WSeg qkv[3] = {{w.wq, qd}, {w.wk, kvd}, {w.wv, kvd}};
         Partials pq = proj(m, qkv, 3, d, T, ah, al, af, d);
-        // K/V into the layer cache, or held in the chunk buffers (deferred commit)
-        launch_rope_kv(st, T, pq, c.qkv_bias ? w.bq : nullptr, c.qkv_bias ? w.bk : nullptr,
-                       c.qkv_bias ? w.bv : nullptr, m->rope, m->pos, m->slot, nh, nkv, hd, c.rope_pairing, m->q,
-                       ps.deferred ? (void *)m->ck : (void *)kc, ps.deferred ? (void *)m->cv : (void *)vc,
-                       c.max_seq, m->ring, kvb, ps.deferred);
         // attention -> a (row stride qd)
         if (ps.decode) {
+            // RoPE and the new K/V rows are formed inside the attention kernel
             const int S = attn_splits_for(m, T, ps.hpos);
+            const RopeArgs ra{pq, c.qkv_bias ? w.bq : nullptr, c.qkv_bias ? w.bk : nullptr,
+                              c.qkv_bias ? w.bv : nullptr, m->rope, c.rope_pairing, m->ring};
             Tick tk(m, DEC_K_ATTN_DECODE);
-            launch_attn_decode(st, T, m->q, kc, vc, kvb, m->pos, m->slot, nh, nkv, hd, c.max_seq, c.sliding_window, S,
-                               m->attn, ah, al, af);
+            launch_attn_decode(st, T, ra, kc, vc, kvb, m->pos, m->slot, nh, nkv, hd, c.max_seq, S, m->attn, ah, al,
+                               af);
             tk.done(kv_read_bytes(c, T, ps.hpos) + 2.0 * T * qd * 4, 0);
         } else {
+            // K/V into the layer cache, or held in the chunk buffers (deferred commit)
+            launch_rope_kv(st, T, pq, c.qkv_bias ? w.bq : nullptr, c.qkv_bias ? w.bk : nullptr,
+                           c.qkv_bias ? w.bv : nullptr, m->rope, m->pos, m->slot, nh, nkv, hd, c.rope_pairing, m->q,
+                           ps.deferred ? (void *)m->ck : (void *)kc, ps.deferred ? (void *)m->cv : (void *)vc,
+                           c.max_seq, m->ring, kvb, ps.deferred);
             // keys per query: positions [p - window + 1, p] (window 0: [0, p])
             const int W = c.sliding_window;
             double flops = 0, keys = 0;

@@ -23,6 +23,13 @@
 // Ring cache: softmax does not depend on key order, and keys are stored already
 // rotated, so the readable slots [0, min(pos+1, max_seq)) are read as one
 // contiguous range whatever the wrap (Pantheon, "Sliding Window (Mistral)").
+//
+// RoPE and the K/V store are folded into the prologue: every block forms the
+// G rotated queries of its group from the projection's split partials (into
+// LDS), and the block whose split covers the row's new slot also forms the
+// rotated key and the value of the new position and stores them in the cache
+// before its first read of it (the same arithmetic, summation order and
+// rounding as launch_rope_kv).
 #include "common.h"
 #include "kernels.h"
 
@@ -100,9 +107,28 @@ __device__ __forceinline__ void store_out(float v, size_t off, u16 *o_hi, u16 *o
 template <int G>
 constexpr int dims_per_lane() { return G <= 4 ? 16 : 8; }
 
+// Element pair i of a head: (i, i + hd/2) when rotated with pairing 1, else
+// (2i, 2i+1).  x0, x1: the pair's q/k/v values (split partials summed in
+// order, bias added); rotated by the row's table entry when rot is set.
+template <int HD>
+__device__ __forceinline__ void rope_pair(const RopeArgs &ra, int b, size_t row, int i, bool rot, const float *bias,
+                                          int &e0, int &e1, float &x0, float &x1) {
+    e0 = (rot && ra.pairing) ? i : 2 * i;
+    e1 = (rot && ra.pairing) ? i + HD / 2 : 2 * i + 1;
+    x0 = sum_splits(ra.qkv.p, ra.qkv.S, ra.qkv.stride, row + e0);
+    x1 = sum_splits(ra.qkv.p, ra.qkv.S, ra.qkv.stride, row + e1);
+    if (bias) { x0 += bias[e0]; x1 += bias[e1]; }
+    if (rot) {
+        const float2 cs = ra.tab[(size_t)b * (HD / 2) + i];
+        const float r0 = x0 * cs.x - x1 * cs.y, r1 = x0 * cs.y + x1 * cs.x;
+        x0 = r0;
+        x1 = r1;
+    }
+}
+
 template <int HD, int G, bool KB>
 __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
-    const float *__restrict__ q, const void *__restrict__ kc, const void *__restrict__ vc,
+    RopeArgs ra, void *__restrict__ kc, void *__restrict__ vc,
     const int32_t *__restrict__ pos, const int32_t *__restrict__ slot, int nh, int nkv, int max_seq,
     int splits, float *__restrict__ part, u16 *__restrict__ o_hi, u16 *__restrict__ o_lo,
     float *__restrict__ o_f32) {
@@ -117,6 +143,7 @@ __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
     constexpr int NB = (KB ? 4 : 8) / NV;
     __shared__ float sm[4][G], sl[4][G];
     __shared__ float sacc[4][G][HD];
+    __shared__ float qs[G][HD];
 
     const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
     const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
@@ -134,6 +161,48 @@ __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
     const char *V = static_cast<const char *>(vc) + head_base * HD * R::ES;
     const float qscale = LOG2E / sqrtf((float)HD);
 
+    // Prologue: tasks [0, G*HD/2) are the query pairs of the group's heads;
+    // the block whose range holds the new slot also takes the HD/2 key pairs
+    // and HD/2 value pairs of the new position and stores them.
+    {
+        constexpr int HALF = HD / 2;
+        const int sp = ra.ring ? p % max_seq : p;
+        const bool owner = sp >= beg && sp < end;
+        const int qd = nh * HD, kvd = nkv * HD;
+        const size_t row = (size_t)b * ra.qkv.ld;
+        const int nq = G * HALF, ntask = nq + (owner ? 2 * HALF : 0);
+        for (int task = threadIdx.x; task < ntask; task += blockDim.x) {
+            int e0, e1;
+            float x0, x1;
+            if (task < nq) {
+                const int h = kvh * G + task / HALF;
+                rope_pair<HD>(ra, b, row + (size_t)h * HD, task % HALF, true, ra.bq ? ra.bq + h * HD : nullptr, e0,
+                              e1, x0, x1);
+                qs[task / HALF][e0] = x0;
+                qs[task / HALF][e1] = x1;
+            } else {
+                const bool isk = task < nq + HALF;
+                const int i = isk ? task - nq : task - nq - HALF;
+                const float *bias = isk ? ra.bk : ra.bv;
+                rope_pair<HD>(ra, b, row + (isk ? qd : qd + kvd) + (size_t)kvh * HD, i, isk,
+                              bias ? bias + kvh * HD : nullptr, e0, e1, x0, x1);
+                const size_t at = (head_base + sp) * HD;
+                if constexpr (KB) {
+                    u16 *c = static_cast<u16 *>(isk ? kc : vc) + at;
+                    c[e0] = (u16)f32_to_bf16_bits(x0);
+                    c[e1] = (u16)f32_to_bf16_bits(x1);
+                } else {
+                    float *c = static_cast<float *>(isk ? kc : vc) + at;
+                    c[e0] = x0;
+                    c[e1] = x1;
+                }
+            }
+        }
+        // the queries are complete in LDS, and the new K/V row is stored (the
+        // barrier's release waits for the stores) before any wave reads it
+        __syncthreads();
+    }
+
     // fp32 cache: q in fp32.  bf16 cache: q as (hi, lo) bf16 pairs matching
     // the packing of the key words, for v_dot2 against the stored keys.
     constexpr int QN = KB ? DPL / 2 : DPL;
@@ -141,7 +210,7 @@ __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
     uint32_t qph[G][KB ? QN : 1], qpl[G][KB ? QN : 1];
 #pragma unroll
     for (int g = 0; g < G; g++) {
-        const float *qg = q + (size_t)b * nh * HD + (size_t)(kvh * G + g) * HD;
+        const float *qg = qs[g];
         if constexpr (KB) {
 #pragma unroll
             for (int j = 0; j < QN; j++) {
@@ -345,10 +414,10 @@ __global__ void __launch_bounds__(128) attn_merge_kernel(int nh, int hd, int spl
 }
 
 template <int HD, bool KB>
-bool launch_decode_hd(hipStream_t st, int G, dim3 grid, const float *q, const void *kc, const void *vc,
+bool launch_decode_hd(hipStream_t st, int G, dim3 grid, const RopeArgs &ra, void *kc, void *vc,
                       const int32_t *pos, const int32_t *slot, int nh, int nkv, int max_seq, int splits,
                       float *part, u16 *o_hi, u16 *o_lo, float *o_f32) {
-#define AD(GG) hipLaunchKernelGGL((attn_decode_kernel<HD, GG, KB>), grid, dim3(256), 0, st, q, kc, vc, pos, \
+#define AD(GG) hipLaunchKernelGGL((attn_decode_kernel<HD, GG, KB>), grid, dim3(256), 0, st, ra, kc, vc, pos, \
                                   slot, nh, nkv, max_seq, splits, part, o_hi, o_lo, o_f32)
     switch (G) {
         case 1: AD(1); return true;
@@ -397,14 +466,13 @@ int attn_decode_splits(int B, int nkv, int readable, int hd, int G, int kv_bf16)
     return s;
 }
 
-void launch_attn_decode(hipStream_t st, int B, const float *q, const void *kc, const void *vc, int kv_bf16,
-                        const int32_t *pos, const int32_t *slot, int nh, int nkv, int hd, int max_seq,
-                        int window, int splits, float *part, u16 *o_hi, u16 *o_lo, float *o_f32) {
-    (void)window;
+void launch_attn_decode(hipStream_t st, int B, const RopeArgs &ra, void *kc, void *vc, int kv_bf16,
+                        const int32_t *pos, const int32_t *slot, int nh, int nkv, int hd, int max_seq, int splits,
+                        float *part, u16 *o_hi, u16 *o_lo, float *o_f32) {
     if (B <= 0) return;
     const int G = nh / nkv;
     dim3 grid(splits, nkv, B);
-#define LD(HD, KB) launch_decode_hd<HD, KB>(st, G, grid, q, kc, vc, pos, slot, nh, nkv, max_seq, splits, part, \
+#define LD(HD, KB) launch_decode_hd<HD, KB>(st, G, grid, ra, kc, vc, pos, slot, nh, nkv, max_seq, splits, part, \
                                             o_hi, o_lo, o_f32)
     if (kv_bf16) {
         if (hd == 128) LD(128, true);

@@ -99,15 +99,29 @@ bool launch_gemv_silu(hipStream_t st, const void *w_gate, const void *w_up, int 
 void launch_gemm_f32(hipStream_t st, const WSeg *segs, int nseg, int K, const float *a, int lda,
                      int M, float *out, int ldo);
 
-// Split-KV decode attention.  Row b: query q[b][nh*hd], slot slot[b], position
-// pos[b]; keys/values of positions [lo, pos] in the layer cache (fp32, or bf16
-// when kv_bf16 is set).  Writes the
-// attention output as bf16 (hi, lo) and/or fp32 rows [B][nh*hd].
+// The decode rows' q | k | v projection (split partials; fp32 biases when
+// given) and the RoPE table of their positions (tab[b][i], see
+// launch_rope_table), from which the decode attention forms its queries and
+// the K/V row of each row's new position.
+struct RopeArgs {
+    Partials qkv;
+    const float *bq, *bk, *bv;
+    const float2 *tab;
+    int pairing;   // 0 rotates elements (2i, 2i+1) of a head, 1 rotates (i, i + hd/2)
+    int ring;      // the cache is a ring: position p sits at slot p % max_seq
+};
+
+// Split-KV decode attention.  Row b (sequence slot slot[b], position pos[b]):
+// q and the new K/V row come from ra (RoPE applied as launch_rope_kv does);
+// the K/V row is stored at the position's slot of the layer cache (fp32, or
+// nearest-even bf16 when kv_bf16 is set) by the block whose split covers it,
+// and the keys/values of the readable slots [0, min(pos+1, max_seq)) are then
+// attended.  Writes the attention output as bf16 (hi, lo) and/or fp32 rows
+// [B][nh*hd].
 int attn_decode_splits(int B, int nkv, int readable, int hd, int G, int kv_bf16);
-void launch_attn_decode(hipStream_t st, int B, const float *q, const void *kc, const void *vc,
-                        int kv_bf16, const int32_t *pos, const int32_t *slot, int nh, int nkv, int hd,
-                        int max_seq, int window, int splits, float *part, u16 *o_hi, u16 *o_lo,
-                        float *o_f32);
+void launch_attn_decode(hipStream_t st, int B, const RopeArgs &ra, void *kc, void *vc, int kv_bf16,
+                        const int32_t *pos, const int32_t *slot, int nh, int nkv, int hd, int max_seq,
+                        int splits, float *part, u16 *o_hi, u16 *o_lo, float *o_f32);
 
 // Causal prefill attention for T rows of one sequence at positions
 // start_pos..start_pos+T-1.  Query p attends to positions [p - window + 1, p]
