@@ -67,11 +67,13 @@ def test_smollm2_width_ring_at_full_depth():
     _chunks(pair, toks, [40, 50, 100, 10], "smollm2-w64")
 
 
-def _mistral_ring(P0, n, sample):
+def _mistral_ring(P0, n, sample, kv_bf16=False):
     """Full-width one-layer Mistral-7B: prefill P0 tokens, then append n more
     in one call (deferred commit); sampled rows of the appended chunk, and one
     decode step after it, against the oracle."""
     cfg = configs.one_layer(configs.MISTRAL)
+    if kv_bf16:
+        cfg = cfg.replace(name=cfg.name + "-kvbf16", kv_bf16=True)
     torch.manual_seed(0)
     wd = synth.make_weights(cfg, seed=0, device="cuda")
     w = _host(wd)
@@ -108,3 +110,11 @@ def test_mistral_one_layer_append_512_after_a_full_ring():
 
 def test_mistral_one_layer_single_prefill_longer_than_the_ring():
     _mistral_ring(0, 4396, [0, 4095, 4096, 4200, 4395])
+
+
+@pytest.mark.parametrize("kv_bf16", [False, True], ids=["f32-cache", "bf16-cache"])
+def test_mistral_one_layer_decode_whose_new_slot_is_in_a_middle_split(kv_bf16):
+    """After 6096 positions the ring's next slot is 2000: the B = 1 decode
+    attention runs 32 splits of 128 slots, and split 15, not the first or the
+    last, stores the new key/value before reading its range."""
+    _mistral_ring(4096, 2000, [0, 1999], kv_bf16=kv_bf16)
