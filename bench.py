@@ -35,22 +35,22 @@ HBM_PEAK_GBS = 8000.0
 _COMMON = {"decoder_only_forward_amd/csrc/common.h":
            "34608c55f95e88c4c9dc0713feb1c89be769be0a7ff3031fa8e6327276c4082b"}
 _ATTN_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_decode.hip":
-                                 "c2f5c9d72da35645a599ebcb8442ac997bcd6b0e8a23d7d744ac74e8f8e304f8"})
+                                 "d61d0a64f52f62e3dff981b9522676bb319802039ef285e9a2130fd9e149e6d6"})
 _GEMV_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemv.hip":
                                  "e8b40692db620676cb8b5a5653b879158cc66c2d689ff00d7afbbe436a81511c"})
 _GEMM_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemm.hip":
                                  "2b5a11a5b66d407bcf10b64d4014b202650f0e067b23c57659c2175110e22eee"})
 MEASURED_TRAFFIC = {
     ("attn_decode_kernel", "fp32"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 1074937926},
+                                     "bytes_per_launch": 1078805193},
     ("attn_decode_kernel", "bf16"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 539258404},
+                                     "bytes_per_launch": 545077257},
     ("gemv_decode", "fp32"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                              "bytes_per_launch": 121764633},
+                              "bytes_per_launch": 121760212},
     ("gemv_decode", "bf16"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                              "bytes_per_launch": 121764633},
+                              "bytes_per_launch": 121760212},
     ("gemm_prefill", "fp32"): {"sources": _GEMM_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                               "bytes_per_launch": 1697121833},
+                               "bytes_per_launch": 1698369371},
 }
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode tok/s + prefill tok/s (Mistral-7B shape) and % of HBM / MFMA roofline"
