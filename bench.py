@@ -238,8 +238,9 @@ def main():
                     help="only run three 1 GiB device-to-device copies (PMC byte-counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by sequence with no exchange; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (sharded, each GPU would "
+              "serve its own sequences with its own copy of the weights and no exchange between GPUs)",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
