@@ -46,7 +46,7 @@ enum {
     DEC_ERR_RANGE = -2,        /* the request does not fit the KV capacity or max sizes */
     DEC_ERR_NOMEM = -3,        /* workspace smaller than dec_workspace_bytes() */
     DEC_ERR_DEVICE = -4,       /* a HIP call or kernel failed */
-    DEC_ERR_UNSUPPORTED = -5   /* a shape this build's kernels do not handle */
+    DEC_ERR_UNSUPPORTED = -5   /* a shape the library's kernels do not handle */
 };
 
 enum { DEC_WEIGHT_BF16 = 0, DEC_WEIGHT_F32 = 1 };
