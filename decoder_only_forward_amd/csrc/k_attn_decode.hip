@@ -234,25 +234,39 @@ __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
         for (int i = 0; i < DPL; i++) acc[g][i] = 0.f;
     }
 
-    for (int base = beg; base < end; base += NG * NB) {
-        u32x4 kr[NB][NV], vr[NB][NV];
-        bool valid[NB];
+    // fp32 cache, groups of up to 4 heads: two stages of NS = NB/2 positions
+    // per lane group, software-pipelined: the next stage's K/V loads are issued
+    // before the current stage's arithmetic, so the stream stays in flight
+    // while it runs (the same registers as one batch of NB; measured 1.4 %
+    // faster per Mistral decode step at B = 32).  Otherwise (bf16 cache, wider
+    // groups, where it measured slower) one batch of NB positions at a time.
+    // The running maximum rescales the accumulators only when it grows.
+    constexpr bool PIPE = !KB && G <= 4;
+    constexpr int NS = PIPE ? NB / 2 : NB;
+    static_assert(!PIPE || NB % 2 == 0, "two stages of NB/2 positions");
+    const int span = NG * NS;
+    const int nstg = beg < end ? (end - beg + span - 1) / span : 0;
+    auto load = [&](u32x4 (&kr)[NS][NV], u32x4 (&vr)[NS][NV], int st) {
+        const int base = beg + st * span;
 #pragma unroll
-        for (int i = 0; i < NB; i++) {
+        for (int i = 0; i < NS; i++) {
             const int j = base + i * NG + gid;
-            valid[i] = j < end;
-            const int jj = valid[i] ? j : beg;
+            const int jj = j < end ? j : beg;   // rows past the range read the first row, masked below
             R::load(K + (size_t)jj * HD * R::ES, u, kr[i]);
         }
 #pragma unroll
-        for (int i = 0; i < NB; i++) {
+        for (int i = 0; i < NS; i++) {
             const int j = base + i * NG + gid;
-            const int jj = valid[i] ? j : beg;
+            const int jj = j < end ? j : beg;
             R::load(V + (size_t)jj * HD * R::ES, u, vr[i]);
         }
-        float s[NB][G];
+    };
+    auto step = [&](const u32x4 (&kr)[NS][NV], const u32x4 (&vr)[NS][NV], int st) {
+        const int base = beg + st * span;
+        float s[NS][G];
 #pragma unroll
-        for (int i = 0; i < NB; i++) {
+        for (int i = 0; i < NS; i++) {
+            const bool valid = base + i * NG + gid < end;
             if constexpr (KB) {
 #pragma unroll
                 for (int g = 0; g < G; g++) {
@@ -271,7 +285,7 @@ __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
                                                                 d, false);
                         }
                     d = group_sum<LP>(d);
-                    s[i][g] = valid[i] ? d : -INFINITY;
+                    s[i][g] = valid ? d : -INFINITY;
                 }
             } else {
                 float kf[DPL];
@@ -282,38 +296,58 @@ __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
 #pragma unroll
                     for (int e = 0; e < DPL; e++) d += qr[g][e] * kf[e];
                     d = group_sum<LP>(d);
-                    s[i][g] = valid[i] ? d : -INFINITY;
+                    s[i][g] = valid ? d : -INFINITY;
                 }
             }
         }
-        // online softmax update per head: s becomes the weights of this batch
+        // online softmax update per head: s becomes the weights of this stage
 #pragma unroll
         for (int g = 0; g < G; g++) {
             float mx = m[g];
 #pragma unroll
-            for (int i = 0; i < NB; i++) mx = fmaxf(mx, s[i][g]);
-            const bool none = mx == -INFINITY;  // no readable position yet
-            const float corr = none ? 1.f : fast_exp2(m[g] - mx);
-            m[g] = mx;
+            for (int i = 0; i < NS; i++) mx = fmaxf(mx, s[i][g]);
+            if (mx > m[g]) {
+                // the maximum grows (from -inf: everything so far is 0)
+                const float corr = fast_exp2(m[g] - mx);
+                l[g] *= corr;
+#pragma unroll
+                for (int e = 0; e < DPL; e++) acc[g][e] *= corr;
+                m[g] = mx;
+            }
             float ps = 0.f;
 #pragma unroll
-            for (int i = 0; i < NB; i++) {
-                s[i][g] = none ? 0.f : fast_exp2(s[i][g] - mx);
+            for (int i = 0; i < NS; i++) {
+                s[i][g] = s[i][g] == -INFINITY ? 0.f : fast_exp2(s[i][g] - m[g]);
                 ps += s[i][g];
             }
-            l[g] = l[g] * corr + ps;
-#pragma unroll
-            for (int e = 0; e < DPL; e++) acc[g][e] *= corr;
+            l[g] += ps;
         }
         // weighted V rows, one row live at a time
 #pragma unroll
-        for (int i = 0; i < NB; i++) {
+        for (int i = 0; i < NS; i++) {
             float vf[DPL];
             R::unpack(vr[i], vf);
 #pragma unroll
             for (int g = 0; g < G; g++)
 #pragma unroll
                 for (int e = 0; e < DPL; e++) acc[g][e] += s[i][g] * vf[e];
+        }
+    };
+    if constexpr (PIPE) {
+        u32x4 kA[NS][NV], vA[NS][NV], kB[NS][NV], vB[NS][NV];
+        if (nstg > 0) load(kA, vA, 0);
+        for (int st = 0; st < nstg; st += 2) {
+            if (st + 1 < nstg) load(kB, vB, st + 1);
+            step(kA, vA, st);
+            if (st + 1 >= nstg) break;
+            if (st + 2 < nstg) load(kA, vA, st + 2);
+            step(kB, vB, st + 1);
+        }
+    } else {
+        for (int st = 0; st < nstg; st++) {
+            u32x4 kr[NS][NV], vr[NS][NV];
+            load(kr, vr, st);
+            step(kr, vr, st);
         }
     }
 
