@@ -35,22 +35,22 @@ HBM_PEAK_GBS = 8000.0
 _COMMON = {"decoder_only_forward_amd/csrc/common.h":
            "34608c55f95e88c4c9dc0713feb1c89be769be0a7ff3031fa8e6327276c4082b"}
 _ATTN_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_decode.hip":
-                                 "d61d0a64f52f62e3dff981b9522676bb319802039ef285e9a2130fd9e149e6d6"})
+                                 "ca3d86f7b73f35f0be29369ea8bd3a6fb1fe27407b3b434c02588de0564dae0e"})
 _GEMV_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemv.hip":
                                  "e8b40692db620676cb8b5a5653b879158cc66c2d689ff00d7afbbe436a81511c"})
 _GEMM_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemm.hip":
                                  "2b5a11a5b66d407bcf10b64d4014b202650f0e067b23c57659c2175110e22eee"})
 MEASURED_TRAFFIC = {
     ("attn_decode_kernel", "fp32"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 1078805193},
+                                     "bytes_per_launch": 1078815360},
     ("attn_decode_kernel", "bf16"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 545077257},
+                                     "bytes_per_launch": 545073204},
     ("gemv_decode", "fp32"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                              "bytes_per_launch": 121760212},
+                              "bytes_per_launch": 121762993},
     ("gemv_decode", "bf16"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                              "bytes_per_launch": 121760212},
+                              "bytes_per_launch": 121762993},
     ("gemm_prefill", "fp32"): {"sources": _GEMM_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                               "bytes_per_launch": 1698369371},
+                               "bytes_per_launch": 1698152177},
 }
 BF16_PEAK_TFLOPS = 2500.0
 METRIC = "decode tok/s + prefill tok/s (Mistral-7B shape) and % of HBM / MFMA roofline"
