@@ -248,6 +248,15 @@ EXPORT void SYM(attention_prefill)(const real *q, const real *k, const real *v, 
 
 /* ---- model ------------------------------------------------------------ */
 
+/* The cache is a ring of max_seq slots written at pos % max_seq only when the
+   window equals max_seq (Pantheon, "Sliding Window (Mistral)": the ring holds
+   the window, min(pos+1, max_seq) positions readable).  A window longer than
+   max_seq can never bind inside max_seq positions: such a cache is linear and
+   full-causal with capacity max_seq (positions past it are a range error). */
+static int is_ring(const ocfg *c) {
+    return c->sliding_window > 0 && !c->window_by_mask && c->max_seq == c->sliding_window;
+}
+
 static int cfg_valid(const ocfg *c) {
     if (c->n_layers <= 0 || c->hidden <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 ||
         c->head_dim <= 0 || c->ffn_dim <= 0 || c->vocab <= 0 || c->max_seq <= 0 || c->n_slots <= 0)
@@ -310,8 +319,7 @@ EXPORT void SYM(kv_row)(void *h, int layer, int slot, int which, int pos, real *
     omodel *m = (omodel *)h;
     const ocfg *c = &m->c;
     size_t kv_dim = (size_t)c->n_kv_heads * c->head_dim;
-    int ring = c->sliding_window > 0 && !c->window_by_mask;
-    int s = ring ? pos % c->max_seq : pos;
+    int s = is_ring(c) ? pos % c->max_seq : pos;
     size_t off = (((size_t)layer * c->n_slots + slot) * c->max_seq + s) * kv_dim;
     memcpy(out, (which ? m->vcache : m->kcache) + off, kv_dim * sizeof(real));
 }
@@ -365,8 +373,7 @@ static void block_kv(omodel *m, int l, int slot, int pos, const real *x, scratch
         for (int i = 0; i < kvd; i++) s->k[i] = bf16_round(s->k[i]);
         for (int i = 0; i < kvd; i++) s->v[i] = bf16_round(s->v[i]);
     }
-    int ring = c->sliding_window > 0 && !c->window_by_mask;
-    int sl = ring ? pos % c->max_seq : pos;
+    int sl = is_ring(c) ? pos % c->max_seq : pos;
     size_t off = (((size_t)l * c->n_slots + slot) * c->max_seq + sl) * (size_t)kvd;
     memcpy(m->kcache + off, s->k, (size_t)kvd * sizeof(real));
     memcpy(m->vcache + off, s->v, (size_t)kvd * sizeof(real));
@@ -380,10 +387,10 @@ static void block_rest(omodel *m, int l, int slot, int pos, real *x, scratch *s,
     const olayer *L = &m->layers[l];
     int f32 = c->weight_f32, d = c->hidden, hd = c->head_dim, f = c->ffn_dim;
     int qd = c->n_heads * hd, kvd = c->n_kv_heads * hd;
-    int ring = c->sliding_window > 0 && !c->window_by_mask;
+    int ring = is_ring(c);
     int lo = 0;
     if (c->sliding_window > 0 && pos - c->sliding_window + 1 > 0) lo = pos - c->sliding_window + 1;
-    int cnt = pos - lo + 1;
+    int cnt = pos - lo + 1;  /* <= max_seq: a ring holds the window, a linear cache every position */
     for (int j = 0; j < cnt; j++) s->slots[j] = ring ? (lo + j) % c->max_seq : lo + j;
     const real *K = m->kcache + ((size_t)l * c->n_slots + slot) * c->max_seq * (size_t)kvd;
     const real *V = m->vcache + ((size_t)l * c->n_slots + slot) * c->max_seq * (size_t)kvd;
@@ -441,8 +448,7 @@ static void head_row(omodel *m, const real *x, scratch *s, real *logits) {
 }
 
 static int capacity_ok(const ocfg *c, int start_pos, int n) {
-    int ring = c->sliding_window > 0 && !c->window_by_mask;
-    if (ring) return 1;
+    if (is_ring(c)) return 1;
     return (long)start_pos + n <= (long)c->max_seq;
 }
 

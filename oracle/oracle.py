@@ -18,10 +18,16 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
-LIBS = {"f32": os.path.join(HERE, "liboracle32.so"), "f64": os.path.join(HERE, "liboracle64.so")}
+# ORACLE_LIB_DIR puts the built libraries elsewhere (a test that builds an
+# instrumented copy uses it); ORACLE_SANITIZE=address builds them with the
+# host compiler's AddressSanitizer (the process must preload libasan).
+_LIB_DIR = os.environ.get("ORACLE_LIB_DIR", HERE)
+LIBS = {"f32": os.path.join(_LIB_DIR, "liboracle32.so"), "f64": os.path.join(_LIB_DIR, "liboracle64.so")}
 # Plain IEEE arithmetic: no FMA contraction, no fast-math, no target-specific ISA.
 CFLAGS = ["-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off",
           "-fno-fast-math", "-fvisibility=hidden", "-lm"]
+if os.environ.get("ORACLE_SANITIZE") == "address":
+    CFLAGS = CFLAGS + ["-g", "-fno-omit-frame-pointer", "-fsanitize=address"]
 
 
 def build(force: bool = True) -> None:

@@ -292,6 +292,34 @@ def test_ring_cache_equals_masked_linear_cache():
     assert not np.array_equal(f["logits"][5:], r2["logits"][5:])
 
 
+def test_window_longer_than_capacity_is_a_linear_full_causal_cache():
+    """A window longer than max_seq cannot bind inside max_seq positions
+    (Pantheon "Sliding Window": readable min(pos + 1, max_seq)): the cache is
+    linear with capacity max_seq, equal to the unwindowed model below it, and a
+    call past it is a range error that changes nothing."""
+    cfg = configs.TINY.replace(name="tiny-w8-cap5", sliding_window=8, max_seq=5)
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 7, cfg.vocab).tolist()
+    w = synth.make_weights(cfg)
+    for kind in ("f32", "f64"):
+        m = O.OracleModel(cfg, w, kind=kind)
+        with pytest.raises(O.OracleError) as e:
+            m.prefill(toks)                        # 7 positions > capacity 5
+        assert e.value.code == -2 and m.length(0) == 0
+        r = m.prefill(toks[:3], rows=[0, 1, 2], capture=True)
+        d = [m.decode([toks[p]], [p], capture=True) for p in (3, 4)]
+        with pytest.raises(O.OracleError) as e:
+            m.decode([toks[5]], [5])
+        assert e.value.code == -2 and m.length(0) == 5
+        lin = O.OracleModel(configs.TINY, w, kind=kind, max_seq=5)
+        rl = lin.prefill(toks[:5], rows=list(range(5)), capture=True)
+        np.testing.assert_array_equal(r["logits"], rl["logits"][:3])
+        np.testing.assert_array_equal(d[0]["logits"][0], rl["logits"][3])
+        np.testing.assert_array_equal(d[1]["logits"][0], rl["logits"][4])
+        np.testing.assert_array_equal(d[1]["hidden"][:, 0], rl["hidden"][:, 4])
+        for p in range(5):
+            np.testing.assert_array_equal(m.kv_row(1, 0, 0, p), lin.kv_row(1, 0, 0, p))
+
+
 def test_window_at_least_length_is_no_window():
     cfg = configs.TINY
     wcfg = cfg.replace(sliding_window=16, max_seq=16)

@@ -1,0 +1,129 @@
+"""The oracle's composed layer against an independent float64 forward.
+
+`torch_ref64.forward` is written from the pages with torch library routines
+(F.linear on [out][in] matrices, F.rms_norm, F.silu, SDPA with enable_gqa and a
+causal / banded mask over a linear key list, complex-phasor RoPE, a stable sort
+for the top-k); it shares no code with oracle.c.  The oracle's float64
+instantiation must agree with it to rounding (rel 1e-12) on every layer's
+hidden state, every position's logits, and (MoE) the router logits and chosen
+experts, for prefill and for decode steps that follow it.  A mistake in the
+oracle's wiring (a transposed matrix, swapped gate and up, a dropped residual,
+the wrong head for a tied model, a mis-indexed ring slot, the window bound)
+moves these far beyond that.
+
+The fp32 oracle must stay within its own precision of the same reference.
+"""
+import numpy as np
+import pytest
+
+from decoder_only_forward_amd import configs, synth
+from oracle import oracle as O
+import torch_ref64 as R
+
+REL64 = 1e-12
+
+
+def _rel(a, b):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+CASES = [
+    (configs.TINY, 12),
+    (configs.TINY_MOE, 12),
+    (configs.TINY_BIAS, 12),          # q/k/v biases, tied LM head
+    (configs.TINY_BF16, 12),          # bf16 matrices
+    (configs.TINY_WINDOW, 16),        # W = 5 ring: wraps three times
+    (configs.TINY_HALF, 10),          # rotate-half pairing
+    (configs.TINY_LLAMA3, 10),        # llama3 frequency scaling, all three bands
+    (configs.TINY_KVBF16, 10),        # K/V rounded to bf16 at store
+    (configs.TINY.replace(name="tiny-window16-cap12", sliding_window=16, max_seq=12), 12),  # never wraps
+]
+
+
+@pytest.mark.parametrize("cfg,n", CASES, ids=lambda c: c.name if hasattr(c, "name") else str(c))
+def test_oracle64_prefill_and_decode_equal_library_forward(cfg, n):
+    w = synth.make_weights(cfg, seed=0)
+    toks = synth.tokens(0, synth.PROMPT_STREAM, n, cfg.vocab).tolist()
+    ref = R.forward(cfg, w, toks)
+    # prefill of the first half (every row), then one decode step per position
+    half = n // 2
+    m = O.OracleModel(cfg, w, kind="f64")
+    r = m.prefill(toks[:half], rows=list(range(half)), capture=True)
+    got_h = [r["hidden"]]
+    got_l = [r["logits"]]
+    got_ids = [r["ids"]] if cfg.n_experts else []
+    got_r = [r["router"]] if cfg.n_experts else []
+    for p in range(half, n):
+        d = m.decode([toks[p]], [p], capture=True)
+        got_h.append(d["hidden"])
+        got_l.append(d["logits"])
+        if cfg.n_experts:
+            got_ids.append(d["ids"])
+            got_r.append(d["router"])
+    hid = np.concatenate(got_h, axis=1)
+    logits = np.concatenate(got_l, axis=0)
+    for l in range(cfg.n_layers + 1):
+        assert _rel(hid[l], ref["hidden"][l]) < REL64, f"hidden after layer {l - 1}"
+    for t in range(n):
+        assert _rel(logits[t], ref["logits"][t]) < REL64, f"logits row {t}"
+    if cfg.n_experts:
+        ids = np.concatenate(got_ids, axis=1)
+        rl = np.concatenate(got_r, axis=1)
+        assert _rel(rl, ref["router"]) < REL64
+        assert np.array_equal(ids, ref["ids"])
+    # the greedy choice of every row, ties to the lowest id, equals the reference's
+    for t in range(n):
+        assert m.argmax(logits[t]) == int(np.argmax(ref["logits"][t]))
+
+
+@pytest.mark.parametrize("cfg", [configs.TINY, configs.TINY_MOE, configs.TINY_WINDOW], ids=lambda c: c.name)
+def test_oracle32_within_fp32_precision_of_library_forward(cfg):
+    w = synth.make_weights(cfg, seed=0)
+    n = 16 if cfg.sliding_window else 10
+    toks = synth.tokens(0, synth.PROMPT_STREAM, n, cfg.vocab).tolist()
+    ref = R.forward(cfg, w, toks)
+    r = O.OracleModel(cfg, w, kind="f32").prefill(toks, rows=list(range(n)), capture=True)
+    assert _rel(r["logits"], ref["logits"]) < 1e-5
+    assert _rel(r["hidden"], ref["hidden"]) < 1e-5
+
+
+def test_smollm2_width_two_layers_equal_library_forward():
+    """The SmolLM2 width (9/3 heads of 64, ffn 1536, tied 49152-entry head) with
+    two layers: the same composition at a real shape."""
+    cfg = configs.SMOLLM2.replace(name="smollm2-2l", n_layers=2)
+    w = synth.make_weights(cfg, seed=0)
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 6, cfg.vocab).tolist()
+    ref = R.forward(cfg, w, toks)
+    r = O.OracleModel(cfg, w, kind="f64").prefill(toks, rows=list(range(6)), capture=True)
+    assert _rel(r["hidden"], ref["hidden"]) < REL64
+    assert _rel(r["logits"], ref["logits"]) < REL64
+
+
+def test_reference_catches_planted_mistakes():
+    """The pin is sensitive: a model whose gate and up matrices are swapped, or
+    whose wo is transposed, differs from the reference by far more than 1e-12
+    (the planted change is made to the weights the oracle sees, on the CPU)."""
+    cfg = configs.TINY
+    w = synth.make_weights(cfg, seed=0)
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 6, cfg.vocab).tolist()
+    ref = R.forward(cfg, w, toks)
+    swapped = dict(w)
+    swapped["layers"] = [dict(L, w_gate=L["w_up"], w_up=L["w_gate"]) for L in w["layers"]]
+    r = O.OracleModel(cfg, swapped, kind="f64").prefill(toks, rows=list(range(6)))
+    assert _rel(r["logits"], ref["logits"]) > 1e-3
+    tr = dict(w)
+    tr["layers"] = [dict(L, wo=L["wo"].t().contiguous()) for L in w["layers"]]
+    r = O.OracleModel(cfg, tr, kind="f64").prefill(toks, rows=list(range(6)))
+    assert _rel(r["logits"], ref["logits"]) > 1e-3
+
+
+def test_argmax_ties_go_to_the_lowest_id():
+    for kind in ("f32", "f64"):
+        dt = O.np_dtype(kind)
+        L = O.lib(kind)
+        for row, want in (([1.0, 3.0, 3.0, 2.0], 1), ([0.0] * 7, 0), ([-5.0, -1.0, -2.0, -1.0], 1),
+                          ([2.0, 1.0, 2.0], 0), ([-np.inf, 4.0, 4.0], 1)):
+            a = np.ascontiguousarray(row, dtype=dt)
+            assert L.argmax(a.ctypes.data, a.size) == want, (kind, row)
