@@ -43,7 +43,13 @@ struct GraphEntry {
     hipGraphExec_t exec = nullptr;
     hipGraphNode_t root = nullptr;
     hipKernelNodeParams kp{};
+    unsigned long long used = 0;  // replay clock of the last use (least recently used is evicted)
 };
+
+// Captured steps kept per handle.  The attention split count follows the
+// context length, so one growing sequence meets a new shape every few hundred
+// positions; the oldest-used graph makes room beyond this many.
+constexpr size_t MAX_GRAPHS = 16;
 
 struct Plan {  // byte offsets into the workspace
     size_t kv_layer;        // elements of one layer's K (or V) cache
@@ -86,6 +92,7 @@ struct dec_model {
     hipStream_t cs = nullptr;
     hipEvent_t fence_in = nullptr, fence_out = nullptr;
     std::vector<GraphEntry> graphs;
+    unsigned long long graph_clock = 0;
     std::vector<std::pair<std::vector<long long>, int>> seen;  // shapes met once (captured on the second)
 };
 
@@ -511,6 +518,7 @@ unsigned timing_mask(const dec_model *m) {
 // Launch a captured step; its first node (the row setup) takes this step's rows,
 // token source and history row.
 int replay(dec_model *m, GraphEntry &g, const RowArgs &ra, const int32_t *src, int32_t *hist) {
+    g.used = ++m->graph_clock;
     int B = g.B;
     int32_t *tok = m->tok, *ps = m->pos, *sl = m->slot;
     void *args[] = {(void *)&ra, (void *)&B, (void *)&src, (void *)&hist, (void *)&tok, (void *)&ps, (void *)&sl};
@@ -564,6 +572,15 @@ GraphEntry *capture(dec_model *m, const RowArgs &ra, int B, int S, const int *po
         hipGraphInstantiate(&g.exec, graph, nullptr, nullptr, 0) != hipSuccess) {
         destroy_graph(g);
         return nullptr;
+    }
+    if (m->graphs.size() >= MAX_GRAPHS) {
+        // evict the least recently replayed graph (after the graph stream drains)
+        size_t lru = 0;
+        for (size_t i = 1; i < m->graphs.size(); i++)
+            if (m->graphs[i].used < m->graphs[lru].used) lru = i;
+        if (hipStreamSynchronize(m->cs) != hipSuccess) { destroy_graph(g); return nullptr; }
+        destroy_graph(m->graphs[lru]);
+        m->graphs.erase(m->graphs.begin() + (long)lru);
     }
     m->graphs.push_back(g);
     return &m->graphs.back();
@@ -798,7 +815,17 @@ int dec_decode_greedy(dec_handle h, int B, const int32_t *tokens, int steps, int
             const int S = attn_splits_for(h, B, hpos);
             for (auto &e : h->graphs)
                 if (e.B == B && e.S == S && e.logits == logits && e.greedy) g = &e;
-            if (!g && steps - s >= 2) g = capture(h, ra, B, S, hpos, logits, true);
+            if (!g && steps - s >= 2) {
+                // a shape whose capture failed once stays eager (no retry per step)
+                const std::vector<long long> key = {B, S, (long long)(uintptr_t)logits, -1};
+                bool failed = false;
+                for (auto &kv : h->seen)
+                    if (kv.first == key) failed = true;
+                if (!failed) {
+                    g = capture(h, ra, B, S, hpos, logits, true);
+                    if (!g) h->seen.push_back({key, 3});
+                }
+            }
         }
         if (g) {
             if (replay(h, *g, ra, src, hist) != DEC_OK) return DEC_ERR_DEVICE;

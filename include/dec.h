@@ -255,12 +255,14 @@ DEC_API int dec_timing_enable(dec_handle h, int kernel_class, int on);
 DEC_API int dec_timing_read(dec_handle h, int kernel_class, double *total_ms, int64_t *launches,
                     double *bytes, double *flops);
 
-/* Number of decode steps captured as HIP graphs so far.  A decode call runs its
-   first call of a given shape (batch, attention split count, logits buffer)
+/* Number of captured decode-step graphs the handle holds.  A decode call runs
+   its first call of a given shape (batch, attention split count, logits buffer)
    eagerly and captures the second; later calls of that shape replay the graph
    on an internal stream ordered after, and before, the caller's stream.
-   Results are identical either way.  While a test capture or per-kernel timing
-   is on, decode runs eagerly. */
+   Results are identical either way.  A handle keeps at most 16 graphs: a new
+   capture beyond that drops the least recently replayed one.  A shape whose
+   capture fails stays eager.  While a test capture or per-kernel timing is on,
+   decode runs eagerly. */
 DEC_API int dec_graph_count(dec_handle h);
 
 /* Text of a status code. */

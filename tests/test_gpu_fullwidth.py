@@ -123,3 +123,26 @@ def test_mistral_one_layer_llama3_scaling_and_half_pairing():
     cfg = configs.one_layer(configs.MISTRAL).replace(name="mistral-1l-llama3-half", rope_pairing=1,
                                                       rope_scaling=1, rope_orig_ctx=8192, rope_factor=8.0)
     _run(cfg, P=1024, B=2, steps=3, sample_rows=[0, 511, 1023], decode_rows=[1], sample_steps={0, 2})
+
+
+def test_qwen25_one_layer_decode_b1_after_2048():
+    """Qwen2.5-0.5B width at the workload's batch 1: decode at positions
+    2048.. reads 2049+ keys of one kv head for seven query heads, the new key's
+    slot inside one of the attention splits."""
+    cfg = configs.one_layer(configs.QWEN25)
+    _run(cfg, P=2048, B=1, steps=4, sample_rows=[2047], decode_rows=[0], sample_steps={0, 1, 3})
+
+
+def test_mixtral_one_layer_decode_b1_after_512():
+    """Mixtral-8x7B width at the workload's batch 1: each step's two experts
+    hold one row each in the grouped expert GEMV (K = 4096 and 14336)."""
+    cfg = configs.one_layer(configs.MIXTRAL)
+    _run(cfg, P=512, B=1, steps=3, sample_rows=[511], decode_rows=[0], sample_steps={0, 1, 2})
+
+
+def test_mistral_one_layer_decode_b32_at_full_ring():
+    """The Mistral-7B decode launch of the throughput workload: 32 rows, each
+    after a 4096-token prompt, so every row reads a full 4096-slot ring (one
+    attention split per row and kv head) and overwrites slot 0, then 1."""
+    cfg = configs.one_layer(configs.MISTRAL)
+    _run(cfg, P=4096, B=32, steps=2, sample_rows=[4095], decode_rows=[0, 31], sample_steps={0, 1})

@@ -10,6 +10,7 @@ import pytest
 import torch
 
 from decoder_only_forward_amd import configs, synth
+from oracle import oracle as O
 from parity_util import (Pair, check_argmax, check_experts, check_hidden, check_logits)
 
 pytestmark = pytest.mark.gpu
@@ -144,6 +145,36 @@ def test_smollm2_decode_b32():
             check_logits(g[b], r["logits"][b], f"row {b} step {s}")
             check_argmax(g[b], r["logits"][b], f"row {b} step {s}")
         nxt = [int(np.argmax(r["logits"][b])) for b in range(B)]
+
+
+def test_smollm2_decode_b32_after_prompt_128():
+    """The SmolLM2 workload's batch-32 decode at positions 128..255: 32 rows
+    each after a 128-token prompt, teacher-forced.  Every row is compared with
+    the oracle at the first two steps; rows 0, 15 and 31 at sampled steps up
+    to position 255 (the oracle recomputes a row as one prefill over its
+    prompt and teacher tokens, equal to per-token calls)."""
+    cfg = configs.SMOLLM2
+    B, P, steps = 32, 128, 128
+    pair = Pair(cfg, n_slots=B, max_prefill=P)
+    pr = synth.prompts(cfg, B, P)
+    teach = synth.prompts(cfg, B, steps, stream=synth.TEACHER_STREAM)
+    for b in range(B):
+        pair.gpu.prefill(pr[b].tolist(), seq=b)
+    lg = torch.empty((B, cfg.vocab), device="cuda")
+    sampled = {0: None, 1: None, 64: None, 127: None}
+    for s in range(steps):
+        pair.gpu.decode(teach[:, s].tolist(), [P + s] * B, logits=lg)
+        if s in sampled:
+            sampled[s] = lg.cpu().numpy()
+    for b in range(B):
+        long_row = b in (0, 15, 31)
+        st = sorted(sampled) if long_row else [0, 1]
+        seq = pr[b].tolist() + teach[b, :st[-1] + 1].tolist()
+        ora = O.OracleModel(cfg, pair.w, n_slots=1, max_seq=cfg.max_seq)
+        r = ora.prefill(seq, rows=[P + s for s in st], partial=True)
+        for i, s in enumerate(st):
+            check_logits(sampled[s][b], r["logits"][i], f"row {b} step {s}")
+            check_argmax(sampled[s][b], r["logits"][i], f"row {b} step {s}")
 
 
 def test_decode_graph_replay_is_bit_identical_to_eager():
