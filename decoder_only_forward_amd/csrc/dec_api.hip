@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "dec.h"
@@ -94,6 +95,7 @@ struct dec_model {
     std::vector<GraphEntry> graphs;
     unsigned long long graph_clock = 0;
     std::vector<std::pair<std::vector<long long>, int>> seen;  // shapes met once (captured on the second)
+    int static_dev = -1;    // >= 0: the workspace is that device's copy of `scratch`
 };
 
 namespace {
@@ -588,6 +590,22 @@ GraphEntry *capture(dec_model *m, const RowArgs &ra, int B, int S, const int *po
 
 }  // namespace
 
+namespace {
+
+// The workspace of handles made by dec_create_noalloc: a file-scope device
+// array, one copy per GPU the library runs on, held until the process ends.
+// Host code never passes `scratch` itself to a kernel or a copy (in host code
+// the name is a stand-in, not a device address): it takes each device's
+// address once from hipGetSymbolAddress and uses that.
+__device__ __align__(256) unsigned char scratch[DEC_NOALLOC_WORKSPACE_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[MAX_DEVICES] = {};   // per device: its copy's address
+bool g_scratch_busy[MAX_DEVICES] = {};   // per device: a live handle uses it
+
+}  // namespace
+
 extern "C" {
 
 size_t dec_workspace_bytes(const dec_config *cfg) {
@@ -686,7 +704,41 @@ void dec_destroy(dec_handle h) {
     if (h->fence_in) hipEventDestroy(h->fence_in);
     if (h->fence_out) hipEventDestroy(h->fence_out);
     if (h->cs) hipStreamDestroy(h->cs);
+    if (h->static_dev >= 0) {
+        std::lock_guard<std::mutex> lk(g_scratch_mu);
+        g_scratch_busy[h->static_dev] = false;
+    }
     delete h;
+}
+
+int dec_create_noalloc(const dec_config *cfg, const dec_weights *w, void *hip_stream, dec_handle *out) {
+    if (!out) return DEC_ERR_INVALID;
+    *out = nullptr;
+    const int vc = validate_cfg(cfg);
+    if (vc != DEC_OK) return vc;
+    Plan p;
+    plan(*cfg, p);
+    if (p.total > DEC_NOALLOC_WORKSPACE_BYTES) return DEC_ERR_NOMEM;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return DEC_ERR_DEVICE;
+    if (hip_stream) {  // the stream's kernels run on its device: it must be the current one
+        int sdev = -1;
+        if (hipStreamGetDevice((hipStream_t)hip_stream, &sdev) != hipSuccess) return DEC_ERR_DEVICE;
+        if (sdev != dev) return DEC_ERR_INVALID;
+    }
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return DEC_ERR_DEVICE;
+        g_scratch_ptr[dev] = ptr;
+    }
+    if (g_scratch_busy[dev]) return DEC_ERR_INVALID;  // one live handle per device
+    const int rc = dec_create(cfg, w, g_scratch_ptr[dev], DEC_NOALLOC_WORKSPACE_BYTES, hip_stream, out);
+    if (rc == DEC_OK) {
+        g_scratch_busy[dev] = true;
+        (*out)->static_dev = dev;
+    }
+    return rc;
 }
 
 int dec_prefill(dec_handle h, int seq, const int32_t *tokens, int n, int start_pos, float *logits) {

@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(HERE, "libdec.so")
 
 DEC_OK, DEC_ERR_INVALID, DEC_ERR_RANGE, DEC_ERR_NOMEM, DEC_ERR_DEVICE, DEC_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 DEC_K_GEMV, DEC_K_ATTN_DECODE, DEC_K_GEMM, DEC_K_ATTN_PREFILL = 0, 1, 2, 3
-EXPORTS = ("dec_workspace_bytes", "dec_create", "dec_destroy", "dec_prefill", "dec_prefill_ex", "dec_decode",
+DEC_NOALLOC_WORKSPACE_BYTES = 64 << 20
+EXPORTS = ("dec_workspace_bytes", "dec_create", "dec_create_noalloc", "dec_destroy", "dec_prefill", "dec_prefill_ex", "dec_decode",
            "dec_decode_greedy", "dec_kv_reset",
            "dec_graph_count", "dec_kv_length", "dec_greedy", "dec_sync", "dec_set_capture", "dec_timing_enable",
            "dec_timing_read", "dec_status_str")
@@ -70,6 +71,8 @@ def load():
     L.dec_create.restype = c_int
     L.dec_create.argtypes = [ctypes.POINTER(DecConfig), ctypes.POINTER(DecWeights), vp, ctypes.c_size_t, vp,
                              ctypes.POINTER(vp)]
+    L.dec_create_noalloc.restype = c_int
+    L.dec_create_noalloc.argtypes = [ctypes.POINTER(DecConfig), ctypes.POINTER(DecWeights), vp, ctypes.POINTER(vp)]
     L.dec_destroy.restype = None
     L.dec_destroy.argtypes = [vp]
     L.dec_prefill.restype = c_int
@@ -132,10 +135,13 @@ def _dptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 class DecModel:
     """One model bound to device weights (dict from synth.make_weights on
-    cuda), with its own workspace and KV cache of `max_batch` sequence slots."""
+    cuda), with its own workspace and KV cache of `max_batch` sequence slots.
+    noalloc=True makes the handle with dec_create_noalloc: the workspace is the
+    library's own device array and nothing is allocated here."""
 
     def __init__(self, cfg: ModelConfig, weights: dict, max_batch: int = 1, max_prefill: int = 1,
-                 max_seq: Optional[int] = None, stream: Optional[torch.cuda.Stream] = None):
+                 max_seq: Optional[int] = None, stream: Optional[torch.cuda.Stream] = None,
+                 noalloc: bool = False):
         self.L = load()
         self.cfg = cfg
         self.w = weights
@@ -144,7 +150,7 @@ class DecModel:
         nbytes = self.L.dec_workspace_bytes(ctypes.byref(self.ccfg))
         if nbytes == 0:
             raise DecError(DEC_ERR_INVALID, "dec_workspace_bytes")
-        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.workspace = None if noalloc else torch.empty(nbytes, dtype=torch.uint8, device="cuda")
         self.stream = stream if stream is not None else torch.cuda.current_stream()
         layers = (DecLayerWeights * cfg.n_layers)()
         for i, lw in enumerate(weights["layers"]):
@@ -154,10 +160,14 @@ class DecModel:
         self.cw = DecWeights(ctypes.sizeof(DecWeights), _dptr(weights["embed"]), _dptr(weights["out_norm"]),
                              _dptr(weights["lm_head"]), layers)
         h = ctypes.c_void_p()
-        rc = self.L.dec_create(ctypes.byref(self.ccfg), ctypes.byref(self.cw), _dptr(self.workspace), nbytes,
-                               ctypes.c_void_p(self.stream.cuda_stream), ctypes.byref(h))
+        if noalloc:
+            rc = self.L.dec_create_noalloc(ctypes.byref(self.ccfg), ctypes.byref(self.cw),
+                                           ctypes.c_void_p(self.stream.cuda_stream), ctypes.byref(h))
+        else:
+            rc = self.L.dec_create(ctypes.byref(self.ccfg), ctypes.byref(self.cw), _dptr(self.workspace), nbytes,
+                                   ctypes.c_void_p(self.stream.cuda_stream), ctypes.byref(h))
         if rc != DEC_OK:
-            raise DecError(rc, "dec_create")
+            raise DecError(rc, "dec_create_noalloc" if noalloc else "dec_create")
         self.h = h
 
     def close(self):

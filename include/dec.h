@@ -154,6 +154,28 @@ DEC_API size_t dec_workspace_bytes(const dec_config *cfg);
 DEC_API int dec_create(const dec_config *cfg, const dec_weights *w, void *workspace, size_t ws_bytes,
                void *hip_stream, dec_handle *out);
 
+/*
+ * dec_create for callers that cannot allocate device memory (code under HIP
+ * graph capture, serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, checks and handle as dec_create, but the workspace is the
+ * library's own file-scope device array of DEC_NOALLOC_WORKSPACE_BYTES (64 MiB;
+ * one copy per GPU, held until the process ends) instead of a caller buffer.
+ * Nothing is allocated on the device.  The handle's stream must belong to the
+ * current device (DEC_ERR_INVALID otherwise).
+ *   DEC_ERR_NOMEM:   dec_workspace_bytes(cfg) exceeds DEC_NOALLOC_WORKSPACE_BYTES
+ *                    (the tiny shapes fit, a SmolLM2-135M shape with up to 4
+ *                    slots of 256 positions and 128-token prefills fits).
+ *   DEC_ERR_INVALID: also when another handle made by this call is still alive
+ *                    on the same device: the array holds one handle's KV cache
+ *                    and activations, and two would overwrite each other.
+ * The array keeps whatever the last handle left in it; nothing in the library
+ * reads workspace memory before writing it (KV slots are read only below their
+ * committed length), so nothing needs clearing.  Calls that overlap on one
+ * GPU's array race.  dec_destroy frees the device's array for the next handle.
+ */
+#define DEC_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+DEC_API int dec_create_noalloc(const dec_config *cfg, const dec_weights *w, void *hip_stream, dec_handle *out);
+
 DEC_API void dec_destroy(dec_handle h);
 
 /*

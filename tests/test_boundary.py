@@ -137,3 +137,27 @@ def test_capacity_without_window_is_range_error():
     assert L.dec_prefill(h, 0, tok.ctypes.data, 17, 0, ctypes.c_void_p(0x7F0000000000)) == D.DEC_ERR_RANGE
     assert L.dec_kv_length(h, 0) == 0
     L.dec_destroy(h)
+
+
+def test_create_noalloc_checks_before_the_device():
+    """dec_create_noalloc refuses a workspace larger than its static array, and
+    a bad config, on the host before any device call."""
+    L = _lib()
+    fake = 0x7F0000000000
+    for cfg, mb, mp, want in ((configs.MISTRAL, 1, 64, D.DEC_ERR_NOMEM),
+                              (configs.SMOLLM2, 32, 128, D.DEC_ERR_NOMEM),
+                              (configs.TINY.replace(head_dim=15), 1, 8, D.DEC_ERR_INVALID)):
+        c = D.make_config(cfg, mb, mp)
+        need = L.dec_workspace_bytes(ctypes.byref(c))
+        assert want != D.DEC_ERR_NOMEM or need > D.DEC_NOALLOC_WORKSPACE_BYTES
+        layers = (D.DecLayerWeights * cfg.n_layers)()
+        for i in range(cfg.n_layers):
+            for f, _ in D.DecLayerWeights._fields_:
+                setattr(layers[i], f, fake)
+        w = D.DecWeights(ctypes.sizeof(D.DecWeights), fake, fake, fake, layers)
+        h = ctypes.c_void_p()
+        assert L.dec_create_noalloc(ctypes.byref(c), ctypes.byref(w), None, ctypes.byref(h)) == want
+        assert not h.value
+    c = D.make_config(configs.TINY, 1, 8)
+    assert L.dec_create_noalloc(ctypes.byref(c), None, None, None) == D.DEC_ERR_INVALID
+    assert D.workspace_bytes(configs.SMOLLM2, 4, 128) <= D.DEC_NOALLOC_WORKSPACE_BYTES
