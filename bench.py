@@ -13,7 +13,16 @@ Prefill tok/s = 4096 / (median prefill call).  The roofline objects come from
 a second timed region of K steps in which every GEMV and attention launch is
 bracketed by HIP events on the library's stream (those steps launch eagerly).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config mistral-7b]
+The other shapes' workloads follow in `workloads` (same method, each on its
+own seeded weights): SmolLM2-135M (prefill 128, decode B = 32 and 1 from
+position 128), Qwen2.5-0.5B (prefill 2048, decode B = 64 and 1 from 2048) and
+Mixtral-8x7B (prefill 512, decode B = 16 and 1 from 512).  Each decode carries
+the step's HBM roofline (algorithmic bytes of one step over its time: every
+weight read once, for MoE the experts the step's tokens chose, the readable
+K/V of every row, the K/V rows written, the logits) and its kernels' rooflines.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py --only qwen2.5-0.5b [--phase prefill|decode]   (one workload, for profiling)
 """
 from __future__ import annotations
 
@@ -53,6 +62,8 @@ MEASURED_TRAFFIC = {
                                "bytes_per_launch": 1698152177},
 }
 BF16_PEAK_TFLOPS = 2500.0
+# The other shapes' workloads: (decode batches, prompt length).
+OTHER = {"smollm2-135m": ((32, 1), 128), "qwen2.5-0.5b": ((64, 1), 2048), "mixtral-8x7b": ((16, 1), 512)}
 METRIC = "decode tok/s + prefill tok/s (Mistral-7B shape) and % of HBM / MFMA roofline"
 
 
@@ -73,25 +84,214 @@ def measured_traffic(kernel, workload):
     return m["bytes_per_launch"]
 
 
-def cpu_baseline(cfg, wd, steps=4):
-    """The oracle, untuned, on the host cores: greedy decode at B = 1 from an
-    empty cache (positions 0..steps-1) on the same model (weights copied to host)."""
+def cpu_baseline(cfg, wd, B=32, prefill_tokens=32):
+    """The oracle, untuned, on the host cores, on the same model (weights copied
+    to the host): one batched decode step of B rows (each row its first token,
+    so the rows read no cached context), then a prefill of the first
+    `prefill_tokens` tokens of the workload's prompt.  The oracle forwards one
+    row at a time, streaming every weight per row, so its rate hardly depends
+    on B; the 4096 cached positions the GPU's decode rows read would add about
+    8 % to its per-row work (attention 2 x 32 heads x 128 x 4096 products per
+    layer against 218 M weight products), which this bounded sample leaves out."""
     import numpy as np
+    from decoder_only_forward_amd import synth
     from oracle import oracle as O
     O.build(force=False)
     w = {k: (v.cpu() if v is not None else None) for k, v in wd.items() if k != "layers"}
     w["layers"] = [{k: v.cpu() for k, v in lw.items()} for lw in wd["layers"]]
-    ora = O.OracleModel(cfg, w, n_slots=1, max_seq=cfg.max_seq)
-    tok = 1
+    ora = O.OracleModel(cfg, w, n_slots=B, max_seq=cfg.max_seq)
+    toks = synth.prompts(cfg, B, 1)[:, 0].tolist()
     t0 = time.perf_counter()
-    for p in range(steps):
-        r = ora.decode([tok], [p])
-        tok = int(np.argmax(r["logits"][0]))
-    dt = time.perf_counter() - t0
+    ora.decode(toks, [0] * B)
+    dt_dec = time.perf_counter() - t0
+    ora.reset()
+    prompt = synth.prompts(cfg, 1, prefill_tokens)[0].tolist()
+    t0 = time.perf_counter()
+    ora.prefill(prompt)
+    dt_pre = time.perf_counter() - t0
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": steps / dt, "unit": "tok/s", "cores": threads, "kind": "oracle",
-            "sample": f"{cfg.name} full depth, decode B=1 at positions 0..{steps - 1} "
-                      f"({dt:.1f} s; the context is short, attention is <1% of the per-token work)"}
+    return {"value": round(B / dt_dec, 3), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "prefill_tok_s": round(prefill_tokens / dt_pre, 3),
+            "sample": f"{cfg.name} full depth: one decode step at B={B} from an empty cache ({dt_dec:.1f} s), "
+                      f"and a prefill of the prompt's first {prefill_tokens} tokens ({dt_pre:.1f} s)"}
+
+
+def decode_step_bytes(cfg, B, readable, experts_per_layer=None):
+    """Algorithmic HBM bytes of one decode step of B rows: every weight read once
+    (for MoE the router and the experts in use: `experts_per_layer`, default
+    min(E, B*k)), `readable` cached K/V positions summed over the rows, one K
+    and one V row written per row and layer, the logits written."""
+    d, q, kv, f, V, L = cfg.hidden, cfg.q_dim, cfg.kv_dim, cfg.ffn_dim, cfg.vocab, cfg.n_layers
+    wb = 4 if cfg.weight_dtype == 1 else 2
+    es = 2 if cfg.kv_bf16 else 4
+    attn = (2 * d * q + 2 * d * kv) * wb
+    if cfg.n_experts:
+        ex = experts_per_layer if experts_per_layer is not None else min(cfg.n_experts, B * cfg.top_k)
+        ffn = ex * 3 * d * f * wb + cfg.n_experts * d * wb
+    else:
+        ffn = 3 * d * f * wb
+    head = V * d * wb
+    return (L * (attn + ffn) + head + B * d * wb + L * 2 * kv * es * (readable + B) + B * V * 4)
+
+
+def prefill_weight_bytes(cfg, P):
+    """Weights one prefill of P tokens reads once (every expert a token chose;
+    a P-token MoE prefill touches min(E, P*k) experts a layer)."""
+    return decode_step_bytes(cfg, P, 0) - P * cfg.hidden * 2 - cfg.n_layers * 2 * cfg.kv_dim * (
+        2 if cfg.kv_bf16 else 4) * P - P * cfg.vocab * 4
+
+
+def _hbm(bytes_, ms):
+    ach = bytes_ / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(ach / HBM_PEAK_GBS, 4), "algorithmic_gb": round(bytes_ / 1e9, 4)}
+
+
+def _kernel_roof(t, bound):
+    if t["launches"] == 0 or t["ms"] <= 0:
+        return None
+    per = t["ms"] / t["launches"]
+    if bound == "hbm":
+        ach = t["bytes"] / t["launches"] / (per * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "avg_launch_us": round(per * 1e3, 2),
+                "launches": t["launches"]}
+    ach = t["flops"] / t["launches"] / (per * 1e-3) / 1e12
+    return {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(ach / BF16_PEAK_TFLOPS, 4), "avg_launch_us": round(per * 1e3, 2),
+            "launches": t["launches"]}
+
+
+def run_other(cfg, Bs, P, steps, warmup, phase="all"):
+    """One shape's workload: prefill P tokens into each of max(Bs) slots, then
+    batched greedy decode at each B in Bs (largest first; a smaller B reuses
+    slots 0..B-1 after re-prefilling them, so it also starts at position P)."""
+    import numpy as np
+    import torch
+    from decoder_only_forward_amd import synth
+    from decoder_only_forward_amd import dec as D
+
+    t0 = time.perf_counter()
+    wd = synth.make_weights(cfg, seed=0, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[{cfg.name}] weights {cfg.matrix_params() / 1e9:.2f} B params drawn in {time.perf_counter() - t0:.1f} s")
+    Bmax = max(Bs)
+    model = D.DecModel(cfg, wd, max_batch=Bmax, max_prefill=P)
+    prompts = synth.prompts(cfg, Bmax, P)
+    logits1 = torch.empty(cfg.vocab, device="cuda")
+    out = {"workload": f"{cfg.name}: prefill P={P} into {Bmax} slots; decode B={'/'.join(map(str, Bs))} "
+                       f"from position {P}", "layers": cfg.n_layers}
+
+    model.timing_enable(D.DEC_K_GEMM)
+    model.timing_enable(D.DEC_K_ATTN_PREFILL)
+    pre_ms = []
+    n_pre = Bmax if phase != "prefill" else min(Bmax, 3)
+    for b in range(n_pre):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        model.prefill(prompts[b].tolist(), seq=b, logits=logits1)
+        torch.cuda.synchronize()
+        pre_ms.append((time.perf_counter() - t) * 1e3)
+    gemm_t = model.timing_read(D.DEC_K_GEMM)
+    apre_t = model.timing_read(D.DEC_K_ATTN_PREFILL)
+    model.timing_enable(D.DEC_K_GEMM, False)
+    model.timing_enable(D.DEC_K_ATTN_PREFILL, False)
+    med = float(np.median(pre_ms[1:] if len(pre_ms) > 2 else pre_ms))
+    pre = {"P": P, "calls": len(pre_ms), "ms": round(med, 3), "tok_s": round(P / (med * 1e-3), 1),
+           "hbm": _hbm(prefill_weight_bytes(cfg, P), med),
+           "roofline_kernels": {"gemm_prefill": _kernel_roof(gemm_t, "mfma"),
+                                "attn_prefill": _kernel_roof(apre_t, "mfma")}}
+    if not cfg.n_experts:
+        # useful flops of the whole call: every layer's projections on P rows, the
+        # LM head on the last row, causal attention (2 hd products per head and key)
+        layer_params = cfg.matrix_params() - cfg.vocab * cfg.hidden * (1 if cfg.tied_embedding else 2)
+        flops = 2.0 * P * layer_params + 2.0 * cfg.vocab * cfg.hidden + \
+            cfg.n_layers * 2.0 * cfg.head_dim * cfg.n_heads * P * (P + 1)
+        pre["mfma_useful_whole_call"] = round(flops / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)
+    out["prefill"] = pre
+    log(f"[{cfg.name}] prefill P={P}: {med:.2f} ms median of {len(pre_ms)}, {P / (med * 1e-3):.0f} tok/s")
+    if phase == "prefill":
+        model.close()
+        return out
+
+    out["decode"] = {}
+    for B in sorted(Bs, reverse=True):
+        if B != Bmax:
+            for b in range(B):
+                model.reset(b)
+                model.prefill(prompts[b].tolist(), seq=b, logits=logits1)
+        lg = torch.empty((B, cfg.vocab), device="cuda")
+        toks = np.asarray(synth.prompts(cfg, B, 1, stream=synth.TEACHER_STREAM)[:, 0], dtype=np.int32)
+        experts = None
+        if cfg.n_experts:
+            # the experts one step's tokens choose (an eager step with the ids captured)
+            ids = torch.zeros((cfg.n_layers, B, cfg.top_k), dtype=torch.int32, device="cuda")
+            model.set_capture(None, ids, None)
+            pos = np.array([model.length(b) for b in range(B)], dtype=np.int32)
+            model.decode(toks, pos, logits=lg)
+            toks[:] = model.greedy(lg, B)
+            model.set_capture(None, None, None)
+            ic = ids.cpu().numpy()
+            experts = float(np.mean([len(np.unique(ic[l])) for l in range(cfg.n_layers)]))
+
+        def step():
+            pos = np.array([model.length(b) for b in range(B)], dtype=np.int32)
+            model.decode(toks, pos, logits=lg)
+            toks[:] = model.greedy(lg, B)
+            return pos
+
+        for _ in range(warmup):
+            step()
+        nbytes = 0.0
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for _ in range(steps):
+            pos = step()
+            nbytes += decode_step_bytes(cfg, B, int(np.sum(np.minimum(pos + 1, cfg.max_seq))), experts)
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t
+        model.timing_enable(D.DEC_K_GEMV)
+        model.timing_enable(D.DEC_K_ATTN_DECODE)
+        for _ in range(steps):
+            step()
+        gemv_t = model.timing_read(D.DEC_K_GEMV)
+        attn_t = model.timing_read(D.DEC_K_ATTN_DECODE)
+        model.timing_enable(D.DEC_K_GEMV, False)
+        model.timing_enable(D.DEC_K_ATTN_DECODE, False)
+        ms = dt * 1e3 / steps
+        r = {"tok_s": round(B * steps / dt, 2), "ms_per_step": round(ms, 4), "steps": steps,
+             "roofline": _hbm(nbytes / steps, ms),
+             "roofline_kernels": {"gemv_decode": _kernel_roof(gemv_t, "hbm"),
+                                  "attn_decode": _kernel_roof(attn_t, "hbm")}}
+        if experts is not None:
+            r["experts_per_layer"] = round(experts, 3)
+            r["note"] = ("step bytes count the experts the step's tokens chose; the GEMV object counts "
+                         "min(E, B*k) experts a layer")
+        out["decode"][f"b{B}"] = r
+        log(f"[{cfg.name}] decode B={B}: {ms:.3f} ms/step, {B * steps / dt:.1f} tok/s, "
+            f"{r['roofline']['frac'] * 100:.1f} % of HBM")
+    model.close()
+    del model, wd
+    torch.cuda.empty_cache()
+    return out
+
+
+def run_prefill_only(cfg, wd, P, calls=3):
+    """A few prefill calls of P tokens (for counter runs of the prefill kernels)."""
+    import torch
+    from decoder_only_forward_amd import synth
+    from decoder_only_forward_amd import dec as D
+    model = D.DecModel(cfg, wd, max_batch=1, max_prefill=P)
+    prompt = synth.prompts(cfg, 1, P)[0].tolist()
+    logits = torch.empty(cfg.vocab, device="cuda")
+    for i in range(calls):
+        model.reset()
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        model.prefill(prompt, logits=logits)
+        torch.cuda.synchronize()
+        log(f"[{cfg.name}] prefill P={P} call {i}: {(time.perf_counter() - t) * 1e3:.1f} ms")
+    model.close()
 
 
 def run_workload(cfg, wd, B, P, steps, warmup, small_batches=()):
@@ -231,11 +431,16 @@ def main():
     ap.add_argument("--batch", type=int, default=32)
     ap.add_argument("--prompt", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-steps", type=int, default=32)
+    ap.add_argument("--cpu-steps", type=int, default=32, help="prompt tokens the oracle's prefill sample takes")
     ap.add_argument("--kv", choices=("both", "fp32"), default="both",
                     help="both: the fp32-cache run gives `value`, a bf16-cache run is reported beside it")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="only run three 1 GiB device-to-device copies (PMC byte-counter calibration)")
+    ap.add_argument("--only", choices=sorted(OTHER) + ["mistral-7b"], default=None,
+                    help="run one workload alone and print its own JSON line (for profiling)")
+    ap.add_argument("--phase", choices=("all", "prefill", "decode"), default="all",
+                    help="with --only: stop after the prefill calls (a few of them) or run everything")
+    ap.add_argument("--no-other", action="store_true", help="skip the other shapes' workloads")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (sharded, each GPU would "
@@ -258,17 +463,25 @@ def main():
         print(json.dumps({"calibration": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30, "launches": 3}))
         return
 
+    torch.cuda.set_device(0)
+    if args.only and args.only != "mistral-7b":
+        Bs, P = OTHER[args.only]
+        print(json.dumps(run_other(configs.CONFIGS[args.only], Bs, P, args.steps, args.warmup, args.phase)),
+              flush=True)
+        return
     cfg = configs.CONFIGS[args.config]
     B, P = args.batch, args.prompt
-    torch.cuda.set_device(0)
     t0 = time.perf_counter()
     wd = synth.make_weights(cfg, seed=0, device="cuda")
     torch.cuda.synchronize()
     log(f"weights {cfg.matrix_params() / 1e9:.2f} B params drawn in {time.perf_counter() - t0:.1f} s")
 
+    if args.only == "mistral-7b" and args.phase == "prefill":
+        run_prefill_only(cfg, wd, P)
+        return
     main_run = run_workload(cfg, wd, B, P, args.steps, args.warmup, small_batches=(1, 8))
     bf16_run = None
-    if args.kv == "both":
+    if args.kv == "both" and not args.only:
         bf16_run = run_workload(cfg.replace(kv_bf16=True), wd, B, P, args.steps, args.warmup, small_batches=(1, 8))
     value, ms_step, pre_med = main_run["value"], main_run["ms_step"], main_run["pre_med"]
     gemm_t, apre_t, gemv_t, attn_t = main_run["gemm"], main_run["apre"], main_run["gemv"], main_run["attn"]
@@ -347,11 +560,18 @@ def main():
             "roofline_kernels": {"gemv_decode": roof(bf16_run["gemv"], "hbm", ("gemv_decode", "bf16")),
                                  "attn_prefill": roof(bf16_run["apre"], "mfma", passes=2)},
         }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not args.only:
         try:
-            out["cpu_baseline"] = cpu_baseline(cfg, wd, args.cpu_steps)
+            out["cpu_baseline"] = cpu_baseline(cfg, wd, B=B, prefill_tokens=args.cpu_steps)
         except Exception as e:  # the host may lack memory for the weights
             out["cpu_baseline"] = {"value": None, "error": str(e)}
+    if not args.no_other and not args.only:
+        del wd
+        torch.cuda.empty_cache()
+        out["workloads"] = {}
+        for name in ("smollm2-135m", "qwen2.5-0.5b", "mixtral-8x7b"):
+            Bs, Pn = OTHER[name]
+            out["workloads"][name] = run_other(configs.CONFIGS[name], Bs, Pn, args.steps, args.warmup)
     print(json.dumps(out), flush=True)
 
 
