@@ -441,6 +441,8 @@ def main():
     ap.add_argument("--phase", choices=("all", "prefill", "decode"), default="all",
                     help="with --only: stop after the prefill calls (a few of them) or run everything")
     ap.add_argument("--no-other", action="store_true", help="skip the other shapes' workloads")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="with --only: keep this many layers (the per-layer shapes unchanged), e.g. for counter runs")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (sharded, each GPU would "
@@ -464,12 +466,17 @@ def main():
         return
 
     torch.cuda.set_device(0)
+    def shape(name):
+        c = configs.CONFIGS[name]
+        if args.only and args.layers > 0:
+            c = c.replace(name=f"{c.name}-{args.layers}l", n_layers=args.layers)
+        return c
+
     if args.only and args.only != "mistral-7b":
         Bs, P = OTHER[args.only]
-        print(json.dumps(run_other(configs.CONFIGS[args.only], Bs, P, args.steps, args.warmup, args.phase)),
-              flush=True)
+        print(json.dumps(run_other(shape(args.only), Bs, P, args.steps, args.warmup, args.phase)), flush=True)
         return
-    cfg = configs.CONFIGS[args.config]
+    cfg = shape(args.only or args.config)
     B, P = args.batch, args.prompt
     t0 = time.perf_counter()
     wd = synth.make_weights(cfg, seed=0, device="cuda")

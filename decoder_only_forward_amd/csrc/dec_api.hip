@@ -134,9 +134,12 @@ bool plan(const dec_config &c, Plan &p) {
             const int TP = T * (int)k;
             need((int)E, (int)d, T);
             const int act = std::min<int>((int)E, TP);
-            // grouped projections: splits sized as for act experts' rows
+            // grouped projections: splits sized as for act experts' rows (GEMV),
+            // or as the grouped GEMM splits k for prefill rows
+            const bool f32w_ = c.weight_dtype == DEC_WEIGHT_F32;
             const int Sgu = (T <= 64) ? proj_splits(c, (int)(2 * F) * act, (int)d, T, true) : 1;
-            const int Sd = (T <= 64) ? proj_splits(c, (int)d * act, (int)F, T, true) : 1;
+            const int Sd = (T <= 64) ? proj_splits(c, (int)d * act, (int)F, T, true)
+                                     : (f32w_ ? 1 : gemm_grouped_splits_for((int)d, (int)F, TP, (int)E, 256));
             pf = std::max(pf, (size_t)Sgu * TP * 2 * F);
             pf = std::max(pf, (size_t)Sd * TP * d);
         } else {
@@ -353,10 +356,14 @@ Partials proj_grouped(dec_model *m, const WSeg *segs, int nseg, int K, int T, co
         tk.done((double)N * K * 2 * act + (double)TP * K * 4 + (double)TP * N * 4, 2.0 * TP * N * K);
         return Partials{m->part, S, (size_t)TP * N, N};
     }
+    // (the k split only where the partial buffer holds it: the workspace plan
+    // sized it for the projections of this shape)
+    int S = gemm_grouped_splits(N, K, TP, E);
+    if ((size_t)S * TP * N > m->pl.part_floats) S = 1;
     Tick tk(m, DEC_K_GEMM);
-    launch_gemm_grouped(m->st, segs, nseg, K, hi, lo, lda, T, E, m->moe_off, es, m->part, N);
+    launch_gemm_grouped(m->st, segs, nseg, K, hi, lo, lda, T, E, m->moe_off, es, m->part, N, S, (size_t)TP * N);
     tk.done((double)N * K * 2 * act + (double)TP * K * 4 + (double)TP * N * 4, 2.0 * TP * N * K);
-    return Partials{m->part, 1, 0, N};
+    return Partials{m->part, S, (size_t)TP * N, N};
 }
 
 void run_pass(dec_model *m, const Pass &ps) {
@@ -457,17 +464,36 @@ void run_pass(dec_model *m, const Pass &ps) {
                                  eps, ah, al, af, caph(l + 1), m->ssq);
         } else {
             const int E = c.n_experts, k = c.top_k, TP = T * k;
-            WSeg wr[1] = {{w.router, E}};
-            Partials pr = proj(m, wr, 1, d, T, ah, al, af, d);
-            launch_moe_route(st, T, E, k, pr, m->moe_ids, m->moe_w,
+            // router logits: the GEMV for decode rows and fp32 weights; prefill
+            // rows form them inside the top-k kernel
+            const bool in_kernel = !f32w && T > 64;
+            Partials pr{nullptr, 0, 0, 0};
+            if (!in_kernel) {
+                WSeg wr[1] = {{w.router, E}};
+                pr = proj(m, wr, 1, d, T, ah, al, af, d);
+            }
+            launch_moe_route(st, T, E, k, pr, in_kernel ? (const u16 *)w.router : nullptr, ah, al, d, d,
+                             m->moe_ids, m->moe_w,
                              m->cap_router ? m->cap_router + ((size_t)l * ps.cap_rows + ps.cap_row) * E : nullptr,
                              m->cap_ids ? m->cap_ids + ((size_t)l * ps.cap_rows + ps.cap_row) * k : nullptr,
                              m->moe_cnt, m->moe_off, m->moe_pairs);
             launch_moe_gather(st, T, k, d, m->moe_pairs, ah, al, af, f32w ? nullptr : m->g_hi,
                               f32w ? nullptr : m->g_lo, f32w ? m->g_f32 : nullptr);
             WSeg gu[2] = {{w.w_gate, F}, {w.w_up, F}};
-            Partials pg = proj_grouped(m, gu, 2, d, T, m->g_hi, m->g_lo, m->g_f32, d);
-            launch_silu_mul(st, TP, F, pg, ah, al, af);
+            // prefill rows: the grouped gate|up GEMM writes silu(gate) * up itself
+            bool fused = false;
+            if (!f32w && T > 64) {
+                Tick tk(m, DEC_K_GEMM);
+                const int act = std::min(E, TP);
+                fused = launch_gemm_grouped_silu(st, w.w_gate, w.w_up, F, d, m->g_hi, m->g_lo, d, T, E, m->moe_off,
+                                                 (size_t)F * d, ah, al, F);
+                if (fused) tk.done(2.0 * F * d * 2 * act + (double)TP * d * 4 + (double)TP * F * 4, 2.0 * TP * 2 * F * d);
+                else tk.cancel();
+            }
+            if (!fused) {
+                Partials pg = proj_grouped(m, gu, 2, d, T, m->g_hi, m->g_lo, m->g_f32, d);
+                launch_silu_mul(st, TP, F, pg, ah, al, af);
+            }
             WSeg wd[1] = {{w.w_down, d}};
             Partials pd = proj_grouped(m, wd, 1, F, T, ah, al, af, F);
             launch_moe_scatter(st, TP, d, m->moe_pairs, pd, m->moe_y);

@@ -27,9 +27,11 @@ struct GemmParams {
     const int32_t *grp_off;
     size_t expert_stride;
     // direct-to-LDS kernel, split over k: block z covers k in
-    // [z*kchunk, (z+1)*kchunk) and writes out + z*split_stride
+    // [z*kchunk, (z+1)*kchunk) and writes out + z*split_stride (grouped:
+    // z = expert * ksplit + split)
     int kchunk;
     size_t split_stride;
+    int ksplit;
 };
 
 // Block tile: BN = 256 output features (weight rows) x BM = 128 tokens x BK = 64.
@@ -233,6 +235,7 @@ void fill(GemmParams &p, const WSeg *segs, int nseg, int K, const u16 *a_hi, con
     p.ldo = ldo;
     p.kchunk = K;
     p.split_stride = 0;
+    p.ksplit = 1;
 }
 
 }  // namespace
@@ -248,6 +251,14 @@ void fill(GemmParams &p, const WSeg *segs, int nseg, int K, const u16 *a_hi, con
 // group fall in distinct banks.  The tile order gives each XCD a contiguous
 // range of feature tiles, walked four token tiles at a time, so the blocks an
 // XCD runs together share few weight and activation panels in its L2.
+//
+// The grouped (MoE prefill) form runs one grid slice per expert (times the k
+// splits): an expert's weights are segs[i].w + e * expert_stride and its rows
+// [offsets[e], offsets[e+1]).  The MFMAs of a wave's 32-token sub-tiles past
+// the expert's last row are skipped.  An expert's rows of a 512-token prefill
+// (about 128-190) fit one 256-token tile, so its weight panel streams from HBM
+// once; a 512-feature x 128-token tile, which fills its rows better but reads
+// the panel again for a second row tile, measured 17-20 % slower.
 namespace {
 
 constexpr int DBN = 256, DBM = 256, DBK = 32;
@@ -267,14 +278,22 @@ __device__ __forceinline__ int dswz(int r, int c) { return r * 4 + (c ^ ((r >> 2
 // features (wave wn: 64 of each, its MFMA row tiles 0, 1 gate and 2, 3 up), so
 // each lane holds gate and up of the same (feature, token) and the epilogue
 // writes silu(gate) * up as bf16 (hi, lo) pairs, row stride p.ldo.
-template <bool SILU>
+template <bool SILU, bool GROUPED>
 __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *__restrict__ s_hi,
                                                             u16 *__restrict__ s_lo) {
     extern __shared__ __attribute__((aligned(16))) u16 smem[];
     const int tid = threadIdx.x;
-    const int lane = tid % WAVE, wv = tid / WAVE;
+    const int lane = tid % WAVE, wv = __builtin_amdgcn_readfirstlane(tid / WAVE);
     const int wn = wv & 1, wm = wv >> 1;
-    const int M = p.M;
+    int M = p.M, mrow0 = 0, kz = blockIdx.z;
+    size_t wofs = 0;
+    if constexpr (GROUPED) {
+        const int e = blockIdx.z / p.ksplit;
+        kz = blockIdx.z - e * p.ksplit;
+        mrow0 = p.grp_off[e];
+        M = p.grp_off[e + 1] - mrow0;
+        wofs = (size_t)e * p.expert_stride;
+    }
 
     constexpr int FPT = SILU ? DBN / 2 : DBN;    // output features per block tile
     const int ntn = (p.N + FPT - 1) / FPT, ntm = gridDim.y;
@@ -299,12 +318,12 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
     const int m0 = tm * DBM;
     if (m0 >= M) return;
     const int n0 = tn * FPT;
-    const int kz0 = blockIdx.z * p.kchunk;   // 0 for SILU (one split)
+    const int kz0 = kz * p.kchunk;   // 0 for SILU (one split)
 
     // load instruction i (0, 1) of an operand array: wave wv fills the 1 KB slot
     // i*8 + wv, lane L the 16-byte chunk slot*64 + L, i.e. row r = chunk / 4 and
     // the logical chunk the swizzle stores there
-    const u16 *src[6];
+    const u16 *srcw[2], *srch[2], *srcl[2];
 #pragma unroll
     for (int i = 0; i < 2; i++) {
         const int P = (i * 8 + wv) * 64 + lane;
@@ -314,7 +333,7 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
             const int t = (r & 127) >> 5;
             int f = n0 + (r >> 7) * 64 + (t & 1) * 32 + (r & 31);
             f = f < p.N ? f : p.N - 1;
-            src[i] = (t < 2 ? p.w[0] : p.w[1]) + (size_t)f * p.K + kz0 + c * 8;
+            srcw[i] = (t < 2 ? p.w[0] : p.w[1]) + wofs + (size_t)f * p.K + kz0 + c * 8;
         } else {
             int n = n0 + r;
             n = n < p.N ? n : p.N - 1;
@@ -322,25 +341,33 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
             int start = 0;
             if (p.nseg > 1 && n >= p.seg_end[0]) { wp = p.w[1]; start = p.seg_end[0]; }
             if (p.nseg > 2 && n >= p.seg_end[1]) { wp = p.w[2]; start = p.seg_end[1]; }
-            src[i] = wp + (size_t)(n - start) * p.K + kz0 + c * 8;
+            srcw[i] = wp + wofs + (size_t)(n - start) * p.K + kz0 + c * 8;
         }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int P = (i * 8 + wv) * 64 + lane;
+        const int r = P >> 2, c = (P & 3) ^ ((r >> 2) & 3);
         int m = m0 + r;
         m = m < M ? m : M - 1;
-        src[2 + i] = p.a_hi + (size_t)m * p.lda + kz0 + c * 8;
-        src[4 + i] = p.a_lo + (size_t)m * p.lda + kz0 + c * 8;
+        srch[i] = p.a_hi + (size_t)(mrow0 + m) * p.lda + kz0 + c * 8;
+        srcl[i] = p.a_lo + (size_t)(mrow0 + m) * p.lda + kz0 + c * 8;
     }
     const int nk = min(p.kchunk, p.K - kz0) / DBK;
     // every iteration issues its loads (the last tile again past the end), so
     // the count of outstanding loads is the same everywhere
     auto load_tile = [&](int kt, int stage) {
         const int k0 = (kt < nk ? kt : nk - 1) * DBK;
+        LDS_AS u16 *base = (LDS_AS u16 *)smem + stage * DSTAGE;
 #pragma unroll
-        for (int a = 0; a < 3; a++)
-#pragma unroll
-            for (int i = 0; i < 2; i++) {
-                LDS_AS u16 *dst = (LDS_AS u16 *)smem + stage * DSTAGE + a * DARR + (i * 8 + wv) * 512;
-                __builtin_amdgcn_global_load_lds((const void *)(src[a * 2 + i] + k0), (LDS_AS void *)dst, 16, 0, 0);
-            }
+        for (int i = 0; i < 2; i++) {
+            const int slot = (i * 8 + wv) * 512;
+            __builtin_amdgcn_global_load_lds((const void *)(srcw[i] + k0), (LDS_AS void *)(base + slot), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(srch[i] + k0), (LDS_AS void *)(base + DARR + slot), 16,
+                                             0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(srcl[i] + k0), (LDS_AS void *)(base + 2 * DARR + slot),
+                                             16, 0, 0);
+        }
     };
 
     floatx16 acc[4][2];
@@ -352,6 +379,8 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
             for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
 
     const int r32 = lane & 31, c2 = lane >> 5;
+    // grouped: a wave's 32-token sub-tiles past the expert's last row multiply nothing
+    const bool live1 = !GROUPED || m0 + wm * 64 + 32 < M;
     auto compute = [&](int stage) {
         const u16 *sw = smem + stage * DSTAGE;
         const u16 *sh = sw + DARR;
@@ -369,13 +398,21 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
                 fh[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sh + off));
                 fl[j] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(sl + off));
             }
+            if (!GROUPED || live1) {
 #pragma unroll
-            for (int i = 0; i < 4; i++)
+                for (int i = 0; i < 4; i++)
 #pragma unroll
-                for (int j = 0; j < 2; j++) {
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fh[j], acc[i][j], 0, 0, 0);
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fl[j], acc[i][j], 0, 0, 0);
+                    for (int j = 0; j < 2; j++) {
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fh[j], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fl[j], acc[i][j], 0, 0, 0);
+                    }
+            } else if (m0 + wm * 64 < M) {
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fh[0], acc[i][0], 0, 0, 0);
+                    acc[i][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fw[i], fl[0], acc[i][0], 0, 0, 0);
                 }
+            }
         }
     };
 
@@ -418,7 +455,7 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
                         const float gt = acc[i][j][4 * g + e], up = acc[i + 2][j][4 * g + e];
                         split_bf16(gt / (1.0f + expf(-gt)) * up, hb[e], lb[e]);
                     }
-                    const size_t off = (size_t)m * p.ldo + f;
+                    const size_t off = (size_t)(mrow0 + m) * p.ldo + f;
                     if (f + 3 < p.N) {
                         *reinterpret_cast<uint2 *>(s_hi + off) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
                         *reinterpret_cast<uint2 *>(s_lo + off) = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
@@ -441,7 +478,7 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
         for (int j = 0; j < 2; j++) {
             const int m = m0 + wm * 64 + j * 32 + r32;
             if (m >= M) continue;
-            float *dst = p.out + blockIdx.z * p.split_stride + (size_t)m * p.ldo;
+            float *dst = p.out + kz * p.split_stride + (size_t)(mrow0 + m) * p.ldo;
 #pragma unroll
             for (int g = 0; g < 4; g++) {
                 const int n = n0 + wn * 128 + i * 32 + g * 8 + c2 * 4;
@@ -459,11 +496,13 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
 
 bool dma_lds_attr() {
     static int ok = -1;
-    if (ok < 0)
-        ok = hipFuncSetAttribute((const void *)gemm_dma_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)DMA_LDS) == hipSuccess &&
-             hipFuncSetAttribute((const void *)gemm_dma_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                 (int)DMA_LDS) == hipSuccess;
+    if (ok < 0) {
+        const void *ks[] = {(const void *)gemm_dma_kernel<false, false>, (const void *)gemm_dma_kernel<true, false>,
+                            (const void *)gemm_dma_kernel<false, true>, (const void *)gemm_dma_kernel<true, true>};
+        ok = 1;
+        for (const void *k : ks)
+            if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DMA_LDS) != hipSuccess) ok = 0;
+    }
     return ok == 1;
 }
 
@@ -496,8 +535,9 @@ void launch_gemm(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
         } else {
             ksplit = 1;
         }
-        hipLaunchKernelGGL(gemm_dma_kernel<false>, dim3((p.N + DBN - 1) / DBN, (M + DBM - 1) / DBM, ksplit),
-                           dim3(DNTHR), DMA_LDS, st, p, nullptr, nullptr);
+        hipLaunchKernelGGL((gemm_dma_kernel<false, false>),
+                           dim3((p.N + DBN - 1) / DBN, (M + DBM - 1) / DBM, ksplit), dim3(DNTHR), DMA_LDS, st, p,
+                           nullptr, nullptr);
         return;
     }
     // (one split: the caller asked for two only where gemm_splits gave two)
@@ -515,22 +555,64 @@ bool launch_gemm_silu(hipStream_t st, const void *w_gate, const void *w_up, int 
     WSeg segs[2] = {{w_gate, F}, {w_up, F}};
     fill(p, segs, 2, K, a_hi, a_lo, lda, M, nullptr, ldo);
     p.N = F;
-    hipLaunchKernelGGL(gemm_dma_kernel<true>, dim3((F + DBN / 2 - 1) / (DBN / 2), (M + DBM - 1) / DBM, 1), dim3(DNTHR),
-                       DMA_LDS, st, p, s_hi, s_lo);
+    hipLaunchKernelGGL((gemm_dma_kernel<true, false>),
+                       dim3((F + DBN / 2 - 1) / (DBN / 2), (M + DBM - 1) / DBM, 1), dim3(DNTHR), DMA_LDS, st, p,
+                       s_hi, s_lo);
     return true;
 }
 
+int gemm_grouped_splits_for(int N, int K, int pairs, int E, int cus) {
+    // an expert's row tiles number about pairs/E/256 rounded up: estimate the
+    // blocks with rows and split k until the grid fills the CUs one and a half times
+    if (K % DBK != 0) return 1;
+    const long ntn = (N + DBN - 1) / DBN;
+    const long blocks = ntn * ((pairs + DBM - 1) / DBM + E / 2);
+    int S = 1;
+    while (S < 4 && blocks * S * 2 < 3L * cus && K % (2 * S * DBK) == 0) S *= 2;
+    return S;
+}
+
+int gemm_grouped_splits(int N, int K, int pairs, int E) { return gemm_grouped_splits_for(N, K, pairs, E, num_cus()); }
+
 void launch_gemm_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi,
                          const u16 *a_lo, int lda, int max_rows, int E, const int32_t *offsets,
-                         size_t expert_stride, float *out, int ldo) {
+                         size_t expert_stride, float *out, int ldo, int ksplit, size_t split_stride) {
     if (max_rows <= 0) return;
     GemmParams p{};
     fill(p, segs, nseg, K, a_hi, a_lo, lda, max_rows, out, ldo);
     p.grp_off = offsets;
     p.expert_stride = expert_stride;
+    if (K % DBK == 0 && dma_lds_attr()) {
+        if (ksplit > 1 && K % (ksplit * DBK) == 0) {
+            p.kchunk = K / ksplit;
+            p.split_stride = split_stride;
+            p.ksplit = ksplit;
+        }
+        hipLaunchKernelGGL((gemm_dma_kernel<false, true>),
+                           dim3((p.N + DBN - 1) / DBN, (max_rows + DBM - 1) / DBM, E * p.ksplit), dim3(DNTHR),
+                           DMA_LDS, st, p, nullptr, nullptr);
+        return;
+    }
     dim3 grid((p.N + BN - 1) / BN, (max_rows + BM - 1) / BM, E);
     gemm_lds_attr();
     hipLaunchKernelGGL(gemm_kernel, grid, dim3(NTHR), GEMM_LDS, st, p);
+}
+
+bool launch_gemm_grouped_silu(hipStream_t st, const void *w_gate, const void *w_up, int F, int K, const u16 *a_hi,
+                              const u16 *a_lo, int lda, int max_rows, int E, const int32_t *offsets,
+                              size_t expert_stride, u16 *s_hi, u16 *s_lo, int ldo) {
+    if (max_rows <= 0) return true;
+    if (K % DBK != 0 || !dma_lds_attr()) return false;
+    GemmParams p{};
+    WSeg segs[2] = {{w_gate, F}, {w_up, F}};
+    fill(p, segs, 2, K, a_hi, a_lo, lda, max_rows, nullptr, ldo);
+    p.N = F;
+    p.grp_off = offsets;
+    p.expert_stride = expert_stride;
+    hipLaunchKernelGGL((gemm_dma_kernel<true, true>),
+                       dim3((F + DBN / 2 - 1) / (DBN / 2), (max_rows + DBM - 1) / DBM, E), dim3(DNTHR), DMA_LDS, st,
+                       p, s_hi, s_lo);
+    return true;
 }
 
 // ---- fp32 weights (the small fp32 model): one thread per output -----------

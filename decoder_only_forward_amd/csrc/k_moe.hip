@@ -14,60 +14,119 @@
 
 namespace {
 constexpr int MAXE = 32;
+constexpr int MAXK = 8;
 constexpr int NT = 256;
 
-__global__ void __launch_bounds__(NT) moe_route_kernel(int T, int E, int k, Partials lg, int32_t *__restrict__ ids,
-                                                       float *__restrict__ w, float *__restrict__ rcap,
-                                                       int32_t *__restrict__ icap, int32_t *__restrict__ counts,
-                                                       int32_t *__restrict__ offsets, int32_t *__restrict__ pairs) {
+// 1. Per token (one wave each): the router logits, from split partials (lg.p)
+//    or computed here from the router weights wr [E][d] (bf16) and the token's
+//    (hi, lo) activation row; then softmax over the E experts, the top k by
+//    repeated selection (ties to the lower id) and the weights p_e / (sum of the
+//    chosen p).  Every lane holds every logit; all register indices are
+//    compile-time constants.
+__global__ void __launch_bounds__(NT) moe_topk_kernel(int T, int E, int k, Partials lg, const u16 *__restrict__ wr,
+                                                      const u16 *__restrict__ ah, const u16 *__restrict__ al,
+                                                      int d, int lda, int32_t *__restrict__ ids,
+                                                      float *__restrict__ w, float *__restrict__ rcap,
+                                                      int32_t *__restrict__ icap) {
+    const int lane = threadIdx.x % WAVE;
+    const int t = blockIdx.x * (NT / WAVE) + threadIdx.x / WAVE;
+    if (t >= T) return;
+    float p[MAXE];
+    if (wr) {
+        float acc[MAXE];
+#pragma unroll
+        for (int e = 0; e < MAXE; e++) acc[e] = 0.f;
+        const u16 *xh = ah + (size_t)t * lda, *xl = al + (size_t)t * lda;
+        for (int k0 = lane * 8; k0 < d; k0 += WAVE * 8) {
+            const u32x4 h = *reinterpret_cast<const u32x4 *>(xh + k0);
+            const u32x4 l = *reinterpret_cast<const u32x4 *>(xl + k0);
+            float x[8];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                x[2 * i] = bf16_bits_to_f32(h[i] & 0xFFFFu) + bf16_bits_to_f32(l[i] & 0xFFFFu);
+                x[2 * i + 1] = __uint_as_float(h[i] & 0xFFFF0000u) + __uint_as_float(l[i] & 0xFFFF0000u);
+            }
+#pragma unroll
+            for (int e = 0; e < MAXE; e++) {
+                if (e >= E) break;
+                const u32x4 wv = *reinterpret_cast<const u32x4 *>(wr + (size_t)e * d + k0);
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    acc[e] += bf16_bits_to_f32(wv[i] & 0xFFFFu) * x[2 * i];
+                    acc[e] += __uint_as_float(wv[i] & 0xFFFF0000u) * x[2 * i + 1];
+                }
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < MAXE; e++) p[e] = e < E ? wave_sum(acc[e]) : -INFINITY;
+    } else {
+        const float v = lane < E ? sum_splits(lg.p, lg.S, lg.stride, (size_t)t * lg.ld + lane) : -INFINITY;
+#pragma unroll
+        for (int e = 0; e < MAXE; e++) p[e] = __shfl(v, e, WAVE);
+    }
+    if (rcap) {
+        float v = 0.f;
+#pragma unroll
+        for (int e = 0; e < MAXE; e++)
+            if (lane == e) v = p[e];
+        if (lane < E) rcap[(size_t)t * E + lane] = v;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < MAXE; e++)
+        if (e < E) mx = fmaxf(mx, p[e]);
+    float z = 0.f;
+#pragma unroll
+    for (int e = 0; e < MAXE; e++)
+        if (e < E) {
+            p[e] = expf(p[e] - mx);
+            z += p[e];
+        }
+#pragma unroll
+    for (int e = 0; e < MAXE; e++)
+        if (e < E) p[e] = p[e] / z;
+    uint32_t taken = 0;
+    float total = 0.f;
+    int sel[MAXK];
+    float selp[MAXK];
+#pragma unroll
+    for (int j = 0; j < MAXK; j++) {
+        sel[j] = 0;
+        selp[j] = 0.f;
+        if (j >= k) continue;
+        int best = -1;
+        float bv = 0.f;
+#pragma unroll
+        for (int e = 0; e < MAXE; e++)
+            if (e < E && !(taken >> e & 1u) && (best < 0 || p[e] > bv)) {
+                best = e;
+                bv = p[e];
+            }
+        taken |= 1u << best;
+        sel[j] = best;
+        selp[j] = bv;
+        total += bv;
+    }
+    if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < MAXK; j++)
+            if (j < k) {
+                ids[t * k + j] = sel[j];
+                w[t * k + j] = selp[j] / total;
+                if (icap) icap[t * k + j] = sel[j];
+            }
+    }
+}
+
+// 2. Stable counting sort of pair index t*k+j by expert (one block): thread
+//    i < nthr counts a contiguous run of pairs, the per-expert scan walks the
+//    runs in order (only as many runs as there are pairs, for short decode rows).
+__global__ void __launch_bounds__(NT) moe_sort_kernel(int n, int E, const int32_t *__restrict__ ids,
+                                                      int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                                                      int32_t *__restrict__ pairs) {
     __shared__ int cnt[NT][MAXE];
     __shared__ int off[MAXE + 1];
     const int tid = threadIdx.x;
-    // 1. per token: EP (E rounded up to a power of two) lanes per token, lane e
-    //    < E sums expert e's split partials, then the token's first lane forms
-    //    the softmax, the top-k and the renormalised weights
-    const int lane = tid % WAVE, wv = tid / WAVE;
-    int EP = 1;
-    while (EP < E) EP <<= 1;
-    const int tpw = WAVE / EP;   // tokens per wave per pass
-    for (int base = wv * tpw; base < T; base += (NT / WAVE) * tpw) {
-        const int t = base + lane / EP, e0 = lane % EP;
-        float v = -INFINITY;
-        if (t < T && e0 < E) {
-            v = sum_splits(lg.p, lg.S, lg.stride, (size_t)t * lg.ld + e0);
-            if (rcap) rcap[(size_t)t * E + e0] = v;
-        }
-        float p[MAXE];
-#pragma unroll
-        for (int e = 0; e < MAXE; e++) p[e] = __shfl(v, (lane & ~(EP - 1)) + (e & (EP - 1)), WAVE);
-        if (e0 != 0 || t >= T) continue;
-        float mx = -INFINITY;
-        for (int e = 0; e < E; e++) mx = fmaxf(mx, p[e]);
-        float z = 0.f;
-        for (int e = 0; e < E; e++) { p[e] = expf(p[e] - mx); z += p[e]; }
-        for (int e = 0; e < E; e++) p[e] = p[e] / z;
-        uint32_t taken = 0;
-        float total = 0.f;
-        int sel[MAXE];
-        for (int j = 0; j < k; j++) {
-            int best = -1;
-            for (int e = 0; e < E; e++)
-                if (!(taken >> e & 1u) && (best < 0 || p[e] > p[best])) best = e;
-            taken |= 1u << best;
-            sel[j] = best;
-            total += p[best];
-        }
-        for (int j = 0; j < k; j++) {
-            ids[t * k + j] = sel[j];
-            w[t * k + j] = p[sel[j]] / total;
-            if (icap) icap[t * k + j] = sel[j];
-        }
-    }
-    __syncthreads();
-    // 2. stable counting sort of pair index t*k+j by expert: thread i < nthr
-    //    counts a contiguous run of pairs, the per-expert scan walks the runs
-    //    in order (only as many runs as there are pairs, for short decode rows)
-    const int n = T * k;
     const int nthr = n < NT ? n : NT;
     const int per = (n + nthr - 1) / nthr;
     const int lo = tid * per, hi = min(n, lo + per);
@@ -127,11 +186,14 @@ __global__ void __launch_bounds__(256) moe_scatter_kernel(int d, const int32_t *
 }
 }  // namespace
 
-void launch_moe_route(hipStream_t st, int T, int E, int k, Partials logits, int32_t *ids, float *w,
-                      float *router_cap, int32_t *ids_cap, int32_t *counts, int32_t *offsets, int32_t *pairs) {
+void launch_moe_route(hipStream_t st, int T, int E, int k, Partials logits, const u16 *router_w, const u16 *a_hi,
+                      const u16 *a_lo, int d, int lda, int32_t *ids, float *w, float *router_cap, int32_t *ids_cap,
+                      int32_t *counts, int32_t *offsets, int32_t *pairs) {
     if (T <= 0) return;
-    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(NT), 0, st, T, E, k, logits, ids, w, router_cap, ids_cap,
-                       counts, offsets, pairs);
+    const int tpb = NT / WAVE;
+    hipLaunchKernelGGL(moe_topk_kernel, dim3((T + tpb - 1) / tpb), dim3(NT), 0, st, T, E, k, logits, router_w, a_hi,
+                       a_lo, d, lda, ids, w, router_cap, ids_cap);
+    hipLaunchKernelGGL(moe_sort_kernel, dim3(1), dim3(NT), 0, st, T * k, E, ids, counts, offsets, pairs);
 }
 
 void launch_moe_gather(hipStream_t st, int T, int k, int d, const int32_t *pairs, const u16 *src_hi,

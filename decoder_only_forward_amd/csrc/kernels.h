@@ -144,12 +144,14 @@ bool launch_attn_prefill_tiles(hipStream_t st, int T, int start_pos, int slot, c
                                const void *vc, int kv_bf16, int nh, int nkv, int hd, int max_seq, void *img,
                                u16 *o_hi, u16 *o_lo, float *o_f32);
 
-// MoE.  Router logits [T][E] (a GEMV/GEMM output) -> softmax, top-k by repeated
-// selection (ties to the lower id), renormalised weights; then the (token, slot)
-// pairs are grouped by expert (counting sort, stable in (token, slot) order).
-void launch_moe_route(hipStream_t st, int T, int E, int k, Partials logits, int32_t *ids,
-                      float *w, float *router_cap, int32_t *ids_cap, int32_t *counts,
-                      int32_t *offsets, int32_t *pairs);
+// MoE.  Router logits [T][E] -> softmax, top-k by repeated selection (ties to
+// the lower id), renormalised weights; then the (token, slot) pairs are grouped
+// by expert (counting sort, stable in (token, slot) order).  The logits are
+// the split partials `logits`, or, when router_w (bf16 [E][d]) is given, formed
+// here from it and the (hi, lo) activation rows a_hi/a_lo [T][lda].
+void launch_moe_route(hipStream_t st, int T, int E, int k, Partials logits, const u16 *router_w, const u16 *a_hi,
+                      const u16 *a_lo, int d, int lda, int32_t *ids, float *w, float *router_cap, int32_t *ids_cap,
+                      int32_t *counts, int32_t *offsets, int32_t *pairs);
 // Gather the normalised rows of the grouped pairs: dst[i] = src[pairs[i] / k].
 void launch_moe_gather(hipStream_t st, int T, int k, int d, const int32_t *pairs, const u16 *src_hi,
                        const u16 *src_lo, const float *src_f32, u16 *dst_hi, u16 *dst_lo, float *dst_f32);
@@ -160,9 +162,21 @@ void launch_moe_gather(hipStream_t st, int T, int k, int d, const int32_t *pairs
 void launch_gemv_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi,
                          const u16 *a_lo, int lda, int max_rows, int E, const int32_t *offsets,
                          size_t expert_stride, float *out, int ksplit, size_t split_stride, int ldo);
+// The MFMA form for prefill rows (bf16 weights): 256-feature x 256-row tiles
+// per expert, k split in `ksplit` partials (out + s*split_stride) as
+// gemm_grouped_splits(N, K, pairs, E) suggests for `pairs` grouped rows.
+int gemm_grouped_splits(int N, int K, int pairs, int E);
+int gemm_grouped_splits_for(int N, int K, int pairs, int E, int cus);   // host-only (the workspace plan)
 void launch_gemm_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi,
                          const u16 *a_lo, int lda, int max_rows, int E, const int32_t *offsets,
-                         size_t expert_stride, float *out, int ldo);
+                         size_t expert_stride, float *out, int ldo, int ksplit = 1, size_t split_stride = 0);
+// Grouped gate|up of the experts' SwiGLU with silu(gate) * up in the epilogue,
+// written as bf16 (hi, lo) pairs at the grouped rows of s_hi/s_lo [rows][ldo]
+// (F features).  Returns false (nothing launched) when K is not a multiple of
+// 32.  s_hi/s_lo must not alias a_hi/a_lo.
+bool launch_gemm_grouped_silu(hipStream_t st, const void *w_gate, const void *w_up, int F, int K, const u16 *a_hi,
+                              const u16 *a_lo, int lda, int max_rows, int E, const int32_t *offsets,
+                              size_t expert_stride, u16 *s_hi, u16 *s_lo, int ldo);
 void launch_gemm_f32_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, const float *a, int lda,
                              int max_rows, int E, const int32_t *offsets, size_t expert_stride, float *out,
                              int ldo);
