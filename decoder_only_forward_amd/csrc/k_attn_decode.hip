@@ -126,6 +126,51 @@ __device__ __forceinline__ void rope_pair(const RopeArgs &ra, int b, size_t row,
     }
 }
 
+// Prologue of a decode attention block: the G rotated queries of kv head kvh
+// into qs[g][HD] (unscaled), and, when the block's position range [beg, end)
+// holds the row's new slot, the rotated key and the value of the new position
+// stored in the cache.  Ends with a block barrier: the queries are complete in
+// LDS and the new K/V row is stored before any wave reads it.
+template <int HD, bool KB>
+__device__ __forceinline__ void decode_prologue(const RopeArgs &ra, void *kc, void *vc, int b, int kvh, int G, int nh,
+                                                int nkv, int p, int max_seq, int beg, int end, size_t head_base,
+                                                float (*qs)[HD]) {
+    constexpr int HALF = HD / 2;
+    const int sp = ra.ring ? p % max_seq : p;
+    const bool owner = sp >= beg && sp < end;
+    const int qd = nh * HD, kvd = nkv * HD;
+    const size_t row = (size_t)b * ra.qkv.ld;
+    const int nq = G * HALF, ntask = nq + (owner ? 2 * HALF : 0);
+    for (int task = threadIdx.x; task < ntask; task += blockDim.x) {
+        int e0, e1;
+        float x0, x1;
+        if (task < nq) {
+            const int h = kvh * G + task / HALF;
+            rope_pair<HD>(ra, b, row + (size_t)h * HD, task % HALF, true, ra.bq ? ra.bq + h * HD : nullptr, e0, e1,
+                          x0, x1);
+            qs[task / HALF][e0] = x0;
+            qs[task / HALF][e1] = x1;
+        } else {
+            const bool isk = task < nq + HALF;
+            const int i = isk ? task - nq : task - nq - HALF;
+            const float *bias = isk ? ra.bk : ra.bv;
+            rope_pair<HD>(ra, b, row + (isk ? qd : qd + kvd) + (size_t)kvh * HD, i, isk,
+                          bias ? bias + kvh * HD : nullptr, e0, e1, x0, x1);
+            const size_t at = (head_base + sp) * HD;
+            if constexpr (KB) {
+                u16 *c = static_cast<u16 *>(isk ? kc : vc) + at;
+                c[e0] = (u16)f32_to_bf16_bits(x0);
+                c[e1] = (u16)f32_to_bf16_bits(x1);
+            } else {
+                float *c = static_cast<float *>(isk ? kc : vc) + at;
+                c[e0] = x0;
+                c[e1] = x1;
+            }
+        }
+    }
+    __syncthreads();
+}
+
 template <int HD, int G, bool KB>
 __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
     RopeArgs ra, void *__restrict__ kc, void *__restrict__ vc,
@@ -161,47 +206,9 @@ __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
     const char *V = static_cast<const char *>(vc) + head_base * HD * R::ES;
     const float qscale = LOG2E / sqrtf((float)HD);
 
-    // Prologue: tasks [0, G*HD/2) are the query pairs of the group's heads;
-    // the block whose range holds the new slot also takes the HD/2 key pairs
-    // and HD/2 value pairs of the new position and stores them.
-    {
-        constexpr int HALF = HD / 2;
-        const int sp = ra.ring ? p % max_seq : p;
-        const bool owner = sp >= beg && sp < end;
-        const int qd = nh * HD, kvd = nkv * HD;
-        const size_t row = (size_t)b * ra.qkv.ld;
-        const int nq = G * HALF, ntask = nq + (owner ? 2 * HALF : 0);
-        for (int task = threadIdx.x; task < ntask; task += blockDim.x) {
-            int e0, e1;
-            float x0, x1;
-            if (task < nq) {
-                const int h = kvh * G + task / HALF;
-                rope_pair<HD>(ra, b, row + (size_t)h * HD, task % HALF, true, ra.bq ? ra.bq + h * HD : nullptr, e0,
-                              e1, x0, x1);
-                qs[task / HALF][e0] = x0;
-                qs[task / HALF][e1] = x1;
-            } else {
-                const bool isk = task < nq + HALF;
-                const int i = isk ? task - nq : task - nq - HALF;
-                const float *bias = isk ? ra.bk : ra.bv;
-                rope_pair<HD>(ra, b, row + (isk ? qd : qd + kvd) + (size_t)kvh * HD, i, isk,
-                              bias ? bias + kvh * HD : nullptr, e0, e1, x0, x1);
-                const size_t at = (head_base + sp) * HD;
-                if constexpr (KB) {
-                    u16 *c = static_cast<u16 *>(isk ? kc : vc) + at;
-                    c[e0] = (u16)f32_to_bf16_bits(x0);
-                    c[e1] = (u16)f32_to_bf16_bits(x1);
-                } else {
-                    float *c = static_cast<float *>(isk ? kc : vc) + at;
-                    c[e0] = x0;
-                    c[e1] = x1;
-                }
-            }
-        }
-        // the queries are complete in LDS, and the new K/V row is stored (the
-        // barrier's release waits for the stores) before any wave reads it
-        __syncthreads();
-    }
+    // Prologue: the group's rotated queries into LDS; the block whose range
+    // holds the new slot stores the new position's key and value first.
+    decode_prologue<HD, KB>(ra, kc, vc, b, kvh, G, nh, nkv, p, max_seq, beg, end, head_base, qs);
 
     // fp32 cache: q in fp32.  bf16 cache: q as (hi, lo) bf16 pairs matching
     // the packing of the key words, for v_dot2 against the stored keys.
@@ -404,6 +411,277 @@ __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
     }
 }
 
+// ---- MFMA form ----------------------------------------------------------------
+// The same split-KV online softmax with the products on MFMA, for groups of up
+// to 16 query heads, in blocks of NW = 4 or 8 waves.  A wave takes 16
+// positions at a time:
+//   S^T = K Q^T    one 16x16 tile (positions x heads, heads past G are zero
+//                  queries), 16x16x32 bf16 MFMAs over the head dims;
+//   O^T += V^T P^T 16x16x16 bf16 MFMAs, one per 16 output dims.
+// The score accumulator leaves lane (r, c) the scores of head r at positions
+// 4c..4c+3, which are exactly the four keys that lane feeds the P^T operand, so
+// the weights never move; every lane's output accumulators are also of head
+// r, so the online-softmax state is per lane (the maximum is reduced over the
+// four lanes of a head).  Each K/V row is read once for all heads of the
+// group.  V goes through a per-wave LDS stage to be read transposed.  fp32
+// operands are split into bf16 (hi, lo) pairs, products hi*hi + hi*lo + lo*hi
+// (a bf16 cache is exact: hi*hi + hi*lo with the query's pair), which keeps
+// fp32 accuracy.  The next chunk's K and V loads are issued before the current
+// chunk's arithmetic.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void split8(const float (&v)[8], bf16x8 &hi, bf16x8 &lo) {
+    u32x4 h, l;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        uint32_t a, bb;
+        split2_bf16(v[2 * j], v[2 * j + 1], a, bb);
+        h[j] = a;
+        l[j] = bb;
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
+__device__ __forceinline__ void split4(const float (&v)[4], s16x4 &hi, s16x4 &lo) {
+    uint32_t h0, l0, h1, l1;
+    split2_bf16(v[0], v[1], h0, l0);
+    split2_bf16(v[2], v[3], h1, l1);
+    hi = __builtin_bit_cast(s16x4, make_uint2(h0, h1));
+    lo = __builtin_bit_cast(s16x4, make_uint2(l0, l1));
+}
+
+// Order this wave's LDS writes before its other lanes' reads (and the reads
+// before the next writes): the waves of a block run different step counts,
+// so only the wave itself is synchronised.  A wave's LDS operations complete
+// in order, so waiting for them (lgkmcnt 0) and keeping the compiler from
+// moving memory accesses across is enough; the next step's global loads stay
+// in flight (a workgroup-scope fence would also wait for those).
+// s_waitcnt fields: vmcnt 63 (no wait), expcnt 7, lgkmcnt 0.
+constexpr int WAIT_LGKM0 = 0xF | (7 << 4) | (0 << 8) | (3 << 14);
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_s_waitcnt(WAIT_LGKM0);
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int HD, bool KB>
+struct MfmaDec {
+    static constexpr int ES = KB ? 2 : 4;
+    static constexpr int CH = 16;                 // positions per wave step
+    static constexpr int NKS = HD / 32;           // k steps of S^T = K Q^T
+    static constexpr int NDT = HD / 16;           // 16-dim tiles of O^T
+    static constexpr int KW = KB ? 1 : 2;         // 16-byte words of a lane's 8 key dims
+    static constexpr int RB = HD * ES;            // bytes of a cache row
+    static constexpr int PPR = RB / 16;           // 16-byte pieces per row
+    static constexpr int VW = CH * PPR / WAVE;    // V pieces per lane per step
+    static constexpr int VLD = KB ? HD + 8 : HD + 4;   // elements per staged V row
+    static constexpr int VSTAGE = CH * VLD * ES;  // bytes of one wave's V stage
+    static constexpr int SACC = 16 * HD * 4;      // bytes of one wave's output block (the merge)
+    static constexpr int WBYTES = VSTAGE > SACC ? VSTAGE : SACC;
+};
+
+template <int HD, bool KB, int NW>
+__global__ void __launch_bounds__(NW * 64, NW <= 4 ? 2 : 1) attn_decode_mfma_kernel(
+    RopeArgs ra, void *__restrict__ kc, void *__restrict__ vc, const int32_t *__restrict__ pos,
+    const int32_t *__restrict__ slot, int nh, int nkv, int max_seq, int splits, float *__restrict__ part,
+    u16 *__restrict__ o_hi, u16 *__restrict__ o_lo, float *__restrict__ o_f32) {
+    using C = MfmaDec<HD, KB>;
+    constexpr int CH = C::CH, NKS = C::NKS, NDT = C::NDT, KW = C::KW, VW = C::VW, PPR = C::PPR, ES = C::ES;
+    __shared__ float qs[16][HD];
+    __shared__ __attribute__((aligned(16))) char wst[NW][C::WBYTES];   // V stage, then the wave's outputs
+    __shared__ float sm[NW][16], sl[NW][16];
+
+    const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+    const int lane = threadIdx.x % WAVE, wv = threadIdx.x / WAVE;
+    const int r = lane & 15, c = lane >> 4;
+    const int G = nh / nkv;
+
+    const int p = pos[b];
+    const int nread = min(p + 1, max_seq);
+    const int chunk = (nread + splits - 1) / splits;
+    const int beg = split * chunk;
+    const int end = min(nread, beg + chunk);
+    const size_t head_base = ((size_t)slot[b] * nkv + kvh) * max_seq;
+    const char *K = static_cast<const char *>(kc) + head_base * C::RB;
+    const char *V = static_cast<const char *>(vc) + head_base * C::RB;
+
+    // The 8 dims lane (r, c) takes in k step ks (the same for the query and the
+    // keys; any assignment of dims to MFMA k slots gives the same dot product):
+    // with 4-byte elements, element e is dim 32ks + 16(e/4) + 4c + e%4, so one
+    // load instruction (16 bytes per lane) covers 64 contiguous bytes of each
+    // key row; with 2-byte elements dims 32ks + 8c + e do the same.
+    auto kdim = [&](int ks, int e) { return KB ? 32 * ks + 8 * c + e : 32 * ks + 16 * (e >> 2) + 4 * c + (e & 3); };
+    auto load = [&](int c0, u32x4 (&kr)[NKS][KW], u32x4 (&vr)[VW]) {
+        // A operand of S^T: lane (r, c) reads position c0 + r at dims kdim(ks, .)
+        const int j = c0 + r;
+        const char *krow = K + (size_t)(j < end ? j : beg) * C::RB;
+#pragma unroll
+        for (int ks = 0; ks < NKS; ks++)
+#pragma unroll
+            for (int w = 0; w < KW; w++) kr[ks][w] = ntload16(krow + kdim(ks, 4 * w) * ES);
+        // V rows c0 .. c0+15 as 16-byte pieces, piece f = q*64 + lane
+#pragma unroll
+        for (int q = 0; q < VW; q++) {
+            const int f = q * WAVE + lane, rr = f / PPR, cc = f % PPR;
+            const int jv = c0 + rr;
+            vr[q] = ntload16(V + (size_t)(jv < end ? jv : beg) * C::RB + 16 * cc);
+        }
+    };
+
+    for (int i = threadIdx.x; i < (16 - G) * HD; i += blockDim.x) qs[G + i / HD][i % HD] = 0.f;
+    decode_prologue<HD, KB>(ra, kc, vc, b, kvh, G, nh, nkv, p, max_seq, beg, end, head_base, qs);
+
+    // B operand of S^T: head r's query over kdim's dims, scaled for base-2
+    // softmax, as a bf16 (hi, lo) pair
+    const float qscale = LOG2E / sqrtf((float)HD);
+    bf16x8 qh[NKS], ql[NKS];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ks++) {
+        float v[8];
+#pragma unroll
+        for (int e = 0; e < 8; e++) v[e] = qs[r][kdim(ks, e)] * qscale;
+        split8(v, qh[ks], ql[ks]);
+    }
+
+    float m = -INFINITY, lsum = 0.f;
+    floatx4 o[NDT];
+#pragma unroll
+    for (int d = 0; d < NDT; d++) o[d] = (floatx4){0.f, 0.f, 0.f, 0.f};
+    char *vs = wst[wv];
+
+    auto step = [&](int c0, const u32x4 (&kr)[NKS][KW], const u32x4 (&vr)[VW]) {
+#pragma unroll
+        for (int q = 0; q < VW; q++) {
+            const int f = q * WAVE + lane, rr = f / PPR, cc = f % PPR;
+            *reinterpret_cast<u32x4 *>(vs + rr * C::VLD * ES + 16 * cc) = vr[q];
+        }
+        floatx4 st = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ks++) {
+            if constexpr (KB) {
+                const bf16x8 kh = __builtin_bit_cast(bf16x8, kr[ks][0]);
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[ks], st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[ks], st, 0, 0, 0);
+            } else {
+                float v[8];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    v[j] = __uint_as_float(kr[ks][0][j]);
+                    v[4 + j] = __uint_as_float(kr[ks][1][j]);
+                }
+                bf16x8 kh, kl;
+                split8(v, kh, kl);
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[ks], st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[ks], st, 0, 0, 0);
+                st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh[ks], st, 0, 0, 0);
+            }
+        }
+        // lane (r, c): head r, positions c0 + 4c + e; online softmax of head r
+        float sv[4], tmax = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            sv[e] = c0 + 4 * c + e < end ? st[e] : -INFINITY;
+            tmax = fmaxf(tmax, sv[e]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, WAVE));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, WAVE));
+        const float mnew = fmaxf(m, tmax);
+        const float corr = m == -INFINITY ? 0.f : fast_exp2(m - mnew);
+        float pw[4], ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            pw[e] = sv[e] == -INFINITY ? 0.f : fast_exp2(sv[e] - mnew);
+            ps += pw[e];
+        }
+        lsum = lsum * corr + ps;
+        m = mnew;
+        s16x4 ph, pl;
+        split4(pw, ph, pl);
+        wave_lds_sync();
+        // A operand of O^T: lane (r, c) holds dim 16d + r of positions 4c .. 4c+3
+#pragma unroll
+        for (int d = 0; d < NDT; d++) {
+#pragma unroll
+            for (int e = 0; e < 4; e++) o[d][e] *= corr;
+            if constexpr (KB) {
+                const u16 *vrow = reinterpret_cast<const u16 *>(vs) + 16 * d + r;
+                uint32_t w0 = (uint32_t)vrow[(4 * c) * C::VLD] | ((uint32_t)vrow[(4 * c + 1) * C::VLD] << 16);
+                uint32_t w1 = (uint32_t)vrow[(4 * c + 2) * C::VLD] | ((uint32_t)vrow[(4 * c + 3) * C::VLD] << 16);
+                const s16x4 vh = __builtin_bit_cast(s16x4, make_uint2(w0, w1));
+                o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vh, ph, o[d], 0, 0, 0);
+                o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vh, pl, o[d], 0, 0, 0);
+            } else {
+                const float *vrow = reinterpret_cast<const float *>(vs) + 16 * d + r;
+                float vv[4];
+#pragma unroll
+                for (int e = 0; e < 4; e++) vv[e] = vrow[(4 * c + e) * C::VLD];
+                s16x4 vh, vl;
+                split4(vv, vh, vl);
+                o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vh, ph, o[d], 0, 0, 0);
+                o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vh, pl, o[d], 0, 0, 0);
+                o[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vl, ph, o[d], 0, 0, 0);
+            }
+        }
+        wave_lds_sync();
+    };
+
+    // Steps of this wave: positions c0, c0 + NW*CH, ...  Each step's loads are
+    // issued unconditionally one step ahead (a step past the range reads valid
+    // rows and is never used), so the count of loads in flight is the same on
+    // every path and each step waits only for its own data.
+    {
+        int c0 = beg + wv * CH;
+        const int nsteps = c0 < end ? (end - c0 + NW * CH - 1) / (NW * CH) : 0;
+        u32x4 kA[NKS][KW], vA[VW], kB[NKS][KW], vB[VW];
+        if (nsteps > 0) load(c0, kA, vA);
+        for (int it = 0; it < nsteps; it += 2) {
+            load(c0 + NW * CH, kB, vB);
+            step(c0, kA, vA);
+            if (it + 1 >= nsteps) break;
+            load(c0 + 2 * NW * CH, kA, vA);
+            step(c0 + NW * CH, kB, vB);
+            c0 += 2 * NW * CH;
+        }
+    }
+    lsum += __shfl_xor(lsum, 16, WAVE);
+    lsum += __shfl_xor(lsum, 32, WAVE);
+
+    // merge the NW waves: each writes its state and its output block (which
+    // reuses its V stage) to LDS
+    __syncthreads();
+    float(*sacc)[HD] = reinterpret_cast<float(*)[HD]>(wst[wv]);
+    if (r < G) {
+        if (c == 0) { sm[wv][r] = m; sl[wv][r] = lsum; }
+#pragma unroll
+        for (int d = 0; d < NDT; d++)
+#pragma unroll
+            for (int e = 0; e < 4; e++) sacc[r][16 * d + 4 * c + e] = o[d][e];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < G * HD; idx += blockDim.x) {
+        const int g = idx / HD, i = idx % HD;
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < NW; w++) mx = fmaxf(mx, sm[w][g]);
+        float L = 0.f, A = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; w++) {
+            const float f = mx == -INFINITY ? 0.f : fast_exp2(sm[w][g] - mx);
+            L += sl[w][g] * f;
+            A += reinterpret_cast<const float(*)[HD]>(wst[w])[g][i] * f;
+        }
+        const int h = kvh * G + g;
+        if (splits == 1) {
+            store_out(A / L, (size_t)b * nh * HD + (size_t)h * HD + i, o_hi, o_lo, o_f32);
+        } else {
+            float *dst = part + (((size_t)b * nh + h) * splits + split) * (HD + 2);
+            dst[i] = A;
+            if (i == 0) { dst[HD] = mx; dst[HD + 1] = L; }
+        }
+    }
+}
+
 // Merge of the splits of one (row, head): weights f_s = 2^(m_s - max m) are
 // formed once per split into LDS; every output dim then sums its splits in
 // ascending order (the loads of a batch issued together), and so does the
@@ -474,9 +752,33 @@ const void *decode_probe_fn(int hd) {
                      : (const void *)attn_decode_kernel<16, 4, KB>;
 }
 
+// Groups of more than 4 heads, and any group with a bf16 cache (head_dim 64 or
+// 128), take the MFMA form: the lane-group kernel repeats each position's
+// softmax update and V products for every head of the group, which made a
+// 7-head group, and the bf16 cache's v_dot2 scores, ALU-limited.  An fp32
+// cache with up to 4 heads stays on the lane-group kernel, which streams it
+// at 83 % of HBM (its MFMA form at head_dim 128 spills registers).
+bool use_mfma(int hd, int G, int kv_bf16) {
+    return G <= 16 && (hd == 64 || hd == 128) && (G > 4 || kv_bf16);
+}
+
 }  // namespace
 
 int attn_decode_splits(int B, int nkv, int readable, int hd, int G, int kv_bf16) {
+    if (use_mfma(hd, G, kv_bf16)) {
+        // As many (row, kv head) pairs as CUs: one 8-wave block each, no merge
+        // (Mistral-7B, bf16 cache, B = 32: 84 us against 91 us for 4-wave
+        // blocks in two splits).  Fewer pairs: 4-wave blocks, two resident per
+        // CU, at least one 16-position step per wave (Qwen2.5-0.5B, B = 64:
+        // 36 us in four splits against 45 us for one 8-wave block per pair).
+        const int pairs = B * nkv;
+        if (pairs >= num_cus()) return 1;
+        int s = 2 * num_cus() / pairs;
+        const int maxs = readable / 64;
+        if (s > maxs) s = maxs;
+        if (s > 64) s = 64;
+        return s < 1 ? 1 : s;
+    }
     // One round of blocks.  An fp32 cache is streamed at the memory's rate by
     // one block per CU, and each extra split costs the merge pass; with a bf16
     // cache the lanes' arithmetic is the limit, so every resident-block slot is
@@ -506,6 +808,25 @@ void launch_attn_decode(hipStream_t st, int B, const RopeArgs &ra, void *kc, voi
     if (B <= 0) return;
     const int G = nh / nkv;
     dim3 grid(splits, nkv, B);
+    if (use_mfma(hd, G, kv_bf16)) {
+        // one 8-wave block per (row, kv head) when the pairs fill the CUs
+        // (attn_decode_splits then gives one split), else 4-wave blocks
+        const bool wide = splits == 1 && B * nkv >= num_cus();
+#define MD(HD, KB, NW) hipLaunchKernelGGL((attn_decode_mfma_kernel<HD, KB, NW>), grid, dim3(NW * 64), 0, st, ra, kc, \
+                                          vc, pos, slot, nh, nkv, max_seq, splits, part, o_hi, o_lo, o_f32)
+        if (kv_bf16) {
+            if (hd == 128) { if (wide) MD(128, true, 8); else MD(128, true, 4); }
+            else { if (wide) MD(64, true, 8); else MD(64, true, 4); }
+        } else {
+            if (hd == 128) { if (wide) MD(128, false, 8); else MD(128, false, 4); }
+            else { if (wide) MD(64, false, 8); else MD(64, false, 4); }
+        }
+#undef MD
+        if (splits > 1)
+            hipLaunchKernelGGL(attn_merge_kernel, dim3(nh, B), dim3(hd), 0, st, nh, hd, splits, part, o_hi, o_lo,
+                               o_f32);
+        return;
+    }
 #define LD(HD, KB) launch_decode_hd<HD, KB>(st, G, grid, ra, kc, vc, pos, slot, nh, nkv, max_seq, splits, part, \
                                             o_hi, o_lo, o_f32)
     if (kv_bf16) {
