@@ -327,9 +327,11 @@ Partials proj(dec_model *m, const WSeg *segs, int nseg, int K, int T, const u16 
         tk.done((double)N * K * 2 + (double)T * K * 4 + (double)T * N * 4, 2.0 * T * N * K);
         return Partials{m->part, S, (size_t)T * N, N};
     }
-    // into the partial buffer, a grid with a half-empty last round is split over k
+    // into the partial buffer, a grid with a half-empty last round, or of fewer
+    // tiles than CUs, is split over k (where the buffer holds the splits)
     const size_t tn = (size_t)T * N;
-    const int S = (!out && 2 * tn <= m->pl.part_floats) ? gemm_splits(N, K, T) : 1;
+    int S = out ? 1 : gemm_splits(N, K, T);
+    if ((size_t)S * tn > m->pl.part_floats) S = 1;
     Tick tk(m, DEC_K_GEMM);
     launch_gemm(m->st, segs, nseg, K, hi, lo, lda, T, dst, N, S, tn);
     tk.done((double)N * K * 2 + (double)T * K * 4 + (double)T * N * 4, 2.0 * T * N * K);

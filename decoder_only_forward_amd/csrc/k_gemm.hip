@@ -509,13 +509,34 @@ bool dma_lds_attr() {
 }  // namespace
 
 int gemm_splits_for(int N, int K, int M, int cus) {
-    // grids of at least one 256 x 256 tile per CU take the direct-to-LDS
+    // Grids of at least one 256 x 256 tile per CU take the direct-to-LDS
     // kernel; one whose last round is at most half full (1.5 rounds of q+k+v
-    // at 4096 tokens) is split in two over k, which evens the rounds
+    // at 4096 tokens) is split in two over k, which evens the rounds.
+    if (K % DBK != 0) return 1;
     const long nb = (long)((N + DBN - 1) / DBN) * ((M + DBM - 1) / DBM);
-    if (K % (2 * DBK) != 0 || nb < cus) return 1;
-    const long r1 = (nb + cus - 1) / cus, r2 = (2 * nb + cus - 1) / cus;
-    return r2 < 2 * r1 ? 2 : 1;
+    const int kt = K / DBK;
+    if (nb >= cus) {
+        if (kt % 2) return 1;
+        const long r1 = (nb + cus - 1) / cus, r2 = (2 * nb + cus - 1) / cus;
+        return r2 < 2 * r1 ? 2 : 1;
+    }
+    // A grid of fewer tiles than CUs (the projections of a small model, or of
+    // a few hundred tokens) is split over k where that pays: each split
+    // shortens every block's k walk (rounds x k-tiles per split, ~1.6 us per
+    // k-tile), and each split past the first writes one more fp32 partial of
+    // the output that the consumer reads back (M x N x 8 bytes at ~5 TB/s).
+    // Splits keep at least 4 k-tiles.  E.g. Qwen2.5-0.5B at 2048 tokens: q+k+v
+    // and o in 4 splits, down (K = 4864) in 8.
+    const double tk = 1.6e-6, extra = (double)M * N * 8.0 / 5e12;
+    int best = 1;
+    double bt = (double)kt * tk;
+    for (int s = 2; s <= 16 && kt / s >= 4; s++) {
+        if (kt % s) continue;
+        const double rounds = (double)((nb * s + cus - 1) / cus);
+        const double t = rounds * (kt / s) * tk + (s - 1) * extra;
+        if (t < bt) { bt = t; best = s; }
+    }
+    return best;
 }
 
 int gemm_splits(int N, int K, int M) { return gemm_splits_for(N, K, M, num_cus()); }
@@ -528,9 +549,9 @@ void launch_gemm(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
     // grids of at least one 256 x 256 tile per CU take the direct-to-LDS kernel;
     // smaller ones keep more, smaller blocks
     const long big = (long)((p.N + DBN - 1) / DBN) * ((M + DBM - 1) / DBM);
-    if (K % DBK == 0 && big >= num_cus() && dma_lds_attr()) {
-        if (ksplit == 2 && K % (2 * DBK) == 0) {
-            p.kchunk = K / 2;
+    if (K % DBK == 0 && (big >= num_cus() || ksplit > 1) && dma_lds_attr()) {
+        if (ksplit > 1 && K % (ksplit * DBK) == 0) {
+            p.kchunk = K / ksplit;
             p.split_stride = split_stride;
         } else {
             ksplit = 1;
@@ -540,7 +561,7 @@ void launch_gemm(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
                            nullptr, nullptr);
         return;
     }
-    // (one split: the caller asked for two only where gemm_splits gave two)
+    // (one split: the caller asks for more only where gemm_splits gave them)
     dim3 grid((p.N + BN - 1) / BN, (M + BM - 1) / BM, 1);
     gemm_lds_attr();
     hipLaunchKernelGGL(gemm_kernel, grid, dim3(NTHR), GEMM_LDS, st, p);

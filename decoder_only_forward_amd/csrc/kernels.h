@@ -73,8 +73,9 @@ void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
                  int lda, int B, float *out, int ksplit, size_t split_stride, int ldo);
 
 // Prefill projection, bf16 weights, MFMA: out[m][n] = sum_k (a_hi+a_lo)[m][k] W[n][k].
-// gemm_splits(N, K, M) is 1 or 2: with 2, launch_gemm writes two k-split
-// partials, the second at out + split_stride (the consumer sums them).
+// gemm_splits(N, K, M) gives the k splits to launch with (1 to 16): with S > 1,
+// launch_gemm writes S k-split partials, split s at out + s*split_stride (the
+// consumer sums them).
 // gemm_splits_for takes the CU count (host-only use: the workspace plan).
 int gemm_splits(int N, int K, int M);
 int gemm_splits_for(int N, int K, int M, int cus);
