@@ -44,22 +44,39 @@ HBM_PEAK_GBS = 8000.0
 _COMMON = {"decoder_only_forward_amd/csrc/common.h":
            "34608c55f95e88c4c9dc0713feb1c89be769be0a7ff3031fa8e6327276c4082b"}
 _ATTN_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_decode.hip":
-                                 "ca3d86f7b73f35f0be29369ea8bd3a6fb1fe27407b3b434c02588de0564dae0e"})
+                                 "cae52ed058060b38e445bdb8323692f2f7481e38ec54819afc64a7fc8f14e507"})
 _GEMV_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemv.hip":
                                  "e8b40692db620676cb8b5a5653b879158cc66c2d689ff00d7afbbe436a81511c"})
 _GEMM_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemm.hip":
-                                 "2b5a11a5b66d407bcf10b64d4014b202650f0e067b23c57659c2175110e22eee"})
+                                 "35914c3a9630eec4fc2e1bac9079f6d5b6dfed7296b837f1545a2752e3ee4509"})
+_TILES_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_prefill_tiles.hip":
+                                  "047e445f50cff41f139b69e5a72454f020bc746fed7ef71329edd1089737b1ae"})
 MEASURED_TRAFFIC = {
+    # B = 32 launches: the lane-group kernel (fp32 cache), the MFMA kernel in
+    # 8-wave blocks (bf16 cache)
     ("attn_decode_kernel", "fp32"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 1078815360},
-    ("attn_decode_kernel", "bf16"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 545073204},
+                                     "bytes_per_launch": 1078824772},
+    ("attn_decode_mfma_kernel", "bf16"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
+                                          "bytes_per_launch": 541894295},
     ("gemv_decode", "fp32"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
                               "bytes_per_launch": 121762993},
     ("gemv_decode", "bf16"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
                               "bytes_per_launch": 121762993},
     ("gemm_prefill", "fp32"): {"sources": _GEMM_SOURCES, "workload": ("mistral-7b", 32, 4096),
                                "bytes_per_launch": 1698152177},
+}
+# MFMA counters of the prefill kernels (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
+# GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES): busy = MFMA-busy
+# SIMD cycles over all SIMD cycles of the launch (GRBM_GUI_ACTIVE / 8 XCDs x
+# 1024 SIMDs); executed = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 flops per launch
+# time, against 2.5 PFLOP/s; clock = GRBM_GUI_ACTIVE / 8 per launch time.  The
+# projections are the time-weighted mean over one prefill's mix (q+k+v, o,
+# gate|up, down); reported only while the sources hash to the profiled ones.
+MEASURED_MFMA = {
+    ("gemm_prefill", "fp32"): {"sources": _GEMM_SOURCES, "workload": ("mistral-7b", 32, 4096),
+                               "busy": 0.592, "executed_frac": 0.470, "clock_ghz": 1.90},
+    ("attn_prefill", "fp32"): {"sources": _TILES_SOURCES, "workload": ("mistral-7b", 32, 4096),
+                               "busy": 0.467, "executed_frac": 0.384, "clock_ghz": 1.96},
 }
 BF16_PEAK_TFLOPS = 2500.0
 # The other shapes' workloads: (decode batches, prompt length).
@@ -71,17 +88,31 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(kernel, workload):
-    """kernel: (name, cache type); workload: (config name, batch, prompt)."""
+def _measured(table, kernel, workload):
+    """The table's entry for kernel (name, cache type) on workload (config name,
+    batch, prompt), while the kernel's sources hash to the profiled ones."""
     import hashlib
-    m = MEASURED_TRAFFIC.get(kernel)
+    m = table.get(kernel)
     if not m or m["workload"] != workload:
         return None
     for rel, sha in m["sources"].items():
         with open(os.path.join(ROOT, rel), "rb") as f:
             if hashlib.sha256(f.read()).hexdigest() != sha:
                 return None
-    return m["bytes_per_launch"]
+    return m
+
+
+def measured_traffic(kernel, workload):
+    m = _measured(MEASURED_TRAFFIC, kernel, workload)
+    return None if m is None else m["bytes_per_launch"]
+
+
+def measured_mfma(kernel, workload):
+    m = _measured(MEASURED_MFMA, kernel, workload)
+    if m is None:
+        return None
+    return {"busy": m["busy"], "executed_frac": m["executed_frac"], "clock_ghz": m["clock_ghz"],
+            "source": "rocprofv3 PMC: SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, SQ_INSTS_VALU_MFMA_MOPS_BF16"}
 
 
 def cpu_baseline(cfg, wd, B=32, prefill_tokens=32):
@@ -514,6 +545,7 @@ def main():
             # MFMA products (the fp32 operand split into a bf16 hi/lo pair)
             r["mfma_passes"] = passes
             r["executed_frac"] = round(passes * ach / BF16_PEAK_TFLOPS, 4)
+            r["mfma_counters"] = measured_mfma(traffic_key, (cfg.name, B, P)) if traffic_key else None
         return r
 
     out = {
@@ -541,13 +573,16 @@ def main():
                              "gemm_prefill": roof(gemm_t, "mfma", ("gemm_prefill", "fp32"), passes=2),
                              # hi*hi + hi*lo + lo*hi; causally masked halves of diagonal
                              # tiles run too, so the executed fraction is a lower bound
-                             "attn_prefill": roof(apre_t, "mfma", passes=3)},
+                             "attn_prefill": roof(apre_t, "mfma", ("attn_prefill", "fp32"), passes=3)},
     }
 
     def attn_roof(t, kv):
-        r = roof(t, "hbm", ("attn_decode_kernel", kv))
+        # groups of up to 4 heads with an fp32 cache take the lane-group kernel,
+        # the others the MFMA form
+        name = "attn_decode_kernel" if kv == "fp32" and cfg.n_heads // cfg.n_kv_heads <= 4 else "attn_decode_mfma_kernel"
+        r = roof(t, "hbm", (name, kv))
         if r is not None:
-            r["kernel"] = f"attn_decode_kernel (split-KV GQA decode attention, {kv} KV)"
+            r["kernel"] = f"{name} (split-KV GQA decode attention, {kv} KV)"
             r["algorithmic_bytes_per_launch_gb"] = round(t["bytes"] / t["launches"] / 1e9, 4)
         return r
 

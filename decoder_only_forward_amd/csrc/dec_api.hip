@@ -423,7 +423,7 @@ void run_pass(dec_model *m, const Pass &ps) {
             // max_seq (the deferred case); below that, slot == position
             if (ps.deferred || !m->kvimg ||
                 !launch_attn_prefill_tiles(st, T, ps.start_pos, ps.seq, m->q, kc, vc, kvb, nh, nkv, hd, c.max_seq,
-                                           m->kvimg, ah, al, af))
+                                           m->kvimg, m->part, m->pl.part_floats, ah, al, af))
                 launch_attn_prefill(st, T, ps.start_pos, ps.seq, m->q, kc, vc, kvb, nh, nkv, hd, c.max_seq, W,
                                     ps.deferred, ps.deferred ? m->ck : nullptr, ps.deferred ? m->cv : nullptr, ah,
                                     al, af);

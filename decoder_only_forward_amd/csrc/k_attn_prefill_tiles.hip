@@ -27,6 +27,13 @@
 //     q is scaled by log2(e)/sqrt(hd) before its split, so the softmax runs in
 //     base 2 (one exp2 per weight); only tiles that reach past a wave's first
 //     query position are masked.
+//  A launch of fewer blocks than twice the CUs (few kv heads, a few hundred
+//  to a few thousand rows: Qwen2.5-0.5B at 2048 tokens has 57 row blocks x 2
+//  kv heads, whose causal lengths run from 1 to 32 tiles) splits the longer
+//  row blocks' key tiles into chunks of at most `chunk` tiles, one block each;
+//  a split row block's chunks write their unnormalised outputs with the
+//  running maximum and normaliser, and attn_chunk_merge_kernel combines them
+//  (the split-KV merge of the decode attention, over key chunks).
 #include "common.h"
 #include "kernels.h"
 
@@ -138,6 +145,7 @@ __device__ __forceinline__ void store_out(float v, size_t off, u16 *o_hi, u16 *o
 template <int HD, int G, bool KB>
 __global__ void __launch_bounds__(NTHR, 1) attn_tiles_kernel(int T, int start_pos, const float *__restrict__ q,
                                                              const u16 *__restrict__ img, int ntiles_all, int nh,
+                                                             int chunk, int nch, float *__restrict__ part,
                                                              u16 *__restrict__ o_hi, u16 *__restrict__ o_lo,
                                                              float *__restrict__ o_f32) {
     using I = Img<HD, KB>;
@@ -148,12 +156,18 @@ __global__ void __launch_bounds__(NTHR, 1) attn_tiles_kernel(int T, int start_po
     constexpr int IMGU16 = I::BYTES / 2;
 
     // blocks are dispatched in linear order (x fastest): walk the row blocks
-    // from the longest (last rows) down, all kv heads of one row block together,
-    // so the longest blocks start first on every CU
+    // from the longest (last rows) down, the key chunks of a row block and all
+    // kv heads together, so the longest blocks start first on every CU
     const int lin = blockIdx.x + blockIdx.y * gridDim.x;
     const int kvh = lin % gridDim.y;
-    const int rb = gridDim.x - 1 - lin / gridDim.y;
+    const int ch = (lin / gridDim.y) % nch;
+    const int rb = gridDim.x / nch - 1 - lin / (gridDim.y * nch);
     const int t0 = rb * ROWS;
+    const int last_pos = start_pos + min(T, t0 + ROWS) - 1;
+    const int ntiles = last_pos / TK + 1;
+    const int nchunks = (ntiles + chunk - 1) / chunk;   // of this row block
+    const int j0 = ch * chunk, j1 = min(ntiles, j0 + chunk);
+    if (j0 >= j1) return;   // a chunk past the row block's keys (block-uniform)
     const int tid = threadIdx.x, lane = tid % WAVE, wv = tid / WAVE;
     const int ql = lane & 31, hh = lane >> 5;
     const int qv = wv * 32 + ql;
@@ -194,8 +208,6 @@ __global__ void __launch_bounds__(NTHR, 1) attn_tiles_kernel(int T, int start_po
         wmax = max(wmax, __shfl_xor(wmax, off, WAVE));
         wmin = min(wmin, __shfl_xor(wmin, off, WAVE));
     }
-    const int last_pos = start_pos + min(T, t0 + ROWS) - 1;
-    const int ntiles = last_pos / TK + 1;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(img + (size_t)kvh * ntiles_all * IMGU16);
 
     // the next tile's image goes from global memory straight into the other
@@ -212,14 +224,14 @@ __global__ void __launch_bounds__(NTHR, 1) attn_tiles_kernel(int T, int start_po
                                              (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
         }
     };
-    dma(0, 0);
+    dma(j0, 0);
     __syncthreads();
 
-    for (int j = 0; j < ntiles; j++) {
-        if (j + 1 < ntiles) dma(j + 1, (j + 1) & 1);
+    for (int j = j0; j < j1; j++) {
+        if (j + 1 < j1) dma(j + 1, (j + 1 - j0) & 1);
         const int kb = j * TK;
         if (kb <= wmax) {
-            const u16 *sb = lds + (j & 1) * IMGU16;
+            const u16 *sb = lds + ((j - j0) & 1) * IMGU16;
             // S^T for the 64 keys: two 32-key sub-tiles
             floatx16 sc[2];
 #pragma unroll
@@ -306,6 +318,21 @@ __global__ void __launch_bounds__(NTHR, 1) attn_tiles_kernel(int T, int start_po
         __syncthreads();
     }
     if (!live) return;
+    if (nchunks > 1) {
+        // a chunk of a split row block: unnormalised output, base-2 running
+        // maximum and normaliser of (row t, head h) over this chunk's keys
+        float *dst = part + (((size_t)ch * T + t) * nh + h) * (HD + 2);
+#pragma unroll
+        for (int d = 0; d < DT; d++)
+#pragma unroll
+            for (int gq = 0; gq < 4; gq++) {
+                const int dim = d * 32 + gq * 8 + 4 * hh;
+                *reinterpret_cast<float4 *>(dst + dim) =
+                    make_float4(o[d][4 * gq], o[d][4 * gq + 1], o[d][4 * gq + 2], o[d][4 * gq + 3]);
+            }
+        if (hh == 0) { dst[HD] = m; dst[HD + 1] = l; }
+        return;
+    }
     const float inv = 1.0f / l;
     const size_t base = (size_t)t * nh * HD + (size_t)h * HD;
 #pragma unroll
@@ -318,6 +345,45 @@ __global__ void __launch_bounds__(NTHR, 1) attn_tiles_kernel(int T, int start_po
         }
 }
 
+// The key chunks of the split row blocks: one wave per (row, head), lane =
+// output dim (two dims per lane at head_dim 128).  Lane c first loads chunk c's
+// running maximum and normaliser; weights f_c = 2^(m_c - max m), output and
+// normaliser summed over ascending c.
+template <int HD>
+__global__ void __launch_bounds__(256) attn_chunk_merge_kernel(int T, int start_pos, int nh, int rows_per_block,
+                                                              int chunk, const float *__restrict__ part,
+                                                              u16 *__restrict__ o_hi, u16 *__restrict__ o_lo,
+                                                              float *__restrict__ o_f32) {
+    const int wid = blockIdx.x * 4 + threadIdx.x / WAVE, lane = threadIdx.x % WAVE;
+    if (wid >= T * nh) return;
+    const int t = wid / nh, h = wid % nh;
+    const int rb = t / rows_per_block;
+    const int last_pos = start_pos + min(T, (rb + 1) * rows_per_block) - 1;
+    const int nchunks = (last_pos / TK + 1 + chunk - 1) / chunk;   // at most 64
+    if (nchunks <= 1) return;   // that row block wrote its output directly
+    constexpr int DPL = HD / WAVE;
+    const size_t cs = (size_t)T * nh * (HD + 2);
+    const float *src = part + ((size_t)t * nh + h) * (HD + 2);
+    const float mc = lane < nchunks ? src[lane * cs + HD] : -INFINITY;
+    const float lc = lane < nchunks ? src[lane * cs + HD + 1] : 0.f;
+    const float mx = wave_max(mc);
+    const float f = mc == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mc - mx);
+    float L = 0.f, A[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; e++) A[e] = 0.f;
+#pragma unroll 4
+    for (int c = 0; c < nchunks; c++) {
+        const float fc = __shfl(f, c, WAVE);
+        L += __shfl(lc, c, WAVE) * fc;
+#pragma unroll
+        for (int e = 0; e < DPL; e++) A[e] += src[c * cs + lane + e * WAVE] * fc;
+    }
+    const float inv = 1.0f / L;
+    const size_t base = (size_t)t * nh * HD + (size_t)h * HD;
+#pragma unroll
+    for (int e = 0; e < DPL; e++) store_out(A[e] * inv, base + lane + e * WAVE, o_hi, o_lo, o_f32);
+}
+
 template <int HD, int G, bool KB>
 void set_lds_attr() {
     static bool done = false;
@@ -328,32 +394,70 @@ void set_lds_attr() {
     }
 }
 
+// Key tiles per chunk for T rows from start_pos (rows_per_block query rows per
+// block, nkv kv heads), and the chunk count of the longest row block: a launch
+// of at least twice as many (row block, kv head) blocks as CUs is not split
+// (the longest-first dispatch order balances it); a smaller one is cut into
+// chunks of 2 x (its tiles / CUs) tiles, at least 2, and at most max_chunks per
+// row block (the partial buffer's room).  Each chunk costs its block's query
+// load, first-tile wait and partial write, and the merge; at Qwen2.5-0.5B's
+// 2048 tokens (1974 block-tiles) chunks of 15 tiles (the longest row blocks
+// in three) measured 7.45 ms per prefill against 7.81 (8 tiles), 8.27 (4
+// tiles) and 8.07 unsplit.
+void chunking(int T, int start_pos, int rows_per_block, int nkv, int max_chunks, int &chunk, int &nch) {
+    const int rbs = (T + rows_per_block - 1) / rows_per_block;
+    const int ntiles_max = (start_pos + T - 1) / TK + 1;
+    chunk = ntiles_max;
+    nch = 1;
+    const int cus = num_cus();
+    if ((long)rbs * nkv >= 2L * cus || max_chunks < 2) return;
+    long total = 0;
+    for (int rb = 0; rb < rbs; rb++) total += (start_pos + std::min(T, (rb + 1) * rows_per_block) - 1) / TK + 1;
+    total *= nkv;
+    int c = (int)((2 * total + cus - 1) / cus);
+    c = std::max(c, 2);
+    if ((ntiles_max + c - 1) / c > max_chunks) c = (ntiles_max + max_chunks - 1) / max_chunks;
+    chunk = std::min(c, ntiles_max);
+    nch = (ntiles_max + chunk - 1) / chunk;
+}
+
 template <int HD, bool KB>
 bool launch_hd(hipStream_t st, int G, int T, int start_pos, int slot, const float *q, const void *kc,
-               const void *vc, int nh, int nkv, int max_seq, u16 *img, u16 *o_hi, u16 *o_lo, float *o_f32) {
+               const void *vc, int nh, int nkv, int max_seq, u16 *img, float *part, size_t part_floats, u16 *o_hi,
+               u16 *o_lo, float *o_f32) {
+    if (G < 1 || G > 8) return false;
     const int npos = start_pos + T;
     const int ntiles = (npos + TK - 1) / TK;
     constexpr int LDSB = 2 * Img<HD, KB>::BYTES;
+    const int rows = NQV / G;
+    const size_t per_chunk = (size_t)T * nh * (HD + 2);
+    const int max_chunks = part ? (int)std::min<size_t>(part_floats / per_chunk, 64) : 1;
+    int chunk, nch;
+    chunking(T, start_pos, rows, nkv, max_chunks, chunk, nch);
+    const int rbs = (T + rows - 1) / rows;
     hipLaunchKernelGGL((kv_tile_kernel<HD, KB>), dim3(ntiles, nkv), dim3(256), 0, st, kc, vc, max_seq, slot, nkv,
                        npos, ntiles, img);
 #define AT(GG)                                                                                                  \
     do {                                                                                                        \
         set_lds_attr<HD, GG, KB>();                                                                             \
-        hipLaunchKernelGGL((attn_tiles_kernel<HD, GG, KB>), dim3((T + NQV / GG - 1) / (NQV / GG), nkv),         \
-                           dim3(NTHR), LDSB, st, T, start_pos, q, img, ntiles, nh, o_hi, o_lo, o_f32);          \
+        hipLaunchKernelGGL((attn_tiles_kernel<HD, GG, KB>), dim3(rbs * nch, nkv), dim3(NTHR), LDSB, st, T,      \
+                           start_pos, q, img, ntiles, nh, chunk, nch, part, o_hi, o_lo, o_f32);                \
     } while (0)
     switch (G) {
-        case 1: AT(1); return true;
-        case 2: AT(2); return true;
-        case 3: AT(3); return true;
-        case 4: AT(4); return true;
-        case 5: AT(5); return true;
-        case 6: AT(6); return true;
-        case 7: AT(7); return true;
-        case 8: AT(8); return true;
+        case 1: AT(1); break;
+        case 2: AT(2); break;
+        case 3: AT(3); break;
+        case 4: AT(4); break;
+        case 5: AT(5); break;
+        case 6: AT(6); break;
+        case 7: AT(7); break;
+        case 8: AT(8); break;
     }
 #undef AT
-    return false;
+    if (nch > 1)
+        hipLaunchKernelGGL((attn_chunk_merge_kernel<HD>), dim3((T * nh + 3) / 4), dim3(256), 0, st, T, start_pos, nh,
+                           rows, chunk, part, o_hi, o_lo, o_f32);
+    return true;
 }
 
 }  // namespace
@@ -368,17 +472,14 @@ size_t attn_tiles_bytes(int max_pos, int nkv, int hd, int kv_bf16) {
 
 bool launch_attn_prefill_tiles(hipStream_t st, int T, int start_pos, int slot, const float *q, const void *kc,
                                const void *vc, int kv_bf16, int nh, int nkv, int hd, int max_seq, void *img,
-                               u16 *o_hi, u16 *o_lo, float *o_f32) {
+                               float *part, size_t part_floats, u16 *o_hi, u16 *o_lo, float *o_f32) {
     if (T <= 0) return true;
     const int G = nh / nkv;
     u16 *im = static_cast<u16 *>(img);
-    if (hd == 128) {
-        return kv_bf16 ? launch_hd<128, true>(st, G, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, im, o_hi, o_lo, o_f32)
-                       : launch_hd<128, false>(st, G, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, im, o_hi, o_lo, o_f32);
-    }
-    if (hd == 64) {
-        return kv_bf16 ? launch_hd<64, true>(st, G, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, im, o_hi, o_lo, o_f32)
-                       : launch_hd<64, false>(st, G, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, im, o_hi, o_lo, o_f32);
-    }
+#define LH(HD, KB) launch_hd<HD, KB>(st, G, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, im, part, part_floats, \
+                                     o_hi, o_lo, o_f32)
+    if (hd == 128) return kv_bf16 ? LH(128, true) : LH(128, false);
+    if (hd == 64) return kv_bf16 ? LH(64, true) : LH(64, false);
+#undef LH
     return false;
 }

@@ -10,6 +10,8 @@
 //
 // An optional expert grouping (MoE prefill) runs one grid slice per expert over
 // that expert's contiguous rows of `a` and its slice of the weights.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -354,19 +356,27 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
         srcl[i] = p.a_lo + (size_t)(mrow0 + m) * p.lda + kz0 + c * 8;
     }
     const int nk = min(p.kchunk, p.K - kz0) / DBK;
-    // every iteration issues its loads (the last tile again past the end), so
-    // the count of outstanding loads is the same everywhere
-    auto load_tile = [&](int kt, int stage) {
+    // Every iteration issues its loads (the last tile again past the end), so
+    // the count of outstanding loads is the same everywhere.  Load instruction
+    // i of wave wv covers token rows (i*8 + wv)*16 .. +15 of the tile; a wave
+    // issues only the token-row loads of groups holding a row below M (NA of
+    // 2: the expert rows of a grouped tile, or the last token tile, often end
+    // early).  LDS rows of skipped groups keep stale values, which reach only
+    // outputs of tokens >= M, never stored.
+    auto load_tile = [&](int kt, int stage, auto na_c) {
+        constexpr int NA = decltype(na_c)::value;
         const int k0 = (kt < nk ? kt : nk - 1) * DBK;
         LDS_AS u16 *base = (LDS_AS u16 *)smem + stage * DSTAGE;
 #pragma unroll
         for (int i = 0; i < 2; i++) {
             const int slot = (i * 8 + wv) * 512;
             __builtin_amdgcn_global_load_lds((const void *)(srcw[i] + k0), (LDS_AS void *)(base + slot), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(srch[i] + k0), (LDS_AS void *)(base + DARR + slot), 16,
-                                             0, 0);
-            __builtin_amdgcn_global_load_lds((const void *)(srcl[i] + k0), (LDS_AS void *)(base + 2 * DARR + slot),
-                                             16, 0, 0);
+            if (i < NA) {
+                __builtin_amdgcn_global_load_lds((const void *)(srch[i] + k0), (LDS_AS void *)(base + DARR + slot),
+                                                 16, 0, 0);
+                __builtin_amdgcn_global_load_lds((const void *)(srcl[i] + k0),
+                                                 (LDS_AS void *)(base + 2 * DARR + slot), 16, 0, 0);
+            }
         }
     };
 
@@ -416,26 +426,37 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
         }
     };
 
-    // Barrier between k-tiles: wait until only the newest tile's 6 loads may be
-    // outstanding and every LDS read is done, then s_barrier.  (__syncthreads
-    // would also wait for the newest tile: its fence covers the LDS writes of
-    // every outstanding load.)  s_waitcnt fields: vmcnt 6, expcnt 7, lgkmcnt 0.
-    constexpr int WAIT_VM6_LGKM0 = 6 | (7 << 4) | (0 << 8);
-    load_tile(0, 0);
-    load_tile(1, 1);
-    __builtin_amdgcn_s_waitcnt(WAIT_VM6_LGKM0);
-    __builtin_amdgcn_s_barrier();
-    for (int kt = 0; kt < nk; kt++) {
-        // stage (kt+2)%3 held tile kt-1, which every wave finished reading before
-        // the previous barrier; tile kt+1 is complete after this iteration's wait
-        load_tile(kt + 2, (kt + 2) % DNSTAGE);
-        compute(kt % DNSTAGE);
-        __builtin_amdgcn_s_waitcnt(WAIT_VM6_LGKM0);
+    // Barrier between k-tiles: wait until only the newest tile's loads (2 + 2 NA
+    // per wave) may be outstanding and every LDS read is done, then s_barrier.
+    // (__syncthreads would also wait for the newest tile: its fence covers the
+    // LDS writes of every outstanding load.)  s_waitcnt fields: vmcnt, expcnt 7,
+    // lgkmcnt 0.  The loop is instantiated per load count, so the waits stay
+    // immediates; the waves of a block may take different instances (same
+    // barrier count).
+    auto ring = [&](auto na_c) {
+        constexpr int NA = decltype(na_c)::value;
+        constexpr int WAIT = (2 + 2 * NA) | (7 << 4) | (0 << 8);
+        load_tile(0, 0, na_c);
+        load_tile(1, 1, na_c);
+        __builtin_amdgcn_s_waitcnt(WAIT);
         __builtin_amdgcn_s_barrier();
-    }
-    // the loads issued past the last tile land in stages nobody reads again;
-    // they must finish before the block's LDS is released
-    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+        for (int kt = 0; kt < nk; kt++) {
+            // stage (kt+2)%3 held tile kt-1, which every wave finished reading
+            // before the previous barrier; tile kt+1 is complete after this
+            // iteration's wait
+            load_tile(kt + 2, (kt + 2) % DNSTAGE, na_c);
+            compute(kt % DNSTAGE);
+            __builtin_amdgcn_s_waitcnt(WAIT);
+            __builtin_amdgcn_s_barrier();
+        }
+        // the loads issued past the last tile land in stages nobody reads again;
+        // they must finish before the block's LDS is released
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    };
+    const int na = (m0 + wv * 16 < M) + (m0 + (8 + wv) * 16 < M);   // wave-uniform
+    if (na == 2) ring(std::integral_constant<int, 2>{});
+    else if (na == 1) ring(std::integral_constant<int, 1>{});
+    else ring(std::integral_constant<int, 0>{});
 
     if constexpr (SILU) {
         // acc[i][j] (gate, i = 0, 1) and acc[i+2][j] (up): feature

@@ -139,11 +139,14 @@ void launch_attn_prefill(hipStream_t st, int T, int start_pos, int slot, const f
 // position at its own slot: start_pos + T <= max_seq).  Each call first writes
 // the tiles of positions [0, start_pos + T) of sequence `slot` into `img`
 // (attn_tiles_bytes(max_seq, nkv, hd, kv_bf16) bytes), then runs the MFMA
-// kernel.  Returns false for an unsupported head_dim (nothing launched).
+// kernel.  A launch of few row blocks splits their key tiles into chunks whose
+// partial results go to `part` (part_floats floats of scratch, free during the
+// call) and a merge pass; part may be null (no split).  Returns false for an
+// unsupported head_dim or group size (nothing launched).
 size_t attn_tiles_bytes(int max_pos, int nkv, int hd, int kv_bf16);
 bool launch_attn_prefill_tiles(hipStream_t st, int T, int start_pos, int slot, const float *q, const void *kc,
                                const void *vc, int kv_bf16, int nh, int nkv, int hd, int max_seq, void *img,
-                               u16 *o_hi, u16 *o_lo, float *o_f32);
+                               float *part, size_t part_floats, u16 *o_hi, u16 *o_lo, float *o_f32);
 
 // MoE.  Router logits [T][E] -> softmax, top-k by repeated selection (ties to
 // the lower id), renormalised weights; then the (token, slot) pairs are grouped
