@@ -48,9 +48,9 @@ _ATTN_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_decode.hi
 _GEMV_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemv.hip":
                                  "e8b40692db620676cb8b5a5653b879158cc66c2d689ff00d7afbbe436a81511c"})
 _GEMM_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemm.hip":
-                                 "35914c3a9630eec4fc2e1bac9079f6d5b6dfed7296b837f1545a2752e3ee4509"})
+                                 "2181d31cb0bd5c0e44380b70c915c2a1b43eb00012d6913039016e57d9af2b60"})
 _TILES_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_prefill_tiles.hip":
-                                  "047e445f50cff41f139b69e5a72454f020bc746fed7ef71329edd1089737b1ae"})
+                                  "a057f7f417eda3f60000afda30eb547ff3158668784e1a69e880429eb018a86f"})
 MEASURED_TRAFFIC = {
     # B = 32 launches: the lane-group kernel (fp32 cache), the MFMA kernel in
     # 8-wave blocks (bf16 cache)
@@ -63,7 +63,9 @@ MEASURED_TRAFFIC = {
     ("gemv_decode", "bf16"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
                               "bytes_per_launch": 121762993},
     ("gemm_prefill", "fp32"): {"sources": _GEMM_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                               "bytes_per_launch": 1698152177},
+                               "bytes_per_launch": 1713454592},
+    ("attn_prefill", "fp32"): {"sources": _TILES_SOURCES, "workload": ("mistral-7b", 32, 4096),
+                               "bytes_per_launch": 269962240},
 }
 # MFMA counters of the prefill kernels (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
 # GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES): busy = MFMA-busy
@@ -74,9 +76,9 @@ MEASURED_TRAFFIC = {
 # gate|up, down); reported only while the sources hash to the profiled ones.
 MEASURED_MFMA = {
     ("gemm_prefill", "fp32"): {"sources": _GEMM_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                               "busy": 0.592, "executed_frac": 0.470, "clock_ghz": 1.90},
+                               "busy": 0.586, "executed_frac": 0.486, "clock_ghz": 1.97},
     ("attn_prefill", "fp32"): {"sources": _TILES_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                               "busy": 0.467, "executed_frac": 0.384, "clock_ghz": 1.96},
+                               "busy": 0.469, "executed_frac": 0.406, "clock_ghz": 2.07},
 }
 BF16_PEAK_TFLOPS = 2500.0
 # The other shapes' workloads: (decode batches, prompt length).
