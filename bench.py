@@ -46,7 +46,7 @@ _COMMON = {"decoder_only_forward_amd/csrc/common.h":
 _ATTN_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_decode.hip":
                                  "cae52ed058060b38e445bdb8323692f2f7481e38ec54819afc64a7fc8f14e507"})
 _GEMV_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemv.hip":
-                                 "e8b40692db620676cb8b5a5653b879158cc66c2d689ff00d7afbbe436a81511c"})
+                                 "11f73b184e2f0a6eac6252819b3d4309b847dfd1a45ddedad296e73af96448c6"})
 _GEMM_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemm.hip":
                                  "2181d31cb0bd5c0e44380b70c915c2a1b43eb00012d6913039016e57d9af2b60"})
 _TILES_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_prefill_tiles.hip":
@@ -59,9 +59,9 @@ MEASURED_TRAFFIC = {
     ("attn_decode_mfma_kernel", "bf16"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
                                           "bytes_per_launch": 541894295},
     ("gemv_decode", "fp32"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                              "bytes_per_launch": 121762993},
+                              "bytes_per_launch": 121774326},
     ("gemv_decode", "bf16"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                              "bytes_per_launch": 121762993},
+                              "bytes_per_launch": 121774326},
     ("gemm_prefill", "fp32"): {"sources": _GEMM_SOURCES, "workload": ("mistral-7b", 32, 4096),
                                "bytes_per_launch": 1713454592},
     ("attn_prefill", "fp32"): {"sources": _TILES_SOURCES, "workload": ("mistral-7b", 32, 4096),

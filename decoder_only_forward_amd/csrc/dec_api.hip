@@ -55,7 +55,7 @@ constexpr size_t MAX_GRAPHS = 16;
 struct Plan {  // byte offsets into the workspace
     size_t kv_layer;        // elements of one layer's K (or V) cache
     size_t k, v, ck, cv, kvimg, s_hi, s_lo, x, a_hi, a_lo, a_f32, part, q, attn, rope, tok, pos, slot, amax, ssq;
-    size_t moe_ids, moe_w, moe_cnt, moe_off, moe_pairs, g_hi, g_lo, g_f32, moe_y;
+    size_t moe_ids, moe_w, moe_cnt, moe_off, moe_pairs, moe_inv, g_hi, g_lo, g_f32;
     size_t part_floats, act_elems, total;
     int rows;               // max rows of one pass (max(max_batch, max_prefill))
 };
@@ -78,10 +78,10 @@ struct dec_model {
     void *kvimg;            // prefill attention's K/V tile images (null: not used)
     u16 *s_hi, *s_lo;       // fused SwiGLU output of a prefill (null: not used)
     int kv_es;
-    float *x, *a_f32, *part, *q, *attn, *moe_w, *g_f32, *moe_y, *ssq;
+    float *x, *a_f32, *part, *q, *attn, *moe_w, *g_f32, *ssq;
     u16 *a_hi, *a_lo, *g_hi, *g_lo;
     float2 *rope;
-    int32_t *tok, *pos, *slot, *amax, *moe_ids, *moe_cnt, *moe_off, *moe_pairs;
+    int32_t *tok, *pos, *slot, *amax, *moe_ids, *moe_cnt, *moe_off, *moe_pairs, *moe_inv;
     std::vector<int> len;
     float *cap_hidden = nullptr, *cap_router = nullptr;
     int32_t *cap_ids = nullptr;
@@ -186,10 +186,10 @@ bool plan(const dec_config &c, Plan &p) {
     p.moe_cnt = take(64 * 4);
     p.moe_off = take(65 * 4);
     p.moe_pairs = take(prow * 4);
+    p.moe_inv = take(prow * 4);
     p.g_hi = take(E && !f32w ? prow * d * 2 : 0);
     p.g_lo = take(E && !f32w ? prow * d * 2 : 0);
     p.g_f32 = take(E && f32w ? prow * d * 4 : 0);
-    p.moe_y = take(E ? prow * d * 4 : 0);
     p.total = off;
     return true;
 }
@@ -339,8 +339,10 @@ Partials proj(dec_model *m, const WSeg *segs, int nseg, int K, int T, const u16 
 }
 
 // Grouped expert projection over TP = T*k pair rows in expert order.
+// row_pairs (decode GEMV only): grouped row r reads token row row_pairs[r] / top_k
+// of (hi, lo) instead of row r.
 Partials proj_grouped(dec_model *m, const WSeg *segs, int nseg, int K, int T, const u16 *hi, const u16 *lo,
-                      const float *f32, int lda) {
+                      const float *f32, int lda, const int32_t *row_pairs = nullptr) {
     const dec_config &c = m->c;
     int N = 0;
     for (int i = 0; i < nseg; i++) N += segs[i].rows;
@@ -354,7 +356,8 @@ Partials proj_grouped(dec_model *m, const WSeg *segs, int nseg, int K, int T, co
     if (T <= 64) {
         const int S = gemv_grouped_splits(N * act, K, T);
         Tick tk(m, DEC_K_GEMV);
-        launch_gemv_grouped(m->st, segs, nseg, K, hi, lo, lda, T, E, m->moe_off, es, m->part, S, (size_t)TP * N, N);
+        launch_gemv_grouped(m->st, segs, nseg, K, hi, lo, lda, T, E, m->moe_off, es, m->part, S, (size_t)TP * N, N,
+                            row_pairs, c.top_k);
         tk.done((double)N * K * 2 * act + (double)TP * K * 4 + (double)TP * N * 4, 2.0 * TP * N * K);
         return Partials{m->part, S, (size_t)TP * N, N};
     }
@@ -381,8 +384,9 @@ void run_pass(dec_model *m, const Pass &ps) {
         return m->cap_hidden ? m->cap_hidden + ((size_t)layer * ps.cap_rows + ps.cap_row) * d : nullptr;
     };
 
-    launch_residual_norm(st, RN_EMBED, T, d, m->x, m->tok, m->embed, f32w, Partials{nullptr, 0, 0, 0}, nullptr,
-                         nullptr, 0, m->L[0].attn_norm, eps, ah, al, af, caph(0), m->ssq);
+    launch_residual_norm(st, RN_EMBED, T, d, m->x, m->tok, m->embed, f32w, Partials{nullptr, 0, 0, 0},
+                         Partials{nullptr, 0, 0, 0}, nullptr, nullptr, 0, m->L[0].attn_norm, eps, ah, al, af, caph(0),
+                         m->ssq);
     launch_rope_table(st, m->pos, T, hd, c.rope_theta, c.rope_scaling, c.rope_factor, c.rope_low_freq_factor,
                       c.rope_high_freq_factor, c.rope_orig_ctx, m->rope);
 
@@ -434,8 +438,8 @@ void run_pass(dec_model *m, const Pass &ps) {
         // output projection, residual, FFN norm
         WSeg wo[1] = {{w.wo, d}};
         Partials po = proj(m, wo, 1, qd, T, ah, al, af, qd);
-        launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, po, nullptr, nullptr, 0, w.ffn_norm,
-                             eps, ah, al, af, nullptr, m->ssq);
+        launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, po, Partials{nullptr, 0, 0, 0}, nullptr,
+                             nullptr, 0, w.ffn_norm, eps, ah, al, af, nullptr, m->ssq);
         const float *next_gain = (l + 1 < c.n_layers) ? m->L[l + 1].attn_norm : m->out_norm;
         if (c.n_experts == 0) {
             WSeg gu[2] = {{w.w_gate, F}, {w.w_up, F}};
@@ -462,8 +466,8 @@ void run_pass(dec_model *m, const Pass &ps) {
             }
             WSeg wd[1] = {{w.w_down, d}};
             Partials pd = proj(m, wd, 1, F, T, fused ? m->s_hi : ah, fused ? m->s_lo : al, af, F);
-            launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, pd, nullptr, nullptr, 0, next_gain,
-                                 eps, ah, al, af, caph(l + 1), m->ssq);
+            launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, pd, Partials{nullptr, 0, 0, 0},
+                                 nullptr, nullptr, 0, next_gain, eps, ah, al, af, caph(l + 1), m->ssq);
         } else {
             const int E = c.n_experts, k = c.top_k, TP = T * k;
             // router logits: the GEMV for decode rows and fp32 weights; prefill
@@ -478,9 +482,14 @@ void run_pass(dec_model *m, const Pass &ps) {
                              m->moe_ids, m->moe_w,
                              m->cap_router ? m->cap_router + ((size_t)l * ps.cap_rows + ps.cap_row) * E : nullptr,
                              m->cap_ids ? m->cap_ids + ((size_t)l * ps.cap_rows + ps.cap_row) * k : nullptr,
-                             m->moe_cnt, m->moe_off, m->moe_pairs);
-            launch_moe_gather(st, T, k, d, m->moe_pairs, ah, al, af, f32w ? nullptr : m->g_hi,
-                              f32w ? nullptr : m->g_lo, f32w ? m->g_f32 : nullptr);
+                             m->moe_cnt, m->moe_off, m->moe_pairs, m->moe_inv);
+            // decode rows (bf16 weights): the grouped GEMV reads each grouped row's
+            // token row of (ah, al) through the pair map; otherwise the rows are
+            // gathered into expert order first
+            const bool mapped = !f32w && T <= 64;
+            if (!mapped)
+                launch_moe_gather(st, T, k, d, m->moe_pairs, ah, al, af, f32w ? nullptr : m->g_hi,
+                                  f32w ? nullptr : m->g_lo, f32w ? m->g_f32 : nullptr);
             WSeg gu[2] = {{w.w_gate, F}, {w.w_up, F}};
             // prefill rows: the grouped gate|up GEMM writes silu(gate) * up itself
             bool fused = false;
@@ -493,14 +502,15 @@ void run_pass(dec_model *m, const Pass &ps) {
                 else tk.cancel();
             }
             if (!fused) {
-                Partials pg = proj_grouped(m, gu, 2, d, T, m->g_hi, m->g_lo, m->g_f32, d);
+                Partials pg = mapped ? proj_grouped(m, gu, 2, d, T, ah, al, nullptr, d, m->moe_pairs)
+                                     : proj_grouped(m, gu, 2, d, T, m->g_hi, m->g_lo, m->g_f32, d);
                 launch_silu_mul(st, TP, F, pg, ah, al, af);
             }
             WSeg wd[1] = {{w.w_down, d}};
             Partials pd = proj_grouped(m, wd, 1, F, T, ah, al, af, F);
-            launch_moe_scatter(st, TP, d, m->moe_pairs, pd, m->moe_y);
-            launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, Partials{nullptr, 0, 0, 0}, m->moe_y,
-                                 m->moe_w, k, next_gain, eps, ah, al, af, caph(l + 1), m->ssq);
+            // the residual reads each token's expert outputs at their grouped rows
+            launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, Partials{nullptr, 0, 0, 0}, pd,
+                                 m->moe_inv, m->moe_w, k, next_gain, eps, ah, al, af, caph(l + 1), m->ssq);
         }
     }
     // LM head on the rows that need logits (a holds the final-norm rows)
@@ -707,10 +717,10 @@ int dec_create(const dec_config *cfg, const dec_weights *w, void *workspace, siz
     m->moe_cnt = (int32_t *)(b + p.moe_cnt);
     m->moe_off = (int32_t *)(b + p.moe_off);
     m->moe_pairs = (int32_t *)(b + p.moe_pairs);
+    m->moe_inv = (int32_t *)(b + p.moe_inv);
     m->g_hi = (u16 *)(b + p.g_hi);
     m->g_lo = (u16 *)(b + p.g_lo);
     m->g_f32 = (float *)(b + p.g_f32);
-    m->moe_y = (float *)(b + p.moe_y);
     m->len.assign(cfg->max_batch, 0);
     m->wf32 = cfg->weight_dtype == DEC_WEIGHT_F32;
     // a ring of max_seq == window slots; a window longer than max_seq never

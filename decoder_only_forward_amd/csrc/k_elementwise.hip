@@ -12,7 +12,7 @@
 template <int VPT, int NTH>
 __global__ void __launch_bounds__(NTH) residual_norm_kernel(
     int mode, int d, float *__restrict__ x, const int32_t *__restrict__ tok,
-    const void *__restrict__ embed, int embed_f32, Partials add, const float *__restrict__ moe_y,
+    const void *__restrict__ embed, int embed_f32, Partials add, Partials moe, const int32_t *__restrict__ moe_inv,
     const float *__restrict__ moe_w, int k, const float *__restrict__ gain, float eps,
     u16 *__restrict__ a_hi, u16 *__restrict__ a_lo, float *__restrict__ a_f32, float *__restrict__ cap) {
     __shared__ float red[16];
@@ -41,11 +41,12 @@ __global__ void __launch_bounds__(NTH) residual_norm_kernel(
                 const float4 a = sum_splits4(add.p, add.S, add.stride, (size_t)t * add.ld + 4 * i4);
                 r.x += a.x; r.y += a.y; r.z += a.z; r.w += a.w;
             }
-            if (moe_y) {
+            if (moe_inv) {
+                // the experts' outputs of this token, read at their grouped rows
                 float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
                 for (int j = 0; j < k; j++) {
                     const float w = moe_w[t * k + j];
-                    const float4 e = *reinterpret_cast<const float4 *>(moe_y + ((size_t)t * k + j) * d + 4 * i4);
+                    const float4 e = sum_splits4(moe.p, moe.S, moe.stride, (size_t)moe_inv[t * k + j] * moe.ld + 4 * i4);
                     y.x += w * e.x; y.y += w * e.y; y.z += w * e.z; y.w += w * e.w;
                 }
                 r.x += y.x; r.y += y.y; r.z += y.z; r.w += y.w;
@@ -96,7 +97,8 @@ __global__ void __launch_bounds__(NTH) residual_norm_kernel(
 constexpr int RN_CHUNK = 1024;
 
 __global__ void __launch_bounds__(256) residual_chunk_kernel(
-    int d, float *__restrict__ x, Partials add, const float *__restrict__ moe_y, const float *__restrict__ moe_w,
+    int d, float *__restrict__ x, Partials add, Partials moe, const int32_t *__restrict__ moe_inv,
+    const float *__restrict__ moe_w,
     int k, float *__restrict__ cap, float *__restrict__ ssq) {
     __shared__ float red[16];
     const int t = blockIdx.x, ch = blockIdx.y;
@@ -109,11 +111,11 @@ __global__ void __launch_bounds__(256) residual_chunk_kernel(
             const float4 a = sum_splits4(add.p, add.S, add.stride, (size_t)t * add.ld + 4 * i4);
             r.x += a.x; r.y += a.y; r.z += a.z; r.w += a.w;
         }
-        if (moe_y) {
+        if (moe_inv) {
             float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
             for (int j = 0; j < k; j++) {
                 const float w = moe_w[t * k + j];
-                const float4 e = *reinterpret_cast<const float4 *>(moe_y + ((size_t)t * k + j) * d + 4 * i4);
+                const float4 e = sum_splits4(moe.p, moe.S, moe.stride, (size_t)moe_inv[t * k + j] * moe.ld + 4 * i4);
                 y.x += w * e.x; y.y += w * e.y; y.z += w * e.z; y.w += w * e.w;
             }
             r.x += y.x; r.y += y.y; r.z += y.z; r.w += y.w;
@@ -152,7 +154,7 @@ __global__ void __launch_bounds__(256) norm_chunk_kernel(int d, const float *__r
 }
 
 void launch_residual_norm(hipStream_t st, int mode, int T, int d, float *x, const int32_t *tok,
-                          const void *embed, int embed_f32, Partials add, const float *moe_y,
+                          const void *embed, int embed_f32, Partials add, Partials moe, const int32_t *moe_inv,
                           const float *moe_w, int k, const float *gain, float eps, u16 *a_hi,
                           u16 *a_lo, float *a_f32, float *cap, float *ssq) {
     if (T <= 0) return;
@@ -160,7 +162,7 @@ void launch_residual_norm(hipStream_t st, int mode, int T, int d, float *x, cons
     if (T <= 64 && nv <= 1024) {
         // few rows: one 1024-thread block per row, one float4 per thread
 #define RN1(NT) hipLaunchKernelGGL((residual_norm_kernel<1, NT>), dim3(T), dim3(NT), 0, st, mode, d, x, tok, embed, \
-                                   embed_f32, add, moe_y, moe_w, k, gain, eps, a_hi, a_lo, a_f32, cap)
+                                   embed_f32, add, moe, moe_inv, moe_w, k, gain, eps, a_hi, a_lo, a_f32, cap)
         if (nv <= 256) RN1(256);
         else RN1(1024);
 #undef RN1
@@ -168,7 +170,7 @@ void launch_residual_norm(hipStream_t st, int mode, int T, int d, float *x, cons
     }
     if (mode == RN_ADD && T <= 64 && ssq) {
         const int nch = (d + RN_CHUNK - 1) / RN_CHUNK;
-        hipLaunchKernelGGL(residual_chunk_kernel, dim3(T, nch), dim3(256), 0, st, d, x, add, moe_y, moe_w, k, cap, ssq);
+        hipLaunchKernelGGL(residual_chunk_kernel, dim3(T, nch), dim3(256), 0, st, d, x, add, moe, moe_inv, moe_w, k, cap, ssq);
         if (gain)
             hipLaunchKernelGGL(norm_chunk_kernel, dim3(T, nch), dim3(256), 0, st, d, x, ssq, nch, gain, eps, a_hi,
                                a_lo, a_f32);
@@ -176,7 +178,7 @@ void launch_residual_norm(hipStream_t st, int mode, int T, int d, float *x, cons
     }
     const int vpt = (nv + 255) / 256;
 #define RN(V) hipLaunchKernelGGL((residual_norm_kernel<V, 256>), dim3(T), dim3(256), 0, st, mode, d, x, tok, \
-                                 embed, embed_f32, add, moe_y, moe_w, k, gain, eps, a_hi, a_lo, a_f32, cap)
+                                 embed, embed_f32, add, moe, moe_inv, moe_w, k, gain, eps, a_hi, a_lo, a_f32, cap)
     if (vpt <= 1) RN(1);
     else if (vpt <= 2) RN(2);
     else if (vpt <= 4) RN(4);

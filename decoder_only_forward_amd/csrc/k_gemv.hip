@@ -33,10 +33,14 @@ struct GemvParams {
     size_t split_stride;
     int ldo;
     int kps;   // k per split (multiple of 64)
-    // Grouped experts: expert e = blockIdx.z owns activation rows
-    // [grp_off[e], grp_off[e+1]) and weight slice e (w + e*expert_stride).
+    // Grouped experts: expert e = blockIdx.z owns grouped rows
+    // [grp_off[e], grp_off[e+1]) and weight slice e (w + e*expert_stride);
+    // grouped row r reads activation row r, or, with row_pairs, the token row
+    // row_pairs[r] / row_k (activations in token order).
     const int32_t *grp_off;
     size_t expert_stride;
+    const int32_t *row_pairs;
+    int row_k;
     int rot;   // start each block's k walk at stage blockIdx.x % stages
     // silu(gate) * up in the epilogue: w[0] gate, w[1] up, N features; the
     // product goes to (s_hi, s_lo) [B][ldo] as bf16 pairs; rt row tiles of 16
@@ -138,7 +142,8 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
             const int t = col >> 4, m = col & 15;
             int b = t * 8 + (m & 7);
             b = b < B ? b : B - 1;   // columns past B read a valid row; their outputs are not stored
-            src[i] = (m < 8 ? p.a_hi : p.a_lo) + (size_t)(arow0 + b) * p.lda + kbeg + lc * 8;
+            const int arow = p.row_pairs ? p.row_pairs[arow0 + b] / p.row_k : arow0 + b;
+            src[i] = (m < 8 ? p.a_hi : p.a_lo) + (size_t)arow * p.lda + kbeg + lc * 8;
         }
     }
     // Every iteration issues its loads (the last stage again past the end), so
@@ -437,7 +442,8 @@ bool launch_gemv_silu(hipStream_t st, const void *w_gate, const void *w_up, int 
 // Grouped-expert form used by the MoE decode path (see k_moe.hip).
 void launch_gemv_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi,
                          const u16 *a_lo, int lda, int max_rows, int E, const int32_t *offsets,
-                         size_t expert_stride, float *out, int ksplit, size_t split_stride, int ldo) {
+                         size_t expert_stride, float *out, int ksplit, size_t split_stride, int ldo,
+                         const int32_t *row_pairs, int row_k) {
     GemvParams p{};
     int end = 0;
     for (int s = 0; s < nseg; s++) {
@@ -457,6 +463,8 @@ void launch_gemv_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, cons
     p.ldo = ldo;
     p.grp_off = offsets;
     p.expert_stride = expert_stride;
+    p.row_pairs = row_pairs;
+    p.row_k = row_k;
     if (max_rows <= 0) return;
     int kps = (K + ksplit - 1) / ksplit;
     kps = (kps + DKS - 1) / DKS * DKS;

@@ -24,13 +24,14 @@ struct WSeg {
 
 // Residual update + RMSNorm of one row per block:
 //   mode EMBED:  x = widen(E[tok[t]])
-//   otherwise:   x += sum of `add` splits (if any) + sum_j moe_w[t][j]*moe_y[t][j] (if any)
+//   otherwise:   x += sum of `add` splits (if any)
+//                     + sum_j moe_w[t][j] * (sum of moe splits at grouped row moe_inv[t*k+j]) (if moe_inv)
 // then a = x / sqrt(mean(x^2)+eps) * gain written as bf16 (hi, lo) and/or fp32.
 // ssq: scratch of T*ceil(d/1024) floats, used to split the work over columns
 // when there are few rows (may be null: one block per row).
 enum { RN_EMBED = 0, RN_ADD = 1 };
 void launch_residual_norm(hipStream_t st, int mode, int T, int d, float *x, const int32_t *tok,
-                          const void *embed, int embed_f32, Partials add, const float *moe_y,
+                          const void *embed, int embed_f32, Partials add, Partials moe, const int32_t *moe_inv,
                           const float *moe_w, int k, const float *gain, float eps, u16 *a_hi,
                           u16 *a_lo, float *a_f32, float *cap, float *ssq);
 
@@ -150,22 +151,26 @@ bool launch_attn_prefill_tiles(hipStream_t st, int T, int start_pos, int slot, c
 
 // MoE.  Router logits [T][E] -> softmax, top-k by repeated selection (ties to
 // the lower id), renormalised weights; then the (token, slot) pairs are grouped
-// by expert (counting sort, stable in (token, slot) order).  The logits are
-// the split partials `logits`, or, when router_w (bf16 [E][d]) is given, formed
+// by expert (counting sort, stable in (token, slot) order): pairs[r] is the
+// pair index t*k+j at grouped row r, and inv[t*k+j] = r.  The logits are the
+// split partials `logits`, or, when router_w (bf16 [E][d]) is given, formed
 // here from it and the (hi, lo) activation rows a_hi/a_lo [T][lda].
 void launch_moe_route(hipStream_t st, int T, int E, int k, Partials logits, const u16 *router_w, const u16 *a_hi,
                       const u16 *a_lo, int d, int lda, int32_t *ids, float *w, float *router_cap, int32_t *ids_cap,
-                      int32_t *counts, int32_t *offsets, int32_t *pairs);
+                      int32_t *counts, int32_t *offsets, int32_t *pairs, int32_t *inv);
 // Gather the normalised rows of the grouped pairs: dst[i] = src[pairs[i] / k].
 void launch_moe_gather(hipStream_t st, int T, int k, int d, const int32_t *pairs, const u16 *src_hi,
                        const u16 *src_lo, const float *src_f32, u16 *dst_hi, u16 *dst_lo, float *dst_f32);
-// Grouped expert projections: expert e (grid z) multiplies rows
-// [offsets[e], offsets[e+1]) of `a` by its slice (segs[i].w + e*expert_stride)
-// of the stacked weights [E][rows][K]; out rows follow the grouped order.
-// max_rows bounds any expert's row count (a token picks an expert at most once).
+// Grouped expert projections: expert e (grid z) multiplies grouped rows
+// [offsets[e], offsets[e+1]) by its slice (segs[i].w + e*expert_stride) of the
+// stacked weights [E][rows][K]; out rows follow the grouped order.  Grouped row
+// r reads row r of `a`, or, with row_pairs, token row row_pairs[r] / row_k of
+// `a` (the activations in token order, no gathered copy).  max_rows bounds any
+// expert's row count (a token picks an expert at most once).
 void launch_gemv_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi,
                          const u16 *a_lo, int lda, int max_rows, int E, const int32_t *offsets,
-                         size_t expert_stride, float *out, int ksplit, size_t split_stride, int ldo);
+                         size_t expert_stride, float *out, int ksplit, size_t split_stride, int ldo,
+                         const int32_t *row_pairs = nullptr, int row_k = 1);
 // The MFMA form for prefill rows (bf16 weights): 256-feature x 256-row tiles
 // per expert, k split in `ksplit` partials (out + s*split_stride) as
 // gemm_grouped_splits(N, K, pairs, E) suggests for `pairs` grouped rows.
@@ -184,8 +189,6 @@ bool launch_gemm_grouped_silu(hipStream_t st, const void *w_gate, const void *w_
 void launch_gemm_f32_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, const float *a, int lda,
                              int max_rows, int E, const int32_t *offsets, size_t expert_stride, float *out,
                              int ldo);
-// Scatter grouped expert outputs back to (token, slot) order: y[pairs[i]] = src[i].
-void launch_moe_scatter(hipStream_t st, int n_pairs, int d, const int32_t *pairs, Partials src, float *y);
 
 // Sum of GEMV split partials into a plain row-major destination.
 void launch_reduce_splits(hipStream_t st, Partials src, int T, int N, float *dst, int ldd);
