@@ -48,7 +48,7 @@ _ATTN_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_decode.hi
 _GEMV_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemv.hip":
                                  "11f73b184e2f0a6eac6252819b3d4309b847dfd1a45ddedad296e73af96448c6"})
 _GEMM_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemm.hip":
-                                 "2181d31cb0bd5c0e44380b70c915c2a1b43eb00012d6913039016e57d9af2b60"})
+                                 "3159cc0aeaa439120a04fdcaae9c0fa2474b7b4fa23deeac88d92dec54d73223"})
 _TILES_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_prefill_tiles.hip":
                                   "a057f7f417eda3f60000afda30eb547ff3158668784e1a69e880429eb018a86f"})
 MEASURED_TRAFFIC = {

@@ -270,6 +270,10 @@ constexpr int DSTAGE = 3 * DARR;             // W, A_hi, A_lo
 constexpr int DNSTAGE = 3;
 constexpr int DGROUP = 4;                    // token tiles an XCD walks together
 constexpr size_t DMA_LDS = DNSTAGE * DSTAGE * sizeof(u16);
+// grouped form: weights in their own ring of DNWS_G stages, then the DNSTAGE
+// stages of the activation pair (160 KB, the whole LDS of a CU)
+constexpr int DNWS_G = 4;
+constexpr size_t DMA_LDS_G = (DNWS_G * DARR + DNSTAGE * 2 * DARR) * sizeof(u16);
 #define LDS_AS __attribute__((address_space(3)))
 
 // 16-byte chunk c (of 4) of row r is stored at chunk c ^ ((r >> 2) & 3) of the row
@@ -380,6 +384,30 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
         }
     };
 
+    // grouped form: the weights (streamed from HBM once, no other block reads
+    // them) get a ring of DNWS_G stages and are loaded a k-tile further ahead
+    // than the activation rows, which other blocks of the expert share in L2
+    auto load_w = [&](int kt, int stage) {
+        const int k0 = (kt < nk ? kt : nk - 1) * DBK;
+        LDS_AS u16 *base = (LDS_AS u16 *)smem + stage * DARR;
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+            __builtin_amdgcn_global_load_lds((const void *)(srcw[i] + k0),
+                                             (LDS_AS void *)(base + (i * 8 + wv) * 512), 16, 0, 0);
+    };
+    auto load_a = [&](int kt, int stage, auto na_c) {
+        constexpr int NA = decltype(na_c)::value;
+        const int k0 = (kt < nk ? kt : nk - 1) * DBK;
+        LDS_AS u16 *base = (LDS_AS u16 *)smem + DNWS_G * DARR + stage * 2 * DARR;
+#pragma unroll
+        for (int i = 0; i < NA; i++) {
+            const int slot = (i * 8 + wv) * 512;
+            __builtin_amdgcn_global_load_lds((const void *)(srch[i] + k0), (LDS_AS void *)(base + slot), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(srcl[i] + k0), (LDS_AS void *)(base + DARR + slot), 16,
+                                             0, 0);
+        }
+    };
+
     floatx16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; i++)
@@ -391,9 +419,11 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
     const int r32 = lane & 31, c2 = lane >> 5;
     // grouped: a wave's 32-token sub-tiles past the expert's last row multiply nothing
     const bool live1 = !GROUPED || m0 + wm * 64 + 32 < M;
-    auto compute = [&](int stage) {
-        const u16 *sw = smem + stage * DSTAGE;
-        const u16 *sh = sw + DARR;
+    // stage s of the dense ring holds (W, A_hi, A_lo) together; the grouped
+    // form reads weight stage ws and activation stage s
+    auto compute = [&](int stage, int ws) {
+        const u16 *sw = GROUPED ? smem + ws * DARR : smem + stage * DSTAGE;
+        const u16 *sh = GROUPED ? smem + DNWS_G * DARR + stage * 2 * DARR : sw + DARR;
         const u16 *sl = sh + DARR;
 #pragma unroll
         for (int ks = 0; ks < DBK / 16; ks++) {
@@ -435,19 +465,41 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_dma_kernel(GemmParams p, u16 *_
     // barrier count).
     auto ring = [&](auto na_c) {
         constexpr int NA = decltype(na_c)::value;
-        constexpr int WAIT = (2 + 2 * NA) | (7 << 4) | (0 << 8);
-        load_tile(0, 0, na_c);
-        load_tile(1, 1, na_c);
-        __builtin_amdgcn_s_waitcnt(WAIT);
-        __builtin_amdgcn_s_barrier();
-        for (int kt = 0; kt < nk; kt++) {
-            // stage (kt+2)%3 held tile kt-1, which every wave finished reading
-            // before the previous barrier; tile kt+1 is complete after this
-            // iteration's wait
-            load_tile(kt + 2, (kt + 2) % DNSTAGE, na_c);
-            compute(kt % DNSTAGE);
+        if constexpr (!GROUPED) {
+            constexpr int WAIT = (2 + 2 * NA) | (7 << 4) | (0 << 8);
+            load_tile(0, 0, na_c);
+            load_tile(1, 1, na_c);
             __builtin_amdgcn_s_waitcnt(WAIT);
             __builtin_amdgcn_s_barrier();
+            for (int kt = 0; kt < nk; kt++) {
+                // stage (kt+2)%3 held tile kt-1, which every wave finished reading
+                // before the previous barrier; tile kt+1 is complete after this
+                // iteration's wait
+                load_tile(kt + 2, (kt + 2) % DNSTAGE, na_c);
+                compute(kt % DNSTAGE, 0);
+                __builtin_amdgcn_s_waitcnt(WAIT);
+                __builtin_amdgcn_s_barrier();
+            }
+        } else {
+            // issue order W0 A0 W1 A1 W2, then per k-tile A(kt+2) W(kt+3):
+            // once tile kt+1 is complete only W(kt+2), A(kt+2) and W(kt+3)
+            // (2 + 2 NA + 2 loads per wave) may still be outstanding.  Weight
+            // stage (kt+3)%4 and activation stage (kt+2)%3 held tile kt-1.
+            constexpr int WAIT = (4 + 2 * NA) | (7 << 4) | (0 << 8);
+            load_w(0, 0);
+            load_a(0, 0, na_c);
+            load_w(1, 1);
+            load_a(1, 1, na_c);
+            load_w(2, 2);
+            __builtin_amdgcn_s_waitcnt(WAIT);
+            __builtin_amdgcn_s_barrier();
+            for (int kt = 0; kt < nk; kt++) {
+                load_a(kt + 2, (kt + 2) % DNSTAGE, na_c);
+                load_w(kt + 3, (kt + 3) % DNWS_G);
+                compute(kt % DNSTAGE, kt % DNWS_G);
+                __builtin_amdgcn_s_waitcnt(WAIT);
+                __builtin_amdgcn_s_barrier();
+            }
         }
         // the loads issued past the last tile land in stages nobody reads again;
         // they must finish before the block's LDS is released
@@ -521,8 +573,10 @@ bool dma_lds_attr() {
         const void *ks[] = {(const void *)gemm_dma_kernel<false, false>, (const void *)gemm_dma_kernel<true, false>,
                             (const void *)gemm_dma_kernel<false, true>, (const void *)gemm_dma_kernel<true, true>};
         ok = 1;
-        for (const void *k : ks)
-            if (hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)DMA_LDS) != hipSuccess) ok = 0;
+        for (int i = 0; i < 4; i++)
+            if (hipFuncSetAttribute(ks[i], hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)(i < 2 ? DMA_LDS : DMA_LDS_G)) != hipSuccess)
+                ok = 0;
     }
     return ok == 1;
 }
@@ -632,7 +686,7 @@ void launch_gemm_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, cons
         }
         hipLaunchKernelGGL((gemm_dma_kernel<false, true>),
                            dim3((p.N + DBN - 1) / DBN, (max_rows + DBM - 1) / DBM, E * p.ksplit), dim3(DNTHR),
-                           DMA_LDS, st, p, nullptr, nullptr);
+                           DMA_LDS_G, st, p, nullptr, nullptr);
         return;
     }
     dim3 grid((p.N + BN - 1) / BN, (max_rows + BM - 1) / BM, E);
@@ -652,7 +706,7 @@ bool launch_gemm_grouped_silu(hipStream_t st, const void *w_gate, const void *w_
     p.grp_off = offsets;
     p.expert_stride = expert_stride;
     hipLaunchKernelGGL((gemm_dma_kernel<true, true>),
-                       dim3((F + DBN / 2 - 1) / (DBN / 2), (max_rows + DBM - 1) / DBM, E), dim3(DNTHR), DMA_LDS, st,
+                       dim3((F + DBN / 2 - 1) / (DBN / 2), (max_rows + DBM - 1) / DBM, E), dim3(DNTHR), DMA_LDS_G, st,
                        p, s_hi, s_lo);
     return true;
 }
