@@ -42,13 +42,13 @@ HBM_PEAK_GBS = 8000.0
 # to the ones profiled, and only for the profiled workload.  GEMV and GEMM
 # figures are the mean over the launches of one step's mix of projections.
 _COMMON = {"decoder_only_forward_amd/csrc/common.h":
-           "34608c55f95e88c4c9dc0713feb1c89be769be0a7ff3031fa8e6327276c4082b"}
+           "35cda32506ca4602aa9641fb45aba06fa60805f124e93a385f7219774610dd86"}
 _ATTN_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_decode.hip":
                                  "cae52ed058060b38e445bdb8323692f2f7481e38ec54819afc64a7fc8f14e507"})
 _GEMV_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemv.hip":
                                  "11f73b184e2f0a6eac6252819b3d4309b847dfd1a45ddedad296e73af96448c6"})
 _GEMM_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemm.hip":
-                                 "3159cc0aeaa439120a04fdcaae9c0fa2474b7b4fa23deeac88d92dec54d73223"})
+                                 "b6c93d8627347338ad306419c21f9804b100e108ec26529608633522f9a87189"})
 _TILES_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_prefill_tiles.hip":
                                   "a057f7f417eda3f60000afda30eb547ff3158668784e1a69e880429eb018a86f"})
 MEASURED_TRAFFIC = {
@@ -476,6 +476,9 @@ def main():
     ap.add_argument("--no-other", action="store_true", help="skip the other shapes' workloads")
     ap.add_argument("--layers", type=int, default=0,
                     help="with --only: keep this many layers (the per-layer shapes unchanged), e.g. for counter runs")
+    ap.add_argument("--prefill-fp8", action="store_true",
+                    help="with --only: prefill projections on fp16 + fp8 split operands (DEC_PREFILL_F16_F8) "
+                         "instead of the bf16 pair")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (sharded, each GPU would "
@@ -503,6 +506,8 @@ def main():
         c = configs.CONFIGS[name]
         if args.only and args.layers > 0:
             c = c.replace(name=f"{c.name}-{args.layers}l", n_layers=args.layers)
+        if args.only and args.prefill_fp8:
+            c = c.replace(name=f"{c.name}-prefill-f16f8", prefill_fp8=True)
         return c
 
     if args.only and args.only != "mistral-7b":
@@ -561,7 +566,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 weights x fp32 (split-bf16 MFMA), fp32 KV",
+        "dtype": ("bf16 weights x fp32 (split-bf16 MFMA), fp32 KV" if not cfg.prefill_fp8 else
+                  "bf16 weights x fp32 (decode: split-bf16 MFMA; prefill q|k|v and gate|up: fp16 + scaled fp8 "
+                  "split operands), fp32 KV"),
         "data": "synthetic (seeded random-init weights and prompts)",
         "config": {"workload": f"{cfg.name} decode B={B} at positions {P}.. (ring KV {cfg.max_seq}), "
                                f"prefill P={P}", "batch": B, "prompt": P, "layers": cfg.n_layers},
@@ -572,7 +579,10 @@ def main():
         "append_prefill_past_ring": main_run["append"],
         "ms_per_step_with_kernel_events": round(dt_timed * 1e3 / args.steps, 3),
         "roofline_kernels": {"gemv_decode": roof(gemv_t, "hbm", ("gemv_decode", "fp32")),
-                             "gemm_prefill": roof(gemm_t, "mfma", ("gemm_prefill", "fp32"), passes=2),
+                             # (with fp16 + fp8 operands the launches mix 1.5- and 2-unit forms:
+                             # no single pass count)
+                             "gemm_prefill": roof(gemm_t, "mfma", ("gemm_prefill", "fp32"),
+                                                  passes=None if cfg.prefill_fp8 else 2),
                              # hi*hi + hi*lo + lo*hi; causally masked halves of diagonal
                              # tiles run too, so the executed fraction is a lower bound
                              "attn_prefill": roof(apre_t, "mfma", ("attn_prefill", "fp32"), passes=3)},

@@ -50,6 +50,10 @@ class ModelConfig:
     rope_orig_ctx: int = 8192
     # K/V cache element type: False = fp32, True = bf16 (rounded to nearest even).
     kv_bf16: bool = False
+    # Prefill projections (more than 64 rows) on fp16 + fp8 split operands
+    # instead of the bf16 (hi, lo) pair: an arithmetic choice of the GPU path
+    # (DEC_PREFILL_F16_F8), not part of the model; the oracle ignores it.
+    prefill_fp8: bool = False
 
     @property
     def q_dim(self) -> int:

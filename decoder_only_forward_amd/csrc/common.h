@@ -40,6 +40,53 @@ __device__ __forceinline__ void split2_bf16(float a, float b, uint32_t &hi, uint
     lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_cvt){a - ah, b - bh}, bf16x2_cvt));
 }
 
+// ---- fp16 + fp8 split operands of the prefill projections ------------------
+// x = hi + lo with hi = fp16(x) (nearest even; |x| above the fp16 maximum is
+// first clamped to it) and lo = x - hi, exact in fp32 (|lo| <= 2^-11 |hi| for
+// normal hi).  lo is stored as OCP fp8 e4m3 (largest finite 448) with one E8M0
+// scale 2^(s - 127) per 32 consecutive k of a row: s - 127 is the smallest
+// exponent e with max |lo| <= 448 * 2^e over the 32 values, so the scaled
+// values stay finite and the largest keeps e4m3's 3 mantissa bits.
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t f16_split(float x, float &lo) {
+    const _Float16 h = (_Float16)fminf(fmaxf(x, -65504.f), 65504.f);
+    lo = x - (float)h;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+// E8M0 byte of a block whose largest magnitude is m (0 for an all-zero block).
+__device__ __forceinline__ uint32_t mx_scale_byte(float m) {
+    if (!(m > 0.f)) return 0u;
+    int ex;
+    const float f = frexpf(m, &ex);          // m = f * 2^ex, f in [0.5, 1)
+    // 448 = 0.875 * 2^9: m <= 448 * 2^(ex - 9) exactly when f <= 0.875
+    int e = ex - 9 + (f > 0.875f ? 1 : 0);
+    e = e < -127 ? -127 : (e > 127 ? 127 : e);
+    return (uint32_t)(e + 127);
+}
+
+// Four values times 2^(127 - s) as fp8 e4m3 (nearest even), value i in byte i.
+__device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d, uint32_t s) {
+    const int sh = 127 - (int)s;
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(a, sh), ldexpf(b, sh), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(c, sh), ldexpf(d, sh), w, true);
+    return (uint32_t)w;
+}
+
+// Position of row r's scale within its 256-row group, in the order the fp16 +
+// fp8 GEMM's lanes read them.  Weight rows: wave half wn = q / 128, row tile
+// i = (q / 32) % 4, lane row q % 32 -> 128 wn + 4 (q % 32) + i.  Token rows:
+// wave row group wm = q / 64, row tile j = (q / 32) % 2 -> 64 wm + 2 (q % 32) + j.
+__host__ __device__ __forceinline__ int f8_wsc_pos(int r) {
+    const int q = r & 255;
+    return (r & ~255) | (q & 128) | ((q & 31) << 2) | ((q >> 5) & 3);
+}
+__host__ __device__ __forceinline__ int f8_asc_pos(int r) {
+    const int q = r & 255;
+    return (r & ~255) | (q & 192) | ((q & 31) << 1) | ((q >> 5) & 1);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);

@@ -58,6 +58,10 @@ struct Plan {  // byte offsets into the workspace
     size_t moe_ids, moe_w, moe_cnt, moe_off, moe_pairs, moe_inv, g_hi, g_lo, g_f32;
     size_t part_floats, act_elems, total;
     int rows;               // max rows of one pass (max(max_batch, max_prefill))
+    // prefill projections on fp16 + fp8 operands: the converted weights of
+    // each layer (q|k|v, then for a dense FFN gate|up)
+    bool f8;
+    size_t f8w, f8_layer;
 };
 
 constexpr int MAX_ATTN_SPLITS = 64;
@@ -83,6 +87,11 @@ struct dec_model {
     float2 *rope;
     int32_t *tok, *pos, *slot, *amax, *moe_ids, *moe_cnt, *moe_off, *moe_pairs, *moe_inv;
     std::vector<int> len;
+    // converted weights of the prefill projections on fp16 + fp8 operands
+    struct F8Layer {
+        F8Weights qkv, gu;
+    };
+    std::vector<F8Layer> f8w;
     float *cap_hidden = nullptr, *cap_router = nullptr;
     int32_t *cap_ids = nullptr;
     Timing tm[DEC_K_COUNT];
@@ -116,13 +125,16 @@ bool plan(const dec_config &c, Plan &p) {
     p.kv_layer = (size_t)c.max_batch * c.n_kv_heads * c.max_seq * hd;
     const size_t kmax = std::max(std::max(d, qd), F);
     p.act_elems = prow * kmax;
+    // fp16 + fp8 prefill operands (bf16 weights: every k is already a multiple of 64)
+    p.f8 = c.prefill_operands == DEC_PREFILL_F16_F8 && c.weight_dtype == DEC_WEIGHT_BF16 && c.max_prefill > 64;
     // projection outputs: largest (splits x rows x N) over the projections
     size_t pf = 0;
     auto need = [&](int N, int K, int T) {
         // GEMM rows: room for the k split a 256-CU device takes (a device with
         // another count falls back to one split where the room is short)
-        const int S = (T <= 64) ? proj_splits(c, N, K, T)
-                                : (c.weight_dtype == DEC_WEIGHT_F32 ? 1 : gemm_splits_for(N, K, T, 256));
+        int S = (T <= 64) ? proj_splits(c, N, K, T)
+                          : (c.weight_dtype == DEC_WEIGHT_F32 ? 1 : gemm_splits_for(N, K, T, 256));
+        if (p.f8 && T > 64) S = std::max(S, gemm_splits_for(N, K, T, 256, 2));
         pf = std::max(pf, (size_t)S * T * N);
     };
     for (int T : {c.max_batch, std::min(c.max_prefill, 64), c.max_prefill}) {
@@ -162,6 +174,10 @@ bool plan(const dec_config &c, Plan &p) {
     // (prefill rows) or GEMV (up to 64 rows)
     const bool fuse_silu = !E && c.weight_dtype != DEC_WEIGHT_F32;
     const size_t s_rows = fuse_silu ? std::max<size_t>(c.max_prefill, std::min(rows, 64)) : 0;
+    // the fp16 + fp8 prefill operands reuse the (hi, lo) buffers: fp16 in hi,
+    // fp8 rows then [k/32][rows rounded up to 256] scales in lo
+    const size_t mpad = ((size_t)c.max_prefill + 255) / 256 * 256;
+    auto f8_lo = [&](size_t K) { return p.f8 ? mpad * K + (K / 32) * mpad : 0; };
     p.s_hi = take(s_rows * F * 2);
     p.s_lo = take(s_rows * F * 2);
     // prefill attention's K/V tile images (positions [0, max_seq) of one sequence)
@@ -170,7 +186,7 @@ bool plan(const dec_config &c, Plan &p) {
     p.x = take((size_t)rows * d * 4);
     const bool f32w = c.weight_dtype == DEC_WEIGHT_F32;
     p.a_hi = take(f32w ? 0 : p.act_elems * 2);
-    p.a_lo = take(f32w ? 0 : p.act_elems * 2);
+    p.a_lo = take(f32w ? 0 : std::max(p.act_elems * 2, f8_lo(d)));
     p.a_f32 = take(f32w ? p.act_elems * 4 : 0);
     p.part = take(pf * 4);
     p.q = take((size_t)rows * qd * 4);
@@ -190,6 +206,9 @@ bool plan(const dec_config &c, Plan &p) {
     p.g_hi = take(E && !f32w ? prow * d * 2 : 0);
     p.g_lo = take(E && !f32w ? prow * d * 2 : 0);
     p.g_f32 = take(E && f32w ? prow * d * 4 : 0);
+    p.f8_layer = p.f8 ? f8_weight_bytes((int)(qd + 2 * kvd), (int)d, false) + (E ? 0 : f8_weight_bytes((int)F, (int)d, true))
+                      : 0;
+    p.f8w = take(p.f8_layer * c.n_layers);
     p.total = off;
     return true;
 }
@@ -212,6 +231,9 @@ int validate_cfg(const dec_config *c) {
          !(c->rope_high_freq_factor > c->rope_low_freq_factor) || c->rope_orig_ctx <= 0))
         return DEC_ERR_INVALID;
     if (c->kv_dtype != DEC_KV_F32 && c->kv_dtype != DEC_KV_BF16) return DEC_ERR_INVALID;
+    if (c->prefill_operands != DEC_PREFILL_BF16_PAIR && c->prefill_operands != DEC_PREFILL_F16_F8)
+        return DEC_ERR_INVALID;
+    if (c->prefill_operands == DEC_PREFILL_F16_F8 && c->weight_dtype != DEC_WEIGHT_BF16) return DEC_ERR_INVALID;
     // shapes the kernels are written for
     if (c->max_batch > 64) return DEC_ERR_UNSUPPORTED;
     if (c->head_dim != 16 && c->head_dim != 64 && c->head_dim != 128) return DEC_ERR_UNSUPPORTED;
@@ -338,6 +360,18 @@ Partials proj(dec_model *m, const WSeg *segs, int nseg, int K, int T, const u16 
     return Partials{dst, S, S > 1 ? tn : 0, N};
 }
 
+// Projection of T > 64 prefill rows on fp16 + fp8 operands (F8Act `a`, the
+// converted weights `w`); split partials as proj's.
+Partials proj_f8(dec_model *m, const F8Weights &w, int T, const F8Act &a) {
+    const size_t tn = (size_t)T * w.N;
+    int S = gemm_splits_f8(w.N, w.K, T);
+    if ((size_t)S * tn > m->pl.part_floats) S = 1;
+    Tick tk(m, DEC_K_GEMM);
+    launch_gemm_f8(m->st, w, a.a16, a.a8, a.asc, a.mpad, a.lda, T, m->part, w.N, S, tn);
+    tk.done((double)w.N * w.K * 3 + (double)T * w.K * 3 + (double)T * w.N * 4, 2.0 * T * w.N * w.K);
+    return Partials{m->part, S, S > 1 ? tn : 0, w.N};
+}
+
 // Grouped expert projection over TP = T*k pair rows in expert order.
 // row_pairs (decode GEMV only): grouped row r reads token row row_pairs[r] / top_k
 // of (hi, lo) instead of row r.
@@ -383,10 +417,18 @@ void run_pass(dec_model *m, const Pass &ps) {
     auto caph = [&](int layer) -> float * {
         return m->cap_hidden ? m->cap_hidden + ((size_t)layer * ps.cap_rows + ps.cap_row) * d : nullptr;
     };
+    // Prefill rows of a model converted for fp16 + fp8 operands: each producer
+    // writes that form where its consumer is such a projection (q|k|v, the
+    // fused gate|up), the bf16 pair otherwise (o, down, the LM head, MoE).
+    const bool f8 = m->pl.f8 && !ps.decode && T > 64 && gemm_f8_ready();
+    const int mpad = (T + 255) / 256 * 256;
+    const F8Act fa_d{ah, (uint8_t *)al, (uint8_t *)al + (size_t)mpad * d, d, mpad};
+    // the fused gate|up takes these operands where it takes the DMA kernel
+    const bool f8_ffn = f8 && c.n_experts == 0 && (long)((F + 127) / 128) * ((T + 255) / 256) >= num_cus();
 
     launch_residual_norm(st, RN_EMBED, T, d, m->x, m->tok, m->embed, f32w, Partials{nullptr, 0, 0, 0},
                          Partials{nullptr, 0, 0, 0}, nullptr, nullptr, 0, m->L[0].attn_norm, eps, ah, al, af, caph(0),
-                         m->ssq);
+                         m->ssq, f8 ? &fa_d : nullptr);
     launch_rope_table(st, m->pos, T, hd, c.rope_theta, c.rope_scaling, c.rope_factor, c.rope_low_freq_factor,
                       c.rope_high_freq_factor, c.rope_orig_ctx, m->rope);
 
@@ -397,7 +439,7 @@ void run_pass(dec_model *m, const Pass &ps) {
         const int kvb = m->kv_es == 2;
         // q | k | v
         WSeg qkv[3] = {{w.wq, qd}, {w.wk, kvd}, {w.wv, kvd}};
-        Partials pq = proj(m, qkv, 3, d, T, ah, al, af, d);
+        Partials pq = f8 ? proj_f8(m, m->f8w[l].qkv, T, fa_d) : proj(m, qkv, 3, d, T, ah, al, af, d);
         // attention -> a (row stride qd)
         if (ps.decode) {
             // RoPE and the new K/V rows are formed inside the attention kernel
@@ -439,13 +481,19 @@ void run_pass(dec_model *m, const Pass &ps) {
         WSeg wo[1] = {{w.wo, d}};
         Partials po = proj(m, wo, 1, qd, T, ah, al, af, qd);
         launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, po, Partials{nullptr, 0, 0, 0}, nullptr,
-                             nullptr, 0, w.ffn_norm, eps, ah, al, af, nullptr, m->ssq);
+                             nullptr, 0, w.ffn_norm, eps, ah, al, af, nullptr, m->ssq, f8_ffn ? &fa_d : nullptr);
         const float *next_gain = (l + 1 < c.n_layers) ? m->L[l + 1].attn_norm : m->out_norm;
         if (c.n_experts == 0) {
             WSeg gu[2] = {{w.w_gate, F}, {w.w_up, F}};
             // a large prefill takes the gate|up GEMM with silu(gate) * up in its epilogue
             bool fused = false;
-            if (!f32w && T > 64 && m->s_hi) {
+            if (f8_ffn) {
+                Tick tk(m, DEC_K_GEMM);
+                fused = launch_gemm_f8_silu(st, m->f8w[l].gu, fa_d.a16, fa_d.a8, fa_d.asc, mpad, d, T, m->s_hi,
+                                            m->s_lo, F);
+                if (fused) tk.done(2.0 * F * d * 3 + (double)T * d * 3 + (double)T * F * 4, 2.0 * T * 2 * F * d);
+                else tk.cancel();
+            } else if (!f32w && T > 64 && m->s_hi) {
                 Tick tk(m, DEC_K_GEMM);
                 fused = launch_gemm_silu(st, w.w_gate, w.w_up, F, d, ah, al, d, T, m->s_hi, m->s_lo, F);
                 if (fused) tk.done(2.0 * F * d * 2 + (double)T * d * 4 + (double)T * F * 4, 2.0 * T * 2 * F * d);
@@ -467,7 +515,8 @@ void run_pass(dec_model *m, const Pass &ps) {
             WSeg wd[1] = {{w.w_down, d}};
             Partials pd = proj(m, wd, 1, F, T, fused ? m->s_hi : ah, fused ? m->s_lo : al, af, F);
             launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, pd, Partials{nullptr, 0, 0, 0},
-                                 nullptr, nullptr, 0, next_gain, eps, ah, al, af, caph(l + 1), m->ssq);
+                                 nullptr, nullptr, 0, next_gain, eps, ah, al, af, caph(l + 1), m->ssq,
+                                 f8 && l + 1 < c.n_layers ? &fa_d : nullptr);
         } else {
             const int E = c.n_experts, k = c.top_k, TP = T * k;
             // router logits: the GEMV for decode rows and fp32 weights; prefill
@@ -510,7 +559,8 @@ void run_pass(dec_model *m, const Pass &ps) {
             Partials pd = proj_grouped(m, wd, 1, F, T, ah, al, af, F);
             // the residual reads each token's expert outputs at their grouped rows
             launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, Partials{nullptr, 0, 0, 0}, pd,
-                                 m->moe_inv, m->moe_w, k, next_gain, eps, ah, al, af, caph(l + 1), m->ssq);
+                                 m->moe_inv, m->moe_w, k, next_gain, eps, ah, al, af, caph(l + 1), m->ssq,
+                                 f8 && l + 1 < c.n_layers ? &fa_d : nullptr);
         }
     }
     // LM head on the rows that need logits (a holds the final-norm rows)
@@ -726,6 +776,30 @@ int dec_create(const dec_config *cfg, const dec_weights *w, void *workspace, siz
     // a ring of max_seq == window slots; a window longer than max_seq never
     // wraps (positions are capped at max_seq like a full-causal cache)
     m->ring = cfg->sliding_window > 0 && cfg->max_seq == cfg->sliding_window;
+    if (p.f8) {
+        // the prefill projections' fp16 + fp8 weights, converted on the stream
+        const int d = cfg->hidden, qd = cfg->n_heads * cfg->head_dim, kvd = cfg->n_kv_heads * cfg->head_dim;
+        const int F = cfg->ffn_dim;
+        m->f8w.assign(cfg->n_layers, dec_model::F8Layer{});
+        for (int l = 0; l < cfg->n_layers; l++) {
+            const dec_layer_weights &L = m->L[l];
+            dec_model::F8Layer &f = m->f8w[l];
+            char *at = b + p.f8w + (size_t)l * p.f8_layer;
+            f.qkv = f8_weights_at(at, qd + 2 * kvd, d, false);
+            at += f8_weight_bytes(qd + 2 * kvd, d, false);
+            WSeg qkv[3] = {{L.wq, qd}, {L.wk, kvd}, {L.wv, kvd}};
+            launch_convert_f8(m->st, qkv, 3, d, false, f.qkv);
+            if (!cfg->n_experts) {
+                f.gu = f8_weights_at(at, F, d, true);
+                WSeg gu[2] = {{L.w_gate, F}, {L.w_up, F}};
+                launch_convert_f8(m->st, gu, 2, d, true, f.gu);
+            }
+        }
+        if (hipGetLastError() != hipSuccess) {
+            delete m;
+            return DEC_ERR_DEVICE;
+        }
+    }
     *out = m;
     return DEC_OK;
 }

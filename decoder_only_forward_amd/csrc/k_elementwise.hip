@@ -14,7 +14,7 @@ __global__ void __launch_bounds__(NTH) residual_norm_kernel(
     int mode, int d, float *__restrict__ x, const int32_t *__restrict__ tok,
     const void *__restrict__ embed, int embed_f32, Partials add, Partials moe, const int32_t *__restrict__ moe_inv,
     const float *__restrict__ moe_w, int k, const float *__restrict__ gain, float eps,
-    u16 *__restrict__ a_hi, u16 *__restrict__ a_lo, float *__restrict__ a_f32, float *__restrict__ cap) {
+    u16 *__restrict__ a_hi, u16 *__restrict__ a_lo, float *__restrict__ a_f32, float *__restrict__ cap, F8Act f8) {
     __shared__ float red[16];
     const int t = blockIdx.x;
     const int nv = d / 4;
@@ -79,7 +79,22 @@ __global__ void __launch_bounds__(NTH) residual_norm_kernel(
         a.x = v[u].x * rs * g[u].x; a.y = v[u].y * rs * g[u].y;
         a.z = v[u].z * rs * g[u].z; a.w = v[u].w * rs * g[u].w;
         if (a_f32) *reinterpret_cast<float4 *>(a_f32 + off) = a;
-        if (a_hi) {
+        if (f8.a16) {
+            // fp16 + fp8 operands: the 8 threads of a 32-column block (d a
+            // multiple of 32) share its scale, kept by the first of them
+            float l0, l1, l2, l3;
+            const uint32_t h0 = f16_split(a.x, l0), h1 = f16_split(a.y, l1);
+            const uint32_t h2 = f16_split(a.z, l2), h3 = f16_split(a.w, l3);
+            float mx = fmaxf(fmaxf(fabsf(l0), fabsf(l1)), fmaxf(fabsf(l2), fabsf(l3)));
+            mx = fmaxf(mx, __shfl_xor(mx, 1, WAVE));
+            mx = fmaxf(mx, __shfl_xor(mx, 2, WAVE));
+            mx = fmaxf(mx, __shfl_xor(mx, 4, WAVE));
+            const uint32_t sb = mx_scale_byte(mx);
+            const size_t fo = (size_t)t * f8.lda + 4 * i4;
+            *reinterpret_cast<uint2 *>(f8.a16 + fo) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+            *reinterpret_cast<uint32_t *>(f8.a8 + fo) = fp8x4(l0, l1, l2, l3, sb);
+            if ((threadIdx.x & 7) == 0) f8.asc[(size_t)(i4 >> 3) * f8.mpad + f8_asc_pos(t)] = (uint8_t)sb;
+        } else if (a_hi) {
             uint2 h, l;
             split2_bf16(a.x, a.y, h.x, l.x);
             split2_bf16(a.z, a.w, h.y, l.y);
@@ -156,13 +171,15 @@ __global__ void __launch_bounds__(256) norm_chunk_kernel(int d, const float *__r
 void launch_residual_norm(hipStream_t st, int mode, int T, int d, float *x, const int32_t *tok,
                           const void *embed, int embed_f32, Partials add, Partials moe, const int32_t *moe_inv,
                           const float *moe_w, int k, const float *gain, float eps, u16 *a_hi,
-                          u16 *a_lo, float *a_f32, float *cap, float *ssq) {
+                          u16 *a_lo, float *a_f32, float *cap, float *ssq, const F8Act *f8) {
     if (T <= 0) return;
     const int nv = d / 4;
+    // fp16 + fp8 operands: prefill rows only (one block per row, d % 32 == 0)
+    const F8Act f8a = (f8 && T > 64 && d % 32 == 0) ? *f8 : F8Act{nullptr, nullptr, nullptr, 0, 0};
     if (T <= 64 && nv <= 1024) {
         // few rows: one 1024-thread block per row, one float4 per thread
 #define RN1(NT) hipLaunchKernelGGL((residual_norm_kernel<1, NT>), dim3(T), dim3(NT), 0, st, mode, d, x, tok, embed, \
-                                   embed_f32, add, moe, moe_inv, moe_w, k, gain, eps, a_hi, a_lo, a_f32, cap)
+                                   embed_f32, add, moe, moe_inv, moe_w, k, gain, eps, a_hi, a_lo, a_f32, cap, f8a)
         if (nv <= 256) RN1(256);
         else RN1(1024);
 #undef RN1
@@ -178,7 +195,8 @@ void launch_residual_norm(hipStream_t st, int mode, int T, int d, float *x, cons
     }
     const int vpt = (nv + 255) / 256;
 #define RN(V) hipLaunchKernelGGL((residual_norm_kernel<V, 256>), dim3(T), dim3(256), 0, st, mode, d, x, tok, \
-                                 embed, embed_f32, add, moe, moe_inv, moe_w, k, gain, eps, a_hi, a_lo, a_f32, cap)
+                                 embed, embed_f32, add, moe, moe_inv, moe_w, k, gain, eps, a_hi, a_lo, a_f32, cap, \
+                                 f8a)
     if (vpt <= 1) RN(1);
     else if (vpt <= 2) RN(2);
     else if (vpt <= 4) RN(4);

@@ -583,7 +583,7 @@ bool dma_lds_attr() {
 
 }  // namespace
 
-int gemm_splits_for(int N, int K, int M, int cus) {
+int gemm_splits_for(int N, int K, int M, int cus, int kmul) {
     // Grids of at least one 256 x 256 tile per CU take the direct-to-LDS
     // kernel; one whose last round is at most half full (1.5 rounds of q+k+v
     // at 4096 tokens) is split in two over k, which evens the rounds.
@@ -591,7 +591,7 @@ int gemm_splits_for(int N, int K, int M, int cus) {
     const long nb = (long)((N + DBN - 1) / DBN) * ((M + DBM - 1) / DBM);
     const int kt = K / DBK;
     if (nb >= cus) {
-        if (kt % 2) return 1;
+        if (kt % (2 * kmul)) return 1;
         const long r1 = (nb + cus - 1) / cus, r2 = (2 * nb + cus - 1) / cus;
         return r2 < 2 * r1 ? 2 : 1;
     }
@@ -606,7 +606,7 @@ int gemm_splits_for(int N, int K, int M, int cus) {
     int best = 1;
     double bt = (double)kt * tk;
     for (int s = 2; s <= 16 && kt / s >= 4; s++) {
-        if (kt % s) continue;
+        if (kt % s || (kt / s) % kmul) continue;
         const double rounds = (double)((nb * s + cus - 1) / cus);
         const double t = rounds * (kt / s) * tk + (s - 1) * extra;
         if (t < bt) { bt = t; best = s; }
@@ -615,6 +615,7 @@ int gemm_splits_for(int N, int K, int M, int cus) {
 }
 
 int gemm_splits(int N, int K, int M) { return gemm_splits_for(N, K, M, num_cus()); }
+int gemm_splits_f8(int N, int K, int M) { return gemm_splits_for(N, K, M, num_cus(), 2); }
 
 void launch_gemm(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi, const u16 *a_lo,
                  int lda, int M, float *out, int ldo, int ksplit, size_t split_stride) {
@@ -708,6 +709,444 @@ bool launch_gemm_grouped_silu(hipStream_t st, const void *w_gate, const void *w_
     hipLaunchKernelGGL((gemm_dma_kernel<true, true>),
                        dim3((F + DBN / 2 - 1) / (DBN / 2), (max_rows + DBM - 1) / DBM, E), dim3(DNTHR), DMA_LDS_G, st,
                        p, s_hi, s_lo);
+    return true;
+}
+
+// ---- prefill projections on fp16 + fp8 operands -----------------------------
+// y = W a with a = a16 + lo (the split of f16_split) and W exact in fp16: the
+// hi pass multiplies W16 by a16 on fp16 MFMAs (32x32x16), the lo pass an fp8
+// copy of W by the fp8 lo, each with an E8M0 scale per 32 k of a row, on the
+// scaled fp8 MFMA (32x32x64), which runs at twice the bf16 rate.  Since
+// |lo| <= 2^-11 |a16|, e4m3's rounding of either lo operand costs about
+// 2^-15 of a product; the two passes cost 1.5 bf16-MFMA units per product
+// against 2 for gemm_dma_kernel's bf16 (hi, lo) pair.
+//
+// Operands (bytes): W16 [npad][K] fp16, W8 [npad][K] e4m3, wsc [K/32][npad];
+// A16 [M][lda] fp16, A8 [M][lda] e4m3, asc [K/32][mpad] (mpad = M rounded up
+// to 256).  Within each 256 rows the scales are stored in the order the
+// lanes take them (f8_wsc_pos, f8_asc_pos): a lane's 4 weight row tiles (i)
+// and 2 token row tiles (j) give one 32-bit and one 16-bit word, byte i or j
+// being the scale the MFMA's selector picks.  Weight rows are stored in the kernel's tile order (the converter
+// writes them so): tile tn holds rows [256 tn, 256 tn + 256).  A SILU tile's
+// row r is wave half r / 128, MFMA row tile (r % 128) / 32 (0, 1 gate; 2, 3 up),
+// i.e. gate or up feature 128 tn + 64 (r / 128) + 32 ((r / 32) & 1) + r % 32.
+//
+// Stage = one 32-k tile: W16 and A16 as in gemm_dma_kernel (64-byte rows,
+// swizzled chunks), W8 and A8 (32-byte rows, halves swizzled), the 256
+// weight-row and 256 token-row scales of the tile's k block.  The fp8 MFMA takes 64 k: lane l
+// (row l % 32, half c2 = l / 32) supplies bytes [16 c2, 16 c2 + 16) of its row
+// from the even k-tile and the same bytes from the odd one that follows, and
+// the scale of its row's even (lanes < 32) or odd (lanes >= 32) k block.  The
+// even tile's fragments and scales are kept in registers until the odd tile
+// (the ring refills the even tile's stage while the odd one is multiplied).
+namespace {
+
+// 16-byte half h of fp8 row r sits at half h ^ f(r) of the row in LDS, so the
+// 32 rows an fp8 fragment read touches spread over all banks
+__device__ __forceinline__ int f8_half(int r, int h) { return h ^ (((r >> 2) ^ (r >> 3)) & 1); }
+
+struct GemmF8Params {
+    const u16 *w16;
+    const uint8_t *w8, *wsc;
+    const u16 *a16;
+    const uint8_t *a8, *asc;
+    int N, K, M, npad, mpad, lda;
+    float *out;
+    int ldo, kchunk;
+    size_t split_stride;
+    u16 *s_hi, *s_lo;
+};
+
+// stage layout, in u16
+constexpr int F8_W16 = 0, F8_A16 = 8192, F8_W8 = 16384, F8_A8 = 20480, F8_WSC = 24576, F8_ASC = 24704;
+constexpr int F8_STG = 24832;
+constexpr size_t F8_LDS = (size_t)DNSTAGE * F8_STG * sizeof(u16);
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <bool SILU>
+__global__ void __launch_bounds__(DNTHR, 1) gemm_f8_kernel(GemmF8Params p) {
+    extern __shared__ __attribute__((aligned(16))) u16 smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid % WAVE, wv = __builtin_amdgcn_readfirstlane(tid / WAVE);
+    const int wn = wv & 1, wm = wv >> 1;
+    const int M = p.M, kz = blockIdx.z;
+    constexpr int FPT = SILU ? DBN / 2 : DBN;
+    const int ntn = (p.N + FPT - 1) / FPT, ntm = gridDim.y;
+    const int bid = blockIdx.x + blockIdx.y * gridDim.x;
+    int tn, tm;
+    if ((ntn & 7) == 0) {
+        const int x = bid & 7, lt = bid >> 3, nx = ntn >> 3;
+        const int G = DGROUP < ntm ? DGROUP : ntm;
+        const int tg = lt / (G * nx), rem = lt - tg * G * nx;
+        const int gsz = min(G, ntm - tg * G);
+        tn = x * nx + rem / gsz;
+        tm = tg * G + rem % gsz;
+    } else {
+        int b = bid;
+        const int nblk = ntn * ntm;
+        if ((nblk & 7) == 0) b = (b & 7) * (nblk >> 3) + (b >> 3);
+        tn = b / ntm;
+        tm = b % ntm;
+    }
+    const int m0 = tm * DBM;
+    if (m0 >= M) return;
+    const int n0 = tn * FPT, r0 = tn * DBN;
+    const int kz0 = kz * p.kchunk;
+    const int nk = min(p.kchunk, p.K - kz0) / DBK;   // even
+
+    // load i (0, 1) of W16 / A16: row (i*8 + wv)*16 + lane/4, logical chunk
+    // (lane & 3) ^ ((row >> 2) & 3); W8 / A8: row wv*32 + lane/2, logical half
+    // f8_half(row, lane & 1); scales: lanes 0-15 of wave 0 the 256 weight-row
+    // bytes, of wave 1 the 256 token-row bytes (the other waves load none)
+    const u16 *srcw[2], *srca[2];
+#pragma unroll
+    for (int i = 0; i < 2; i++) {
+        const int P = (i * 8 + wv) * 64 + lane;
+        const int r = P >> 2, c = (P & 3) ^ ((r >> 2) & 3);
+        srcw[i] = p.w16 + (size_t)(r0 + r) * p.K + kz0 + c * 8;
+        const int m = min(m0 + r, M - 1);
+        srca[i] = p.a16 + (size_t)m * p.lda + kz0 + c * 8;
+    }
+    const int r8 = (wv * 64 + lane) >> 1, c8 = f8_half(r8, lane & 1);
+    const uint8_t *srcw8 = p.w8 + (size_t)(r0 + r8) * p.K + kz0 + c8 * 16;
+    const uint8_t *srca8 = p.a8 + (size_t)min(m0 + r8, M - 1) * p.lda + kz0 + c8 * 16;
+    const uint8_t *srcsc = wv == 0 ? p.wsc + r0 + lane * 16 : p.asc + m0 + lane * 16;
+    const size_t scp = wv == 0 ? (size_t)p.npad : (size_t)p.mpad;
+    const int scdst = wv == 0 ? F8_WSC : F8_ASC;
+    const int kb0 = kz0 / DBK;
+
+    auto load_tile = [&](int kt, int stage, auto na_c, auto sc_c) {
+        constexpr int NA = decltype(na_c)::value;
+        constexpr int SC = decltype(sc_c)::value;
+        const int t = kt < nk ? kt : nk - 1;
+        const int k0 = t * DBK;
+        LDS_AS u16 *base = (LDS_AS u16 *)smem + stage * F8_STG;
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+            __builtin_amdgcn_global_load_lds((const void *)(srcw[i] + k0),
+                                             (LDS_AS void *)(base + F8_W16 + (i * 8 + wv) * 512), 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NA; i++)
+            __builtin_amdgcn_global_load_lds((const void *)(srca[i] + k0),
+                                             (LDS_AS void *)(base + F8_A16 + (i * 8 + wv) * 512), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(srcw8 + k0), (LDS_AS void *)(base + F8_W8 + wv * 512), 16,
+                                         0, 0);
+        __builtin_amdgcn_global_load_lds((const void *)(srca8 + k0), (LDS_AS void *)(base + F8_A8 + wv * 512), 16,
+                                         0, 0);
+        if (SC && lane < 16)
+            __builtin_amdgcn_global_load_lds((const void *)(srcsc + (size_t)(kb0 + t) * scp),
+                                             (LDS_AS void *)(base + scdst), 16, 0, 0);
+    };
+
+    floatx16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++)
+#pragma unroll
+            for (int e = 0; e < 16; e++) acc[i][j][e] = 0.f;
+
+    const int r32 = lane & 31, c2 = lane >> 5;
+    // hi pass of one k-tile: fp16 MFMAs as gemm_dma_kernel's bf16 ones
+    auto hi_pass = [&](int s) {
+        const u16 *sw = smem + s * F8_STG + F8_W16;
+        const u16 *sa = smem + s * F8_STG + F8_A16;
+#pragma unroll
+        for (int ks = 0; ks < DBK / 16; ks++) {
+            f16x8 fw[4], fa[2];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                fw[i] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
+                                                      sw + 8 * dswz(wn * 128 + i * 32 + r32, 2 * ks + c2)));
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+                fa[j] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
+                                                      sa + 8 * dswz(wm * 64 + j * 32 + r32, 2 * ks + c2)));
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+#pragma unroll
+                for (int j = 0; j < 2; j++)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fw[i], fa[j], acc[i][j], 0, 0, 0);
+        }
+    };
+    // the fp8 fragments of stage s (bytes [16 c2, 16 c2 + 16) of each row) and
+    // its scales, packed one byte per row tile (weights: byte i, tokens: byte j)
+    auto lo_frags = [&](int s, u32x4 (&w8)[4], u32x4 (&a8)[2], uint32_t &ws, uint32_t &as) {
+        const uint8_t *sb = reinterpret_cast<const uint8_t *>(smem + s * F8_STG);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int row = wn * 128 + i * 32 + r32;
+            w8[i] = *reinterpret_cast<const u32x4 *>(sb + 2 * F8_W8 + row * 32 + f8_half(row, c2) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int row = wm * 64 + j * 32 + r32;
+            a8[j] = *reinterpret_cast<const u32x4 *>(sb + 2 * F8_A8 + row * 32 + f8_half(row, c2) * 16);
+        }
+        // the scales of the lane's 4 weight / 2 token row tiles, one word each
+        ws = *reinterpret_cast<const uint32_t *>(sb + 2 * F8_WSC + wn * 128 + r32 * 4);
+        as = *reinterpret_cast<const uint16_t *>(sb + 2 * F8_ASC + wm * 64 + r32 * 2);
+    };
+
+    // per k-tile and wave: 2 W16 + NA A16 + W8 + A8 (+ the scales on waves 0,
+    // 1) = 4 + NA (+ 1) loads; the wait leaves the newest tile's in flight (see
+    // gemm_dma_kernel), and the loop is instantiated per count.  The
+    // loop takes k-tiles in pairs (nk is even): the even tile's fp8 fragments
+    // and scales stay in registers, since the odd iteration's load refills the
+    // even tile's stage.
+    auto ring = [&](auto na_c, auto sc_c) {
+        constexpr int NA = decltype(na_c)::value;
+        constexpr int WAIT = (4 + NA + decltype(sc_c)::value) | (7 << 4) | (0 << 8);
+        load_tile(0, 0, na_c, sc_c);
+        load_tile(1, 1, na_c, sc_c);
+        __builtin_amdgcn_s_waitcnt(WAIT);
+        __builtin_amdgcn_s_barrier();
+        for (int kt = 0; kt < nk; kt += 2) {
+            const int se = kt % DNSTAGE, so = (kt + 1) % DNSTAGE;
+            load_tile(kt + 2, (kt + 2) % DNSTAGE, na_c, sc_c);
+            u32x4 w8e[4], a8e[2];
+            uint32_t wse, ase;
+            lo_frags(se, w8e, a8e, wse, ase);
+            hi_pass(se);
+            __builtin_amdgcn_s_waitcnt(WAIT);
+            __builtin_amdgcn_s_barrier();
+            load_tile(kt + 3, (kt + 3) % DNSTAGE, na_c, sc_c);
+            u32x4 w8o[4], a8o[2];
+            uint32_t wso, aso;
+            lo_frags(so, w8o, a8o, wso, aso);
+            // lanes < 32 give the even k block's scales, lanes >= 32 the odd one's
+            const int wsc = (int)(c2 ? wso : wse), asc = (int)(c2 ? aso : ase);
+            hi_pass(so);
+            i32x8 wop[4], aop[2];
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                wop[i] = i32x8{(int)w8e[i][0], (int)w8e[i][1], (int)w8e[i][2], (int)w8e[i][3],
+                               (int)w8o[i][0], (int)w8o[i][1], (int)w8o[i][2], (int)w8o[i][3]};
+#pragma unroll
+            for (int j = 0; j < 2; j++)
+                aop[j] = i32x8{(int)a8e[j][0], (int)a8e[j][1], (int)a8e[j][2], (int)a8e[j][3],
+                               (int)a8o[j][0], (int)a8o[j][1], (int)a8o[j][2], (int)a8o[j][3]};
+            // (the scale byte selectors are immediates)
+#define F8MMA(I, J) \
+    acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop[I], aop[J], acc[I][J], 0, 0, I, wsc, J, asc)
+            F8MMA(0, 0); F8MMA(0, 1); F8MMA(1, 0); F8MMA(1, 1);
+            F8MMA(2, 0); F8MMA(2, 1); F8MMA(3, 0); F8MMA(3, 1);
+#undef F8MMA
+            __builtin_amdgcn_s_waitcnt(WAIT);
+            __builtin_amdgcn_s_barrier();
+        }
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+    };
+    const int na = (m0 + wv * 16 < M) + (m0 + (8 + wv) * 16 < M);   // wave-uniform
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    if (wv < 2) {
+        if (na == 2) ring(I2{}, I1{});
+        else if (na == 1) ring(I1{}, I1{});
+        else ring(I0{}, I1{});
+    } else {
+        if (na == 2) ring(I2{}, I0{});
+        else if (na == 1) ring(I1{}, I0{});
+        else ring(I0{}, I0{});
+    }
+
+    if constexpr (SILU) {
+        // acc[i][j] (gate, i = 0, 1) and acc[i+2][j] (up): feature
+        // n0 + wn*64 + i*32 + (e/4)*8 + c2*4 + e%4, token m0 + wm*64 + j*32 + r32
+#pragma unroll
+        for (int i = 0; i < 2; i++)
+#pragma unroll
+            for (int j = 0; j < 2; j++) {
+                const int m = m0 + wm * 64 + j * 32 + r32;
+                if (m >= M) continue;
+#pragma unroll
+                for (int g = 0; g < 4; g++) {
+                    const int f = n0 + wn * 64 + i * 32 + g * 8 + c2 * 4;
+                    uint32_t hb[4], lb[4];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        const float gt = acc[i][j][4 * g + e], up = acc[i + 2][j][4 * g + e];
+                        split_bf16(gt / (1.0f + expf(-gt)) * up, hb[e], lb[e]);
+                    }
+                    const size_t off = (size_t)m * p.ldo + f;
+                    if (f + 3 < p.N) {
+                        *reinterpret_cast<uint2 *>(p.s_hi + off) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+                        *reinterpret_cast<uint2 *>(p.s_lo + off) = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; e++)
+                            if (f + e < p.N) {
+                                p.s_hi[off + e] = (u16)hb[e];
+                                p.s_lo[off + e] = (u16)lb[e];
+                            }
+                    }
+                }
+            }
+        return;
+    }
+    // acc[i][j]: features n0 + wn*128 + i*32 + (e/4)*8 + c2*4 + e%4, token m0 + wm*64 + j*32 + r32
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const int m = m0 + wm * 64 + j * 32 + r32;
+            if (m >= M) continue;
+            float *dst = p.out + kz * p.split_stride + (size_t)m * p.ldo;
+#pragma unroll
+            for (int g = 0; g < 4; g++) {
+                const int n = n0 + wn * 128 + i * 32 + g * 8 + c2 * 4;
+                const floatx16 &v = acc[i][j];
+                if (n + 3 < p.N) {
+                    *reinterpret_cast<float4 *>(dst + n) = make_float4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
+                } else {
+                    if (n < p.N) dst[n] = v[4 * g];
+                    if (n + 1 < p.N) dst[n + 1] = v[4 * g + 1];
+                    if (n + 2 < p.N) dst[n + 2] = v[4 * g + 2];
+                }
+            }
+        }
+}
+
+bool f8_lds_attr() {
+    static int ok = -1;
+    if (ok < 0) {
+        ok = hipFuncSetAttribute((const void *)gemm_f8_kernel<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)F8_LDS) == hipSuccess &&
+             hipFuncSetAttribute((const void *)gemm_f8_kernel<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                 (int)F8_LDS) == hipSuccess;
+    }
+    return ok == 1;
+}
+
+// Converted weights: row R of the output (kernel tile order), k block kb of
+// 32: W16 = fp16(W), W8 = e4m3(W / 2^e) with the block's E8M0 scale at
+// wsc[kb * npad + f8_wsc_pos(R)]; rows past the matrix are zero.
+__global__ void __launch_bounds__(256) convert_f8_kernel(const u16 *__restrict__ s0, const u16 *__restrict__ s1,
+                                                          const u16 *__restrict__ s2, int e0, int e1, int N, int K,
+                                                          int silu_f, int npad, u16 *__restrict__ w16,
+                                                          uint8_t *__restrict__ w8, uint8_t *__restrict__ wsc) {
+    const int nb = K / 32;
+    const long idx = blockIdx.x * (long)blockDim.x + threadIdx.x;
+    if (idx >= (long)npad * nb) return;
+    const int R = (int)(idx / nb), kb = (int)(idx % nb);
+    const u16 *src = nullptr;
+    if (silu_f > 0) {
+        const int tn = R >> 8, r = R & 255, t = (r >> 5) & 3;
+        const int f = tn * 128 + (r >> 7) * 64 + (t & 1) * 32 + (r & 31);
+        if (f < silu_f) src = (t < 2 ? s0 : s1) + (size_t)f * K;
+    } else if (R < N) {
+        src = R < e0 ? s0 + (size_t)R * K : (R < e1 ? s1 + (size_t)(R - e0) * K : s2 + (size_t)(R - e1) * K);
+    }
+    float v[32];
+    float mx = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        u32x4 b = src ? *reinterpret_cast<const u32x4 *>(src + kb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            v[q * 8 + 2 * e] = bf16_bits_to_f32(b[e] & 0xFFFFu);
+            v[q * 8 + 2 * e + 1] = __uint_as_float(b[e] & 0xFFFF0000u);
+        }
+    }
+    u16 *dst16 = w16 + (size_t)R * K + kb * 32;
+#pragma unroll
+    for (int q = 0; q < 4; q++) {
+        u32x4 h;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            float lo0, lo1;
+            h[e] = f16_split(v[q * 8 + 2 * e], lo0) | (f16_split(v[q * 8 + 2 * e + 1], lo1) << 16);
+        }
+        *reinterpret_cast<u32x4 *>(dst16 + q * 8) = h;
+    }
+#pragma unroll
+    for (int i = 0; i < 32; i++) mx = fmaxf(mx, fabsf(v[i]));
+    const uint32_t sb = mx_scale_byte(mx);
+    wsc[(size_t)kb * npad + f8_wsc_pos(R)] = (uint8_t)sb;
+    uint8_t *dst8 = w8 + (size_t)R * K + kb * 32;
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+        u32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+            const int b = q * 16 + e * 4;
+            o[e] = fp8x4(v[b], v[b + 1], v[b + 2], v[b + 3], sb);
+        }
+        *reinterpret_cast<u32x4 *>(dst8 + q * 16) = o;
+    }
+}
+
+}  // namespace
+
+bool gemm_f8_ready() { return f8_lds_attr(); }
+
+int f8_npad(int N, bool silu) { return silu ? ((N + 127) / 128) * 256 : ((N + 255) / 256) * 256; }
+
+size_t f8_weight_bytes(int N, int K, bool silu) {
+    const size_t np = (size_t)f8_npad(N, silu);
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    return al(np * K * 2) + al(np * K) + al(np * (K / 32));
+}
+
+F8Weights f8_weights_at(void *base, int N, int K, bool silu) {
+    const size_t np = (size_t)f8_npad(N, silu);
+    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    char *b = (char *)base;
+    F8Weights w;
+    w.w16 = (const u16 *)b;
+    w.w8 = (const uint8_t *)(b + al(np * K * 2));
+    w.wsc = (const uint8_t *)(b + al(np * K * 2) + al(np * K));
+    w.N = N;
+    w.K = K;
+    w.npad = (int)np;
+    w.silu = silu;
+    return w;
+}
+
+void launch_convert_f8(hipStream_t st, const WSeg *segs, int nseg, int K, bool silu, const F8Weights &w) {
+    const u16 *s[3] = {nullptr, nullptr, nullptr};
+    int e0 = 0, e1 = 0, end = 0;
+    for (int i = 0; i < nseg; i++) {
+        s[i] = (const u16 *)segs[i].w;
+        end += segs[i].rows;
+        if (i == 0) e0 = end;
+        if (i == 1) e1 = end;
+    }
+    if (nseg < 2) e0 = end;
+    if (nseg < 3) e1 = end;
+    const long n = (long)w.npad * (K / 32);
+    hipLaunchKernelGGL(convert_f8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, s[0], s[1], s[2], e0,
+                       e1, silu ? 0 : end, K, silu ? w.N : 0, w.npad, (u16 *)w.w16, (uint8_t *)w.w8,
+                       (uint8_t *)w.wsc);
+}
+
+bool launch_gemm_f8(hipStream_t st, const F8Weights &w, const u16 *a16, const uint8_t *a8, const uint8_t *asc,
+                    int mpad, int lda, int M, float *out, int ldo, int ksplit, size_t split_stride) {
+    if (M <= 0) return true;
+    if (w.silu || w.K % 64 || !f8_lds_attr()) return false;
+    if (ksplit < 1 || w.K % (ksplit * 64)) ksplit = 1;
+    GemmF8Params p{};
+    p.w16 = w.w16; p.w8 = w.w8; p.wsc = w.wsc;
+    p.a16 = a16; p.a8 = a8; p.asc = asc;
+    p.N = w.N; p.K = w.K; p.M = M; p.npad = w.npad; p.mpad = mpad; p.lda = lda;
+    p.out = out; p.ldo = ldo; p.kchunk = w.K / ksplit; p.split_stride = ksplit > 1 ? split_stride : 0;
+    hipLaunchKernelGGL(gemm_f8_kernel<false>, dim3((w.N + DBN - 1) / DBN, (M + DBM - 1) / DBM, ksplit), dim3(DNTHR),
+                       F8_LDS, st, p);
+    return true;
+}
+
+bool launch_gemm_f8_silu(hipStream_t st, const F8Weights &w, const u16 *a16, const uint8_t *a8, const uint8_t *asc,
+                         int mpad, int lda, int M, u16 *s_hi, u16 *s_lo, int ldo) {
+    if (M <= 0) return true;
+    if (!w.silu || w.K % 64 || !f8_lds_attr()) return false;
+    GemmF8Params p{};
+    p.w16 = w.w16; p.w8 = w.w8; p.wsc = w.wsc;
+    p.a16 = a16; p.a8 = a8; p.asc = asc;
+    p.N = w.N; p.K = w.K; p.M = M; p.npad = w.npad; p.mpad = mpad; p.lda = lda;
+    p.kchunk = w.K; p.s_hi = s_hi; p.s_lo = s_lo; p.ldo = ldo;
+    hipLaunchKernelGGL(gemm_f8_kernel<true>, dim3((w.N + DBN / 2 - 1) / (DBN / 2), (M + DBM - 1) / DBM, 1),
+                       dim3(DNTHR), F8_LDS, st, p);
     return true;
 }
 

@@ -20,20 +20,30 @@ struct WSeg {
     const void *w;
     int rows;
 };
+
+// Prefill activations as fp16 + fp8 split operands: a16 [rows][lda] fp16,
+// a8 [rows][lda] fp8 e4m3 and E8M0 scales asc [lda/32][mpad], mpad = rows
+// rounded up to 256 (written with f16_split / mx_scale_byte / fp8x4).
+struct F8Act {
+    u16 *a16;
+    uint8_t *a8, *asc;
+    int lda, mpad;
+};
 #define MAX_SEGS 3
 
 // Residual update + RMSNorm of one row per block:
 //   mode EMBED:  x = widen(E[tok[t]])
 //   otherwise:   x += sum of `add` splits (if any)
 //                     + sum_j moe_w[t][j] * (sum of moe splits at grouped row moe_inv[t*k+j]) (if moe_inv)
-// then a = x / sqrt(mean(x^2)+eps) * gain written as bf16 (hi, lo) and/or fp32.
+// then a = x / sqrt(mean(x^2)+eps) * gain written as bf16 (hi, lo) and/or fp32,
+// or, with f8 (rows written one block per row), as fp16 + fp8 split operands.
 // ssq: scratch of T*ceil(d/1024) floats, used to split the work over columns
 // when there are few rows (may be null: one block per row).
 enum { RN_EMBED = 0, RN_ADD = 1 };
 void launch_residual_norm(hipStream_t st, int mode, int T, int d, float *x, const int32_t *tok,
                           const void *embed, int embed_f32, Partials add, Partials moe, const int32_t *moe_inv,
                           const float *moe_w, int k, const float *gain, float eps, u16 *a_hi,
-                          u16 *a_lo, float *a_f32, float *cap, float *ssq);
+                          u16 *a_lo, float *a_f32, float *cap, float *ssq, const F8Act *f8 = nullptr);
 
 // cos/sin of pos[t] * f_i for pair i, f_i = theta^(-2i/hd) (llama3-scaled when
 // scaling == 1), formed in double: tab[t][i].
@@ -79,7 +89,9 @@ void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
 // consumer sums them).
 // gemm_splits_for takes the CU count (host-only use: the workspace plan).
 int gemm_splits(int N, int K, int M);
-int gemm_splits_for(int N, int K, int M, int cus);
+// kmul: k-tiles of 32 per split a multiple of kmul (2 for the fp16 + fp8 form)
+int gemm_splits_for(int N, int K, int M, int cus, int kmul = 1);
+int gemm_splits_f8(int N, int K, int M);
 void launch_gemm(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi, const u16 *a_lo,
                  int lda, int M, float *out, int ldo, int ksplit = 1, size_t split_stride = 0);
 
@@ -186,6 +198,31 @@ void launch_gemm_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, cons
 bool launch_gemm_grouped_silu(hipStream_t st, const void *w_gate, const void *w_up, int F, int K, const u16 *a_hi,
                               const u16 *a_lo, int lda, int max_rows, int E, const int32_t *offsets,
                               size_t expert_stride, u16 *s_hi, u16 *s_lo, int ldo);
+
+// ---- prefill projections on fp16 + fp8 operands (k_gemm.hip) ---------------
+// A weight matrix converted once: W16 [npad][K] fp16, W8 [npad][K] fp8 e4m3
+// and E8M0 scales [K/32][npad], rows in the GEMM's tile order (SILU: gate and
+// up rows interleaved per tile).  K a multiple of 64.
+struct F8Weights {
+    const u16 *w16;
+    const uint8_t *w8, *wsc;
+    int N, K, npad;
+    bool silu;
+};
+// the form's kernels can be launched (their LDS attribute is set); decided
+// before any producer writes the form
+bool gemm_f8_ready();
+int f8_npad(int N, bool silu);
+size_t f8_weight_bytes(int N, int K, bool silu);      // bytes of one converted matrix (256-aligned parts)
+F8Weights f8_weights_at(void *base, int N, int K, bool silu);
+// segs: the bf16 row segments (SILU: gate then up, F rows each)
+void launch_convert_f8(hipStream_t st, const WSeg *segs, int nseg, int K, bool silu, const F8Weights &w);
+// false where the form does not apply (K % 64, a SILU/non-SILU mismatch); the
+// k split must leave a multiple of 64 k per split, else one split is taken
+bool launch_gemm_f8(hipStream_t st, const F8Weights &w, const u16 *a16, const uint8_t *a8, const uint8_t *asc,
+                    int mpad, int lda, int M, float *out, int ldo, int ksplit = 1, size_t split_stride = 0);
+bool launch_gemm_f8_silu(hipStream_t st, const F8Weights &w, const u16 *a16, const uint8_t *a8, const uint8_t *asc,
+                         int mpad, int lda, int M, u16 *s_hi, u16 *s_lo, int ldo);
 void launch_gemm_f32_grouped(hipStream_t st, const WSeg *segs, int nseg, int K, const float *a, int lda,
                              int max_rows, int E, const int32_t *offsets, size_t expert_stride, float *out,
                              int ldo);

@@ -33,7 +33,8 @@ class DecConfig(ctypes.Structure):
         "qkv_bias", "tied_embedding", "sliding_window", "max_seq", "max_batch", "max_prefill",
         "weight_dtype")] + [("rms_eps", ctypes.c_double), ("rope_theta", ctypes.c_double)] + [
         (n, ctypes.c_int32) for n in ("rope_pairing", "rope_scaling", "rope_orig_ctx", "kv_dtype")] + [
-        (n, ctypes.c_double) for n in ("rope_factor", "rope_low_freq_factor", "rope_high_freq_factor")]
+        (n, ctypes.c_double) for n in ("rope_factor", "rope_low_freq_factor", "rope_high_freq_factor")] + [
+        ("prefill_operands", ctypes.c_int32)]
 
 
 class DecLayerWeights(ctypes.Structure):
@@ -112,7 +113,8 @@ def make_config(cfg: ModelConfig, max_batch: int, max_prefill: int, max_seq: Opt
                      int(cfg.tied_embedding), cfg.sliding_window, cfg.max_seq if max_seq is None else max_seq,
                      max_batch, max_prefill, 1 if cfg.weight_dtype == WEIGHT_F32 else 0, cfg.rms_eps,
                      cfg.rope_theta, cfg.rope_pairing, cfg.rope_scaling, cfg.rope_orig_ctx, int(cfg.kv_bf16),
-                     cfg.rope_factor, cfg.rope_low_freq_factor, cfg.rope_high_freq_factor)
+                     cfg.rope_factor, cfg.rope_low_freq_factor, cfg.rope_high_freq_factor,
+                     int(getattr(cfg, "prefill_fp8", False)))
 
 
 def workspace_bytes(cfg: ModelConfig, max_batch: int, max_prefill: int, max_seq: Optional[int] = None) -> int:

@@ -53,6 +53,7 @@ enum { DEC_WEIGHT_BF16 = 0, DEC_WEIGHT_F32 = 1 };
 enum { DEC_ROPE_ADJACENT = 0, DEC_ROPE_HALF = 1 };
 enum { DEC_ROPE_PLAIN = 0, DEC_ROPE_LLAMA3 = 1 };
 enum { DEC_KV_F32 = 0, DEC_KV_BF16 = 1 };
+enum { DEC_PREFILL_BF16_PAIR = 0, DEC_PREFILL_F16_F8 = 1 };
 
 /*
  * Model configuration: the base recipe plus switches (rml "The decoder",
@@ -108,6 +109,24 @@ typedef struct dec_config {
     double rope_factor;
     double rope_low_freq_factor;
     double rope_high_freq_factor;
+    /* Operands of the prefill projections (calls of more than 64 rows, bf16
+       weights): an arithmetic choice of this library, not a step of the
+       forward.  Both forms compute y = W a with a split a = hi + lo, so that
+       the product keeps near-fp32 accuracy against the exact weights.
+       DEC_PREFILL_BF16_PAIR: hi = bf16(a), lo = bf16(a - hi), two bf16 MFMA
+       passes against the caller's weights.
+       DEC_PREFILL_F16_F8: hi = fp16(a) against an fp16 copy of the weights,
+       plus lo = a - hi as fp8 e4m3 with a power-of-two scale per 32 inputs
+       against an fp8 copy of the weights (same scaling) on the fp8 MFMA, which
+       runs at twice the bf16 rate.  It covers the q|k|v projection and, for a
+       dense FFN whose fused gate|up grid fills the device, gate|up; the other
+       projections and MoE experts keep the pair, and so does a config whose
+       max_prefill is 64 or less.  The converted weights live in the
+       workspace (dec_workspace_bytes grows by about 3 bytes per q|k|v and
+       gate|up weight) and are written by dec_create on its stream from the
+       caller's weights, which must hold their values by then.  |a| above 65504 (the
+       fp16 maximum) keeps only fp8 accuracy for that element.  */
+    int32_t prefill_operands;
 } dec_config;
 
 /*

@@ -161,3 +161,36 @@ def test_create_noalloc_checks_before_the_device():
     c = D.make_config(configs.TINY, 1, 8)
     assert L.dec_create_noalloc(ctypes.byref(c), None, None, None) == D.DEC_ERR_INVALID
     assert D.workspace_bytes(configs.SMOLLM2, 4, 128) <= D.DEC_NOALLOC_WORKSPACE_BYTES
+
+
+def _f8_matrix_bytes(N, K, silu):
+    """Workspace bytes of one matrix converted for fp16 + fp8 prefill operands:
+    rows padded to 256-row tiles (a gate|up tile holds 128 features of each),
+    fp16 copy, fp8 copy and one scale byte per 32 k, each part 256-aligned."""
+    npad = ((N + 127) // 128) * 256 if silu else ((N + 255) // 256) * 256
+    al = lambda x: (x + 255) // 256 * 256
+    return al(npad * K * 2) + al(npad * K) + al(npad * (K // 32))
+
+
+def test_fp16_fp8_prefill_operands_workspace_and_validation():
+    _lib()
+    m = configs.MISTRAL
+    base = D.workspace_bytes(m, max_batch=32, max_prefill=4096)
+    f8 = D.workspace_bytes(m.replace(prefill_fp8=True), max_batch=32, max_prefill=4096)
+    d, qd, kvd, F = m.hidden, m.q_dim, m.kv_dim, m.ffn_dim
+    per_layer = _f8_matrix_bytes(qd + 2 * kvd, d, False) + _f8_matrix_bytes(F, d, True)
+    # the converted weights are the only growth here (the (hi, lo) buffers already hold the operands)
+    assert f8 - base == m.n_layers * per_layer
+    # MoE: only q|k|v is converted
+    x = configs.MIXTRAL
+    gx = (D.workspace_bytes(x.replace(prefill_fp8=True), max_batch=16, max_prefill=512)
+          - D.workspace_bytes(x, max_batch=16, max_prefill=512))
+    assert gx == x.n_layers * _f8_matrix_bytes(x.q_dim + 2 * x.kv_dim, x.hidden, False)
+    # prefills of at most 64 rows never take the form
+    assert D.workspace_bytes(m.replace(prefill_fp8=True), 32, 64) == D.workspace_bytes(m, 32, 64)
+    # an unknown form, and the form with fp32 weights, are refused
+    c = D.make_config(m, 32, 4096)
+    c.prefill_operands = 2
+    assert _lib().dec_workspace_bytes(ctypes.byref(c)) == 0
+    assert D.workspace_bytes(configs.TINY.replace(prefill_fp8=True, max_seq=256), 2, 128) == 0   # fp32 weights
+    assert _create(configs.TINY, prefill_operands=1)[0] == D.DEC_ERR_INVALID
