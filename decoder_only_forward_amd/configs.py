@@ -48,8 +48,11 @@ class ModelConfig:
     rope_low_freq_factor: float = 1.0
     rope_high_freq_factor: float = 4.0
     rope_orig_ctx: int = 8192
-    # K/V cache element type: False = fp32, True = bf16 (rounded to nearest even).
+    # K/V cache element type: fp32 by default; kv_bf16: bf16 (rounded to
+    # nearest even); kv_f24: a 24-bit float (fp32 rounded to nearest even at
+    # 15 stored mantissa bits, 16 significant bits).  At most one is set.
     kv_bf16: bool = False
+    kv_f24: bool = False
     # Prefill projections (more than 64 rows) on fp16 + fp8 split operands
     # instead of the bf16 (hi, lo) pair: an arithmetic choice of the GPU path
     # (DEC_PREFILL_F16_F8), not part of the model; the oracle ignores it.
@@ -113,6 +116,7 @@ TINY_LLAMA3 = TINY.replace(name="tiny-llama3", rope_scaling=1, rope_factor=8.0, 
                            rope_high_freq_factor=4.0, rope_orig_ctx=64)
 TINY_HALF = TINY.replace(name="tiny-half", rope_pairing=1)
 TINY_KVBF16 = TINY_BF16.replace(name="tiny-kvbf16", kv_bf16=True)
+TINY_KVF24 = TINY_BF16.replace(name="tiny-kvf24", kv_f24=True)
 
 
 def one_layer(cfg: ModelConfig) -> ModelConfig:

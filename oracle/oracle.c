@@ -72,8 +72,11 @@ typedef struct {
        scaling 0 = none, 1 = llama3 frequency scaling with factor, low/high
        frequency factors and original context. */
     int32_t rope_pairing, rope_scaling, rope_orig_ctx;
-    /* 1: K and V are rounded to bf16 (nearest even) when stored in the cache. */
-    int32_t kv_bf16;
+    /* Rounding of K and V when stored in the cache: 0 none (the working
+       precision), 1 bf16 (8 significant bits, nearest even), 2 a 24-bit float
+       (sign, 8 exponent bits, 15 stored mantissa bits: 16 significant bits,
+       nearest even). */
+    int32_t kv_round;
     double rope_factor, rope_low_freq_factor, rope_high_freq_factor;
 } ocfg;
 
@@ -176,6 +179,17 @@ static real bf16_round(real v) {
     return (real)f;
 }
 
+/* The value as a float with its low 8 mantissa bits cleared, rounded to
+   nearest even first: fp32's layout with 15 stored mantissa bits. */
+static real f24_round(real v) {
+    float f = (float)v;
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    u = (u + 0x7Fu + ((u >> 8) & 1u)) & 0xFFFFFF00u;
+    memcpy(&f, &u, sizeof f);
+    return (real)f;
+}
+
 static inline real silu(real z) { return z / ((real)1 + R_EXP(-z)); }
 
 /* Router: softmax over all experts, top-k by repeated selection (ties to the
@@ -271,6 +285,7 @@ static int cfg_valid(const ocfg *c) {
     if (c->n_experts < 0 || c->n_experts > 256) return 0;
     if (c->n_experts > 0 && (c->top_k < 1 || c->top_k > c->n_experts)) return 0;
     if (c->sliding_window < 0) return 0;
+    if (c->kv_round < 0 || c->kv_round > 2) return 0;
     if (c->sliding_window > 0 && !c->window_by_mask && c->max_seq > c->sliding_window) return 0;
     return 1;
 }
@@ -369,9 +384,12 @@ static void block_kv(omodel *m, int l, int slot, int pos, const real *x, scratch
                  c->rope_low_freq_factor, c->rope_high_freq_factor, c->rope_orig_ctx);
     SYM(rope_ex)(s->k, c->n_kv_heads, hd, pos, c->rope_theta, c->rope_pairing, c->rope_scaling, c->rope_factor,
                  c->rope_low_freq_factor, c->rope_high_freq_factor, c->rope_orig_ctx);
-    if (c->kv_bf16) {
+    if (c->kv_round == 1) {
         for (int i = 0; i < kvd; i++) s->k[i] = bf16_round(s->k[i]);
         for (int i = 0; i < kvd; i++) s->v[i] = bf16_round(s->v[i]);
+    } else if (c->kv_round == 2) {
+        for (int i = 0; i < kvd; i++) s->k[i] = f24_round(s->k[i]);
+        for (int i = 0; i < kvd; i++) s->v[i] = f24_round(s->v[i]);
     }
     int sl = is_ring(c) ? pos % c->max_seq : pos;
     size_t off = (((size_t)l * c->n_slots + slot) * c->max_seq + sl) * (size_t)kvd;

@@ -45,7 +45,7 @@ class OCfg(ctypes.Structure):
         "n_layers", "hidden", "n_heads", "n_kv_heads", "head_dim", "ffn_dim", "vocab",
         "n_experts", "top_k", "qkv_bias", "sliding_window", "max_seq", "n_slots", "weight_f32",
         "window_by_mask")] + [("rms_eps", ctypes.c_double), ("rope_theta", ctypes.c_double)] + [
-        (n, ctypes.c_int32) for n in ("rope_pairing", "rope_scaling", "rope_orig_ctx", "kv_bf16")] + [
+        (n, ctypes.c_int32) for n in ("rope_pairing", "rope_scaling", "rope_orig_ctx", "kv_round")] + [
         (n, ctypes.c_double) for n in ("rope_factor", "rope_low_freq_factor", "rope_high_freq_factor")]
 
 
@@ -56,6 +56,13 @@ class OLayer(ctypes.Structure):
 
 
 _loaded = {}
+
+
+def kv_round(cfg) -> int:
+    """Rounding of K/V at store: 0 none, 1 bf16, 2 the 24-bit float."""
+    if getattr(cfg, "kv_f24", False):
+        return 2
+    return 1 if getattr(cfg, "kv_bf16", False) else 0
 
 
 def lib(kind: str = "f32"):
@@ -187,7 +194,7 @@ class OracleModel:
                          cfg.ffn_dim, cfg.vocab, cfg.n_experts, cfg.top_k, int(cfg.qkv_bias),
                          cfg.sliding_window, ms, n_slots, int(cfg.weight_dtype == 1),
                          int(window_by_mask), cfg.rms_eps, cfg.rope_theta, cfg.rope_pairing, cfg.rope_scaling,
-                         cfg.rope_orig_ctx, int(cfg.kv_bf16), cfg.rope_factor, cfg.rope_low_freq_factor,
+                         cfg.rope_orig_ctx, kv_round(cfg), cfg.rope_factor, cfg.rope_low_freq_factor,
                          cfg.rope_high_freq_factor)
         self.n_slots = n_slots
         arr = (OLayer * cfg.n_layers)()

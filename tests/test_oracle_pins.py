@@ -539,3 +539,70 @@ def test_bf16_cache_spread_between_oracle_precisions_is_within_its_bound():
                           for b in range(B))
     assert spread[False] < 1e-5
     assert 20 * spread[False] < spread[True] <= 2.0 ** -7
+
+
+# ---- 24-bit K/V cache -----------------------------------------------------------
+
+def _sig16(x: np.ndarray) -> np.ndarray:
+    """fp32 values rounded to 16 significant bits, ties to even: frexp's
+    mantissa in [0.5, 1) times 2^16, rounded half to even by numpy."""
+    m, e = np.frexp(x.astype(np.float64))
+    return np.ldexp(np.round(m * 65536.0), e - 16).astype(np.float32)
+
+
+def test_sig16_reference_rounding_cases():
+    # exact at 16 bits, halfway cases to even, carries into the exponent
+    one_ulp = 2.0 ** -15                      # 16th significant bit of 1.x
+    x = np.array([1.0, 1.0 + one_ulp, 1.0 + one_ulp / 2, 1.0 + 3 * one_ulp / 2,
+                  2.0 - one_ulp / 2, -(1.0 + one_ulp / 2), 3.0 * 2.0 ** -30], dtype=np.float32)
+    want = np.array([1.0, 1.0 + one_ulp, 1.0, 1.0 + 2 * one_ulp, 2.0, -1.0, 3.0 * 2.0 ** -30], dtype=np.float32)
+    np.testing.assert_array_equal(_sig16(x), want)
+
+
+def test_f24_kv_rows_are_fp32_rows_rounded_to_16_significant_bits():
+    cfg = configs.TINY_KVF24
+    w = synth.make_weights(cfg)
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 5, cfg.vocab).tolist()
+    a = O.OracleModel(cfg, w)
+    b = O.OracleModel(cfg.replace(kv_f24=False), w)
+    a.prefill(toks)
+    b.prefill(toks)
+    changed = 0
+    for p in range(5):
+        for which in (0, 1):
+            want = _sig16(b.kv_row(0, 0, which, p))
+            got = a.kv_row(0, 0, which, p)
+            np.testing.assert_array_equal(got, want)
+            changed += int(np.sum(got != b.kv_row(0, 0, which, p)))
+            # the low 8 bits of every stored fp32 word are zero
+            assert not np.any(got.view(np.uint32) & 0xFF)
+    assert changed > 0
+    ra = a.decode([3], [5])["logits"]
+    rb = b.decode([3], [5])["logits"]
+    rel = np.linalg.norm(ra - rb) / np.linalg.norm(rb)
+    assert 0 < rel < 1e-4
+
+
+def test_f24_cache_stays_within_the_fp32_tolerance_at_depth():
+    """The 24-bit cache keeps 16 significant bits (u = 2^-16): at SmolLM2 depth
+    (measured 1.7e-5) its logits stay within 1e-4 relative of the fp32-cache
+    model's, a tenth of the fp32 path's tolerance, and so does the spread
+    between the oracle's fp32 and fp64 instantiations that both round at store
+    (measured 1.4e-5, against 2.1e-6 with an fp32 cache): a 16-bit rounding
+    decision that flips on fp32 noise moves one element by 2^-16 of itself,
+    256 times less than a bf16 flip.  So the fp32 path's tolerance applies."""
+    B, P = 8, 4
+    cfg = configs.SMOLLM2.replace(kv_f24=True)
+    w = synth.make_weights(cfg)
+    pr = synth.prompts(cfg, B, P)
+    out = {}
+    for name, c, kind in (("f24_32", cfg, "f32"), ("f24_64", cfg, "f64"), ("fp32", cfg.replace(kv_f24=False), "f64")):
+        m = O.OracleModel(c, w, n_slots=B, kind=kind)
+        for b in range(B):
+            m.prefill(pr[b].tolist(), slot=b)
+        out[name] = m.decode([1 + b for b in range(B)], [P] * B)["logits"].astype(np.float64)
+
+    def worst(a, b):
+        return max(np.linalg.norm(out[a][r] - out[b][r]) / np.linalg.norm(out[b][r]) for r in range(B))
+    assert 0 < worst("f24_64", "fp32") < 1e-4
+    assert worst("f24_32", "f24_64") < 1e-4

@@ -38,6 +38,7 @@ CASES = [
     (configs.TINY_HALF, 10),          # rotate-half pairing
     (configs.TINY_LLAMA3, 10),        # llama3 frequency scaling, all three bands
     (configs.TINY_KVBF16, 10),        # K/V rounded to bf16 at store
+    (configs.TINY_KVF24, 10),         # K/V rounded to 16 significant bits at store
     (configs.TINY.replace(name="tiny-window16-cap12", sliding_window=16, max_seq=12), 12),  # never wraps
 ]
 

@@ -74,6 +74,13 @@ def _bf16(t):
     return t.to(torch.float32).to(torch.bfloat16).to(D)
 
 
+def _sig16(t):
+    """The fp32 value of t rounded to 16 significant bits, ties to even
+    (frexp's mantissa in [0.5, 1) scaled by 2^16 and rounded half to even)."""
+    m, e = torch.frexp(t.to(torch.float32).to(torch.float64))
+    return torch.ldexp(torch.round(m * 65536.0), e - 16)
+
+
 def route(r: torch.Tensor, k: int):
     """Router logits r [E] -> (ids [k], weights [k]): softmax, the k largest
     probabilities with ties to the lower id (a stable descending sort keeps
@@ -110,6 +117,8 @@ def forward(cfg, w: dict, tokens) -> dict:
         v = v.view(n, nkv, hd)
         if cfg.kv_bf16:
             k, v = _bf16(k), _bf16(v)
+        if getattr(cfg, "kv_f24", False):
+            k, v = _sig16(k), _sig16(v)
         o = F.scaled_dot_product_attention(q.transpose(0, 1)[None], k.transpose(0, 1)[None],
                                            v.transpose(0, 1)[None], attn_mask=mask, enable_gqa=True)
         o = o[0].transpose(0, 1).reshape(n, nh * hd)
