@@ -149,6 +149,15 @@ def cpu_baseline(cfg, wd, B=32, prefill_tokens=32):
                       f"and a prefill of the prompt's first {prefill_tokens} tokens ({dt_pre:.1f} s)"}
 
 
+def kv_bytes(cfg):
+    """Bytes of one cached K or V element: fp32 4, bf16 2, the 24-bit format 3."""
+    return 2 if cfg.kv_bf16 else (3 if getattr(cfg, "kv_f24", False) else 4)
+
+
+def kv_name(cfg):
+    return "bf16" if cfg.kv_bf16 else ("f24" if getattr(cfg, "kv_f24", False) else "fp32")
+
+
 def decode_step_bytes(cfg, B, readable, experts_per_layer=None):
     """Algorithmic HBM bytes of one decode step of B rows: every weight read once
     (for MoE the router and the experts in use: `experts_per_layer`, default
@@ -156,7 +165,7 @@ def decode_step_bytes(cfg, B, readable, experts_per_layer=None):
     and one V row written per row and layer, the logits written."""
     d, q, kv, f, V, L = cfg.hidden, cfg.q_dim, cfg.kv_dim, cfg.ffn_dim, cfg.vocab, cfg.n_layers
     wb = 4 if cfg.weight_dtype == 1 else 2
-    es = 2 if cfg.kv_bf16 else 4
+    es = kv_bytes(cfg)
     attn = (2 * d * q + 2 * d * kv) * wb
     if cfg.n_experts:
         ex = experts_per_layer if experts_per_layer is not None else min(cfg.n_experts, B * cfg.top_k)
@@ -170,8 +179,8 @@ def decode_step_bytes(cfg, B, readable, experts_per_layer=None):
 def prefill_weight_bytes(cfg, P):
     """Weights one prefill of P tokens reads once (every expert a token chose;
     a P-token MoE prefill touches min(E, P*k) experts a layer)."""
-    return decode_step_bytes(cfg, P, 0) - P * cfg.hidden * 2 - cfg.n_layers * 2 * cfg.kv_dim * (
-        2 if cfg.kv_bf16 else 4) * P - P * cfg.vocab * 4
+    return decode_step_bytes(cfg, P, 0) - P * cfg.hidden * 2 - cfg.n_layers * 2 * cfg.kv_dim * kv_bytes(cfg) * P \
+        - P * cfg.vocab * 4
 
 
 def _hbm(bytes_, ms):
@@ -335,7 +344,7 @@ def run_workload(cfg, wd, B, P, steps, warmup, small_batches=()):
     from decoder_only_forward_amd import dec as D
 
     model = D.DecModel(cfg, wd, max_batch=B, max_prefill=P)
-    kvname = "bf16" if cfg.kv_bf16 else "fp32"
+    kvname = kv_name(cfg)
     log(f"[{kvname} KV] workspace {model.workspace.numel() / 2**30:.1f} GiB")
     prompts = synth.prompts(cfg, B, P)
 
@@ -465,8 +474,10 @@ def main():
     ap.add_argument("--prompt", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=32, help="prompt tokens the oracle's prefill sample takes")
-    ap.add_argument("--kv", choices=("both", "fp32"), default="both",
-                    help="both: the fp32-cache run gives `value`, a bf16-cache run is reported beside it")
+    ap.add_argument("--kv", choices=("all", "fp32", "f24"), default="all",
+                    help="all: the fp32-cache run gives `value`; runs on a bf16 cache and on the 24-bit cache are "
+                         "reported beside it.  fp32: only the fp32-cache run.  f24: only a 24-bit-cache run (with "
+                         "--only mistral-7b, for profiling)")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="only run three 1 GiB device-to-device copies (PMC byte-counter calibration)")
     ap.add_argument("--only", choices=sorted(OTHER) + ["mistral-7b"], default=None,
@@ -508,6 +519,8 @@ def main():
             c = c.replace(name=f"{c.name}-{args.layers}l", n_layers=args.layers)
         if args.only and args.prefill_fp8:
             c = c.replace(name=f"{c.name}-prefill-f16f8", prefill_fp8=True)
+        if args.kv == "f24":
+            c = c.replace(kv_f24=True)
         return c
 
     if args.only and args.only != "mistral-7b":
@@ -525,9 +538,10 @@ def main():
         run_prefill_only(cfg, wd, P)
         return
     main_run = run_workload(cfg, wd, B, P, args.steps, args.warmup, small_batches=(1, 8))
-    bf16_run = None
-    if args.kv == "both" and not args.only:
+    bf16_run = f24_run = None
+    if args.kv == "all" and not args.only:
         bf16_run = run_workload(cfg.replace(kv_bf16=True), wd, B, P, args.steps, args.warmup, small_batches=(1, 8))
+        f24_run = run_workload(cfg.replace(kv_f24=True), wd, B, P, args.steps, args.warmup, small_batches=(1, 8))
     value, ms_step, pre_med = main_run["value"], main_run["ms_step"], main_run["pre_med"]
     gemm_t, apre_t, gemv_t, attn_t = main_run["gemm"], main_run["apre"], main_run["gemv"], main_run["attn"]
     extra, dt_timed = main_run["extra"], main_run["dt_timed"]
@@ -566,9 +580,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("bf16 weights x fp32 (split-bf16 MFMA), fp32 KV" if not cfg.prefill_fp8 else
+        "dtype": ("bf16 weights x fp32 (split-bf16 MFMA), " if not cfg.prefill_fp8 else
                   "bf16 weights x fp32 (decode: split-bf16 MFMA; prefill q|k|v and gate|up: fp16 + scaled fp8 "
-                  "split operands), fp32 KV"),
+                  "split operands), ") + {"fp32": "fp32 KV", "f24": "24-bit KV (16 significant bits)",
+                                          "bf16": "bf16 KV"}[kv_name(cfg)],
         "data": "synthetic (seeded random-init weights and prompts)",
         "config": {"workload": f"{cfg.name} decode B={B} at positions {P}.. (ring KV {cfg.max_seq}), "
                                f"prefill P={P}", "batch": B, "prompt": P, "layers": cfg.n_layers},
@@ -591,14 +606,15 @@ def main():
     def attn_roof(t, kv):
         # groups of up to 4 heads with an fp32 cache take the lane-group kernel,
         # the others the MFMA form
-        name = "attn_decode_kernel" if kv == "fp32" and cfg.n_heads // cfg.n_kv_heads <= 4 else "attn_decode_mfma_kernel"
+        name = ("attn_decode_kernel" if kv != "bf16" and cfg.n_heads // cfg.n_kv_heads <= 4
+                else "attn_decode_mfma_kernel")
         r = roof(t, "hbm", (name, kv))
         if r is not None:
             r["kernel"] = f"{name} (split-KV GQA decode attention, {kv} KV)"
             r["algorithmic_bytes_per_launch_gb"] = round(t["bytes"] / t["launches"] / 1e9, 4)
         return r
 
-    out["roofline"] = attn_roof(attn_t, "fp32")
+    out["roofline"] = attn_roof(attn_t, kv_name(cfg))
     if bf16_run is not None:
         out["kv_bf16"] = {
             "note": "same workload with the K/V cache stored as nearest-even bf16 (arithmetic fp32)",
@@ -613,6 +629,23 @@ def main():
             "roofline": attn_roof(bf16_run["attn"], "bf16"),
             "roofline_kernels": {"gemv_decode": roof(bf16_run["gemv"], "hbm", ("gemv_decode", "bf16")),
                                  "attn_prefill": roof(bf16_run["apre"], "mfma", passes=2)},
+        }
+    if f24_run is not None:
+        out["kv_f24"] = {
+            "note": ("same workload with the K/V cache stored at 16 significant bits (fp32 rounded to nearest "
+                     "even at 15 stored mantissa bits, 3 bytes an element; arithmetic fp32); parity-tested at "
+                     "the fp32 cache's tolerances, also against the fp32-cache oracle"),
+            "decode_tok_s": round(f24_run["value"], 2),
+            "ms_per_step": round(f24_run["ms_step"], 3),
+            "prefill_tok_s": round(P / (f24_run["pre_med"] * 1e-3), 1),
+            "prefill_ms": round(f24_run["pre_med"], 2),
+            "decode": f24_run["extra"],
+            "decode_device_loop": f24_run["loop"],
+            "append_prefill_past_ring": f24_run["append"],
+            "ms_per_step_with_kernel_events": round(f24_run["dt_timed"] * 1e3 / args.steps, 3),
+            "roofline": attn_roof(f24_run["attn"], "f24"),
+            "roofline_kernels": {"gemv_decode": roof(f24_run["gemv"], "hbm", ("gemv_decode", "f24")),
+                                 "attn_prefill": roof(f24_run["apre"], "mfma", passes=3)},
         }
     if not args.no_cpu_baseline and not args.only:
         try:

@@ -17,6 +17,10 @@
 
 #include "dec.h"
 #include "kernels.h"
+#include "kvcache.h"
+
+static_assert(DEC_KV_F32 == KV_F32 && DEC_KV_BF16 == KV_BF16 && DEC_KV_F24 == KV_F24,
+              "the cache formats of the kernels are dec_config.kv_dtype's values");
 
 namespace {
 
@@ -111,6 +115,11 @@ namespace {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// bytes of one K/V cache element: fp32 4, bf16 2, 24-bit 3
+inline size_t kv_elem_bytes(const dec_config &c) {
+    return c.kv_dtype == DEC_KV_BF16 ? 2 : (c.kv_dtype == DEC_KV_F24 ? 3 : 4);
+}
+
 int proj_splits(const dec_config &c, int N, int K, int B, bool grouped = false) {
     if (c.weight_dtype == DEC_WEIGHT_F32 || B > 64) return 1;
     return grouped ? gemv_grouped_max_splits(K) : gemv_max_splits(N, K);
@@ -162,7 +171,7 @@ bool plan(const dec_config &c, Plan &p) {
     p.part_floats = pf;
     size_t off = 0;
     auto take = [&](size_t bytes) { size_t o = off; off = align256(off + bytes); return o; };
-    const size_t es = c.kv_dtype == DEC_KV_BF16 ? 2 : 4;
+    const size_t es = kv_elem_bytes(c);
     p.k = take(p.kv_layer * c.n_layers * es);
     p.v = take(p.kv_layer * c.n_layers * es);
     // one layer's K/V of a prefill chunk held back from a ring cache until the
@@ -182,7 +191,7 @@ bool plan(const dec_config &c, Plan &p) {
     p.s_lo = take(s_rows * F * 2);
     // prefill attention's K/V tile images (positions [0, max_seq) of one sequence)
     p.kvimg = take(c.weight_dtype == DEC_WEIGHT_F32 ? 0
-                   : attn_tiles_bytes(c.max_seq, c.n_kv_heads, c.head_dim, c.kv_dtype == DEC_KV_BF16));
+                   : attn_tiles_bytes(c.max_seq, c.n_kv_heads, c.head_dim, c.kv_dtype));
     p.x = take((size_t)rows * d * 4);
     const bool f32w = c.weight_dtype == DEC_WEIGHT_F32;
     p.a_hi = take(f32w ? 0 : p.act_elems * 2);
@@ -230,7 +239,7 @@ int validate_cfg(const dec_config *c) {
         (!(c->rope_factor > 0) || !(c->rope_low_freq_factor > 0) ||
          !(c->rope_high_freq_factor > c->rope_low_freq_factor) || c->rope_orig_ctx <= 0))
         return DEC_ERR_INVALID;
-    if (c->kv_dtype != DEC_KV_F32 && c->kv_dtype != DEC_KV_BF16) return DEC_ERR_INVALID;
+    if (c->kv_dtype != DEC_KV_F32 && c->kv_dtype != DEC_KV_BF16 && c->kv_dtype != DEC_KV_F24) return DEC_ERR_INVALID;
     if (c->prefill_operands != DEC_PREFILL_BF16_PAIR && c->prefill_operands != DEC_PREFILL_F16_F8)
         return DEC_ERR_INVALID;
     if (c->prefill_operands == DEC_PREFILL_F16_F8 && c->weight_dtype != DEC_WEIGHT_BF16) return DEC_ERR_INVALID;
@@ -299,7 +308,7 @@ int harvest(dec_model *m) {
 
 double kv_read_bytes(const dec_config &c, int T, const int *hpos) {
     double b = 0;
-    const int es = c.kv_dtype == DEC_KV_BF16 ? 2 : 4;
+    const int es = kv_elem_bytes(c);
     for (int i = 0; i < T; i++) b += 2.0 * std::min(hpos[i] + 1, c.max_seq) * c.n_kv_heads * c.head_dim * es;
     return b;
 }
@@ -309,7 +318,7 @@ int attn_splits_for(const dec_model *m, int T, const int *hpos) {
     int maxread = 1;
     for (int b = 0; b < T; b++) maxread = std::max(maxread, std::min(hpos[b] + 1, c.max_seq));
     return std::min(attn_decode_splits(T, c.n_kv_heads, maxread, c.head_dim, c.n_heads / c.n_kv_heads,
-                                       c.kv_dtype == DEC_KV_BF16),
+                                       c.kv_dtype),
                     MAX_ATTN_SPLITS);
 }
 
@@ -436,7 +445,7 @@ void run_pass(dec_model *m, const Pass &ps) {
         const dec_layer_weights &w = m->L[l];
         char *kc = m->kc + (size_t)l * m->pl.kv_layer * m->kv_es;
         char *vc = m->vc + (size_t)l * m->pl.kv_layer * m->kv_es;
-        const int kvb = m->kv_es == 2;
+        const int kvk = c.kv_dtype;   // DEC_KV_* values are the kernels' cache formats
         // q | k | v
         WSeg qkv[3] = {{w.wq, qd}, {w.wk, kvd}, {w.wv, kvd}};
         Partials pq = f8 ? proj_f8(m, m->f8w[l].qkv, T, fa_d) : proj(m, qkv, 3, d, T, ah, al, af, d);
@@ -447,7 +456,7 @@ void run_pass(dec_model *m, const Pass &ps) {
             const RopeArgs ra{pq, c.qkv_bias ? w.bq : nullptr, c.qkv_bias ? w.bk : nullptr,
                               c.qkv_bias ? w.bv : nullptr, m->rope, c.rope_pairing, m->ring};
             Tick tk(m, DEC_K_ATTN_DECODE);
-            launch_attn_decode(st, T, ra, kc, vc, kvb, m->pos, m->slot, nh, nkv, hd, c.max_seq, S, m->attn, ah, al,
+            launch_attn_decode(st, T, ra, kc, vc, kvk, m->pos, m->slot, nh, nkv, hd, c.max_seq, S, m->attn, ah, al,
                                af);
             tk.done(kv_read_bytes(c, T, ps.hpos) + 2.0 * T * qd * 4, 0);
         } else {
@@ -455,7 +464,7 @@ void run_pass(dec_model *m, const Pass &ps) {
             launch_rope_kv(st, T, pq, c.qkv_bias ? w.bq : nullptr, c.qkv_bias ? w.bk : nullptr,
                            c.qkv_bias ? w.bv : nullptr, m->rope, m->pos, m->slot, nh, nkv, hd, c.rope_pairing, m->q,
                            ps.deferred ? (void *)m->ck : (void *)kc, ps.deferred ? (void *)m->cv : (void *)vc,
-                           c.max_seq, m->ring, kvb, ps.deferred);
+                           c.max_seq, m->ring, kvk, ps.deferred);
             // keys per query: positions [p - window + 1, p] (window 0: [0, p])
             const int W = c.sliding_window;
             double flops = 0, keys = 0;
@@ -468,9 +477,9 @@ void run_pass(dec_model *m, const Pass &ps) {
             // history is read through ring slots only when the call reaches past
             // max_seq (the deferred case); below that, slot == position
             if (ps.deferred || !m->kvimg ||
-                !launch_attn_prefill_tiles(st, T, ps.start_pos, ps.seq, m->q, kc, vc, kvb, nh, nkv, hd, c.max_seq,
+                !launch_attn_prefill_tiles(st, T, ps.start_pos, ps.seq, m->q, kc, vc, kvk, nh, nkv, hd, c.max_seq,
                                            m->kvimg, m->part, m->pl.part_floats, ah, al, af))
-                launch_attn_prefill(st, T, ps.start_pos, ps.seq, m->q, kc, vc, kvb, nh, nkv, hd, c.max_seq, W,
+                launch_attn_prefill(st, T, ps.start_pos, ps.seq, m->q, kc, vc, kvk, nh, nkv, hd, c.max_seq, W,
                                     ps.deferred, ps.deferred ? m->ck : nullptr, ps.deferred ? m->cv : nullptr, ah,
                                     al, af);
             tk.done(keys * kvd * 2 * m->kv_es + 2.0 * T * qd * 4, flops);
@@ -748,7 +757,7 @@ int dec_create(const dec_config *cfg, const dec_weights *w, void *workspace, siz
     m->kvimg = p.kvimg < p.x ? (void *)(b + p.kvimg) : nullptr;
     m->s_hi = p.s_hi < p.s_lo ? (u16 *)(b + p.s_hi) : nullptr;
     m->s_lo = m->s_hi ? (u16 *)(b + p.s_lo) : nullptr;
-    m->kv_es = cfg->kv_dtype == DEC_KV_BF16 ? 2 : 4;
+    m->kv_es = (int)kv_elem_bytes(*cfg);
     m->x = (float *)(b + p.x);
     m->a_hi = (u16 *)(b + p.a_hi);
     m->a_lo = (u16 *)(b + p.a_lo);

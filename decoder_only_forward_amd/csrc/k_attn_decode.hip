@@ -32,6 +32,7 @@
 // rounding as launch_rope_kv).
 #include "common.h"
 #include "kernels.h"
+#include "kvcache.h"
 
 namespace {
 
@@ -67,30 +68,57 @@ __device__ __forceinline__ float group_sum(float v) {
 }
 
 // Per-lane view of a cache row: NV 16-byte words of EPW elements each.  Word w
-// of lane u sits at element (w*LP + u)*EPW of the row.
-template <int HD, int DPL, bool KB>
+// of lane u sits at element (w*LP + u)*EPW of the row.  A 24-bit row adds, for
+// each word of 8 elements, the 8-byte run of their third bytes, two runs to a
+// 16-byte register quad after the NV words (with two words a lane, LP = HD/16,
+// the two runs are one 16-byte word of the row: one load).
+template <int HD, int DPL, int KT>
 struct Row {
-    static constexpr int ES = KB ? 2 : 4;       // bytes per element
-    static constexpr int EPW = 16 / ES;         // elements per 16-byte word
-    static constexpr int NV = DPL / EPW;        // words per lane per row
+    static constexpr int EPW = KT == KV_F32 ? 4 : 8;   // elements per 16-byte word
+    static constexpr int NV = DPL / EPW;                // words per lane per row
+    static constexpr int NW = KT == KV_F24 ? NV + (NV + 1) / 2 : NV;   // register quads per row
     static constexpr int LP = HD / DPL;
+    static constexpr int RB = kv_row_bytes<KT>(HD);
     static __device__ __forceinline__ int dim(int u, int e) { return ((e / EPW) * LP + u) * EPW + e % EPW; }
-    static __device__ __forceinline__ void load(const char *row, int u, u32x4 (&r)[NV]) {
+    static __device__ __forceinline__ void load(const char *row, int u, u32x4 (&r)[NW]) {
+        constexpr int ES = KT == KV_F32 ? 4 : 2;
 #pragma unroll
         for (int w = 0; w < NV; w++) r[w] = ntload16(row + (size_t)((w * LP + u) * EPW) * ES);
-    }
-    static __device__ __forceinline__ void unpack(const u32x4 (&r)[NV], float (&f)[DPL]) {
+        if constexpr (KT == KV_F24) {
+            if constexpr (NV == 2 && LP == HD / 16) {
+                r[NV] = ntload16(row + f24_lo_off(HD, u * EPW));
+            } else {
 #pragma unroll
-        for (int w = 0; w < NV; w++)
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                if constexpr (KB) {
-                    f[w * 8 + 2 * j] = __uint_as_float(r[w][j] << 16);
-                    f[w * 8 + 2 * j + 1] = __uint_as_float(r[w][j] & 0xFFFF0000u);
-                } else {
-                    f[w * 4 + j] = __uint_as_float(r[w][j]);
+                for (int w = 0; w < NV; w++) {
+                    const u32x2 l = __builtin_nontemporal_load(
+                        reinterpret_cast<const u32x2 *>(row + f24_lo_off(HD, (w * LP + u) * EPW)));
+                    r[NV + w / 2][2 * (w % 2)] = l[0];
+                    r[NV + w / 2][2 * (w % 2) + 1] = l[1];
                 }
             }
+        }
+    }
+    static __device__ __forceinline__ void unpack(const u32x4 (&r)[NW], float (&f)[DPL]) {
+#pragma unroll
+        for (int w = 0; w < NV; w++) {
+            if constexpr (KT == KV_F24) {
+                const u32x2 l = {r[NV + w / 2][2 * (w % 2)], r[NV + w / 2][2 * (w % 2) + 1]};
+                float e8[8];
+                f24_unpack8(r[w], l, e8);
+#pragma unroll
+                for (int j = 0; j < 8; j++) f[w * 8 + j] = e8[j];
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    if constexpr (KT == KV_BF16) {
+                        f[w * 8 + 2 * j] = __uint_as_float(r[w][j] << 16);
+                        f[w * 8 + 2 * j + 1] = __uint_as_float(r[w][j] & 0xFFFF0000u);
+                    } else {
+                        f[w * 4 + j] = __uint_as_float(r[w][j]);
+                    }
+                }
+            }
+        }
     }
 };
 
@@ -131,7 +159,7 @@ __device__ __forceinline__ void rope_pair(const RopeArgs &ra, int b, size_t row,
 // holds the row's new slot, the rotated key and the value of the new position
 // stored in the cache.  Ends with a block barrier: the queries are complete in
 // LDS and the new K/V row is stored before any wave reads it.
-template <int HD, bool KB>
+template <int HD, int KT>
 __device__ __forceinline__ void decode_prologue(const RopeArgs &ra, void *kc, void *vc, int b, int kvh, int G, int nh,
                                                 int nkv, int p, int max_seq, int beg, int end, size_t head_base,
                                                 float (*qs)[HD]) {
@@ -157,10 +185,14 @@ __device__ __forceinline__ void decode_prologue(const RopeArgs &ra, void *kc, vo
             rope_pair<HD>(ra, b, row + (isk ? qd : qd + kvd) + (size_t)kvh * HD, i, isk,
                           bias ? bias + kvh * HD : nullptr, e0, e1, x0, x1);
             const size_t at = (head_base + sp) * HD;
-            if constexpr (KB) {
+            if constexpr (KT == KV_BF16) {
                 u16 *c = static_cast<u16 *>(isk ? kc : vc) + at;
                 c[e0] = (u16)f32_to_bf16_bits(x0);
                 c[e1] = (u16)f32_to_bf16_bits(x1);
+            } else if constexpr (KT == KV_F24) {
+                char *c = static_cast<char *>(isk ? kc : vc) + (head_base + sp) * kv_row_bytes<KV_F24>(HD);
+                f24_store(c, HD, e0, x0);
+                f24_store(c, HD, e1, x1);
             } else {
                 float *c = static_cast<float *>(isk ? kc : vc) + at;
                 c[e0] = x0;
@@ -171,23 +203,29 @@ __device__ __forceinline__ void decode_prologue(const RopeArgs &ra, void *kc, vo
     __syncthreads();
 }
 
-template <int HD, int G, bool KB>
-__global__ void __launch_bounds__(256, 2) attn_decode_kernel(
+// NWV waves a block: 4 (two blocks resident per CU), or 8 where one block per
+// CU takes a (row, kv head) pair whole (24-bit cache: its 48 bytes a lane and
+// position keep fewer loads in flight than the fp32 cache's 64, so it takes
+// twice the waves; Mistral-7B B = 32: 132 us against 135 in 4-wave blocks,
+// while the fp32 cache measured 167 against 164).
+template <int HD, int G, int KT, int NWV = 4>
+__global__ void __launch_bounds__(NWV * 64, 8 / NWV) attn_decode_kernel(
     RopeArgs ra, void *__restrict__ kc, void *__restrict__ vc,
     const int32_t *__restrict__ pos, const int32_t *__restrict__ slot, int nh, int nkv, int max_seq,
     int splits, float *__restrict__ part, u16 *__restrict__ o_hi, u16 *__restrict__ o_lo,
     float *__restrict__ o_f32) {
     constexpr int DPL = dims_per_lane<G>() < HD ? dims_per_lane<G>() : HD;
-    using R = Row<HD, DPL, KB>;
+    constexpr bool KB = KT == KV_BF16;
+    using R = Row<HD, DPL, KT>;
     constexpr int LP = R::LP;                 // lanes per position
     constexpr int PPW = WAVE / LP;            // positions per wave
-    constexpr int NG = 4 * PPW;               // lane groups per block
-    constexpr int NV = R::NV;
-    // positions per lane group per iteration: 8 (fp32) or 4 (bf16) words of K
-    // and of V in flight per lane
-    constexpr int NB = (KB ? 4 : 8) / NV;
-    __shared__ float sm[4][G], sl[4][G];
-    __shared__ float sacc[4][G][HD];
+    constexpr int NG = NWV * PPW;             // lane groups per block
+    constexpr int NV = R::NV, NW = R::NW;
+    // positions per lane group per iteration: 8 (fp32) or 4 (bf16, 24-bit)
+    // words of K and of V in flight per lane
+    constexpr int NB = (KT == KV_F32 ? 8 : 4) / NV;
+    __shared__ float sm[NWV][G], sl[NWV][G];
+    __shared__ float sacc[NWV][G][HD];
     __shared__ float qs[G][HD];
 
     const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -202,15 +240,15 @@ __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
     const int end = min(nread, beg + chunk);
 
     const size_t head_base = ((size_t)slot[b] * nkv + kvh) * max_seq;
-    const char *K = static_cast<const char *>(kc) + head_base * HD * R::ES;
-    const char *V = static_cast<const char *>(vc) + head_base * HD * R::ES;
+    const char *K = static_cast<const char *>(kc) + head_base * R::RB;
+    const char *V = static_cast<const char *>(vc) + head_base * R::RB;
     const float qscale = LOG2E / sqrtf((float)HD);
 
     // Prologue: the group's rotated queries into LDS; the block whose range
     // holds the new slot stores the new position's key and value first.
-    decode_prologue<HD, KB>(ra, kc, vc, b, kvh, G, nh, nkv, p, max_seq, beg, end, head_base, qs);
+    decode_prologue<HD, KT>(ra, kc, vc, b, kvh, G, nh, nkv, p, max_seq, beg, end, head_base, qs);
 
-    // fp32 cache: q in fp32.  bf16 cache: q as (hi, lo) bf16 pairs matching
+    // fp32 and 24-bit caches: q in fp32.  bf16 cache: q as (hi, lo) bf16 pairs matching
     // the packing of the key words, for v_dot2 against the stored keys.
     constexpr int QN = KB ? DPL / 2 : DPL;
     float qr[G][KB ? 1 : DPL];
@@ -241,7 +279,7 @@ __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
         for (int i = 0; i < DPL; i++) acc[g][i] = 0.f;
     }
 
-    // fp32 cache, groups of up to 4 heads: two stages of NS = NB/2 positions
+    // fp32 or 24-bit cache, groups of up to 4 heads: two stages of NS = NB/2 positions
     // per lane group, software-pipelined: the next stage's K/V loads are issued
     // before the current stage's arithmetic, so the stream stays in flight
     // while it runs (the same registers as one batch of NB; measured 1.4 %
@@ -253,22 +291,22 @@ __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
     static_assert(!PIPE || NB % 2 == 0, "two stages of NB/2 positions");
     const int span = NG * NS;
     const int nstg = beg < end ? (end - beg + span - 1) / span : 0;
-    auto load = [&](u32x4 (&kr)[NS][NV], u32x4 (&vr)[NS][NV], int st) {
+    auto load = [&](u32x4 (&kr)[NS][NW], u32x4 (&vr)[NS][NW], int st) {
         const int base = beg + st * span;
 #pragma unroll
         for (int i = 0; i < NS; i++) {
             const int j = base + i * NG + gid;
             const int jj = j < end ? j : beg;   // rows past the range read the first row, masked below
-            R::load(K + (size_t)jj * HD * R::ES, u, kr[i]);
+            R::load(K + (size_t)jj * R::RB, u, kr[i]);
         }
 #pragma unroll
         for (int i = 0; i < NS; i++) {
             const int j = base + i * NG + gid;
             const int jj = j < end ? j : beg;
-            R::load(V + (size_t)jj * HD * R::ES, u, vr[i]);
+            R::load(V + (size_t)jj * R::RB, u, vr[i]);
         }
     };
-    auto step = [&](const u32x4 (&kr)[NS][NV], const u32x4 (&vr)[NS][NV], int st) {
+    auto step = [&](const u32x4 (&kr)[NS][NW], const u32x4 (&vr)[NS][NW], int st) {
         const int base = beg + st * span;
         float s[NS][G];
 #pragma unroll
@@ -341,7 +379,7 @@ __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
         }
     };
     if constexpr (PIPE) {
-        u32x4 kA[NS][NV], vA[NS][NV], kB[NS][NV], vB[NS][NV];
+        u32x4 kA[NS][NW], vA[NS][NW], kB[NS][NW], vB[NS][NW];
         if (nstg > 0) load(kA, vA, 0);
         for (int st = 0; st < nstg; st += 2) {
             if (st + 1 < nstg) load(kB, vB, st + 1);
@@ -352,7 +390,7 @@ __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
         }
     } else {
         for (int st = 0; st < nstg; st++) {
-            u32x4 kr[NS][NV], vr[NS][NV];
+            u32x4 kr[NS][NW], vr[NS][NW];
             load(kr, vr, st);
             step(kr, vr, st);
         }
@@ -386,15 +424,15 @@ __global__ void __launch_bounds__(256, 2) attn_decode_kernel(
         }
     }
     __syncthreads();
-    // merge the 4 waves: thread (g, i) handles one output element
+    // merge the NWV waves: thread (g, i) handles one output element
     for (int idx = threadIdx.x; idx < G * HD; idx += blockDim.x) {
         const int g = idx / HD, i = idx % HD;
         float mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < 4; w++) mx = fmaxf(mx, sm[w][g]);
+        for (int w = 0; w < NWV; w++) mx = fmaxf(mx, sm[w][g]);
         float L = 0.f, A = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; w++) {
+        for (int w = 0; w < NWV; w++) {
             const float f = mx == -INFINITY ? 0.f : fast_exp2(sm[w][g] - mx);
             L += sl[w][g] * f;
             A += sacc[w][g][i] * f;
@@ -465,15 +503,23 @@ __device__ __forceinline__ void wave_lds_sync() {
     asm volatile("" ::: "memory");
 }
 
-template <int HD, bool KB>
+// A 24-bit cache goes the fp32 way from registers on: its rows are rebuilt
+// as fp32 words, whose bf16 (hi, lo) split is exact (16 significant bits).
+// Its loads take the bf16 cache's dim order (8 consecutive dims a lane: one
+// 16-byte word of upper halves and the 8-byte run of their third bytes), and
+// its V pieces are 8 elements in two register quads.
+template <int HD, int KT>
 struct MfmaDec {
-    static constexpr int ES = KB ? 2 : 4;
+    static constexpr bool KB = KT == KV_BF16;
+    static constexpr int ES = KB ? 2 : 4;         // bytes of a staged V element
     static constexpr int CH = 16;                 // positions per wave step
     static constexpr int NKS = HD / 32;           // k steps of S^T = K Q^T
     static constexpr int NDT = HD / 16;           // 16-dim tiles of O^T
-    static constexpr int KW = KB ? 1 : 2;         // 16-byte words of a lane's 8 key dims
-    static constexpr int RB = HD * ES;            // bytes of a cache row
-    static constexpr int PPR = RB / 16;           // 16-byte pieces per row
+    static constexpr int KW = KB ? 1 : 2;         // register quads of a lane's 8 key dims
+    static constexpr int RB = kv_row_bytes<KT>(HD);   // bytes of a cache row
+    static constexpr int EPP = KT == KV_F32 ? 4 : 8;  // elements of a V piece
+    static constexpr int VQ = KT == KV_F24 ? 2 : 1;   // register quads of a V piece
+    static constexpr int PPR = HD / EPP;          // V pieces per row
     static constexpr int VW = CH * PPR / WAVE;    // V pieces per lane per step
     static constexpr int VLD = KB ? HD + 8 : HD + 4;   // elements per staged V row
     static constexpr int VSTAGE = CH * VLD * ES;  // bytes of one wave's V stage
@@ -481,13 +527,15 @@ struct MfmaDec {
     static constexpr int WBYTES = VSTAGE > SACC ? VSTAGE : SACC;
 };
 
-template <int HD, bool KB, int NW>
+template <int HD, int KT, int NW>
 __global__ void __launch_bounds__(NW * 64, NW <= 4 ? 2 : 1) attn_decode_mfma_kernel(
     RopeArgs ra, void *__restrict__ kc, void *__restrict__ vc, const int32_t *__restrict__ pos,
     const int32_t *__restrict__ slot, int nh, int nkv, int max_seq, int splits, float *__restrict__ part,
     u16 *__restrict__ o_hi, u16 *__restrict__ o_lo, float *__restrict__ o_f32) {
-    using C = MfmaDec<HD, KB>;
+    using C = MfmaDec<HD, KT>;
+    constexpr bool KB = C::KB;
     constexpr int CH = C::CH, NKS = C::NKS, NDT = C::NDT, KW = C::KW, VW = C::VW, PPR = C::PPR, ES = C::ES;
+    constexpr int VQ = C::VQ, EPP = C::EPP;
     __shared__ float qs[16][HD];
     __shared__ __attribute__((aligned(16))) char wst[NW][C::WBYTES];   // V stage, then the wave's outputs
     __shared__ float sm[NW][16], sl[NW][16];
@@ -510,27 +558,46 @@ __global__ void __launch_bounds__(NW * 64, NW <= 4 ? 2 : 1) attn_decode_mfma_ker
     // keys; any assignment of dims to MFMA k slots gives the same dot product):
     // with 4-byte elements, element e is dim 32ks + 16(e/4) + 4c + e%4, so one
     // load instruction (16 bytes per lane) covers 64 contiguous bytes of each
-    // key row; with 2-byte elements dims 32ks + 8c + e do the same.
-    auto kdim = [&](int ks, int e) { return KB ? 32 * ks + 8 * c + e : 32 * ks + 16 * (e >> 2) + 4 * c + (e & 3); };
-    auto load = [&](int c0, u32x4 (&kr)[NKS][KW], u32x4 (&vr)[VW]) {
+    // key row; with 2-byte elements (and the 24-bit rows' upper halves) dims
+    // 32ks + 8c + e do the same.
+    auto kdim = [&](int ks, int e) {
+        return KT != KV_F32 ? 32 * ks + 8 * c + e : 32 * ks + 16 * (e >> 2) + 4 * c + (e & 3);
+    };
+    auto load = [&](int c0, u32x4 (&kr)[NKS][KW], u32x4 (&vr)[VW * VQ]) {
         // A operand of S^T: lane (r, c) reads position c0 + r at dims kdim(ks, .)
         const int j = c0 + r;
         const char *krow = K + (size_t)(j < end ? j : beg) * C::RB;
 #pragma unroll
-        for (int ks = 0; ks < NKS; ks++)
+        for (int ks = 0; ks < NKS; ks++) {
+            if constexpr (KT == KV_F24) {
+                kr[ks][0] = ntload16(krow + kdim(ks, 0) * 2);
+                const u32x2 l = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(krow + f24_lo_off(HD, kdim(ks, 0))));
+                kr[ks][1][0] = l[0];
+                kr[ks][1][1] = l[1];
+            } else {
 #pragma unroll
-            for (int w = 0; w < KW; w++) kr[ks][w] = ntload16(krow + kdim(ks, 4 * w) * ES);
-        // V rows c0 .. c0+15 as 16-byte pieces, piece f = q*64 + lane
+                for (int w = 0; w < KW; w++) kr[ks][w] = ntload16(krow + kdim(ks, 4 * w) * ES);
+            }
+        }
+        // V rows c0 .. c0+15 as pieces of EPP elements, piece f = q*64 + lane
 #pragma unroll
         for (int q = 0; q < VW; q++) {
             const int f = q * WAVE + lane, rr = f / PPR, cc = f % PPR;
             const int jv = c0 + rr;
-            vr[q] = ntload16(V + (size_t)(jv < end ? jv : beg) * C::RB + 16 * cc);
+            const char *vrow = V + (size_t)(jv < end ? jv : beg) * C::RB;
+            if constexpr (KT == KV_F24) {
+                vr[2 * q] = ntload16(vrow + 16 * cc);
+                const u32x2 l = __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(vrow + f24_lo_off(HD, 8 * cc)));
+                vr[2 * q + 1][0] = l[0];
+                vr[2 * q + 1][1] = l[1];
+            } else {
+                vr[q] = ntload16(vrow + 16 * cc);
+            }
         }
     };
 
     for (int i = threadIdx.x; i < (16 - G) * HD; i += blockDim.x) qs[G + i / HD][i % HD] = 0.f;
-    decode_prologue<HD, KB>(ra, kc, vc, b, kvh, G, nh, nkv, p, max_seq, beg, end, head_base, qs);
+    decode_prologue<HD, KT>(ra, kc, vc, b, kvh, G, nh, nkv, p, max_seq, beg, end, head_base, qs);
 
     // B operand of S^T: head r's query over kdim's dims, scaled for base-2
     // softmax, as a bf16 (hi, lo) pair
@@ -550,11 +617,20 @@ __global__ void __launch_bounds__(NW * 64, NW <= 4 ? 2 : 1) attn_decode_mfma_ker
     for (int d = 0; d < NDT; d++) o[d] = (floatx4){0.f, 0.f, 0.f, 0.f};
     char *vs = wst[wv];
 
-    auto step = [&](int c0, const u32x4 (&kr)[NKS][KW], const u32x4 (&vr)[VW]) {
+    auto step = [&](int c0, const u32x4 (&kr)[NKS][KW], const u32x4 (&vr)[VW * VQ]) {
 #pragma unroll
         for (int q = 0; q < VW; q++) {
             const int f = q * WAVE + lane, rr = f / PPR, cc = f % PPR;
-            *reinterpret_cast<u32x4 *>(vs + rr * C::VLD * ES + 16 * cc) = vr[q];
+            if constexpr (KT == KV_F24) {
+                // staged as the fp32 words
+                float e8[8];
+                f24_unpack8(vr[2 * q], (u32x2){vr[2 * q + 1][0], vr[2 * q + 1][1]}, e8);
+                float *dst = reinterpret_cast<float *>(vs + rr * C::VLD * ES) + EPP * cc;
+                *reinterpret_cast<float4 *>(dst) = make_float4(e8[0], e8[1], e8[2], e8[3]);
+                *reinterpret_cast<float4 *>(dst + 4) = make_float4(e8[4], e8[5], e8[6], e8[7]);
+            } else {
+                *reinterpret_cast<u32x4 *>(vs + rr * C::VLD * ES + 16 * cc) = vr[q];
+            }
         }
         floatx4 st = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -564,14 +640,29 @@ __global__ void __launch_bounds__(NW * 64, NW <= 4 ? 2 : 1) attn_decode_mfma_ker
                 st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[ks], st, 0, 0, 0);
                 st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[ks], st, 0, 0, 0);
             } else {
-                float v[8];
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    v[j] = __uint_as_float(kr[ks][0][j]);
-                    v[4 + j] = __uint_as_float(kr[ks][1][j]);
-                }
                 bf16x8 kh, kl;
-                split8(v, kh, kl);
+                if constexpr (KT == KV_F24) {
+                    // hi: the stored upper halves; lo: the rest of each rebuilt word, exact in bf16
+                    float v[8];
+                    f24_unpack8(kr[ks][0], (u32x2){kr[ks][1][0], kr[ks][1][1]}, v);
+                    u32x4 lw;
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const float l0 = v[2 * j] - __uint_as_float(kr[ks][0][j] << 16);
+                        const float l1 = v[2 * j + 1] - __uint_as_float(kr[ks][0][j] & 0xFFFF0000u);
+                        lw[j] = (__float_as_uint(l0) >> 16) | (__float_as_uint(l1) & 0xFFFF0000u);
+                    }
+                    kh = __builtin_bit_cast(bf16x8, kr[ks][0]);
+                    kl = __builtin_bit_cast(bf16x8, lw);
+                } else {
+                    float v[8];
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        v[j] = __uint_as_float(kr[ks][0][j]);
+                        v[4 + j] = __uint_as_float(kr[ks][1][j]);
+                    }
+                    split8(v, kh, kl);
+                }
                 st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, qh[ks], st, 0, 0, 0);
                 st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, ql[ks], st, 0, 0, 0);
                 st = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kl, qh[ks], st, 0, 0, 0);
@@ -633,7 +724,7 @@ __global__ void __launch_bounds__(NW * 64, NW <= 4 ? 2 : 1) attn_decode_mfma_ker
     {
         int c0 = beg + wv * CH;
         const int nsteps = c0 < end ? (end - c0 + NW * CH - 1) / (NW * CH) : 0;
-        u32x4 kA[NKS][KW], vA[VW], kB[NKS][KW], vB[VW];
+        u32x4 kA[NKS][KW], vA[VW * VQ], kB[NKS][KW], vB[VW * VQ];
         if (nsteps > 0) load(c0, kA, vA);
         for (int it = 0; it < nsteps; it += 2) {
             load(c0 + NW * CH, kB, vB);
@@ -725,11 +816,26 @@ __global__ void __launch_bounds__(128) attn_merge_kernel(int nh, int hd, int spl
     }
 }
 
-template <int HD, bool KB>
+template <int HD, int KT>
 bool launch_decode_hd(hipStream_t st, int G, dim3 grid, const RopeArgs &ra, void *kc, void *vc,
                       const int32_t *pos, const int32_t *slot, int nh, int nkv, int max_seq, int splits,
-                      float *part, u16 *o_hi, u16 *o_lo, float *o_f32) {
-#define AD(GG) hipLaunchKernelGGL((attn_decode_kernel<HD, GG, KB>), grid, dim3(256), 0, st, ra, kc, vc, pos, \
+                      float *part, u16 *o_hi, u16 *o_lo, float *o_f32, bool wide) {
+    if constexpr (KT == KV_F24 && HD >= 64) {
+        // one 8-wave block per (row, kv head) pair
+        if (wide && G <= 4) {
+#define ADW(GG) hipLaunchKernelGGL((attn_decode_kernel<HD, GG, KT, 8>), grid, dim3(512), 0, st, ra, kc, vc, pos, \
+                                   slot, nh, nkv, max_seq, splits, part, o_hi, o_lo, o_f32)
+            switch (G) {
+                case 1: ADW(1); return true;
+                case 2: ADW(2); return true;
+                case 3: ADW(3); return true;
+                case 4: ADW(4); return true;
+            }
+#undef ADW
+        }
+    }
+    (void)wide;
+#define AD(GG) hipLaunchKernelGGL((attn_decode_kernel<HD, GG, KT>), grid, dim3(256), 0, st, ra, kc, vc, pos, \
                                   slot, nh, nkv, max_seq, splits, part, o_hi, o_lo, o_f32)
     switch (G) {
         case 1: AD(1); return true;
@@ -745,27 +851,28 @@ bool launch_decode_hd(hipStream_t st, int G, dim3 grid, const RopeArgs &ra, void
     return false;
 }
 
-template <bool KB>
+template <int KT>
 const void *decode_probe_fn(int hd) {
-    return hd == 128 ? (const void *)attn_decode_kernel<128, 4, KB>
-         : hd == 64  ? (const void *)attn_decode_kernel<64, 4, KB>
-                     : (const void *)attn_decode_kernel<16, 4, KB>;
+    return hd == 128 ? (const void *)attn_decode_kernel<128, 4, KT>
+         : hd == 64  ? (const void *)attn_decode_kernel<64, 4, KT>
+                     : (const void *)attn_decode_kernel<16, 4, KT>;
 }
 
 // Groups of more than 4 heads, and any group with a bf16 cache (head_dim 64 or
 // 128), take the MFMA form: the lane-group kernel repeats each position's
 // softmax update and V products for every head of the group, which made a
-// 7-head group, and the bf16 cache's v_dot2 scores, ALU-limited.  An fp32
-// cache with up to 4 heads stays on the lane-group kernel, which streams it
-// at 83 % of HBM (its MFMA form at head_dim 128 spills registers).
-bool use_mfma(int hd, int G, int kv_bf16) {
-    return G <= 16 && (hd == 64 || hd == 128) && (G > 4 || kv_bf16);
+// 7-head group, and the bf16 cache's v_dot2 scores, ALU-limited.  An fp32 or
+// 24-bit cache with up to 4 heads stays on the lane-group kernel, which
+// streams an fp32 cache at 83 % of HBM (its MFMA form at head_dim 128 spills
+// registers).
+bool use_mfma(int hd, int G, int kv_kind) {
+    return G <= 16 && (hd == 64 || hd == 128) && (G > 4 || kv_kind == KV_BF16);
 }
 
 }  // namespace
 
-int attn_decode_splits(int B, int nkv, int readable, int hd, int G, int kv_bf16) {
-    if (use_mfma(hd, G, kv_bf16)) {
+int attn_decode_splits(int B, int nkv, int readable, int hd, int G, int kv_kind) {
+    if (use_mfma(hd, G, kv_kind)) {
         // As many (row, kv head) pairs as CUs: one 8-wave block each, no merge
         // (Mistral-7B, bf16 cache, B = 32: 84 us against 91 us for 4-wave
         // blocks in two splits).  Fewer pairs: 4-wave blocks, two resident per
@@ -779,21 +886,22 @@ int attn_decode_splits(int B, int nkv, int readable, int hd, int G, int kv_bf16)
         if (s > 64) s = 64;
         return s < 1 ? 1 : s;
     }
-    // One round of blocks.  An fp32 cache is streamed at the memory's rate by
-    // one block per CU, and each extra split costs the merge pass; with a bf16
-    // cache the lanes' arithmetic is the limit, so every resident-block slot is
-    // filled.  At least 128 positions per split.
-    static int occ_cache[2][3] = {{0, 0, 0}, {0, 0, 0}};
+    // One round of blocks.  An fp32 (or 24-bit) cache is streamed at the
+    // memory's rate by one block per CU, and each extra split costs the merge
+    // pass; with a bf16 cache the lanes' arithmetic is the limit, so every
+    // resident-block slot is filled.  At least 128 positions per split.
+    const bool kb = kv_kind == KV_BF16;
+    static int occ_cache[3] = {0, 0, 0};
     const int which = hd == 128 ? 0 : hd == 64 ? 1 : 2;
-    int &occ_c = occ_cache[kv_bf16 ? 1 : 0][which];
-    if (!occ_c) {
+    int &occ_c = occ_cache[which];
+    if (kb && !occ_c) {
         int occ = 0;
-        const void *fn = kv_bf16 ? decode_probe_fn<true>(hd) : decode_probe_fn<false>(hd);
+        const void *fn = decode_probe_fn<KV_BF16>(hd);
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, 256, 0) != hipSuccess || occ <= 0) occ = 2;
         occ_c = occ;
     }
     (void)G;
-    const int slots = (kv_bf16 ? occ_c : 1) * num_cus();
+    const int slots = (kb ? occ_c : 1) * num_cus();
     int s = slots / (B * nkv);
     const int maxs = readable / 128;
     if (s > maxs) s = maxs;
@@ -802,42 +910,44 @@ int attn_decode_splits(int B, int nkv, int readable, int hd, int G, int kv_bf16)
     return s;
 }
 
-void launch_attn_decode(hipStream_t st, int B, const RopeArgs &ra, void *kc, void *vc, int kv_bf16,
+void launch_attn_decode(hipStream_t st, int B, const RopeArgs &ra, void *kc, void *vc, int kv_kind,
                         const int32_t *pos, const int32_t *slot, int nh, int nkv, int hd, int max_seq, int splits,
                         float *part, u16 *o_hi, u16 *o_lo, float *o_f32) {
     if (B <= 0) return;
     const int G = nh / nkv;
     dim3 grid(splits, nkv, B);
-    if (use_mfma(hd, G, kv_bf16)) {
+    if (use_mfma(hd, G, kv_kind)) {
         // one 8-wave block per (row, kv head) when the pairs fill the CUs
         // (attn_decode_splits then gives one split), else 4-wave blocks
         const bool wide = splits == 1 && B * nkv >= num_cus();
-#define MD(HD, KB, NW) hipLaunchKernelGGL((attn_decode_mfma_kernel<HD, KB, NW>), grid, dim3(NW * 64), 0, st, ra, kc, \
+#define MD(HD, KT, NW) hipLaunchKernelGGL((attn_decode_mfma_kernel<HD, KT, NW>), grid, dim3(NW * 64), 0, st, ra, kc, \
                                           vc, pos, slot, nh, nkv, max_seq, splits, part, o_hi, o_lo, o_f32)
-        if (kv_bf16) {
-            if (hd == 128) { if (wide) MD(128, true, 8); else MD(128, true, 4); }
-            else { if (wide) MD(64, true, 8); else MD(64, true, 4); }
-        } else {
-            if (hd == 128) { if (wide) MD(128, false, 8); else MD(128, false, 4); }
-            else { if (wide) MD(64, false, 8); else MD(64, false, 4); }
-        }
+#define MDH(KT)                                                        \
+        if (hd == 128) { if (wide) MD(128, KT, 8); else MD(128, KT, 4); } \
+        else { if (wide) MD(64, KT, 8); else MD(64, KT, 4); }
+        if (kv_kind == KV_BF16) { MDH(KV_BF16) }
+        else if (kv_kind == KV_F24) { MDH(KV_F24) }
+        else { MDH(KV_F32) }
+#undef MDH
 #undef MD
         if (splits > 1)
             hipLaunchKernelGGL(attn_merge_kernel, dim3(nh, B), dim3(hd), 0, st, nh, hd, splits, part, o_hi, o_lo,
                                o_f32);
         return;
     }
-#define LD(HD, KB) launch_decode_hd<HD, KB>(st, G, grid, ra, kc, vc, pos, slot, nh, nkv, max_seq, splits, part, \
-                                            o_hi, o_lo, o_f32)
-    if (kv_bf16) {
-        if (hd == 128) LD(128, true);
-        else if (hd == 64) LD(64, true);
-        else LD(16, true);
-    } else {
-        if (hd == 128) LD(128, false);
-        else if (hd == 64) LD(64, false);
-        else LD(16, false);
-    }
+    // the lane-group kernel on a 24-bit cache in 8-wave blocks where one split
+    // covers the readable range and the pairs fill the CUs
+    const bool wide = splits == 1 && B * nkv >= num_cus();
+#define LD(HD, KT) launch_decode_hd<HD, KT>(st, G, grid, ra, kc, vc, pos, slot, nh, nkv, max_seq, splits, part, \
+                                            o_hi, o_lo, o_f32, wide)
+#define LDH(KT)                        \
+        if (hd == 128) LD(128, KT);    \
+        else if (hd == 64) LD(64, KT); \
+        else LD(16, KT);
+    if (kv_kind == KV_BF16) { LDH(KV_BF16) }
+    else if (kv_kind == KV_F24) { LDH(KV_F24) }
+    else { LDH(KV_F32) }
+#undef LDH
 #undef LD
     if (splits > 1)
         hipLaunchKernelGGL(attn_merge_kernel, dim3(nh, B), dim3(hd < 64 ? 64 : hd), 0, st, nh, hd, splits, part,

@@ -5,6 +5,7 @@
 // section "Attend".
 #include "common.h"
 #include "kernels.h"
+#include "kvcache.h"
 
 namespace {
 
@@ -22,27 +23,15 @@ __device__ __forceinline__ void store_out(float v, size_t off, u16 *o_hi, u16 *o
 // chunk buffer [T][nkv][HD] for chunk positions when a chunk buffer is given,
 // else the layer cache row at slot j % ring_mod (ring) or j.
 // GEN = false: every position is in the cache at slot == position.
-template <int HD, bool KB, bool GEN>
+template <int HD, int KT, bool GEN>
 __device__ __forceinline__ const char *kv_row(const void *cache, const void *chunk, size_t head_base, int j,
                                               int start_pos, int ring_mod, int nkv, int kvh) {
-    constexpr int ES = KB ? 2 : 4;
-    if constexpr (!GEN) return static_cast<const char *>(cache) + (head_base + j) * HD * ES;
+    constexpr int RB = kv_row_bytes<KT>(HD);
+    if constexpr (!GEN) return static_cast<const char *>(cache) + (head_base + j) * RB;
     if (j >= start_pos)
-        return static_cast<const char *>(chunk) + ((size_t)(j - start_pos) * nkv + kvh) * HD * ES;
+        return static_cast<const char *>(chunk) + ((size_t)(j - start_pos) * nkv + kvh) * RB;
     const int s = ring_mod ? j % ring_mod : j;
-    return static_cast<const char *>(cache) + (head_base + s) * HD * ES;
-}
-
-// Four elements of a K/V row (fp32, or bf16 bits), from element e.
-template <bool KB>
-__device__ __forceinline__ float4 row4(const char *row, int e) {
-    if constexpr (KB) {
-        const uint2 r = *reinterpret_cast<const uint2 *>(row + (size_t)e * 2);
-        return make_float4(__uint_as_float(r.x << 16), __uint_as_float(r.x & 0xFFFF0000u),
-                           __uint_as_float(r.y << 16), __uint_as_float(r.y & 0xFFFF0000u));
-    } else {
-        return *reinterpret_cast<const float4 *>(row + (size_t)e * 4);
-    }
+    return static_cast<const char *>(cache) + (head_base + s) * RB;
 }
 
 }  // namespace
@@ -57,7 +46,7 @@ namespace {
 
 constexpr int BQ = 32, BKV = 32, SB = 8;
 
-template <int HD, int G, int SPLIT, bool KB, bool GEN>
+template <int HD, int G, int SPLIT, int KT, bool GEN>
 __global__ void __launch_bounds__(BQ * G * SPLIT) attn_prefill_kernel(
     int T, int start_pos, int slot, const float *__restrict__ q, const void *__restrict__ kc,
     const void *__restrict__ vc, int nh, int nkv, int max_seq, int window, int ring_mod,
@@ -102,8 +91,8 @@ __global__ void __launch_bounds__(BQ * G * SPLIT) attn_prefill_kernel(
             const int j = kb + row;
             float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
             if (j <= last_pos) {
-                kv = row4<KB>(kv_row<HD, KB, GEN>(kc, ck, head_base, j, start_pos, ring_mod, nkv, kvh), 4 * c4);
-                vv = row4<KB>(kv_row<HD, KB, GEN>(vc, cv, head_base, j, start_pos, ring_mod, nkv, kvh), 4 * c4);
+                kv = kv_load4<KT, HD>(kv_row<HD, KT, GEN>(kc, ck, head_base, j, start_pos, ring_mod, nkv, kvh), 4 * c4);
+                vv = kv_load4<KT, HD>(kv_row<HD, KT, GEN>(vc, cv, head_base, j, start_pos, ring_mod, nkv, kvh), 4 * c4);
             }
             *reinterpret_cast<float4 *>(&sk[row][4 * c4]) = kv;
             *reinterpret_cast<float4 *>(&sv[row][4 * c4]) = vv;
@@ -158,11 +147,11 @@ __global__ void __launch_bounds__(BQ * G * SPLIT) attn_prefill_kernel(
     for (int i = 0; i < D; i++) store_out(acc[i] * inv, off + i, o_hi, o_lo, o_f32);
 }
 
-template <int HD, int SPLIT, bool KB, bool GEN>
+template <int HD, int SPLIT, int KT, bool GEN>
 bool launch_prefill_hd(hipStream_t st, int G, dim3 grid, int T, int start_pos, int slot, const float *q,
                        const void *kc, const void *vc, int nh, int nkv, int max_seq, int window, int ring_mod,
                        const void *ck, const void *cv, u16 *o_hi, u16 *o_lo, float *o_f32) {
-#define AP(GG) hipLaunchKernelGGL((attn_prefill_kernel<HD, GG, SPLIT, KB, GEN>), grid, dim3(BQ * GG * SPLIT), 0, st, T, \
+#define AP(GG) hipLaunchKernelGGL((attn_prefill_kernel<HD, GG, SPLIT, KT, GEN>), grid, dim3(BQ * GG * SPLIT), 0, st, T, \
                                   start_pos, slot, q, kc, vc, nh, nkv, max_seq, window, ring_mod, ck, cv, o_hi, \
                                   o_lo, o_f32)
     switch (G) {
@@ -207,7 +196,7 @@ __device__ __forceinline__ bf16x8 pack8(const uint32_t *h) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
-template <int HD, int G, bool KB, bool GEN>
+template <int HD, int G, int KT, bool GEN>
 __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
     int T, int start_pos, int slot, const float *__restrict__ q, const void *__restrict__ kc,
     const void *__restrict__ vc, int nh, int nkv, int max_seq, int window, int ring_mod,
@@ -219,6 +208,7 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
     constexpr int KS = HD / 16;     // MFMA k-steps over head_dim
     constexpr int DT = HD / 32;     // output dim tiles
     __shared__ __attribute__((aligned(16))) u16 sKh[MKV * KLD];
+    constexpr bool KB = KT == KV_BF16;
     __shared__ __attribute__((aligned(16))) u16 sKl[KB ? 8 : MKV * KLD];
     __shared__ __attribute__((aligned(16))) u16 sVh[HD * VLD];
     __shared__ __attribute__((aligned(16))) u16 sVl[KB ? 8 : HD * VLD];
@@ -277,8 +267,8 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
     for (int kb = first_key; kb <= last_pos; kb += MKV) {
         __syncthreads();
         // K tile -> [key][dim] hi/lo; V tile -> transposed [dim][key] hi/lo
-        auto krow = [&](int j) { return kv_row<HD, KB, GEN>(kc, ck, head_base, j, start_pos, ring_mod, nkv, kvh); };
-        auto vrow = [&](int j) { return kv_row<HD, KB, GEN>(vc, cv, head_base, j, start_pos, ring_mod, nkv, kvh); };
+        auto krow = [&](int j) { return kv_row<HD, KT, GEN>(kc, ck, head_base, j, start_pos, ring_mod, nkv, kvh); };
+        auto vrow = [&](int j) { return kv_row<HD, KT, GEN>(vc, cv, head_base, j, start_pos, ring_mod, nkv, kvh); };
         if constexpr (KB) {
             for (int i = tid; i < MKV * HD / 8; i += 256) {
                 const int key = i / (HD / 8), c8 = i % (HD / 8);
@@ -307,7 +297,7 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
                 const int key = i / (HD / 4), c4 = i % (HD / 4);
                 const int j = kb + key;
                 float4 kv = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (j <= last_pos) kv = *reinterpret_cast<const float4 *>(krow(j) + 16 * c4);
+                if (j <= last_pos) kv = kv_load4<KT, HD>(krow(j), 4 * c4);
                 uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
                 split_bf16(kv.x, h0, l0); split_bf16(kv.y, h1, l1); split_bf16(kv.z, h2, l2); split_bf16(kv.w, h3, l3);
                 *reinterpret_cast<uint2 *>(sKh + key * KLD + 4 * c4) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
@@ -317,8 +307,8 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
                 const int kp = i / (HD / 4), c4 = i % (HD / 4);
                 const int j = kb + 2 * kp;
                 float4 v0 = make_float4(0.f, 0.f, 0.f, 0.f), v1 = v0;
-                if (j <= last_pos) v0 = *reinterpret_cast<const float4 *>(vrow(j) + 16 * c4);
-                if (j + 1 <= last_pos) v1 = *reinterpret_cast<const float4 *>(vrow(j + 1) + 16 * c4);
+                if (j <= last_pos) v0 = kv_load4<KT, HD>(vrow(j), 4 * c4);
+                if (j + 1 <= last_pos) v1 = kv_load4<KT, HD>(vrow(j + 1), 4 * c4);
                 const float a0[4] = {v0.x, v0.y, v0.z, v0.w}, a1[4] = {v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
                 for (int e = 0; e < 4; e++) {
@@ -420,11 +410,11 @@ __global__ void __launch_bounds__(256, 2) attn_prefill_mfma_kernel(
         }
 }
 
-template <int HD, bool KB, bool GEN>
+template <int HD, int KT, bool GEN>
 bool launch_prefill_mfma_hd(hipStream_t st, int G, int T, int start_pos, int slot, const float *q, const void *kc,
                             const void *vc, int nh, int nkv, int max_seq, int window, int ring_mod, const void *ck,
                             const void *cv, u16 *o_hi, u16 *o_lo, float *o_f32) {
-#define APM(GG) hipLaunchKernelGGL((attn_prefill_mfma_kernel<HD, GG, KB, GEN>), dim3((T + NQV / GG - 1) / (NQV / GG), nkv), \
+#define APM(GG) hipLaunchKernelGGL((attn_prefill_mfma_kernel<HD, GG, KT, GEN>), dim3((T + NQV / GG - 1) / (NQV / GG), nkv), \
                                    dim3(256), 0, st, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, window, \
                                    ring_mod, ck, cv, o_hi, o_lo, o_f32)
     switch (G) {
@@ -444,7 +434,7 @@ bool launch_prefill_mfma_hd(hipStream_t st, int G, int T, int start_pos, int slo
 }  // namespace
 
 void launch_attn_prefill(hipStream_t st, int T, int start_pos, int slot, const float *q, const void *kc,
-                         const void *vc, int kv_bf16, int nh, int nkv, int hd, int max_seq, int window, int ring,
+                         const void *vc, int kv_kind, int nh, int nkv, int hd, int max_seq, int window, int ring,
                          const void *ck, const void *cv, u16 *o_hi, u16 *o_lo, float *o_f32) {
     if (T <= 0) return;
     const int G = nh / nkv;
@@ -452,26 +442,25 @@ void launch_attn_prefill(hipStream_t st, int T, int start_pos, int slot, const f
     dim3 grid((T + BQ - 1) / BQ, nkv);
     // the general form (ring slots, chunk buffers, window bound) only for a
     // chunk held back from the cache; otherwise slot == position
-#define LM(HD, KB, GEN) launch_prefill_mfma_hd<HD, KB, GEN>(st, G, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, \
+#define LM(HD, KT, GEN) launch_prefill_mfma_hd<HD, KT, GEN>(st, G, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, \
                                                             window, ring_mod, ck, cv, o_hi, o_lo, o_f32)
-#define LF(HD, KB, GEN) launch_prefill_hd<HD, 1, KB, GEN>(st, G, grid, T, start_pos, slot, q, kc, vc, nh, nkv, \
+#define LF(HD, KT, GEN) launch_prefill_hd<HD, 1, KT, GEN>(st, G, grid, T, start_pos, slot, q, kc, vc, nh, nkv, \
                                                           max_seq, window, ring_mod, ck, cv, o_hi, o_lo, o_f32)
-#define PICK(GEN)                                   \
-    if (kv_bf16) {                                  \
-        if (hd == 128) LM(128, true, GEN);          \
-        else if (hd == 64) LM(64, true, GEN);       \
-        else LF(16, true, GEN);                     \
-    } else {                                        \
-        if (hd == 128) LM(128, false, GEN);         \
-        else if (hd == 64) LM(64, false, GEN);      \
-        else LF(16, false, GEN);                    \
-    }
+#define PICKK(KT, GEN)                  \
+    if (hd == 128) LM(128, KT, GEN);        \
+    else if (hd == 64) LM(64, KT, GEN);     \
+    else LF(16, KT, GEN);
+#define PICK(GEN)                                                  \
+    if (kv_kind == KV_BF16) { PICKK(KV_BF16, GEN) }                \
+    else if (kv_kind == KV_F24) { PICKK(KV_F24, GEN) }             \
+    else { PICKK(KV_F32, GEN) }
     if (ck) {
         PICK(true)
     } else {
         PICK(false)
     }
 #undef PICK
+#undef PICKK
 #undef LM
 #undef LF
 }

@@ -36,6 +36,7 @@
 //  (the split-KV merge of the decode attention, over key chunks).
 #include "common.h"
 #include "kernels.h"
+#include "kvcache.h"
 
 namespace {
 
@@ -59,11 +60,14 @@ struct Img {
 
 __device__ __forceinline__ uint32_t bf16_rne(float x) { return f32_to_bf16_bits(x); }
 
-// One tile (64 positions) of one kv head.  Positions >= npos are zero.
-template <int HD, bool KB>
+// One tile (64 positions) of one kv head.  Positions >= npos are zero.  A
+// 24-bit cache (KT = KV_F24) makes the fp32 cache's image: its rebuilt fp32
+// words split exactly into the (hi, lo) pair.
+template <int HD, int KT>
 __global__ void __launch_bounds__(256) kv_tile_kernel(const void *__restrict__ kc, const void *__restrict__ vc,
                                                       int max_seq, int slot, int nkv, int npos, int ntiles,
                                                       u16 *__restrict__ img) {
+    constexpr bool KB = KT == KV_BF16;
     using I = Img<HD, KB>;
     __shared__ float sv[TK][HD + 1];
     const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
@@ -84,8 +88,9 @@ __global__ void __launch_bounds__(256) kv_tile_kernel(const void *__restrict__ k
                 vx[0] = bf16_bits_to_f32(vb2.x & 0xFFFFu); vx[1] = bf16_bits_to_f32(vb2.x >> 16);
                 vx[2] = bf16_bits_to_f32(vb2.y & 0xFFFFu); vx[3] = bf16_bits_to_f32(vb2.y >> 16);
             } else {
-                const float4 a = *reinterpret_cast<const float4 *>(static_cast<const float *>(kc) + (hb + p) * HD + 4 * c4);
-                const float4 b = *reinterpret_cast<const float4 *>(static_cast<const float *>(vc) + (hb + p) * HD + 4 * c4);
+                constexpr int RB = kv_row_bytes<KT>(HD);
+                const float4 a = kv_load4<KT, HD>(static_cast<const char *>(kc) + (hb + p) * RB, 4 * c4);
+                const float4 b = kv_load4<KT, HD>(static_cast<const char *>(vc) + (hb + p) * RB, 4 * c4);
                 kx[0] = a.x; kx[1] = a.y; kx[2] = a.z; kx[3] = a.w;
                 vx[0] = b.x; vx[1] = b.y; vx[2] = b.z; vx[3] = b.w;
             }
@@ -421,11 +426,12 @@ void chunking(int T, int start_pos, int rows_per_block, int nkv, int max_chunks,
     nch = (ntiles_max + chunk - 1) / chunk;
 }
 
-template <int HD, bool KB>
+template <int HD, int KT>
 bool launch_hd(hipStream_t st, int G, int T, int start_pos, int slot, const float *q, const void *kc,
                const void *vc, int nh, int nkv, int max_seq, u16 *img, float *part, size_t part_floats, u16 *o_hi,
                u16 *o_lo, float *o_f32) {
     if (G < 1 || G > 8) return false;
+    constexpr bool KB = KT == KV_BF16;
     const int npos = start_pos + T;
     const int ntiles = (npos + TK - 1) / TK;
     constexpr int LDSB = 2 * Img<HD, KB>::BYTES;
@@ -435,7 +441,7 @@ bool launch_hd(hipStream_t st, int G, int T, int start_pos, int slot, const floa
     int chunk, nch;
     chunking(T, start_pos, rows, nkv, max_chunks, chunk, nch);
     const int rbs = (T + rows - 1) / rows;
-    hipLaunchKernelGGL((kv_tile_kernel<HD, KB>), dim3(ntiles, nkv), dim3(256), 0, st, kc, vc, max_seq, slot, nkv,
+    hipLaunchKernelGGL((kv_tile_kernel<HD, KT>), dim3(ntiles, nkv), dim3(256), 0, st, kc, vc, max_seq, slot, nkv,
                        npos, ntiles, img);
 #define AT(GG)                                                                                                  \
     do {                                                                                                        \
@@ -462,7 +468,8 @@ bool launch_hd(hipStream_t st, int G, int T, int start_pos, int slot, const floa
 
 }  // namespace
 
-size_t attn_tiles_bytes(int max_pos, int nkv, int hd, int kv_bf16) {
+size_t attn_tiles_bytes(int max_pos, int nkv, int hd, int kv_kind) {
+    const bool kv_bf16 = kv_kind == KV_BF16;
     const size_t ntiles = (size_t)(max_pos + TK - 1) / TK;
     size_t per = 0;
     if (hd == 128) per = kv_bf16 ? Img<128, true>::BYTES : Img<128, false>::BYTES;
@@ -471,15 +478,17 @@ size_t attn_tiles_bytes(int max_pos, int nkv, int hd, int kv_bf16) {
 }
 
 bool launch_attn_prefill_tiles(hipStream_t st, int T, int start_pos, int slot, const float *q, const void *kc,
-                               const void *vc, int kv_bf16, int nh, int nkv, int hd, int max_seq, void *img,
+                               const void *vc, int kv_kind, int nh, int nkv, int hd, int max_seq, void *img,
                                float *part, size_t part_floats, u16 *o_hi, u16 *o_lo, float *o_f32) {
     if (T <= 0) return true;
     const int G = nh / nkv;
     u16 *im = static_cast<u16 *>(img);
-#define LH(HD, KB) launch_hd<HD, KB>(st, G, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, im, part, part_floats, \
+#define LH(HD, KT) launch_hd<HD, KT>(st, G, T, start_pos, slot, q, kc, vc, nh, nkv, max_seq, im, part, part_floats, \
                                      o_hi, o_lo, o_f32)
-    if (hd == 128) return kv_bf16 ? LH(128, true) : LH(128, false);
-    if (hd == 64) return kv_bf16 ? LH(64, true) : LH(64, false);
+#define LHK(HD) (kv_kind == KV_BF16 ? LH(HD, KV_BF16) : kv_kind == KV_F24 ? LH(HD, KV_F24) : LH(HD, KV_F32))
+    if (hd == 128) return LHK(128);
+    if (hd == 64) return LHK(64);
+#undef LHK
 #undef LH
     return false;
 }

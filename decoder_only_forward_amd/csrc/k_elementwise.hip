@@ -3,6 +3,7 @@
 // K/V cache store, silu(gate)*up, and the greedy argmax.
 #include "common.h"
 #include "kernels.h"
+#include "kvcache.h"
 
 // ---- residual + RMSNorm ----------------------------------------------------
 // RMSNorm: a = x / sqrt(mean(x^2) + eps) * g  (Pantheon "Llama Forward Pass",
@@ -249,21 +250,20 @@ void launch_rope_table(hipStream_t st, const int32_t *pos, int T, int hd, double
 // of a head (hd is 16, 64 or 128), moved as float4 words: elements
 // [i, i+4) and [i+hd/2, i+hd/2+4) for halves, [2i, 2i+8) for adjacent pairs
 // (and for v, which is not rotated).
-__device__ __forceinline__ void store4(void *cache, size_t at, int kv_bf16, float4 v) {
-    if (kv_bf16) {
-        *reinterpret_cast<uint2 *>(static_cast<u16 *>(cache) + at) =
-            make_uint2(f32_to_bf16_bits(v.x) | (f32_to_bf16_bits(v.y) << 16),
-                       f32_to_bf16_bits(v.z) | (f32_to_bf16_bits(v.w) << 16));
-    } else {
-        *reinterpret_cast<float4 *>(static_cast<float *>(cache) + at) = v;
-    }
+// Elements col .. col+3 of cache row `row` (rows of hd elements in the cache
+// format kv_kind).
+__device__ __forceinline__ void store4(void *cache, size_t row, int col, int hd, int kv_kind, float4 v) {
+    char *c = static_cast<char *>(cache);
+    if (kv_kind == KV_BF16) kv_store4<KV_BF16, 0>(c + row * kv_row_bytes<KV_BF16>(hd), col, v);
+    else if (kv_kind == KV_F24) f24_store4(c + row * kv_row_bytes<KV_F24>(hd), hd, col, v);
+    else kv_store4<KV_F32, 0>(c + row * kv_row_bytes<KV_F32>(hd), col, v);
 }
 
 __global__ void __launch_bounds__(256) rope_kv_kernel(
     Partials qkv, const float *__restrict__ bq, const float *__restrict__ bk, const float *__restrict__ bv,
     const float2 *__restrict__ tab, const int32_t *__restrict__ pos, const int32_t *__restrict__ slot,
     int nh, int nkv, int hd, int pairing, float *__restrict__ q_out, void *__restrict__ kc,
-    void *__restrict__ vc, int max_seq, int ring, int kv_bf16, int chunk) {
+    void *__restrict__ vc, int max_seq, int ring, int kv_kind, int chunk) {
     const int t = blockIdx.x;
     const int qd = nh * hd, kvd = nkv * hd, half = hd / 2;
     const int npairs = (qd + 2 * kvd) / 2;
@@ -323,21 +323,20 @@ __global__ void __launch_bounds__(256) rope_kv_kernel(
         const int s = ring ? p % max_seq : p;
         void *cache = base == qd ? kc : vc;
         // the layer cache at the position's slot, or row t of a chunk buffer [T][nkv][hd]
-        const size_t dst = chunk ? ((size_t)t * nkv + head) * hd
-                                 : (((size_t)slot[t] * nkv + head) * max_seq + s) * hd;
-        store4(cache, dst + w0 - head * hd, kv_bf16, a);
-        store4(cache, dst + w1 - head * hd, kv_bf16, c);
+        const size_t row = chunk ? (size_t)t * nkv + head : ((size_t)slot[t] * nkv + head) * max_seq + s;
+        store4(cache, row, w0 - head * hd, hd, kv_kind, a);
+        store4(cache, row, w1 - head * hd, hd, kv_kind, c);
     }
 }
 
 void launch_rope_kv(hipStream_t st, int T, Partials qkv, const float *bq, const float *bk,
                     const float *bv, const float2 *tab, const int32_t *pos, const int32_t *slot,
                     int nh, int nkv, int hd, int pairing, float *q_out, void *kc, void *vc, int max_seq,
-                    int ring, int kv_bf16, int chunk) {
+                    int ring, int kv_kind, int chunk) {
     if (T <= 0) return;
     const int nquads = (nh + 2 * nkv) * hd / 8;
     hipLaunchKernelGGL(rope_kv_kernel, dim3(T, (nquads + 255) / 256), dim3(256), 0, st, qkv, bq, bk, bv, tab, pos,
-                       slot, nh, nkv, hd, pairing, q_out, kc, vc, max_seq, ring, kv_bf16, chunk);
+                       slot, nh, nkv, hd, pairing, q_out, kc, vc, max_seq, ring, kv_kind, chunk);
 }
 
 // Commit a chunk's K/V rows [T][nkv][hd] to the ring slots of positions
@@ -359,7 +358,7 @@ __global__ void commit_chunk_kernel(const uint32_t *__restrict__ ck, const uint3
 void launch_commit_chunk(hipStream_t st, const void *ck, const void *cv, int T, int start, int s, int nkv, int hd,
                          int es, int max_seq, void *kc, void *vc) {
     const int first = T > max_seq ? T - max_seq : 0;
-    const int words = hd * es / 4;
+    const int words = hd * es / 4;   // es = 4, 2 or 3 bytes an element: rows of whole words for hd % 16 == 0
     if (T - first <= 0) return;
     hipLaunchKernelGGL(commit_chunk_kernel, dim3(T - first, nkv), dim3(64), 0, st,
                        static_cast<const uint32_t *>(ck), static_cast<const uint32_t *>(cv), T, first, start, s, nkv,

@@ -52,14 +52,14 @@ void launch_rope_table(hipStream_t st, const int32_t *pos, int T, int hd, double
 
 // q/k/v (+bias) -> RoPE on q and k -> q_out [T][q_dim]; k, v stored in the
 // layer's cache [slot][kvh][max_seq][hd] at position pos % max_seq (ring) or pos,
-// or, when chunk is set, in rows [T][nkv][hd] of the buffers kc, vc; as fp32,
-// or as nearest-even bf16 when kv_bf16 is set.
+// or, when chunk is set, in rows [T][nkv][hd] of the buffers kc, vc; in the
+// cache format kv_kind (KV_F32, KV_BF16 or KV_F24 of kvcache.h).
 // pairing 0 rotates elements (2i, 2i+1) of a head, 1 rotates (i, i + hd/2).
 void launch_rope_kv(hipStream_t st, int T, Partials qkv, const float *bq, const float *bk,
                     const float *bv, const float2 *tab, const int32_t *pos, const int32_t *slot,
                     int nh, int nkv, int hd, int pairing, float *q_out, void *kc, void *vc, int max_seq,
-                    int ring, int kv_bf16, int chunk);
-// Store a chunk's rows [T][nkv][hd] (es bytes per element) at the ring slots of
+                    int ring, int kv_kind, int chunk);
+// Store a chunk's rows [T][nkv][hd] (es = 4, 2 or 3 bytes per element) at the ring slots of
 // positions start.. of sequence slot s: the last min(T, max_seq) rows.
 void launch_commit_chunk(hipStream_t st, const void *ck, const void *cv, int T, int start, int s, int nkv, int hd,
                          int es, int max_seq, void *kc, void *vc);
@@ -127,13 +127,13 @@ struct RopeArgs {
 
 // Split-KV decode attention.  Row b (sequence slot slot[b], position pos[b]):
 // q and the new K/V row come from ra (RoPE applied as launch_rope_kv does);
-// the K/V row is stored at the position's slot of the layer cache (fp32, or
-// nearest-even bf16 when kv_bf16 is set) by the block whose split covers it,
+// the K/V row is stored at the position's slot of the layer cache (in the
+// cache format kv_kind) by the block whose split covers it,
 // and the keys/values of the readable slots [0, min(pos+1, max_seq)) are then
 // attended.  Writes the attention output as bf16 (hi, lo) and/or fp32 rows
 // [B][nh*hd].
-int attn_decode_splits(int B, int nkv, int readable, int hd, int G, int kv_bf16);
-void launch_attn_decode(hipStream_t st, int B, const RopeArgs &ra, void *kc, void *vc, int kv_bf16,
+int attn_decode_splits(int B, int nkv, int readable, int hd, int G, int kv_kind);
+void launch_attn_decode(hipStream_t st, int B, const RopeArgs &ra, void *kc, void *vc, int kv_kind,
                         const int32_t *pos, const int32_t *slot, int nh, int nkv, int hd, int max_seq,
                         int splits, float *part, u16 *o_hi, u16 *o_lo, float *o_f32);
 
@@ -144,21 +144,21 @@ void launch_attn_decode(hipStream_t st, int B, const RopeArgs &ra, void *kc, voi
 // come from the cache as well (ck == nullptr: already stored there) or from the
 // chunk buffers ck, cv [T][nkv][hd] (deferred commit).
 void launch_attn_prefill(hipStream_t st, int T, int start_pos, int slot, const float *q,
-                         const void *kc, const void *vc, int kv_bf16, int nh, int nkv, int hd, int max_seq,
+                         const void *kc, const void *vc, int kv_kind, int nh, int nkv, int hd, int max_seq,
                          int window, int ring, const void *ck, const void *cv, u16 *o_hi, u16 *o_lo,
                          float *o_f32);
 
 // The same attention over pre-split K/V tiles (head_dim 64 or 128, every key
 // position at its own slot: start_pos + T <= max_seq).  Each call first writes
 // the tiles of positions [0, start_pos + T) of sequence `slot` into `img`
-// (attn_tiles_bytes(max_seq, nkv, hd, kv_bf16) bytes), then runs the MFMA
+// (attn_tiles_bytes(max_seq, nkv, hd, kv_kind) bytes), then runs the MFMA
 // kernel.  A launch of few row blocks splits their key tiles into chunks whose
 // partial results go to `part` (part_floats floats of scratch, free during the
 // call) and a merge pass; part may be null (no split).  Returns false for an
 // unsupported head_dim or group size (nothing launched).
-size_t attn_tiles_bytes(int max_pos, int nkv, int hd, int kv_bf16);
+size_t attn_tiles_bytes(int max_pos, int nkv, int hd, int kv_kind);
 bool launch_attn_prefill_tiles(hipStream_t st, int T, int start_pos, int slot, const float *q, const void *kc,
-                               const void *vc, int kv_bf16, int nh, int nkv, int hd, int max_seq, void *img,
+                               const void *vc, int kv_kind, int nh, int nkv, int hd, int max_seq, void *img,
                                float *part, size_t part_floats, u16 *o_hi, u16 *o_lo, float *o_f32);
 
 // MoE.  Router logits [T][E] -> softmax, top-k by repeated selection (ties to

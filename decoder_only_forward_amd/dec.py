@@ -19,6 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdec.so")
 
 DEC_OK, DEC_ERR_INVALID, DEC_ERR_RANGE, DEC_ERR_NOMEM, DEC_ERR_DEVICE, DEC_ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+DEC_KV_F32, DEC_KV_BF16, DEC_KV_F24 = 0, 1, 2
 DEC_K_GEMV, DEC_K_ATTN_DECODE, DEC_K_GEMM, DEC_K_ATTN_PREFILL = 0, 1, 2, 3
 DEC_NOALLOC_WORKSPACE_BYTES = 64 << 20
 EXPORTS = ("dec_workspace_bytes", "dec_create", "dec_create_noalloc", "dec_destroy", "dec_prefill", "dec_prefill_ex", "dec_decode",
@@ -107,12 +108,19 @@ def load():
     return L
 
 
+def kv_dtype(cfg: ModelConfig) -> int:
+    """dec_config.kv_dtype of a config: DEC_KV_F32, DEC_KV_BF16 or DEC_KV_F24."""
+    if getattr(cfg, "kv_f24", False):
+        return DEC_KV_F24
+    return DEC_KV_BF16 if cfg.kv_bf16 else DEC_KV_F32
+
+
 def make_config(cfg: ModelConfig, max_batch: int, max_prefill: int, max_seq: Optional[int] = None) -> DecConfig:
     return DecConfig(ctypes.sizeof(DecConfig), cfg.n_layers, cfg.hidden, cfg.n_heads, cfg.n_kv_heads,
                      cfg.head_dim, cfg.ffn_dim, cfg.vocab, cfg.n_experts, cfg.top_k, int(cfg.qkv_bias),
                      int(cfg.tied_embedding), cfg.sliding_window, cfg.max_seq if max_seq is None else max_seq,
                      max_batch, max_prefill, 1 if cfg.weight_dtype == WEIGHT_F32 else 0, cfg.rms_eps,
-                     cfg.rope_theta, cfg.rope_pairing, cfg.rope_scaling, cfg.rope_orig_ctx, int(cfg.kv_bf16),
+                     cfg.rope_theta, cfg.rope_pairing, cfg.rope_scaling, cfg.rope_orig_ctx, kv_dtype(cfg),
                      cfg.rope_factor, cfg.rope_low_freq_factor, cfg.rope_high_freq_factor,
                      int(getattr(cfg, "prefill_fp8", False)))
 

@@ -52,7 +52,7 @@ enum {
 enum { DEC_WEIGHT_BF16 = 0, DEC_WEIGHT_F32 = 1 };
 enum { DEC_ROPE_ADJACENT = 0, DEC_ROPE_HALF = 1 };
 enum { DEC_ROPE_PLAIN = 0, DEC_ROPE_LLAMA3 = 1 };
-enum { DEC_KV_F32 = 0, DEC_KV_BF16 = 1 };
+enum { DEC_KV_F32 = 0, DEC_KV_BF16 = 1, DEC_KV_F24 = 2 };
 enum { DEC_PREFILL_BF16_PAIR = 0, DEC_PREFILL_F16_F8 = 1 };
 
 /*
@@ -103,8 +103,15 @@ typedef struct dec_config {
        as it reads it).  DEC_KV_F32: fp32.  DEC_KV_BF16: each rotated key and
        each value element is rounded to the nearest-even bf16 when stored,
        halving the cache's bytes and its bytes read per decode step; every
-       later read (decode and prefill) sees the rounded value.  Arithmetic
-       stays fp32. */
+       later read (decode and prefill) sees the rounded value.  DEC_KV_F24:
+       each element is rounded to nearest even at 16 significant bits (fp32's
+       sign and exponent, 15 stored mantissa bits) and stored as 3 bytes: a
+       cache row of head_dim elements is head_dim 16-bit words (the upper half
+       of the rounded fp32 word) followed by head_dim bytes (the third bytes,
+       by blocks of 8 elements: block b at byte 16 (b % L) + 8 (b / L) of that
+       part, L = head_dim / 16).
+       Three quarters of the fp32 cache's bytes; readers rebuild the fp32
+       word exactly.  Arithmetic stays fp32. */
     int32_t kv_dtype;
     double rope_factor;
     double rope_low_freq_factor;

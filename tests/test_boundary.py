@@ -52,6 +52,16 @@ def test_bf16_cache_halves_the_kv_bytes():
     assert f32 - b16 == kv + chunk + img
 
 
+def test_f24_cache_takes_three_quarters_of_the_kv_bytes():
+    _lib()
+    f32 = D.workspace_bytes(configs.MISTRAL, max_batch=32, max_prefill=4096)
+    f24 = D.workspace_bytes(configs.MISTRAL.replace(kv_f24=True), max_batch=32, max_prefill=4096)
+    kv = 2 * 32 * 32 * 8 * 4096 * 128 * 1        # K and V of 32 slots, 1 byte saved per element
+    chunk = 2 * 4096 * 8 * 128 * 1                # the ring's deferred-commit chunk K/V
+    assert f32 - f24 == kv + chunk                 # same (hi, lo) tile images as the fp32 cache
+    assert D.kv_dtype(configs.MISTRAL.replace(kv_f24=True)) == D.DEC_KV_F24
+
+
 def _create(cfg, max_batch=2, max_prefill=8, ws=None, ws_bytes=None, layer_field=None, **over):
     L = _lib()
     c = D.make_config(cfg, max_batch, max_prefill)
@@ -87,10 +97,11 @@ def test_create_validation():
     assert _create(configs.TINY, n_experts=2, top_k=3)[0] == D.DEC_ERR_INVALID   # top_k > n_experts
     assert _create(configs.TINY_BF16, ffn_dim=100)[0] == D.DEC_ERR_UNSUPPORTED    # bf16 tiles need 64 | ffn
     assert _create(configs.TINY_WINDOW, max_seq=6)[0] == D.DEC_ERR_INVALID       # ring longer than the window
-    assert _create(configs.TINY, kv_dtype=2)[0] == D.DEC_ERR_INVALID              # no such cache type
-    rc, h, L = _create(configs.TINY_KVBF16)
-    assert rc == D.DEC_OK
-    L.dec_destroy(h)
+    assert _create(configs.TINY, kv_dtype=3)[0] == D.DEC_ERR_INVALID              # no such cache type
+    for cfg in (configs.TINY_KVBF16, configs.TINY_KVF24):
+        rc, h, L = _create(cfg)
+        assert rc == D.DEC_OK
+        L.dec_destroy(h)
     rc, h, L = _create(configs.TINY)
     assert rc == D.DEC_OK
     L.dec_destroy(h)

@@ -4,7 +4,8 @@ and value in its prologue, at slot pos % max_seq of a ring (Pantheon "Llama
 Forward Pass", "Sliding Window (Mistral)") or at pos, and the rows the
 prefills wrote must stay as they were.  Cache layout [layer][slot][kv head]
 [max_seq][head_dim] at the start of the workspace, K then V (256-byte aligned);
-fp32, or nearest-even bf16 bits."""
+fp32, nearest-even bf16 bits, or 24-bit rows (head_dim upper halves, then
+head_dim third bytes in blocks of 8)."""
 import numpy as np
 import pytest
 import torch
@@ -15,14 +16,16 @@ from parity_util import Pair, rel_l2, tol
 pytestmark = pytest.mark.gpu
 
 CASES = [configs.TINY_WINDOW, configs.TINY_WINDOW.replace(name="tiny-window-kvbf16", kv_bf16=True),
-         configs.TINY_BF16, configs.TINY_KVBF16]
+         configs.TINY_WINDOW.replace(name="tiny-window-kvf24", kv_f24=True),
+         configs.TINY_BF16, configs.TINY_KVBF16, configs.TINY_KVF24]
 
 
 def _caches(pair):
     c, g = pair.cfg, pair.gpu
     S, ms = g.ccfg.max_batch, g.ccfg.max_seq
-    es = 2 if c.kv_bf16 else 4
-    n = c.n_layers * S * c.n_kv_heads * ms * c.head_dim
+    es = 2 if c.kv_bf16 else (3 if c.kv_f24 else 4)
+    hd = c.head_dim
+    n = c.n_layers * S * c.n_kv_heads * ms * hd
     kbytes = n * es
     voff = (kbytes + 255) // 256 * 256
     raw = g.workspace[: voff + kbytes].cpu().numpy()
@@ -31,9 +34,17 @@ def _caches(pair):
         b = raw[off: off + kbytes]
         if es == 2:
             a = (np.frombuffer(b.tobytes(), dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+        elif es == 3:
+            rows = np.frombuffer(b.tobytes(), dtype=np.uint8).reshape(-1, 3 * hd)
+            hi = rows[:, : 2 * hd].copy().view(np.uint16).astype(np.uint32)
+            # third bytes by blocks of 8 elements, block j at 16 (j % L) + 8 (j // L), L = hd / 16
+            L = hd // 16
+            e = np.arange(hd)
+            lo = rows[:, 2 * hd + 16 * ((e // 8) % L) + 8 * ((e // 8) // L) + e % 8].astype(np.uint32)
+            a = ((hi << 16) | (lo << 8)).view(np.float32)
         else:
             a = np.frombuffer(b.tobytes(), dtype=np.float32)
-        out.append(a.reshape(c.n_layers, S, c.n_kv_heads, ms, c.head_dim))
+        out.append(a.reshape(c.n_layers, S, c.n_kv_heads, ms, hd))
     return out, ms
 
 

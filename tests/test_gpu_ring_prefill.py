@@ -43,7 +43,8 @@ def _chunks(pair, toks, sizes, what):
 @pytest.mark.parametrize("cfg", [configs.TINY_WINDOW,
                                  configs.TINY_WINDOW.replace(name="tiny-window-bf16w", weight_dtype=0, ffn_dim=192),
                                  configs.TINY_WINDOW.replace(name="tiny-window-moe", n_experts=8, top_k=2),
-                                 configs.TINY_WINDOW.replace(name="tiny-window-kvbf16", kv_bf16=True)],
+                                 configs.TINY_WINDOW.replace(name="tiny-window-kvbf16", kv_bf16=True),
+                                 configs.TINY_WINDOW.replace(name="tiny-window-kvf24", kv_f24=True)],
                          ids=lambda c: c.name)
 def test_tiny_ring_appends_past_the_ring(cfg):
     """W = 5: chunks of 3, 4 (wraps), 9 (longer than the ring), 1, then decode."""
@@ -65,6 +66,15 @@ def test_smollm2_width_ring_at_full_depth():
     pair = Pair(cfg, max_prefill=100)
     toks = synth.tokens(0, synth.PROMPT_STREAM, 200, cfg.vocab).tolist()
     _chunks(pair, toks, [40, 50, 100, 10], "smollm2-w64")
+
+
+def test_smollm2_width_ring_at_full_depth_f24_cache():
+    """The same appends with a 24-bit cache: the general MFMA prefill kernel
+    reads ring slots and chunk rows in that format, the commit copies them."""
+    cfg = configs.SMOLLM2.replace(name="smollm2-w64-kvf24", sliding_window=64, max_seq=64, kv_f24=True)
+    pair = Pair(cfg, max_prefill=100)
+    toks = synth.tokens(0, synth.PROMPT_STREAM, 200, cfg.vocab).tolist()
+    _chunks(pair, toks, [40, 50, 100, 10], "smollm2-w64-kvf24")
 
 
 def _mistral_ring(P0, n, sample, kv_bf16=False):
