@@ -44,7 +44,9 @@ HBM_PEAK_GBS = 8000.0
 _COMMON = {"decoder_only_forward_amd/csrc/common.h":
            "35cda32506ca4602aa9641fb45aba06fa60805f124e93a385f7219774610dd86"}
 _ATTN_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_decode.hip":
-                                 "cae52ed058060b38e445bdb8323692f2f7481e38ec54819afc64a7fc8f14e507"})
+                                 "d6ccf7fc8e96ff4a9eb77b3d993a96be23e9ec6eb1360fe1e0c727cc01120a2c",
+                                 "decoder_only_forward_amd/csrc/kvcache.h":
+                                 "b917a66e4ecfcb8f83f86f04cd3aed72acacdc8f768e657cc443a9cc9aa212b4"})
 _GEMV_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemv.hip":
                                  "11f73b184e2f0a6eac6252819b3d4309b847dfd1a45ddedad296e73af96448c6"})
 _GEMM_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemm.hip":
@@ -52,12 +54,14 @@ _GEMM_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemm.hip":
 _TILES_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_prefill_tiles.hip":
                                   "a057f7f417eda3f60000afda30eb547ff3158668784e1a69e880429eb018a86f"})
 MEASURED_TRAFFIC = {
-    # B = 32 launches: the lane-group kernel (fp32 cache), the MFMA kernel in
-    # 8-wave blocks (bf16 cache)
+    # B = 32 launches: the lane-group kernel (fp32 cache; the 24-bit cache in
+    # 8-wave blocks), the MFMA kernel in 8-wave blocks (bf16 cache)
     ("attn_decode_kernel", "fp32"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 1078824772},
+                                     "bytes_per_launch": 1078642260},
     ("attn_decode_mfma_kernel", "bf16"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                          "bytes_per_launch": 541894295},
+                                          "bytes_per_launch": 541775006},
+    ("attn_decode_kernel", "f24"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
+                                    "bytes_per_launch": 810146246},
     ("gemv_decode", "fp32"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
                               "bytes_per_launch": 121774326},
     ("gemv_decode", "bf16"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
