@@ -379,15 +379,22 @@ __global__ void __launch_bounds__(NWV * 64, 8 / NWV) attn_decode_kernel(
         }
     };
     if constexpr (PIPE) {
+        // Pairs of stages; each stage's successor is loaded unconditionally (a
+        // stage past the last reads the range's first row and is never used),
+        // so every path into a stage has the same loads in flight and its wait
+        // covers its own loads only.  (A conditional load, or a path from a
+        // mid-pair exit back to the loop head, makes the compiler's waits also
+        // cover the stage just issued, which undoes the pipelining.)
         u32x4 kA[NS][NW], vA[NS][NW], kB[NS][NW], vB[NS][NW];
         if (nstg > 0) load(kA, vA, 0);
-        for (int st = 0; st < nstg; st += 2) {
-            if (st + 1 < nstg) load(kB, vB, st + 1);
-            step(kA, vA, st);
-            if (st + 1 >= nstg) break;
-            if (st + 2 < nstg) load(kA, vA, st + 2);
-            step(kB, vB, st + 1);
+        const int npair = nstg >> 1;
+        for (int it = 0; it < npair; it++) {
+            load(kB, vB, 2 * it + 1);
+            step(kA, vA, 2 * it);
+            load(kA, vA, 2 * it + 2);
+            step(kB, vB, 2 * it + 1);
         }
+        if (nstg & 1) step(kA, vA, nstg - 1);
     } else {
         for (int st = 0; st < nstg; st++) {
             u32x4 kr[NS][NW], vr[NS][NW];
