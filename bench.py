@@ -340,6 +340,35 @@ def run_prefill_only(cfg, wd, P, calls=3):
     model.close()
 
 
+def run_prefill_variant(cfg, wd, P, calls=5):
+    """Prefill calls of P tokens into one slot (the first call discarded): the
+    median call time and the GEMM launches' timing."""
+    import numpy as np
+    import torch
+    from decoder_only_forward_amd import synth
+    from decoder_only_forward_amd import dec as D
+    model = D.DecModel(cfg, wd, max_batch=1, max_prefill=P)
+    prompt = synth.prompts(cfg, 1, P)[0].tolist()
+    logits = torch.empty(cfg.vocab, device="cuda")
+    ms = []
+    for i in range(calls):
+        model.reset()
+        if i == 1:
+            model.timing_enable(D.DEC_K_GEMM)
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        model.prefill(prompt, logits=logits)
+        torch.cuda.synchronize()
+        ms.append((time.perf_counter() - t) * 1e3)
+    gemm_t = model.timing_read(D.DEC_K_GEMM)
+    model.close()
+    del model
+    torch.cuda.empty_cache()
+    med = float(np.median(ms[1:]))
+    log(f"[{cfg.name}] prefill P={P}: {med:.1f} ms median of {calls - 1}")
+    return {"ms": med, "gemm": gemm_t}
+
+
 def run_workload(cfg, wd, B, P, steps, warmup, small_batches=()):
     """Prefill P tokens into each of B slots, then time batched greedy decode."""
     import numpy as np
@@ -650,6 +679,22 @@ def main():
             "roofline": attn_roof(f24_run["attn"], "f24"),
             "roofline_kernels": {"gemv_decode": roof(f24_run["gemv"], "hbm", ("gemv_decode", "f24")),
                                  "attn_prefill": roof(f24_run["apre"], "mfma", passes=3)},
+        }
+    if args.kv == "all" and not args.only and not cfg.prefill_fp8:
+        # the same prefill with the q|k|v and gate|up projections on fp16 + fp8
+        # split operands (opt-in DEC_PREFILL_F16_F8), next to the bf16 pair's
+        # prefill on the same model slot
+        pv = run_prefill_variant(cfg.replace(name=cfg.name + "-prefill-f16f8", prefill_fp8=True), wd, P)
+        pb = run_prefill_variant(cfg, wd, P)
+        out["prefill_f16f8"] = {
+            "note": ("prefill with q|k|v and gate|up as an fp16 pass plus a scaled fp8 pass (the weights' "
+                     "upper bytes as e5m2 against the activation's fp8 remainder), o and down on the bf16 "
+                     "pair; parity-tested at the fp32 path's tolerances; one slot, median of 4 calls, with "
+                     "the bf16 pair timed the same way beside it"),
+            "prefill_ms": round(pv["ms"], 2), "prefill_tok_s": round(P / (pv["ms"] * 1e-3), 1),
+            "bf16_pair_prefill_ms": round(pb["ms"], 2),
+            "gemm_prefill": roof(pv["gemm"], "mfma"),
+            "gemm_prefill_bf16_pair": roof(pb["gemm"], "mfma"),
         }
     if not args.no_cpu_baseline and not args.only:
         try:

@@ -75,13 +75,8 @@ __device__ __forceinline__ uint32_t fp8x4(float a, float b, float c, float d, ui
 }
 
 // Position of row r's scale within its 256-row group, in the order the fp16 +
-// fp8 GEMM's lanes read them.  Weight rows: wave half wn = q / 128, row tile
-// i = (q / 32) % 4, lane row q % 32 -> 128 wn + 4 (q % 32) + i.  Token rows:
-// wave row group wm = q / 64, row tile j = (q / 32) % 2 -> 64 wm + 2 (q % 32) + j.
-__host__ __device__ __forceinline__ int f8_wsc_pos(int r) {
-    const int q = r & 255;
-    return (r & ~255) | (q & 128) | ((q & 31) << 2) | ((q >> 5) & 3);
-}
+// fp8 GEMM's lanes read them: wave row group wm = q / 64, row tile
+// j = (q / 32) % 2 -> 64 wm + 2 (q % 32) + j.
 __host__ __device__ __forceinline__ int f8_asc_pos(int r) {
     const int q = r & 255;
     return (r & ~255) | (q & 192) | ((q & 31) << 1) | ((q >> 5) & 1);

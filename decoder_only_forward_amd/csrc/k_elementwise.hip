@@ -93,7 +93,11 @@ __global__ void __launch_bounds__(NTH) residual_norm_kernel(
             const uint32_t sb = mx_scale_byte(mx);
             const size_t fo = (size_t)t * f8.lda + 4 * i4;
             *reinterpret_cast<uint2 *>(f8.a16 + fo) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-            *reinterpret_cast<uint32_t *>(f8.a8 + fo) = fp8x4(l0, l1, l2, l3, sb);
+            // the fp8 row's 32-k blocks hold k 0-7, 16-23, 8-15, 24-31 (the order
+            // the GEMM's lanes take the weights' bytes from their fp16 fragments)
+            const int q = i4 & 7, qs = (q == 2 || q == 3) ? q + 2 : ((q == 4 || q == 5) ? q - 2 : q);
+            *reinterpret_cast<uint32_t *>(f8.a8 + (size_t)t * f8.lda + 4 * ((i4 & ~7) | qs)) =
+                fp8x4(l0, l1, l2, l3, sb);
             if ((threadIdx.x & 7) == 0) f8.asc[(size_t)(i4 >> 3) * f8.mpad + f8_asc_pos(t)] = (uint8_t)sb;
         } else if (a_hi) {
             uint2 h, l;

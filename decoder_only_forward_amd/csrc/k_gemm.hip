@@ -714,31 +714,39 @@ bool launch_gemm_grouped_silu(hipStream_t st, const void *w_gate, const void *w_
 
 // ---- prefill projections on fp16 + fp8 operands -----------------------------
 // y = W a with a = a16 + lo (the split of f16_split) and W exact in fp16: the
-// hi pass multiplies W16 by a16 on fp16 MFMAs (32x32x16), the lo pass an fp8
-// copy of W by the fp8 lo, each with an E8M0 scale per 32 k of a row, on the
-// scaled fp8 MFMA (32x32x64), which runs at twice the bf16 rate.  Since
-// |lo| <= 2^-11 |a16|, e4m3's rounding of either lo operand costs about
-// 2^-15 of a product; the two passes cost 1.5 bf16-MFMA units per product
-// against 2 for gemm_dma_kernel's bf16 (hi, lo) pair.
+// hi pass multiplies W16 by a16 on fp16 MFMAs (32x32x16), the lo pass W8 by
+// the fp8 lo (e4m3 with an E8M0 scale per 32 k of a row) on the scaled fp8
+// MFMA (32x32x64), which runs at twice the bf16 rate.  W8 is no copy: it is
+// the upper byte of each fp16 weight, which read as e5m2 is the weight
+// truncated to 2 mantissa bits; the lanes take those bytes from the W16
+// fragments of the hi pass.  Since |lo| <= 2^-11 |a16|, the truncation and
+// e4m3's rounding of lo cost about 2^-14 of a product (a CPU emulation of one
+// K = 4096 projection: 2.1e-5 rel L2, against 2.5e-6 for the bf16 pair and
+// 2.1e-4 for fp16 alone); the two passes cost 1.5 bf16-MFMA units per
+// product against 2 for gemm_dma_kernel's bf16 (hi, lo) pair, and each k-tile
+// moves 40 KB into LDS instead of 48.
 //
-// Operands (bytes): W16 [npad][K] fp16, W8 [npad][K] e4m3, wsc [K/32][npad];
-// A16 [M][lda] fp16, A8 [M][lda] e4m3, asc [K/32][mpad] (mpad = M rounded up
-// to 256).  Within each 256 rows the scales are stored in the order the
-// lanes take them (f8_wsc_pos, f8_asc_pos): a lane's 4 weight row tiles (i)
-// and 2 token row tiles (j) give one 32-bit and one 16-bit word, byte i or j
-// being the scale the MFMA's selector picks.  Weight rows are stored in the kernel's tile order (the converter
-// writes them so): tile tn holds rows [256 tn, 256 tn + 256).  A SILU tile's
-// row r is wave half r / 128, MFMA row tile (r % 128) / 32 (0, 1 gate; 2, 3 up),
-// i.e. gate or up feature 128 tn + 64 (r / 128) + 32 ((r / 32) & 1) + r % 32.
+// Operands (bytes): W16 [npad][K] fp16; A16 [M][lda] fp16, A8 [M][lda] e4m3,
+// asc [K/32][mpad] (mpad = M rounded up to 256).  Within each 256 rows the
+// scales are stored in the order the lanes take them (f8_asc_pos): a lane's 2
+// token row tiles (j) give one 16-bit word, byte j being the scale the MFMA's
+// selector picks.  An A8 row's 32-k blocks hold k 0-7, 16-23, 8-15, 24-31:
+// lane half c2 of a 32x32x16 fp16 fragment holds k 8c2 .. 8c2+7 of each
+// 16-k step, so its weight bytes of a k-tile are k {8c2.., 16+8c2..}, which
+// the fp8 MFMA pairs with bytes [16 c2, 16 c2 + 16) of the A8 row.  Weight
+// rows are stored in the kernel's tile order (the converter writes them so):
+// tile tn holds rows [256 tn, 256 tn + 256).  A SILU tile's row r is wave half
+// r / 128, MFMA row tile (r % 128) / 32 (0, 1 gate; 2, 3 up), i.e. gate or up
+// feature 128 tn + 64 (r / 128) + 32 ((r / 32) & 1) + r % 32.
 //
 // Stage = one 32-k tile: W16 and A16 as in gemm_dma_kernel (64-byte rows,
-// swizzled chunks), W8 and A8 (32-byte rows, halves swizzled), the 256
-// weight-row and 256 token-row scales of the tile's k block.  The fp8 MFMA takes 64 k: lane l
-// (row l % 32, half c2 = l / 32) supplies bytes [16 c2, 16 c2 + 16) of its row
-// from the even k-tile and the same bytes from the odd one that follows, and
-// the scale of its row's even (lanes < 32) or odd (lanes >= 32) k block.  The
-// even tile's fragments and scales are kept in registers until the odd tile
-// (the ring refills the even tile's stage while the odd one is multiplied).
+// swizzled chunks), A8 (32-byte rows, halves swizzled), the 256 token-row
+// scales of the tile's k block.  The fp8 MFMA takes 64 k: lane l (row l % 32,
+// half c2 = l / 32) supplies its 16 bytes of its row from the even k-tile and
+// the same bytes from the odd one that follows, and the scale of its row's
+// even (lanes < 32) or odd (lanes >= 32) k block.  The even tile's fragments
+// and scales are kept in registers until the odd tile (the ring refills the
+// even tile's stage while the odd one is multiplied).
 namespace {
 
 // 16-byte half h of fp8 row r sits at half h ^ f(r) of the row in LDS, so the
@@ -747,7 +755,6 @@ __device__ __forceinline__ int f8_half(int r, int h) { return h ^ (((r >> 2) ^ (
 
 struct GemmF8Params {
     const u16 *w16;
-    const uint8_t *w8, *wsc;
     const u16 *a16;
     const uint8_t *a8, *asc;
     int N, K, M, npad, mpad, lda;
@@ -758,8 +765,8 @@ struct GemmF8Params {
 };
 
 // stage layout, in u16
-constexpr int F8_W16 = 0, F8_A16 = 8192, F8_W8 = 16384, F8_A8 = 20480, F8_WSC = 24576, F8_ASC = 24704;
-constexpr int F8_STG = 24832;
+constexpr int F8_W16 = 0, F8_A16 = 8192, F8_A8 = 16384, F8_ASC = 20480;
+constexpr int F8_STG = 20608;
 constexpr size_t F8_LDS = (size_t)DNSTAGE * F8_STG * sizeof(u16);
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
@@ -795,9 +802,9 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_f8_kernel(GemmF8Params p) {
     const int nk = min(p.kchunk, p.K - kz0) / DBK;   // even
 
     // load i (0, 1) of W16 / A16: row (i*8 + wv)*16 + lane/4, logical chunk
-    // (lane & 3) ^ ((row >> 2) & 3); W8 / A8: row wv*32 + lane/2, logical half
-    // f8_half(row, lane & 1); scales: lanes 0-15 of wave 0 the 256 weight-row
-    // bytes, of wave 1 the 256 token-row bytes (the other waves load none)
+    // (lane & 3) ^ ((row >> 2) & 3); A8: row wv*32 + lane/2, logical half
+    // f8_half(row, lane & 1); scales: lanes 0-15 of wave 0 the 256 token-row
+    // bytes (the other waves load none)
     const u16 *srcw[2], *srca[2];
 #pragma unroll
     for (int i = 0; i < 2; i++) {
@@ -808,11 +815,8 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_f8_kernel(GemmF8Params p) {
         srca[i] = p.a16 + (size_t)m * p.lda + kz0 + c * 8;
     }
     const int r8 = (wv * 64 + lane) >> 1, c8 = f8_half(r8, lane & 1);
-    const uint8_t *srcw8 = p.w8 + (size_t)(r0 + r8) * p.K + kz0 + c8 * 16;
     const uint8_t *srca8 = p.a8 + (size_t)min(m0 + r8, M - 1) * p.lda + kz0 + c8 * 16;
-    const uint8_t *srcsc = wv == 0 ? p.wsc + r0 + lane * 16 : p.asc + m0 + lane * 16;
-    const size_t scp = wv == 0 ? (size_t)p.npad : (size_t)p.mpad;
-    const int scdst = wv == 0 ? F8_WSC : F8_ASC;
+    const uint8_t *srcsc = p.asc + m0 + lane * 16;
     const int kb0 = kz0 / DBK;
 
     auto load_tile = [&](int kt, int stage, auto na_c, auto sc_c) {
@@ -829,13 +833,11 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_f8_kernel(GemmF8Params p) {
         for (int i = 0; i < NA; i++)
             __builtin_amdgcn_global_load_lds((const void *)(srca[i] + k0),
                                              (LDS_AS void *)(base + F8_A16 + (i * 8 + wv) * 512), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void *)(srcw8 + k0), (LDS_AS void *)(base + F8_W8 + wv * 512), 16,
-                                         0, 0);
         __builtin_amdgcn_global_load_lds((const void *)(srca8 + k0), (LDS_AS void *)(base + F8_A8 + wv * 512), 16,
                                          0, 0);
         if (SC && lane < 16)
-            __builtin_amdgcn_global_load_lds((const void *)(srcsc + (size_t)(kb0 + t) * scp),
-                                             (LDS_AS void *)(base + scdst), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void *)(srcsc + (size_t)(kb0 + t) * p.mpad),
+                                             (LDS_AS void *)(base + F8_ASC), 16, 0, 0);
     };
 
     floatx16 acc[4][2];
@@ -848,7 +850,11 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_f8_kernel(GemmF8Params p) {
 
     const int r32 = lane & 31, c2 = lane >> 5;
     // hi pass of one k-tile: fp16 MFMAs as gemm_dma_kernel's bf16 ones
-    auto hi_pass = [&](int s) {
+    // w8 gets the upper byte of each W16 fragment element: for the fp8 pass
+    // the weight is that byte read as e5m2 (fp16 truncated to 2 mantissa
+    // bits), lane half c2 of a tile holding k 8c2 .. 8c2+7 and 16+8c2 ..
+    // 16+8c2+7 in its 16 bytes (the A8 rows are stored in that k order)
+    auto hi_pass = [&](int s, u32x4 (&w8)[4]) {
         const u16 *sw = smem + s * F8_STG + F8_W16;
         const u16 *sa = smem + s * F8_STG + F8_A16;
 #pragma unroll
@@ -863,6 +869,12 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_f8_kernel(GemmF8Params p) {
                 fa[j] = __builtin_bit_cast(f16x8, *reinterpret_cast<const u32x4 *>(
                                                       sa + 8 * dswz(wm * 64 + j * 32 + r32, 2 * ks + c2)));
 #pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const u32x4 b = __builtin_bit_cast(u32x4, fw[i]);
+                w8[i][2 * ks] = __builtin_amdgcn_perm(b[1], b[0], 0x07050301u);
+                w8[i][2 * ks + 1] = __builtin_amdgcn_perm(b[3], b[2], 0x07050301u);
+            }
+#pragma unroll
             for (int i = 0; i < 4; i++)
 #pragma unroll
                 for (int j = 0; j < 2; j++)
@@ -871,32 +883,26 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_f8_kernel(GemmF8Params p) {
     };
     // the fp8 fragments of stage s (bytes [16 c2, 16 c2 + 16) of each row) and
     // its scales, packed one byte per row tile (weights: byte i, tokens: byte j)
-    auto lo_frags = [&](int s, u32x4 (&w8)[4], u32x4 (&a8)[2], uint32_t &ws, uint32_t &as) {
+    auto lo_frags = [&](int s, u32x4 (&a8)[2], uint32_t &as) {
         const uint8_t *sb = reinterpret_cast<const uint8_t *>(smem + s * F8_STG);
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const int row = wn * 128 + i * 32 + r32;
-            w8[i] = *reinterpret_cast<const u32x4 *>(sb + 2 * F8_W8 + row * 32 + f8_half(row, c2) * 16);
-        }
 #pragma unroll
         for (int j = 0; j < 2; j++) {
             const int row = wm * 64 + j * 32 + r32;
             a8[j] = *reinterpret_cast<const u32x4 *>(sb + 2 * F8_A8 + row * 32 + f8_half(row, c2) * 16);
         }
-        // the scales of the lane's 4 weight / 2 token row tiles, one word each
-        ws = *reinterpret_cast<const uint32_t *>(sb + 2 * F8_WSC + wn * 128 + r32 * 4);
+        // the scales of the lane's 2 token row tiles
         as = *reinterpret_cast<const uint16_t *>(sb + 2 * F8_ASC + wm * 64 + r32 * 2);
     };
 
-    // per k-tile and wave: 2 W16 + NA A16 + W8 + A8 (+ the scales on waves 0,
-    // 1) = 4 + NA (+ 1) loads; the wait leaves the newest tile's in flight (see
+    // per k-tile and wave: 2 W16 + NA A16 + A8 (+ the scales on wave 0) =
+    // 3 + NA (+ 1) loads; the wait leaves the newest tile's in flight (see
     // gemm_dma_kernel), and the loop is instantiated per count.  The
     // loop takes k-tiles in pairs (nk is even): the even tile's fp8 fragments
     // and scales stay in registers, since the odd iteration's load refills the
     // even tile's stage.
     auto ring = [&](auto na_c, auto sc_c) {
         constexpr int NA = decltype(na_c)::value;
-        constexpr int WAIT = (4 + NA + decltype(sc_c)::value) | (7 << 4) | (0 << 8);
+        constexpr int WAIT = (3 + NA + decltype(sc_c)::value) | (7 << 4) | (0 << 8);
         load_tile(0, 0, na_c, sc_c);
         load_tile(1, 1, na_c, sc_c);
         __builtin_amdgcn_s_waitcnt(WAIT);
@@ -905,18 +911,19 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_f8_kernel(GemmF8Params p) {
             const int se = kt % DNSTAGE, so = (kt + 1) % DNSTAGE;
             load_tile(kt + 2, (kt + 2) % DNSTAGE, na_c, sc_c);
             u32x4 w8e[4], a8e[2];
-            uint32_t wse, ase;
-            lo_frags(se, w8e, a8e, wse, ase);
-            hi_pass(se);
+            uint32_t ase;
+            lo_frags(se, a8e, ase);
+            hi_pass(se, w8e);
             __builtin_amdgcn_s_waitcnt(WAIT);
             __builtin_amdgcn_s_barrier();
             load_tile(kt + 3, (kt + 3) % DNSTAGE, na_c, sc_c);
             u32x4 w8o[4], a8o[2];
-            uint32_t wso, aso;
-            lo_frags(so, w8o, a8o, wso, aso);
-            // lanes < 32 give the even k block's scales, lanes >= 32 the odd one's
-            const int wsc = (int)(c2 ? wso : wse), asc = (int)(c2 ? aso : ase);
-            hi_pass(so);
+            uint32_t aso;
+            lo_frags(so, a8o, aso);
+            // lanes < 32 give the even k block's scales, lanes >= 32 the odd one's;
+            // the weights' bytes take scale 2^0
+            const int asc = (int)(c2 ? aso : ase);
+            hi_pass(so, w8o);
             i32x8 wop[4], aop[2];
 #pragma unroll
             for (int i = 0; i < 4; i++)
@@ -928,7 +935,7 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_f8_kernel(GemmF8Params p) {
                                (int)a8o[j][0], (int)a8o[j][1], (int)a8o[j][2], (int)a8o[j][3]};
             // (the scale byte selectors are immediates)
 #define F8MMA(I, J) \
-    acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop[I], aop[J], acc[I][J], 0, 0, I, wsc, J, asc)
+    acc[I][J] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wop[I], aop[J], acc[I][J], 1, 0, 0, 0x7F7F7F7F, J, asc)
             F8MMA(0, 0); F8MMA(0, 1); F8MMA(1, 0); F8MMA(1, 1);
             F8MMA(2, 0); F8MMA(2, 1); F8MMA(3, 0); F8MMA(3, 1);
 #undef F8MMA
@@ -941,7 +948,7 @@ __global__ void __launch_bounds__(DNTHR, 1) gemm_f8_kernel(GemmF8Params p) {
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    if (wv < 2) {
+    if (wv == 0) {
         if (na == 2) ring(I2{}, I1{});
         else if (na == 1) ring(I1{}, I1{});
         else ring(I0{}, I1{});
@@ -1020,12 +1027,11 @@ bool f8_lds_attr() {
 }
 
 // Converted weights: row R of the output (kernel tile order), k block kb of
-// 32: W16 = fp16(W), W8 = e4m3(W / 2^e) with the block's E8M0 scale at
-// wsc[kb * npad + f8_wsc_pos(R)]; rows past the matrix are zero.
+// 32: W16 = fp16(W) (exact for bf16 values in fp16's normal range); rows past
+// the matrix are zero.
 __global__ void __launch_bounds__(256) convert_f8_kernel(const u16 *__restrict__ s0, const u16 *__restrict__ s1,
                                                           const u16 *__restrict__ s2, int e0, int e1, int N, int K,
-                                                          int silu_f, int npad, u16 *__restrict__ w16,
-                                                          uint8_t *__restrict__ w8, uint8_t *__restrict__ wsc) {
+                                                          int silu_f, int npad, u16 *__restrict__ w16) {
     const int nb = K / 32;
     const long idx = blockIdx.x * (long)blockDim.x + threadIdx.x;
     if (idx >= (long)npad * nb) return;
@@ -1038,42 +1044,18 @@ __global__ void __launch_bounds__(256) convert_f8_kernel(const u16 *__restrict__
     } else if (R < N) {
         src = R < e0 ? s0 + (size_t)R * K : (R < e1 ? s1 + (size_t)(R - e0) * K : s2 + (size_t)(R - e1) * K);
     }
-    float v[32];
-    float mx = 0.f;
-#pragma unroll
-    for (int q = 0; q < 4; q++) {
-        u32x4 b = src ? *reinterpret_cast<const u32x4 *>(src + kb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            v[q * 8 + 2 * e] = bf16_bits_to_f32(b[e] & 0xFFFFu);
-            v[q * 8 + 2 * e + 1] = __uint_as_float(b[e] & 0xFFFF0000u);
-        }
-    }
     u16 *dst16 = w16 + (size_t)R * K + kb * 32;
 #pragma unroll
     for (int q = 0; q < 4; q++) {
+        const u32x4 b = src ? *reinterpret_cast<const u32x4 *>(src + kb * 32 + q * 8) : u32x4{0u, 0u, 0u, 0u};
         u32x4 h;
 #pragma unroll
         for (int e = 0; e < 4; e++) {
             float lo0, lo1;
-            h[e] = f16_split(v[q * 8 + 2 * e], lo0) | (f16_split(v[q * 8 + 2 * e + 1], lo1) << 16);
+            h[e] = f16_split(bf16_bits_to_f32(b[e] & 0xFFFFu), lo0) |
+                   (f16_split(__uint_as_float(b[e] & 0xFFFF0000u), lo1) << 16);
         }
         *reinterpret_cast<u32x4 *>(dst16 + q * 8) = h;
-    }
-#pragma unroll
-    for (int i = 0; i < 32; i++) mx = fmaxf(mx, fabsf(v[i]));
-    const uint32_t sb = mx_scale_byte(mx);
-    wsc[(size_t)kb * npad + f8_wsc_pos(R)] = (uint8_t)sb;
-    uint8_t *dst8 = w8 + (size_t)R * K + kb * 32;
-#pragma unroll
-    for (int q = 0; q < 2; q++) {
-        u32x4 o;
-#pragma unroll
-        for (int e = 0; e < 4; e++) {
-            const int b = q * 16 + e * 4;
-            o[e] = fp8x4(v[b], v[b + 1], v[b + 2], v[b + 3], sb);
-        }
-        *reinterpret_cast<u32x4 *>(dst8 + q * 16) = o;
     }
 }
 
@@ -1085,8 +1067,7 @@ int f8_npad(int N, bool silu) { return silu ? ((N + 127) / 128) * 256 : ((N + 25
 
 size_t f8_weight_bytes(int N, int K, bool silu) {
     const size_t np = (size_t)f8_npad(N, silu);
-    auto al = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    return al(np * K * 2) + al(np * K) + al(np * (K / 32));
+    return (np * K * 2 + 255) & ~(size_t)255;
 }
 
 F8Weights f8_weights_at(void *base, int N, int K, bool silu) {
@@ -1095,8 +1076,6 @@ F8Weights f8_weights_at(void *base, int N, int K, bool silu) {
     char *b = (char *)base;
     F8Weights w;
     w.w16 = (const u16 *)b;
-    w.w8 = (const uint8_t *)(b + al(np * K * 2));
-    w.wsc = (const uint8_t *)(b + al(np * K * 2) + al(np * K));
     w.N = N;
     w.K = K;
     w.npad = (int)np;
@@ -1117,8 +1096,7 @@ void launch_convert_f8(hipStream_t st, const WSeg *segs, int nseg, int K, bool s
     if (nseg < 3) e1 = end;
     const long n = (long)w.npad * (K / 32);
     hipLaunchKernelGGL(convert_f8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, s[0], s[1], s[2], e0,
-                       e1, silu ? 0 : end, K, silu ? w.N : 0, w.npad, (u16 *)w.w16, (uint8_t *)w.w8,
-                       (uint8_t *)w.wsc);
+                       e1, silu ? 0 : end, K, silu ? w.N : 0, w.npad, (u16 *)w.w16);
 }
 
 bool launch_gemm_f8(hipStream_t st, const F8Weights &w, const u16 *a16, const uint8_t *a8, const uint8_t *asc,
@@ -1127,7 +1105,7 @@ bool launch_gemm_f8(hipStream_t st, const F8Weights &w, const u16 *a16, const ui
     if (w.silu || w.K % 64 || !f8_lds_attr()) return false;
     if (ksplit < 1 || w.K % (ksplit * 64)) ksplit = 1;
     GemmF8Params p{};
-    p.w16 = w.w16; p.w8 = w.w8; p.wsc = w.wsc;
+    p.w16 = w.w16;
     p.a16 = a16; p.a8 = a8; p.asc = asc;
     p.N = w.N; p.K = w.K; p.M = M; p.npad = w.npad; p.mpad = mpad; p.lda = lda;
     p.out = out; p.ldo = ldo; p.kchunk = w.K / ksplit; p.split_stride = ksplit > 1 ? split_stride : 0;
@@ -1141,7 +1119,7 @@ bool launch_gemm_f8_silu(hipStream_t st, const F8Weights &w, const u16 *a16, con
     if (M <= 0) return true;
     if (!w.silu || w.K % 64 || !f8_lds_attr()) return false;
     GemmF8Params p{};
-    p.w16 = w.w16; p.w8 = w.w8; p.wsc = w.wsc;
+    p.w16 = w.w16;
     p.a16 = a16; p.a8 = a8; p.asc = asc;
     p.N = w.N; p.K = w.K; p.M = M; p.npad = w.npad; p.mpad = mpad; p.lda = lda;
     p.kchunk = w.K; p.s_hi = s_hi; p.s_lo = s_lo; p.ldo = ldo;

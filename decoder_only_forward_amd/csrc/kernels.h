@@ -200,12 +200,11 @@ bool launch_gemm_grouped_silu(hipStream_t st, const void *w_gate, const void *w_
                               size_t expert_stride, u16 *s_hi, u16 *s_lo, int ldo);
 
 // ---- prefill projections on fp16 + fp8 operands (k_gemm.hip) ---------------
-// A weight matrix converted once: W16 [npad][K] fp16, W8 [npad][K] fp8 e4m3
-// and E8M0 scales [K/32][npad], rows in the GEMM's tile order (SILU: gate and
-// up rows interleaved per tile).  K a multiple of 64.
+// A weight matrix converted once: W16 [npad][K] fp16, rows in the GEMM's tile
+// order (SILU: gate and up rows interleaved per tile); the fp8 pass reads each
+// weight's upper byte as e5m2.  K a multiple of 64.
 struct F8Weights {
     const u16 *w16;
-    const uint8_t *w8, *wsc;
     int N, K, npad;
     bool silu;
 };

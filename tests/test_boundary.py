@@ -177,10 +177,9 @@ def test_create_noalloc_checks_before_the_device():
 def _f8_matrix_bytes(N, K, silu):
     """Workspace bytes of one matrix converted for fp16 + fp8 prefill operands:
     rows padded to 256-row tiles (a gate|up tile holds 128 features of each),
-    fp16 copy, fp8 copy and one scale byte per 32 k, each part 256-aligned."""
+    the fp16 copy, 256-aligned (the fp8 pass reads its upper bytes)."""
     npad = ((N + 127) // 128) * 256 if silu else ((N + 255) // 256) * 256
-    al = lambda x: (x + 255) // 256 * 256
-    return al(npad * K * 2) + al(npad * K) + al(npad * (K // 32))
+    return (npad * K * 2 + 255) // 256 * 256
 
 
 def test_fp16_fp8_prefill_operands_workspace_and_validation():
