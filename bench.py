@@ -42,34 +42,38 @@ HBM_PEAK_GBS = 8000.0
 # to the ones profiled, and only for the profiled workload.  GEMV and GEMM
 # figures are the mean over the launches of one step's mix of projections.
 _COMMON = {"decoder_only_forward_amd/csrc/common.h":
-           "35cda32506ca4602aa9641fb45aba06fa60805f124e93a385f7219774610dd86"}
+           "a08d4f553fd07b7970e5b481899ba0e771341cb515b05933bd0498a71b7869c7"}
 _ATTN_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_decode.hip":
-                                 "d6ccf7fc8e96ff4a9eb77b3d993a96be23e9ec6eb1360fe1e0c727cc01120a2c",
+                                 "c1374de5317ec7f7de41b536a73140d901edab53f93c66558c2820bf7b86dd4c",
                                  "decoder_only_forward_amd/csrc/kvcache.h":
                                  "b917a66e4ecfcb8f83f86f04cd3aed72acacdc8f768e657cc443a9cc9aa212b4"})
 _GEMV_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemv.hip":
                                  "11f73b184e2f0a6eac6252819b3d4309b847dfd1a45ddedad296e73af96448c6"})
 _GEMM_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemm.hip":
-                                 "b6c93d8627347338ad306419c21f9804b100e108ec26529608633522f9a87189"})
+                                 "35831c13a16babcb3c1ade248842e44497a91aad2bb89f9ccf4e9ddf241b8c66"})
 _TILES_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_prefill_tiles.hip":
-                                  "a057f7f417eda3f60000afda30eb547ff3158668784e1a69e880429eb018a86f"})
+                                  "27be5b4fc493def0a3d08cbf2e9adc0dfb8cf0482bfed8deadcb94b669819d12",
+                                  "decoder_only_forward_amd/csrc/kvcache.h":
+                                  "b917a66e4ecfcb8f83f86f04cd3aed72acacdc8f768e657cc443a9cc9aa212b4"})
 MEASURED_TRAFFIC = {
     # B = 32 launches: the lane-group kernel (fp32 cache; the 24-bit cache in
     # 8-wave blocks), the MFMA kernel in 8-wave blocks (bf16 cache)
     ("attn_decode_kernel", "fp32"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 1078642260},
+                                     "bytes_per_launch": 1078972198},
     ("attn_decode_mfma_kernel", "bf16"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                          "bytes_per_launch": 541775006},
+                                          "bytes_per_launch": 541900500},
     ("attn_decode_kernel", "f24"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                    "bytes_per_launch": 810146246},
+                                    "bytes_per_launch": 810591850},
     ("gemv_decode", "fp32"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                              "bytes_per_launch": 121774326},
+                              "bytes_per_launch": 121778370},
     ("gemv_decode", "bf16"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                              "bytes_per_launch": 121774326},
+                              "bytes_per_launch": 121778370},
+    ("gemv_decode", "f24"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
+                             "bytes_per_launch": 121778370},
     ("gemm_prefill", "fp32"): {"sources": _GEMM_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                               "bytes_per_launch": 1713454592},
+                               "bytes_per_launch": 1716674994},
     ("attn_prefill", "fp32"): {"sources": _TILES_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                               "bytes_per_launch": 269962240},
+                               "bytes_per_launch": 267578635},
 }
 # MFMA counters of the prefill kernels (rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
 # GRBM_GUI_ACTIVE SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES): busy = MFMA-busy
@@ -80,9 +84,14 @@ MEASURED_TRAFFIC = {
 # gate|up, down); reported only while the sources hash to the profiled ones.
 MEASURED_MFMA = {
     ("gemm_prefill", "fp32"): {"sources": _GEMM_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                               "busy": 0.586, "executed_frac": 0.486, "clock_ghz": 1.97},
+                               "busy": 0.569, "executed_frac": 0.466, "clock_ghz": 1.95},
     ("attn_prefill", "fp32"): {"sources": _TILES_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                               "busy": 0.469, "executed_frac": 0.406, "clock_ghz": 2.07},
+                               "busy": 0.461, "executed_frac": 0.394, "clock_ghz": 2.04},
+    # the fp16 + fp8 form (q|k|v and gate|up; o and down on the bf16 pair):
+    # executed counts each product's fp16 and fp8 flops (the fp8 pass runs at
+    # twice the bf16 rate), against 2.5 PFLOP/s
+    ("gemm_prefill_f16f8", "fp32"): {"sources": _GEMM_SOURCES, "workload": ("mistral-7b", 32, 4096),
+                                     "busy": 0.491, "executed_frac": 0.506, "clock_ghz": 2.05},
 }
 BF16_PEAK_TFLOPS = 2500.0
 # The other shapes' workloads: (decode batches, prompt length).
@@ -696,6 +705,9 @@ def main():
             "gemm_prefill": roof(pv["gemm"], "mfma"),
             "gemm_prefill_bf16_pair": roof(pb["gemm"], "mfma"),
         }
+        if out["prefill_f16f8"]["gemm_prefill"] is not None:
+            out["prefill_f16f8"]["gemm_prefill"]["mfma_counters"] = measured_mfma(("gemm_prefill_f16f8", "fp32"),
+                                                                                  (cfg.name, B, P))
     if not args.no_cpu_baseline and not args.only:
         try:
             out["cpu_baseline"] = cpu_baseline(cfg, wd, B=B, prefill_tokens=args.cpu_steps)
