@@ -58,7 +58,7 @@ constexpr size_t MAX_GRAPHS = 16;
 
 struct Plan {  // byte offsets into the workspace
     size_t kv_layer;        // elements of one layer's K (or V) cache
-    size_t k, v, ck, cv, kvimg, s_hi, s_lo, x, a_hi, a_lo, a_f32, part, q, attn, rope, tok, pos, slot, amax, ssq;
+    size_t k, v, ck, cv, kvimg, s_hi, s_lo, x, x2, part2, a_hi, a_lo, a_f32, part, q, attn, rope, tok, pos, slot, amax, ssq;
     size_t moe_ids, moe_w, moe_cnt, moe_off, moe_pairs, moe_inv, g_hi, g_lo, g_f32;
     size_t part_floats, act_elems, total;
     int rows;               // max rows of one pass (max(max_batch, max_prefill))
@@ -86,7 +86,7 @@ struct dec_model {
     void *kvimg;            // prefill attention's K/V tile images (null: not used)
     u16 *s_hi, *s_lo;       // fused SwiGLU output of a prefill (null: not used)
     int kv_es;
-    float *x, *a_f32, *part, *q, *attn, *moe_w, *g_f32, *ssq;
+    float *x, *x2, *part2, *a_f32, *part, *q, *attn, *moe_w, *g_f32, *ssq;
     u16 *a_hi, *a_lo, *g_hi, *g_lo;
     float2 *rope;
     int32_t *tok, *pos, *slot, *amax, *moe_ids, *moe_cnt, *moe_off, *moe_pairs, *moe_inv;
@@ -193,6 +193,11 @@ bool plan(const dec_config &c, Plan &p) {
     p.kvimg = take(c.weight_dtype == DEC_WEIGHT_F32 ? 0
                    : attn_tiles_bytes(c.max_seq, c.n_kv_heads, c.head_dim, c.kv_dtype));
     p.x = take((size_t)rows * d * 4);
+    p.x2 = take(d * 4);   // the other residual row of one-row decode (normed inside the projections)
+    // one-row decode: the down projection's k-split partials, apart from the
+    // partial buffer the next projection writes while its blocks still read
+    // them (at most one split per 64 k)
+    p.part2 = take((size_t)((c.ffn_dim + 63) / 64) * d * 4);
     const bool f32w = c.weight_dtype == DEC_WEIGHT_F32;
     p.a_hi = take(f32w ? 0 : p.act_elems * 2);
     p.a_lo = take(f32w ? 0 : std::max(p.act_elems * 2, f8_lo(d)));
@@ -340,7 +345,7 @@ struct Pass {
 // Projection of T rows.  The result is a set of split partials in `part`; a
 // single-split result (GEMM, fp32 weights) goes to `out` instead when given.
 Partials proj(dec_model *m, const WSeg *segs, int nseg, int K, int T, const u16 *hi, const u16 *lo,
-              const float *f32, int lda, float *out = nullptr) {
+              const float *f32, int lda, float *out = nullptr, const RowNorm *rn = nullptr) {
     int N = 0;
     for (int i = 0; i < nseg; i++) N += segs[i].rows;
     const bool gemv = T <= 64;
@@ -354,7 +359,7 @@ Partials proj(dec_model *m, const WSeg *segs, int nseg, int K, int T, const u16 
     if (gemv) {
         const int S = gemv_splits(N, K, T);
         Tick tk(m, DEC_K_GEMV);
-        launch_gemv(m->st, segs, nseg, K, hi, lo, lda, T, m->part, S, (size_t)T * N, N);
+        launch_gemv(m->st, segs, nseg, K, hi, lo, lda, T, m->part, S, (size_t)T * N, N, rn);
         tk.done((double)N * K * 2 + (double)T * K * 4 + (double)T * N * 4, 2.0 * T * N * K);
         return Partials{m->part, S, (size_t)T * N, N};
     }
@@ -434,6 +439,19 @@ void run_pass(dec_model *m, const Pass &ps) {
     const F8Act fa_d{ah, (uint8_t *)al, (uint8_t *)al + (size_t)mpad * d, d, mpad};
     // the fused gate|up takes these operands where it takes the DMA kernel
     const bool f8_ffn = f8 && c.n_experts == 0 && (long)((F + 127) / 128) * ((T + 255) / 256) >= num_cus();
+    // One decode row, bf16 weights, dense FFN: the residual + RMSNorm before
+    // gate|up, before q|k|v (after layer 0) and before the LM head is formed in
+    // those projections' own blocks (the row is read by every block) instead of
+    // a kernel of its own; the residual row alternates between x and x2.  Each
+    // block then reads the row and its k-split partials before its first
+    // product, which pays only where the projections are short: Qwen2.5-0.5B
+    // 1.232 -> 1.166 ms a step, SmolLM2-135M 1.256 -> 1.148, but Mistral-7B
+    // (d x F = 58.7 M) 3.600 -> 3.690, so the larger FFNs keep the norm kernel.
+    const bool rnf = ps.decode && T == 1 && !f32w && c.n_experts == 0 && ps.logits && ps.logit_rows == 1 &&
+                     m->s_hi && F % 8 == 0 && d % 64 == 0 && d <= 8192 &&
+                     (long)d * F <= (16l << 20);
+    float *xc = m->x, *xn = m->x2;
+    Partials pend{nullptr, 0, 0, 0};   // the down partials the next projection's prologue adds
 
     launch_residual_norm(st, RN_EMBED, T, d, m->x, m->tok, m->embed, f32w, Partials{nullptr, 0, 0, 0},
                          Partials{nullptr, 0, 0, 0}, nullptr, nullptr, 0, m->L[0].attn_norm, eps, ah, al, af, caph(0),
@@ -448,7 +466,14 @@ void run_pass(dec_model *m, const Pass &ps) {
         const int kvk = c.kv_dtype;   // DEC_KV_* values are the kernels' cache formats
         // q | k | v
         WSeg qkv[3] = {{w.wq, qd}, {w.wk, kvd}, {w.wv, kvd}};
-        Partials pq = f8 ? proj_f8(m, m->f8w[l].qkv, T, fa_d) : proj(m, qkv, 3, d, T, ah, al, af, d);
+        Partials pq;
+        if (rnf && pend.p) {
+            const RowNorm rn{xc, xn, caph(l), pend, w.attn_norm, eps, d};
+            pq = proj(m, qkv, 3, d, T, nullptr, nullptr, nullptr, d, nullptr, &rn);
+            std::swap(xc, xn);
+        } else {
+            pq = f8 ? proj_f8(m, m->f8w[l].qkv, T, fa_d) : proj(m, qkv, 3, d, T, ah, al, af, d);
+        }
         // attention -> a (row stride qd)
         if (ps.decode) {
             // RoPE and the new K/V rows are formed inside the attention kernel
@@ -489,14 +514,30 @@ void run_pass(dec_model *m, const Pass &ps) {
         // output projection, residual, FFN norm
         WSeg wo[1] = {{w.wo, d}};
         Partials po = proj(m, wo, 1, qd, T, ah, al, af, qd);
-        launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, po, Partials{nullptr, 0, 0, 0}, nullptr,
-                             nullptr, 0, w.ffn_norm, eps, ah, al, af, nullptr, m->ssq, f8_ffn ? &fa_d : nullptr);
+        // one decode row: the fused gate|up forms this residual + norm itself
+        bool rn_gu = false;
+        if (rnf) {
+            const RowNorm rn{xc, xn, nullptr, po, w.ffn_norm, eps, d};
+            Tick tk(m, DEC_K_GEMV);
+            rn_gu = launch_gemv_silu(st, w.w_gate, w.w_up, F, d, nullptr, nullptr, d, T, m->s_hi, m->s_lo, F, &rn);
+            if (rn_gu) {
+                tk.done(2.0 * F * d * 2 + (double)T * d * 4 + (double)T * F * 4, 2.0 * T * 2 * F * d);
+                std::swap(xc, xn);
+            } else {
+                tk.cancel();
+            }
+        }
+        if (!rn_gu)
+            launch_residual_norm(st, RN_ADD, T, d, xc, nullptr, nullptr, 0, po, Partials{nullptr, 0, 0, 0}, nullptr,
+                                 nullptr, 0, w.ffn_norm, eps, ah, al, af, nullptr, m->ssq, f8_ffn ? &fa_d : nullptr);
         const float *next_gain = (l + 1 < c.n_layers) ? m->L[l + 1].attn_norm : m->out_norm;
         if (c.n_experts == 0) {
             WSeg gu[2] = {{w.w_gate, F}, {w.w_up, F}};
             // a large prefill takes the gate|up GEMM with silu(gate) * up in its epilogue
-            bool fused = false;
-            if (f8_ffn) {
+            bool fused = rn_gu;
+            if (fused) {
+                // (formed above with the residual + norm)
+            } else if (f8_ffn) {
                 Tick tk(m, DEC_K_GEMM);
                 fused = launch_gemm_f8_silu(st, m->f8w[l].gu, fa_d.a16, fa_d.a8, fa_d.asc, mpad, d, T, m->s_hi,
                                             m->s_lo, F);
@@ -522,10 +563,22 @@ void run_pass(dec_model *m, const Pass &ps) {
                 launch_silu_mul(st, T, F, pg, ah, al, af);
             }
             WSeg wd[1] = {{w.w_down, d}};
-            Partials pd = proj(m, wd, 1, F, T, fused ? m->s_hi : ah, fused ? m->s_lo : al, af, F);
-            launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, pd, Partials{nullptr, 0, 0, 0},
-                                 nullptr, nullptr, 0, next_gain, eps, ah, al, af, caph(l + 1), m->ssq,
-                                 f8 && l + 1 < c.n_layers ? &fa_d : nullptr);
+            if (rn_gu) {
+                // into the second partial buffer: the next q|k|v (or the LM
+                // head) adds these partials in its prologue while it writes
+                // its own into the first
+                const int S = gemv_splits(d, F, 1);
+                Tick tk(m, DEC_K_GEMV);
+                launch_gemv(st, wd, 1, F, m->s_hi, m->s_lo, F, 1, m->part2, S, (size_t)d, d);
+                tk.done((double)d * F * 2 + (double)F * 4 + (double)d * 4, 2.0 * d * F);
+                pend = Partials{m->part2, S, (size_t)d, d};
+            } else {
+                Partials pd = proj(m, wd, 1, F, T, fused ? m->s_hi : ah, fused ? m->s_lo : al, af, F);
+                launch_residual_norm(st, RN_ADD, T, d, xc, nullptr, nullptr, 0, pd, Partials{nullptr, 0, 0, 0},
+                                     nullptr, nullptr, 0, next_gain, eps, ah, al, af, caph(l + 1), m->ssq,
+                                     f8 && l + 1 < c.n_layers ? &fa_d : nullptr);
+                pend = Partials{nullptr, 0, 0, 0};
+            }
         } else {
             const int E = c.n_experts, k = c.top_k, TP = T * k;
             // router logits: the GEMV for decode rows and fp32 weights; prefill
@@ -567,7 +620,7 @@ void run_pass(dec_model *m, const Pass &ps) {
             WSeg wd[1] = {{w.w_down, d}};
             Partials pd = proj_grouped(m, wd, 1, F, T, ah, al, af, F);
             // the residual reads each token's expert outputs at their grouped rows
-            launch_residual_norm(st, RN_ADD, T, d, m->x, nullptr, nullptr, 0, Partials{nullptr, 0, 0, 0}, pd,
+            launch_residual_norm(st, RN_ADD, T, d, xc, nullptr, nullptr, 0, Partials{nullptr, 0, 0, 0}, pd,
                                  m->moe_inv, m->moe_w, k, next_gain, eps, ah, al, af, caph(l + 1), m->ssq,
                                  f8 && l + 1 < c.n_layers ? &fa_d : nullptr);
         }
@@ -577,8 +630,14 @@ void run_pass(dec_model *m, const Pass &ps) {
         const void *head = c.tied_embedding ? m->embed : m->lm_head;
         WSeg hs[1] = {{head, c.vocab}};
         const size_t ro = (size_t)ps.logit_row0 * d;
-        Partials pl = proj(m, hs, 1, d, ps.logit_rows, ah ? ah + ro : nullptr, al ? al + ro : nullptr,
-                           af ? af + ro : nullptr, d, ps.logits);
+        Partials pl;
+        if (rnf && pend.p) {
+            const RowNorm rn{xc, xn, caph(c.n_layers), pend, m->out_norm, eps, d};
+            pl = proj(m, hs, 1, d, ps.logit_rows, nullptr, nullptr, nullptr, d, ps.logits, &rn);
+        } else {
+            pl = proj(m, hs, 1, d, ps.logit_rows, ah ? ah + ro : nullptr, al ? al + ro : nullptr,
+                      af ? af + ro : nullptr, d, ps.logits);
+        }
         if (pl.p != ps.logits) launch_reduce_splits(st, pl, ps.logit_rows, c.vocab, ps.logits, c.vocab);
     }
 }
@@ -759,6 +818,8 @@ int dec_create(const dec_config *cfg, const dec_weights *w, void *workspace, siz
     m->s_lo = m->s_hi ? (u16 *)(b + p.s_lo) : nullptr;
     m->kv_es = (int)kv_elem_bytes(*cfg);
     m->x = (float *)(b + p.x);
+    m->x2 = (float *)(b + p.x2);
+    m->part2 = (float *)(b + p.part2);
     m->a_hi = (u16 *)(b + p.a_hi);
     m->a_lo = (u16 *)(b + p.a_lo);
     m->a_f32 = (float *)(b + p.a_f32);

@@ -47,6 +47,9 @@ struct GemvParams {
     // per block (8 features each)
     u16 *s_hi, *s_lo;
     int rt;
+    // residual + RMSNorm of the one batch row formed in the kernel (the RN
+    // instances); the (hi, lo) operand of the block's k range then sits in LDS
+    RowNorm rn;
 };
 
 constexpr int DKS = 64;            // k per stage
@@ -58,6 +61,8 @@ constexpr int CPOL_NT = 2;         // cache-policy operand of global_load_lds: t
 
 template <int NT>
 constexpr size_t dma_lds() { return (size_t)DNSTAGE * (DROWS * DKS + 16 * NT * DKS) * 2; }
+// RN instances: the ring, then the (hi, lo) operand of a k range of kps
+inline size_t dma_lds_rn(int kps) { return dma_lds<2>() + (size_t)2 * kps * 2; }
 
 // Stage layout: the weight tile [128 rows][64 k] then the activation tile
 // [16*NT columns][64 k] (column t*16 + m: hi of batch row t*8 + m for m < 8,
@@ -79,16 +84,21 @@ constexpr int ring_wait(int n) {
     return ((n * (DNSTAGE - 2)) & 15) | (7 << 4) | (0 << 8) | (((n * (DNSTAGE - 2)) >> 4) << 14);
 }
 
-template <int NT, int FORM>
+// RN: one batch row whose residual + RMSNorm the block forms itself (p.rn):
+// the ring carries only weights, and the B operand comes from the row's
+// (hi, lo) pair of the block's k range, kept in LDS after the ring.
+template <int NT, int FORM, bool RN = false>
 __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
     constexpr bool SILU = FORM == SILU_FUSED;
     static_assert(NT >= 2, "the activation tile needs one load per wave");
+    static_assert(!RN || (NT == 2 && FORM != GROUPED), "one dense or fused-SwiGLU row");
     extern __shared__ __attribute__((aligned(16))) u16 smem[];
+    __shared__ float rn_red[16];
     constexpr int NSTAGE = DNSTAGE;
     constexpr int WST = DROWS * DKS;           // u16 of the weight tile
     constexpr int STG = WST + 16 * NT * DKS;   // u16 per stage
     constexpr int NW = DROWS * DCH / 256;      // weight loads per thread per stage (4)
-    constexpr int NLD = NW + NT / 2;           // 16-byte loads per thread per stage
+    constexpr int NLD = RN ? NW : NW + NT / 2; // 16-byte loads per thread per stage
     // the wave index as a scalar: tests on it branch per wave, not per lane
     const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, c = lane >> 4;
@@ -112,6 +122,55 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
     // every block at once, concentrate on few memory channels; a per-block
     // start stage spreads the column offsets in flight.
     const int rot = p.rot && nst > 0 ? (int)(blockIdx.x % nst) : 0;
+    const int KR = kend - kbeg;                      // RN: the operand row's length in LDS
+    u16 *act = smem + NSTAGE * STG;                  // RN: hi [KR], then lo [KR]
+
+    // RN prologue: x_new = x + sum of the split partials over the whole row,
+    // its sum of squares, then the normed (hi, lo) pair of [kbeg, kend) into
+    // LDS; the same operations and order as the residual + RMSNorm kernel
+    // (split partials summed in order, then added to x; a = x * rs * g).
+    auto rn_prologue = [&]() {
+        const RowNorm &n = p.rn;
+        const int nv = n.d / 4;
+        constexpr int VPT = 8;
+        float4 v[VPT];
+        float ss = 0.f;
+        const bool first = blockIdx.x == 0 && blockIdx.y == 0;
+#pragma unroll
+        for (int u = 0; u < VPT; u++) {
+            const int i4 = tid + u * 256;
+            if (i4 >= nv) break;
+            float4 r4 = *reinterpret_cast<const float4 *>(n.x + 4 * i4);
+            if (n.add.p) {
+                const float4 a = sum_splits4(n.add.p, n.add.S, n.add.stride, (size_t)4 * i4);
+                r4.x += a.x; r4.y += a.y; r4.z += a.z; r4.w += a.w;
+            }
+            v[u] = r4;
+            ss += r4.x * r4.x + r4.y * r4.y + r4.z * r4.z + r4.w * r4.w;
+            if (first) {
+                *reinterpret_cast<float4 *>(n.x_new + 4 * i4) = r4;
+                if (n.cap) *reinterpret_cast<float4 *>(n.cap + 4 * i4) = r4;
+            }
+        }
+        const float tot = block_sum(ss, rn_red);
+        const float rs = 1.0f / sqrtf(tot / (float)n.d + n.eps);
+#pragma unroll
+        for (int u = 0; u < VPT; u++) {
+            const int i4 = tid + u * 256;
+            if (i4 >= nv) break;
+            const int k = 4 * i4;
+            if (k < kbeg || k >= kend) continue;
+            const float4 g = *reinterpret_cast<const float4 *>(n.gain + k);
+            float4 a;
+            a.x = v[u].x * rs * g.x; a.y = v[u].y * rs * g.y;
+            a.z = v[u].z * rs * g.z; a.w = v[u].w * rs * g.w;
+            uint2 h, l;
+            split2_bf16(a.x, a.y, h.x, l.x);
+            split2_bf16(a.z, a.w, h.y, l.y);
+            *reinterpret_cast<uint2 *>(act + (k - kbeg)) = h;
+            *reinterpret_cast<uint2 *>(act + KR + (k - kbeg)) = l;
+        }
+    };
 
     // load i of this thread fills stage chunk P = (i*4 + wv)*64 + lane (lane
     // L of a wave writes 16 bytes at the wave's base + 16 L): the weight tile
@@ -179,15 +238,19 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
 
     // The tiles of a SILU block past rt are multiplied like the others (on
     // stale LDS) but never stored.
+    // the ring's first NSTAGE-1 stages
+    auto ring_start = [&](auto nwl_c) {
+#pragma unroll
+        for (int g = 0; g < NSTAGE - 1; g++) load_stage(g, g, nwl_c);
+    };
     auto ring_loop = [&](auto nwl_c) {
         constexpr int NWL = decltype(nwl_c)::value;
         // between stages: wait until the loads of the newest NSTAGE-2 stages at
         // most are outstanding and every LDS read is done, then a plain barrier
         // (__syncthreads would also wait for the newest stages)
-        static_assert((NWL + NT / 2) * (NSTAGE - 2) < 64, "vmcnt field");
-        constexpr int WAIT = ring_wait(NWL + NT / 2);
-#pragma unroll
-        for (int g = 0; g < NSTAGE - 1; g++) load_stage(g, g, nwl_c);
+        constexpr int NA = RN ? 0 : NT / 2;
+        static_assert((NWL + NA) * (NSTAGE - 2) < 64, "vmcnt field");
+        constexpr int WAIT = ring_wait(NWL + NA);
         __builtin_amdgcn_s_waitcnt(WAIT);
         __builtin_amdgcn_s_barrier();
         for (int g = 0; g < nst; g++) {
@@ -208,8 +271,17 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
 #pragma unroll
                 for (int t = 0; t < NT; t++) {
                     const int col = t * 16 + r;
-                    const bf16x8 bf = __builtin_bit_cast(
-                        bf16x8, *reinterpret_cast<const u32x4 *>(sa + col * DKS + 8 * (lc ^ (col & (DCH - 1)))));
+                    bf16x8 bf;
+                    if constexpr (RN) {
+                        // every column reads the one row's hi (col % 16 < 8) or lo
+                        int gg = g + rot;
+                        gg = gg >= nst ? gg - nst : gg;
+                        bf = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4 *>(
+                                                            act + ((r & 8) ? KR : 0) + gg * DKS + 8 * lc));
+                    } else {
+                        bf = __builtin_bit_cast(
+                            bf16x8, *reinterpret_cast<const u32x4 *>(sa + col * DKS + 8 * (lc ^ (col & (DCH - 1)))));
+                    }
 #pragma unroll
                     for (int rt = 0; rt < 2; rt++)
                         acc[rt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[rt], bf, acc[rt][t], 0, 0, 0);
@@ -222,21 +294,31 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
         // is released
         __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
     };
+    // RN: the row's operand is formed while the ring's first stages are in
+    // flight (its LDS writes are complete and visible after the ring's first
+    // wait and barrier)
     if (nst > 0) {
         if constexpr (!SILU) {
+            ring_start(std::integral_constant<int, NW>{});
+            if constexpr (RN) rn_prologue();
             ring_loop(std::integral_constant<int, NW>{});
         } else {
             static_assert(NW == 4, "one instance per weight-load count");
             int nwl = 0;   // wave-uniform
 #pragma unroll
             for (int i = 0; i < NW; i++) nwl += i * 4 + wv < 2 * RT;
-            switch (nwl) {
-                case 4: ring_loop(std::integral_constant<int, 4>{}); break;
-                case 3: ring_loop(std::integral_constant<int, 3>{}); break;
-                case 2: ring_loop(std::integral_constant<int, 2>{}); break;
-                case 1: ring_loop(std::integral_constant<int, 1>{}); break;
-                default: ring_loop(std::integral_constant<int, 0>{}); break;
+#define NWL_SWITCH(F)                                          \
+            switch (nwl) {                                     \
+                case 4: F(std::integral_constant<int, 4>{}); break; \
+                case 3: F(std::integral_constant<int, 3>{}); break; \
+                case 2: F(std::integral_constant<int, 2>{}); break; \
+                case 1: F(std::integral_constant<int, 1>{}); break; \
+                default: F(std::integral_constant<int, 0>{}); break; \
             }
+            NWL_SWITCH(ring_start)
+            if constexpr (RN) rn_prologue();
+            NWL_SWITCH(ring_loop)
+#undef NWL_SWITCH
         }
     }
 
@@ -314,6 +396,19 @@ void launch_dma_nt(hipStream_t st, const GemvParams &p, dim3 grid) {
     hipLaunchKernelGGL((gemv_dma_kernel<NT, FORM>), grid, dim3(256), dma_lds<NT>(), st, p);
 }
 
+// one row with its residual + RMSNorm formed in the kernel
+template <int FORM>
+void launch_dma_rn(hipStream_t st, const GemvParams &p, dim3 grid) {
+    const size_t lds = dma_lds_rn(p.kps);
+    static size_t attr = 0;
+    if (attr < lds) {
+        (void)hipFuncSetAttribute((const void *)gemv_dma_kernel<2, FORM, true>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        attr = lds;
+    }
+    hipLaunchKernelGGL((gemv_dma_kernel<2, FORM, true>), grid, dim3(256), lds, st, p);
+}
+
 template <int FORM>
 void launch_dma(hipStream_t st, const GemvParams &p, dim3 grid, int rows) {
     const int NT = (rows + 7) / 8;   // up to 16 rows share the two-tile kernel
@@ -378,7 +473,7 @@ int gemv_splits(int N, int K, int B) {
 }
 
 void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi, const u16 *a_lo,
-                 int lda, int B, float *out, int ksplit, size_t split_stride, int ldo) {
+                 int lda, int B, float *out, int ksplit, size_t split_stride, int ldo, const RowNorm *rn) {
     GemvParams p{};
     int end = 0;
     for (int s = 0; s < nseg; s++) {
@@ -405,12 +500,18 @@ void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
     p.kps = kps;
     // a row pitch that is a multiple of 8 KB with few split offsets: rotate
     p.rot = (K % 4096 == 0 && ksplit < 8) ? 1 : 0;
+    if (rn && B == 1) {
+        p.rn = *rn;
+        launch_dma_rn<DENSE>(st, p, dim3((p.N + DROWS - 1) / DROWS, ksplit, 1));
+        return;
+    }
     launch_dma<DENSE>(st, p, dim3((p.N + DROWS - 1) / DROWS, ksplit, 1), B);
 }
 
 bool launch_gemv_silu(hipStream_t st, const void *w_gate, const void *w_up, int F, int K, const u16 *a_hi,
-                      const u16 *a_lo, int lda, int B, u16 *s_hi, u16 *s_lo, int ldo) {
+                      const u16 *a_lo, int lda, int B, u16 *s_hi, u16 *s_lo, int ldo, const RowNorm *rn) {
     if (B <= 0 || B > 64 || K % DKS != 0 || F % 8 != 0) return false;
+    if (rn && B != 1) return false;
     // Up to 32 rows the 8-feature tiles are spread over the CUs (rt tiles per
     // block, one block per CU).  With more rows each block's activation tile
     // outweighs its weight rows, and fewer, full blocks (8 tiles) measured
@@ -435,6 +536,11 @@ bool launch_gemv_silu(hipStream_t st, const void *w_gate, const void *w_up, int 
     p.s_hi = s_hi;
     p.s_lo = s_lo;
     p.rt = rt;
+    if (rn) {
+        p.rn = *rn;
+        launch_dma_rn<SILU_FUSED>(st, p, dim3(blocks, 1, 1));
+        return true;
+    }
     launch_dma<SILU_FUSED>(st, p, dim3(blocks, 1, 1), B);
     return true;
 }

@@ -80,8 +80,24 @@ int gemv_grouped_splits(int N, int K, int B);   // the split count for launch_ge
 int gemv_max_splits(int N, int K);
 int gemv_grouped_max_splits(int K);
 int num_cus();
+// Residual + RMSNorm of one decode row, formed by a projection's own blocks
+// ahead of their products (Pantheon "Llama Forward Pass", section "RMSNorm"):
+// x_new = x + the previous projection's split partials (summed in split
+// order), a = x_new / sqrt(mean(x_new^2) + eps) * gain; every block reads the
+// whole row and keeps the bf16 (hi, lo) pair of its own k range in LDS, and
+// block (0, 0) stores x_new (and the capture row, when given).  x and x_new
+// are distinct buffers (the other blocks still read x); d <= 8192.
+struct RowNorm {
+    const float *x;
+    float *x_new;
+    float *cap;
+    Partials add;
+    const float *gain;
+    float eps;
+    int d;
+};
 void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi, const u16 *a_lo,
-                 int lda, int B, float *out, int ksplit, size_t split_stride, int ldo);
+                 int lda, int B, float *out, int ksplit, size_t split_stride, int ldo, const RowNorm *rn = nullptr);
 
 // Prefill projection, bf16 weights, MFMA: out[m][n] = sum_k (a_hi+a_lo)[m][k] W[n][k].
 // gemm_splits(N, K, M) gives the k splits to launch with (1 to 16): with S > 1,
@@ -105,9 +121,10 @@ bool launch_gemm_silu(hipStream_t st, const void *w_gate, const void *w_up, int 
 // each) against B <= 64 activation rows, one k split, silu(gate) * up written
 // as bf16 (hi, lo) pairs to s_hi/s_lo [B][ldo].  Returns false (nothing
 // launched) for shapes it does not take: K not a multiple of 64 or F not a
-// multiple of 8.
+// multiple of 8.  With rn (B = 1), the row's residual + RMSNorm is formed in
+// the kernel and a_hi/a_lo are not read.
 bool launch_gemv_silu(hipStream_t st, const void *w_gate, const void *w_up, int F, int K, const u16 *a_hi,
-                      const u16 *a_lo, int lda, int B, u16 *s_hi, u16 *s_lo, int ldo);
+                      const u16 *a_lo, int lda, int B, u16 *s_hi, u16 *s_lo, int ldo, const RowNorm *rn = nullptr);
 
 // fp32-weight projection (any M): out[m][n] = sum_k a[m][k] W[n][k].
 void launch_gemm_f32(hipStream_t st, const WSeg *segs, int nseg, int K, const float *a, int lda,
