@@ -345,7 +345,8 @@ struct Pass {
 // Projection of T rows.  The result is a set of split partials in `part`; a
 // single-split result (GEMM, fp32 weights) goes to `out` instead when given.
 Partials proj(dec_model *m, const WSeg *segs, int nseg, int K, int T, const u16 *hi, const u16 *lo,
-              const float *f32, int lda, float *out = nullptr, const RowNorm *rn = nullptr) {
+              const float *f32, int lda, float *out = nullptr, const RowNorm *rn = nullptr,
+              const AttnMerge *am = nullptr) {
     int N = 0;
     for (int i = 0; i < nseg; i++) N += segs[i].rows;
     const bool gemv = T <= 64;
@@ -359,7 +360,7 @@ Partials proj(dec_model *m, const WSeg *segs, int nseg, int K, int T, const u16 
     if (gemv) {
         const int S = gemv_splits(N, K, T);
         Tick tk(m, DEC_K_GEMV);
-        launch_gemv(m->st, segs, nseg, K, hi, lo, lda, T, m->part, S, (size_t)T * N, N, rn);
+        launch_gemv(m->st, segs, nseg, K, hi, lo, lda, T, m->part, S, (size_t)T * N, N, rn, am);
         tk.done((double)N * K * 2 + (double)T * K * 4 + (double)T * N * 4, 2.0 * T * N * K);
         return Partials{m->part, S, (size_t)T * N, N};
     }
@@ -475,14 +476,21 @@ void run_pass(dec_model *m, const Pass &ps) {
             pq = f8 ? proj_f8(m, m->f8w[l].qkv, T, fa_d) : proj(m, qkv, 3, d, T, ah, al, af, d);
         }
         // attention -> a (row stride qd)
+        // one decode row in several attention splits: the output projection's
+        // blocks merge the splits of their k range (no merge kernel; Mistral-7B
+        // B = 1 3.604 -> 3.542 ms a step, Qwen2.5-0.5B 1.166 -> 1.108)
+        bool am_o = false;
+        int am_s = 0;
         if (ps.decode) {
             // RoPE and the new K/V rows are formed inside the attention kernel
             const int S = attn_splits_for(m, T, ps.hpos);
+            am_o = T == 1 && !f32w && S > 1 && S <= 64;
             const RopeArgs ra{pq, c.qkv_bias ? w.bq : nullptr, c.qkv_bias ? w.bk : nullptr,
                               c.qkv_bias ? w.bv : nullptr, m->rope, c.rope_pairing, m->ring};
             Tick tk(m, DEC_K_ATTN_DECODE);
             launch_attn_decode(st, T, ra, kc, vc, kvk, m->pos, m->slot, nh, nkv, hd, c.max_seq, S, m->attn, ah, al,
-                               af);
+                               af, !am_o);
+            am_s = S;
             tk.done(kv_read_bytes(c, T, ps.hpos) + 2.0 * T * qd * 4, 0);
         } else {
             // K/V into the layer cache, or held in the chunk buffers (deferred commit)
@@ -513,7 +521,8 @@ void run_pass(dec_model *m, const Pass &ps) {
         }
         // output projection, residual, FFN norm
         WSeg wo[1] = {{w.wo, d}};
-        Partials po = proj(m, wo, 1, qd, T, ah, al, af, qd);
+        const AttnMerge am{m->attn, hd, am_s};
+        Partials po = proj(m, wo, 1, qd, T, ah, al, af, qd, nullptr, nullptr, am_o ? &am : nullptr);
         // one decode row: the fused gate|up forms this residual + norm itself
         bool rn_gu = false;
         if (rnf) {

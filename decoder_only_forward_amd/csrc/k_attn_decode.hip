@@ -919,7 +919,7 @@ int attn_decode_splits(int B, int nkv, int readable, int hd, int G, int kv_kind)
 
 void launch_attn_decode(hipStream_t st, int B, const RopeArgs &ra, void *kc, void *vc, int kv_kind,
                         const int32_t *pos, const int32_t *slot, int nh, int nkv, int hd, int max_seq, int splits,
-                        float *part, u16 *o_hi, u16 *o_lo, float *o_f32) {
+                        float *part, u16 *o_hi, u16 *o_lo, float *o_f32, bool merge) {
     if (B <= 0) return;
     const int G = nh / nkv;
     dim3 grid(splits, nkv, B);
@@ -937,7 +937,7 @@ void launch_attn_decode(hipStream_t st, int B, const RopeArgs &ra, void *kc, voi
         else { MDH(KV_F32) }
 #undef MDH
 #undef MD
-        if (splits > 1)
+        if (splits > 1 && merge)
             hipLaunchKernelGGL(attn_merge_kernel, dim3(nh, B), dim3(hd), 0, st, nh, hd, splits, part, o_hi, o_lo,
                                o_f32);
         return;
@@ -956,7 +956,7 @@ void launch_attn_decode(hipStream_t st, int B, const RopeArgs &ra, void *kc, voi
     else { LDH(KV_F32) }
 #undef LDH
 #undef LD
-    if (splits > 1)
+    if (splits > 1 && merge)
         hipLaunchKernelGGL(attn_merge_kernel, dim3(nh, B), dim3(hd < 64 ? 64 : hd), 0, st, nh, hd, splits, part,
                            o_hi, o_lo, o_f32);
 }

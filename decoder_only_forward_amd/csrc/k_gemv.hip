@@ -50,6 +50,9 @@ struct GemvParams {
     // residual + RMSNorm of the one batch row formed in the kernel (the RN
     // instances); the (hi, lo) operand of the block's k range then sits in LDS
     RowNorm rn;
+    // the one batch row's attention output merged from its split partials in
+    // the kernel (the AM instances), into the same LDS operand
+    AttnMerge am;
 };
 
 constexpr int DKS = 64;            // k per stage
@@ -61,8 +64,13 @@ constexpr int CPOL_NT = 2;         // cache-policy operand of global_load_lds: t
 
 template <int NT>
 constexpr size_t dma_lds() { return (size_t)DNSTAGE * (DROWS * DKS + 16 * NT * DKS) * 2; }
-// RN instances: the ring, then the (hi, lo) operand of a k range of kps
+// one-row instances: the ring, then the (hi, lo) operand of a k range of kps
 inline size_t dma_lds_rn(int kps) { return dma_lds<2>() + (size_t)2 * kps * 2; }
+
+// The B operand of one batch row formed by the block itself (PRO): none (the
+// ring carries the activation columns), the residual + RMSNorm of the row
+// (PRO_RN), or the merge of the row's attention split partials (PRO_AM).
+enum { PRO_NONE = 0, PRO_RN = 1, PRO_AM = 2 };
 
 // Stage layout: the weight tile [128 rows][64 k] then the activation tile
 // [16*NT columns][64 k] (column t*16 + m: hi of batch row t*8 + m for m < 8,
@@ -84,14 +92,17 @@ constexpr int ring_wait(int n) {
     return ((n * (DNSTAGE - 2)) & 15) | (7 << 4) | (0 << 8) | (((n * (DNSTAGE - 2)) >> 4) << 14);
 }
 
-// RN: one batch row whose residual + RMSNorm the block forms itself (p.rn):
-// the ring carries only weights, and the B operand comes from the row's
-// (hi, lo) pair of the block's k range, kept in LDS after the ring.
-template <int NT, int FORM, bool RN = false>
+// PRO_RN / PRO_AM: one batch row whose operand the block forms itself (the
+// residual + RMSNorm of p.rn, or the split merge of p.am): the ring carries
+// only weights, and the B operand comes from the row's (hi, lo) pair of the
+// block's k range, kept in LDS after the ring.
+template <int NT, int FORM, int PRO = PRO_NONE>
 __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
     constexpr bool SILU = FORM == SILU_FUSED;
     static_assert(NT >= 2, "the activation tile needs one load per wave");
+    constexpr bool RN = PRO != PRO_NONE;   // one row, operand in LDS
     static_assert(!RN || (NT == 2 && FORM != GROUPED), "one dense or fused-SwiGLU row");
+    static_assert(PRO != PRO_AM || FORM == DENSE, "the merged attention row feeds a dense projection");
     extern __shared__ __attribute__((aligned(16))) u16 smem[];
     __shared__ float rn_red[16];
     constexpr int NSTAGE = DNSTAGE;
@@ -169,6 +180,58 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
             split2_bf16(a.z, a.w, h.y, l.y);
             *reinterpret_cast<uint2 *>(act + (k - kbeg)) = h;
             *reinterpret_cast<uint2 *>(act + KR + (k - kbeg)) = l;
+        }
+    };
+
+    // AM prologue: element k of [kbeg, kend) is dim k % hd of head k / hd;
+    // its split partials o_s (unnormalised), maxima m_s and normalisers l_s
+    // combine as sum_s f_s o_s / sum_s f_s l_s with f_s = 2^(m_s - max m), the
+    // splits taken in ascending order (the split merge kernel's operations and
+    // order).  A thread takes two adjacent dims and issues the loads of up to
+    // 32 splits' (m, l) and (o, o') at once (lanes of one head read the same
+    // (m, l)); splits past 32 are read one by one.
+    auto am_prologue = [&]() {
+        const AttnMerge &a = p.am;
+        const int hd = a.hd, S = a.splits, ld = hd + 2;
+        const int S1 = S < 32 ? S : 32;
+        for (int k = kbeg + 2 * tid; k < kend; k += 512) {
+            const int h = k / hd, i = k % hd;
+            const float *src = a.part + (size_t)h * S * ld;
+            float2 ml[32], o[32];
+#pragma unroll
+            for (int u = 0; u < 32; u++) {
+                if (u < S1) {
+                    ml[u] = *reinterpret_cast<const float2 *>(src + u * ld + hd);
+                    o[u] = *reinterpret_cast<const float2 *>(src + u * ld + i);
+                }
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < 32; u++)
+                if (u < S1) mx = fmaxf(mx, ml[u].x);
+            for (int s2 = 32; s2 < S; s2++) mx = fmaxf(mx, src[s2 * ld + hd]);
+            float A0 = 0.f, A1 = 0.f, L = 0.f;
+#pragma unroll
+            for (int u = 0; u < 32; u++) {
+                if (u < S1) {
+                    const float f = ml[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[u].x - mx);
+                    L += ml[u].y * f;
+                    A0 += o[u].x * f;
+                    A1 += o[u].y * f;
+                }
+            }
+            for (int s2 = 32; s2 < S; s2++) {
+                const float2 m2 = *reinterpret_cast<const float2 *>(src + s2 * ld + hd);
+                const float2 o2 = *reinterpret_cast<const float2 *>(src + s2 * ld + i);
+                const float f = m2.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2.x - mx);
+                L += m2.y * f;
+                A0 += o2.x * f;
+                A1 += o2.y * f;
+            }
+            uint32_t hi, lo;
+            split2_bf16(A0 / L, A1 / L, hi, lo);
+            *reinterpret_cast<uint32_t *>(act + (k - kbeg)) = hi;
+            *reinterpret_cast<uint32_t *>(act + KR + (k - kbeg)) = lo;
         }
     };
 
@@ -300,7 +363,8 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
     if (nst > 0) {
         if constexpr (!SILU) {
             ring_start(std::integral_constant<int, NW>{});
-            if constexpr (RN) rn_prologue();
+            if constexpr (PRO == PRO_RN) rn_prologue();
+            if constexpr (PRO == PRO_AM) am_prologue();
             ring_loop(std::integral_constant<int, NW>{});
         } else {
             static_assert(NW == 4, "one instance per weight-load count");
@@ -316,7 +380,7 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
                 default: F(std::integral_constant<int, 0>{}); break; \
             }
             NWL_SWITCH(ring_start)
-            if constexpr (RN) rn_prologue();
+            if constexpr (PRO == PRO_RN) rn_prologue();
             NWL_SWITCH(ring_loop)
 #undef NWL_SWITCH
         }
@@ -402,11 +466,22 @@ void launch_dma_rn(hipStream_t st, const GemvParams &p, dim3 grid) {
     const size_t lds = dma_lds_rn(p.kps);
     static size_t attr = 0;
     if (attr < lds) {
-        (void)hipFuncSetAttribute((const void *)gemv_dma_kernel<2, FORM, true>,
+        (void)hipFuncSetAttribute((const void *)gemv_dma_kernel<2, FORM, PRO_RN>,
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         attr = lds;
     }
-    hipLaunchKernelGGL((gemv_dma_kernel<2, FORM, true>), grid, dim3(256), lds, st, p);
+    hipLaunchKernelGGL((gemv_dma_kernel<2, FORM, PRO_RN>), grid, dim3(256), lds, st, p);
+}
+
+void launch_dma_am(hipStream_t st, const GemvParams &p, dim3 grid) {
+    const size_t lds = dma_lds_rn(p.kps);
+    static size_t attr = 0;
+    if (attr < lds) {
+        (void)hipFuncSetAttribute((const void *)gemv_dma_kernel<2, DENSE, PRO_AM>,
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        attr = lds;
+    }
+    hipLaunchKernelGGL((gemv_dma_kernel<2, DENSE, PRO_AM>), grid, dim3(256), lds, st, p);
 }
 
 template <int FORM>
@@ -473,7 +548,8 @@ int gemv_splits(int N, int K, int B) {
 }
 
 void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi, const u16 *a_lo,
-                 int lda, int B, float *out, int ksplit, size_t split_stride, int ldo, const RowNorm *rn) {
+                 int lda, int B, float *out, int ksplit, size_t split_stride, int ldo, const RowNorm *rn,
+                 const AttnMerge *am) {
     GemvParams p{};
     int end = 0;
     for (int s = 0; s < nseg; s++) {
@@ -503,6 +579,11 @@ void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a
     if (rn && B == 1) {
         p.rn = *rn;
         launch_dma_rn<DENSE>(st, p, dim3((p.N + DROWS - 1) / DROWS, ksplit, 1));
+        return;
+    }
+    if (am && B == 1) {
+        p.am = *am;
+        launch_dma_am(st, p, dim3((p.N + DROWS - 1) / DROWS, ksplit, 1));
         return;
     }
     launch_dma<DENSE>(st, p, dim3((p.N + DROWS - 1) / DROWS, ksplit, 1), B);

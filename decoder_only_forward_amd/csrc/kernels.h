@@ -96,8 +96,21 @@ struct RowNorm {
     float eps;
     int d;
 };
+
+// The one decode row's attention output formed inside the output projection's
+// blocks (launch_gemv with B = 1): the split-KV partials of the decode
+// attention ([head][split][hd + 2]: hd unnormalised outputs, the split's
+// maximum, its normaliser) merged per element in split order, as the
+// separate merge kernel does (the running maximum and normaliser of rml "The
+// decoder", section "Attend", combined over splits).  splits <= 64.
+struct AttnMerge {
+    const float *part;
+    int hd;
+    int splits;
+};
 void launch_gemv(hipStream_t st, const WSeg *segs, int nseg, int K, const u16 *a_hi, const u16 *a_lo,
-                 int lda, int B, float *out, int ksplit, size_t split_stride, int ldo, const RowNorm *rn = nullptr);
+                 int lda, int B, float *out, int ksplit, size_t split_stride, int ldo, const RowNorm *rn = nullptr,
+                 const AttnMerge *am = nullptr);
 
 // Prefill projection, bf16 weights, MFMA: out[m][n] = sum_k (a_hi+a_lo)[m][k] W[n][k].
 // gemm_splits(N, K, M) gives the k splits to launch with (1 to 16): with S > 1,
@@ -152,7 +165,7 @@ struct RopeArgs {
 int attn_decode_splits(int B, int nkv, int readable, int hd, int G, int kv_kind);
 void launch_attn_decode(hipStream_t st, int B, const RopeArgs &ra, void *kc, void *vc, int kv_kind,
                         const int32_t *pos, const int32_t *slot, int nh, int nkv, int hd, int max_seq,
-                        int splits, float *part, u16 *o_hi, u16 *o_lo, float *o_f32);
+                        int splits, float *part, u16 *o_hi, u16 *o_lo, float *o_f32, bool merge = true);
 
 // Causal prefill attention for T rows of one sequence at positions
 // start_pos..start_pos+T-1.  Query p attends to positions [p - window + 1, p]
