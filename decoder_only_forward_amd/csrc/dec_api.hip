@@ -125,6 +125,18 @@ int proj_splits(const dec_config &c, int N, int K, int B, bool grouped = false) 
     return grouped ? gemv_grouped_max_splits(K) : gemv_max_splits(N, K);
 }
 
+// One decode row of a model whose residual + RMSNorm the next projection's
+// blocks form in their prologue (bf16 weights, dense FFN; each block reads the
+// row and its k-split partials before its first product, which pays only
+// where the projections are short: Qwen2.5-0.5B B = 1 1.232 -> 1.166 ms a
+// step, SmolLM2-135M 1.256 -> 1.148, but Mistral-7B, d x F = 58.7 M, 3.600 ->
+// 3.690, so the larger FFNs keep the norm kernel).
+bool row_norm_fused(const dec_config &c) {
+    const long d = c.hidden, F = c.ffn_dim;
+    return c.weight_dtype != DEC_WEIGHT_F32 && c.n_experts == 0 && F % 8 == 0 && d % 64 == 0 && d <= 8192 &&
+           d * F <= (16l << 20);
+}
+
 bool plan(const dec_config &c, Plan &p) {
     const size_t d = c.hidden, hd = c.head_dim, qd = (size_t)c.n_heads * hd, kvd = (size_t)c.n_kv_heads * hd;
     const size_t F = c.ffn_dim, E = c.n_experts, k = c.n_experts ? c.top_k : 0;
@@ -193,11 +205,13 @@ bool plan(const dec_config &c, Plan &p) {
     p.kvimg = take(c.weight_dtype == DEC_WEIGHT_F32 ? 0
                    : attn_tiles_bytes(c.max_seq, c.n_kv_heads, c.head_dim, c.kv_dtype));
     p.x = take((size_t)rows * d * 4);
-    p.x2 = take(d * 4);   // the other residual row of one-row decode (normed inside the projections)
-    // one-row decode: the down projection's k-split partials, apart from the
-    // partial buffer the next projection writes while its blocks still read
-    // them (at most one split per 64 k)
-    p.part2 = take((size_t)((c.ffn_dim + 63) / 64) * d * 4);
+    // row_norm_fused: the other residual row of one-row decode, and the down
+    // projection's k-split partials apart from the partial buffer the next
+    // projection writes while its blocks still read them (at most one split
+    // per 64 k)
+    const bool rnf = row_norm_fused(c);
+    p.x2 = take(rnf ? d * 4 : 0);
+    p.part2 = take(rnf ? (F + 63) / 64 * d * 4 : 0);
     const bool f32w = c.weight_dtype == DEC_WEIGHT_F32;
     p.a_hi = take(f32w ? 0 : p.act_elems * 2);
     p.a_lo = take(f32w ? 0 : std::max(p.act_elems * 2, f8_lo(d)));
@@ -440,17 +454,11 @@ void run_pass(dec_model *m, const Pass &ps) {
     const F8Act fa_d{ah, (uint8_t *)al, (uint8_t *)al + (size_t)mpad * d, d, mpad};
     // the fused gate|up takes these operands where it takes the DMA kernel
     const bool f8_ffn = f8 && c.n_experts == 0 && (long)((F + 127) / 128) * ((T + 255) / 256) >= num_cus();
-    // One decode row, bf16 weights, dense FFN: the residual + RMSNorm before
-    // gate|up, before q|k|v (after layer 0) and before the LM head is formed in
-    // those projections' own blocks (the row is read by every block) instead of
-    // a kernel of its own; the residual row alternates between x and x2.  Each
-    // block then reads the row and its k-split partials before its first
-    // product, which pays only where the projections are short: Qwen2.5-0.5B
-    // 1.232 -> 1.166 ms a step, SmolLM2-135M 1.256 -> 1.148, but Mistral-7B
-    // (d x F = 58.7 M) 3.600 -> 3.690, so the larger FFNs keep the norm kernel.
-    const bool rnf = ps.decode && T == 1 && !f32w && c.n_experts == 0 && ps.logits && ps.logit_rows == 1 &&
-                     m->s_hi && F % 8 == 0 && d % 64 == 0 && d <= 8192 &&
-                     (long)d * F <= (16l << 20);
+    // One decode row (row_norm_fused): the residual + RMSNorm before gate|up,
+    // before q|k|v (after layer 0) and before the LM head is formed in those
+    // projections' own blocks instead of a kernel of its own; the residual row
+    // alternates between x and x2.
+    const bool rnf = ps.decode && T == 1 && ps.logits && ps.logit_rows == 1 && m->s_hi && row_norm_fused(c);
     float *xc = m->x, *xn = m->x2;
     Partials pend{nullptr, 0, 0, 0};   // the down partials the next projection's prologue adds
 
