@@ -484,15 +484,18 @@ void run_pass(dec_model *m, const Pass &ps) {
             pq = f8 ? proj_f8(m, m->f8w[l].qkv, T, fa_d) : proj(m, qkv, 3, d, T, ah, al, af, d);
         }
         // attention -> a (row stride qd)
-        // one decode row in several attention splits: the output projection's
+        // one decode row in 2-32 attention splits: the output projection's
         // blocks merge the splits of their k range (no merge kernel; Mistral-7B
-        // B = 1 3.604 -> 3.542 ms a step, Qwen2.5-0.5B 1.166 -> 1.108)
+        // B = 1 3.604 -> 3.542 and 3.617 -> 3.595 ms a step on two boxes,
+        // Qwen2.5-0.5B 1.166 -> 1.108).  64 splits (the bf16 cache's MFMA
+        // attention at 4096 positions) measured 3.510 -> 3.598: the merge
+        // kernel stays there.
         bool am_o = false;
         int am_s = 0;
         if (ps.decode) {
             // RoPE and the new K/V rows are formed inside the attention kernel
             const int S = attn_splits_for(m, T, ps.hpos);
-            am_o = T == 1 && !f32w && S > 1 && S <= 64;
+            am_o = T == 1 && !f32w && S > 1 && S <= 32;
             const RopeArgs ra{pq, c.qkv_bias ? w.bq : nullptr, c.qkv_bias ? w.bk : nullptr,
                               c.qkv_bias ? w.bv : nullptr, m->rope, c.rope_pairing, m->ring};
             Tick tk(m, DEC_K_ATTN_DECODE);

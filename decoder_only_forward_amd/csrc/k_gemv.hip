@@ -187,20 +187,19 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
     // its split partials o_s (unnormalised), maxima m_s and normalisers l_s
     // combine as sum_s f_s o_s / sum_s f_s l_s with f_s = 2^(m_s - max m), the
     // splits taken in ascending order (the split merge kernel's operations and
-    // order).  A thread takes two adjacent dims and issues the loads of up to
-    // 32 splits' (m, l) and (o, o') at once (lanes of one head read the same
-    // (m, l)); splits past 32 are read one by one.
+    // order).  A thread takes two adjacent dims and issues every (m, l) and
+    // (o, o') load of its up to 32 splits at once (lanes of one head read the
+    // same (m, l)).
     auto am_prologue = [&]() {
         const AttnMerge &a = p.am;
         const int hd = a.hd, S = a.splits, ld = hd + 2;
-        const int S1 = S < 32 ? S : 32;
         for (int k = kbeg + 2 * tid; k < kend; k += 512) {
             const int h = k / hd, i = k % hd;
             const float *src = a.part + (size_t)h * S * ld;
             float2 ml[32], o[32];
 #pragma unroll
             for (int u = 0; u < 32; u++) {
-                if (u < S1) {
+                if (u < S) {
                     ml[u] = *reinterpret_cast<const float2 *>(src + u * ld + hd);
                     o[u] = *reinterpret_cast<const float2 *>(src + u * ld + i);
                 }
@@ -208,25 +207,16 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
             float mx = -INFINITY;
 #pragma unroll
             for (int u = 0; u < 32; u++)
-                if (u < S1) mx = fmaxf(mx, ml[u].x);
-            for (int s2 = 32; s2 < S; s2++) mx = fmaxf(mx, src[s2 * ld + hd]);
+                if (u < S) mx = fmaxf(mx, ml[u].x);
             float A0 = 0.f, A1 = 0.f, L = 0.f;
 #pragma unroll
             for (int u = 0; u < 32; u++) {
-                if (u < S1) {
+                if (u < S) {
                     const float f = ml[u].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[u].x - mx);
                     L += ml[u].y * f;
                     A0 += o[u].x * f;
                     A1 += o[u].y * f;
                 }
-            }
-            for (int s2 = 32; s2 < S; s2++) {
-                const float2 m2 = *reinterpret_cast<const float2 *>(src + s2 * ld + hd);
-                const float2 o2 = *reinterpret_cast<const float2 *>(src + s2 * ld + i);
-                const float f = m2.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2.x - mx);
-                L += m2.y * f;
-                A0 += o2.x * f;
-                A1 += o2.y * f;
             }
             uint32_t hi, lo;
             split2_bf16(A0 / L, A1 / L, hi, lo);

@@ -102,7 +102,7 @@ struct RowNorm {
 // attention ([head][split][hd + 2]: hd unnormalised outputs, the split's
 // maximum, its normaliser) merged per element in split order, as the
 // separate merge kernel does (the running maximum and normaliser of rml "The
-// decoder", section "Attend", combined over splits).  splits <= 64.
+// decoder", section "Attend", combined over splits).  2 <= splits <= 32.
 struct AttnMerge {
     const float *part;
     int hd;

@@ -146,3 +146,11 @@ def test_mistral_one_layer_decode_b32_at_full_ring():
     attention split per row and kv head) and overwrites slot 0, then 1."""
     cfg = configs.one_layer(configs.MISTRAL)
     _run(cfg, P=4096, B=32, steps=2, sample_rows=[4095], decode_rows=[0, 31], sample_steps={0, 1})
+
+
+def test_mistral_one_layer_decode_b1_at_full_ring():
+    """Mistral-7B width at batch 1 after a 4096-token prompt: the attention
+    runs in 32 splits per kv head and the output projection's blocks merge
+    them (one split range holds the overwritten ring slot)."""
+    cfg = configs.one_layer(configs.MISTRAL)
+    _run(cfg, P=4096, B=1, steps=3, sample_rows=[4095], decode_rows=[0], sample_steps={0, 1, 2})

@@ -74,6 +74,13 @@ def test_mistral_one_layer_bf16_cache_prefill_4096_and_decode_through_ring_wrap(
          decode_rows=[0, 7], sample_steps={0, 5})
 
 
+def test_mistral_one_layer_bf16_cache_decode_b1_at_full_ring():
+    """Batch 1 on the bf16 cache after 4096 prompt tokens: the MFMA decode
+    attention in 64 splits per kv head, merged by the split merge kernel."""
+    cfg = configs.one_layer(configs.MISTRAL).replace(name="mistral-1l-kvbf16", kv_bf16=True)
+    _run(cfg, P=4096, B=1, steps=3, sample_rows=[4095], decode_rows=[0], sample_steps={0, 1, 2})
+
+
 def test_qwen25_one_layer_bf16_cache_prefill_1024_and_decode_b16():
     cfg = configs.one_layer(configs.QWEN25).replace(name="qwen25-1l-kvbf16", kv_bf16=True)
     _run(cfg, P=1024, B=16, steps=3, sample_rows=[0, 127, 128, 1023],
