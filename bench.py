@@ -44,11 +44,11 @@ HBM_PEAK_GBS = 8000.0
 _COMMON = {"decoder_only_forward_amd/csrc/common.h":
            "a08d4f553fd07b7970e5b481899ba0e771341cb515b05933bd0498a71b7869c7"}
 _ATTN_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_decode.hip":
-                                 "c1374de5317ec7f7de41b536a73140d901edab53f93c66558c2820bf7b86dd4c",
+                                 "0f2fd612465bb7cbb947ee0ad3a5ffe3f28fc1e9d7af5722580cdc48688cebfd",
                                  "decoder_only_forward_amd/csrc/kvcache.h":
                                  "b917a66e4ecfcb8f83f86f04cd3aed72acacdc8f768e657cc443a9cc9aa212b4"})
 _GEMV_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemv.hip":
-                                 "11f73b184e2f0a6eac6252819b3d4309b847dfd1a45ddedad296e73af96448c6"})
+                                 "1627cf069bef2462bdf9daaeb309411304b10900ac40d8b763d7086f4e07736f"})
 _GEMM_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemm.hip":
                                  "35831c13a16babcb3c1ade248842e44497a91aad2bb89f9ccf4e9ddf241b8c66"})
 _TILES_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_prefill_tiles.hip":
@@ -59,17 +59,17 @@ MEASURED_TRAFFIC = {
     # B = 32 launches: the lane-group kernel (fp32 cache; the 24-bit cache in
     # 8-wave blocks), the MFMA kernel in 8-wave blocks (bf16 cache)
     ("attn_decode_kernel", "fp32"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                     "bytes_per_launch": 1078972198},
+                                     "bytes_per_launch": 1078970933},
     ("attn_decode_mfma_kernel", "bf16"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                          "bytes_per_launch": 541900500},
+                                          "bytes_per_launch": 541889690},
     ("attn_decode_kernel", "f24"): {"sources": _ATTN_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                                    "bytes_per_launch": 810591850},
+                                    "bytes_per_launch": 810591101},
     ("gemv_decode", "fp32"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                              "bytes_per_launch": 121778370},
+                              "bytes_per_launch": 121781241},
     ("gemv_decode", "bf16"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                              "bytes_per_launch": 121778370},
+                              "bytes_per_launch": 121781241},
     ("gemv_decode", "f24"): {"sources": _GEMV_SOURCES, "workload": ("mistral-7b", 32, 4096),
-                             "bytes_per_launch": 121778370},
+                             "bytes_per_launch": 121781241},
     ("gemm_prefill", "fp32"): {"sources": _GEMM_SOURCES, "workload": ("mistral-7b", 32, 4096),
                                "bytes_per_launch": 1716674994},
     ("attn_prefill", "fp32"): {"sources": _TILES_SOURCES, "workload": ("mistral-7b", 32, 4096),
