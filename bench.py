@@ -162,6 +162,29 @@ def cpu_baseline(cfg, wd, B=32, prefill_tokens=32):
                       f"and a prefill of the prompt's first {prefill_tokens} tokens ({dt_pre:.1f} s)"}
 
 
+def ceilings():
+    """Measured ceilings beside the published peaks (libdec_probe.so): a
+    streaming read of 4 GiB with non-temporal 16-byte loads, a 1 GiB
+    device-to-device copy (read + write bytes), and back-to-back bf16 MFMAs
+    (32x32x16, four chains a wave, no loads); mean of 5 timed launches each."""
+    import torch
+    from decoder_only_forward_amd import probe
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    ms_r = probe.stream_read(buf, reps=5)
+    read = buf.numel() / (ms_r * 1e-3) / 1e9
+    del buf
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    ms_c = probe.copy(src, dst, reps=5)
+    copy = 2 * src.numel() / (ms_c * 1e-3) / 1e9
+    del src, dst
+    ms_m, fl = probe.mfma_bf16(iters=4096, reps=5)
+    torch.cuda.empty_cache()
+    return {"hbm_read_GBps": round(read, 1), "hbm_copy_GBps": round(copy, 1),
+            "mfma_bf16_TFLOPs": round(fl / (ms_m * 1e-3) / 1e12, 1),
+            "source": "probe kernels of libdec_probe.so (include/dec_probe.h), HIP events"}
+
+
 def kv_bytes(cfg):
     """Bytes of one cached K or V element: fp32 4, bf16 2, the 24-bit format 3."""
     return 2 if cfg.kv_bf16 else (3 if getattr(cfg, "kv_f24", False) else 4)
@@ -708,6 +731,11 @@ def main():
         if out["prefill_f16f8"]["gemm_prefill"] is not None:
             out["prefill_f16f8"]["gemm_prefill"]["mfma_counters"] = measured_mfma(("gemm_prefill_f16f8", "fp32"),
                                                                                   (cfg.name, B, P))
+    if not args.only:
+        # measured ceilings beside the published peaks the roofline objects use
+        out["ceilings"] = ceilings()
+        out["roofline"]["frac_of_measured_read"] = round(out["roofline"]["achieved"] /
+                                                         out["ceilings"]["hbm_read_GBps"], 4)
     if not args.no_cpu_baseline and not args.only:
         try:
             out["cpu_baseline"] = cpu_baseline(cfg, wd, B=B, prefill_tokens=args.cpu_steps)

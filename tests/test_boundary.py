@@ -30,6 +30,18 @@ def test_header_exports_are_all_present():
         assert hasattr(L, n), n
 
 
+def test_probe_header_exports_are_all_present():
+    from decoder_only_forward_amd import probe
+    if not os.path.exists(probe.LIB_PATH):
+        pytest.skip("libdec_probe.so not built (run __graft_entry__.build())")
+    L = probe.load()
+    with open(os.path.join(ROOT, "include", "dec_probe.h")) as f:
+        names = re.findall(r"\bint\s+(decp_\w+)\s*\(", f.read())
+    assert set(names) == set(probe.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
 def test_workspace_bytes_is_host_only_and_validates():
     _lib()
     n = D.workspace_bytes(configs.MISTRAL, max_batch=32, max_prefill=4096)
