@@ -373,10 +373,12 @@ Partials proj(dec_model *m, const WSeg *segs, int nseg, int K, int T, const u16 
     }
     if (gemv) {
         const int S = gemv_splits(N, K, T);
+        // one split (the LM head): straight into `out`, no reduction pass
+        float *g = (out && S == 1) ? out : m->part;
         Tick tk(m, DEC_K_GEMV);
-        launch_gemv(m->st, segs, nseg, K, hi, lo, lda, T, m->part, S, (size_t)T * N, N, rn, am);
+        launch_gemv(m->st, segs, nseg, K, hi, lo, lda, T, g, S, (size_t)T * N, N, rn, am);
         tk.done((double)N * K * 2 + (double)T * K * 4 + (double)T * N * 4, 2.0 * T * N * K);
-        return Partials{m->part, S, (size_t)T * N, N};
+        return Partials{g, S, (size_t)T * N, N};
     }
     // into the partial buffer, a grid with a half-empty last round, or of fewer
     // tiles than CUs, is split over k (where the buffer holds the splits)
