@@ -48,7 +48,7 @@ _ATTN_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_decode.hi
                                  "decoder_only_forward_amd/csrc/kvcache.h":
                                  "b917a66e4ecfcb8f83f86f04cd3aed72acacdc8f768e657cc443a9cc9aa212b4"})
 _GEMV_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemv.hip":
-                                 "1627cf069bef2462bdf9daaeb309411304b10900ac40d8b763d7086f4e07736f"})
+                                 "1a0a2991d209dd4af919067425a54230bea3a10e27f96688d06e0025b86b6ee5"})
 _GEMM_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_gemm.hip":
                                  "35831c13a16babcb3c1ade248842e44497a91aad2bb89f9ccf4e9ddf241b8c66"})
 _TILES_SOURCES = dict(_COMMON, **{"decoder_only_forward_amd/csrc/k_attn_prefill_tiles.hip":

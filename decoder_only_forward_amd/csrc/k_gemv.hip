@@ -138,8 +138,9 @@ __global__ void __launch_bounds__(256, 1) gemv_dma_kernel(GemvParams p) {
 
     // RN prologue: x_new = x + sum of the split partials over the whole row,
     // its sum of squares, then the normed (hi, lo) pair of [kbeg, kend) into
-    // LDS; the same operations and order as the residual + RMSNorm kernel
-    // (split partials summed in order, then added to x; a = x * rs * g).
+    // LDS; the residual + RMSNorm kernel's operations (split partials summed
+    // in order, then added to x; a = x * rs * g), with the sum of squares
+    // reduced over this block's 256 threads (its own lane and wave order).
     auto rn_prologue = [&]() {
         const RowNorm &n = p.rn;
         const int nv = n.d / 4;
